@@ -1,0 +1,313 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv.so: the paged KV-cache hot path on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Three steps, as the source pages describe them:
+ *   1. turn each request's block table (logical block -> physical block id)
+ *      into a per-token write slot: slot = physical_id * block_size +
+ *      position % block_size;
+ *   2. scatter this step's new K/V rows into the paged cache at those slots;
+ *   3. attend over each request's cached K/V by walking its block table
+ *      across non-contiguous physical blocks, with a softmax whose normaliser
+ *      spans all blocks (computed online, split over long contexts and merged).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [W]  "Deep Dive into vLLM Worker-Side GPU KV Cache Initialization"
+ *        (kongchang.com) and its Chinese original "vLLM Worker侧GPU KV
+ *        Cache初始化流程深度解析" [W-zh].
+ *   [E]  "vLLM의 KV cache 연결 흐름" (llm-engineer.pages.dev card
+ *        vllm-kv-cache-engine-to-worker).
+ *   [P]  "Understanding PageAttention Memory Optimization" (freaks.city).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All array arguments are DEVICE pointers owned by the caller, except the
+ *   pkv_cache descriptor and plan structs, which live in host memory and are
+ *   read during the call only.  The library never allocates, frees or
+ *   synchronises; each call enqueues its kernels on `stream` and returns.
+ *   Inputs must stay alive until the stream has passed the call.
+ * - Integer ids, lengths and offsets are int32 unless stated; slots are int64.
+ * - Host-side argument checks run before anything is enqueued.  On failure a
+ *   negative pkv_status is returned and nothing is launched.  A launch failure
+ *   returns PKV_ERR_HIP.  Zero-sized work (no tokens, no sequences) returns
+ *   PKV_OK and launches nothing.
+ * - Data-dependent errors never fault: see each call.
+ * - The only library state is a per-device cache of the compute-unit count;
+ *   calls are reentrant.  Calls on one stream run in order; calls that share
+ *   an output or workspace on different streams race.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Every entry point is exported from the shared library; nothing else is. */
+#define PKV_API __attribute__((visibility("default")))
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = -1,        /* a required pointer is NULL                     */
+  PKV_ERR_SHAPE = -2,       /* sizes, strides or alignment inconsistent       */
+  PKV_ERR_DTYPE = -3,       /* unknown dtype or unsupported dtype combination */
+  PKV_ERR_UNSUPPORTED = -4, /* head_dim / block_size / group size not built   */
+  PKV_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required        */
+  PKV_ERR_HIP = -6          /* the HIP runtime reported an error              */
+} pkv_status;
+
+typedef enum {
+  PKV_F32 = 0,       /* IEEE binary32                                        */
+  PKV_BF16 = 1,      /* bfloat16                                             */
+  PKV_FP8_E4M3 = 2   /* OCP FP8 E4M3 ("FN"): bias 7, max 448, NaN = 0x7F/0xFF */
+} pkv_dtype;
+
+/*
+ * One attention layer's view of a paged KV cache [W § Step 2: View
+ * Transformation; W-zh § Worker与ModelRunner的协作: the
+ * [num_blocks, block_size, num_heads, head_dim] layout].
+ *
+ * `k` and `v` each point at a plane of `num_blocks` physical blocks.  Block b
+ * starts `b * block_stride` ELEMENTS after the plane base and holds
+ * [block_size, num_kv_heads, head_dim] contiguous elements (token-major, then
+ * head, then dim).  block_stride >= block_size * num_kv_heads * head_dim lets
+ * K and V of one block interleave in one byte buffer.  Several layers may
+ * share the same planes (layers of different groups in the same slot share a
+ * tensor [W § Physical View: Two KVCacheTensors]); their block ids never
+ * collide because the groups draw from one pool.
+ *
+ * Alignment: k, v and block_stride * element size must be multiples of 16 B
+ * (256 B recommended [W-zh § 第一步：物理分配]).
+ *
+ * dtype PKV_FP8_E4M3: stored code c means value decode(c) * k_scale (or
+ * v_scale); a write quantises x as encode(float(x) * (1.0f / scale)) with
+ * round-to-nearest-even and saturation to +-448 [W-zh § KV Cache技术背景:
+ * one byte per element halves the cache].  Scales are ignored otherwise.
+ */
+typedef struct {
+  void* k;
+  void* v;
+  int64_t block_stride;
+  int32_t num_blocks;
+  int32_t block_size;    /* 4, 8, 16 or 32 tokens [W § PagedAttention and Block Management] */
+  int32_t num_kv_heads;
+  int32_t head_dim;      /* 8, 16, 32, 64, 128 or 256 */
+  int32_t dtype;         /* pkv_dtype */
+  float k_scale;
+  float v_scale;
+} pkv_cache;
+
+/* Human-readable name of a pkv_status value (static storage). */
+PKV_API const char* pkv_status_string(int status);
+
+/*
+ * KV bytes one token occupies across `num_layers` layers:
+ * num_layers * num_kv_heads * head_dim * 2 (K and V) * element bytes
+ * [W-zh § KV Cache技术背景, the 80-layer / 8-head / 128-dim example].
+ * Host-only arithmetic.  Returns -1 for a bad dtype or negative sizes.
+ */
+PKV_API int64_t pkv_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t dtype);
+
+/*
+ * Step 1 -- slot mapping [W § Pinpointing the Token Slot; E § Slot mapping은
+ * 왜 필요한가; E § EngineCore가 하는 일 (num_new_tokens)].
+ *
+ * block_table      [num_reqs, bt_stride] int32; entry j of row r is the
+ *                  physical id of request r's logical block j, -1 if none.
+ * query_start_loc  [num_reqs + 1] int32, non-decreasing; request r owns the
+ *                  step's tokens [query_start_loc[r], query_start_loc[r+1]).
+ * num_computed     [num_reqs] int32: tokens of r already in the cache; token
+ *                  t of r sits at position num_computed[r] + t - qsl[r].
+ * slot_mapping     [num_tokens] int64 output; every element is written:
+ *                  slot = id * block_size + position % block_size, or -1 for
+ *                  padding tokens (t >= query_start_loc[num_reqs]) and for
+ *                  tokens whose lookup is invalid (logical block >= bt_stride,
+ *                  id < 0 or id >= num_blocks, negative position).
+ * err_count        optional device int32; each invalid lookup adds 1 to it
+ *                  (padding does not).  The caller zeroes it.
+ */
+PKV_API int pkv_slot_mapping(const int32_t* block_table, int32_t bt_stride,
+                     int32_t num_reqs, const int32_t* query_start_loc,
+                     const int32_t* num_computed, int32_t block_size,
+                     int32_t num_blocks, int32_t num_tokens,
+                     int64_t* slot_mapping, int32_t* err_count,
+                     hipStream_t stream);
+
+/*
+ * Step 2 -- KV cache write ("reshape and cache") [W § Summary: the slot
+ * decides where each new token is written; E § Slot mapping은 왜 필요한가].
+ *
+ * key, value       token t, head h, dim d at element
+ *                  t * src_token_stride + h * src_head_stride + d, of dtype
+ *                  src_dtype (PKV_F32 or PKV_BF16).  Strides in elements;
+ *                  base pointers and strides 16-B aligned in bytes.
+ * slot_mapping     [num_tokens] int64; slot s >= 0 writes row s % block_size of
+ *                  block s / block_size; s < 0 is skipped; s >= num_blocks *
+ *                  block_size is skipped too (never written out of range).
+ * cache            destination planes.  Same dtype as the source: bit copy.
+ *                  F32 -> BF16: round to nearest even.  -> FP8_E4M3: quantise
+ *                  with the cache's k_scale / v_scale.
+ * Two tokens with one slot in a call race (the pages leave it undefined).
+ */
+PKV_API int pkv_cache_write(const void* key, const void* value, int32_t src_dtype,
+                    int64_t src_token_stride, int64_t src_head_stride,
+                    const int64_t* slot_mapping, int32_t num_tokens,
+                    const pkv_cache* cache, hipStream_t stream);
+
+/*
+ * Split plan of the decode attention: how each sequence's visible blocks are
+ * cut into splits, and the workspace the partial results need.  Depends only
+ * on the arguments and on the current device's compute-unit count.
+ */
+typedef struct {
+  int32_t split_blocks;   /* blocks per split (the last split may be shorter)  */
+  int32_t max_splits;     /* splits of the longest possible sequence           */
+  int32_t heads_per_item; /* query heads one work item processes               */
+  int32_t reserved;
+  size_t workspace_bytes; /* partial (acc, m, l) storage for num_rows rows      */
+} pkv_decode_plan;
+
+/*
+ * Fill `plan` for a decode (one query token per row) over `num_rows` rows.
+ * max_seq_len bounds every seq_lens entry; sliding_window 0 = full attention.
+ */
+PKV_API int pkv_decode_plan_make(int32_t num_rows, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t max_seq_len,
+                         int32_t sliding_window, pkv_decode_plan* plan);
+
+/*
+ * Step 3 (decode form) -- paged attention, one query token per sequence
+ * [E § Slot mapping은 왜 필요한가 (attention reads past K/V through the block
+ * table) and § Forward 직전의 metadata; P § Handling Softmax Across Blocks;
+ * W-zh § Worker与ModelRunner的协作 (tiling + online softmax); W § Hybrid
+ * Attention Mechanisms (GQA, sliding window)].
+ *
+ * out, q           [num_seqs, num_q_heads, head_dim], dtype q_dtype.  q_dtype
+ *                  is PKV_F32 for an F32 cache and PKV_BF16 for BF16 / FP8
+ *                  caches; out has q's dtype.
+ * block_table      [num_seqs, bt_stride] int32 physical ids.
+ * seq_lens         [num_seqs] int32 in [1, max_seq_len]: tokens of the
+ *                  sequence including this step's (already written) token.
+ * softmax_scale    multiplies q.k before the softmax (usually 1/sqrt(D)).
+ * sliding_window   0, or W > 0: a query at position p sees keys p-W+1 .. p.
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ * workspace        device scratch of at least plan.workspace_bytes
+ *                  (pkv_decode_plan_make with the same arguments and
+ *                  num_rows = num_seqs); need not be initialised.
+ * A row whose seq_len is out of range, or that needs a block-table entry that
+ * is past bt_stride, negative or >= num_blocks, gets NaN outputs; no memory
+ * outside the cache planes is ever read for it.
+ */
+PKV_API int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dtype,
+                               int32_t num_seqs, int32_t num_q_heads,
+                               const pkv_cache* cache,
+                               const int32_t* block_table, int32_t bt_stride,
+                               const int32_t* seq_lens, int32_t max_seq_len,
+                               float softmax_scale, int32_t sliding_window,
+                               void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
+ * The two phases of pkv_paged_attention_decode as separate calls, for callers
+ * that merge partial results themselves (for example across devices) or time
+ * the phases.  Phase 1 writes, per (row, query head, split), the base-2
+ * partial softmax state
+ *     m,  l = sum_j 2^(s_j - m),  acc = sum_j 2^(s_j - m) v_j,
+ *     s_j = softmax_scale * log2(e) * q.k_j,
+ * into `workspace`; rows with a single split get their final output written
+ * to `out` directly.  Phase 2 merges the splits of the remaining rows:
+ *     out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
+ * Both take the plan that pkv_decode_plan_make produced for these arguments.
+ * Workspace layout (float32): acc [rows, Hq, max_splits, D], then
+ * m [rows, Hq, max_splits], then l [rows, Hq, max_splits].
+ */
+PKV_API int pkv_paged_attention_decode_partials(void* out, const void* q,
+                                        int32_t q_dtype, int32_t num_seqs,
+                                        int32_t num_q_heads,
+                                        const pkv_cache* cache,
+                                        const int32_t* block_table,
+                                        int32_t bt_stride,
+                                        const int32_t* seq_lens,
+                                        int32_t max_seq_len,
+                                        float softmax_scale,
+                                        int32_t sliding_window,
+                                        const pkv_decode_plan* plan,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+
+PKV_API int pkv_paged_attention_decode_combine(void* out, int32_t out_dtype,
+                                       int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t head_dim, int32_t block_size,
+                                       const int32_t* seq_lens,
+                                       int32_t sliding_window,
+                                       const pkv_decode_plan* plan,
+                                       const void* workspace,
+                                       size_t workspace_bytes,
+                                       hipStream_t stream);
+
+/*
+ * Workspace bytes pkv_paged_attention_chunked needs for these arguments.
+ */
+PKV_API int pkv_chunked_workspace_size(int32_t num_tokens, int32_t num_reqs,
+                               int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size,
+                               int32_t max_query_len, int32_t max_seq_len,
+                               int32_t sliding_window, size_t* bytes);
+
+/*
+ * Step 3 (chunked form) -- paged attention for a mixed step: requests with
+ * several query tokens (prefill chunks) and requests with one (decode)
+ * [E § EngineCore가 하는 일 (num_new_tokens per request) and § Forward 직전의
+ * metadata; W § Hybrid Attention Mechanisms; W-zh § 混合注意力机制].
+ *
+ * out, q           [num_tokens, num_q_heads, head_dim], dtype q_dtype (as in
+ *                  the decode form).
+ * query_start_loc  [num_reqs + 1] int32 as in pkv_slot_mapping; query_start_loc
+ *                  [num_reqs] <= num_tokens; rows past it are left untouched.
+ * seq_lens         [num_reqs] int32: tokens including this step's; query i of
+ *                  request r sits at position seq_lens[r] - q_len_r + i.
+ * max_query_len    bounds every q_len_r; max_seq_len bounds every seq_lens[r].
+ * causal           1: query at p sees keys <= p.  0: all keys < seq_len.
+ * sliding_window   0, or W: keys >= p - W + 1 only.
+ * workspace        at least pkv_chunked_workspace_size(...) bytes.
+ * Invalid rows (q_len > seq_len, lengths out of range, missing blocks) get NaN.
+ */
+PKV_API int pkv_paged_attention_chunked(void* out, const void* q, int32_t q_dtype,
+                                int32_t num_tokens, int32_t num_q_heads,
+                                const int32_t* query_start_loc,
+                                const int32_t* seq_lens, int32_t num_reqs,
+                                int32_t max_query_len, const pkv_cache* cache,
+                                const int32_t* block_table, int32_t bt_stride,
+                                int32_t max_seq_len, float softmax_scale,
+                                int32_t causal, int32_t sliding_window,
+                                void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/*
+ * FP8 E4M3 bulk codec with the exact conversions the cache write and the
+ * attention kernels use [W-zh § KV Cache技术背景].
+ *   quantize:   codes[i] = encode(float(x[i]) * (1.0f / scale)), x of src_dtype
+ *               (PKV_F32 or PKV_BF16); nearest-even, saturating to +-448,
+ *               NaN kept.
+ *   dequantize: out_dtype PKV_F32: out[i] = decode(codes[i]) * scale (the
+ *               conversion the attention kernels apply to V);
+ *               out_dtype PKV_BF16: out[i] = decode(codes[i]) as bfloat16,
+ *               exact, scale must be 1.0f (the conversion applied to K before
+ *               the bf16 dot products; the scale is applied to the score).
+ */
+PKV_API int pkv_fp8_e4m3_quantize(const void* x, int32_t src_dtype, int64_t n,
+                          float scale, uint8_t* codes, hipStream_t stream);
+PKV_API int pkv_fp8_e4m3_dequantize(const uint8_t* codes, int64_t n, float scale,
+                            int32_t out_dtype, void* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -113,7 +113,8 @@ def inv_scale(scale):
 
 def quantize(x, scale):
     """float32 elements -> e4m3 codes with a per-tensor scale."""
-    prod = (np.asarray(x, dtype=np.float32) * inv_scale(scale)).astype(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):   # inf/NaN inputs stay inf/NaN
+        prod = (np.asarray(x, dtype=np.float32) * inv_scale(scale)).astype(np.float32)
     return encode_fast(prod)
 
 

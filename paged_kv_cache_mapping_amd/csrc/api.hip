@@ -1,0 +1,49 @@
+// Library-wide entry points: status strings, sizing closed form, device info.
+#include <mutex>
+
+#include "host_common.h"
+
+namespace pkv {
+
+int device_cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    std::lock_guard<std::mutex> lock(mu);
+    if (cached[dev] > 0) return cached[dev];
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  if (dev < 64) {
+    std::lock_guard<std::mutex> lock(mu);
+    cached[dev] = cus;
+  }
+  return cus;
+}
+
+}  // namespace pkv
+
+extern "C" const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_ERR_NULL: return "PKV_ERR_NULL: a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "PKV_ERR_SHAPE: inconsistent sizes, strides or alignment";
+    case PKV_ERR_DTYPE: return "PKV_ERR_DTYPE: unknown or unsupported dtype combination";
+    case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED: head_dim, block_size or group size not built";
+    case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE: workspace missing or too small";
+    case PKV_ERR_HIP: return "PKV_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown pkv_status";
+  }
+}
+
+// Per-token KV bytes over all layers: layers * kv_heads * head_dim * 2 * elt.
+extern "C" int64_t pkv_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t dtype) {
+  const int elt = pkv::dtype_size(dtype);
+  if (elt == 0 || num_layers < 0 || num_kv_heads < 0 || head_dim < 0) return -1;
+  return (int64_t)num_layers * num_kv_heads * head_dim * 2 * elt;
+}

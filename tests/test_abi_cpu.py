@@ -1,0 +1,123 @@
+"""The C ABI without a GPU: exports, closed forms, host-side argument checks.
+
+Only calls that return before anything reaches the HIP runtime are made here
+(failing argument checks and pure host arithmetic).
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from paged_kv_cache_mapping_amd import _lib
+from paged_kv_cache_mapping_amd._lib import PkvCache
+from oracle import sizing
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"PKV_API\s+[\w\s\*]+?\b(pkv_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_the_expected_calls():
+    names = _declared()
+    for want in ("pkv_slot_mapping", "pkv_cache_write", "pkv_paged_attention_decode",
+                 "pkv_paged_attention_chunked", "pkv_decode_plan_make",
+                 "pkv_paged_attention_decode_partials", "pkv_paged_attention_decode_combine",
+                 "pkv_chunked_workspace_size", "pkv_kv_bytes_per_token", "pkv_status_string",
+                 "pkv_fp8_e4m3_quantize", "pkv_fp8_e4m3_dequantize"):
+        assert want in names
+    assert set(names) == set(_lib.SIGNATURES)   # the binding covers every declaration
+
+
+def test_library_exports_every_declared_symbol_and_nothing_else(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    declared = set(_declared())
+    assert declared <= exported
+    assert {s for s in exported if s.startswith("pkv_")} == declared
+    for name in declared:
+        assert getattr(lib, name) is not None
+
+
+def test_kv_bytes_per_token_matches_the_oracle_closed_form(lib):
+    assert lib.pkv_kv_bytes_per_token(80, 8, 128, _lib.PKV_BF16) == 327680
+    assert lib.pkv_kv_bytes_per_token(80, 8, 128, _lib.PKV_FP8_E4M3) == 163840
+    for layers, heads, d in ((1, 1, 8), (32, 8, 128), (12, 12, 64)):
+        for dt, name in ((_lib.PKV_F32, "f32"), (_lib.PKV_BF16, "bf16"), (_lib.PKV_FP8_E4M3, "fp8")):
+            assert lib.pkv_kv_bytes_per_token(layers, heads, d, dt) == \
+                sizing.kv_bytes_per_token(layers, heads, d, name)
+    assert lib.pkv_kv_bytes_per_token(1, 1, 8, 7) == -1
+
+
+def test_status_strings(lib):
+    for st in range(-6, 1):
+        assert lib.pkv_status_string(st).startswith(b"PKV_")
+    assert lib.pkv_status_string(-99) == b"unknown pkv_status"
+
+
+def _cache(**kw):
+    c = dict(k=0x1000, v=0x2000, block_stride=16 * 8 * 128, num_blocks=16, block_size=16,
+             num_kv_heads=8, head_dim=128, dtype=_lib.PKV_BF16, k_scale=1.0, v_scale=1.0)
+    c.update(kw)
+    return PkvCache(**c)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), _lib.PKV_ERR_NULL),
+    (dict(dtype=9), _lib.PKV_ERR_DTYPE),
+    (dict(head_dim=96), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(block_size=12), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(block_stride=100), _lib.PKV_ERR_SHAPE),
+    (dict(k=0x1008), _lib.PKV_ERR_SHAPE),                     # misaligned plane
+    (dict(dtype=_lib.PKV_FP8_E4M3, k_scale=0.0), _lib.PKV_ERR_SHAPE),
+])
+def test_cache_descriptor_checks(lib, kw, status):
+    c = _cache(**kw)
+    st = lib.pkv_cache_write(0x100, 0x100, _lib.PKV_BF16, 1024, 128, 0x100, 4, ctypes.byref(c), None)
+    assert st == status
+    st = lib.pkv_paged_attention_decode(0x100, 0x100, _lib.PKV_BF16, 4, 32, ctypes.byref(c), 0x100, 8,
+                                        0x100, 64, 0.1, 0, None, 0, None)
+    assert st == status
+
+
+def test_argument_checks_return_before_launching(lib):
+    c = _cache()
+    # slot mapping: unsupported block size, negative sizes, missing pointers
+    assert lib.pkv_slot_mapping(0x100, 4, 1, 0x100, 0x100, 12, 16, 4, 0x100, None, None) == \
+        _lib.PKV_ERR_UNSUPPORTED
+    assert lib.pkv_slot_mapping(0x100, 4, -1, 0x100, 0x100, 16, 16, 4, 0x100, None, None) == \
+        _lib.PKV_ERR_SHAPE
+    assert lib.pkv_slot_mapping(0x100, 4, 1, None, 0x100, 16, 16, 4, 0x100, None, None) == \
+        _lib.PKV_ERR_NULL
+    assert lib.pkv_slot_mapping(0x100, 4, 1, 0x100, 0x100, 16, 16, 0, 0x100, None, None) == _lib.PKV_OK
+    # cache write: bf16 source into an f32 cache, strides too small, misaligned source
+    c32 = _cache(dtype=_lib.PKV_F32)
+    assert lib.pkv_cache_write(0x100, 0x100, _lib.PKV_BF16, 1024, 128, 0x100, 4, ctypes.byref(c32),
+                               None) == _lib.PKV_ERR_DTYPE
+    assert lib.pkv_cache_write(0x100, 0x100, _lib.PKV_BF16, 100, 128, 0x100, 4, ctypes.byref(c),
+                               None) == _lib.PKV_ERR_SHAPE
+    assert lib.pkv_cache_write(0x108, 0x100, _lib.PKV_BF16, 1024, 128, 0x100, 4, ctypes.byref(c),
+                               None) == _lib.PKV_ERR_SHAPE
+    assert lib.pkv_cache_write(0x100, 0x100, _lib.PKV_BF16, 1024, 128, 0x100, 0, ctypes.byref(c),
+                               None) == _lib.PKV_OK
+    # attention: f32 query against a bf16 cache; heads not a multiple of KV heads
+    assert lib.pkv_paged_attention_decode(0x100, 0x100, _lib.PKV_F32, 4, 32, ctypes.byref(c), 0x100, 8,
+                                          0x100, 64, 0.1, 0, None, 0, None) in (_lib.PKV_ERR_DTYPE,)
+    # codec
+    assert lib.pkv_fp8_e4m3_quantize(0x100, _lib.PKV_FP8_E4M3, 16, 1.0, 0x100, None) == _lib.PKV_ERR_DTYPE
+    assert lib.pkv_fp8_e4m3_quantize(0x100, _lib.PKV_BF16, 16, 0.0, 0x100, None) == _lib.PKV_ERR_SHAPE
+    assert lib.pkv_fp8_e4m3_dequantize(0x100, 16, 2.0, _lib.PKV_BF16, 0x100, None) == \
+        _lib.PKV_ERR_UNSUPPORTED
+    assert lib.pkv_fp8_e4m3_dequantize(0x100, 0, 1.0, _lib.PKV_F32, 0x100, None) == _lib.PKV_OK
