@@ -1,0 +1,279 @@
+"""Benchmark of the paged KV-cache hot path on one MI355X.
+
+One step = one decode step of the Llama-3-8B-shaped layer (bf16, 32 query /
+8 KV heads, head_dim 128, block 16, 64 sequences with 128..2048 tokens):
+slot mapping -> KV cache write -> paged decode attention (split phase +
+combine).  Steps rotate over three KV pools that hold the same logical data
+under different physical block permutations (3 GiB in total), so the 256 MB
+last-level cache cannot serve the KV reads.
+
+Prints one JSON line: the whole step's algorithmic HBM bytes per second
+(value), the split kernel's roofline (HIP events around each of its launches),
+bulk KV-write rates, and the CPU oracle on a bounded sample of the same step.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E, AMD's published peak
+POOLS = 3
+SPLIT_KERNEL = "decode_stream_mfma_kernel"
+PMC_FILE = os.path.join(ROOT, "profiles", "decode_split_llama8b_b64_pmc.json")
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_mapping_amd", "csrc", "decode.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--split-blocks", type=int, default=0, help="override the decode split (tuning)")
+    p.add_argument("--variant", type=int, default=0, help="decode kernel variant (tuning)")
+    p.add_argument("--workers", type=int, default=0, help="balanced-scheme workers (tuning)")
+    p.add_argument("--calibration-copy", action="store_true",
+                   help="also run a plain 1 GiB device copy (scale reference for HBM counters)")
+    return p.parse_args()
+
+
+def source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per split-kernel launch from committed rocprofv3 counters,
+    or None when absent or taken on a different kernel source."""
+    try:
+        with open(PMC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def algorithmic_bytes(w):
+    """HBM bytes a decode step must move, by kernel (see the roofline notes)."""
+    B, Hq, D, Hkv = w.num_reqs, w.num_q_heads, w.head_dim, w.num_kv_heads
+    nblk = int(sum(-(-int(L) // w.block_size) for L in w.seq_lens))
+    kv = w.kv_read_bytes()
+    q = B * Hq * D * 2
+    out = B * Hq * D * 2
+    split = kv + q + nblk * 4 + B * 4
+    combine = out
+    slot = B * (4 * 3 + 4 + 8)            # qsl, computed, table entry, slot out
+    write = B * Hkv * D * 2 * 2 * 2 + B * 8  # read + write K and V rows, slots
+    return dict(kv=kv, split=split, combine=combine, slot=slot, write=write,
+                step=split + combine + slot + write)
+
+
+def cpu_baseline(w, sample_seqs, min_seconds=10.0):
+    """The oracle, as it stands, on the first `sample_seqs` sequences of the
+    step, repeated until about `min_seconds` of CPU work have been timed."""
+    from oracle import attention, paging
+    import copy
+    sub = copy.copy(w)
+    sel = np.arange(sample_seqs)
+    sub.seq_lens = w.seq_lens[sel]
+    sub.block_table = w.block_table[sel]
+    sub.query_start_loc = np.arange(sample_seqs + 1, dtype=np.int32)
+    sub.num_computed = w.num_computed[sel]
+    sub.new_k, sub.new_v, sub.q = w.new_k[sel], w.new_v[sel], w.q[sel]
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        slots, _ = paging.slot_mapping(sub.block_table, sub.query_start_loc, sub.num_computed,
+                                       sub.block_size)
+        kp, vp = paging.cache_write(sub.k_plane, sub.v_plane, sub.new_k, sub.new_v, slots, "bf16",
+                                    "bf16")
+        attention.paged_decode(sub.q, "bf16", kp, vp, "bf16", sub.block_table, sub.seq_lens,
+                               sub.scale)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    ab = algorithmic_bytes(sub)["step"] * reps
+    try:
+        import threadpoolctl
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    return dict(value=round(ab / dt / 1e9, 4), unit="GB/s", cores=int(threads), kind="oracle",
+                sample="%d of %d sequences of one step (%d tokens of context), %d repeats, %.1f s"
+                       % (sample_seqs, w.num_reqs, int(sub.seq_lens.sum()), reps, dt),
+                seconds=round(dt, 2), bytes=ab)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import paged_kv_cache_mapping_amd as pkv
+    from paged_kv_cache_mapping_amd import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.llama8b_decode()
+    base = w.device(dev)
+    nb = w.num_blocks
+
+    # three pools with the same logical data under different permutations
+    pools = [(base.cache, base.block_table)]
+    rng = np.random.default_rng(1234)
+    for _ in range(POOLS - 1):
+        perm = rng.permutation(nb)
+        pt = torch.from_numpy(perm.astype(np.int64)).to(dev)
+        k2 = torch.empty_like(base.cache.k)
+        v2 = torch.empty_like(base.cache.v)
+        k2.index_copy_(0, pt, base.cache.k)
+        v2.index_copy_(0, pt, base.cache.v)
+        bt = np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)], -1).astype(np.int32)
+        pools.append((pkv.CacheView.from_planes(k2, v2), torch.from_numpy(bt).to(dev)))
+
+    plan = pkv.decode_plan(w.num_reqs, w.num_q_heads, base.cache, w.max_seq_len)
+    pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, base.cache, w.max_seq_len,
+                  split_blocks=args.split_blocks or None, num_workers=args.workers or None,
+                  kernel_variant=args.variant)
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(base.q)
+    slots = torch.empty(w.num_reqs, dtype=torch.int64, device=dev)
+
+    def step(i, ev=None):
+        cache, bt = pools[i % POOLS]
+        pkv.slot_mapping(bt, base.query_start_loc, base.num_computed, w.block_size, nb, out=slots)
+        pkv.cache_write(base.new_k, base.new_v, slots, cache)
+        if ev is not None:
+            ev[0].record()
+        pkv.paged_attention_decode_partials(base.q, cache, bt, base.seq_lens, w.max_seq_len, w.scale,
+                                            plan, ws, out)
+        if ev is not None:
+            ev[1].record()
+        pkv.paged_attention_decode_combine(out, base.seq_lens, w.block_size, plan, ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps between synchronised events
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # split kernel alone: events around each launch, same rotation
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    split_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    ab = algorithmic_bytes(w)
+    value = ab["step"] / (ms_per_step * 1e-3) / 1e9
+    split_gbps = ab["split"] / (split_ms * 1e-3) / 1e9
+
+    # bulk KV writes: distinct random slots, bf16 -> bf16 and bf16 -> fp8
+    writes = {}
+    for T in (16384, 131072):
+        gen = torch.Generator(device=dev).manual_seed(T)
+        kx = torch.randn((T, w.num_kv_heads, w.head_dim), generator=gen, device=dev).to(torch.bfloat16)
+        vx = torch.randn((T, w.num_kv_heads, w.head_dim), generator=gen, device=dev).to(torch.bfloat16)
+        sl = torch.randperm(nb * w.block_size, generator=gen, device=dev)[:T]
+        for dst in ("bf16", "fp8"):
+            if dst == "bf16":
+                cache = pools[0][0]
+            else:
+                k8 = torch.empty(base.cache.k.shape, dtype=torch.uint8, device=dev)
+                v8 = torch.empty(base.cache.v.shape, dtype=torch.uint8, device=dev)
+                cache = pkv.CacheView.from_planes(k8, v8, 0.01, 0.01)
+            for _ in range(3):
+                pkv.cache_write(kx, vx, sl, cache)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 20
+            a.record()
+            for _ in range(reps):
+                pkv.cache_write(kx, vx, sl, cache)
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / reps
+            elt = 2 if dst == "bf16" else 1
+            nbytes = T * w.num_kv_heads * w.head_dim * 2 * (2 + elt) + T * 8
+            writes["%s_T%d" % (dst, T)] = dict(tokens_per_s=round(T / (ms * 1e-3)),
+                                              GBps=round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                              us=round(ms * 1e3, 2))
+    # one decode step's 64-token write (launch-latency bound)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(50):
+        pkv.cache_write(base.new_k, base.new_v, slots, pools[0][0])
+    b.record()
+    torch.cuda.synchronize()
+    writes["bf16_T64_step"] = dict(us=round(a.elapsed_time(b) / 50 * 1e3, 2))
+
+    if args.calibration_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    traffic = traffic_from_profile()
+    res = {
+        "metric": "paged decode attention HBM GB/s (% of peak) + KV cache writes tokens/s, 1 GPU",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)/sqrt(128) bf16 K/V/Q; lengths uniform 128..2048)",
+        "config": {"workload": w.name, "batch": w.num_reqs, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "pool_blocks": nb, "rotating_pools": POOLS,
+                   "context_tokens": int(w.seq_lens.sum()), "parallelism": "none (1 GPU)",
+                   "scheme": int(plan.scheme), "workers": int(plan.num_workers),
+                   "split_blocks": int(plan.split_blocks), "max_splits": int(plan.max_splits)},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "decode_attention": {"split_kernel_us": round(split_ms * 1e3, 2),
+                             "split_GBps": round(split_gbps, 1),
+                             "kv_bytes": ab["kv"], "step_bytes": ab["step"]},
+        "kv_write": writes,
+        "roofline": {"bound": "hbm", "achieved": round(split_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(split_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": SPLIT_KERNEL,
+                     "algorithmic_bytes_per_launch": ab["split"]},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, sample_seqs=w.num_reqs)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -160,26 +160,42 @@ PKV_API int pkv_cache_write(const void* key, const void* value, int32_t src_dtyp
                     const pkv_cache* cache, hipStream_t stream);
 
 /*
- * Split plan of the decode attention: how each sequence's visible blocks are
- * cut into splits, and the workspace the partial results need.  Depends only
- * on the arguments and on the current device's compute-unit count.
+ * Plan of the decode attention: how each row's visible blocks are cut into
+ * pieces that are folded independently and merged afterwards, and the
+ * workspace the partial results need.  Depends only on the arguments and on
+ * the current device's compute-unit count.
+ *
+ * scheme 0 (fixed splits): row r's visible blocks are cut into splits of
+ *   split_blocks blocks; one work item per (row, head group, split).
+ * scheme 1 (balanced): num_workers workers each take an equal contiguous
+ *   share (at least split_blocks blocks) of all (row, KV head group, block)
+ *   units; a row is cut wherever a share ends.  Used with bf16 / fp8 caches,
+ *   head_dim a multiple of 32 and block sizes that are multiples of 16.
  */
 typedef struct {
-  int32_t split_blocks;   /* blocks per split (the last split may be shorter)  */
-  int32_t max_splits;     /* splits of the longest possible sequence           */
-  int32_t heads_per_item; /* query heads one work item processes               */
-  int32_t reserved;
-  size_t workspace_bytes; /* partial (acc, m, l) storage for num_rows rows      */
+  int32_t split_blocks;   /* scheme 0: blocks per split; 1: least blocks per worker */
+  int32_t max_splits;     /* partial slots per (row, query head)                  */
+  int32_t heads_per_item; /* query heads one work item processes                  */
+  int32_t kernel_variant; /* 0: the library's choice.  Tuning only: 1 = vector
+                             ALUs for the scores (scheme 0 only); 2, 3, 4 =
+                             matrix cores with loads issued 0, 1 or 2 steps
+                             ahead (head_dim 128).  Every variant computes
+                             the same result up to rounding order.           */
+  size_t workspace_bytes; /* partial (acc, m, l) storage (+ piece counts)         */
+  int32_t scheme;         /* 0 or 1, see above                                    */
+  int32_t num_workers;    /* scheme 1: workers launched                           */
 } pkv_decode_plan;
 
 /*
- * Fill `plan` for a decode (one query token per row) over `num_rows` rows.
- * max_seq_len bounds every seq_lens entry; sliding_window 0 = full attention.
+ * Fill `plan` for a decode (one query token per row) over `num_rows` rows of
+ * a cache of `kv_dtype`.  max_seq_len bounds every seq_lens entry;
+ * sliding_window 0 = full attention.
  */
 PKV_API int pkv_decode_plan_make(int32_t num_rows, int32_t num_q_heads,
-                         int32_t num_kv_heads, int32_t head_dim,
-                         int32_t block_size, int32_t max_seq_len,
-                         int32_t sliding_window, pkv_decode_plan* plan);
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t kv_dtype,
+                                 int32_t max_seq_len, int32_t sliding_window,
+                                 pkv_decode_plan* plan);
 
 /*
  * Step 3 (decode form) -- paged attention, one query token per sequence
@@ -225,7 +241,8 @@ PKV_API int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dtype
  *     out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
  * Both take the plan that pkv_decode_plan_make produced for these arguments.
  * Workspace layout (float32): acc [rows, Hq, max_splits, D], then
- * m [rows, Hq, max_splits], then l [rows, Hq, max_splits].
+ * m [rows, Hq, max_splits], then l [rows, Hq, max_splits]; scheme 1 appends
+ * int32 piece counts [rows, Hq / heads_per_item].
  */
 PKV_API int pkv_paged_attention_decode_partials(void* out, const void* q,
                                         int32_t q_dtype, int32_t num_seqs,
@@ -257,8 +274,9 @@ PKV_API int pkv_paged_attention_decode_combine(void* out, int32_t out_dtype,
 PKV_API int pkv_chunked_workspace_size(int32_t num_tokens, int32_t num_reqs,
                                int32_t num_q_heads, int32_t num_kv_heads,
                                int32_t head_dim, int32_t block_size,
-                               int32_t max_query_len, int32_t max_seq_len,
-                               int32_t sliding_window, size_t* bytes);
+                               int32_t kv_dtype, int32_t max_query_len,
+                               int32_t max_seq_len, int32_t sliding_window,
+                               size_t* bytes);
 
 /*
  * Step 3 (chunked form) -- paged attention for a mixed step: requests with

@@ -43,8 +43,10 @@ class PkvDecodePlan(ctypes.Structure):
         ("split_blocks", ctypes.c_int32),
         ("max_splits", ctypes.c_int32),
         ("heads_per_item", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("kernel_variant", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
+        ("scheme", ctypes.c_int32),
+        ("num_workers", ctypes.c_int32),
     ]
 
 
@@ -61,7 +63,8 @@ SIGNATURES = {
     "pkv_kv_bytes_per_token": (_i64, [_i32, _i32, _i32, _i32]),
     "pkv_slot_mapping": (_int, [_vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "pkv_cache_write": (_int, [_vp, _vp, _i32, _i64, _i64, _vp, _i32, ctypes.POINTER(PkvCache), _vp]),
-    "pkv_decode_plan_make": (_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(PkvDecodePlan)]),
+    "pkv_decode_plan_make": (_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                    ctypes.POINTER(PkvDecodePlan)]),
     "pkv_paged_attention_decode": (_int, [_vp, _vp, _i32, _i32, _i32, ctypes.POINTER(PkvCache), _vp, _i32,
                                           _vp, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pkv_paged_attention_decode_partials": (_int, [_vp, _vp, _i32, _i32, _i32, ctypes.POINTER(PkvCache), _vp,
@@ -69,7 +72,7 @@ SIGNATURES = {
                                                    _vp, _sz, _vp]),
     "pkv_paged_attention_decode_combine": (_int, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _i32,
                                                   ctypes.POINTER(PkvDecodePlan), _vp, _sz, _vp]),
-    "pkv_chunked_workspace_size": (_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+    "pkv_chunked_workspace_size": (_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                           ctypes.POINTER(_sz)]),
     "pkv_paged_attention_chunked": (_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _i32, _i32,
                                            ctypes.POINTER(PkvCache), _vp, _i32, _i32, _f32, _i32, _i32,

@@ -137,7 +137,36 @@ def decode_plan(num_rows, num_q_heads, cache, max_seq_len, sliding_window=0):
     plan = PkvDecodePlan()
     check("pkv_decode_plan_make", lib.pkv_decode_plan_make(
         num_rows, num_q_heads, cache.num_kv_heads, cache.head_dim, cache.block_size,
-        max_seq_len, sliding_window, ctypes.byref(plan)))
+        cache.dtype, max_seq_len, sliding_window, ctypes.byref(plan)))
+    return plan
+
+
+def tune_plan(plan, num_rows, num_q_heads, cache, max_seq_len, sliding_window=0,
+              split_blocks=None, num_workers=None, kernel_variant=None):
+    """Override a plan's tuning fields and recompute the sizes they imply.
+
+    Scheme 0: split_blocks = blocks per split.  Scheme 1: split_blocks =
+    least blocks per worker, num_workers = workers launched.  The sizes follow
+    the rules documented with ``pkv_decode_plan`` in pagedkv.h.
+    """
+    bs = cache.block_size
+    nvis = -(-max(max_seq_len, 1) // bs)
+    if sliding_window > 0:
+        nvis = min(nvis, -(-(sliding_window + bs - 1) // bs))
+    if split_blocks is not None:
+        plan.split_blocks = int(split_blocks)
+    if num_workers is not None:
+        plan.num_workers = int(num_workers)
+    if kernel_variant is not None:
+        plan.kernel_variant = int(kernel_variant)
+    per_slot = num_rows * num_q_heads * (cache.head_dim + 2) * 4
+    if plan.scheme == 1:
+        plan.max_splits = -(-nvis // plan.split_blocks) + 1
+        plan.workspace_bytes = (per_slot * plan.max_splits
+                                + num_rows * (num_q_heads // plan.heads_per_item) * 4)
+    else:
+        plan.max_splits = -(-nvis // plan.split_blocks)
+        plan.workspace_bytes = per_slot * plan.max_splits if plan.max_splits > 1 else 0
     return plan
 
 
@@ -200,7 +229,7 @@ def chunked_workspace_size(num_tokens, num_reqs, num_q_heads, cache, max_query_l
     n = ctypes.c_size_t(0)
     check("pkv_chunked_workspace_size", lib.pkv_chunked_workspace_size(
         num_tokens, num_reqs, num_q_heads, cache.num_kv_heads, cache.head_dim, cache.block_size,
-        max_query_len, max_seq_len, sliding_window, ctypes.byref(n)))
+        cache.dtype, max_query_len, max_seq_len, sliding_window, ctypes.byref(n)))
     return n.value
 
 

@@ -20,6 +20,8 @@
 // partial states (m, l, acc) in the workspace for the combine kernel.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "host_common.h"
 
@@ -30,15 +32,19 @@ constexpr float kLazyRescale = 8.0f;  // keep a stale max until a score beats it
 struct DecodeArgs {
   void* out;
   const void* q;
-  // Row mode.  Decode: row b is sequence b, its query token is row b of q/out.
-  // Chunked: row t is token t of the step; its request is found through
-  // query_start_loc, its position is seq_len - q_len + (t - qsl[r]).
-  int32_t chunked;
+  // Row mode.  0 (decode): row b is sequence b, its query is row b of q/out.
+  // 1 (chunked tokens): row t is token t of the step; its request is found
+  //   through query_start_loc; position seq_len - q_len + (t - qsl[r]).
+  //   Tokens of single-query requests are skipped when skip_single is set.
+  // 2 (chunked requests): row r is request r; only requests with exactly one
+  //   query are processed (their query token is qsl[r]).
+  int32_t row_mode;
   int32_t causal;
-  int32_t single_only;      // chunked: skip rows of requests with q_len != 1
+  int32_t skip_single;
   const int32_t* qsl;
   int32_t num_reqs;
   int32_t max_query_len;
+  int32_t num_tokens;       // rows of q / out
   int32_t num_rows;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -62,6 +68,10 @@ struct DecodeArgs {
   float* ws_acc;
   float* ws_m;
   float* ws_l;
+  int32_t kernel_variant;   // 0 default; tuning: 1 vector-only, 2/3/4 prefetch depth 0/1/2
+  int32_t stream;           // balanced partition (piece counts in ws_np)
+  int32_t heads_per_item;
+  int32_t* ws_np;           // balanced partition: pieces per (row, head group)
 };
 
 // What one row attends to.
@@ -69,6 +79,7 @@ struct RowInfo {
   bool skip;      // not this kernel's row (padding, or handled elsewhere)
   bool valid;     // lengths and block-table row consistent
   int req;        // block-table row
+  int tok;        // row of q / out
   int lo, hi;     // inclusive visible key positions
   int first_blk;  // lo / block_size
   int nvis;       // visible logical blocks
@@ -79,8 +90,17 @@ __device__ __forceinline__ RowInfo row_info(const DecodeArgs& a, int row) {
   r.skip = false;
   r.valid = false;
   r.req = row;
+  r.tok = row;
+  r.nvis = 0;
   int L, p;
-  if (!a.chunked) {
+  if (a.row_mode == 0) {
+    L = a.seq_lens[row];
+    p = L - 1;
+    if (L <= 0 || L > a.max_seq_len) return r;
+  } else if (a.row_mode == 2) {
+    const int t0 = a.qsl[row];
+    if (a.qsl[row + 1] - t0 != 1 || t0 < 0 || t0 >= a.num_tokens) { r.skip = true; return r; }
+    r.tok = t0;
     L = a.seq_lens[row];
     p = L - 1;
     if (L <= 0 || L > a.max_seq_len) return r;
@@ -94,12 +114,12 @@ __device__ __forceinline__ RowInfo row_info(const DecodeArgs& a, int row) {
     }
     r.req = lo;
     const int ql = a.qsl[lo + 1] - a.qsl[lo];
-    if (a.single_only && ql != 1) { r.skip = true; return r; }
+    if (a.skip_single && ql == 1) { r.skip = true; return r; }
     L = a.seq_lens[lo];
     if (L <= 0 || L > a.max_seq_len || ql > L || ql > a.max_query_len) return r;
     p = L - ql + (row - a.qsl[lo]);
   }
-  r.hi = (a.chunked && !a.causal) ? L - 1 : p;
+  r.hi = (a.row_mode != 0 && !a.causal) ? L - 1 : p;
   r.lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
   if (r.lo > r.hi) return r;
   r.first_blk = r.lo >> a.bs_log2;
@@ -170,8 +190,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 
   const RowInfo span = row_info(a, b);
   if (span.skip) return;
-  const int tok = b;
-  const int64_t out_row = ((int64_t)tok * a.num_q_heads + h0) * D;
+  const int64_t out_row = ((int64_t)span.tok * a.num_q_heads + h0) * D;
   if (!span.valid) {
     // Invalid row: NaN output (split 0) and NaN partials in every split slot,
     // so that a combine pass over this row can only produce NaN.
@@ -211,7 +230,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   uint32_t qr[GT][QW];
   float qf[GT][kBf16Dot ? 1 : EPL];
   if constexpr (kBf16Dot) {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)tok * a.num_q_heads + h0) * D + sub * EPL;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + out_row + sub * EPL;
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
 #pragma unroll
@@ -219,7 +238,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         qr[h][i] = reinterpret_cast<const uint32_t*>(qp + h * D)[i];
     }
   } else {
-    const float* qp = reinterpret_cast<const float*>(a.q) + ((int64_t)tok * a.num_q_heads + h0) * D + sub * EPL;
+    const float* qp = reinterpret_cast<const float*>(a.q) + out_row + sub * EPL;
 #pragma unroll
     for (int h = 0; h < GT; ++h)
 #pragma unroll
@@ -414,6 +433,708 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 }
 
 // --------------------------------------------------------------------------
+// Split phase, uniform-block form: used when every wave load of RPW rows (and
+// every step of 16 rows) lies inside one block, i.e. block_size >= 16 and a
+// row takes >= 64 bytes.  The physical id of a step is wave-uniform, so it
+// lives in a scalar register and every K/V load is one 16-byte vector load at
+// a scalar base plus a per-lane constant offset.  Only a split's first and
+// last steps can hold positions outside the visible range; they take a masked
+// path.  The lazy-rescale test runs once per head per step on the lane's
+// largest score of the step.
+template <int D, int GT, int KV, int QT>
+__global__ __launch_bounds__(64) void decode_split_uni_kernel(DecodeArgs a) {
+  constexpr int kElt = KV == PKV_F32 ? 4 : (KV == PKV_BF16 ? 2 : 1);
+  constexpr int kRowBytes = D * kElt;
+  static_assert(kRowBytes >= 64, "uniform form needs rows of at least 64 bytes");
+  constexpr int LPR = kRowBytes / 16;                      // lanes per row
+  constexpr int EPL = 16 / kElt;                           // elements per lane
+  constexpr int RPW = kWave / LPR;                         // rows per wave load
+  constexpr int U = 16 / RPW;                              // loads per 16-row step
+  constexpr int kStepRows = U * RPW;                       // == 16
+  constexpr bool kBf16Dot = (QT == PKV_BF16);
+  constexpr int QW = kBf16Dot ? EPL / 2 : EPL;
+
+  const int lane = threadIdx.x;
+  const int grp = lane / LPR;
+  const int sub = lane % LPR;
+
+  const int kvgroups = a.num_kv_heads * a.sub_groups;
+  int w = blockIdx.x;
+  const int s = w % a.max_splits;
+  w /= a.max_splits;
+  const int kvg = w % kvgroups;
+  const int b = w / kvgroups;
+  const int kvh = kvg / a.sub_groups;
+  const int h0 = kvh * a.group + (kvg % a.sub_groups) * GT;
+
+  const RowInfo span = row_info(a, b);
+  if (span.skip) return;
+  const int64_t out_row = ((int64_t)span.tok * a.num_q_heads + h0) * D;
+  if (!span.valid) {
+    if (grp == 0) {
+      float nanv[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) nanv[e] = __builtin_nanf("");
+      for (int h = 0; h < GT; ++h) {
+        if (s == 0) store_out<QT, EPL>(a.out, out_row + h * D + sub * EPL, nanv);
+        if (a.max_splits > 1) {
+          const int64_t pr = ((int64_t)b * a.num_q_heads + h0 + h) * a.max_splits + s;
+          float* dst = a.ws_acc + pr * D + sub * EPL;
+          for (int e = 0; e < EPL; ++e) dst[e] = nanv[e];
+          if (sub == 0) {
+            a.ws_m[pr] = 0.f;
+            a.ws_l[pr] = nanv[0];
+          }
+        }
+      }
+    }
+    return;
+  }
+  const int nsplit = ceil_div(span.nvis, a.split_blocks);
+  if (s >= nsplit) return;
+
+  const int blk_begin = span.first_blk + s * a.split_blocks;
+  const int nb = min(a.split_blocks, span.first_blk + span.nvis - blk_begin);
+  const int bs = 1 << a.bs_log2;
+
+  int tab = -1;
+  if (lane < nb) tab = a.bt[(int64_t)span.req * a.bt_stride + blk_begin + lane];
+  const bool bad = (lane < nb) && (tab < 0 || tab >= a.num_blocks);
+  const bool any_bad = __ballot(bad) != 0;
+
+  uint32_t qr[GT][QW];
+  float qf[GT][kBf16Dot ? 1 : EPL];
+  if constexpr (kBf16Dot) {
+    const uint4* qp = reinterpret_cast<const uint4*>(
+        reinterpret_cast<const uint16_t*>(a.q) + out_row + sub * EPL);
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+#pragma unroll
+      for (int i = 0; i < QW / 4; ++i) {
+        const uint4 t = qp[h * (D * 2 / 16) + i];
+        qr[h][4 * i] = t.x; qr[h][4 * i + 1] = t.y; qr[h][4 * i + 2] = t.z; qr[h][4 * i + 3] = t.w;
+      }
+    }
+  } else {
+    const float* qp = reinterpret_cast<const float*>(a.q) + out_row + sub * EPL;
+#pragma unroll
+    for (int h = 0; h < GT; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qf[h][e] = qp[h * D + e];
+  }
+  (void)qr;
+  (void)qf;
+  // The query and block-table loads must be complete before the pipelined
+  // loop; otherwise the wait-count tracking cannot tell them apart from the
+  // prefetched K/V loads and waits for everything at the top of each step.
+  __builtin_amdgcn_s_waitcnt(0);
+
+  float m[GT], l[GT], acc[GT][EPL];
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+
+  if (!any_bad) {
+    const int steps_per_block = bs / kStepRows;
+    const int nsteps = nb * steps_per_block;
+    const int64_t blk_bytes = a.block_stride * kElt;
+    const int row_bytes = a.num_kv_heads * kRowBytes;      // one token of all KV heads
+    // per-lane byte offset inside a 16-row step (fits 32 bits: a block is
+    // at most 32 rows x 64 heads x 512 bytes)
+    const uint32_t lane_off = (uint32_t)((grp * a.num_kv_heads + kvh) * kRowBytes + sub * 16);
+    const int pos_base = blk_begin << a.bs_log2;
+
+    auto issue = [&](int st, uint4 (&kd)[U], uint4 (&vd)[U]) {
+      const int blk = st / steps_per_block;
+      const int r0 = (st - blk * steps_per_block) * kStepRows;
+      const int phys = __builtin_amdgcn_readlane(tab, blk);
+      const int64_t off = (int64_t)phys * blk_bytes + (int64_t)r0 * row_bytes;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        // wave-uniform base (scalar registers) + 32-bit lane offset
+        const char* kp = a.kbase + off + (int64_t)u * RPW * row_bytes;
+        const char* vp = a.vbase + off + (int64_t)u * RPW * row_bytes;
+        kd[u] = *reinterpret_cast<const uint4*>(kp + lane_off);
+        vd[u] = *reinterpret_cast<const uint4*>(vp + lane_off);
+      }
+    };
+
+    auto compute = [&](auto full_tag, int st, const uint4 (&kd)[U], const uint4 (&vd)[U]) {
+      constexpr bool full = decltype(full_tag)::value;
+      const int p0 = pos_base + st * kStepRows;                 // first row of the step
+      float z[U][GT];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t kwa[4] = {kd[u].x, kd[u].y, kd[u].z, kd[u].w};
+        uint32_t kp[kBf16Dot ? EPL / 2 : 1];
+        float kf[kBf16Dot ? 1 : EPL];
+        (void)kp;
+        (void)kf;
+        if constexpr (KV == PKV_BF16) {
+#pragma unroll
+          for (int i = 0; i < EPL / 2; ++i) {
+            if constexpr (kBf16Dot) kp[i] = kwa[i];
+            else { kf[2 * i] = bf16_lo(kwa[i]); kf[2 * i + 1] = bf16_hi(kwa[i]); }
+          }
+        } else if constexpr (KV == PKV_F32) {
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) kf[i] = as_float(kwa[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < EPL / 4; ++i) {
+            if constexpr (kBf16Dot) {
+              kp[2 * i] = e4m3x2_to_bf16x2<false>(kwa[i]);
+              kp[2 * i + 1] = e4m3x2_to_bf16x2<true>(kwa[i]);
+            } else {
+              const f32x2 k01 = e4m3x2_to_f32<false>(kwa[i]);
+              const f32x2 k23 = e4m3x2_to_f32<true>(kwa[i]);
+              kf[4 * i] = k01.x; kf[4 * i + 1] = k01.y; kf[4 * i + 2] = k23.x; kf[4 * i + 3] = k23.y;
+            }
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+          float sc = 0.f;
+          if constexpr (kBf16Dot) {
+#pragma unroll
+            for (int i = 0; i < EPL / 2; ++i) sc = dot2_bf16(qr[h][i], kp[i], sc);
+          } else {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) sc = fmaf(qf[h][e], kf[e], sc);
+          }
+          z[u][h] = sc;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int h = 0; h < GT; ++h) z[u][h] = group_sum<LPR>(z[u][h]) * a.scale_log2;
+
+      bool live[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int pos = p0 + u * RPW + grp;
+        live[u] = full || (pos >= span.lo && pos <= span.hi);
+        if (!live[u]) {
+#pragma unroll
+          for (int h = 0; h < GT; ++h) z[u][h] = -INFINITY;
+        }
+      }
+
+      // V rows in compute form; masked rows are zeroed so that stale or
+      // poisoned bytes never reach the accumulators.
+      float vf[U][EPL];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t vwa[4] = {vd[u].x, vd[u].y, vd[u].z, vd[u].w};
+        if constexpr (KV == PKV_BF16) {
+#pragma unroll
+          for (int i = 0; i < EPL / 2; ++i) { vf[u][2 * i] = bf16_lo(vwa[i]); vf[u][2 * i + 1] = bf16_hi(vwa[i]); }
+        } else if constexpr (KV == PKV_F32) {
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) vf[u][i] = as_float(vwa[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < EPL / 4; ++i) {
+            const f32x2 v01 = e4m3x2_to_f32<false>(vwa[i]);
+            const f32x2 v23 = e4m3x2_to_f32<true>(vwa[i]);
+            vf[u][4 * i] = v01.x; vf[u][4 * i + 1] = v01.y; vf[u][4 * i + 2] = v23.x; vf[u][4 * i + 3] = v23.y;
+          }
+        }
+        if (!full) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) vf[u][e] = live[u] ? vf[u][e] : 0.f;
+        }
+      }
+
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        float zmax = z[0][h];
+#pragma unroll
+        for (int u = 1; u < U; ++u) zmax = fmaxf(zmax, z[u][h]);
+        if (zmax > m[h] + kLazyRescale) {
+          const float alpha = __builtin_amdgcn_exp2f(m[h] - zmax);
+          l[h] *= alpha;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+          m[h] = zmax;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          // a lane whose rows are all masked keeps m = -inf; its p must be 0
+          const float p = (full || live[u]) ? __builtin_amdgcn_exp2f(z[u][h] - m[h]) : 0.f;
+          l[h] += p;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vf[u][e], acc[h][e]);
+        }
+      }
+    };
+
+    // Steps whose 16 rows are all visible skip every mask.
+    auto step_is_full = [&](int st) {
+      const int p0 = pos_base + st * kStepRows;
+      return p0 >= span.lo && p0 + kStepRows - 1 <= span.hi;
+    };
+    auto run = [&](int st, const uint4 (&kd)[U], const uint4 (&vd)[U]) {
+      if (step_is_full(st)) compute(std::true_type{}, st, kd, vd);
+      else compute(std::false_type{}, st, kd, vd);
+    };
+
+    // Loads are issued unconditionally, one step ahead; past the end the last
+    // step is fetched again (an L2 hit).  A branch around a prefetch would
+    // make the wait-count tracking merge two paths and wait for everything.
+    uint4 ka[U], va[U], kb2[U], vb2[U];
+    const int last = nsteps - 1;
+    issue(0, ka, va);
+    for (int st = 0; st < nsteps; st += 2) {
+      issue(min(st + 1, last), kb2, vb2);
+      run(st, ka, va);
+      issue(min(st + 2, last), ka, va);
+      if (st + 1 < nsteps) run(st + 1, kb2, vb2);
+    }
+
+#pragma unroll
+    for (int step = LPR; step < kWave; step <<= 1) {
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        const float mo = shfl_xor_t(m[h], step);
+        const float lo_ = shfl_xor_t(l[h], step);
+        const float mn = fmaxf(m[h], mo);
+        const float fa = m[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[h] - mn);
+        const float fb = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
+        l[h] = l[h] * fa + lo_ * fb;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const float ao = shfl_xor_t(acc[h][e], step);
+          acc[h][e] = acc[h][e] * fa + ao * fb;
+        }
+        m[h] = mn;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      m[h] = 0.f;
+      l[h] = __builtin_nanf("");
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = __builtin_nanf("");
+    }
+  }
+
+  if (grp != 0) return;
+  if (nsplit == 1) {
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      const float inv = a.v_scale / l[h];
+      float o[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = acc[h][e] * inv;
+      store_out<QT, EPL>(a.out, out_row + h * D + sub * EPL, o);
+    }
+    return;
+  }
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    const int64_t pr = ((int64_t)b * a.num_q_heads + h0 + h) * a.max_splits + s;
+    float* dst = a.ws_acc + pr * D + sub * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dst[e] = acc[h][e];
+    if (sub == 0) {
+      a.ws_m[pr] = m[h];
+      a.ws_l[pr] = l[h];
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Balanced split phase on the matrix cores.
+//
+// Work units are (row, KV-head group, visible block), ordered row-major.  The
+// grid is a fixed number of single-wave workers sized to the resident wave
+// slots; worker w takes the contiguous units [w P, (w + 1) P) with P =
+// max(ceil(U / workers), min_units), so every worker reads the same number of
+// blocks and no straggler round follows the first.  Each stretch of a
+// worker's range that belongs to one (row, head group) is a "piece": it is
+// folded with an online softmax and written either as the final output (when
+// the piece covers the whole row) or as a partial (m, l, acc) in slot
+// `piece` of that row, with the piece count stored for the combine kernel.
+//
+// Scores of a 16-token step are one chain of 16x16x32 bf16 MFMAs,
+// S[q head][token] = Q . K^T: Q is the A operand (rows = query heads of the
+// item, unused rows zero) and K rows load straight into the B operand (lane l:
+// token l % 16, 8 consecutive elements from 32c + 8 (l / 16)).  The running
+// max of every head is wave-uniform (a 16-lane max of S read into a scalar
+// register), so one scalar test per head and step decides the lazy rescale
+// and pieces merge without rescaling inside the wave.  P.V stays on the
+// vector ALUs in fp32: lane L = VLPR g + sub holds V[token u VRPW + g]
+// [sub VEPL ..] and fetches that token's probability with a lane permute.
+// Requirements: bf16 or fp8 cache, bf16 query, head_dim % 32 == 0, row of at
+// least 64 bytes, block size a multiple of 16, at most 16 query heads per item.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int D, int GT, int KV>
+struct MfmaShape {
+  static constexpr int kElt = KV == PKV_BF16 ? 2 : 1;
+  static constexpr int NC = D / 32;                  // MFMA k-chunks
+  static constexpr int VLPR = D * kElt / 16;         // V: lanes per row
+  static constexpr int VRPW = kWave / VLPR;          // V: rows per load
+  static constexpr int VU = 16 / VRPW;               // V: loads per 16-token step
+  static constexpr int VEPL = 16 / kElt;             // V: elements per lane
+  static constexpr int KB = 8 * kElt;                // K: bytes per lane per chunk
+  static constexpr int RG = (GT + 3) / 4;            // MFMA row groups in use
+  static_assert(VRPW <= 16 && VU * VRPW == 16, "V layout");
+  static_assert(GT <= 16, "at most 16 query heads per item");
+};
+
+// Fold visible blocks [blk0, blk0 + nblk) of one (row, KV head) into the
+// running state.  Returns false if a needed block-table entry is invalid
+// (nothing is loaded from the cache then).
+template <int D, int GT, int KV, int DEPTH>
+__device__ __forceinline__ bool mfma_fold(const DecodeArgs& a, const RowInfo& span, int kvh,
+                                          const bf16x8_t (&qa)[MfmaShape<D, GT, KV>::NC],
+                                          int blk0, int nblk,
+                                          float (&acc)[GT][MfmaShape<D, GT, KV>::VEPL],
+                                          float (&m)[GT], f32x4_t& lsum) {
+  using S = MfmaShape<D, GT, KV>;
+  constexpr int NC = S::NC, VLPR = S::VLPR, VRPW = S::VRPW, VU = S::VU, VEPL = S::VEPL;
+  constexpr int KB = S::KB, RG = S::RG, kElt = S::kElt;
+  const int lane = threadIdx.x;
+  const int vg = lane / VLPR;
+  const int vsub = lane % VLPR;
+  const int bs = 1 << a.bs_log2;
+  const int steps_per_block = bs / 16;
+  const int64_t blk_bytes = a.block_stride * kElt;
+  const int row_bytes = a.num_kv_heads * D * kElt;           // one token, all KV heads
+  const uint32_t k_lane = (uint32_t)((lane % 16) * row_bytes + kvh * D * kElt + (lane / 16) * KB);
+  const uint32_t v_lane = (uint32_t)(vg * row_bytes + kvh * D * kElt + vsub * 16);
+
+  struct Buf {
+    uint32_t k[NC][KB / 4];
+    uint4 v[VU];
+  };
+
+  for (int c0 = 0; c0 < nblk; c0 += 64) {                    // table slices of 64 entries
+    const int nb = min(64, nblk - c0);
+    int tab = -1;
+    if (lane < nb) tab = a.bt[(int64_t)span.req * a.bt_stride + blk0 + c0 + lane];
+    if (__ballot((lane < nb) && (tab < 0 || tab >= a.num_blocks)) != 0) return false;
+    const int pos_base = (blk0 + c0) << a.bs_log2;
+    const int nsteps = nb * steps_per_block;
+
+    auto issue = [&](int st, Buf& bf) {
+      const int blk = st / steps_per_block;
+      const int r0 = (st - blk * steps_per_block) * 16;
+      const int phys = __builtin_amdgcn_readlane(tab, blk);
+      const int64_t off = (int64_t)phys * blk_bytes + (int64_t)r0 * row_bytes;
+      const char* kp = a.kbase + off;
+      const char* vp = a.vbase + off;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        if constexpr (KB == 16) {
+          const uint4 t = *reinterpret_cast<const uint4*>(kp + k_lane + c * 32 * kElt);
+          bf.k[c][0] = t.x; bf.k[c][1] = t.y; bf.k[c][2] = t.z; bf.k[c][3] = t.w;
+        } else {
+          const uint2 t = *reinterpret_cast<const uint2*>(kp + k_lane + c * 32 * kElt);
+          bf.k[c][0] = t.x; bf.k[c][1] = t.y;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < VU; ++u)
+        bf.v[u] = *reinterpret_cast<const uint4*>(vp + v_lane + (int64_t)u * VRPW * row_bytes);
+    };
+
+    auto compute = [&](auto full_tag, int st, const Buf& bf) {
+      constexpr bool full = decltype(full_tag)::value;
+      const int p0 = pos_base + st * 16;
+      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        uint4 kw;
+        if constexpr (KB == 16) {
+          kw = make_uint4(bf.k[c][0], bf.k[c][1], bf.k[c][2], bf.k[c][3]);
+        } else {
+          kw = make_uint4(e4m3x2_to_bf16x2<false>(bf.k[c][0]), e4m3x2_to_bf16x2<true>(bf.k[c][0]),
+                          e4m3x2_to_bf16x2<false>(bf.k[c][1]), e4m3x2_to_bf16x2<true>(bf.k[c][1]));
+        }
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[c], __builtin_bit_cast(bf16x8_t, kw), sc, 0, 0, 0);
+      }
+      float z[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[i] = sc[i] * a.scale_log2;
+      if constexpr (!full) {
+        const int pos = p0 + (lane % 16);
+        if (pos < span.lo || pos > span.hi) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) z[i] = -INFINITY;
+        }
+      }
+      // per-head max over the step's 16 tokens (a row group), made wave-uniform
+      float mx[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = z[i];
+        v = fmaxf(v, dpp<kDppQuadXor1>(v));
+        v = fmaxf(v, dpp<kDppQuadXor2>(v));
+        v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
+        v = fmaxf(v, dpp<kDppRowMirror>(v));
+        mx[i] = v;
+      }
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        const float mb = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+            __builtin_bit_cast(int, mx[h % 4]), 16 * (h / 4)));
+        if (mb > m[h] + kLazyRescale) {
+          const float alpha = __builtin_amdgcn_exp2f(m[h] - mb);   // 0 when m = -inf
+#pragma unroll
+          for (int e = 0; e < VEPL; ++e) acc[h][e] *= alpha;
+          if (lane / 16 == h / 4) lsum[h % 4] *= alpha;
+          m[h] = mb;
+        }
+      }
+      float pr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float mv = m[i < GT ? i : 0];
+#pragma unroll
+        for (int r = 1; r < RG; ++r)
+          if (lane / 16 == r && 4 * r + i < GT) mv = m[4 * r + i];
+        float pv = __builtin_amdgcn_exp2f(z[i] - mv);
+        if constexpr (!full) pv = z[i] == -INFINITY ? 0.f : pv;
+        pr[i] = pv;
+        lsum[i] += pv;
+      }
+#pragma unroll
+      for (int u = 0; u < VU; ++u) {
+        const int tok = u * VRPW + vg;                // token inside the step
+        const uint32_t vwa[4] = {bf.v[u].x, bf.v[u].y, bf.v[u].z, bf.v[u].w};
+        float vf[VEPL];
+        if constexpr (KV == PKV_BF16) {
+#pragma unroll
+          for (int i = 0; i < VEPL / 2; ++i) { vf[2 * i] = bf16_lo(vwa[i]); vf[2 * i + 1] = bf16_hi(vwa[i]); }
+        } else {
+#pragma unroll
+          for (int i = 0; i < VEPL / 4; ++i) {
+            const f32x2 v01 = e4m3x2_to_f32<false>(vwa[i]);
+            const f32x2 v23 = e4m3x2_to_f32<true>(vwa[i]);
+            vf[4 * i] = v01.x; vf[4 * i + 1] = v01.y; vf[4 * i + 2] = v23.x; vf[4 * i + 3] = v23.y;
+          }
+        }
+        if constexpr (!full) {
+          const int pos = p0 + tok;
+          const bool live = pos >= span.lo && pos <= span.hi;
+#pragma unroll
+          for (int e = 0; e < VEPL; ++e) vf[e] = live ? vf[e] : 0.f;
+        }
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+          const int src = (tok + 16 * (h / 4)) * 4;
+          const float ph = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+              src, __builtin_bit_cast(int, pr[h % 4])));
+#pragma unroll
+          for (int e = 0; e < VEPL; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
+        }
+      }
+    };
+
+    auto run = [&](int st, const Buf& bf) {
+      const int p0 = pos_base + st * 16;
+      if (p0 >= span.lo && p0 + 15 <= span.hi) compute(std::true_type{}, st, bf);
+      else compute(std::false_type{}, st, bf);
+    };
+
+    // Loads run DEPTH steps ahead of the step being folded, unconditionally:
+    // past the end the last step is fetched again (an L2 hit).  A branch
+    // around a prefetch would make the wait-count tracking merge two paths
+    // and wait for every load at the top of each step.
+    const int last = nsteps - 1;
+    if constexpr (DEPTH == 2) {
+      Buf b0, b1, b2;
+      issue(0, b0);
+      issue(min(1, last), b1);
+      for (int st = 0; st < nsteps; st += 3) {
+        issue(min(st + 2, last), b2);
+        run(st, b0);
+        issue(min(st + 3, last), b0);
+        if (st + 1 < nsteps) run(st + 1, b1);
+        issue(min(st + 4, last), b1);
+        if (st + 2 < nsteps) run(st + 2, b2);
+      }
+    } else if constexpr (DEPTH == 1) {
+      Buf b0, b1;
+      issue(0, b0);
+      for (int st = 0; st < nsteps; st += 2) {
+        issue(min(st + 1, last), b1);
+        run(st, b0);
+        issue(min(st + 2, last), b0);
+        if (st + 1 < nsteps) run(st + 1, b1);
+      }
+    } else {
+      for (int st = 0; st < nsteps; ++st) {
+        Buf b0;
+        issue(st, b0);
+        run(st, b0);
+      }
+    }
+  }
+  return true;
+}
+
+template <int D, int GT, int KV, int DEPTH>
+__global__ __launch_bounds__(64) void decode_stream_mfma_kernel(DecodeArgs a) {
+  using S = MfmaShape<D, GT, KV>;
+  constexpr int NC = S::NC, VLPR = S::VLPR, VEPL = S::VEPL;
+  extern __shared__ int cum[];              // cum[r]: visible blocks of rows < r
+  const int lane = threadIdx.x;
+  const int kvgroups = a.num_kv_heads * a.sub_groups;
+
+  // ---- visible blocks per row, prefix sums in LDS
+  int carry = 0;
+  for (int r0 = 0; r0 < a.num_rows; r0 += kWave) {
+    const int r = r0 + lane;
+    int nv = 0;
+    if (r < a.num_rows) {
+      const RowInfo ri = row_info(a, r);
+      nv = (!ri.skip && ri.valid) ? ri.nvis : 0;
+    }
+    int incl = nv;                            // inclusive wave scan
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    if (r < a.num_rows) cum[r] = carry + incl - nv;
+    carry += __shfl(incl, kWave - 1);
+  }
+  if (lane == 0) cum[a.num_rows] = carry;
+  __syncthreads();
+
+  const long long U = (long long)carry * kvgroups;
+  const int W = gridDim.x;
+  long long P = (U + W - 1) / W;
+  if (P < a.split_blocks) P = a.split_blocks;        // minimum units per worker
+  const long long u_lo = (long long)blockIdx.x * P;
+  const long long u_hi = min(U, u_lo + P);
+
+  // ---- rows that cannot be computed: NaN output, written by one worker each
+  for (int r = blockIdx.x; r < a.num_rows; r += W) {
+    const RowInfo ri = row_info(a, r);
+    if (ri.skip || ri.valid) continue;
+    const int64_t base = (int64_t)ri.tok * a.num_q_heads * D;
+    for (int e = lane; e < a.num_q_heads * D; e += kWave)
+      reinterpret_cast<uint16_t*>(a.out)[base + e] = 0x7FC0;
+    for (int g = lane; g < kvgroups; g += kWave) a.ws_np[(int64_t)r * kvgroups + g] = 0;
+  }
+
+  long long u = u_lo;
+  while (u < u_hi) {
+    // row b: largest b with cum[b] * kvgroups <= u
+    int lo = 0, hi = a.num_rows;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((long long)cum[mid] * kvgroups <= u) lo = mid; else hi = mid;
+    }
+    const int b = lo;
+    const long long row_base = (long long)cum[b] * kvgroups;
+    const int nv = cum[b + 1] - cum[b];
+    const int kvg = (int)((u - row_base) / nv);
+    const long long seg_base = row_base + (long long)kvg * nv;   // first unit of (b, kvg)
+    const int j = (int)(u - seg_base);
+    const long long seg_end = min(u_hi, seg_base + nv);
+    const int nblk = (int)(seg_end - u);
+    const int piece = (int)(u / P - seg_base / P);
+    const int npieces = (int)((seg_base + nv - 1) / P - seg_base / P + 1);
+
+    const RowInfo span = row_info(a, b);
+    const int kvh = kvg / a.sub_groups;
+    const int h0 = kvh * a.group + (kvg % a.sub_groups) * GT;
+    const int64_t out_row = ((int64_t)span.tok * a.num_q_heads + h0) * D;
+
+    bf16x8_t qa[NC];
+    {
+      const int row = lane % 16;
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + out_row + (int64_t)row * D + 8 * (lane / 16);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        uint4 t = make_uint4(0, 0, 0, 0);
+        if (row < GT) t = *reinterpret_cast<const uint4*>(qp + 32 * c);
+        qa[c] = __builtin_bit_cast(bf16x8_t, t);
+      }
+    }
+    float acc[GT][VEPL];
+    float m[GT];
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      m[h] = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < VEPL; ++e) acc[h][e] = 0.f;
+    }
+    f32x4_t lsum = {0.f, 0.f, 0.f, 0.f};
+    // the query loads must be complete before the pipelined loop, or the
+    // wait-count tracking cannot tell them from the prefetched K/V loads
+    __builtin_amdgcn_s_waitcnt(0);
+
+    const bool ok = mfma_fold<D, GT, KV, DEPTH>(a, span, kvh, qa, span.first_blk + j, nblk,
+                                                   acc, m, lsum);
+    if (!ok) {
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        m[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEPL; ++e) acc[h][e] = __builtin_nanf("");
+      }
+      lsum[0] = lsum[1] = lsum[2] = lsum[3] = __builtin_nanf("");
+    }
+    // the V layout's token groups hold partial sums under the same maxima
+#pragma unroll
+    for (int step = VLPR; step < kWave; step <<= 1)
+#pragma unroll
+      for (int h = 0; h < GT; ++h)
+#pragma unroll
+        for (int e = 0; e < VEPL; ++e) acc[h][e] += shfl_xor_t(acc[h][e], step);
+    float lt[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lt[i] = group_sum<16>(lsum[i]);
+    float lh[GT];
+#pragma unroll
+    for (int h = 0; h < GT; ++h)
+      lh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lt[h % 4]), 16 * (h / 4)));
+
+    const int vg = lane / VLPR, vsub = lane % VLPR;
+    if (vg == 0) {
+      if (npieces == 1) {
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+          const float inv = a.v_scale / lh[h];
+          float o[VEPL];
+#pragma unroll
+          for (int e = 0; e < VEPL; ++e) o[e] = acc[h][e] * inv;
+          store_out<PKV_BF16, VEPL>(a.out, out_row + h * D + vsub * VEPL, o);
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+          const int64_t pr = ((int64_t)b * a.num_q_heads + h0 + h) * a.max_splits + piece;
+          float* dst = a.ws_acc + pr * D + vsub * VEPL;
+#pragma unroll
+          for (int e = 0; e < VEPL; ++e) dst[e] = acc[h][e];
+          if (vsub == 0) {
+            a.ws_m[pr] = m[h];
+            a.ws_l[pr] = lh[h];
+          }
+        }
+      }
+    }
+    if (piece == 0 && lane == 0) a.ws_np[(int64_t)b * kvgroups + kvg] = npieces;
+    u = seg_end;
+  }
+}
+
+// --------------------------------------------------------------------------
 // Combine phase: one wave per (row, query head) with more than one split.
 template <int D, int OT>
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
@@ -425,8 +1146,15 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   // count is clamped to the slots that exist.
   const RowInfo span = row_info(a, b);
   if (span.skip || !span.valid) return;
-  const int tok = b;
-  const int nsplit = min(ceil_div(span.nvis, a.split_blocks), a.max_splits);
+  const int tok = span.tok;
+  int nsplit;
+  if (a.stream) {   // rows the split phase rejected have a piece count of 0
+    const int groups = a.num_q_heads / a.heads_per_item;
+    nsplit = a.ws_np[(int64_t)b * groups + h / a.heads_per_item];
+  } else {
+    nsplit = ceil_div(span.nvis, a.split_blocks);
+  }
+  nsplit = min(nsplit, a.max_splits);
   if (nsplit <= 1) return;
 
   const int64_t pr0 = ((int64_t)b * a.num_q_heads + h) * a.max_splits;
@@ -479,56 +1207,117 @@ static int max_visible_blocks(int max_seq_len, int bs, int window, int extra) {
   return full < win ? full : win;
 }
 
-static int heads_per_item(int group) {
+// Query heads one vector-ALU work item handles.
+static int heads_per_item_valu(int group) {
   if (group >= 8) return (group % 8 == 0) ? 8 : 0;
   return (group == 1 || group == 2 || group == 4) ? group : 0;
 }
+
+// Query heads one matrix-core work item handles (MFMA rows).
+static int heads_per_item_mfma(int group) {
+  if (group >= 16) return (group % 16 == 0) ? 16 : 0;
+  return (group == 1 || group == 2 || group == 4 || group == 8) ? group : 0;
+}
+
+static bool mfma_eligible(int kv_dtype, int d, int bs) {
+  const int elt = dtype_size(kv_dtype);
+  return (kv_dtype == PKV_BF16 || kv_dtype == PKV_FP8_E4M3) && d % 32 == 0 && d * elt >= 64 &&
+         bs % 16 == 0;
+}
+
+constexpr int kMaxStreamRows = 8192;   // prefix sums of the balanced scheme live in LDS
+constexpr int kStreamMinUnits = 8;     // blocks per worker at least (bounds the pieces)
+constexpr int kStreamWavesPerCU = 8;
 
 static size_t partial_bytes(int rows, int hq, int splits, int d) {
   return (size_t)rows * hq * splits * ((size_t)d + 2) * sizeof(float);
 }
 
-static int make_plan(int rows, int hq, int hkv, int d, int bs, int max_seq_len, int window,
-                     int extra, pkv_decode_plan* plan) {
+static size_t plan_bytes(const pkv_decode_plan& p, int rows, int hq, int d) {
+  if (p.scheme == 1)
+    return partial_bytes(rows, hq, p.max_splits, d) +
+           (size_t)rows * (hq / p.heads_per_item) * sizeof(int32_t);
+  return p.max_splits > 1 ? partial_bytes(rows, hq, p.max_splits, d) : 0;
+}
+
+static int make_plan(int rows, int hq, int hkv, int d, int bs, int kv_dtype, int max_seq_len,
+                     int window, int extra, bool allow_stream, pkv_decode_plan* plan) {
   if (!plan) return PKV_ERR_NULL;
   if (rows < 0 || hq <= 0 || hkv <= 0 || max_seq_len < 0 || window < 0) return PKV_ERR_SHAPE;
   if (hq % hkv) return PKV_ERR_SHAPE;
+  if (dtype_size(kv_dtype) == 0) return PKV_ERR_DTYPE;
   if (!head_dim_supported(d) || !block_size_supported(bs)) return PKV_ERR_UNSUPPORTED;
-  const int gt = heads_per_item(hq / hkv);
-  if (gt == 0) return PKV_ERR_UNSUPPORTED;
+  const int group = hq / hkv;
   const int nvis = max_visible_blocks(max_seq_len, bs, window, extra);
-  const int kvgroups = hkv * (hq / hkv / gt);
-  // Aim for about 16 single-wave work items per compute unit if every row
-  // were as long as the longest; splits are powers of two in [1, 64] blocks.
   const long long cus = device_cu_count();
-  const long long items1 = (long long)(rows > 0 ? rows : 1) * kvgroups * nvis;
-  const long long target = cus * 16;
-  int split = 1;
-  while (split < 64 && items1 / split > target) split <<= 1;
-  plan->split_blocks = split;
-  plan->max_splits = ceil_div(nvis, split);
-  plan->heads_per_item = gt;
-  plan->reserved = 0;
-  plan->workspace_bytes = plan->max_splits > 1 ? partial_bytes(rows, hq, plan->max_splits, d) : 0;
+  const int gm = heads_per_item_mfma(group);
+  plan->kernel_variant = 0;
+  if (allow_stream && mfma_eligible(kv_dtype, d, bs) && gm > 0 && rows <= kMaxStreamRows) {
+    // balanced partition over resident wave slots
+    const long long units = (long long)(rows > 0 ? rows : 1) * (hq / gm) * nvis;
+    long long workers = cus * kStreamWavesPerCU;
+    const long long need = (units + kStreamMinUnits - 1) / kStreamMinUnits;
+    if (workers > need) workers = need;
+    if (workers < 1) workers = 1;
+    plan->scheme = 1;
+    plan->num_workers = (int32_t)workers;
+    plan->split_blocks = kStreamMinUnits;
+    plan->max_splits = ceil_div(nvis, kStreamMinUnits) + 1;
+    plan->heads_per_item = gm;
+  } else {
+    const int gt = heads_per_item_valu(group);
+    if (gt == 0) return PKV_ERR_UNSUPPORTED;
+    // fixed splits: about 16 single-wave work items per compute unit if
+    // every row were as long as the longest; powers of two in [1, 64]
+    const long long items1 = (long long)(rows > 0 ? rows : 1) * (hq / gt) * nvis;
+    const long long target = cus * 16;
+    int split = 1;
+    while (split < 64 && items1 / split > target) split <<= 1;
+    plan->scheme = 0;
+    plan->num_workers = 0;
+    plan->split_blocks = split;
+    plan->max_splits = ceil_div(nvis, split);
+    plan->heads_per_item = gt;
+  }
+  plan->workspace_bytes = plan_bytes(*plan, rows, hq, d);
   return PKV_OK;
 }
 
-static int check_plan(const pkv_decode_plan* plan, int hq, int hkv, int bs, int max_seq_len,
-                      int window, int extra) {
+static int check_plan(const pkv_decode_plan* plan, int rows, int hq, int hkv, int d, int bs,
+                      int kv_dtype, int max_seq_len, int window, int extra) {
   if (!plan) return PKV_ERR_NULL;
+  if (plan->kernel_variant < 0 || plan->kernel_variant > 4) return PKV_ERR_SHAPE;
+  const int group = hq / hkv;
+  const int nvis = max_visible_blocks(max_seq_len, bs, window, extra);
+  if (plan->scheme == 1) {
+    if (!mfma_eligible(kv_dtype, d, bs) || rows > kMaxStreamRows) return PKV_ERR_SHAPE;
+    if (plan->heads_per_item != heads_per_item_mfma(group) || plan->heads_per_item == 0)
+      return PKV_ERR_SHAPE;
+    if (plan->split_blocks < 1 || plan->num_workers < 1) return PKV_ERR_SHAPE;
+    if (plan->max_splits < ceil_div(nvis, plan->split_blocks) + 1) return PKV_ERR_SHAPE;
+    return PKV_OK;
+  }
+  if (plan->scheme != 0) return PKV_ERR_SHAPE;
   if (plan->split_blocks < 1 || plan->split_blocks > 64) return PKV_ERR_SHAPE;
-  const int gt = heads_per_item(hq / hkv);
+  const int gt = heads_per_item_valu(group);
   if (gt == 0) return PKV_ERR_UNSUPPORTED;
   if (plan->heads_per_item != gt) return PKV_ERR_SHAPE;
-  const int nvis = max_visible_blocks(max_seq_len, bs, window, extra);
   if (plan->max_splits < ceil_div(nvis, plan->split_blocks)) return PKV_ERR_SHAPE;
   return PKV_OK;
 }
 
+// ---- fixed-split launches
 template <int D, int GT, int KV, int QT>
 static void launch_split(const DecodeArgs& a, hipStream_t s) {
   const long long kvgroups = (long long)a.num_kv_heads * a.sub_groups;
   const dim3 grid((unsigned)((long long)a.num_rows * kvgroups * a.max_splits));
+  constexpr int kRowBytes = D * (KV == PKV_F32 ? 4 : (KV == PKV_BF16 ? 2 : 1));
+  if constexpr (kRowBytes >= 64) {
+    if ((1 << a.bs_log2) >= 16) {
+      decode_split_uni_kernel<D, GT, KV, QT><<<grid, 64, 0, s>>>(a);
+      return;
+    }
+  }
   decode_split_kernel<D, GT, KV, QT><<<grid, 64, 0, s>>>(a);
 }
 
@@ -562,6 +1351,50 @@ static int dispatch_split(const DecodeArgs& a, int gt, int kv, hipStream_t s) {
   return PKV_ERR_UNSUPPORTED;
 }
 
+// ---- balanced (matrix-core) launches
+template <int D, int GT, int KV>
+static void launch_stream(const DecodeArgs& a, int workers, hipStream_t s) {
+  const size_t lds = ((size_t)a.num_rows + 1) * sizeof(int);
+  // prefetch depth: two steps ahead while the registers allow two waves per
+  // SIMD (up to four query heads per item), one step ahead beyond that
+  constexpr int kDepth = GT >= 8 ? 1 : 2;
+  if constexpr (D == 128) {
+    if (a.kernel_variant >= 2 && a.kernel_variant <= 4) {
+      const int depth = a.kernel_variant - 2;
+      if (depth == 0) decode_stream_mfma_kernel<D, GT, KV, 0><<<workers, 64, lds, s>>>(a);
+      else if (depth == 1) decode_stream_mfma_kernel<D, GT, KV, 1><<<workers, 64, lds, s>>>(a);
+      else decode_stream_mfma_kernel<D, GT, KV, 2><<<workers, 64, lds, s>>>(a);
+      return;
+    }
+  }
+  decode_stream_mfma_kernel<D, GT, KV, kDepth><<<workers, 64, lds, s>>>(a);
+}
+
+template <int D, int KV>
+static int stream_gt(const DecodeArgs& a, int workers, hipStream_t s) {
+  if constexpr (D * (KV == PKV_BF16 ? 2 : 1) >= 64) {
+    switch (a.heads_per_item) {
+      case 1: launch_stream<D, 1, KV>(a, workers, s); return PKV_OK;
+      case 2: launch_stream<D, 2, KV>(a, workers, s); return PKV_OK;
+      case 4: launch_stream<D, 4, KV>(a, workers, s); return PKV_OK;
+      case 8: launch_stream<D, 8, KV>(a, workers, s); return PKV_OK;
+      case 16: launch_stream<D, 16, KV>(a, workers, s); return PKV_OK;
+    }
+  }
+  return PKV_ERR_UNSUPPORTED;
+}
+
+static int dispatch_stream(const DecodeArgs& a, int kv, int workers, hipStream_t s) {
+  const bool bf = kv == PKV_BF16;
+  switch (a.head_dim) {
+    case 32: return bf ? stream_gt<32, PKV_BF16>(a, workers, s) : PKV_ERR_UNSUPPORTED;
+    case 64: return bf ? stream_gt<64, PKV_BF16>(a, workers, s) : stream_gt<64, PKV_FP8_E4M3>(a, workers, s);
+    case 128: return bf ? stream_gt<128, PKV_BF16>(a, workers, s) : stream_gt<128, PKV_FP8_E4M3>(a, workers, s);
+    case 256: return bf ? stream_gt<256, PKV_BF16>(a, workers, s) : stream_gt<256, PKV_FP8_E4M3>(a, workers, s);
+  }
+  return PKV_ERR_UNSUPPORTED;
+}
+
 template <int D>
 static void launch_combine_d(const DecodeArgs& a, int ot, hipStream_t s) {
   const dim3 grid((unsigned)((long long)a.num_rows * a.num_q_heads));
@@ -581,45 +1414,61 @@ static int dispatch_combine(const DecodeArgs& a, int ot, hipStream_t s) {
   return PKV_ERR_UNSUPPORTED;
 }
 
+// Carve the partial arrays out of a workspace region.
+static void bind_workspace(DecodeArgs& a, void* ws, int rows, int hq, int d, int splits, int gt) {
+  float* wsf = reinterpret_cast<float*>(ws);
+  const size_t nacc = (size_t)rows * hq * splits;
+  a.ws_acc = wsf;
+  a.ws_m = wsf ? wsf + nacc * d : nullptr;
+  a.ws_l = wsf ? a.ws_m + nacc : nullptr;
+  a.ws_np = wsf ? reinterpret_cast<int32_t*>(a.ws_l + nacc) : nullptr;
+  (void)gt;
+}
+
 // Validates everything host-visible and fills DecodeArgs (no launch).
-// qsl == nullptr: decode rows; otherwise chunked rows (rows = tokens).
+// row_mode 0: decode rows; 1: chunked token rows; 2: chunked request rows.
 static int prepare(DecodeArgs& a, void* out, const void* q, int q_dtype, int rows, int hq,
                    const pkv_cache* cache, const int32_t* bt, int bt_stride,
                    const int32_t* seq_lens, int max_seq_len, float scale, int window,
-                   const int32_t* qsl, int num_reqs, int max_query_len, int causal,
+                   int row_mode, const int32_t* qsl, int num_reqs, int max_query_len, int causal,
                    const pkv_decode_plan* plan, void* ws, size_t ws_bytes) {
   int st = check_cache(cache);
   if (st != PKV_OK) return st;
   if (rows < 0 || hq <= 0 || bt_stride < 0 || max_seq_len < 0 || window < 0) return PKV_ERR_SHAPE;
-  if (qsl && (num_reqs < 0 || max_query_len < 0)) return PKV_ERR_SHAPE;
+  if (row_mode != 0 && (num_reqs < 0 || max_query_len < 0 || !qsl)) return PKV_ERR_SHAPE;
   if (hq % cache->num_kv_heads) return PKV_ERR_SHAPE;
   const int want_q = cache->dtype == PKV_F32 ? PKV_F32 : PKV_BF16;
   if (q_dtype != want_q) return PKV_ERR_DTYPE;
-  const int extra = (qsl && !causal && max_query_len > 0) ? max_query_len - 1 : 0;
-  st = check_plan(plan, hq, cache->num_kv_heads, cache->block_size, max_seq_len, window, extra);
+  const int extra = (row_mode == 1 && !causal && max_query_len > 0) ? max_query_len - 1 : 0;
+  st = check_plan(plan, rows, hq, cache->num_kv_heads, cache->head_dim, cache->block_size,
+                  cache->dtype, max_seq_len, window, extra);
   if (st != PKV_OK) return st;
   if (!(scale > 0.0f) || !isfinite(scale)) return PKV_ERR_SHAPE;
-  const int nrows_eff = qsl ? (num_reqs > 0 ? rows : 0) : rows;
+  const int nrows_eff = (row_mode != 0 && num_reqs == 0) ? 0 : rows;
   if (nrows_eff > 0) {
     if (!out || !q || !bt || !seq_lens) return PKV_ERR_NULL;
     if (bt_stride == 0) return PKV_ERR_SHAPE;
   }
-  const size_t need = plan->max_splits > 1 ? partial_bytes(rows, hq, plan->max_splits, cache->head_dim) : 0;
+  const size_t need = plan_bytes(*plan, rows, hq, cache->head_dim);
   if (need > 0 && nrows_eff > 0 && (!ws || ws_bytes < need)) return PKV_ERR_WORKSPACE;
   if (ws && (reinterpret_cast<uintptr_t>(ws) & 15u)) return PKV_ERR_SHAPE;
-  const long long items = (long long)rows * hq / plan->heads_per_item * plan->max_splits;
+  const long long items = plan->scheme == 1
+      ? (long long)plan->num_workers
+      : (long long)rows * hq / plan->heads_per_item * plan->max_splits;
   if (items > 0x7FFFFFFFLL) return PKV_ERR_SHAPE;
 
   const float log2e = 1.4426950408889634f;
+  a = DecodeArgs{};
   a.out = out;
   a.q = q;
-  a.chunked = qsl != nullptr;
+  a.row_mode = row_mode;
   a.causal = causal != 0;
-  a.single_only = 0;
+  a.skip_single = 0;
   a.qsl = qsl;
   a.num_reqs = num_reqs;
   a.max_query_len = max_query_len;
   a.num_rows = nrows_eff;
+  a.num_tokens = rows;
   a.num_q_heads = hq;
   a.num_kv_heads = cache->num_kv_heads;
   a.group = hq / cache->num_kv_heads;
@@ -637,20 +1486,20 @@ static int prepare(DecodeArgs& a, void* out, const void* q, int q_dtype, int row
   a.window = window;
   a.split_blocks = plan->split_blocks;
   a.max_splits = plan->max_splits;
+  a.kernel_variant = plan->kernel_variant;
+  a.stream = plan->scheme == 1;
+  a.heads_per_item = plan->heads_per_item;
   a.scale_log2 = scale * log2e * (cache->dtype == PKV_FP8_E4M3 ? cache->k_scale : 1.0f);
   a.v_scale = cache->dtype == PKV_FP8_E4M3 ? cache->v_scale : 1.0f;
-  float* wsf = reinterpret_cast<float*>(ws);
-  const size_t nacc = (size_t)rows * hq * plan->max_splits;
-  a.ws_acc = wsf;
-  a.ws_m = wsf ? wsf + nacc * cache->head_dim : nullptr;
-  a.ws_l = wsf ? a.ws_m + nacc : nullptr;
+  bind_workspace(a, ws, rows, hq, cache->head_dim, plan->max_splits, plan->heads_per_item);
   return PKV_OK;
 }
 
-static int run_split(const DecodeArgs& a, int kv_dtype, hipStream_t s) {
+static int run_split(const DecodeArgs& a, const pkv_decode_plan& plan, int kv_dtype, hipStream_t s) {
   if (a.num_rows == 0) return PKV_OK;
-  const int gt = a.group / a.sub_groups;
-  const int st = dispatch_split(a, gt, kv_dtype, s);
+  int st;
+  if (plan.scheme == 1) st = dispatch_stream(a, kv_dtype, plan.num_workers, s);
+  else st = dispatch_split(a, a.group / a.sub_groups, kv_dtype, s);
   if (st != PKV_OK) return st;
   return launch_status();
 }
@@ -667,10 +1516,11 @@ static int run_combine(const DecodeArgs& a, int out_dtype, hipStream_t s) {
 using namespace pkv;
 
 extern "C" int pkv_decode_plan_make(int32_t num_rows, int32_t num_q_heads, int32_t num_kv_heads,
-                                    int32_t head_dim, int32_t block_size, int32_t max_seq_len,
-                                    int32_t sliding_window, pkv_decode_plan* plan) {
-  return make_plan(num_rows, num_q_heads, num_kv_heads, head_dim, block_size, max_seq_len,
-                   sliding_window, 0, plan);
+                                    int32_t head_dim, int32_t block_size, int32_t kv_dtype,
+                                    int32_t max_seq_len, int32_t sliding_window,
+                                    pkv_decode_plan* plan) {
+  return make_plan(num_rows, num_q_heads, num_kv_heads, head_dim, block_size, kv_dtype,
+                   max_seq_len, sliding_window, 0, true, plan);
 }
 
 extern "C" int pkv_paged_attention_decode_partials(
@@ -680,10 +1530,10 @@ extern "C" int pkv_paged_attention_decode_partials(
     const pkv_decode_plan* plan, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   DecodeArgs a;
   int st = prepare(a, out, q, q_dtype, num_seqs, num_q_heads, cache, block_table, bt_stride,
-                   seq_lens, max_seq_len, softmax_scale, sliding_window, nullptr, 0, 0, 1, plan,
+                   seq_lens, max_seq_len, softmax_scale, sliding_window, 0, nullptr, 0, 0, 1, plan,
                    workspace, workspace_bytes);
   if (st != PKV_OK) return st;
-  return run_split(a, cache->dtype, stream);
+  return run_split(a, *plan, cache->dtype, stream);
 }
 
 extern "C" int pkv_paged_attention_decode_combine(void* out, int32_t out_dtype, int32_t num_seqs,
@@ -697,10 +1547,12 @@ extern "C" int pkv_paged_attention_decode_combine(void* out, int32_t out_dtype, 
   if (out_dtype != PKV_F32 && out_dtype != PKV_BF16) return PKV_ERR_DTYPE;
   if (num_seqs < 0 || num_q_heads <= 0 || sliding_window < 0) return PKV_ERR_SHAPE;
   if (!head_dim_supported(head_dim) || !block_size_supported(block_size)) return PKV_ERR_UNSUPPORTED;
-  if (plan->split_blocks < 1 || plan->split_blocks > 64 || plan->max_splits < 1) return PKV_ERR_SHAPE;
+  if (plan->split_blocks < 1 || plan->max_splits < 1 || plan->heads_per_item < 1 ||
+      num_q_heads % plan->heads_per_item || (plan->scheme != 0 && plan->scheme != 1))
+    return PKV_ERR_SHAPE;
   if (num_seqs == 0 || plan->max_splits == 1) return PKV_OK;
   if (!out || !seq_lens) return PKV_ERR_NULL;
-  const size_t need = partial_bytes(num_seqs, num_q_heads, plan->max_splits, head_dim);
+  const size_t need = plan_bytes(*plan, num_seqs, num_q_heads, head_dim);
   if (!workspace || workspace_bytes < need) return PKV_ERR_WORKSPACE;
   DecodeArgs a = {};
   a.out = out;
@@ -710,18 +1562,17 @@ extern "C" int pkv_paged_attention_decode_combine(void* out, int32_t out_dtype, 
   a.bs_log2 = log2_int(block_size);
   a.seq_lens = seq_lens;
   // Bounds are the split phase's business: rows it rejected carry NaN in
-  // every split slot, so the merge reproduces NaN for them.
+  // every split slot (fixed splits) or a piece count of 0 (balanced).
   a.max_seq_len = 0x7FFFFFFF;
   a.bt_stride = 0x7FFFFFFF;
   a.window = sliding_window;
   a.split_blocks = plan->split_blocks;
   a.max_splits = plan->max_splits;
+  a.stream = plan->scheme == 1;
+  a.heads_per_item = plan->heads_per_item;
   a.v_scale = 1.0f;
-  float* wsf = reinterpret_cast<float*>(const_cast<void*>(workspace));
-  const size_t nacc = (size_t)num_seqs * num_q_heads * plan->max_splits;
-  a.ws_acc = wsf;
-  a.ws_m = wsf + nacc * head_dim;
-  a.ws_l = a.ws_m + nacc;
+  bind_workspace(a, const_cast<void*>(workspace), num_seqs, num_q_heads, head_dim, plan->max_splits,
+                 plan->heads_per_item);
   return run_combine(a, out_dtype, stream);
 }
 
@@ -737,32 +1588,59 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dt
   if (q_dtype != (cache->dtype == PKV_F32 ? PKV_F32 : PKV_BF16)) return PKV_ERR_DTYPE;
   pkv_decode_plan plan;
   st = make_plan(num_seqs, num_q_heads, cache->num_kv_heads, cache->head_dim, cache->block_size,
-                 max_seq_len, sliding_window, 0, &plan);
+                 cache->dtype, max_seq_len, sliding_window, 0, true, &plan);
   if (st != PKV_OK) return st;
   DecodeArgs a;
   st = prepare(a, out, q, q_dtype, num_seqs, num_q_heads, cache, block_table, bt_stride, seq_lens,
-               max_seq_len, softmax_scale, sliding_window, nullptr, 0, 0, 1, &plan, workspace,
+               max_seq_len, softmax_scale, sliding_window, 0, nullptr, 0, 0, 1, &plan, workspace,
                workspace_bytes);
   if (st != PKV_OK) return st;
-  st = run_split(a, cache->dtype, stream);
+  st = run_split(a, plan, cache->dtype, stream);
   if (st != PKV_OK) return st;
   return run_combine(a, q_dtype, stream);
+}
+
+// The chunked form runs two passes over disjoint rows: requests with one
+// query take the decode kernels (rows = requests), every other request's
+// tokens take the per-token rows.  Each pass has its own workspace region.
+struct ChunkPlans {
+  pkv_decode_plan single, multi;
+  size_t single_bytes, multi_bytes;
+};
+
+static int chunk_plans(int num_tokens, int num_reqs, int hq, const pkv_cache* c, int max_query_len,
+                       int max_seq_len, int window, ChunkPlans& p) {
+  int st = make_plan(num_reqs, hq, c->num_kv_heads, c->head_dim, c->block_size, c->dtype,
+                     max_seq_len, window, 0, true, &p.single);
+  if (st != PKV_OK) return st;
+  // Non-causal windowed rows see up to W + q_len - 1 keys; size for that case.
+  const int extra = max_query_len > 0 ? max_query_len - 1 : 0;
+  st = make_plan(num_tokens, hq, c->num_kv_heads, c->head_dim, c->block_size, c->dtype,
+                 max_seq_len, window, extra, false, &p.multi);
+  if (st != PKV_OK) return st;
+  p.single_bytes = (p.single.workspace_bytes + 255) & ~(size_t)255;
+  p.multi_bytes = max_query_len > 1 ? p.multi.workspace_bytes : 0;
+  return PKV_OK;
 }
 
 extern "C" int pkv_chunked_workspace_size(int32_t num_tokens, int32_t num_reqs,
                                           int32_t num_q_heads, int32_t num_kv_heads,
                                           int32_t head_dim, int32_t block_size,
-                                          int32_t max_query_len, int32_t max_seq_len,
-                                          int32_t sliding_window, size_t* bytes) {
+                                          int32_t kv_dtype, int32_t max_query_len,
+                                          int32_t max_seq_len, int32_t sliding_window,
+                                          size_t* bytes) {
   if (!bytes) return PKV_ERR_NULL;
   if (num_tokens < 0 || num_reqs < 0 || max_query_len < 0) return PKV_ERR_SHAPE;
-  pkv_decode_plan plan;
-  // Non-causal windowed rows see up to W + q_len - 1 keys; size for that case.
-  const int extra = max_query_len > 0 ? max_query_len - 1 : 0;
-  int st = make_plan(num_tokens, num_q_heads, num_kv_heads, head_dim, block_size, max_seq_len,
-                     sliding_window, extra, &plan);
+  pkv_cache c = {};
+  c.num_kv_heads = num_kv_heads;
+  c.head_dim = head_dim;
+  c.block_size = block_size;
+  c.dtype = kv_dtype;
+  ChunkPlans p;
+  const int st = chunk_plans(num_tokens, num_reqs, num_q_heads, &c, max_query_len, max_seq_len,
+                             sliding_window, p);
   if (st != PKV_OK) return st;
-  *bytes = plan.workspace_bytes;
+  *bytes = p.single_bytes + p.multi_bytes;
   return PKV_OK;
 }
 
@@ -778,21 +1656,37 @@ extern "C" int pkv_paged_attention_chunked(void* out, const void* q, int32_t q_d
                                            hipStream_t stream) {
   int st = check_cache(cache);
   if (st != PKV_OK) return st;
-  if (num_tokens < 0 || num_reqs < 0) return PKV_ERR_SHAPE;
+  if (num_tokens < 0 || num_reqs < 0 || max_query_len < 0) return PKV_ERR_SHAPE;
   if (q_dtype != (cache->dtype == PKV_F32 ? PKV_F32 : PKV_BF16)) return PKV_ERR_DTYPE;
   if (num_tokens == 0 || num_reqs == 0) return PKV_OK;
   if (!query_start_loc) return PKV_ERR_NULL;
-  pkv_decode_plan plan;
-  const int extra = max_query_len > 0 ? max_query_len - 1 : 0;
-  st = make_plan(num_tokens, num_q_heads, cache->num_kv_heads, cache->head_dim,
-                 cache->block_size, max_seq_len, sliding_window, extra, &plan);
+  ChunkPlans p;
+  st = chunk_plans(num_tokens, num_reqs, num_q_heads, cache, max_query_len, max_seq_len,
+                   sliding_window, p);
   if (st != PKV_OK) return st;
-  DecodeArgs a;
-  st = prepare(a, out, q, q_dtype, num_tokens, num_q_heads, cache, block_table, bt_stride,
-               seq_lens, max_seq_len, softmax_scale, sliding_window, query_start_loc, num_reqs,
-               max_query_len, causal, &plan, workspace, workspace_bytes);
+  if (p.single_bytes + p.multi_bytes > 0 && (!workspace || workspace_bytes < p.single_bytes + p.multi_bytes))
+    return PKV_ERR_WORKSPACE;
+  char* ws = reinterpret_cast<char*>(workspace);
+  // requests with a single query (causal or not, one query sees keys <= p)
+  DecodeArgs a1;
+  st = prepare(a1, out, q, q_dtype, num_reqs, num_q_heads, cache, block_table, bt_stride, seq_lens,
+               max_seq_len, softmax_scale, sliding_window, 2, query_start_loc, num_reqs,
+               max_query_len, 1, &p.single, ws, p.single_bytes);
   if (st != PKV_OK) return st;
-  st = run_split(a, cache->dtype, stream);
+  a1.num_tokens = num_tokens;
+  if (max_query_len > 1) {
+    DecodeArgs a2;
+    st = prepare(a2, out, q, q_dtype, num_tokens, num_q_heads, cache, block_table, bt_stride,
+                 seq_lens, max_seq_len, softmax_scale, sliding_window, 1, query_start_loc, num_reqs,
+                 max_query_len, causal, &p.multi, ws ? ws + p.single_bytes : nullptr, p.multi_bytes);
+    if (st != PKV_OK) return st;
+    a2.skip_single = 1;
+    st = run_split(a2, p.multi, cache->dtype, stream);
+    if (st != PKV_OK) return st;
+    st = run_combine(a2, q_dtype, stream);
+    if (st != PKV_OK) return st;
+  }
+  st = run_split(a1, p.single, cache->dtype, stream);
   if (st != PKV_OK) return st;
-  return run_combine(a, q_dtype, stream);
+  return run_combine(a1, q_dtype, stream);
 }

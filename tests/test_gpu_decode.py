@@ -51,7 +51,7 @@ def _small(seed, B, Lmax, Hq, Hkv, D, bs, dtype="bf16", Lmin=1, pool=None):
         sigma=1.0 if dtype == "f32" else 0.35)
 
 
-def _check_attention_only(w, window=0, plan_split=None):
+def _check_attention_only(w, window=0, plan_split=None, variant=None):
     """Decode attention over the planes as given (no write) vs the oracle."""
     d = w.device()
     if plan_split is None:
@@ -59,13 +59,10 @@ def _check_attention_only(w, window=0, plan_split=None):
                                          w.scale, sliding_window=window)
     else:
         plan = pkv.decode_plan(w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len, window)
-        plan.split_blocks = plan_split
-        nvis = -(-w.max_seq_len // w.block_size)
-        if window:
-            nvis = min(nvis, -(-(window + w.block_size - 1) // w.block_size))
-        plan.max_splits = -(-nvis // plan_split)
-        ws = torch.empty(w.num_reqs * w.num_q_heads * plan.max_splits * (w.head_dim + 2) * 4,
-                         dtype=torch.uint8, device="cuda")
+        workers = None if plan.scheme == 0 else max(1, plan.num_workers // plan_split)
+        pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len, window,
+                      split_blocks=plan_split, num_workers=workers, kernel_variant=variant)
+        ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
         out = torch.empty_like(d.q)
         pkv.paged_attention_decode_partials(d.q, d.cache, d.block_table, d.seq_lens, w.max_seq_len,
                                             w.scale, plan, ws, out, sliding_window=window)
@@ -118,13 +115,37 @@ def test_sliding_window(W):
 
 
 @pytest.mark.parametrize("split", [1, 2, 3, 8, 64])
-def test_any_split_plan_gives_the_same_answer(split):
-    say("decode split", split)
+@pytest.mark.parametrize("variant", [0, 2, 3, 4])
+def test_any_split_plan_gives_the_same_answer(split, variant):
+    say("decode split", split, "variant", variant)
     w = _small(150, B=6, Lmax=1500, Hq=32, Hkv=8, D=128, bs=16, Lmin=200)
-    _, err = _check_attention_only(w, plan_split=split)
+    _, err = _check_attention_only(w, plan_split=split, variant=variant)
     assert err <= TOL["bf16"]
-    _, err = _check_attention_only(w, window=333, plan_split=split)
+    _, err = _check_attention_only(w, window=333, plan_split=split, variant=variant)
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("split", [1, 8, 64])
+def test_vector_alu_fixed_split_path(split):
+    """The vector-ALU kernels behind scheme 0 on a shape the matrix path would take."""
+    say("decode fixed-split vector path", split)
+    w = _small(151, B=5, Lmax=900, Hq=32, Hkv=8, D=128, bs=32, Lmin=100)
+    d = w.device()
+    plan = pkv.decode_plan(w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len)
+    if plan.scheme != 0:
+        # build the equivalent scheme-0 plan by hand: vector kernels, fixed splits
+        plan.scheme, plan.num_workers, plan.heads_per_item = 0, 0, 4
+    pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len, split_blocks=split,
+                  kernel_variant=1)
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d.q)
+    pkv.paged_attention_decode_partials(d.q, d.cache, d.block_table, d.seq_lens, w.max_seq_len,
+                                        w.scale, plan, ws, out)
+    pkv.paged_attention_decode_combine(out, d.seq_lens, w.block_size, plan, ws)
+    torch.cuda.synchronize()
+    ref = attention.paged_decode(w.q, "bf16", w.k_plane, w.v_plane, "bf16", w.block_table,
+                                 w.seq_lens, w.scale)
+    assert max_err(out_f64(out), ref) <= TOL["bf16"]
 
 
 def test_phases_equal_the_one_call_form_bit_for_bit():
