@@ -947,6 +947,111 @@ __device__ __forceinline__ bool mfma_fold(const DecodeArgs& a, const RowInfo& sp
       else compute(std::false_type{}, st, bf);
     };
 
+    if constexpr (DEPTH < 0) {
+      // Two full steps per iteration as straight-line code: two independent
+      // MFMA chains, one max / lane-read / rescale decision per head for the
+      // 32 tokens, then both P.V halves.  Steps with masked rows (only at the
+      // two ends of a row's visible range) go one at a time.
+      auto scores = [&](const Buf& bf) {
+        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          uint4 kw;
+          if constexpr (KB == 16) {
+            kw = make_uint4(bf.k[c][0], bf.k[c][1], bf.k[c][2], bf.k[c][3]);
+          } else {
+            kw = make_uint4(e4m3x2_to_bf16x2<false>(bf.k[c][0]), e4m3x2_to_bf16x2<true>(bf.k[c][0]),
+                            e4m3x2_to_bf16x2<false>(bf.k[c][1]), e4m3x2_to_bf16x2<true>(bf.k[c][1]));
+          }
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[c], __builtin_bit_cast(bf16x8_t, kw), sc, 0, 0, 0);
+        }
+        return sc;
+      };
+      auto pv = [&](const Buf& bf, const float (&pr)[4]) {
+#pragma unroll
+        for (int u = 0; u < VU; ++u) {
+          const int tok = u * VRPW + vg;
+          const uint32_t vwa[4] = {bf.v[u].x, bf.v[u].y, bf.v[u].z, bf.v[u].w};
+          float vf[VEPL];
+          if constexpr (KV == PKV_BF16) {
+#pragma unroll
+            for (int i = 0; i < VEPL / 2; ++i) { vf[2 * i] = bf16_lo(vwa[i]); vf[2 * i + 1] = bf16_hi(vwa[i]); }
+          } else {
+#pragma unroll
+            for (int i = 0; i < VEPL / 4; ++i) {
+              const f32x2 v01 = e4m3x2_to_f32<false>(vwa[i]);
+              const f32x2 v23 = e4m3x2_to_f32<true>(vwa[i]);
+              vf[4 * i] = v01.x; vf[4 * i + 1] = v01.y; vf[4 * i + 2] = v23.x; vf[4 * i + 3] = v23.y;
+            }
+          }
+#pragma unroll
+          for (int h = 0; h < GT; ++h) {
+            const int src = (tok + 16 * (h / 4)) * 4;
+            const float ph = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                src, __builtin_bit_cast(int, pr[h % 4])));
+#pragma unroll
+            for (int e = 0; e < VEPL; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
+          }
+        }
+      };
+      auto full_step = [&](int st) {
+        const int p0 = pos_base + st * 16;
+        return p0 >= span.lo && p0 + 15 <= span.hi;
+      };
+      int st = 0;
+      while (st < nsteps) {
+        if (st + 1 < nsteps && full_step(st) && full_step(st + 1)) {
+          Buf ba, bb;
+          issue(st, ba);
+          issue(st + 1, bb);
+          const f32x4_t sa = scores(ba);
+          const f32x4_t sb = scores(bb);
+          float za[4], zb[4], mx[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            za[i] = sa[i] * a.scale_log2;
+            zb[i] = sb[i] * a.scale_log2;
+            float v = fmaxf(za[i], zb[i]);
+            v = fmaxf(v, dpp<kDppQuadXor1>(v));
+            v = fmaxf(v, dpp<kDppQuadXor2>(v));
+            v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
+            v = fmaxf(v, dpp<kDppRowMirror>(v));
+            mx[i] = v;
+          }
+#pragma unroll
+          for (int h = 0; h < GT; ++h) {
+            const float mb = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                __builtin_bit_cast(int, mx[h % 4]), 16 * (h / 4)));
+            if (mb > m[h] + kLazyRescale) {
+              const float alpha = __builtin_amdgcn_exp2f(m[h] - mb);
+#pragma unroll
+              for (int e = 0; e < VEPL; ++e) acc[h][e] *= alpha;
+              if (lane / 16 == h / 4) lsum[h % 4] *= alpha;
+              m[h] = mb;
+            }
+          }
+          float pa[4], pb[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float mv = m[i < GT ? i : 0];
+#pragma unroll
+            for (int r = 1; r < RG; ++r)
+              if (lane / 16 == r && 4 * r + i < GT) mv = m[4 * r + i];
+            pa[i] = __builtin_amdgcn_exp2f(za[i] - mv);
+            pb[i] = __builtin_amdgcn_exp2f(zb[i] - mv);
+            lsum[i] += pa[i] + pb[i];
+          }
+          pv(ba, pa);
+          pv(bb, pb);
+          st += 2;
+        } else {
+          Buf b0;
+          issue(st, b0);
+          run(st, b0);
+          st += 1;
+        }
+      }
+    } else {
     // Loads run DEPTH steps ahead of the step being folded, unconditionally:
     // past the end the last step is fetched again (an L2 hit).  A branch
     // around a prefetch would make the wait-count tracking merge two paths
@@ -979,6 +1084,7 @@ __device__ __forceinline__ bool mfma_fold(const DecodeArgs& a, const RowInfo& sp
         issue(st, b0);
         run(st, b0);
       }
+    }
     }
   }
   return true;
@@ -1286,7 +1392,7 @@ static int make_plan(int rows, int hq, int hkv, int d, int bs, int kv_dtype, int
 static int check_plan(const pkv_decode_plan* plan, int rows, int hq, int hkv, int d, int bs,
                       int kv_dtype, int max_seq_len, int window, int extra) {
   if (!plan) return PKV_ERR_NULL;
-  if (plan->kernel_variant < 0 || plan->kernel_variant > 4) return PKV_ERR_SHAPE;
+  if (plan->kernel_variant < 0 || plan->kernel_variant > 5) return PKV_ERR_SHAPE;
   const int group = hq / hkv;
   const int nvis = max_visible_blocks(max_seq_len, bs, window, extra);
   if (plan->scheme == 1) {
@@ -1359,6 +1465,10 @@ static void launch_stream(const DecodeArgs& a, int workers, hipStream_t s) {
   // SIMD (up to four query heads per item), one step ahead beyond that
   constexpr int kDepth = GT >= 8 ? 1 : 2;
   if constexpr (D == 128) {
+    if (a.kernel_variant == 5) {
+      decode_stream_mfma_kernel<D, GT, KV, -1><<<workers, 64, lds, s>>>(a);
+      return;
+    }
     if (a.kernel_variant >= 2 && a.kernel_variant <= 4) {
       const int depth = a.kernel_variant - 2;
       if (depth == 0) decode_stream_mfma_kernel<D, GT, KV, 0><<<workers, 64, lds, s>>>(a);
