@@ -8,7 +8,7 @@ under different physical block permutations (3 GiB in total), so the 256 MB
 last-level cache cannot serve the KV reads.
 
 Prints one JSON line: the whole step's algorithmic HBM bytes per second
-(value), the split kernel's roofline (HIP events around each of its launches),
+(value), the split kernel's roofline (HIP events around back-to-back launches of it),
 bulk KV-write rates, and the CPU oracle on a bounded sample of the same step.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--split-blocks", type=int, default=0, help="override the decode split (tuning)")
     p.add_argument("--variant", type=int, default=0, help="decode kernel variant (tuning)")
     p.add_argument("--workers", type=int, default=0, help="balanced-scheme workers (tuning)")
+    p.add_argument("--summarize-profiles", default="",
+                   help="write profiles/ summaries from rocprofv3 output under this folder")
     p.add_argument("--calibration-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (scale reference for HBM counters)")
     return p.parse_args()
@@ -117,8 +119,71 @@ def cpu_baseline(w, sample_seqs, min_seconds=10.0):
                 seconds=round(dt, 2), bytes=ab)
 
 
+PROFILE_CMDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_decode -o run "
+             "-- python bench.py --no-cpu-baseline --steps 200",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o p "
+             "-- python bench.py --no-cpu-baseline --steps 20 --warmup 2 --calibration-copy",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o p "
+             "-- python bench.py --no-cpu-baseline --steps 20 --warmup 2 --calibration-copy",
+}
+CALIBRATION_BYTES = 3 * (1 << 30)   # three 1 GiB copies under --calibration-copy
+
+
+def _find(d, suffix):
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError("%s under %s" % (suffix, d))
+
+
+def summarize_profiles(out_dir):
+    """Turn the rocprofv3 outputs of PROFILE_CMDS (under out_dir) into the
+    short summaries kept in profiles/ (run on the host after the GPU run)."""
+    import csv
+    prof = os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+    stats = list(csv.DictReader(open(_find(os.path.join(out_dir, "prof_decode"), "kernel_stats.csv"))))
+    lines = ["rocprofv3 kernel trace of the Llama-3-8B-shaped decode step (bench.py)",
+             "command: " + PROFILE_CMDS["trace"], "",
+             "%-70s %7s %12s %10s" % ("kernel", "calls", "avg us", "share %")]
+    for r in stats:
+        name = r["Name"].split("(")[0][:70]
+        lines.append("%-70s %7s %12.2f %10.2f" % (name, r["Calls"], float(r["AverageNs"]) / 1e3,
+                                                   float(r["Percentage"])))
+    with open(os.path.join(prof, "decode_llama8b_b64_kernel_trace.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    def counters(sub, name):
+        rows = list(csv.DictReader(open(_find(os.path.join(out_dir, sub), "counter_collection.csv"))))
+        split = [float(r["Counter_Value"]) for r in rows
+                 if SPLIT_KERNEL in r["Kernel_Name"] and r["Counter_Name"] == name]
+        copy = [float(r["Counter_Value"]) for r in rows
+                if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == name]
+        return float(np.mean(split)), len(split), float(np.mean(copy)), len(copy)
+
+    fetch, nf, fcopy, ncf = counters("pmc_fetch", "FETCH_SIZE")
+    write, nw, wcopy, ncw = counters("pmc_write", "WRITE_SIZE")
+    f_fetch = (CALIBRATION_BYTES / ncf) / (fcopy * 1024.0)   # known bytes per copy dispatch
+    f_write = (CALIBRATION_BYTES / ncw) / (wcopy * 1024.0)
+    hbm = fetch * 1024.0 * f_fetch + write * 1024.0 * f_write
+    rec = dict(kernel=SPLIT_KERNEL, kernel_source_sha256_16=source_hash(),
+               fetch_kib_per_launch=fetch, write_kib_per_launch=write, launches=[nf, nw],
+               calibration=dict(copy_dispatch_bytes=[CALIBRATION_BYTES / ncf, CALIBRATION_BYTES / ncw],
+                                fetch_kib=fcopy, write_kib=wcopy, fetch_factor=f_fetch,
+                                write_factor=f_write),
+               hbm_bytes_per_launch=int(hbm), commands=[PROFILE_CMDS["fetch"], PROFILE_CMDS["write"]])
+    with open(PMC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
+
+
 def main():
     args = parse()
+    if args.summarize_profiles:
+        print(json.dumps(summarize_profiles(args.summarize_profiles)))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -154,16 +219,12 @@ def main():
     out = torch.empty_like(base.q)
     slots = torch.empty(w.num_reqs, dtype=torch.int64, device=dev)
 
-    def step(i, ev=None):
+    def step(i):
         cache, bt = pools[i % POOLS]
         pkv.slot_mapping(bt, base.query_start_loc, base.num_computed, w.block_size, nb, out=slots)
         pkv.cache_write(base.new_k, base.new_v, slots, cache)
-        if ev is not None:
-            ev[0].record()
         pkv.paged_attention_decode_partials(base.q, cache, bt, base.seq_lens, w.max_seq_len, w.scale,
                                             plan, ws, out)
-        if ev is not None:
-            ev[1].record()
         pkv.paged_attention_decode_combine(out, base.seq_lens, w.block_size, plan, ws)
 
     for i in range(args.warmup):
@@ -181,14 +242,18 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
-    # split kernel alone: events around each launch, same rotation
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # split kernel alone: `steps` back-to-back launches over the same pool
+    # rotation between two events (no event inside, so no per-event overhead)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    a.record()
     for i in range(args.steps):
-        step(i, evs[i])
+        cache, bt = pools[i % POOLS]
+        pkv.paged_attention_decode_partials(base.q, cache, bt, base.seq_lens, w.max_seq_len, w.scale,
+                                            plan, ws, out)
+    b.record()
     torch.cuda.synchronize()
-    split_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    split_ms = a.elapsed_time(b) / args.steps
 
     ab = algorithmic_bytes(w)
     value = ab["step"] / (ms_per_step * 1e-3) / 1e9
