@@ -28,9 +28,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E, AMD's published peak
 POOLS = 3
-SPLIT_KERNEL = "decode_stream_mfma_kernel"
+SPLIT_KERNEL = "decode_flat_kernel"
 PMC_FILE = os.path.join(ROOT, "profiles", "decode_split_llama8b_b64_pmc.json")
-KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_mapping_amd", "csrc", "decode.hip")
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_mapping_amd", "csrc", "decode_kernels.h")
 
 
 def parse():

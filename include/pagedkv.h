@@ -177,10 +177,10 @@ typedef struct {
   int32_t max_splits;     /* partial slots per (row, query head)                  */
   int32_t heads_per_item; /* query heads one work item processes                  */
   int32_t kernel_variant; /* 0: the library's choice.  Tuning only: 1 = vector
-                             ALUs for the scores (scheme 0 only); 2, 3, 4 =
-                             matrix cores with loads issued 0, 1 or 2 steps
-                             ahead (head_dim 128).  Every variant computes
-                             the same result up to rounding order.           */
+                             ALUs for the scores (scheme 0 only); 2, 3 =
+                             scheme 1 with K/V loads issued 1 or 2 steps
+                             ahead.  Every variant computes the same result
+                             up to rounding order.                           */
   size_t workspace_bytes; /* partial (acc, m, l) storage (+ piece counts)         */
   int32_t scheme;         /* 0 or 1, see above                                    */
   int32_t num_workers;    /* scheme 1: workers launched                           */

@@ -1,0 +1,1400 @@
+// Paged decode attention kernels: split phase (per-split online softmax) and
+// combine, with their launch templates.  Included by decode.hip (host side)
+// and by the decode_*.hip files that instantiate the kernels per head size.
+//
+// Attention reads each sequence's past K/V by following its block table
+// instead of assuming one contiguous tensor ("vLLM의 KV cache 연결 흐름",
+// sections on slot mapping and on the metadata handed to the backend).  The
+// softmax normaliser spans every block ("Understanding PageAttention Memory
+// Optimization", section "Handling Softmax Across Blocks"); kernels tile the
+// keys and keep a running (online) softmax (Chinese original of the
+// worker-side page, section "Worker与ModelRunner的协作").  Grouped-query
+// heads share a KV head and a sliding window limits keys to the most recent W
+// positions ("Deep Dive into vLLM Worker-Side GPU KV Cache Initialization",
+// section "Hybrid Attention Mechanisms").
+//
+// Work decomposition (MI355X): one wave per (row, KV head, group of query
+// heads, split of consecutive visible blocks).  A wave reads a token row of
+// one KV head with LPR lanes x 16 bytes (RPW = 64 / LPR rows per load), keeps
+// one online-softmax state per lane for the rows it sees, and merges the
+// lanes' states with cross-lane exchanges at the end.  Scores reduce over the
+// LPR lanes of a row with DPP.  Sequences with more than one split leave base-2
+// partial states (m, l, acc) in the workspace for the combine kernel.
+#pragma once
+
+#include <math.h>
+
+#include <type_traits>
+
+#include "common.h"
+#include "host_common.h"
+
+namespace pkv {
+
+constexpr float kLazyRescale = 8.0f;  // keep a stale max until a score beats it by 2^8
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  // Row mode.  0 (decode): row b is sequence b, its query is row b of q/out.
+  // 1 (chunked tokens): row t is token t of the step; its request is found
+  //   through query_start_loc; position seq_len - q_len + (t - qsl[r]).
+  //   Tokens of single-query requests are skipped when skip_single is set.
+  // 2 (chunked requests): row r is request r; only requests with exactly one
+  //   query are processed (their query token is qsl[r]).
+  int32_t row_mode;
+  int32_t causal;
+  int32_t skip_single;
+  const int32_t* qsl;
+  int32_t num_reqs;
+  int32_t max_query_len;
+  int32_t num_tokens;       // rows of q / out
+  int32_t num_rows;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;            // query heads per KV head
+  int32_t sub_groups;       // group / heads per work item
+  int32_t head_dim;
+  const char* kbase;
+  const char* vbase;
+  int64_t block_stride;     // elements
+  int32_t num_blocks;
+  int32_t bs_log2;
+  const int32_t* bt;
+  int32_t bt_stride;
+  const int32_t* seq_lens;
+  int32_t max_seq_len;
+  int32_t window;
+  int32_t split_blocks;
+  int32_t max_splits;
+  float scale_log2;         // softmax_scale * log2(e) (* k_scale for fp8)
+  float v_scale;            // 1, or the fp8 V scale
+  float* ws_acc;
+  float* ws_m;
+  float* ws_l;
+  int32_t kernel_variant;   // 0 default; tuning: 1 vector-only, 2/3 loads 1/2 steps ahead
+  int32_t stream;           // balanced partition (piece counts in ws_np)
+  int32_t heads_per_item;
+  int32_t* ws_np;           // balanced partition: pieces per (row, head group)
+};
+
+// What one row attends to.
+struct RowInfo {
+  bool skip;      // not this kernel's row (padding, or handled elsewhere)
+  bool valid;     // lengths and block-table row consistent
+  int req;        // block-table row
+  int tok;        // row of q / out
+  int lo, hi;     // inclusive visible key positions
+  int first_blk;  // lo / block_size
+  int nvis;       // visible logical blocks
+};
+
+__device__ __forceinline__ RowInfo row_info(const DecodeArgs& a, int row) {
+  RowInfo r;
+  r.skip = false;
+  r.valid = false;
+  r.req = row;
+  r.tok = row;
+  r.nvis = 0;
+  int L, p;
+  if (a.row_mode == 0) {
+    L = a.seq_lens[row];
+    p = L - 1;
+    if (L <= 0 || L > a.max_seq_len) return r;
+  } else if (a.row_mode == 2) {
+    const int t0 = a.qsl[row];
+    if (a.qsl[row + 1] - t0 != 1 || t0 < 0 || t0 >= a.num_tokens) { r.skip = true; return r; }
+    r.tok = t0;
+    L = a.seq_lens[row];
+    p = L - 1;
+    if (L <= 0 || L > a.max_seq_len) return r;
+  } else {
+    const int end = a.qsl[a.num_reqs];
+    if (row < a.qsl[0] || row >= end) { r.skip = true; return r; }
+    int lo = 0, hi = a.num_reqs;  // largest q with qsl[q] <= row
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.qsl[mid] <= row) lo = mid; else hi = mid;
+    }
+    r.req = lo;
+    const int ql = a.qsl[lo + 1] - a.qsl[lo];
+    if (a.skip_single && ql == 1) { r.skip = true; return r; }
+    L = a.seq_lens[lo];
+    if (L <= 0 || L > a.max_seq_len || ql > L || ql > a.max_query_len) return r;
+    p = L - ql + (row - a.qsl[lo]);
+  }
+  r.hi = (a.row_mode != 0 && !a.causal) ? L - 1 : p;
+  r.lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
+  if (r.lo > r.hi) return r;
+  r.first_blk = r.lo >> a.bs_log2;
+  const int last = r.hi >> a.bs_log2;
+  if (last >= a.bt_stride) return r;
+  r.nvis = last - r.first_blk + 1;
+  r.valid = true;
+  return r;
+}
+
+template <typename T>
+__device__ __forceinline__ T shfl_xor_t(T v, int m) { return __shfl_xor(v, m); }
+
+// Store n consecutive floats of one output row as the output dtype.
+template <int OT, int N>
+__device__ __forceinline__ void store_out(void* base, int64_t elem, const float (&v)[N]) {
+  if constexpr (OT == PKV_F32) {
+    float* p = reinterpret_cast<float*>(base) + elem;
+#pragma unroll
+    for (int i = 0; i < N; ++i) p[i] = v[i];
+  } else {
+    uint16_t* p = reinterpret_cast<uint16_t*>(base) + elem;
+    if constexpr (N % 8 == 0) {
+#pragma unroll
+      for (int i = 0; i < N / 8; ++i) {
+        uint4 w;
+        w.x = f32_to_bf16_rne(v[8 * i + 0]) | (f32_to_bf16_rne(v[8 * i + 1]) << 16);
+        w.y = f32_to_bf16_rne(v[8 * i + 2]) | (f32_to_bf16_rne(v[8 * i + 3]) << 16);
+        w.z = f32_to_bf16_rne(v[8 * i + 4]) | (f32_to_bf16_rne(v[8 * i + 5]) << 16);
+        w.w = f32_to_bf16_rne(v[8 * i + 6]) | (f32_to_bf16_rne(v[8 * i + 7]) << 16);
+        reinterpret_cast<uint4*>(p)[i] = w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; ++i) p[i] = (uint16_t)f32_to_bf16_rne(v[i]);
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Split phase.  D: head_dim; GT: query heads per work item; KV: cache dtype;
+// QT: query/output dtype (F32 with an F32 cache, BF16 otherwise).
+template <int D, int GT, int KV, int QT>
+__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+  constexpr int kElt = KV == PKV_F32 ? 4 : (KV == PKV_BF16 ? 2 : 1);
+  constexpr int kRowBytes = D * kElt;
+  constexpr int kVec = kRowBytes >= 16 ? 16 : kRowBytes;  // bytes per lane per row
+  constexpr int LPR = kRowBytes / kVec;                    // lanes per row
+  constexpr int EPL = kVec / kElt;                         // elements per lane
+  constexpr int RPW = kWave / LPR;                         // rows per wave load
+  constexpr int U = RPW >= 16 ? 1 : 16 / RPW;              // loads per step (>= 16 rows)
+  constexpr bool kBf16Dot = (QT == PKV_BF16);              // q.k on packed bf16 pairs
+  static_assert(EPL % 2 == 0 || !kBf16Dot, "bf16 dot needs pairs");
+  constexpr int QW = kBf16Dot ? EPL / 2 : EPL;             // q registers per head
+
+  const int lane = threadIdx.x;
+  const int grp = lane / LPR;
+  const int sub = lane % LPR;
+
+  const int kvgroups = a.num_kv_heads * a.sub_groups;
+  int w = blockIdx.x;
+  const int s = w % a.max_splits;
+  w /= a.max_splits;
+  const int kvg = w % kvgroups;
+  const int b = w / kvgroups;
+  const int kvh = kvg / a.sub_groups;
+  const int h0 = kvh * a.group + (kvg % a.sub_groups) * GT;
+
+  const RowInfo span = row_info(a, b);
+  if (span.skip) return;
+  const int64_t out_row = ((int64_t)span.tok * a.num_q_heads + h0) * D;
+  if (!span.valid) {
+    // Invalid row: NaN output (split 0) and NaN partials in every split slot,
+    // so that a combine pass over this row can only produce NaN.
+    if (grp == 0) {
+      float nanv[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) nanv[e] = __builtin_nanf("");
+      for (int h = 0; h < GT; ++h) {
+        if (s == 0) store_out<QT, EPL>(a.out, out_row + h * D + sub * EPL, nanv);
+        if (a.max_splits > 1) {
+          const int64_t pr = ((int64_t)b * a.num_q_heads + h0 + h) * a.max_splits + s;
+          float* dst = a.ws_acc + pr * D + sub * EPL;
+          for (int e = 0; e < EPL; ++e) dst[e] = nanv[e];
+          if (sub == 0) {
+            a.ws_m[pr] = 0.f;
+            a.ws_l[pr] = nanv[0];
+          }
+        }
+      }
+    }
+    return;
+  }
+  const int nsplit = ceil_div(span.nvis, a.split_blocks);
+  if (s >= nsplit) return;
+
+  const int blk_begin = span.first_blk + s * a.split_blocks;
+  const int nb = min(a.split_blocks, span.first_blk + span.nvis - blk_begin);
+  const int bs = 1 << a.bs_log2;
+
+  // Stage this split's block ids in a register: lane i holds entry i.
+  int tab = -1;
+  if (lane < nb) tab = a.bt[(int64_t)span.req * a.bt_stride + blk_begin + lane];
+  const bool bad = (lane < nb) && (tab < 0 || tab >= a.num_blocks);
+  const bool any_bad = __ballot(bad) != 0;
+
+  // Query slice of this lane: heads h0..h0+GT-1, elements sub*EPL .. +EPL.
+  uint32_t qr[GT][QW];
+  float qf[GT][kBf16Dot ? 1 : EPL];
+  if constexpr (kBf16Dot) {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + out_row + sub * EPL;
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+#pragma unroll
+      for (int i = 0; i < QW; ++i)
+        qr[h][i] = reinterpret_cast<const uint32_t*>(qp + h * D)[i];
+    }
+  } else {
+    const float* qp = reinterpret_cast<const float*>(a.q) + out_row + sub * EPL;
+#pragma unroll
+    for (int h = 0; h < GT; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qf[h][e] = qp[h * D + e];
+  }
+  (void)qr;
+  (void)qf;
+
+  float m[GT], l[GT], acc[GT][EPL];
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+
+  if (!any_bad) {
+    const int pos0 = blk_begin << a.bs_log2;           // first position of the split
+    const int pos_end = min((blk_begin + nb) << a.bs_log2, span.hi + 1);
+    const int ntiles = ceil_div(pos_end - pos0, RPW);
+    const int nsteps = ceil_div(ntiles, U);
+    const int64_t head_off = (int64_t)kvh * D + sub * EPL;  // elements inside a token row
+    const int64_t row_elems = (int64_t)a.num_kv_heads * D;
+
+    uint4 ka[U], va[U], kb2[U], vb2[U];
+    bool la[U], lb[U];
+
+    auto issue = [&](int step, uint4 (&kd)[U], uint4 (&vd)[U], bool (&vl)[U]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int pos = pos0 + (step * U + u) * RPW + grp;
+        const bool live = pos >= span.lo && pos < pos_end;
+        const int local = (pos >> a.bs_log2) - blk_begin;
+        const int phys = __shfl(tab, local < 0 ? 0 : (local > 63 ? 63 : local));
+        vl[u] = live;
+        kd[u] = make_uint4(0, 0, 0, 0);
+        vd[u] = make_uint4(0, 0, 0, 0);
+        if (live) {
+          const int64_t e = (int64_t)phys * a.block_stride + (pos & (bs - 1)) * row_elems + head_off;
+          if constexpr (kVec == 16) {
+            kd[u] = *reinterpret_cast<const uint4*>(a.kbase + e * kElt);
+            vd[u] = *reinterpret_cast<const uint4*>(a.vbase + e * kElt);
+          } else if constexpr (kVec == 8) {
+            uint2 k2 = *reinterpret_cast<const uint2*>(a.kbase + e * kElt);
+            uint2 v2 = *reinterpret_cast<const uint2*>(a.vbase + e * kElt);
+            kd[u] = make_uint4(k2.x, k2.y, 0, 0);
+            vd[u] = make_uint4(v2.x, v2.y, 0, 0);
+          }
+        }
+      }
+    };
+
+    // One step: U row loads of K and V per lane, folded into the state.
+    auto compute = [&](const uint4 (&kd)[U], const uint4 (&vd)[U], const bool (&vl)[U]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint4 kw = kd[u];
+        const uint4 vw = vd[u];
+        const bool live = vl[u];
+        const uint32_t kwa[4] = {kw.x, kw.y, kw.z, kw.w};
+        const uint32_t vwa[4] = {vw.x, vw.y, vw.z, vw.w};
+
+        // K and V of this lane's row chunk in compute form.
+        float vf[EPL];
+        uint32_t kp[kBf16Dot ? EPL / 2 : 1];
+        float kf[kBf16Dot ? 1 : EPL];
+        (void)kp;
+        (void)kf;
+        if constexpr (KV == PKV_BF16) {
+#pragma unroll
+          for (int i = 0; i < EPL / 2; ++i) {
+            vf[2 * i] = bf16_lo(vwa[i]);
+            vf[2 * i + 1] = bf16_hi(vwa[i]);
+            if constexpr (kBf16Dot) kp[i] = kwa[i];
+            else { kf[2 * i] = bf16_lo(kwa[i]); kf[2 * i + 1] = bf16_hi(kwa[i]); }
+          }
+        } else if constexpr (KV == PKV_F32) {
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) {
+            vf[i] = as_float(vwa[i]);
+            kf[i] = as_float(kwa[i]);
+          }
+        } else {  // fp8 codes, 4 per dword
+#pragma unroll
+          for (int i = 0; i < EPL / 4; ++i) {
+            const f32x2 v01 = e4m3x2_to_f32<false>(vwa[i]);
+            const f32x2 v23 = e4m3x2_to_f32<true>(vwa[i]);
+            vf[4 * i] = v01.x; vf[4 * i + 1] = v01.y; vf[4 * i + 2] = v23.x; vf[4 * i + 3] = v23.y;
+            if constexpr (kBf16Dot) {
+              kp[2 * i] = e4m3x2_to_bf16x2<false>(kwa[i]);
+              kp[2 * i + 1] = e4m3x2_to_bf16x2<true>(kwa[i]);
+            } else {
+              const f32x2 k01 = e4m3x2_to_f32<false>(kwa[i]);
+              const f32x2 k23 = e4m3x2_to_f32<true>(kwa[i]);
+              kf[4 * i] = k01.x; kf[4 * i + 1] = k01.y; kf[4 * i + 2] = k23.x; kf[4 * i + 3] = k23.y;
+            }
+          }
+        }
+
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+          float sc = 0.f;
+          if constexpr (kBf16Dot) {
+#pragma unroll
+            for (int i = 0; i < EPL / 2; ++i) sc = dot2_bf16(qr[h][i], kp[i], sc);
+          } else {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) sc = fmaf(qf[h][e], kf[e], sc);
+          }
+          sc = group_sum<LPR>(sc);
+          const float z = sc * a.scale_log2;
+          if (live && z > m[h] + kLazyRescale) {
+            const float alpha = __builtin_amdgcn_exp2f(m[h] - z);
+            l[h] *= alpha;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+            m[h] = z;
+          }
+          const float p = live ? __builtin_amdgcn_exp2f(z - m[h]) : 0.f;
+          l[h] += p;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+        }
+      }
+    };
+
+    // Two register sets: the next step's loads are in flight while the
+    // current step is folded in.
+    if (nsteps > 0) issue(0, ka, va, la);
+    for (int st = 0; st < nsteps; st += 2) {
+      if (st + 1 < nsteps) issue(st + 1, kb2, vb2, lb);
+      compute(ka, va, la);
+      if (st + 1 < nsteps) {
+        if (st + 2 < nsteps) issue(st + 2, ka, va, la);
+        compute(kb2, vb2, lb);
+      }
+    }
+
+    // Merge the RPW row-lanes that share a column chunk (same `sub`).
+#pragma unroll
+    for (int step = LPR; step < kWave; step <<= 1) {
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        const float mo = shfl_xor_t(m[h], step);
+        const float lo_ = shfl_xor_t(l[h], step);
+        const float mn = fmaxf(m[h], mo);
+        const float fa = m[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[h] - mn);
+        const float fb = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
+        l[h] = l[h] * fa + lo_ * fb;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const float ao = shfl_xor_t(acc[h][e], step);
+          acc[h][e] = acc[h][e] * fa + ao * fb;
+        }
+        m[h] = mn;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      m[h] = 0.f;
+      l[h] = __builtin_nanf("");
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = __builtin_nanf("");
+    }
+  }
+
+  if (grp != 0) return;
+  if (nsplit == 1) {
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      const float inv = a.v_scale / l[h];
+      float o[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = acc[h][e] * inv;
+      store_out<QT, EPL>(a.out, out_row + h * D + sub * EPL, o);
+    }
+    return;
+  }
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    const int64_t pr = ((int64_t)b * a.num_q_heads + h0 + h) * a.max_splits + s;
+    float* dst = a.ws_acc + pr * D + sub * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dst[e] = acc[h][e];
+    if (sub == 0) {
+      a.ws_m[pr] = m[h];
+      a.ws_l[pr] = l[h];
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Split phase, uniform-block form: used when every wave load of RPW rows (and
+// every step of 16 rows) lies inside one block, i.e. block_size >= 16 and a
+// row takes >= 64 bytes.  The physical id of a step is wave-uniform, so it
+// lives in a scalar register and every K/V load is one 16-byte vector load at
+// a scalar base plus a per-lane constant offset.  Only a split's first and
+// last steps can hold positions outside the visible range; they take a masked
+// path.  The lazy-rescale test runs once per head per step on the lane's
+// largest score of the step.
+template <int D, int GT, int KV, int QT>
+__global__ __launch_bounds__(64) void decode_split_uni_kernel(DecodeArgs a) {
+  constexpr int kElt = KV == PKV_F32 ? 4 : (KV == PKV_BF16 ? 2 : 1);
+  constexpr int kRowBytes = D * kElt;
+  static_assert(kRowBytes >= 64, "uniform form needs rows of at least 64 bytes");
+  constexpr int LPR = kRowBytes / 16;                      // lanes per row
+  constexpr int EPL = 16 / kElt;                           // elements per lane
+  constexpr int RPW = kWave / LPR;                         // rows per wave load
+  constexpr int U = 16 / RPW;                              // loads per 16-row step
+  constexpr int kStepRows = U * RPW;                       // == 16
+  constexpr bool kBf16Dot = (QT == PKV_BF16);
+  constexpr int QW = kBf16Dot ? EPL / 2 : EPL;
+
+  const int lane = threadIdx.x;
+  const int grp = lane / LPR;
+  const int sub = lane % LPR;
+
+  const int kvgroups = a.num_kv_heads * a.sub_groups;
+  int w = blockIdx.x;
+  const int s = w % a.max_splits;
+  w /= a.max_splits;
+  const int kvg = w % kvgroups;
+  const int b = w / kvgroups;
+  const int kvh = kvg / a.sub_groups;
+  const int h0 = kvh * a.group + (kvg % a.sub_groups) * GT;
+
+  const RowInfo span = row_info(a, b);
+  if (span.skip) return;
+  const int64_t out_row = ((int64_t)span.tok * a.num_q_heads + h0) * D;
+  if (!span.valid) {
+    if (grp == 0) {
+      float nanv[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) nanv[e] = __builtin_nanf("");
+      for (int h = 0; h < GT; ++h) {
+        if (s == 0) store_out<QT, EPL>(a.out, out_row + h * D + sub * EPL, nanv);
+        if (a.max_splits > 1) {
+          const int64_t pr = ((int64_t)b * a.num_q_heads + h0 + h) * a.max_splits + s;
+          float* dst = a.ws_acc + pr * D + sub * EPL;
+          for (int e = 0; e < EPL; ++e) dst[e] = nanv[e];
+          if (sub == 0) {
+            a.ws_m[pr] = 0.f;
+            a.ws_l[pr] = nanv[0];
+          }
+        }
+      }
+    }
+    return;
+  }
+  const int nsplit = ceil_div(span.nvis, a.split_blocks);
+  if (s >= nsplit) return;
+
+  const int blk_begin = span.first_blk + s * a.split_blocks;
+  const int nb = min(a.split_blocks, span.first_blk + span.nvis - blk_begin);
+  const int bs = 1 << a.bs_log2;
+
+  int tab = -1;
+  if (lane < nb) tab = a.bt[(int64_t)span.req * a.bt_stride + blk_begin + lane];
+  const bool bad = (lane < nb) && (tab < 0 || tab >= a.num_blocks);
+  const bool any_bad = __ballot(bad) != 0;
+
+  uint32_t qr[GT][QW];
+  float qf[GT][kBf16Dot ? 1 : EPL];
+  if constexpr (kBf16Dot) {
+    const uint4* qp = reinterpret_cast<const uint4*>(
+        reinterpret_cast<const uint16_t*>(a.q) + out_row + sub * EPL);
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+#pragma unroll
+      for (int i = 0; i < QW / 4; ++i) {
+        const uint4 t = qp[h * (D * 2 / 16) + i];
+        qr[h][4 * i] = t.x; qr[h][4 * i + 1] = t.y; qr[h][4 * i + 2] = t.z; qr[h][4 * i + 3] = t.w;
+      }
+    }
+  } else {
+    const float* qp = reinterpret_cast<const float*>(a.q) + out_row + sub * EPL;
+#pragma unroll
+    for (int h = 0; h < GT; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qf[h][e] = qp[h * D + e];
+  }
+  (void)qr;
+  (void)qf;
+  // The query and block-table loads must be complete before the pipelined
+  // loop; otherwise the wait-count tracking cannot tell them apart from the
+  // prefetched K/V loads and waits for everything at the top of each step.
+  __builtin_amdgcn_s_waitcnt(0);
+
+  float m[GT], l[GT], acc[GT][EPL];
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+
+  if (!any_bad) {
+    const int steps_per_block = bs / kStepRows;
+    const int nsteps = nb * steps_per_block;
+    const int64_t blk_bytes = a.block_stride * kElt;
+    const int row_bytes = a.num_kv_heads * kRowBytes;      // one token of all KV heads
+    // per-lane byte offset inside a 16-row step (fits 32 bits: a block is
+    // at most 32 rows x 64 heads x 512 bytes)
+    const uint32_t lane_off = (uint32_t)((grp * a.num_kv_heads + kvh) * kRowBytes + sub * 16);
+    const int pos_base = blk_begin << a.bs_log2;
+
+    auto issue = [&](int st, uint4 (&kd)[U], uint4 (&vd)[U]) {
+      const int blk = st / steps_per_block;
+      const int r0 = (st - blk * steps_per_block) * kStepRows;
+      const int phys = __builtin_amdgcn_readlane(tab, blk);
+      const int64_t off = (int64_t)phys * blk_bytes + (int64_t)r0 * row_bytes;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        // wave-uniform base (scalar registers) + 32-bit lane offset
+        const char* kp = a.kbase + off + (int64_t)u * RPW * row_bytes;
+        const char* vp = a.vbase + off + (int64_t)u * RPW * row_bytes;
+        kd[u] = *reinterpret_cast<const uint4*>(kp + lane_off);
+        vd[u] = *reinterpret_cast<const uint4*>(vp + lane_off);
+      }
+    };
+
+    auto compute = [&](auto full_tag, int st, const uint4 (&kd)[U], const uint4 (&vd)[U]) {
+      constexpr bool full = decltype(full_tag)::value;
+      const int p0 = pos_base + st * kStepRows;                 // first row of the step
+      float z[U][GT];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t kwa[4] = {kd[u].x, kd[u].y, kd[u].z, kd[u].w};
+        uint32_t kp[kBf16Dot ? EPL / 2 : 1];
+        float kf[kBf16Dot ? 1 : EPL];
+        (void)kp;
+        (void)kf;
+        if constexpr (KV == PKV_BF16) {
+#pragma unroll
+          for (int i = 0; i < EPL / 2; ++i) {
+            if constexpr (kBf16Dot) kp[i] = kwa[i];
+            else { kf[2 * i] = bf16_lo(kwa[i]); kf[2 * i + 1] = bf16_hi(kwa[i]); }
+          }
+        } else if constexpr (KV == PKV_F32) {
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) kf[i] = as_float(kwa[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < EPL / 4; ++i) {
+            if constexpr (kBf16Dot) {
+              kp[2 * i] = e4m3x2_to_bf16x2<false>(kwa[i]);
+              kp[2 * i + 1] = e4m3x2_to_bf16x2<true>(kwa[i]);
+            } else {
+              const f32x2 k01 = e4m3x2_to_f32<false>(kwa[i]);
+              const f32x2 k23 = e4m3x2_to_f32<true>(kwa[i]);
+              kf[4 * i] = k01.x; kf[4 * i + 1] = k01.y; kf[4 * i + 2] = k23.x; kf[4 * i + 3] = k23.y;
+            }
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+          float sc = 0.f;
+          if constexpr (kBf16Dot) {
+#pragma unroll
+            for (int i = 0; i < EPL / 2; ++i) sc = dot2_bf16(qr[h][i], kp[i], sc);
+          } else {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) sc = fmaf(qf[h][e], kf[e], sc);
+          }
+          z[u][h] = sc;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int h = 0; h < GT; ++h) z[u][h] = group_sum<LPR>(z[u][h]) * a.scale_log2;
+
+      bool live[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int pos = p0 + u * RPW + grp;
+        live[u] = full || (pos >= span.lo && pos <= span.hi);
+        if (!live[u]) {
+#pragma unroll
+          for (int h = 0; h < GT; ++h) z[u][h] = -INFINITY;
+        }
+      }
+
+      // V rows in compute form; masked rows are zeroed so that stale or
+      // poisoned bytes never reach the accumulators.
+      float vf[U][EPL];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t vwa[4] = {vd[u].x, vd[u].y, vd[u].z, vd[u].w};
+        if constexpr (KV == PKV_BF16) {
+#pragma unroll
+          for (int i = 0; i < EPL / 2; ++i) { vf[u][2 * i] = bf16_lo(vwa[i]); vf[u][2 * i + 1] = bf16_hi(vwa[i]); }
+        } else if constexpr (KV == PKV_F32) {
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) vf[u][i] = as_float(vwa[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < EPL / 4; ++i) {
+            const f32x2 v01 = e4m3x2_to_f32<false>(vwa[i]);
+            const f32x2 v23 = e4m3x2_to_f32<true>(vwa[i]);
+            vf[u][4 * i] = v01.x; vf[u][4 * i + 1] = v01.y; vf[u][4 * i + 2] = v23.x; vf[u][4 * i + 3] = v23.y;
+          }
+        }
+        if (!full) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) vf[u][e] = live[u] ? vf[u][e] : 0.f;
+        }
+      }
+
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        float zmax = z[0][h];
+#pragma unroll
+        for (int u = 1; u < U; ++u) zmax = fmaxf(zmax, z[u][h]);
+        if (zmax > m[h] + kLazyRescale) {
+          const float alpha = __builtin_amdgcn_exp2f(m[h] - zmax);
+          l[h] *= alpha;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+          m[h] = zmax;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          // a lane whose rows are all masked keeps m = -inf; its p must be 0
+          const float p = (full || live[u]) ? __builtin_amdgcn_exp2f(z[u][h] - m[h]) : 0.f;
+          l[h] += p;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vf[u][e], acc[h][e]);
+        }
+      }
+    };
+
+    // Steps whose 16 rows are all visible skip every mask.
+    auto step_is_full = [&](int st) {
+      const int p0 = pos_base + st * kStepRows;
+      return p0 >= span.lo && p0 + kStepRows - 1 <= span.hi;
+    };
+    auto run = [&](int st, const uint4 (&kd)[U], const uint4 (&vd)[U]) {
+      if (step_is_full(st)) compute(std::true_type{}, st, kd, vd);
+      else compute(std::false_type{}, st, kd, vd);
+    };
+
+    // Loads are issued unconditionally, one step ahead; past the end the last
+    // step is fetched again (an L2 hit).  A branch around a prefetch would
+    // make the wait-count tracking merge two paths and wait for everything.
+    uint4 ka[U], va[U], kb2[U], vb2[U];
+    const int last = nsteps - 1;
+    issue(0, ka, va);
+    for (int st = 0; st < nsteps; st += 2) {
+      issue(min(st + 1, last), kb2, vb2);
+      run(st, ka, va);
+      issue(min(st + 2, last), ka, va);
+      if (st + 1 < nsteps) run(st + 1, kb2, vb2);
+    }
+
+#pragma unroll
+    for (int step = LPR; step < kWave; step <<= 1) {
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        const float mo = shfl_xor_t(m[h], step);
+        const float lo_ = shfl_xor_t(l[h], step);
+        const float mn = fmaxf(m[h], mo);
+        const float fa = m[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[h] - mn);
+        const float fb = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
+        l[h] = l[h] * fa + lo_ * fb;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const float ao = shfl_xor_t(acc[h][e], step);
+          acc[h][e] = acc[h][e] * fa + ao * fb;
+        }
+        m[h] = mn;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      m[h] = 0.f;
+      l[h] = __builtin_nanf("");
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = __builtin_nanf("");
+    }
+  }
+
+  if (grp != 0) return;
+  if (nsplit == 1) {
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      const float inv = a.v_scale / l[h];
+      float o[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = acc[h][e] * inv;
+      store_out<QT, EPL>(a.out, out_row + h * D + sub * EPL, o);
+    }
+    return;
+  }
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    const int64_t pr = ((int64_t)b * a.num_q_heads + h0 + h) * a.max_splits + s;
+    float* dst = a.ws_acc + pr * D + sub * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dst[e] = acc[h][e];
+    if (sub == 0) {
+      a.ws_m[pr] = m[h];
+      a.ws_l[pr] = l[h];
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Balanced split phase on the matrix cores, one load pipeline per worker.
+//
+// Work units are (row, KV-head group, visible block), ordered row-major.  The
+// grid is a fixed number of single-wave workers, one per SIMD (a second wave
+// on a SIMD loses instruction issue to the older one and lags it by a fifth,
+// so equal shares would finish unequally); worker w takes the contiguous units
+// [w P, (w + 1) P) with P = max(ceil(U / workers), min_units).  Each stretch
+// of a worker's range that belongs to one (row, head group) is a "piece": it
+// is folded with an online softmax and written either as the final output
+// (when the piece covers the whole row) or as a partial (m, l, acc) in slot
+// `piece` of that row, with the piece count stored for the combine kernel.
+//
+// A worker streams its range as one load pipeline that runs across piece
+// boundaries.  Before any K/V load, lane i resolves unit wbase + i of a
+// 64-unit window (its row through the prefix sums, the row's visible span,
+// the block-table entry, the KV head) into registers, and the query rows of
+// every piece that starts in the window are staged in LDS; the loop then
+// reads the physical block of each step with one lane read, and crossing
+// into the next piece costs an LDS read instead of a wait on memory.
+//
+// Scores of a 16-token step are one chain of 16x16x32 bf16 MFMAs,
+// S[q head][token] = Q . K^T: Q is the A operand (rows = query heads of the
+// item, unused rows zero) and K rows load straight into the B operand (lane l:
+// token l % 16, 8 consecutive elements from 32c + 8 (l / 16)).  The running
+// max of every head is wave-uniform (a 16-lane max of S read into a scalar
+// register), so one scalar test per head and step decides the lazy rescale.
+// P.V stays on the vector ALUs in fp32: lane L = VLPR g + sub holds
+// V[token u VRPW + g][sub VEPL ..] and fetches that token's probability with
+// a lane permute.  Requirements: bf16 or fp8 cache, bf16 query, head_dim % 32
+// == 0, row of at least 64 bytes, block size a multiple of 16, at most 16
+// query heads per item.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int D, int GT, int KV>
+struct MfmaShape {
+  static constexpr int kElt = KV == PKV_BF16 ? 2 : 1;
+  static constexpr int NC = D / 32;                  // MFMA k-chunks
+  static constexpr int VLPR = D * kElt / 16;         // V: lanes per row
+  static constexpr int VRPW = kWave / VLPR;          // V: rows per load
+  static constexpr int VU = 16 / VRPW;               // V: loads per 16-token step
+  static constexpr int VEPL = 16 / kElt;             // V: elements per lane
+  static constexpr int KB = 8 * kElt;                // K: bytes per lane per chunk
+  static constexpr int RG = (GT + 3) / 4;            // MFMA row groups in use
+  static constexpr int QE = GT * D;                  // query elements of one piece
+  static constexpr int QL = (QE + 8 * kWave - 1) / (8 * kWave);  // 16-byte loads per lane
+  static_assert(VRPW <= 16 && VU * VRPW == 16, "V layout");
+  static_assert(GT <= 16, "at most 16 query heads per item");
+};
+
+// LDS layout of the balanced kernel (dynamic shared memory, 16-byte aligned
+// sections): prefix sums cum[rows + 1]; per-row records {req, tok, lo, hi}
+// when rows <= kRowRecRows; query rows of up to qslots pieces.
+constexpr int kRowRecRows = 1024;
+
+struct FlatLds {
+  int cum_off, rec_off, q_off, qslots;
+  size_t bytes;
+};
+
+__host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+__host__ __device__ inline FlatLds flat_lds_layout(int rows, int gt, int d) {
+  FlatLds l;
+  l.cum_off = 0;
+  size_t off = align16(((size_t)rows + 1) * sizeof(int));
+  l.rec_off = (int)off;
+  if (rows <= kRowRecRows) off += align16((size_t)rows * 4 * sizeof(int));
+  l.q_off = (int)off;
+  const size_t per = (size_t)gt * d * 2;
+  int slots = (int)((16384 + per - 1) / per);      // about 16 KiB of staged queries
+  if (slots > kWave) slots = kWave;
+  if (slots < 2) slots = 2;
+  l.qslots = slots;
+  l.bytes = off + (size_t)slots * per;
+  return l;
+}
+
+template <int D, int GT, int KV, int DEPTH>
+__global__ __launch_bounds__(64) void decode_flat_kernel(DecodeArgs a) {
+  using S = MfmaShape<D, GT, KV>;
+  constexpr int NC = S::NC, VLPR = S::VLPR, VRPW = S::VRPW, VU = S::VU, VEPL = S::VEPL;
+  constexpr int KB = S::KB, RG = S::RG, kElt = S::kElt, QE = S::QE, QL = S::QL;
+  static_assert(DEPTH >= 1 && DEPTH <= 2, "prefetch depth");
+  extern __shared__ __align__(16) char lds[];
+  const FlatLds L = flat_lds_layout(a.num_rows, GT, D);
+  int* cum = reinterpret_cast<int*>(lds + L.cum_off);     // cum[r]: visible blocks of rows < r
+  int4* rrec = reinterpret_cast<int4*>(lds + L.rec_off);  // {req, tok, lo, hi}
+  uint16_t* qst = reinterpret_cast<uint16_t*>(lds + L.q_off);
+  const bool have_rec = a.num_rows <= kRowRecRows;
+  const int lane = threadIdx.x;
+  const int kvgroups = a.num_kv_heads * a.sub_groups;
+
+  // ---- visible blocks per row, prefix sums (and row records) in LDS
+  int carry = 0;
+  for (int r0 = 0; r0 < a.num_rows; r0 += kWave) {
+    const int r = r0 + lane;
+    int nv = 0;
+    if (r < a.num_rows) {
+      const RowInfo ri = row_info(a, r);
+      nv = (!ri.skip && ri.valid) ? ri.nvis : 0;
+      if (have_rec) rrec[r] = make_int4(ri.req, ri.tok, ri.lo, ri.hi);
+    }
+    int incl = nv;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    if (r < a.num_rows) cum[r] = carry + incl - nv;
+    carry += __shfl(incl, kWave - 1);
+  }
+  if (lane == 0) cum[a.num_rows] = carry;
+  __syncthreads();
+
+  const long long U = (long long)carry * kvgroups;
+  const int W = gridDim.x;
+  long long P = (U + W - 1) / W;
+  if (P < a.split_blocks) P = a.split_blocks;
+  const long long u_lo = min(U, (long long)blockIdx.x * P);
+  const long long u_hi = min(U, u_lo + P);
+
+  const int spb_log2 = a.bs_log2 - 4;                     // 16-token steps per block
+  const int64_t blk_bytes = a.block_stride * kElt;
+  const int row_bytes = a.num_kv_heads * D * kElt;          // one token, all KV heads
+  const int vg = lane / VLPR, vsub = lane % VLPR;
+  const uint32_t k_lane = (uint32_t)((lane % 16) * row_bytes + (lane / 16) * KB);
+  const uint32_t v_lane = (uint32_t)(vg * row_bytes + vsub * 16);
+
+  // one lane's unit record
+  int rec_phys = -1, rec_hoff = 0, rec_gid = -1, rec_pos0 = 0, rec_lo = 0, rec_hi = -1, rec_tok = 0;
+
+  // running piece
+  int cur = -1, s_lo = 0, s_hi = -1, s_tok = 0, s_ord = 0;
+  long long s_first = 0;
+  bool s_bad = false;
+  bf16x8_t qa[NC];
+  float acc[GT][VEPL];
+  float m[GT];
+  f32x4_t lsum = {0.f, 0.f, 0.f, 0.f};
+
+  // first query element of the piece (gid = row * kvgroups + head group)
+  auto q_elem = [&](int gid, int tok) __attribute__((always_inline)) -> int64_t {
+    const int kvg = gid % kvgroups;
+    const int h0 = (kvg / a.sub_groups) * a.group + (kvg % a.sub_groups) * GT;
+    return ((int64_t)tok * a.num_q_heads + h0) * D;
+  };
+  // A operand of the piece's query rows: lane l takes row l % 16, elements
+  // 32 c + 8 (l / 16) .. + 8 (rows past GT are zero)
+  auto q_from_lds = [&](int slot) __attribute__((always_inline)) {
+    const int row = lane % 16;
+    const uint16_t* src = qst + (size_t)slot * QE + row * D + 8 * (lane / 16);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      uint4 t = make_uint4(0, 0, 0, 0);
+      if (row < GT) t = *reinterpret_cast<const uint4*>(src + 32 * c);
+      qa[c] = __builtin_bit_cast(bf16x8_t, t);
+    }
+  };
+  auto q_from_global = [&](int64_t qe) __attribute__((always_inline)) {
+    const int row = lane % 16;
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(a.q) + qe + row * D + 8 * (lane / 16);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      uint4 t = make_uint4(0, 0, 0, 0);
+      if (row < GT) t = *reinterpret_cast<const uint4*>(src + 32 * c);
+      qa[c] = __builtin_bit_cast(bf16x8_t, t);
+    }
+    // settle here, so that no wait for these loads lands inside the loop
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      uint4 t = __builtin_bit_cast(uint4, qa[c]);
+      asm volatile("" : "+v"(t.x), "+v"(t.y), "+v"(t.z), "+v"(t.w));
+      qa[c] = __builtin_bit_cast(bf16x8_t, t);
+    }
+  };
+  auto start = [&](int unit, int gid) __attribute__((always_inline)) {
+    cur = gid;
+    s_lo = __builtin_amdgcn_readlane(rec_lo, unit);
+    s_hi = __builtin_amdgcn_readlane(rec_hi, unit);
+    s_tok = __builtin_amdgcn_readlane(rec_tok, unit);
+    s_bad = false;
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      m[h] = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < VEPL; ++e) acc[h][e] = 0.f;
+    }
+    lsum[0] = lsum[1] = lsum[2] = lsum[3] = 0.f;
+  };
+  auto flush = [&]() __attribute__((always_inline)) {
+    const int b = cur / kvgroups;
+    const int kvg = cur % kvgroups;
+    const int h0 = (kvg / a.sub_groups) * a.group + (kvg % a.sub_groups) * GT;
+    const int nv = cum[b + 1] - cum[b];
+    const long long seg_base = (long long)cum[b] * kvgroups + (long long)kvg * nv;
+    const int piece = (int)(s_first / P - seg_base / P);
+    const int npieces = (int)((seg_base + nv - 1) / P - seg_base / P + 1);
+    if (s_bad) {
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        m[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEPL; ++e) acc[h][e] = __builtin_nanf("");
+      }
+      lsum[0] = lsum[1] = lsum[2] = lsum[3] = __builtin_nanf("");
+    }
+    // the V layout's token groups hold partial sums under the same maxima
+#pragma unroll
+    for (int step = VLPR; step < kWave; step <<= 1)
+#pragma unroll
+      for (int h = 0; h < GT; ++h)
+#pragma unroll
+        for (int e = 0; e < VEPL; ++e) acc[h][e] += shfl_xor_t(acc[h][e], step);
+    float lt[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lt[i] = group_sum<16>(lsum[i]);
+    float lh[GT];
+#pragma unroll
+    for (int h = 0; h < GT; ++h)
+      lh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lt[h % 4]), 16 * (h / 4)));
+    const int64_t out_row = ((int64_t)s_tok * a.num_q_heads + h0) * D;
+    if (vg == 0) {
+      if (npieces == 1) {
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+          const float inv = a.v_scale / lh[h];
+          float o[VEPL];
+#pragma unroll
+          for (int e = 0; e < VEPL; ++e) o[e] = acc[h][e] * inv;
+          store_out<PKV_BF16, VEPL>(a.out, out_row + h * D + vsub * VEPL, o);
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+          const int64_t pr = ((int64_t)b * a.num_q_heads + h0 + h) * a.max_splits + piece;
+          float* dst = a.ws_acc + pr * D + vsub * VEPL;
+#pragma unroll
+          for (int e = 0; e < VEPL; ++e) dst[e] = acc[h][e];
+          if (vsub == 0) {
+            a.ws_m[pr] = m[h];
+            a.ws_l[pr] = lh[h];
+          }
+        }
+      }
+    }
+    if (piece == 0 && lane == 0) a.ws_np[(int64_t)b * kvgroups + kvg] = npieces;
+  };
+
+  struct Buf {
+    uint32_t k[NC][KB / 4];
+    uint4 v[VU];
+  };
+
+  for (long long wbase = u_lo; wbase < u_hi; wbase += kWave) {
+    const int nunits = (int)min((long long)kWave, u_hi - wbase);
+    // ---- unit records of this window
+    rec_phys = -1; rec_gid = -1;
+    if (lane < nunits) {
+      const long long u = wbase + lane;
+      int lo = 0, hi = a.num_rows;            // largest b with cum[b] * kvgroups <= u
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((long long)cum[mid] * kvgroups <= u) lo = mid; else hi = mid;
+      }
+      const int b = lo;
+      const int nv = cum[b + 1] - cum[b];
+      const long long rel = u - (long long)cum[b] * kvgroups;
+      const int kvg = (int)(rel / nv);
+      const int j = (int)(rel - (long long)kvg * nv);
+      int req, tok, klo, khi;
+      if (have_rec) {
+        const int4 rr = rrec[b];
+        req = rr.x; tok = rr.y; klo = rr.z; khi = rr.w;
+      } else {
+        const RowInfo ri = row_info(a, b);
+        req = ri.req; tok = ri.tok; klo = ri.lo; khi = ri.hi;
+      }
+      const int first_blk = klo >> a.bs_log2;
+      const int t = a.bt[(int64_t)req * a.bt_stride + first_blk + j];
+      rec_phys = (t >= 0 && t < a.num_blocks) ? t : -1;
+      rec_hoff = (kvg / a.sub_groups) * D * kElt;
+      rec_gid = b * kvgroups + kvg;
+      rec_pos0 = (first_blk + j) << a.bs_log2;
+      rec_lo = klo;
+      rec_hi = khi;
+      rec_tok = tok;
+    }
+    // ---- query rows of the pieces that start in this window (slot = order
+    // of the piece in the window; the window's first unit always opens slot 0)
+    const int gprev = __shfl_up(rec_gid, 1);
+    unsigned long long starts = __ballot(lane < nunits && (lane == 0 || rec_gid != gprev));
+    const int nstage = min(__popcll(starts), L.qslots);
+    {
+      uint4 qv[4][QL];
+      unsigned long long sm = starts;
+      for (int s0 = 0; s0 < nstage; s0 += 4) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if (s0 + k < nstage) {
+            const int ln = __builtin_ctzll(sm);
+            sm &= sm - 1;
+            const int64_t qe = q_elem(__builtin_amdgcn_readlane(rec_gid, ln),
+                                      __builtin_amdgcn_readlane(rec_tok, ln));
+            const uint16_t* src = reinterpret_cast<const uint16_t*>(a.q) + qe;
+#pragma unroll
+            for (int i = 0; i < QL; ++i) {
+              const int e = (i * kWave + lane) * 8;
+              qv[k][i] = e < QE ? *reinterpret_cast<const uint4*>(src + e) : make_uint4(0, 0, 0, 0);
+            }
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if (s0 + k < nstage) {
+#pragma unroll
+            for (int i = 0; i < QL; ++i) {
+              const int e = (i * kWave + lane) * 8;
+              if (e < QE) *reinterpret_cast<uint4*>(qst + (size_t)(s0 + k) * QE + e) = qv[k][i];
+            }
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" : "+v"(rec_phys), "+v"(rec_gid), "+v"(rec_hoff), "+v"(rec_pos0),
+                 "+v"(rec_lo), "+v"(rec_hi), "+v"(rec_tok));
+    const int g0 = __builtin_amdgcn_readfirstlane(rec_gid);
+    s_ord = 0;
+    if (g0 != cur) {
+      if (cur >= 0) flush();
+      start(0, g0);
+      s_first = wbase;
+      q_from_lds(0);
+    }
+
+    const int nsteps = nunits << spb_log2;
+    const int last = nsteps - 1;
+    const int smask = (1 << spb_log2) - 1;
+
+    auto issue = [&](int st, Buf& bf) __attribute__((always_inline)) {
+      const int unit = st >> spb_log2;
+      const int r0 = (st & smask) * 16;
+      int phys = __builtin_amdgcn_readlane(rec_phys, unit);
+      const int hoff = __builtin_amdgcn_readlane(rec_hoff, unit);
+      phys = phys < 0 ? 0 : phys;             // flagged at the fold; block 0 is always mapped
+      const int64_t off = (int64_t)phys * blk_bytes + hoff + (int64_t)r0 * row_bytes;
+      const char* kp = a.kbase + off;
+      const char* vp = a.vbase + off;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        if constexpr (KB == 16) {
+          const uint4 t = *reinterpret_cast<const uint4*>(kp + k_lane + c * 32 * kElt);
+          bf.k[c][0] = t.x; bf.k[c][1] = t.y; bf.k[c][2] = t.z; bf.k[c][3] = t.w;
+        } else {
+          const uint2 t = *reinterpret_cast<const uint2*>(kp + k_lane + c * 32 * kElt);
+          bf.k[c][0] = t.x; bf.k[c][1] = t.y;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < VU; ++u)
+        bf.v[u] = *reinterpret_cast<const uint4*>(vp + v_lane + (int64_t)u * VRPW * row_bytes);
+    };
+
+    auto body = [&](auto full_tag, int p0, const Buf& bf) __attribute__((always_inline)) {
+      constexpr bool full = decltype(full_tag)::value;
+      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        uint4 kw;
+        if constexpr (KB == 16) {
+          kw = make_uint4(bf.k[c][0], bf.k[c][1], bf.k[c][2], bf.k[c][3]);
+        } else {
+          kw = make_uint4(e4m3x2_to_bf16x2<false>(bf.k[c][0]), e4m3x2_to_bf16x2<true>(bf.k[c][0]),
+                          e4m3x2_to_bf16x2<false>(bf.k[c][1]), e4m3x2_to_bf16x2<true>(bf.k[c][1]));
+        }
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[c], __builtin_bit_cast(bf16x8_t, kw), sc, 0, 0, 0);
+      }
+      float z[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[i] = sc[i] * a.scale_log2;
+      if constexpr (!full) {
+        const int pos = p0 + (lane % 16);
+        if (pos < s_lo || pos > s_hi) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) z[i] = -INFINITY;
+        }
+      }
+      float mx[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = z[i];
+        v = fmaxf(v, dpp<kDppQuadXor1>(v));
+        v = fmaxf(v, dpp<kDppQuadXor2>(v));
+        v = fmaxf(v, dpp<kDppRowHalfMirror>(v));
+        v = fmaxf(v, dpp<kDppRowMirror>(v));
+        mx[i] = v;
+      }
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        const float mb = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+            __builtin_bit_cast(int, mx[h % 4]), 16 * (h / 4)));
+        if (mb > m[h] + kLazyRescale) {
+          const float alpha = __builtin_amdgcn_exp2f(m[h] - mb);   // 0 when m = -inf
+#pragma unroll
+          for (int e = 0; e < VEPL; ++e) acc[h][e] *= alpha;
+          if (lane / 16 == h / 4) lsum[h % 4] *= alpha;
+          m[h] = mb;
+        }
+      }
+      float pr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float mv = m[i < GT ? i : 0];
+#pragma unroll
+        for (int r = 1; r < RG; ++r)
+          if (lane / 16 == r && 4 * r + i < GT) mv = m[4 * r + i];
+        float pv = __builtin_amdgcn_exp2f(z[i] - mv);
+        if constexpr (!full) pv = z[i] == -INFINITY ? 0.f : pv;
+        pr[i] = pv;
+        lsum[i] += pv;
+      }
+#pragma unroll
+      for (int u = 0; u < VU; ++u) {
+        const int tok = u * VRPW + vg;                // token inside the step
+        const uint32_t vwa[4] = {bf.v[u].x, bf.v[u].y, bf.v[u].z, bf.v[u].w};
+        float vf[VEPL];
+        if constexpr (KV == PKV_BF16) {
+#pragma unroll
+          for (int i = 0; i < VEPL / 2; ++i) { vf[2 * i] = bf16_lo(vwa[i]); vf[2 * i + 1] = bf16_hi(vwa[i]); }
+        } else {
+#pragma unroll
+          for (int i = 0; i < VEPL / 4; ++i) {
+            const f32x2 v01 = e4m3x2_to_f32<false>(vwa[i]);
+            const f32x2 v23 = e4m3x2_to_f32<true>(vwa[i]);
+            vf[4 * i] = v01.x; vf[4 * i + 1] = v01.y; vf[4 * i + 2] = v23.x; vf[4 * i + 3] = v23.y;
+          }
+        }
+        if constexpr (!full) {
+          const int pos = p0 + tok;
+          const bool live = pos >= s_lo && pos <= s_hi;
+#pragma unroll
+          for (int e = 0; e < VEPL; ++e) vf[e] = live ? vf[e] : 0.f;
+        }
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+          const int src = (tok + 16 * (h / 4)) * 4;
+          const float ph = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+              src, __builtin_bit_cast(int, pr[h % 4])));
+#pragma unroll
+          for (int e = 0; e < VEPL; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
+        }
+      }
+    };
+
+    auto run = [&](int st, const Buf& bf) __attribute__((always_inline)) {
+      const int unit = st >> spb_log2;
+      const int gid = __builtin_amdgcn_readlane(rec_gid, unit);
+      if (gid != cur) {                        // next piece of the window
+        flush();
+        start(unit, gid);
+        s_first = wbase + unit;
+        ++s_ord;
+        if (s_ord < nstage) q_from_lds(s_ord);
+        else q_from_global(q_elem(gid, s_tok));
+      }
+      s_bad |= __builtin_amdgcn_readlane(rec_phys, unit) < 0;
+      const int p0 = __builtin_amdgcn_readlane(rec_pos0, unit) + (st & smask) * 16;
+      if (p0 >= s_lo && p0 + 15 <= s_hi) body(std::true_type{}, p0, bf);
+      else body(std::false_type{}, p0, bf);
+    };
+
+    // loads run DEPTH steps ahead, unconditionally (past the end the last
+    // step is fetched again, an L2 hit), so the wait counts stay static
+    if constexpr (DEPTH == 2) {
+      Buf b0, b1, b2;
+      issue(0, b0);
+      issue(min(1, last), b1);
+      for (int st = 0; st < nsteps; st += 3) {
+        issue(min(st + 2, last), b2);
+        run(st, b0);
+        issue(min(st + 3, last), b0);
+        if (st + 1 < nsteps) run(st + 1, b1);
+        issue(min(st + 4, last), b1);
+        if (st + 2 < nsteps) run(st + 2, b2);
+      }
+    } else {
+      Buf b0, b1;
+      issue(0, b0);
+      for (int st = 0; st < nsteps; st += 2) {
+        issue(min(st + 1, last), b1);
+        run(st, b0);
+        issue(min(st + 2, last), b0);
+        if (st + 1 < nsteps) run(st + 1, b1);
+      }
+    }
+  }
+  if (cur >= 0) flush();
+
+  // ---- rows that cannot be computed: NaN output, written by one worker each
+  for (int r = blockIdx.x; r < a.num_rows; r += W) {
+    const RowInfo ri = row_info(a, r);
+    if (ri.skip || ri.valid) continue;
+    const int64_t base = (int64_t)ri.tok * a.num_q_heads * D;
+    for (int e = lane; e < a.num_q_heads * D; e += kWave)
+      reinterpret_cast<uint16_t*>(a.out)[base + e] = 0x7FC0;
+    for (int g = lane; g < kvgroups; g += kWave) a.ws_np[(int64_t)r * kvgroups + g] = 0;
+  }
+}
+
+// --------------------------------------------------------------------------
+// Combine phase: one wave per (row, query head) with more than one split.
+template <int D, int OT>
+__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
+  constexpr int PER = D >= kWave ? D / kWave : 1;  // elements per lane
+  const int lane = threadIdx.x;
+  const int h = blockIdx.x % a.num_q_heads;
+  const int b = blockIdx.x / a.num_q_heads;
+  // Rows the split phase rejected hold NaN in every split slot; the split
+  // count is clamped to the slots that exist.
+  const RowInfo span = row_info(a, b);
+  if (span.skip || !span.valid) return;
+  const int tok = span.tok;
+  int nsplit;
+  if (a.stream) {   // rows the split phase rejected have a piece count of 0
+    const int groups = a.num_q_heads / a.heads_per_item;
+    nsplit = a.ws_np[(int64_t)b * groups + h / a.heads_per_item];
+  } else {
+    nsplit = ceil_div(span.nvis, a.split_blocks);
+  }
+  nsplit = min(nsplit, a.max_splits);
+  if (nsplit <= 1) return;
+
+  const int64_t pr0 = ((int64_t)b * a.num_q_heads + h) * a.max_splits;
+  float M = -INFINITY;
+  for (int s = lane; s < nsplit; s += kWave) M = fmaxf(M, a.ws_m[pr0 + s]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+
+  float den = 0.f;
+  float num[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) num[i] = 0.f;
+  const bool active = D >= kWave || lane < D;
+  for (int s = 0; s < nsplit; ++s) {
+    const float ms = a.ws_m[pr0 + s];
+    const float wgt = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+    den = fmaf(wgt, a.ws_l[pr0 + s], den);
+    if (active) {
+      const float* src = a.ws_acc + (pr0 + s) * D;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) num[i] = fmaf(wgt, src[lane + i * kWave], num[i]);
+    }
+  }
+  if (!active) return;
+  const float inv = a.v_scale / den;
+  const int64_t out_row = ((int64_t)tok * a.num_q_heads + h) * D;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    float v[1] = {num[i] * inv};
+    store_out<OT, 1>(a.out, out_row + lane + i * kWave, v);
+  }
+}
+
+// ---- launch templates, one instantiation set per (head_dim, KV dtype)
+template <int D, int GT, int KV, int QT>
+void launch_split(const DecodeArgs& a, hipStream_t s) {
+  const long long kvgroups = (long long)a.num_kv_heads * a.sub_groups;
+  const dim3 grid((unsigned)((long long)a.num_rows * kvgroups * a.max_splits));
+  constexpr int kRowBytes = D * (KV == PKV_F32 ? 4 : (KV == PKV_BF16 ? 2 : 1));
+  if constexpr (kRowBytes >= 64) {
+    if ((1 << a.bs_log2) >= 16) {
+      decode_split_uni_kernel<D, GT, KV, QT><<<grid, 64, 0, s>>>(a);
+      return;
+    }
+  }
+  decode_split_kernel<D, GT, KV, QT><<<grid, 64, 0, s>>>(a);
+}
+
+// Fixed splits (vector ALUs), `gt` query heads per work item.
+template <int D, int KV>
+int run_split_dk(const DecodeArgs& a, int gt, hipStream_t s) {
+  constexpr int QT = KV == PKV_F32 ? PKV_F32 : PKV_BF16;
+  switch (gt) {
+    case 1: launch_split<D, 1, KV, QT>(a, s); return PKV_OK;
+    case 2: launch_split<D, 2, KV, QT>(a, s); return PKV_OK;
+    case 4: launch_split<D, 4, KV, QT>(a, s); return PKV_OK;
+    case 8: launch_split<D, 8, KV, QT>(a, s); return PKV_OK;
+  }
+  return PKV_ERR_UNSUPPORTED;
+}
+
+template <int D, int GT, int KV>
+void launch_stream(const DecodeArgs& a, int workers, hipStream_t s) {
+  const size_t lds = flat_lds_layout(a.num_rows, GT, D).bytes;
+  // loads two steps ahead; one where the registers run short (16 heads)
+  constexpr int kDepth = GT >= 16 ? 1 : 2;
+  if (a.kernel_variant == 2) decode_flat_kernel<D, GT, KV, 1><<<workers, 64, lds, s>>>(a);
+  else if (a.kernel_variant == 3) decode_flat_kernel<D, GT, KV, 2><<<workers, 64, lds, s>>>(a);
+  else decode_flat_kernel<D, GT, KV, kDepth><<<workers, 64, lds, s>>>(a);
+}
+
+// Balanced partition (matrix cores), a.heads_per_item query heads per item.
+template <int D, int KV>
+int run_stream_dk(const DecodeArgs& a, int workers, hipStream_t s) {
+  if constexpr (KV != PKV_F32 && D * (KV == PKV_BF16 ? 2 : 1) >= 64) {
+    switch (a.heads_per_item) {
+      case 1: launch_stream<D, 1, KV>(a, workers, s); return PKV_OK;
+      case 2: launch_stream<D, 2, KV>(a, workers, s); return PKV_OK;
+      case 4: launch_stream<D, 4, KV>(a, workers, s); return PKV_OK;
+      case 8: launch_stream<D, 8, KV>(a, workers, s); return PKV_OK;
+      case 16: launch_stream<D, 16, KV>(a, workers, s); return PKV_OK;
+    }
+  }
+  return PKV_ERR_UNSUPPORTED;
+}
+
+template <int D>
+int run_combine_d(const DecodeArgs& a, int ot, hipStream_t s) {
+  const dim3 grid((unsigned)((long long)a.num_rows * a.num_q_heads));
+  if (ot == PKV_F32) decode_combine_kernel<D, PKV_F32><<<grid, 64, 0, s>>>(a);
+  else decode_combine_kernel<D, PKV_BF16><<<grid, 64, 0, s>>>(a);
+  return PKV_OK;
+}
+
+// Every instantiation the host side calls; each source file decode_*.hip
+// instantiates its share, the host side declares them extern.
+#define PKV_DECODE_SPLIT_INST(EXT, D, KV) \
+  EXT template int run_split_dk<D, KV>(const DecodeArgs&, int, hipStream_t);
+#define PKV_DECODE_STREAM_INST(EXT, D, KV) \
+  EXT template int run_stream_dk<D, KV>(const DecodeArgs&, int, hipStream_t);
+#define PKV_DECODE_COMBINE_INST(EXT, D) \
+  EXT template int run_combine_d<D>(const DecodeArgs&, int, hipStream_t);
+#define PKV_DECODE_ALL_D(EXT, D)                  \
+  PKV_DECODE_SPLIT_INST(EXT, D, PKV_F32)          \
+  PKV_DECODE_SPLIT_INST(EXT, D, PKV_BF16)         \
+  PKV_DECODE_SPLIT_INST(EXT, D, PKV_FP8_E4M3)     \
+  PKV_DECODE_STREAM_INST(EXT, D, PKV_BF16)        \
+  PKV_DECODE_STREAM_INST(EXT, D, PKV_FP8_E4M3)    \
+  PKV_DECODE_COMBINE_INST(EXT, D)
+
+}  // namespace pkv
