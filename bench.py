@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--split-blocks", type=int, default=0, help="override the decode split (tuning)")
     p.add_argument("--variant", type=int, default=0, help="decode kernel variant (tuning)")
     p.add_argument("--workers", type=int, default=0, help="balanced-scheme workers (tuning)")
+    p.add_argument("--lead", type=int, default=-1, help="balanced scheme: full-share workers (tuning)")
+    p.add_argument("--trail-pct", type=int, default=0, help="balanced scheme: other share %% (tuning)")
     p.add_argument("--summarize-profiles", default="",
                    help="write profiles/ summaries from rocprofv3 output under this folder")
     p.add_argument("--calibration-copy", action="store_true",
@@ -214,7 +216,9 @@ def main():
     plan = pkv.decode_plan(w.num_reqs, w.num_q_heads, base.cache, w.max_seq_len)
     pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, base.cache, w.max_seq_len,
                   split_blocks=args.split_blocks or None, num_workers=args.workers or None,
-                  kernel_variant=args.variant)
+                  kernel_variant=args.variant,
+                  lead_workers=args.lead if args.lead >= 0 else None,
+                  trail_share_pct=args.trail_pct or None)
     ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
     out = torch.empty_like(base.q)
     slots = torch.empty(w.num_reqs, dtype=torch.int64, device=dev)
@@ -324,7 +328,8 @@ def main():
                    "block_size": w.block_size, "pool_blocks": nb, "rotating_pools": POOLS,
                    "context_tokens": int(w.seq_lens.sum()), "parallelism": "none (1 GPU)",
                    "scheme": int(plan.scheme), "workers": int(plan.num_workers),
-                   "split_blocks": int(plan.split_blocks), "max_splits": int(plan.max_splits)},
+                   "split_blocks": int(plan.split_blocks), "max_splits": int(plan.max_splits),
+                   "lead_workers": int(plan.lead_workers), "trail_share_pct": int(plan.trail_share_pct)},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_attention": {"split_kernel_us": round(split_ms * 1e3, 2),
                              "split_GBps": round(split_gbps, 1),

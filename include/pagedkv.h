@@ -177,13 +177,18 @@ typedef struct {
   int32_t max_splits;     /* partial slots per (row, query head)                  */
   int32_t heads_per_item; /* query heads one work item processes                  */
   int32_t kernel_variant; /* 0: the library's choice.  Tuning only: 1 = vector
-                             ALUs for the scores (scheme 0 only); 2, 3 =
-                             scheme 1 with K/V loads issued 1 or 2 steps
+                             ALUs for the scores (scheme 0 only); 2..5 =
+                             scheme 1 with K/V loads issued 1..4 steps
                              ahead.  Every variant computes the same result
                              up to rounding order.                           */
   size_t workspace_bytes; /* partial (acc, m, l) storage (+ piece counts)         */
   int32_t scheme;         /* 0 or 1, see above                                    */
   int32_t num_workers;    /* scheme 1: workers launched                           */
+  int32_t lead_workers;   /* scheme 1: the first lead_workers workers take a full
+                             share each, the others trail_share_pct percent of
+                             one (a second wave on a SIMD issues more slowly);
+                             0 = all shares equal                             */
+  int32_t trail_share_pct;/* scheme 1: 1..100, see lead_workers                   */
 } pkv_decode_plan;
 
 /*
@@ -240,9 +245,11 @@ PKV_API int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dtype
  * to `out` directly.  Phase 2 merges the splits of the remaining rows:
  *     out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s,  M = max_s m_s.
  * Both take the plan that pkv_decode_plan_make produced for these arguments.
- * Workspace layout (float32): acc [rows, Hq, max_splits, D], then
- * m [rows, Hq, max_splits], then l [rows, Hq, max_splits]; scheme 1 appends
- * int32 piece counts [rows, Hq / heads_per_item].
+ * Workspace layout (float32): acc [rows, Hq, max_splits, D], then for
+ * scheme 0 m [rows, Hq, max_splits] and l [rows, Hq, max_splits]; for
+ * scheme 1 (G = heads_per_item) records [rows, Hq / G, max_splits, 2, G]
+ * holding the G heads' m then their l, followed by int32 piece counts
+ * [rows, Hq / G].
  */
 PKV_API int pkv_paged_attention_decode_partials(void* out, const void* q,
                                         int32_t q_dtype, int32_t num_seqs,

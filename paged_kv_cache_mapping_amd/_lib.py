@@ -47,6 +47,8 @@ class PkvDecodePlan(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("scheme", ctypes.c_int32),
         ("num_workers", ctypes.c_int32),
+        ("lead_workers", ctypes.c_int32),
+        ("trail_share_pct", ctypes.c_int32),
     ]
 
 

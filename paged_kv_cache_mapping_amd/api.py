@@ -142,11 +142,13 @@ def decode_plan(num_rows, num_q_heads, cache, max_seq_len, sliding_window=0):
 
 
 def tune_plan(plan, num_rows, num_q_heads, cache, max_seq_len, sliding_window=0,
-              split_blocks=None, num_workers=None, kernel_variant=None):
+              split_blocks=None, num_workers=None, kernel_variant=None, lead_workers=None,
+              trail_share_pct=None):
     """Override a plan's tuning fields and recompute the sizes they imply.
 
     Scheme 0: split_blocks = blocks per split.  Scheme 1: split_blocks =
-    least blocks per worker, num_workers = workers launched.  The sizes follow
+    least blocks per worker, num_workers = workers launched, lead_workers /
+    trail_share_pct = unequal shares (see pagedkv.h).  The sizes follow
     the rules documented with ``pkv_decode_plan`` in pagedkv.h.
     """
     bs = cache.block_size
@@ -157,6 +159,12 @@ def tune_plan(plan, num_rows, num_q_heads, cache, max_seq_len, sliding_window=0,
         plan.split_blocks = int(split_blocks)
     if num_workers is not None:
         plan.num_workers = int(num_workers)
+        if lead_workers is None:
+            plan.lead_workers = plan.num_workers // 2 if plan.lead_workers else 0
+    if lead_workers is not None:
+        plan.lead_workers = int(lead_workers)
+    if trail_share_pct is not None:
+        plan.trail_share_pct = int(trail_share_pct)
     if kernel_variant is not None:
         plan.kernel_variant = int(kernel_variant)
     per_slot = num_rows * num_q_heads * (cache.head_dim + 2) * 4

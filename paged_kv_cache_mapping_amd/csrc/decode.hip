@@ -44,7 +44,12 @@ static bool mfma_eligible(int kv_dtype, int d, int bs) {
 
 constexpr int kMaxStreamRows = 4096;   // prefix sums of the balanced scheme live in LDS
 constexpr int kStreamMinUnits = 8;     // blocks per worker at least (bounds the pieces)
-constexpr int kStreamWavesPerCU = 4;     // one worker per SIMD
+constexpr int kTrailPct = 80;            // second wave on a SIMD: share in percent
+constexpr int kLdsPerCU = 160 * 1024;
+
+// Resident waves per CU for the balanced kernels: two per SIMD while the
+// registers allow it (up to four query heads per item), else one.
+static int stream_waves_per_cu(int heads_per_item) { return heads_per_item <= 4 ? 8 : 4; }
 
 static size_t partial_bytes(int rows, int hq, int splits, int d) {
   return (size_t)rows * hq * splits * ((size_t)d + 2) * sizeof(float);
@@ -72,9 +77,17 @@ static int make_plan(int rows, int hq, int hkv, int d, int bs, int kv_dtype, int
   if (allow_stream && mfma_eligible(kv_dtype, d, bs) && gm > 0 && rows <= kMaxStreamRows) {
     // balanced partition over resident wave slots
     const long long units = (long long)(rows > 0 ? rows : 1) * (hq / gm) * nvis;
-    long long workers = cus * kStreamWavesPerCU;
+    const int per_cu = stream_waves_per_cu(gm);
+    long long workers = cus * per_cu;
     const long long need = (units + kStreamMinUnits - 1) / kStreamMinUnits;
-    if (workers > need) workers = need;
+    plan->lead_workers = 0;
+    plan->trail_share_pct = 100;
+    if (workers > need) {
+      workers = need;
+    } else if (per_cu > 4) {
+      plan->lead_workers = (int32_t)(workers / 2);
+      plan->trail_share_pct = kTrailPct;
+    }
     if (workers < 1) workers = 1;
     plan->scheme = 1;
     plan->num_workers = (int32_t)workers;
@@ -92,6 +105,8 @@ static int make_plan(int rows, int hq, int hkv, int d, int bs, int kv_dtype, int
     while (split < 64 && items1 / split > target) split <<= 1;
     plan->scheme = 0;
     plan->num_workers = 0;
+    plan->lead_workers = 0;
+    plan->trail_share_pct = 100;
     plan->split_blocks = split;
     plan->max_splits = ceil_div(nvis, split);
     plan->heads_per_item = gt;
@@ -103,7 +118,7 @@ static int make_plan(int rows, int hq, int hkv, int d, int bs, int kv_dtype, int
 static int check_plan(const pkv_decode_plan* plan, int rows, int hq, int hkv, int d, int bs,
                       int kv_dtype, int max_seq_len, int window, int extra) {
   if (!plan) return PKV_ERR_NULL;
-  if (plan->kernel_variant < 0 || plan->kernel_variant > 3) return PKV_ERR_SHAPE;
+  if (plan->kernel_variant < 0 || plan->kernel_variant > 5) return PKV_ERR_SHAPE;
   const int group = hq / hkv;
   const int nvis = max_visible_blocks(max_seq_len, bs, window, extra);
   if (plan->scheme == 1) {
@@ -111,6 +126,8 @@ static int check_plan(const pkv_decode_plan* plan, int rows, int hq, int hkv, in
     if (plan->heads_per_item != heads_per_item_mfma(group) || plan->heads_per_item == 0)
       return PKV_ERR_SHAPE;
     if (plan->split_blocks < 1 || plan->num_workers < 1) return PKV_ERR_SHAPE;
+    if (plan->lead_workers < 0 || plan->lead_workers > plan->num_workers) return PKV_ERR_SHAPE;
+    if (plan->trail_share_pct < 1 || plan->trail_share_pct > 100) return PKV_ERR_SHAPE;
     if (plan->max_splits < ceil_div(nvis, plan->split_blocks) + 1) return PKV_ERR_SHAPE;
     return PKV_OK;
   }
@@ -254,6 +271,16 @@ static int prepare(DecodeArgs& a, void* out, const void* q, int q_dtype, int row
   a.kernel_variant = plan->kernel_variant;
   a.stream = plan->scheme == 1;
   a.heads_per_item = plan->heads_per_item;
+  a.lead_workers = plan->lead_workers;
+  a.trail_pct = plan->trail_share_pct;
+  {
+    // LDS one worker may take so that all workers stay resident
+    const long long cus = device_cu_count();
+    const long long per_cu = plan->num_workers > 0 ? (plan->num_workers + cus - 1) / cus : 1;
+    long long budget = kLdsPerCU / (per_cu > 0 ? per_cu : 1);
+    if (budget > 64 * 1024) budget = 64 * 1024;
+    a.lds_budget = (int32_t)(budget & ~15LL);
+  }
   a.scale_log2 = scale * log2e * (cache->dtype == PKV_FP8_E4M3 ? cache->k_scale : 1.0f);
   a.v_scale = cache->dtype == PKV_FP8_E4M3 ? cache->v_scale : 1.0f;
   bind_workspace(a, ws, rows, hq, cache->head_dim, plan->max_splits, plan->heads_per_item);

@@ -72,10 +72,13 @@ struct DecodeArgs {
   float* ws_acc;
   float* ws_m;
   float* ws_l;
-  int32_t kernel_variant;   // 0 default; tuning: 1 vector-only, 2/3 loads 1/2 steps ahead
+  int32_t kernel_variant;   // 0 default; tuning: 1 vector-only, 2..5 loads 1..4 steps ahead
   int32_t stream;           // balanced partition (piece counts in ws_np)
   int32_t heads_per_item;
   int32_t* ws_np;           // balanced partition: pieces per (row, head group)
+  int32_t lead_workers;     // balanced partition: workers with a full share (0: all)
+  int32_t trail_pct;        // share of the other workers, percent of a full share
+  int32_t lds_budget;       // bytes of LDS one worker may take
 };
 
 // What one row attends to.
@@ -806,31 +809,67 @@ struct MfmaShape {
 };
 
 // LDS layout of the balanced kernel (dynamic shared memory, 16-byte aligned
-// sections): prefix sums cum[rows + 1]; per-row records {req, tok, lo, hi}
-// when rows <= kRowRecRows; query rows of up to qslots pieces.
+// sections) within a budget of bytes per worker: prefix sums cum[rows + 1];
+// per-row records {req, tok, lo, hi} when rows <= kRowRecRows and they fit;
+// query rows of as many pieces as the rest holds (2 to 64).
 constexpr int kRowRecRows = 1024;
 
 struct FlatLds {
   int cum_off, rec_off, q_off, qslots;
+  bool recs;
   size_t bytes;
 };
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
-__host__ __device__ inline FlatLds flat_lds_layout(int rows, int gt, int d) {
+__host__ __device__ inline FlatLds flat_lds_layout(int rows, int gt, int d, int budget) {
   FlatLds l;
   l.cum_off = 0;
   size_t off = align16(((size_t)rows + 1) * sizeof(int));
-  l.rec_off = (int)off;
-  if (rows <= kRowRecRows) off += align16((size_t)rows * 4 * sizeof(int));
-  l.q_off = (int)off;
   const size_t per = (size_t)gt * d * 2;
-  int slots = (int)((16384 + per - 1) / per);      // about 16 KiB of staged queries
+  const size_t rec = align16((size_t)rows * 4 * sizeof(int));
+  l.rec_off = (int)off;
+  l.recs = rows <= kRowRecRows && off + rec + 2 * per <= (size_t)budget;
+  if (l.recs) off += rec;
+  l.q_off = (int)off;
+  long long slots = off + 2 * per <= (size_t)budget ? (long long)(((size_t)budget - off) / per) : 2;
   if (slots > kWave) slots = kWave;
   if (slots < 2) slots = 2;
-  l.qslots = slots;
+  l.qslots = (int)slots;
   l.bytes = off + (size_t)slots * per;
   return l;
+}
+
+// Contiguous shares of the unit range [0, U): workers w < lead take p_lead
+// units each, the others p_trail (both at least min_units).  With lead equal
+// to the worker count every share is equal.  range_of(u) numbers the shares.
+struct Shares {
+  long long p_lead, p_trail, lead_end;
+  int lead;
+  __device__ long long begin(long long w) const {
+    return w <= lead ? w * p_lead : lead_end + (w - lead) * p_trail;
+  }
+  __device__ long long range_of(long long u) const {
+    return u < lead_end ? u / p_lead : lead + (u - lead_end) / p_trail;
+  }
+};
+
+__device__ inline Shares make_shares(long long U, int W, int lead, int pct, int min_units) {
+  Shares s;
+  if (lead <= 0 || lead >= W || pct >= 100 || pct <= 0) {
+    s.lead = W;
+    s.p_lead = (U + W - 1) / W;
+  } else {
+    s.lead = lead;
+    const long long den = (long long)lead * 100 + (long long)(W - lead) * pct;
+    s.p_lead = (U * 100 + den - 1) / den;
+  }
+  if (s.p_lead < min_units) s.p_lead = min_units;
+  s.lead_end = (long long)s.lead * s.p_lead;
+  const long long rest = U - s.lead_end;
+  s.p_trail = (s.lead < W && rest > 0) ? (rest + (W - s.lead) - 1) / (W - s.lead) : 1;
+  if (s.p_trail < min_units) s.p_trail = min_units;
+  return s;
 }
 
 template <int D, int GT, int KV, int DEPTH>
@@ -838,13 +877,13 @@ __global__ __launch_bounds__(64) void decode_flat_kernel(DecodeArgs a) {
   using S = MfmaShape<D, GT, KV>;
   constexpr int NC = S::NC, VLPR = S::VLPR, VRPW = S::VRPW, VU = S::VU, VEPL = S::VEPL;
   constexpr int KB = S::KB, RG = S::RG, kElt = S::kElt, QE = S::QE, QL = S::QL;
-  static_assert(DEPTH >= 1 && DEPTH <= 2, "prefetch depth");
+  static_assert(DEPTH >= 1 && DEPTH <= 4, "prefetch depth");
   extern __shared__ __align__(16) char lds[];
-  const FlatLds L = flat_lds_layout(a.num_rows, GT, D);
+  const FlatLds L = flat_lds_layout(a.num_rows, GT, D, a.lds_budget);
   int* cum = reinterpret_cast<int*>(lds + L.cum_off);     // cum[r]: visible blocks of rows < r
   int4* rrec = reinterpret_cast<int4*>(lds + L.rec_off);  // {req, tok, lo, hi}
   uint16_t* qst = reinterpret_cast<uint16_t*>(lds + L.q_off);
-  const bool have_rec = a.num_rows <= kRowRecRows;
+  const bool have_rec = L.recs;
   const int lane = threadIdx.x;
   const int kvgroups = a.num_kv_heads * a.sub_groups;
 
@@ -872,10 +911,9 @@ __global__ __launch_bounds__(64) void decode_flat_kernel(DecodeArgs a) {
 
   const long long U = (long long)carry * kvgroups;
   const int W = gridDim.x;
-  long long P = (U + W - 1) / W;
-  if (P < a.split_blocks) P = a.split_blocks;
-  const long long u_lo = min(U, (long long)blockIdx.x * P);
-  const long long u_hi = min(U, u_lo + P);
+  const Shares sh = make_shares(U, W, a.lead_workers, a.trail_pct, a.split_blocks);
+  const long long u_lo = min(U, sh.begin(blockIdx.x));
+  const long long u_hi = min(U, sh.begin((long long)blockIdx.x + 1));
 
   const int spb_log2 = a.bs_log2 - 4;                     // 16-token steps per block
   const int64_t blk_bytes = a.block_stride * kElt;
@@ -952,8 +990,9 @@ __global__ __launch_bounds__(64) void decode_flat_kernel(DecodeArgs a) {
     const int h0 = (kvg / a.sub_groups) * a.group + (kvg % a.sub_groups) * GT;
     const int nv = cum[b + 1] - cum[b];
     const long long seg_base = (long long)cum[b] * kvgroups + (long long)kvg * nv;
-    const int piece = (int)(s_first / P - seg_base / P);
-    const int npieces = (int)((seg_base + nv - 1) / P - seg_base / P + 1);
+    const long long r0 = sh.range_of(seg_base);
+    const int piece = (int)(sh.range_of(s_first) - r0);
+    const int npieces = (int)(sh.range_of(seg_base + nv - 1) - r0 + 1);
     if (s_bad) {
 #pragma unroll
       for (int h = 0; h < GT; ++h) {
@@ -989,16 +1028,35 @@ __global__ __launch_bounds__(64) void decode_flat_kernel(DecodeArgs a) {
           store_out<PKV_BF16, VEPL>(a.out, out_row + h * D + vsub * VEPL, o);
         }
       } else {
+        // acc rows: full 128-byte lines, streamed past the caches (the
+        // combine kernel reads them once)
 #pragma unroll
         for (int h = 0; h < GT; ++h) {
           const int64_t pr = ((int64_t)b * a.num_q_heads + h0 + h) * a.max_splits + piece;
           float* dst = a.ws_acc + pr * D + vsub * VEPL;
 #pragma unroll
-          for (int e = 0; e < VEPL; ++e) dst[e] = acc[h][e];
-          if (vsub == 0) {
-            a.ws_m[pr] = m[h];
-            a.ws_l[pr] = lh[h];
+          for (int e = 0; e < VEPL; e += 4) {
+            const f32x4_t v4 = {acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]};
+            __builtin_nontemporal_store(v4, reinterpret_cast<f32x4_t*>(dst + e));
           }
+        }
+      }
+    }
+    if (npieces > 1) {
+      // m and l of the piece's heads side by side: one record of 2 GT floats
+      float* ml = a.ws_m + (((int64_t)b * kvgroups + kvg) * a.max_splits + piece) * (2 * GT);
+      constexpr int NV = (2 * GT + 3) / 4;
+      if (lane < NV) {
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 2 * GT; ++e)
+          if (e / 4 == lane) v[e % 4] = e < GT ? m[e] : lh[e - GT];
+        if constexpr (2 * GT >= 4) {
+          const f32x4_t v4 = {v[0], v[1], v[2], v[3]};
+          __builtin_nontemporal_store(v4, reinterpret_cast<f32x4_t*>(ml + 4 * lane));
+        } else {
+          ml[0] = v[0];
+          ml[1] = v[1];
         }
       }
     }
@@ -1229,27 +1287,16 @@ __global__ __launch_bounds__(64) void decode_flat_kernel(DecodeArgs a) {
     };
 
     // loads run DEPTH steps ahead, unconditionally (past the end the last
-    // step is fetched again, an L2 hit), so the wait counts stay static
-    if constexpr (DEPTH == 2) {
-      Buf b0, b1, b2;
-      issue(0, b0);
-      issue(min(1, last), b1);
-      for (int st = 0; st < nsteps; st += 3) {
-        issue(min(st + 2, last), b2);
-        run(st, b0);
-        issue(min(st + 3, last), b0);
-        if (st + 1 < nsteps) run(st + 1, b1);
-        issue(min(st + 4, last), b1);
-        if (st + 2 < nsteps) run(st + 2, b2);
-      }
-    } else {
-      Buf b0, b1;
-      issue(0, b0);
-      for (int st = 0; st < nsteps; st += 2) {
-        issue(min(st + 1, last), b1);
-        run(st, b0);
-        issue(min(st + 2, last), b0);
-        if (st + 1 < nsteps) run(st + 1, b1);
+    // step is fetched again, an L2 hit), so the wait counts stay static; the
+    // ring of DEPTH + 1 buffers is unrolled so every index is a constant
+    Buf ring[DEPTH + 1];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) issue(min(d, last), ring[d]);
+    for (int st = 0; st < nsteps; st += DEPTH + 1) {
+#pragma unroll
+      for (int k = 0; k <= DEPTH; ++k) {
+        issue(min(st + k + DEPTH, last), ring[(k + DEPTH) % (DEPTH + 1)]);
+        if (st + k < nsteps) run(st + k, ring[k]);
       }
     }
   }
@@ -1290,8 +1337,24 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   if (nsplit <= 1) return;
 
   const int64_t pr0 = ((int64_t)b * a.num_q_heads + h) * a.max_splits;
+  // where piece s keeps m and l: fixed splits use two plain arrays; the
+  // balanced kernel packs the heads of a piece into one record (m..., l...)
+  const float* mp;
+  const float* lp;
+  int mstride;
+  if (a.stream) {
+    const int gt = a.heads_per_item;
+    const int64_t rec0 = ((int64_t)b * (a.num_q_heads / gt) + h / gt) * a.max_splits;
+    mp = a.ws_m + rec0 * 2 * gt + h % gt;
+    lp = mp + gt;
+    mstride = 2 * gt;
+  } else {
+    mp = a.ws_m + pr0;
+    lp = a.ws_l + pr0;
+    mstride = 1;
+  }
   float M = -INFINITY;
-  for (int s = lane; s < nsplit; s += kWave) M = fmaxf(M, a.ws_m[pr0 + s]);
+  for (int s = lane; s < nsplit; s += kWave) M = fmaxf(M, mp[(int64_t)s * mstride]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
 
@@ -1301,9 +1364,9 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   for (int i = 0; i < PER; ++i) num[i] = 0.f;
   const bool active = D >= kWave || lane < D;
   for (int s = 0; s < nsplit; ++s) {
-    const float ms = a.ws_m[pr0 + s];
+    const float ms = mp[(int64_t)s * mstride];
     const float wgt = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-    den = fmaf(wgt, a.ws_l[pr0 + s], den);
+    den = fmaf(wgt, lp[(int64_t)s * mstride], den);
     if (active) {
       const float* src = a.ws_acc + (pr0 + s) * D;
 #pragma unroll
@@ -1350,12 +1413,18 @@ int run_split_dk(const DecodeArgs& a, int gt, hipStream_t s) {
 
 template <int D, int GT, int KV>
 void launch_stream(const DecodeArgs& a, int workers, hipStream_t s) {
-  const size_t lds = flat_lds_layout(a.num_rows, GT, D).bytes;
-  // loads two steps ahead; one where the registers run short (16 heads)
-  constexpr int kDepth = GT >= 16 ? 1 : 2;
-  if (a.kernel_variant == 2) decode_flat_kernel<D, GT, KV, 1><<<workers, 64, lds, s>>>(a);
-  else if (a.kernel_variant == 3) decode_flat_kernel<D, GT, KV, 2><<<workers, 64, lds, s>>>(a);
-  else decode_flat_kernel<D, GT, KV, kDepth><<<workers, 64, lds, s>>>(a);
+  const size_t lds = flat_lds_layout(a.num_rows, GT, D, a.lds_budget).bytes;
+  // loads one step ahead: deeper rings measured slower here (more requests in
+  // flight raise the latency of all of them, and past 256 registers only one
+  // wave fits on a SIMD)
+  constexpr int kDepth = 1;
+  switch (a.kernel_variant) {
+    case 2: decode_flat_kernel<D, GT, KV, 1><<<workers, 64, lds, s>>>(a); break;
+    case 3: decode_flat_kernel<D, GT, KV, 2><<<workers, 64, lds, s>>>(a); break;
+    case 4: decode_flat_kernel<D, GT, KV, 3><<<workers, 64, lds, s>>>(a); break;
+    case 5: decode_flat_kernel<D, GT, KV, 4><<<workers, 64, lds, s>>>(a); break;
+    default: decode_flat_kernel<D, GT, KV, kDepth><<<workers, 64, lds, s>>>(a);
+  }
 }
 
 // Balanced partition (matrix cores), a.heads_per_item query heads per item.

@@ -115,7 +115,7 @@ def test_sliding_window(W):
 
 
 @pytest.mark.parametrize("split", [1, 2, 3, 8, 64])
-@pytest.mark.parametrize("variant", [0, 2, 3])
+@pytest.mark.parametrize("variant", [0, 2, 3, 4, 5])
 def test_any_split_plan_gives_the_same_answer(split, variant):
     say("decode split", split, "variant", variant)
     w = _small(150, B=6, Lmax=1500, Hq=32, Hkv=8, D=128, bs=16, Lmin=200)
