@@ -2,6 +2,7 @@
 // layout and the C entry points (decode and chunked).  The kernels and their
 // launch templates are in decode_kernels.h; decode_*.hip instantiate them.
 #include "decode_kernels.h"
+#include "prefill.h"
 
 namespace pkv {
 
@@ -398,6 +399,7 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dt
 struct ChunkPlans {
   pkv_decode_plan single, multi;
   size_t single_bytes, multi_bytes;
+  bool prefill;           // multi-query requests on the matrix-core prefill kernel
 };
 
 static int chunk_plans(int num_tokens, int num_reqs, int hq, const pkv_cache* c, int max_query_len,
@@ -411,7 +413,9 @@ static int chunk_plans(int num_tokens, int num_reqs, int hq, const pkv_cache* c,
                  max_seq_len, window, extra, false, &p.multi);
   if (st != PKV_OK) return st;
   p.single_bytes = (p.single.workspace_bytes + 255) & ~(size_t)255;
-  p.multi_bytes = max_query_len > 1 ? p.multi.workspace_bytes : 0;
+  p.prefill = prefill_supported(c->dtype, c->head_dim, hq / c->num_kv_heads, max_seq_len,
+                                c->block_size, window, max_query_len);
+  p.multi_bytes = (max_query_len > 1 && !p.prefill) ? p.multi.workspace_bytes : 0;
   return PKV_OK;
 }
 
@@ -466,7 +470,39 @@ extern "C" int pkv_paged_attention_chunked(void* out, const void* q, int32_t q_d
                max_query_len, 1, &p.single, ws, p.single_bytes);
   if (st != PKV_OK) return st;
   a1.num_tokens = num_tokens;
-  if (max_query_len > 1) {
+  if (max_query_len > 1 && p.prefill) {
+    if (!out || !q || !block_table || !seq_lens) return PKV_ERR_NULL;
+    if (bt_stride <= 0 || max_seq_len < 0 || sliding_window < 0) return PKV_ERR_SHAPE;
+    if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return PKV_ERR_SHAPE;
+    if (num_q_heads % cache->num_kv_heads) return PKV_ERR_SHAPE;
+    PrefillArgs pa = {};
+    pa.out = out;
+    pa.q = q;
+    pa.qsl = query_start_loc;
+    pa.seq_lens = seq_lens;
+    pa.num_reqs = num_reqs;
+    pa.num_tokens = num_tokens;
+    pa.max_query_len = max_query_len;
+    pa.max_seq_len = max_seq_len;
+    pa.num_q_heads = num_q_heads;
+    pa.num_kv_heads = cache->num_kv_heads;
+    pa.kbase = reinterpret_cast<const char*>(cache->k);
+    pa.vbase = reinterpret_cast<const char*>(cache->v);
+    pa.block_stride = cache->block_stride;
+    pa.num_blocks = cache->num_blocks;
+    pa.bs_log2 = log2_int(cache->block_size);
+    pa.bt = block_table;
+    pa.bt_stride = bt_stride;
+    pa.causal = causal != 0;
+    pa.window = sliding_window;
+    const float log2e = 1.4426950408889634f;
+    pa.scale_log2 = softmax_scale * log2e * (cache->dtype == PKV_FP8_E4M3 ? cache->k_scale : 1.0f);
+    pa.v_scale = cache->dtype == PKV_FP8_E4M3 ? cache->v_scale : 1.0f;
+    st = launch_prefill(pa, cache->dtype, cache->head_dim, stream);
+    if (st != PKV_OK) return st;
+    st = launch_status();
+    if (st != PKV_OK) return st;
+  } else if (max_query_len > 1) {
     DecodeArgs a2;
     st = prepare(a2, out, q, q_dtype, num_tokens, num_q_heads, cache, block_table, bt_stride,
                  seq_lens, max_seq_len, softmax_scale, sliding_window, 1, query_start_loc, num_reqs,

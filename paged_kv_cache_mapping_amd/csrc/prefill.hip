@@ -1,0 +1,472 @@
+// Chunked prefill attention on the matrix cores.
+//
+// A chunk of a prompt attends, causally (or not) and within an optional
+// sliding window, to the request's cached keys, which it finds by walking the
+// request's block table ("vLLM의 KV cache 연결 흐름", sections on slot mapping
+// and on the metadata handed to the backend); the softmax spans every block
+// and is kept online ("Understanding PageAttention Memory Optimization",
+// "Handling Softmax Across Blocks"; Chinese worker-side page, section
+// "Worker与ModelRunner的协作"); grouped-query heads share a KV head and a
+// window keeps the most recent W positions ("Deep Dive into vLLM Worker-Side
+// GPU KV Cache Initialization", "Hybrid Attention Mechanisms").
+//
+// Decomposition (MI355X): one workgroup of four waves per (request, KV head,
+// tile of query tokens).  A wave owns NBW blocks of 16 rows; a row is one
+// (query token, query head of the group).  Keys stream through LDS in tiles
+// of 32 (K and V double-buffered, staged by the whole workgroup from the
+// block table slice in LDS).  Per tile and 16-row block:
+//   S^T = K Q^T   on v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = Q
+//                 rows kept in registers): lane l holds keys 4(l/16)+i of
+//                 row l%16, so each row's softmax state lives in one lane
+//                 (replicated over the four lane groups);
+//   O^T += V^T P^T on the same instruction: P^T needs no data movement -- its
+//                 eight k slots per lane are the lane's own probabilities,
+//                 which fixes the order of keys along k -- and V^T comes from
+//                 the LDS tile through the gfx950 transpose read, which hands
+//                 lane j of a 16-lane group element j of four consecutive
+//                 key rows.
+// The running max is lazy (rescale only when it grows by more than 2^8); P
+// enters the product as a bf16 high part plus a bf16 remainder (about 16
+// significant bits, so the result stays within the bf16 output's own
+// rounding); everything else accumulates in fp32.
+#include <math.h>
+
+#include <type_traits>
+
+#include "common.h"
+#include "host_common.h"
+#include "prefill.h"
+
+namespace pkv {
+
+namespace {
+
+typedef __bf16 pf_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float pf_f32x4 __attribute__((ext_vector_type(4)));
+typedef short pf_i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) pf_i16x4 lds_i16x4;
+
+constexpr int kPfWaves = 4;
+constexpr int kPfKeys = 32;          // keys per tile
+constexpr float kPfLazy = 8.0f;      // keep a stale max until a score beats it by 2^8
+
+template <int D, int G>
+struct PfShape {
+  static constexpr int NBW = D >= 256 ? 2 : 4;   // 16-row blocks per wave
+  static constexpr int TPN = 16 / G;             // query tokens per row block
+  static constexpr int TW = NBW * TPN;           // query tokens per wave
+  static constexpr int TWG = kPfWaves * TW;      // query tokens per workgroup
+  static constexpr int NC = D / 32;              // k-chunks of the score product
+  static constexpr int MB = D / 16;              // 16-dim blocks of the output
+  static constexpr int RS = D * 2 + 16;          // LDS bytes per staged key row
+  static constexpr int TILE = kPfKeys * RS;      // LDS bytes of one K or V tile
+  static constexpr int CPR = D / 8;              // 16-byte bf16 chunks per key row
+  static constexpr int CPT = kPfKeys * CPR;      // chunks per tile
+  static constexpr int CPTH = (CPT + 255) / 256; // chunks per thread and plane
+  static_assert(16 % G == 0, "group must divide 16");
+};
+
+inline size_t pf_align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+template <int D, int G>
+size_t pf_lds_bytes(int max_blocks) {
+  return 4 * (size_t)PfShape<D, G>::TILE + pf_align16((size_t)max_blocks * sizeof(int));
+}
+
+template <int D, int G, int KV>
+__global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
+  using S = PfShape<D, G>;
+  constexpr int NBW = S::NBW, TPN = S::TPN, TW = S::TW, TWG = S::TWG;
+  constexpr int NC = S::NC, MB = S::MB, RS = S::RS, TILE = S::TILE;
+  constexpr int CPR = S::CPR, CPT = S::CPT, CPTH = S::CPTH;
+  constexpr int kElt = KV == PKV_BF16 ? 2 : 1;
+  extern __shared__ __align__(16) char lds[];
+  int* tab = reinterpret_cast<int*>(lds + 4 * TILE);   // phys block or -1, from block b0
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int grp = lane >> 4;           // lane group of the MFMA layouts
+  const int ln16 = lane & 15;
+  const int kvh = blockIdx.y;
+  const int r = blockIdx.x / a.tiles_per_req;
+  const int qt = blockIdx.x % a.tiles_per_req;
+  const int q0 = a.qsl[r];
+  const int ql = a.qsl[r + 1] - q0;
+  if (ql <= 1 || qt * TWG >= ql) return;            // whole workgroup
+  if (q0 < 0 || q0 + ql > a.num_tokens) return;     // rows outside q / out: nothing to write
+  const int L = a.seq_lens[r];
+  const int tok_lo = qt * TWG;
+  const int tok_hi = min(ql, tok_lo + TWG);
+  const int p0 = L - ql;                              // position of query 0
+  const int hq = a.num_q_heads;
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
+
+  const int khi = a.causal ? p0 + tok_hi - 1 : L - 1;
+  const int klo = a.window > 0 ? max(0, p0 + tok_lo - a.window + 1) : 0;
+  const int b0 = klo >> a.bs_log2;
+  const int nblk = (khi >> a.bs_log2) - b0 + 1;
+  const bool req_ok = L > 0 && L <= a.max_seq_len && ql <= L && ql <= a.max_query_len &&
+                      nblk <= a.max_blocks;
+  if (!req_ok) {
+    // lengths inconsistent with the arguments: NaN rows, as the other paths
+    const int n = (tok_hi - tok_lo) * G * D;
+    for (int e = tid; e < n; e += 256) {
+      const int t = e / (G * D);
+      const int rem = e - t * G * D;
+      out[((int64_t)(q0 + tok_lo + t) * hq + kvh * G) * D + rem] = 0x7FC0;
+    }
+    return;
+  }
+
+  // ---- table slice of the blocks this workgroup can touch
+  for (int i = tid; i < nblk; i += 256) {
+    const int j = b0 + i;
+    int e = -1;
+    if (j < a.bt_stride) e = a.bt[(int64_t)r * a.bt_stride + j];
+    tab[i] = (e >= 0 && e < a.num_blocks) ? e : -1;
+  }
+  __syncthreads();
+
+  // ---- this wave's rows
+  const int tw0 = tok_lo + wave * TW;                 // first query token of the wave
+  const bool wave_live = tw0 < tok_hi;
+  const int tw_last = min(tw0 + TW, tok_hi) - 1;
+  const int wqlo = p0 + tw0, wqhi = p0 + tw_last;     // positions of the wave's queries
+  const int wkhi = a.causal ? wqhi : L - 1;
+  const int wklo = a.window > 0 ? max(0, wqlo - a.window + 1) : 0;
+  const bool wave_full_rows = tw0 + TW <= tok_hi;
+
+  int row_t[NBW];        // query token (request-relative) of this lane's row per block
+  int row_h[NBW];        // query head
+  bool row_ok[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    row_t[nb] = tw0 + nb * TPN + ln16 / G;
+    row_h[nb] = kvh * G + ln16 % G;
+    row_ok[nb] = row_t[nb] < tok_hi;
+  }
+
+  // B operand of the score product: Q rows, lane l: row l % 16, dims 8 (l / 16) + 32 c
+  pf_bf16x8 bq[NBW][NC];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                         ((int64_t)(q0 + row_t[nb]) * hq + row_h[nb]) * D + 8 * grp;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      uint4 t = make_uint4(0, 0, 0, 0);
+      if (row_ok[nb]) t = *reinterpret_cast<const uint4*>(qp + 32 * c);
+      bq[nb][c] = __builtin_bit_cast(pf_bf16x8, t);
+    }
+  }
+
+  pf_f32x4 acc[NBW][MB];
+  float m[NBW], lsum[NBW];
+  bool bad[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    m[nb] = -INFINITY;
+    lsum[nb] = 0.f;
+    bad[nb] = false;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = pf_f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // ---- staging: chunk c = tid + 256 j of a tile is key c / CPR, 16 bytes
+  // (8 bf16) at column chunk c % CPR; keys outside [klo, khi] or on an
+  // unmapped block stage as zeros
+  const int64_t blk_bytes = a.block_stride * kElt;
+  const int row_bytes = a.num_kv_heads * D * kElt;
+  const int bmask = (1 << a.bs_log2) - 1;
+  typedef typename std::conditional<KV == PKV_BF16, uint4, uint2>::type Raw;
+  Raw kr[CPTH], vr[CPTH];
+  auto stage_load = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < CPTH; ++j) {
+      const int c = tid + 256 * j;
+      Raw kz, vz;
+      if constexpr (KV == PKV_BF16) {
+        kz = make_uint4(0, 0, 0, 0);
+        vz = make_uint4(0, 0, 0, 0);
+      } else {
+        kz = make_uint2(0, 0);
+        vz = make_uint2(0, 0);
+      }
+      if (c < CPT) {
+        const int kp = kt * kPfKeys + c / CPR;
+        const int cc = c % CPR;
+        const int phys = (kp >= klo && kp <= khi) ? tab[(kp >> a.bs_log2) - b0] : -1;
+        if (phys >= 0) {
+          const int64_t off = (int64_t)phys * blk_bytes + (int64_t)(kp & bmask) * row_bytes +
+                              kvh * D * kElt + cc * 8 * kElt;
+          kz = *reinterpret_cast<const Raw*>(a.kbase + off);
+          vz = *reinterpret_cast<const Raw*>(a.vbase + off);
+        }
+      }
+      kr[j] = kz;
+      vr[j] = vz;
+    }
+  };
+  auto widen = [&](const Raw& x) __attribute__((always_inline)) -> uint4 {
+    if constexpr (KV == PKV_BF16) {
+      return x;
+    } else {
+      return make_uint4(e4m3x2_to_bf16x2<false>(x.x), e4m3x2_to_bf16x2<true>(x.x),
+                        e4m3x2_to_bf16x2<false>(x.y), e4m3x2_to_bf16x2<true>(x.y));
+    }
+  };
+  auto stage_store = [&](int buf) __attribute__((always_inline)) {
+    char* kt_l = lds + buf * 2 * TILE;
+    char* vt_l = kt_l + TILE;
+#pragma unroll
+    for (int j = 0; j < CPTH; ++j) {
+      const int c = tid + 256 * j;
+      if (c < CPT) {
+        const int o = (c / CPR) * RS + (c % CPR) * 16;
+        *reinterpret_cast<uint4*>(kt_l + o) = widen(kr[j]);
+        *reinterpret_cast<uint4*>(vt_l + o) = widen(vr[j]);
+      }
+    }
+  };
+
+  auto compute = [&](int kt, int buf) __attribute__((always_inline)) {
+    const int kbase = kt * kPfKeys;
+    if (!wave_live || kbase > wkhi || kbase + kPfKeys - 1 < wklo) return;
+    const char* kt_l = lds + buf * 2 * TILE;
+    const char* vt_l = kt_l + TILE;
+    // an unmapped block among the tile's keys makes the rows that see it NaN
+    bool tile_bad = false;
+    {
+      const int lo = max(kbase, klo), hi = min(kbase + kPfKeys - 1, khi);
+      for (int bi = (lo >> a.bs_log2) - b0; bi <= (hi >> a.bs_log2) - b0; ++bi)
+        tile_bad |= tab[bi] < 0;
+    }
+    bool full = wave_full_rows && !tile_bad && kbase >= wklo && kbase + kPfKeys - 1 <= L - 1;
+    if (a.causal) full = full && kbase + kPfKeys - 1 <= wqlo;
+    if (a.window > 0) full = full && kbase >= wqhi - a.window + 1;
+
+    // A operand of the score product: K rows 16 kh + l % 16, dims 8 (l / 16) + 32 c
+    pf_bf16x8 ak[2][NC];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        ak[kh][c] = *reinterpret_cast<const pf_bf16x8*>(kt_l + (16 * kh + ln16) * RS + (8 * grp + 32 * c) * 2);
+
+    pf_bf16x8 pb[NBW], pl[NBW];   // P = bf16 high part + bf16 remainder
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      float z[2][4];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        pf_f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[kh][c], bq[nb][c], sc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[kh][i] = sc[i] * a.scale_log2;
+      }
+      if (!full) {
+        const int qpos = p0 + row_t[nb];
+        const int rhi = a.causal ? qpos : L - 1;
+        const int rlo = a.window > 0 ? max(0, qpos - a.window + 1) : 0;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kp = kbase + 16 * kh + 4 * grp + i;
+            const bool vis = row_ok[nb] && kp >= rlo && kp <= rhi;
+            if (vis && tile_bad && tab[(kp >> a.bs_log2) - b0] < 0) bad[nb] = true;
+            if (!vis) z[kh][i] = -INFINITY;
+          }
+      }
+      float mt = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
+                       fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const bool grow = mt > m[nb] + kPfLazy;
+      if (__ballot(grow) != 0) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m[nb] - mt) : 1.0f;   // 0 when m = -inf
+        if (grow) m[nb] = mt;
+        lsum[nb] *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[nb][mb] *= alpha;
+      }
+      float p[2][4];
+      float ps = 0.f;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = __builtin_amdgcn_exp2f(z[kh][i] - m[nb]);
+          p[kh][i] = z[kh][i] == -INFINITY ? 0.f : e;
+          ps += p[kh][i];
+        }
+      lsum[nb] += ps;
+      // k slots 8 (l / 16) + i: keys 4 (l / 16) + i, then 16 + 4 (l / 16) + i.
+      // P goes in as two bf16 terms (high part and the rest), so that the
+      // product keeps about 16 bits of each probability.
+      __bf16 hi[8], lo[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float x = p[k / 4][k % 4];
+        hi[k] = (__bf16)x;
+        lo[k] = (__bf16)(x - (float)hi[k]);
+      }
+      pb[nb] = pf_bf16x8{hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7]};
+      pl[nb] = pf_bf16x8{lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]};
+    }
+
+    // O^T += V^T P^T: A = V^T from the tile by transpose reads.  Lane s of a
+    // 16-lane group points at key k0 + s / 4, dims d0 + 4 (s % 4); lane j
+    // then holds V[k0 + i][d0 + j], i = 0..3.
+    const int vrow = 4 * grp + (ln16 >> 2);
+    const int vcol = 4 * (ln16 & 3);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const char* v1 = vt_l + vrow * RS + (16 * mb + vcol) * 2;
+      const char* v2 = v1 + 16 * RS;
+      const pf_i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v1));
+      const pf_i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v2));
+      const pf_bf16x8 av = __builtin_bit_cast(
+          pf_bf16x8, (short __attribute__((ext_vector_type(8)))){lo4[0], lo4[1], lo4[2], lo4[3],
+                                                                  hi4[0], hi4[1], hi4[2], hi4[3]});
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) {
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[nb], acc[nb][mb], 0, 0, 0);
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pl[nb], acc[nb][mb], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- key tiles, double-buffered through LDS, one barrier per tile
+  const int kt0 = klo / kPfKeys, kt1 = khi / kPfKeys;
+  stage_load(kt0);
+  stage_store(0);
+  __syncthreads();
+  for (int kt = kt0; kt <= kt1; ++kt) {
+    const int buf = (kt - kt0) & 1;
+    const bool more = kt < kt1;
+    if (more) stage_load(kt + 1);
+    compute(kt, buf);
+    if (more) stage_store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- normalise and store: lane l holds dims 16 mb + 4 (l / 16) + i of row l % 16
+  if (!wave_live) return;
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    float lt = lsum[nb];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    // every lane takes part in both exchanges (no short-circuit: a lane that
+    // skipped the exchange would not hand its flag to the others)
+    int bi = bad[nb] ? 1 : 0;
+    bi |= __shfl_xor(bi, 16);
+    bi |= __shfl_xor(bi, 32);
+    const bool b = bi != 0;
+    if (!row_ok[nb]) continue;
+    const float inv = a.v_scale / lt;
+    uint16_t* dst = out + ((int64_t)(q0 + row_t[nb]) * hq + row_h[nb]) * D + 4 * grp;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      uint2 w;
+      if (b) {
+        w = make_uint2(0x7FC07FC0u, 0x7FC07FC0u);
+      } else {
+        w.x = f32_to_bf16_rne(acc[nb][mb][0] * inv) | (f32_to_bf16_rne(acc[nb][mb][1] * inv) << 16);
+        w.y = f32_to_bf16_rne(acc[nb][mb][2] * inv) | (f32_to_bf16_rne(acc[nb][mb][3] * inv) << 16);
+      }
+      *reinterpret_cast<uint2*>(dst + 16 * mb) = w;
+    }
+  }
+}
+
+template <int D, int G>
+constexpr int pf_tokens_per_wg() { return PfShape<D, G>::TWG; }
+
+int pf_tokens(int d, int g) {
+  switch (d * 100 + g) {
+    case 6401: return pf_tokens_per_wg<64, 1>();
+    case 6402: return pf_tokens_per_wg<64, 2>();
+    case 6404: return pf_tokens_per_wg<64, 4>();
+    case 6408: return pf_tokens_per_wg<64, 8>();
+    case 6416: return pf_tokens_per_wg<64, 16>();
+    case 12801: return pf_tokens_per_wg<128, 1>();
+    case 12802: return pf_tokens_per_wg<128, 2>();
+    case 12804: return pf_tokens_per_wg<128, 4>();
+    case 12808: return pf_tokens_per_wg<128, 8>();
+    case 12816: return pf_tokens_per_wg<128, 16>();
+    case 25601: return pf_tokens_per_wg<256, 1>();
+    case 25602: return pf_tokens_per_wg<256, 2>();
+    case 25604: return pf_tokens_per_wg<256, 4>();
+    case 25608: return pf_tokens_per_wg<256, 8>();
+    case 25616: return pf_tokens_per_wg<256, 16>();
+  }
+  return 0;
+}
+
+template <int D, int G, int KV>
+void pf_launch(const PrefillArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((long long)a.num_reqs * a.tiles_per_req), (unsigned)a.num_kv_heads);
+  prefill_tile_kernel<D, G, KV><<<grid, 256, pf_lds_bytes<D, G>(a.max_blocks), s>>>(a);
+}
+
+template <int D, int KV>
+int pf_launch_g(const PrefillArgs& a, int g, hipStream_t s) {
+  switch (g) {
+    case 1: pf_launch<D, 1, KV>(a, s); return PKV_OK;
+    case 2: pf_launch<D, 2, KV>(a, s); return PKV_OK;
+    case 4: pf_launch<D, 4, KV>(a, s); return PKV_OK;
+    case 8: pf_launch<D, 8, KV>(a, s); return PKV_OK;
+    case 16: pf_launch<D, 16, KV>(a, s); return PKV_OK;
+  }
+  return PKV_ERR_UNSUPPORTED;
+}
+
+// Table entries one workgroup may need: its keys span the longest context, or
+// with a window the window plus the workgroup's own query tokens.
+// (tokens: the query tokens one workgroup spans, or the longest query for
+// rows that see up to the end of the context)
+int pf_max_blocks(int max_seq_len, int bs, int window, int tokens) {
+  const long long full = (max_seq_len + (long long)bs - 1) / bs + 1;
+  if (window <= 0) return (int)full;
+  const long long win = ((long long)window + tokens + 2 * bs - 2) / bs + 1;
+  return (int)(full < win ? full : win);
+}
+
+}  // namespace
+
+bool prefill_supported(int kv_dtype, int head_dim, int group, int max_seq_len, int block_size,
+                       int window, int max_query_len) {
+  if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3) return false;
+  if (head_dim != 64 && head_dim != 128) return false;   // 256: tiles exceed 64 KiB of LDS
+  if (group < 1 || group > 16 || 16 % group) return false;
+  if (max_query_len < 2) return false;
+  const int tok = pf_tokens(head_dim, group);
+  const int mb = pf_max_blocks(max_seq_len, block_size, window, tok > max_query_len ? tok : max_query_len);
+  // the staged tiles plus the table slice within 64 KiB of LDS per workgroup
+  const size_t bytes = 4 * (size_t)(32 * (head_dim * 2 + 16)) + pf_align16((size_t)mb * 4);
+  return bytes <= 64 * 1024;
+}
+
+int launch_prefill(const PrefillArgs& a0, int kv_dtype, int head_dim, hipStream_t s) {
+  PrefillArgs a = a0;
+  const int g = a.num_q_heads / a.num_kv_heads;
+  const int tok = pf_tokens(head_dim, g);
+  if (tok == 0) return PKV_ERR_UNSUPPORTED;
+  a.tiles_per_req = (a.max_query_len + tok - 1) / tok;
+  a.max_blocks = pf_max_blocks(a.max_seq_len, 1 << a.bs_log2, a.window,
+                               tok > a.max_query_len ? tok : a.max_query_len);
+  if (a.num_reqs == 0 || a.tiles_per_req == 0) return PKV_OK;
+  if ((long long)a.num_reqs * a.tiles_per_req > 0x7FFFFFFFLL) return PKV_ERR_SHAPE;
+  const bool bf = kv_dtype == PKV_BF16;
+  switch (head_dim) {
+    case 64: return bf ? pf_launch_g<64, PKV_BF16>(a, g, s) : pf_launch_g<64, PKV_FP8_E4M3>(a, g, s);
+    case 128: return bf ? pf_launch_g<128, PKV_BF16>(a, g, s) : pf_launch_g<128, PKV_FP8_E4M3>(a, g, s);
+  }
+  return PKV_ERR_UNSUPPORTED;
+}
+
+}  // namespace pkv

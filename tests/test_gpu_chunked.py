@@ -20,7 +20,7 @@ def _gpu():
     gpu_or_skip()
 
 
-def _chunk_case(seed, R, Lmax, qmax, Hq, Hkv, D, bs):
+def _chunk_case(seed, R, Lmax, qmax, Hq, Hkv, D, bs, v_sigma=0.4):
     rng = np.random.default_rng(seed)
     L = rng.integers(1, Lmax + 1, size=R)
     ql = np.minimum(rng.integers(1, qmax + 1, size=R), L)
@@ -36,7 +36,7 @@ def _chunk_case(seed, R, Lmax, qmax, Hq, Hkv, D, bs):
         k += n
     shape = (nb, bs, Hkv, D)
     kp = bf16_bits(rng.standard_normal(shape).astype(np.float32) * 0.4)
-    vp = bf16_bits(rng.standard_normal(shape).astype(np.float32) * 0.4)
+    vp = bf16_bits(rng.standard_normal(shape).astype(np.float32) * np.float32(v_sigma))
     qsl = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
     q = bf16_bits(rng.standard_normal((int(qsl[-1]), Hq, D)).astype(np.float32) * 0.4)
     return dict(L=L.astype(np.int32), qsl=qsl, bt=bt, kp=kp, vp=vp, q=q, nb=nb, bs=bs, Hkv=Hkv, D=D)
@@ -102,6 +102,94 @@ def test_padding_rows_are_left_untouched():
     ref = attention.paged_attention(c["q"], "bf16", c["kp"], c["vp"], "bf16", c["bt"], c["L"],
                                     c["qsl"], 0.1)
     assert max_err(out_f64(out[:T]), ref) <= 2e-3
+
+
+def _chunk_case_fp8(seed, R, Lmax, qmax, Hq, Hkv, D, bs):
+    """As _chunk_case, with K/V stored as E4M3 codes under per-tensor scales."""
+    c = _chunk_case(seed, R, Lmax, qmax, Hq, Hkv, D, bs)
+    rng = np.random.default_rng(seed + 1)
+    shape = (c["nb"], bs, Hkv, D)
+    kx = rng.standard_normal(shape).astype(np.float32)
+    vx = rng.standard_normal(shape).astype(np.float32)
+    c["k_scale"] = float(np.float32(np.abs(kx).max() / 448.0))
+    c["v_scale"] = float(np.float32(np.abs(vx).max() / 448.0))
+    c["kp"] = workloads.fp8_codes(kx, c["k_scale"])
+    c["vp"] = workloads.fp8_codes(vx, c["v_scale"])
+    return c
+
+
+@pytest.mark.parametrize("D,bs,Hq,Hkv", [(128, 16, 8, 2), (64, 32, 16, 1)])
+def test_chunked_fp8_cache(D, bs, Hq, Hkv):
+    """E4M3 cache through the chunked call: prefill rows on the matrix-core
+    kernel (fp8 widened to bf16 while staging), against the oracle on the
+    dequantised cache."""
+    say("chunked fp8", D, bs, Hq, Hkv)
+    c = _chunk_case_fp8(810 + D, R=5, Lmax=300, qmax=90, Hq=Hq, Hkv=Hkv, D=D, bs=bs)
+
+    def dev16(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    cache = pkv.CacheView.from_planes(torch.from_numpy(c["kp"]).cuda(), torch.from_numpy(c["vp"]).cuda(),
+                                      c["k_scale"], c["v_scale"])
+    out = pkv.paged_attention_chunked(dev16(c["q"]), torch.from_numpy(c["qsl"]).cuda(),
+                                      torch.from_numpy(c["L"]).cuda(), int(np.diff(c["qsl"]).max()),
+                                      cache, torch.from_numpy(c["bt"]).cuda(), int(c["L"].max()), 0.09)
+    torch.cuda.synchronize()
+    ref = attention.paged_attention(c["q"], "bf16", c["kp"], c["vp"], "fp8", c["bt"], c["L"],
+                                    c["qsl"], 0.09, k_scale=c["k_scale"], v_scale=c["v_scale"])
+    assert np.isfinite(out_f64(out)).all()
+    assert max_err(out_f64(out), ref) <= 3e-2
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (4, 2), (16, 2), (16, 1)])
+@pytest.mark.parametrize("causal,W", [(True, 0), (True, 300), (False, 100)])
+def test_chunked_long_queries_span_several_tiles(Hq, Hkv, causal, W):
+    """Queries of up to 600 tokens: several query tiles per request (ragged
+    last tile), keys over many 32-key tiles, windows that start mid-tile.
+    Early causal rows see one or two keys, so their outputs are single V
+    values; V ~ N(0, 0.2^2) keeps every output below 1, where bf16's own
+    rounding of the output stays inside the 2e-3 bound."""
+    say("chunked long queries", Hq, Hkv, causal, W)
+    c = _chunk_case(900 + Hq + Hkv + W, R=4, Lmax=900, qmax=600, Hq=Hq, Hkv=Hkv, D=128, bs=16,
+                    v_sigma=0.2)
+    out, ref = _run_chunked(c, causal, W)
+    assert max_err(out_f64(out), ref) <= 2e-3
+
+
+def test_chunked_unmapped_block_poisons_only_rows_that_reach_it():
+    """A prefill request whose table has an unmapped entry: causal rows whose
+    keys stop before that block are exact, rows that reach it are NaN."""
+    say("chunked unmapped block")
+    bs, D, Hq, Hkv = 16, 128, 8, 2
+    rng = np.random.default_rng(77)
+    L = np.array([10, 200], np.int32)
+    ql = np.array([1, 40], np.int32)
+    qsl = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    nb = 64
+    perm = rng.permutation(nb)
+    bt = np.full((2, 13), -1, np.int32)
+    bt[0, :1] = perm[:1]
+    bt[1, :13] = perm[1:14]
+    shape = (nb, bs, Hkv, D)
+    kp = bf16_bits(rng.standard_normal(shape).astype(np.float32) * 0.4)
+    vp = bf16_bits(rng.standard_normal(shape).astype(np.float32) * 0.4)
+    q = bf16_bits(rng.standard_normal((int(qsl[-1]), Hq, D)).astype(np.float32) * 0.4)
+    ref = attention.paged_attention(q, "bf16", kp, vp, "bf16", bt, L, qsl, 0.125)
+    bad = bt.copy()
+    bad[1, 11] = -1                       # keys 176..191
+
+    def dev16(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    cache = pkv.CacheView.from_planes(dev16(kp), dev16(vp))
+    out = pkv.paged_attention_chunked(dev16(q), torch.from_numpy(qsl).cuda(), torch.from_numpy(L).cuda(),
+                                      40, cache, torch.from_numpy(bad).cuda(), 200, 0.125)
+    torch.cuda.synchronize()
+    got = out_f64(out)
+    pos = 160 + np.arange(40)             # positions of request 1's queries
+    reach = pos >= 176
+    rows = 1 + np.arange(40)
+    assert np.isnan(got[rows[reach]]).all()
+    assert max_err(got[rows[~reach]], ref[rows[~reach]]) <= 2e-3
+    assert max_err(got[:1], ref[:1]) <= 2e-3
 
 
 # --------------------------------------------------------------------------- hybrid
