@@ -27,6 +27,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E, AMD's published peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+DATA_NOTE = {
+    "llama8b": "synthetic (seeded N(0,1)/sqrt(128) bf16 K/V/Q; lengths uniform 128..2048)",
+    "llama70b": "synthetic (seeded N(0,1)/sqrt(128) bf16 K/V/Q; 32 sequences of 4096 tokens)",
+    "fp8": "synthetic (seeded N(0,1) K/V quantised to e4m3 with amax/448 scales, N(0,1) bf16 Q; "
+           "lognormal lengths, median 1024, clipped to 16..32768)",
+    "hybrid": "synthetic (seeded N(0,1)/sqrt(128) bf16; 96 decode requests 1k..16k + 4 prefill "
+              "chunks of 512, full and sliding-window groups over shared tensors)",
+}
 POOLS = 3
 SPLIT_KERNEL = "decode_flat_kernel"
 PMC_FILE = os.path.join(ROOT, "profiles", "decode_split_llama8b_b64_pmc.json")
@@ -36,6 +45,9 @@ KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_mapping_amd", "csrc", "decode
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--workload", default="llama8b", choices=["llama8b", "llama70b", "fp8", "hybrid"],
+                   help="llama8b (default line), llama70b (80 allocated layers), fp8, hybrid")
+    p.add_argument("--layers", type=int, default=80, help="llama70b: layers allocated and rotated")
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -102,9 +114,9 @@ def cpu_baseline(w, sample_seqs, min_seconds=10.0):
         slots, _ = paging.slot_mapping(sub.block_table, sub.query_start_loc, sub.num_computed,
                                        sub.block_size)
         kp, vp = paging.cache_write(sub.k_plane, sub.v_plane, sub.new_k, sub.new_v, slots, "bf16",
-                                    "bf16")
-        attention.paged_decode(sub.q, "bf16", kp, vp, "bf16", sub.block_table, sub.seq_lens,
-                               sub.scale)
+                                    sub.cache_dtype, k_scale=sub.k_scale, v_scale=sub.v_scale)
+        attention.paged_decode(sub.q, "bf16", kp, vp, sub.cache_dtype, sub.block_table, sub.seq_lens,
+                               sub.scale, k_scale=sub.k_scale, v_scale=sub.v_scale)
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
@@ -181,6 +193,174 @@ def summarize_profiles(out_dir):
     return rec
 
 
+def rotating_pools(w, base, dev, count):
+    """`count` KV pools holding the same logical data under different physical
+    block permutations (so the last-level cache cannot serve the reads)."""
+    import torch
+    import paged_kv_cache_mapping_amd as pkv
+    nb = w.num_blocks
+    pools = [(base.cache, base.block_table)]
+    rng = np.random.default_rng(1234)
+    for _ in range(count - 1):
+        perm = rng.permutation(nb)
+        pt = torch.from_numpy(perm.astype(np.int64)).to(dev)
+        k2 = torch.empty_like(base.cache.k)
+        v2 = torch.empty_like(base.cache.v)
+        k2.index_copy_(0, pt, base.cache.k)
+        v2.index_copy_(0, pt, base.cache.v)
+        bt = np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)], -1).astype(np.int32)
+        pools.append((pkv.CacheView.from_planes(k2, v2, base.cache.k_scale, base.cache.v_scale),
+                      torch.from_numpy(bt).to(dev)))
+    return pools
+
+
+def layer_pools(w, base, dev, layers):
+    """The whole model's cache at once: one byte buffer per layer (the pages'
+    allocation), each layer's used blocks filled with the workload's data
+    under its own block permutation; returns the per-layer (view, table)
+    pairs and the allocation size and time."""
+    import torch
+    from paged_kv_cache_mapping_amd import kv_cache
+    spec = kv_cache.KVCacheSpec(w.block_size, w.num_kv_heads, w.head_dim, w.cache_dtype)
+    names = ["layer%d" % i for i in range(layers)]
+    cfg = kv_cache.hybrid_config([kv_cache.KVCacheGroupSpec(names, spec)], w.num_blocks)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    views, bufs = kv_cache.allocate(cfg, dev)
+    torch.cuda.synchronize()
+    alloc_s = time.perf_counter() - t0
+    used = np.unique(w.block_table[w.block_table >= 0]).astype(np.int64)
+    used_t = torch.from_numpy(used).to(dev)
+    ksrc = base.cache.k.index_select(0, used_t)
+    vsrc = base.cache.v.index_select(0, used_t)
+    rng = np.random.default_rng(4321)
+    pools = []
+    for name in names:
+        perm = rng.permutation(w.num_blocks)
+        dst = torch.from_numpy(perm[used]).to(dev)
+        v = views[name]
+        v.k.index_copy_(0, dst, ksrc)
+        v.v.index_copy_(0, dst, vsrc)
+        bt = np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)], -1).astype(np.int32)
+        pools.append((v, torch.from_numpy(bt).to(dev)))
+    torch.cuda.synchronize()
+    total = sum(t.size for t in cfg.tensors)
+    return pools, {"layers_allocated": layers, "allocated_bytes": int(total),
+                   "allocation_s": round(alloc_s, 3)}
+
+
+def hybrid_layer_bytes(w, W):
+    """Algorithmic bytes of one hybrid layer's attention: every request reads
+    the keys its queries can see once (K and V), plus q and out."""
+    ql = np.diff(w.query_start_loc)
+    kv = 0
+    flops = 0
+    for L, q in zip(w.seq_lens.astype(np.int64), ql.astype(np.int64)):
+        p0 = L - q
+        lo = max(0, p0 - W + 1) if W > 0 else 0
+        kv += (L - lo) * w.num_kv_heads * w.head_dim * 2 * 2
+        if q > 1:
+            pos = p0 + np.arange(q)
+            vis = pos + 1 - (np.maximum(0, pos - W + 1) if W > 0 else 0)
+            flops += int(vis.sum()) * w.num_q_heads * w.head_dim * 4
+    T = w.num_tokens
+    qo = T * w.num_q_heads * w.head_dim * 2 * 2
+    write = T * w.num_kv_heads * w.head_dim * 2 * 2 * 2 + T * 8
+    return kv + qo, write, flops
+
+
+def bench_hybrid(args, dev):
+    """Hybrid KV groups with chunked prefill: four layers (full, SWA, full,
+    SWA) over two shared tensors and two group tables; one step = per group
+    slot mapping, then per layer cache write + chunked attention."""
+    import torch
+    import paged_kv_cache_mapping_amd as pkv
+    from paged_kv_cache_mapping_amd import workloads
+    w = workloads.hybrid_chunked()
+    cfg, views, bufs = w.device_tensors(dev)
+    qsl = torch.from_numpy(w.query_start_loc).to(dev)
+    sl = torch.from_numpy(w.seq_lens).to(dev)
+    nc = torch.from_numpy(w.num_computed).to(dev)
+    tables = [torch.from_numpy(t).to(dev) for t in w.tables]
+    layers = [name for grp in w.groups for name in grp]
+    layers.sort()
+    group_of = {name: g for g, grp in enumerate(w.groups) for name in grp}
+    inputs = {name: w.step_inputs(int(name[1:]), dev) for name in layers}
+    slots = [torch.empty(w.num_tokens, dtype=torch.int64, device=dev) for _ in w.groups]
+    outs = {name: torch.empty_like(inputs[name][0]) for name in layers}
+    ws = {}
+    for g, W in enumerate(w.windows):
+        nbytes = pkv.chunked_workspace_size(w.num_tokens, len(w.seq_lens), w.num_q_heads, views[layers[0]],
+                                            w.max_query_len, w.max_seq_len, W)
+        ws[g] = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+
+    def attend(name):
+        g = group_of[name]
+        q, nk, nv = inputs[name]
+        pkv.cache_write(nk, nv, slots[g], views[name])
+        pkv.paged_attention_chunked(q, qsl, sl, w.max_query_len, views[name], tables[g], w.max_seq_len,
+                                    w.scale, causal=True, sliding_window=w.windows[g], out=outs[name],
+                                    workspace=ws[g])
+
+    def step():
+        for g in range(len(w.groups)):
+            pkv.slot_mapping(tables[g], qsl, nc, w.block_size, w.num_blocks, out=slots[g])
+        for name in layers:
+            attend(name)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    per_layer = {}
+    for name in layers:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            attend(name)
+        b.record()
+        torch.cuda.synchronize()
+        per_layer[name] = a.elapsed_time(b) / args.steps
+    step_bytes = 0
+    layer_rec = {}
+    total_flops = 0
+    for name in layers:
+        W = w.windows[group_of[name]]
+        rd, wr, fl = hybrid_layer_bytes(w, W)
+        step_bytes += rd + wr
+        total_flops += fl
+        layer_rec[name] = {"window": W, "us": round(per_layer[name] * 1e3, 1),
+                           "GBps": round((rd + wr) / (per_layer[name] * 1e-3) / 1e9, 1),
+                           "prefill_gflop": round(fl / 1e9, 2)}
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dom = max(layers, key=lambda n: per_layer[n])
+    rd, wr, _ = hybrid_layer_bytes(w, w.windows[group_of[dom]])
+    gbps = (rd + wr) / (per_layer[dom] * 1e-3) / 1e9
+    res = {
+        "metric": "paged decode attention HBM GB/s (% of peak) + KV cache writes tokens/s, 1 GPU",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": DATA_NOTE["hybrid"],
+        "config": {"workload": "hybrid_groups_chunked_prefill_96dec_4x512", "layers": layers,
+                   "num_tokens": w.num_tokens, "requests": int(len(w.seq_lens)),
+                   "windows": list(w.windows), "pool_blocks": int(w.num_blocks),
+                   "context_tokens": int(w.seq_lens.sum()), "parallelism": "none (1 GPU)"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "layers": layer_rec,
+        "prefill_gflop_per_step": round(total_flops / 1e9, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "chunked attention of layer %s (all its kernels)" % dom},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_profiles:
@@ -196,22 +376,18 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = workloads.llama8b_decode()
+    if args.workload == "hybrid":
+        return bench_hybrid(args, dev)
+    w = {"llama8b": workloads.llama8b_decode, "llama70b": workloads.llama70b_decode,
+         "fp8": workloads.fp8_decode}[args.workload]()
     base = w.device(dev)
     nb = w.num_blocks
-
-    # three pools with the same logical data under different permutations
-    pools = [(base.cache, base.block_table)]
-    rng = np.random.default_rng(1234)
-    for _ in range(POOLS - 1):
-        perm = rng.permutation(nb)
-        pt = torch.from_numpy(perm.astype(np.int64)).to(dev)
-        k2 = torch.empty_like(base.cache.k)
-        v2 = torch.empty_like(base.cache.v)
-        k2.index_copy_(0, pt, base.cache.k)
-        v2.index_copy_(0, pt, base.cache.v)
-        bt = np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)], -1).astype(np.int32)
-        pools.append((pkv.CacheView.from_planes(k2, v2), torch.from_numpy(bt).to(dev)))
+    extra = {}
+    if args.workload == "llama70b":
+        pools, extra = layer_pools(w, base, dev, args.layers)
+    else:
+        pools = rotating_pools(w, base, dev, POOLS)
+    npools = len(pools)
 
     plan = pkv.decode_plan(w.num_reqs, w.num_q_heads, base.cache, w.max_seq_len)
     pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, base.cache, w.max_seq_len,
@@ -224,7 +400,7 @@ def main():
     slots = torch.empty(w.num_reqs, dtype=torch.int64, device=dev)
 
     def step(i):
-        cache, bt = pools[i % POOLS]
+        cache, bt = pools[i % npools]
         pkv.slot_mapping(bt, base.query_start_loc, base.num_computed, w.block_size, nb, out=slots)
         pkv.cache_write(base.new_k, base.new_v, slots, cache)
         pkv.paged_attention_decode_partials(base.q, cache, bt, base.seq_lens, w.max_seq_len, w.scale,
@@ -252,7 +428,7 @@ def main():
     torch.cuda.synchronize()
     a.record()
     for i in range(args.steps):
-        cache, bt = pools[i % POOLS]
+        cache, bt = pools[i % npools]
         pkv.paged_attention_decode_partials(base.q, cache, bt, base.seq_lens, w.max_seq_len, w.scale,
                                             plan, ws, out)
     b.record()
@@ -265,7 +441,7 @@ def main():
 
     # bulk KV writes: distinct random slots, bf16 -> bf16 and bf16 -> fp8
     writes = {}
-    for T in (16384, 131072):
+    for T in ((16384, 131072) if args.workload == "llama8b" else ()):
         gen = torch.Generator(device=dev).manual_seed(T)
         kx = torch.randn((T, w.num_kv_heads, w.head_dim), generator=gen, device=dev).to(torch.bfloat16)
         vx = torch.randn((T, w.num_kv_heads, w.head_dim), generator=gen, device=dev).to(torch.bfloat16)
@@ -309,7 +485,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    traffic = traffic_from_profile()
+    traffic = traffic_from_profile() if args.workload == "llama8b" else None
     res = {
         "metric": "paged decode attention HBM GB/s (% of peak) + KV cache writes tokens/s, 1 GPU",
         "value": round(value, 1),
@@ -321,15 +497,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1)/sqrt(128) bf16 K/V/Q; lengths uniform 128..2048)",
+        "dtype": "bf16" if w.cache_dtype == "bf16" else "e4m3 KV, bf16 q/out",
+        "data": DATA_NOTE[args.workload],
         "config": {"workload": w.name, "batch": w.num_reqs, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
-                   "block_size": w.block_size, "pool_blocks": nb, "rotating_pools": POOLS,
+                   "block_size": w.block_size, "pool_blocks": nb, "rotating_pools": npools,
                    "context_tokens": int(w.seq_lens.sum()), "parallelism": "none (1 GPU)",
                    "scheme": int(plan.scheme), "workers": int(plan.num_workers),
                    "split_blocks": int(plan.split_blocks), "max_splits": int(plan.max_splits),
-                   "lead_workers": int(plan.lead_workers), "trail_share_pct": int(plan.trail_share_pct)},
+                   "lead_workers": int(plan.lead_workers), "trail_share_pct": int(plan.trail_share_pct),
+                   **extra},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_attention": {"split_kernel_us": round(split_ms * 1e3, 2),
                              "split_GBps": round(split_gbps, 1),
