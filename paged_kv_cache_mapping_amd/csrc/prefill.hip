@@ -10,7 +10,7 @@
 // window keeps the most recent W positions ("Deep Dive into vLLM Worker-Side
 // GPU KV Cache Initialization", "Hybrid Attention Mechanisms").
 //
-// Decomposition (MI355X): one workgroup of four waves per (request, KV head,
+// Decomposition (MI355X): one workgroup of eight waves per (request, KV head,
 // tile of query tokens).  A wave owns NBW blocks of 16 rows; a row is one
 // (query token, query head of the group).  Keys stream through LDS in tiles
 // of 32 (K and V double-buffered, staged by the whole workgroup from the
@@ -46,23 +46,30 @@ typedef float pf_f32x4 __attribute__((ext_vector_type(4)));
 typedef short pf_i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) pf_i16x4 lds_i16x4;
 
-constexpr int kPfWaves = 4;
+constexpr int kPfWaves = 8;          // two per SIMD: one computes while the other waits
+constexpr int kPfThreads = kPfWaves * 64;
 constexpr int kPfKeys = 32;          // keys per tile
 constexpr float kPfLazy = 8.0f;      // keep a stale max until a score beats it by 2^8
 
 template <int D, int G>
 struct PfShape {
-  static constexpr int NBW = D >= 256 ? 2 : 4;   // 16-row blocks per wave
+  static constexpr int NBW = 2;                  // 16-row blocks per wave
   static constexpr int TPN = 16 / G;             // query tokens per row block
   static constexpr int TW = NBW * TPN;           // query tokens per wave
   static constexpr int TWG = kPfWaves * TW;      // query tokens per workgroup
   static constexpr int NC = D / 32;              // k-chunks of the score product
   static constexpr int MB = D / 16;              // 16-dim blocks of the output
-  static constexpr int RS = D * 2 + 16;          // LDS bytes per staged key row
-  static constexpr int TILE = kPfKeys * RS;      // LDS bytes of one K or V tile
+  // LDS bytes per staged key row.  K rows are read 16 rows x 16 bytes per
+  // pass (a 16-byte pad puts the rows on disjoint banks); V rows are read by
+  // the transpose load, 8 rows x 32 bytes per pass (a 32-byte pad does).
+  static constexpr int RSK = D * 2 + 16;
+  static constexpr int RSV = D * 2 + 32;
+  static constexpr int TILEK = kPfKeys * RSK;    // LDS bytes of one K tile
+  static constexpr int TILEV = kPfKeys * RSV;    // LDS bytes of one V tile
+  static constexpr int TILE = TILEK + TILEV;     // LDS bytes of one staged K + V tile
   static constexpr int CPR = D / 8;              // 16-byte bf16 chunks per key row
   static constexpr int CPT = kPfKeys * CPR;      // chunks per tile
-  static constexpr int CPTH = (CPT + 255) / 256; // chunks per thread and plane
+  static constexpr int CPTH = (CPT + kPfThreads - 1) / kPfThreads;  // chunks per thread and plane
   static_assert(16 % G == 0, "group must divide 16");
 };
 
@@ -70,18 +77,18 @@ inline size_t pf_align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
 template <int D, int G>
 size_t pf_lds_bytes(int max_blocks) {
-  return 4 * (size_t)PfShape<D, G>::TILE + pf_align16((size_t)max_blocks * sizeof(int));
+  return 2 * (size_t)PfShape<D, G>::TILE + pf_align16((size_t)max_blocks * sizeof(int));
 }
 
 template <int D, int G, int KV>
-__global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPfThreads) void prefill_tile_kernel(PrefillArgs a) {
   using S = PfShape<D, G>;
   constexpr int NBW = S::NBW, TPN = S::TPN, TW = S::TW, TWG = S::TWG;
-  constexpr int NC = S::NC, MB = S::MB, RS = S::RS, TILE = S::TILE;
+  constexpr int NC = S::NC, MB = S::MB, RSK = S::RSK, RSV = S::RSV, TILE = S::TILE;
   constexpr int CPR = S::CPR, CPT = S::CPT, CPTH = S::CPTH;
   constexpr int kElt = KV == PKV_BF16 ? 2 : 1;
   extern __shared__ __align__(16) char lds[];
-  int* tab = reinterpret_cast<int*>(lds + 4 * TILE);   // phys block or -1, from block b0
+  int* tab = reinterpret_cast<int*>(lds + 2 * TILE);   // phys block or -1, from block b0
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -111,7 +118,7 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
   if (!req_ok) {
     // lengths inconsistent with the arguments: NaN rows, as the other paths
     const int n = (tok_hi - tok_lo) * G * D;
-    for (int e = tid; e < n; e += 256) {
+    for (int e = tid; e < n; e += kPfThreads) {
       const int t = e / (G * D);
       const int rem = e - t * G * D;
       out[((int64_t)(q0 + tok_lo + t) * hq + kvh * G) * D + rem] = 0x7FC0;
@@ -120,7 +127,7 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
   }
 
   // ---- table slice of the blocks this workgroup can touch
-  for (int i = tid; i < nblk; i += 256) {
+  for (int i = tid; i < nblk; i += kPfThreads) {
     const int j = b0 + i;
     int e = -1;
     if (j < a.bt_stride) e = a.bt[(int64_t)r * a.bt_stride + j];
@@ -173,39 +180,36 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
     for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = pf_f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- staging: chunk c = tid + 256 j of a tile is key c / CPR, 16 bytes
+  // ---- staging: chunk c = tid + 512 j of a tile is key c / CPR, 16 bytes
   // (8 bf16) at column chunk c % CPR; keys outside [klo, khi] or on an
   // unmapped block stage as zeros
   const int64_t blk_bytes = a.block_stride * kElt;
   const int row_bytes = a.num_kv_heads * D * kElt;
   const int bmask = (1 << a.bs_log2) - 1;
   typedef typename std::conditional<KV == PKV_BF16, uint4, uint2>::type Raw;
-  Raw kr[CPTH], vr[CPTH];
-  auto stage_load = [&](int kt) __attribute__((always_inline)) {
+  // Loads are issued unconditionally (keys outside [klo, khi] or on unmapped
+  // blocks read block 0's first row, which always exists) and their data is
+  // dropped afterwards: a load skipped under a branch would leave the wait
+  // counters unknown at the store and make it wait for every load in flight.
+  struct Stage {
+    Raw k[CPTH], v[CPTH];
+    bool ok[CPTH];
+  };
+  auto stage_load = [&](int kt, Stage& st) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < CPTH; ++j) {
-      const int c = tid + 256 * j;
-      Raw kz, vz;
-      if constexpr (KV == PKV_BF16) {
-        kz = make_uint4(0, 0, 0, 0);
-        vz = make_uint4(0, 0, 0, 0);
-      } else {
-        kz = make_uint2(0, 0);
-        vz = make_uint2(0, 0);
-      }
-      if (c < CPT) {
-        const int kp = kt * kPfKeys + c / CPR;
-        const int cc = c % CPR;
-        const int phys = (kp >= klo && kp <= khi) ? tab[(kp >> a.bs_log2) - b0] : -1;
-        if (phys >= 0) {
-          const int64_t off = (int64_t)phys * blk_bytes + (int64_t)(kp & bmask) * row_bytes +
-                              kvh * D * kElt + cc * 8 * kElt;
-          kz = *reinterpret_cast<const Raw*>(a.kbase + off);
-          vz = *reinterpret_cast<const Raw*>(a.vbase + off);
-        }
-      }
-      kr[j] = kz;
-      vr[j] = vz;
+      const int c = (tid + kPfThreads * j) % CPT;     // threads past the tile repeat a chunk
+      const int kp = kt * kPfKeys + c / CPR;
+      const int cc = c % CPR;
+      const bool in = kp >= klo && kp <= khi;
+      const int phys = in ? tab[(kp >> a.bs_log2) - b0] : -1;
+      const bool ok = phys >= 0;
+      const int64_t off = ok ? (int64_t)phys * blk_bytes + (int64_t)(kp & bmask) * row_bytes +
+                                   kvh * D * kElt + cc * 8 * kElt
+                             : (int64_t)(cc * 8 * kElt);
+      st.k[j] = *reinterpret_cast<const Raw*>(a.kbase + off);
+      st.v[j] = *reinterpret_cast<const Raw*>(a.vbase + off);
+      st.ok[j] = ok;
     }
   };
   auto widen = [&](const Raw& x) __attribute__((always_inline)) -> uint4 {
@@ -216,16 +220,16 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
                         e4m3x2_to_bf16x2<false>(x.y), e4m3x2_to_bf16x2<true>(x.y));
     }
   };
-  auto stage_store = [&](int buf) __attribute__((always_inline)) {
-    char* kt_l = lds + buf * 2 * TILE;
-    char* vt_l = kt_l + TILE;
+  auto stage_store = [&](int buf, const Stage& st) __attribute__((always_inline)) {
+    char* kt_l = lds + buf * TILE;
+    char* vt_l = kt_l + S::TILEK;
 #pragma unroll
     for (int j = 0; j < CPTH; ++j) {
-      const int c = tid + 256 * j;
+      const int c = tid + kPfThreads * j;
       if (c < CPT) {
-        const int o = (c / CPR) * RS + (c % CPR) * 16;
-        *reinterpret_cast<uint4*>(kt_l + o) = widen(kr[j]);
-        *reinterpret_cast<uint4*>(vt_l + o) = widen(vr[j]);
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(kt_l + (c / CPR) * RSK + (c % CPR) * 16) = st.ok[j] ? widen(st.k[j]) : z;
+        *reinterpret_cast<uint4*>(vt_l + (c / CPR) * RSV + (c % CPR) * 16) = st.ok[j] ? widen(st.v[j]) : z;
       }
     }
   };
@@ -233,8 +237,8 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
   auto compute = [&](int kt, int buf) __attribute__((always_inline)) {
     const int kbase = kt * kPfKeys;
     if (!wave_live || kbase > wkhi || kbase + kPfKeys - 1 < wklo) return;
-    const char* kt_l = lds + buf * 2 * TILE;
-    const char* vt_l = kt_l + TILE;
+    const char* kt_l = lds + buf * TILE;
+    const char* vt_l = kt_l + S::TILEK;
     // an unmapped block among the tile's keys makes the rows that see it NaN
     bool tile_bad = false;
     {
@@ -252,7 +256,7 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        ak[kh][c] = *reinterpret_cast<const pf_bf16x8*>(kt_l + (16 * kh + ln16) * RS + (8 * grp + 32 * c) * 2);
+        ak[kh][c] = *reinterpret_cast<const pf_bf16x8*>(kt_l + (16 * kh + ln16) * RSK + (8 * grp + 32 * c) * 2);
 
     pf_bf16x8 pb[NBW], pl[NBW];   // P = bf16 high part + bf16 remainder
 #pragma unroll
@@ -324,8 +328,8 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
     const int vcol = 4 * (ln16 & 3);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const char* v1 = vt_l + vrow * RS + (16 * mb + vcol) * 2;
-      const char* v2 = v1 + 16 * RS;
+      const char* v1 = vt_l + vrow * RSV + (16 * mb + vcol) * 2;
+      const char* v2 = v1 + 16 * RSV;
       const pf_i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v1));
       const pf_i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v2));
       const pf_bf16x8 av = __builtin_bit_cast(
@@ -339,18 +343,31 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(PrefillArgs a) {
     }
   };
 
-  // ---- key tiles, double-buffered through LDS, one barrier per tile
+  // ---- key tiles: loads run three tiles ahead in a ring of register
+  // stages, tiles are double-buffered in LDS, one barrier per tile.  Tile t
+  // is loaded at step t - 3 into stage t % 3 (unconditionally: past the last
+  // tile the last one is fetched again), stored to LDS buffer t % 2 at step
+  // t - 1 and folded at step t.
   const int kt0 = klo / kPfKeys, kt1 = khi / kPfKeys;
-  stage_load(kt0);
-  stage_store(0);
+  Stage s0, s1, s2;
+  stage_load(kt0, s0);
+  stage_load(min(kt0 + 1, kt1), s1);
+  stage_load(min(kt0 + 2, kt1), s2);
+  stage_store(0, s0);
   __syncthreads();
-  for (int kt = kt0; kt <= kt1; ++kt) {
-    const int buf = (kt - kt0) & 1;
-    const bool more = kt < kt1;
-    if (more) stage_load(kt + 1);
-    compute(kt, buf);
-    if (more) stage_store(buf ^ 1);
+  auto step = [&](int kt, Stage& cur, const Stage& next) __attribute__((always_inline)) {
+    const int rel = kt - kt0;
+    if (kt + 1 <= kt1) stage_store((rel + 1) & 1, next);
+    stage_load(min(kt + 3, kt1), cur);
+    compute(kt, rel & 1);
     __syncthreads();
+  };
+  for (int kt = kt0; kt <= kt1; kt += 3) {
+    step(kt, s0, s1);
+    if (kt + 1 > kt1) break;
+    step(kt + 1, s1, s2);
+    if (kt + 2 > kt1) break;
+    step(kt + 2, s2, s0);
   }
 
   // ---- normalise and store: lane l holds dims 16 mb + 4 (l / 16) + i of row l % 16
@@ -410,7 +427,7 @@ int pf_tokens(int d, int g) {
 template <int D, int G, int KV>
 void pf_launch(const PrefillArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((long long)a.num_reqs * a.tiles_per_req), (unsigned)a.num_kv_heads);
-  prefill_tile_kernel<D, G, KV><<<grid, 256, pf_lds_bytes<D, G>(a.max_blocks), s>>>(a);
+  prefill_tile_kernel<D, G, KV><<<grid, kPfThreads, pf_lds_bytes<D, G>(a.max_blocks), s>>>(a);
 }
 
 template <int D, int KV>
@@ -447,7 +464,7 @@ bool prefill_supported(int kv_dtype, int head_dim, int group, int max_seq_len, i
   const int tok = pf_tokens(head_dim, group);
   const int mb = pf_max_blocks(max_seq_len, block_size, window, tok > max_query_len ? tok : max_query_len);
   // the staged tiles plus the table slice within 64 KiB of LDS per workgroup
-  const size_t bytes = 4 * (size_t)(32 * (head_dim * 2 + 16)) + pf_align16((size_t)mb * 4);
+  const size_t bytes = 2 * (size_t)(32 * (head_dim * 4 + 48)) + pf_align16((size_t)mb * 4);
   return bytes <= 64 * 1024;
 }
 
