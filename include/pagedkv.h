@@ -248,8 +248,9 @@ PKV_API int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dtype
  * Workspace layout (float32): acc [rows, Hq, max_splits, D], then for
  * scheme 0 m [rows, Hq, max_splits] and l [rows, Hq, max_splits]; for
  * scheme 1 (G = heads_per_item) records [rows, Hq / G, max_splits, 2, G]
- * holding the G heads' m then their l, followed by int32 piece counts
- * [rows, Hq / G].
+ * holding the G heads' m then their l, followed by int32 pairs (piece
+ * count, output row) [rows, Hq / G, 2].  acc holds dequantised V sums (for an
+ * fp8 cache the V scale is already applied), so phase 2 needs no cache.
  */
 PKV_API int pkv_paged_attention_decode_partials(void* out, const void* q,
                                         int32_t q_dtype, int32_t num_seqs,

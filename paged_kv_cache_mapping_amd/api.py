@@ -171,7 +171,7 @@ def tune_plan(plan, num_rows, num_q_heads, cache, max_seq_len, sliding_window=0,
     if plan.scheme == 1:
         plan.max_splits = -(-nvis // plan.split_blocks) + 1
         plan.workspace_bytes = (per_slot * plan.max_splits
-                                + num_rows * (num_q_heads // plan.heads_per_item) * 4)
+                                + num_rows * (num_q_heads // plan.heads_per_item) * 8)
     else:
         plan.max_splits = -(-nvis // plan.split_blocks)
         plan.workspace_bytes = per_slot * plan.max_splits if plan.max_splits > 1 else 0

@@ -59,7 +59,7 @@ static size_t partial_bytes(int rows, int hq, int splits, int d) {
 static size_t plan_bytes(const pkv_decode_plan& p, int rows, int hq, int d) {
   if (p.scheme == 1)
     return partial_bytes(rows, hq, p.max_splits, d) +
-           (size_t)rows * (hq / p.heads_per_item) * sizeof(int32_t);
+           (size_t)rows * (hq / p.heads_per_item) * 2 * sizeof(int32_t);
   return p.max_splits > 1 ? partial_bytes(rows, hq, p.max_splits, d) : 0;
 }
 
@@ -350,6 +350,7 @@ extern "C" int pkv_paged_attention_decode_combine(void* out, int32_t out_dtype, 
   DecodeArgs a = {};
   a.out = out;
   a.num_rows = num_seqs;
+  a.num_tokens = num_seqs;
   a.num_q_heads = num_q_heads;
   a.head_dim = head_dim;
   a.bs_log2 = log2_int(block_size);

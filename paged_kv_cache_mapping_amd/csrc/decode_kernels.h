@@ -431,7 +431,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     const int64_t pr = ((int64_t)b * a.num_q_heads + h0 + h) * a.max_splits + s;
     float* dst = a.ws_acc + pr * D + sub * EPL;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) dst[e] = acc[h][e];
+    for (int e = 0; e < EPL; ++e) dst[e] = acc[h][e] * a.v_scale;   // partials hold dequantised V sums
     if (sub == 0) {
       a.ws_m[pr] = m[h];
       a.ws_l[pr] = l[h];
@@ -749,7 +749,7 @@ __global__ __launch_bounds__(64) void decode_split_uni_kernel(DecodeArgs a) {
     const int64_t pr = ((int64_t)b * a.num_q_heads + h0 + h) * a.max_splits + s;
     float* dst = a.ws_acc + pr * D + sub * EPL;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) dst[e] = acc[h][e];
+    for (int e = 0; e < EPL; ++e) dst[e] = acc[h][e] * a.v_scale;   // partials hold dequantised V sums
     if (sub == 0) {
       a.ws_m[pr] = m[h];
       a.ws_l[pr] = l[h];
@@ -1036,7 +1036,9 @@ __global__ __launch_bounds__(64) void decode_flat_kernel(DecodeArgs a) {
           float* dst = a.ws_acc + pr * D + vsub * VEPL;
 #pragma unroll
           for (int e = 0; e < VEPL; e += 4) {
-            const f32x4_t v4 = {acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]};
+            // partials hold dequantised V sums (the fp8 V scale applied)
+            const f32x4_t v4 = {acc[h][e] * a.v_scale, acc[h][e + 1] * a.v_scale,
+                                acc[h][e + 2] * a.v_scale, acc[h][e + 3] * a.v_scale};
             __builtin_nontemporal_store(v4, reinterpret_cast<f32x4_t*>(dst + e));
           }
         }
@@ -1060,7 +1062,10 @@ __global__ __launch_bounds__(64) void decode_flat_kernel(DecodeArgs a) {
         }
       }
     }
-    if (piece == 0 && lane == 0) a.ws_np[(int64_t)b * kvgroups + kvg] = npieces;
+    if (piece == 0 && lane == 0) {
+      a.ws_np[2 * ((int64_t)b * kvgroups + kvg)] = npieces;
+      a.ws_np[2 * ((int64_t)b * kvgroups + kvg) + 1] = s_tok;
+    }
   };
 
   struct Buf {
@@ -1302,19 +1307,85 @@ __global__ __launch_bounds__(64) void decode_flat_kernel(DecodeArgs a) {
   }
   if (cur >= 0) flush();
 
-  // ---- rows that cannot be computed: NaN output, written by one worker each
+  // ---- rows without units, one worker each: rows this pass skips (another
+  // pass owns them) get a piece count of 0 so that the merge phase leaves
+  // them alone; rows that cannot be computed also get NaN output
   for (int r = blockIdx.x; r < a.num_rows; r += W) {
     const RowInfo ri = row_info(a, r);
-    if (ri.skip || ri.valid) continue;
-    const int64_t base = (int64_t)ri.tok * a.num_q_heads * D;
-    for (int e = lane; e < a.num_q_heads * D; e += kWave)
-      reinterpret_cast<uint16_t*>(a.out)[base + e] = 0x7FC0;
-    for (int g = lane; g < kvgroups; g += kWave) a.ws_np[(int64_t)r * kvgroups + g] = 0;
+    if (ri.valid && !ri.skip) continue;
+    if (!ri.skip) {
+      const int64_t base = (int64_t)ri.tok * a.num_q_heads * D;
+      for (int e = lane; e < a.num_q_heads * D; e += kWave)
+        reinterpret_cast<uint16_t*>(a.out)[base + e] = 0x7FC0;
+    }
+    for (int g = lane; g < kvgroups; g += kWave) a.ws_np[2 * ((int64_t)r * kvgroups + g)] = 0;
   }
 }
 
 // --------------------------------------------------------------------------
 // Combine phase: one wave per (row, query head) with more than one split.
+// Merge phase of the balanced scheme: one wave per (row, head group) with
+// more than one piece.  The split phase leaves, per (row, group), the piece
+// count and the output row, so the wave needs no row lookup; lane l merges
+// elements l + 64 i of the group's GT x D block, online over the pieces, four
+// pieces' loads in flight at a time.
+template <int D, int GT, int OT>
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int NE = GT * D;
+  constexpr int EPL = (NE + kWave - 1) / kWave;    // elements per lane
+  constexpr int U = 4;                              // pieces per round of loads
+  const int lane = threadIdx.x;
+  const int groups = a.num_q_heads / GT;
+  const int b = blockIdx.x / groups;
+  const int g = blockIdx.x % groups;
+  const int64_t rg = (int64_t)b * groups + g;
+  const int np = min(a.ws_np[2 * rg], a.max_splits);
+  if (np <= 1) return;                              // written by the split phase (or rejected)
+  const int tok = a.ws_np[2 * rg + 1];
+  if (tok < 0 || tok >= a.num_tokens) return;       // not a row this call wrote
+  const float* ml = a.ws_m + rg * a.max_splits * (2 * GT);
+  float M[EPL], den[EPL], num[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) { M[i] = -INFINITY; den[i] = 0.f; num[i] = 0.f; }
+  for (int s0 = 0; s0 < np; s0 += U) {
+    float mv[U][EPL], lv[U][EPL], av[U][EPL];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = min(s0 + u, np - 1);            // past the end: repeat the last (skipped below)
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int e = lane + kWave * i;
+        const int h = (e < NE ? e : 0) / D;
+        const int d = (e < NE ? e : 0) % D;
+        mv[u][i] = ml[s * (2 * GT) + h];
+        lv[u][i] = ml[s * (2 * GT) + GT + h];
+        av[u][i] = a.ws_acc[(((int64_t)b * a.num_q_heads + g * GT + h) * a.max_splits + s) * D + d];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u >= np) break;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const float mn = fmaxf(M[i], mv[u][i]);
+        const float c_old = M[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M[i] - mn);
+        const float c_new = mv[u][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv[u][i] - mn);
+        den[i] = den[i] * c_old + lv[u][i] * c_new;
+        num[i] = num[i] * c_old + av[u][i] * c_new;
+        M[i] = mn;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + kWave * i;
+    if (e < NE) {
+      float v[1] = {num[i] / den[i]};
+      store_out<OT, 1>(a.out, ((int64_t)tok * a.num_q_heads + g * GT) * D + e, v);
+    }
+  }
+}
+
 template <int D, int OT>
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   constexpr int PER = D >= kWave ? D / kWave : 1;  // elements per lane
@@ -1329,7 +1400,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   int nsplit;
   if (a.stream) {   // rows the split phase rejected have a piece count of 0
     const int groups = a.num_q_heads / a.heads_per_item;
-    nsplit = a.ws_np[(int64_t)b * groups + h / a.heads_per_item];
+    nsplit = a.ws_np[2 * ((int64_t)b * groups + h / a.heads_per_item)];
   } else {
     nsplit = ceil_div(span.nvis, a.split_blocks);
   }
@@ -1374,7 +1445,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
     }
   }
   if (!active) return;
-  const float inv = a.v_scale / den;
+  const float inv = 1.0f / den;
   const int64_t out_row = ((int64_t)tok * a.num_q_heads + h) * D;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -1442,8 +1513,25 @@ int run_stream_dk(const DecodeArgs& a, int workers, hipStream_t s) {
   return PKV_ERR_UNSUPPORTED;
 }
 
+template <int D, int GT>
+void launch_merge(const DecodeArgs& a, int ot, hipStream_t s) {
+  const dim3 grid((unsigned)((long long)a.num_rows * (a.num_q_heads / GT)));
+  if (ot == PKV_F32) decode_merge_kernel<D, GT, PKV_F32><<<grid, 64, 0, s>>>(a);
+  else decode_merge_kernel<D, GT, PKV_BF16><<<grid, 64, 0, s>>>(a);
+}
+
 template <int D>
 int run_combine_d(const DecodeArgs& a, int ot, hipStream_t s) {
+  if (a.stream) {
+    switch (a.heads_per_item) {
+      case 1: launch_merge<D, 1>(a, ot, s); return PKV_OK;
+      case 2: launch_merge<D, 2>(a, ot, s); return PKV_OK;
+      case 4: launch_merge<D, 4>(a, ot, s); return PKV_OK;
+      case 8: launch_merge<D, 8>(a, ot, s); return PKV_OK;
+      case 16: launch_merge<D, 16>(a, ot, s); return PKV_OK;
+    }
+    return PKV_ERR_UNSUPPORTED;
+  }
   const dim3 grid((unsigned)((long long)a.num_rows * a.num_q_heads));
   if (ot == PKV_F32) decode_combine_kernel<D, PKV_F32><<<grid, 64, 0, s>>>(a);
   else decode_combine_kernel<D, PKV_BF16><<<grid, 64, 0, s>>>(a);

@@ -163,6 +163,41 @@ def test_phases_equal_the_one_call_form_bit_for_bit():
     assert torch.equal(one.view(torch.int16), two.view(torch.int16))
 
 
+@pytest.mark.parametrize("split", [None, 4, 32])
+def test_fp8_phases_called_separately(split):
+    """fp8 cache through the two phases as separate calls: the merge phase
+    takes no cache, so the partials must already carry the V scale.  Rows
+    with several pieces are forced by small shares; the fixed-split vector
+    kernels are covered as well (split 32 with scheme 0)."""
+    say("decode fp8 phases", split)
+    w = workloads.decode_workload(
+        "fp8_phases", 93, lambda rng: rng.integers(200, 1500, size=9), lambda n: n + 5,
+        block_size=16, num_q_heads=32, num_kv_heads=8, head_dim=128, cache_dtype="fp8",
+        q_dtype="bf16", sigma=1.0)
+    d = w.device()
+    plan = pkv.decode_plan(w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len)
+    if split == 32:
+        plan.scheme, plan.num_workers, plan.heads_per_item = 0, 0, 4
+        pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len, split_blocks=8,
+                      kernel_variant=1)
+    elif split is not None:
+        pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len,
+                      num_workers=max(1, plan.num_workers // split))
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d.q)
+    pkv.paged_attention_decode_partials(d.q, d.cache, d.block_table, d.seq_lens, w.max_seq_len,
+                                        w.scale, plan, ws, out)
+    pkv.paged_attention_decode_combine(out, d.seq_lens, w.block_size, plan, ws)
+    one = pkv.paged_attention_decode(d.q, d.cache, d.block_table, d.seq_lens, w.max_seq_len, w.scale)
+    torch.cuda.synchronize()
+    ref = attention.paged_decode(w.q, w.q_dtype, w.k_plane, w.v_plane, w.cache_dtype,
+                                 w.block_table, w.seq_lens, w.scale, k_scale=w.k_scale,
+                                 v_scale=w.v_scale)
+    assert max_err(out_f64(out), ref) <= TOL["fp8"]
+    if split is None:
+        assert torch.equal(one.view(torch.int16), out.view(torch.int16))
+
+
 def test_physical_placement_does_not_change_a_single_bit():
     say("decode permutation invariance")
     w = workloads.llama8b_decode()
