@@ -1326,13 +1326,14 @@ __global__ __launch_bounds__(64) void decode_flat_kernel(DecodeArgs a) {
 // Combine phase: one wave per (row, query head) with more than one split.
 // Merge phase of the balanced scheme: one wave per (row, head group) with
 // more than one piece.  The split phase leaves, per (row, group), the piece
-// count and the output row, so the wave needs no row lookup; lane l merges
-// elements l + 64 i of the group's GT x D block, online over the pieces, four
-// pieces' loads in flight at a time.
+// count and the output row, so the wave needs no row lookup.  Lane l takes
+// head l / LPH of the group and DPL consecutive dims, so it reads one (m, l)
+// pair and one run of acc per piece and merges online, four pieces' loads in
+// flight at a time.
 template <int D, int GT, int OT>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
-  constexpr int NE = GT * D;
-  constexpr int EPL = (NE + kWave - 1) / kWave;    // elements per lane
+  constexpr int LPH = kWave / GT;                   // lanes per head
+  constexpr int DPL = D >= LPH ? D / LPH : 1;       // dims per lane
   constexpr int U = 4;                              // pieces per round of loads
   const int lane = threadIdx.x;
   const int groups = a.num_q_heads / GT;
@@ -1343,47 +1344,44 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   if (np <= 1) return;                              // written by the split phase (or rejected)
   const int tok = a.ws_np[2 * rg + 1];
   if (tok < 0 || tok >= a.num_tokens) return;       // not a row this call wrote
+  const int h = lane / LPH;
+  const int d0 = (lane % LPH) * DPL;
+  const bool active = d0 < D;
   const float* ml = a.ws_m + rg * a.max_splits * (2 * GT);
-  float M[EPL], den[EPL], num[EPL];
+  const float* accp = a.ws_acc + (((int64_t)b * a.num_q_heads + g * GT + h) * a.max_splits) * D +
+                      (active ? d0 : 0);
+  float M = -INFINITY, den = 0.f;
+  float num[DPL];
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) { M[i] = -INFINITY; den[i] = 0.f; num[i] = 0.f; }
+  for (int i = 0; i < DPL; ++i) num[i] = 0.f;
   for (int s0 = 0; s0 < np; s0 += U) {
-    float mv[U][EPL], lv[U][EPL], av[U][EPL];
+    float mv[U], lv[U], av[U][DPL];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = min(s0 + u, np - 1);            // past the end: repeat the last (skipped below)
+      mv[u] = ml[s * (2 * GT) + h];
+      lv[u] = ml[s * (2 * GT) + GT + h];
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        const int e = lane + kWave * i;
-        const int h = (e < NE ? e : 0) / D;
-        const int d = (e < NE ? e : 0) % D;
-        mv[u][i] = ml[s * (2 * GT) + h];
-        lv[u][i] = ml[s * (2 * GT) + GT + h];
-        av[u][i] = a.ws_acc[(((int64_t)b * a.num_q_heads + g * GT + h) * a.max_splits + s) * D + d];
-      }
+      for (int i = 0; i < DPL; ++i) av[u][i] = accp[(int64_t)s * D + i];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (s0 + u >= np) break;
+      const float mn = fmaxf(M, mv[u]);
+      const float c_old = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mn);
+      const float c_new = mv[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv[u] - mn);
+      den = den * c_old + lv[u] * c_new;
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        const float mn = fmaxf(M[i], mv[u][i]);
-        const float c_old = M[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M[i] - mn);
-        const float c_new = mv[u][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv[u][i] - mn);
-        den[i] = den[i] * c_old + lv[u][i] * c_new;
-        num[i] = num[i] * c_old + av[u][i] * c_new;
-        M[i] = mn;
-      }
+      for (int i = 0; i < DPL; ++i) num[i] = num[i] * c_old + av[u][i] * c_new;
+      M = mn;
     }
   }
+  if (!active) return;
+  const float inv = 1.0f / den;
+  float o[DPL];
 #pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = lane + kWave * i;
-    if (e < NE) {
-      float v[1] = {num[i] / den[i]};
-      store_out<OT, 1>(a.out, ((int64_t)tok * a.num_q_heads + g * GT) * D + e, v);
-    }
-  }
+  for (int i = 0; i < DPL; ++i) o[i] = num[i] * inv;
+  store_out<OT, DPL>(a.out, ((int64_t)tok * a.num_q_heads + g * GT + h) * D + d0, o);
 }
 
 template <int D, int OT>
