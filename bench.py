@@ -37,7 +37,7 @@ DATA_NOTE = {
               "chunks of 512, full and sliding-window groups over shared tensors)",
 }
 POOLS = 3
-SPLIT_KERNEL = "decode_flat_kernel"
+SPLIT_KERNEL = "decode_flat_kernel_2w"
 PMC_FILE = os.path.join(ROOT, "profiles", "decode_split_llama8b_b64_pmc.json")
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_mapping_amd", "csrc", "decode_kernels.h")
 
@@ -56,6 +56,7 @@ def parse():
     p.add_argument("--workers", type=int, default=0, help="balanced-scheme workers (tuning)")
     p.add_argument("--lead", type=int, default=-1, help="balanced scheme: full-share workers (tuning)")
     p.add_argument("--trail-pct", type=int, default=0, help="balanced scheme: other share %% (tuning)")
+    p.add_argument("--heads-per-item", type=int, default=0, help="balanced scheme: query heads per item")
     p.add_argument("--summarize-profiles", default="",
                    help="write profiles/ summaries from rocprofv3 output under this folder")
     p.add_argument("--calibration-copy", action="store_true",
@@ -394,7 +395,8 @@ def main():
                   split_blocks=args.split_blocks or None, num_workers=args.workers or None,
                   kernel_variant=args.variant,
                   lead_workers=args.lead if args.lead >= 0 else None,
-                  trail_share_pct=args.trail_pct or None)
+                  trail_share_pct=args.trail_pct or None,
+                  heads_per_item=args.heads_per_item or None)
     ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
     out = torch.empty_like(base.q)
     slots = torch.empty(w.num_reqs, dtype=torch.int64, device=dev)

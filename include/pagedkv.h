@@ -175,7 +175,8 @@ PKV_API int pkv_cache_write(const void* key, const void* value, int32_t src_dtyp
 typedef struct {
   int32_t split_blocks;   /* scheme 0: blocks per split; 1: least blocks per worker */
   int32_t max_splits;     /* partial slots per (row, query head)                  */
-  int32_t heads_per_item; /* query heads one work item processes                  */
+  int32_t heads_per_item; /* query heads one work item processes (scheme 1: a
+                             power of two up to 16 dividing the group)     */
   int32_t kernel_variant; /* 0: the library's choice.  Tuning only: 1 = vector
                              ALUs for the scores (scheme 0 only); 2..5 =
                              scheme 1 with K/V loads issued 1..4 steps

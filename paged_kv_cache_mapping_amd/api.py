@@ -143,7 +143,7 @@ def decode_plan(num_rows, num_q_heads, cache, max_seq_len, sliding_window=0):
 
 def tune_plan(plan, num_rows, num_q_heads, cache, max_seq_len, sliding_window=0,
               split_blocks=None, num_workers=None, kernel_variant=None, lead_workers=None,
-              trail_share_pct=None):
+              trail_share_pct=None, heads_per_item=None):
     """Override a plan's tuning fields and recompute the sizes they imply.
 
     Scheme 0: split_blocks = blocks per split.  Scheme 1: split_blocks =
@@ -165,6 +165,8 @@ def tune_plan(plan, num_rows, num_q_heads, cache, max_seq_len, sliding_window=0,
         plan.lead_workers = int(lead_workers)
     if trail_share_pct is not None:
         plan.trail_share_pct = int(trail_share_pct)
+    if heads_per_item is not None:
+        plan.heads_per_item = int(heads_per_item)
     if kernel_variant is not None:
         plan.kernel_variant = int(kernel_variant)
     per_slot = num_rows * num_q_heads * (cache.head_dim + 2) * 4

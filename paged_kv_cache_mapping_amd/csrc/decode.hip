@@ -119,13 +119,15 @@ static int make_plan(int rows, int hq, int hkv, int d, int bs, int kv_dtype, int
 static int check_plan(const pkv_decode_plan* plan, int rows, int hq, int hkv, int d, int bs,
                       int kv_dtype, int max_seq_len, int window, int extra) {
   if (!plan) return PKV_ERR_NULL;
-  if (plan->kernel_variant < 0 || plan->kernel_variant > 5) return PKV_ERR_SHAPE;
+  if (plan->kernel_variant < 0 || plan->kernel_variant > 6) return PKV_ERR_SHAPE;
   const int group = hq / hkv;
   const int nvis = max_visible_blocks(max_seq_len, bs, window, extra);
   if (plan->scheme == 1) {
     if (!mfma_eligible(kv_dtype, d, bs) || rows > kMaxStreamRows) return PKV_ERR_SHAPE;
-    if (plan->heads_per_item != heads_per_item_mfma(group) || plan->heads_per_item == 0)
-      return PKV_ERR_SHAPE;
+    // any of 1, 2, 4, 8, 16 that divides the group (items of a KV head then
+    // share its blocks); the planner picks the largest
+    const int hpi = plan->heads_per_item;
+    if (hpi <= 0 || hpi > 16 || (hpi & (hpi - 1)) || group % hpi) return PKV_ERR_SHAPE;
     if (plan->split_blocks < 1 || plan->num_workers < 1) return PKV_ERR_SHAPE;
     if (plan->lead_workers < 0 || plan->lead_workers > plan->num_workers) return PKV_ERR_SHAPE;
     if (plan->trail_share_pct < 1 || plan->trail_share_pct > 100) return PKV_ERR_SHAPE;

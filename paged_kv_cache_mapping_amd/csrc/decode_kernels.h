@@ -72,7 +72,7 @@ struct DecodeArgs {
   float* ws_acc;
   float* ws_m;
   float* ws_l;
-  int32_t kernel_variant;   // 0 default; tuning: 1 vector-only, 2..5 loads 1..4 steps ahead
+  int32_t kernel_variant;   // 0 default; tuning: 1 vector-only, 2..5 loads 1..4 steps ahead, 6 two waves per SIMD
   int32_t stream;           // balanced partition (piece counts in ws_np)
   int32_t heads_per_item;
   int32_t* ws_np;           // balanced partition: pieces per (row, head group)
@@ -873,7 +873,7 @@ __device__ inline Shares make_shares(long long U, int W, int lead, int pct, int 
 }
 
 template <int D, int GT, int KV, int DEPTH>
-__global__ __launch_bounds__(64) void decode_flat_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
   using S = MfmaShape<D, GT, KV>;
   constexpr int NC = S::NC, VLPR = S::VLPR, VRPW = S::VRPW, VU = S::VU, VEPL = S::VEPL;
   constexpr int KB = S::KB, RG = S::RG, kElt = S::kElt, QE = S::QE, QL = S::QL;
@@ -1324,6 +1324,20 @@ __global__ __launch_bounds__(64) void decode_flat_kernel(DecodeArgs a) {
 
 // --------------------------------------------------------------------------
 // Combine phase: one wave per (row, query head) with more than one split.
+// The balanced kernel; decode_flat_kernel_2w asks the compiler to fit two
+// waves per SIMD (used for eight query heads per item, where the default
+// register allocation leaves room for only one).
+template <int D, int GT, int KV, int DEPTH>
+__global__ __launch_bounds__(64) void decode_flat_kernel(DecodeArgs a) {
+  decode_flat_body<D, GT, KV, DEPTH>(a);
+}
+
+template <int D, int GT, int KV, int DEPTH>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_flat_kernel_2w(
+    DecodeArgs a) {
+  decode_flat_body<D, GT, KV, DEPTH>(a);
+}
+
 // Merge phase of the balanced scheme: one wave per (row, head group) with
 // more than one piece.  The split phase leaves, per (row, group), the piece
 // count and the output row, so the wave needs no row lookup.  Lane l takes
@@ -1492,7 +1506,13 @@ void launch_stream(const DecodeArgs& a, int workers, hipStream_t s) {
     case 3: decode_flat_kernel<D, GT, KV, 2><<<workers, 64, lds, s>>>(a); break;
     case 4: decode_flat_kernel<D, GT, KV, 3><<<workers, 64, lds, s>>>(a); break;
     case 5: decode_flat_kernel<D, GT, KV, 4><<<workers, 64, lds, s>>>(a); break;
-    default: decode_flat_kernel<D, GT, KV, kDepth><<<workers, 64, lds, s>>>(a);
+    case 6: decode_flat_kernel_2w<D, GT, KV, 1><<<workers, 64, lds, s>>>(a); break;
+    default:
+      // up to four heads per item the plan counts on two waves per SIMD, so
+      // the kernel must fit in 256 registers (the fp8 build does not unless
+      // asked); eight or more heads run one wave per SIMD
+      if constexpr (GT <= 4) decode_flat_kernel_2w<D, GT, KV, kDepth><<<workers, 64, lds, s>>>(a);
+      else decode_flat_kernel<D, GT, KV, kDepth><<<workers, 64, lds, s>>>(a);
   }
 }
 
