@@ -345,29 +345,31 @@ __global__ __launch_bounds__(kPfThreads) void prefill_tile_kernel(PrefillArgs a)
 
   // ---- key tiles: loads run three tiles ahead in a ring of register
   // stages, tiles are double-buffered in LDS, one barrier per tile.  Tile t
-  // is loaded at step t - 3 into stage t % 3 (unconditionally: past the last
-  // tile the last one is fetched again), stored to LDS buffer t % 2 at step
-  // t - 1 and folded at step t.
+  // is loaded at step t - 3 into stage t % 3, stored to LDS buffer t % 2 at
+  // step t - 1 and folded at step t.  The steps run in whole rounds of three
+  // with no exit inside a round and every load and store unconditional
+  // (past the last tile the last one is fetched and staged again and not
+  // folded): a round with branches around the stages leads the compiler to
+  // move stage registers around, and each such copy waits for the load in
+  // flight.
   const int kt0 = klo / kPfKeys, kt1 = khi / kPfKeys;
+  const int rounds = (kt1 - kt0 + 3) / 3;
   Stage s0, s1, s2;
   stage_load(kt0, s0);
   stage_load(min(kt0 + 1, kt1), s1);
   stage_load(min(kt0 + 2, kt1), s2);
   stage_store(0, s0);
   __syncthreads();
-  auto step = [&](int kt, Stage& cur, const Stage& next) __attribute__((always_inline)) {
-    const int rel = kt - kt0;
-    if (kt + 1 <= kt1) stage_store((rel + 1) & 1, next);
-    stage_load(min(kt + 3, kt1), cur);
-    compute(kt, rel & 1);
+  auto step = [&](int rel, Stage& cur, const Stage& next) __attribute__((always_inline)) {
+    stage_store((rel + 1) & 1, next);
+    stage_load(min(kt0 + rel + 3, kt1), cur);
+    if (kt0 + rel <= kt1) compute(kt0 + rel, rel & 1);
     __syncthreads();
   };
-  for (int kt = kt0; kt <= kt1; kt += 3) {
-    step(kt, s0, s1);
-    if (kt + 1 > kt1) break;
-    step(kt + 1, s1, s2);
-    if (kt + 2 > kt1) break;
-    step(kt + 2, s2, s0);
+  for (int i = 0; i < rounds; ++i) {
+    step(3 * i, s0, s1);
+    step(3 * i + 1, s1, s2);
+    step(3 * i + 2, s2, s0);
   }
 
   // ---- normalise and store: lane l holds dims 16 mb + 4 (l / 16) + i of row l % 16
