@@ -75,6 +75,17 @@ struct PfShape {
 
 inline size_t pf_align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
+// Maximum over the four 16-lane groups of a wave (lanes l, l^16, l^32,
+// l^48), on the gfx950 lane-swap instructions instead of LDS permutes:
+// swapping a value with itself across the two halves, then across odd and
+// even rows, hands each lane its partner's copy.
+__device__ __forceinline__ float pf_group4_max(float x) {
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 template <int D, int G>
 size_t pf_lds_bytes(int max_blocks) {
   return 2 * (size_t)PfShape<D, G>::TILE + pf_align16((size_t)max_blocks * sizeof(int));
@@ -126,14 +137,18 @@ __global__ __launch_bounds__(kPfThreads) void prefill_tile_kernel(PrefillArgs a)
     return;
   }
 
-  // ---- table slice of the blocks this workgroup can touch
+  // ---- table slice of the blocks this workgroup can touch; whether any of
+  // them is unmapped is decided once, for the whole workgroup
+  int unmapped = 0;
   for (int i = tid; i < nblk; i += kPfThreads) {
     const int j = b0 + i;
     int e = -1;
     if (j < a.bt_stride) e = a.bt[(int64_t)r * a.bt_stride + j];
-    tab[i] = (e >= 0 && e < a.num_blocks) ? e : -1;
+    const bool ok = e >= 0 && e < a.num_blocks;
+    tab[i] = ok ? e : -1;
+    unmapped |= ok ? 0 : 1;
   }
-  __syncthreads();
+  const bool any_unmapped = __syncthreads_or(unmapped) != 0;
 
   // ---- this wave's rows
   const int tw0 = tok_lo + wave * TW;                 // first query token of the wave
@@ -241,7 +256,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_tile_kernel(PrefillArgs a)
     const char* vt_l = kt_l + S::TILEK;
     // an unmapped block among the tile's keys makes the rows that see it NaN
     bool tile_bad = false;
-    {
+    if (any_unmapped) {
       const int lo = max(kbase, klo), hi = min(kbase + kPfKeys - 1, khi);
       for (int bi = (lo >> a.bs_log2) - b0; bi <= (hi >> a.bs_log2) - b0; ++bi)
         tile_bad |= tab[bi] < 0;
@@ -286,8 +301,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_tile_kernel(PrefillArgs a)
       }
       float mt = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
                        fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = pf_group4_max(mt);
       const bool grow = mt > m[nb] + kPfLazy;
       if (__ballot(grow) != 0) {
         const float alpha = grow ? __builtin_amdgcn_exp2f(m[nb] - mt) : 1.0f;   // 0 when m = -inf
