@@ -401,7 +401,7 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dt
 // tokens take the per-token rows.  Each pass has its own workspace region.
 struct ChunkPlans {
   pkv_decode_plan single, multi;
-  size_t single_bytes, multi_bytes;
+  size_t single_bytes, multi_bytes;   // multi_bytes: the per-token rows, or the prefill slots
   bool prefill;           // multi-query requests on the matrix-core prefill kernel
 };
 
@@ -418,7 +418,9 @@ static int chunk_plans(int num_tokens, int num_reqs, int hq, const pkv_cache* c,
   p.single_bytes = (p.single.workspace_bytes + 255) & ~(size_t)255;
   p.prefill = prefill_supported(c->dtype, c->head_dim, hq / c->num_kv_heads, max_seq_len,
                                 c->block_size, window, max_query_len);
-  p.multi_bytes = (max_query_len > 1 && !p.prefill) ? p.multi.workspace_bytes : 0;
+  p.multi_bytes = max_query_len <= 1 ? 0
+                  : p.prefill       ? prefill_workspace_bytes(c->head_dim)
+                                    : p.multi.workspace_bytes;
   return PKV_OK;
 }
 
@@ -501,6 +503,7 @@ extern "C" int pkv_paged_attention_chunked(void* out, const void* q, int32_t q_d
     const float log2e = 1.4426950408889634f;
     pa.scale_log2 = softmax_scale * log2e * (cache->dtype == PKV_FP8_E4M3 ? cache->k_scale : 1.0f);
     pa.v_scale = cache->dtype == PKV_FP8_E4M3 ? cache->v_scale : 1.0f;
+    pa.part = reinterpret_cast<float*>(ws + p.single_bytes);
     st = launch_prefill(pa, cache->dtype, cache->head_dim, stream);
     if (st != PKV_OK) return st;
     st = launch_status();

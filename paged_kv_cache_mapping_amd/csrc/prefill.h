@@ -29,8 +29,10 @@ struct PrefillArgs {
   int32_t bt_stride;
   int32_t causal;
   int32_t window;           // 0: none
-  int32_t tiles_per_req;    // query tiles per request in the grid
-  int32_t max_blocks;       // table entries one workgroup may stage
+  int32_t tiles_per_req;    // query tiles per request (max_query_len over the tile height)
+  int32_t max_blocks;       // table entries one piece may stage
+  int32_t workers;          // workgroups of the balanced partition
+  float* part;              // 2 * workers partial slots (prefill_workspace_bytes)
   float scale_log2;         // softmax_scale * log2(e) (* k_scale for fp8)
   float v_scale;            // 1, or the fp8 V scale
 };
@@ -39,7 +41,13 @@ struct PrefillArgs {
 bool prefill_supported(int kv_dtype, int head_dim, int group, int max_seq_len, int block_size,
                        int window, int max_query_len);
 
-// Launches the prefill kernel for every request with more than one query.
+// Workspace bytes of the partial slots (two per workgroup, one workgroup per
+// compute unit of the current device).
+size_t prefill_workspace_bytes(int head_dim);
+
+// Launches the prefill kernel for every request with more than one query,
+// then the merge of pieces cut by share boundaries; `part` must hold
+// prefill_workspace_bytes(head_dim) bytes.
 int launch_prefill(const PrefillArgs& a, int kv_dtype, int head_dim, hipStream_t s);
 
 }  // namespace pkv

@@ -91,14 +91,153 @@ size_t pf_lds_bytes(int max_blocks) {
   return 2 * (size_t)PfShape<D, G>::TILE + pf_align16((size_t)max_blocks * sizeof(int));
 }
 
+// ---- the balanced partition
+//
+// Work units are key tiles of items; an item is (request, KV head, tile of
+// query tokens), ordered request-major, then KV head, then query tile, so
+// that neighbouring units read the same KV head's blocks.  Workgroup share
+// w (of W) owns units [floor(U w / W), floor(U (w + 1) / W)).  A stretch of
+// one item inside a share is a piece: a piece that is the whole item writes
+// the output; a piece cut by a share boundary writes its unnormalised state
+// into one of the share's two slots (2w: the piece that continues an item
+// begun in an earlier share, 2w + 1: the piece whose item goes on into a
+// later share) and the merge kernel combines the item's slots.
+
+// One request as the partition sees it.
+struct PfReq {
+  int r;        // request index
+  int q0, ql, L, p0;
+  int ntq;      // query tiles with rows to write (0: not a multi-query request)
+  bool valid;   // lengths agree with the arguments (otherwise its rows get NaN)
+};
+
+template <int TWG>
+__device__ __forceinline__ PfReq pf_req(const PrefillArgs& a, int r) {
+  PfReq q;
+  q.r = r;
+  q.q0 = a.qsl[r];
+  const int end = a.qsl[r + 1];
+  q.ql = end - q.q0;
+  q.L = a.seq_lens[r];
+  q.p0 = q.L - q.ql;
+  const bool rows = q.ql > 1 && q.q0 >= 0 && end <= a.num_tokens;
+  q.ntq = rows ? min((q.ql + TWG - 1) / TWG, a.tiles_per_req) : 0;
+  q.valid = q.L > 0 && q.L <= a.max_seq_len && q.ql <= q.L && q.ql <= a.max_query_len;
+  return q;
+}
+
+// Key tiles of query tile qt (one unit for an invalid request: its rows are
+// written as NaN by whichever share owns that unit).
+template <int TWG>
+__device__ __forceinline__ int pf_item_units(const PrefillArgs& a, const PfReq& q, int qt) {
+  if (!q.valid) return 1;
+  const int tok_lo = qt * TWG, tok_hi = min(q.ql, tok_lo + TWG);
+  const int khi = a.causal ? q.p0 + tok_hi - 1 : q.L - 1;
+  const int klo = a.window > 0 ? max(0, q.p0 + tok_lo - a.window + 1) : 0;
+  return khi / kPfKeys - klo / kPfKeys + 1;
+}
+
+// Units of one KV head's items of a request.
+template <int TWG>
+__device__ __forceinline__ long long pf_head_units(const PrefillArgs& a, const PfReq& q) {
+  long long n = 0;
+  for (int qt = 0; qt < q.ntq; ++qt) n += pf_item_units<TWG>(a, q, qt);
+  return n;
+}
+
+// Whole workgroup: the total unit count; for target >= 0 also the request
+// holding unit `target` and that request's first unit.
+template <int TWG>
+__device__ long long pf_scan(const PrefillArgs& a, long long target, int& req, long long& req_first) {
+  __shared__ long long wsum[kPfWaves];
+  __shared__ long long found[2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();   // an earlier call may still be reading `found`
+  if (threadIdx.x == 0) {
+    found[0] = -1;
+    found[1] = 0;
+  }
+  __syncthreads();
+  long long carry = 0;
+  for (int base = 0; base < a.num_reqs; base += kPfThreads) {
+    const int r = base + (int)threadIdx.x;
+    long long u = 0;
+    if (r < a.num_reqs) u = pf_head_units<TWG>(a, pf_req<TWG>(a, r)) * a.num_kv_heads;
+    long long x = u;   // inclusive scan over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const long long y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    long long before = carry, chunk = 0;
+    for (int i = 0; i < kPfWaves; ++i) {
+      if (i < wave) before += wsum[i];
+      chunk += wsum[i];
+    }
+    const long long first = before + x - u;
+    if (target >= 0 && u > 0 && first <= target && target < first + u) {
+      found[0] = r;
+      found[1] = first;
+    }
+    carry += chunk;
+    __syncthreads();
+  }
+  req = (int)found[0];
+  req_first = found[1];
+  return carry;
+}
+
+// The item holding unit u of request r (whose first unit is rfirst).
+struct PfItem {
+  int kvh, qt;
+  long long first;   // the item's first unit
+  int units;
+};
+
+template <int TWG>
+__device__ __forceinline__ PfItem pf_item(const PrefillArgs& a, const PfReq& q, long long rfirst,
+                                          long long u) {
+  const long long per_head = pf_head_units<TWG>(a, q);
+  PfItem it;
+  const long long local = u - rfirst;
+  it.kvh = (int)(local / per_head);
+  long long rem = local - (long long)it.kvh * per_head;
+  it.qt = 0;
+  int n = pf_item_units<TWG>(a, q, 0);
+  while (rem >= n) {
+    rem -= n;
+    ++it.qt;
+    n = pf_item_units<TWG>(a, q, it.qt);
+  }
+  it.first = u - rem;
+  it.units = n;
+  return it;
+}
+
+// Share boundaries and the XCD-aware order of shares: workgroups are dealt
+// to the eight XCDs in turn, so share w goes to the workgroup that puts
+// consecutive shares (which read the same KV head) on one XCD's L2.
+__device__ __forceinline__ long long pf_bound(long long U, int w, int W) {
+  return U * w / W;
+}
+__device__ __forceinline__ int pf_share_of_block(int b, int W) {
+  return (W % 8 == 0) ? (b % 8) * (W / 8) + b / 8 : b;
+}
+
+// One piece: key tiles [ta, tb) of item (request q, KV head kvh, query tile
+// qt), counted from the item's first key tile.  slot < 0: the piece is the
+// whole item and writes the output; otherwise it writes its unnormalised
+// state to that slot.
 template <int D, int G, int KV>
-__global__ __launch_bounds__(kPfThreads) void prefill_tile_kernel(PrefillArgs a) {
+__device__ __forceinline__ void pf_piece(const PrefillArgs& a, char* lds, const PfReq& rq, int kvh,
+                                         int qt, int ta, int tb, int slot) {
   using S = PfShape<D, G>;
   constexpr int NBW = S::NBW, TPN = S::TPN, TW = S::TW, TWG = S::TWG;
   constexpr int NC = S::NC, MB = S::MB, RSK = S::RSK, RSV = S::RSV, TILE = S::TILE;
   constexpr int CPR = S::CPR, CPT = S::CPT, CPTH = S::CPTH;
   constexpr int kElt = KV == PKV_BF16 ? 2 : 1;
-  extern __shared__ __align__(16) char lds[];
   int* tab = reinterpret_cast<int*>(lds + 2 * TILE);   // phys block or -1, from block b0
 
   const int tid = threadIdx.x;
@@ -106,28 +245,15 @@ __global__ __launch_bounds__(kPfThreads) void prefill_tile_kernel(PrefillArgs a)
   const int lane = tid & 63;
   const int grp = lane >> 4;           // lane group of the MFMA layouts
   const int ln16 = lane & 15;
-  const int kvh = blockIdx.y;
-  const int r = blockIdx.x / a.tiles_per_req;
-  const int qt = blockIdx.x % a.tiles_per_req;
-  const int q0 = a.qsl[r];
-  const int ql = a.qsl[r + 1] - q0;
-  if (ql <= 1 || qt * TWG >= ql) return;            // whole workgroup
-  if (q0 < 0 || q0 + ql > a.num_tokens) return;     // rows outside q / out: nothing to write
-  const int L = a.seq_lens[r];
+  const int q0 = rq.q0, ql = rq.ql, L = rq.L, p0 = rq.p0;   // p0: position of query 0
   const int tok_lo = qt * TWG;
   const int tok_hi = min(ql, tok_lo + TWG);
-  const int p0 = L - ql;                              // position of query 0
   const int hq = a.num_q_heads;
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
 
-  const int khi = a.causal ? p0 + tok_hi - 1 : L - 1;
-  const int klo = a.window > 0 ? max(0, p0 + tok_lo - a.window + 1) : 0;
-  const int b0 = klo >> a.bs_log2;
-  const int nblk = (khi >> a.bs_log2) - b0 + 1;
-  const bool req_ok = L > 0 && L <= a.max_seq_len && ql <= L && ql <= a.max_query_len &&
-                      nblk <= a.max_blocks;
-  if (!req_ok) {
+  if (!rq.valid) {
     // lengths inconsistent with the arguments: NaN rows, as the other paths
+    // (such an item is one unit, so this piece is the whole item)
     const int n = (tok_hi - tok_lo) * G * D;
     for (int e = tid; e < n; e += kPfThreads) {
       const int t = e / (G * D);
@@ -137,13 +263,25 @@ __global__ __launch_bounds__(kPfThreads) void prefill_tile_kernel(PrefillArgs a)
     return;
   }
 
-  // ---- table slice of the blocks this workgroup can touch; whether any of
+  // the item's keys, then this piece's share of them
+  const int khi_item = a.causal ? p0 + tok_hi - 1 : L - 1;
+  const int klo_item = a.window > 0 ? max(0, p0 + tok_lo - a.window + 1) : 0;
+  const int kt0 = klo_item / kPfKeys + ta, kt1 = klo_item / kPfKeys + tb - 1;
+  const int klo = max(klo_item, kt0 * kPfKeys);
+  const int khi = min(khi_item, kt1 * kPfKeys + kPfKeys - 1);
+  const int b0 = klo >> a.bs_log2;
+  const int nblk = (khi >> a.bs_log2) - b0 + 1;
+  // more table entries than the launch sized for: the rows are poisoned
+  // instead of staging past the slice
+  const bool poisoned = nblk > a.max_blocks;
+
+  // ---- table slice of the blocks this piece can touch; whether any of
   // them is unmapped is decided once, for the whole workgroup
   int unmapped = 0;
-  for (int i = tid; i < nblk; i += kPfThreads) {
+  for (int i = tid; i < (poisoned ? 0 : nblk); i += kPfThreads) {
     const int j = b0 + i;
     int e = -1;
-    if (j < a.bt_stride) e = a.bt[(int64_t)r * a.bt_stride + j];
+    if (j < a.bt_stride) e = a.bt[(int64_t)rq.r * a.bt_stride + j];
     const bool ok = e >= 0 && e < a.num_blocks;
     tab[i] = ok ? e : -1;
     unmapped |= ok ? 0 : 1;
@@ -366,14 +504,15 @@ __global__ __launch_bounds__(kPfThreads) void prefill_tile_kernel(PrefillArgs a)
   // folded): a round with branches around the stages leads the compiler to
   // move stage registers around, and each such copy waits for the load in
   // flight.
-  const int kt0 = klo / kPfKeys, kt1 = khi / kPfKeys;
-  const int rounds = (kt1 - kt0 + 3) / 3;
+  const int rounds = poisoned ? 0 : (kt1 - kt0 + 3) / 3;
   Stage s0, s1, s2;
-  stage_load(kt0, s0);
-  stage_load(min(kt0 + 1, kt1), s1);
-  stage_load(min(kt0 + 2, kt1), s2);
-  stage_store(0, s0);
-  __syncthreads();
+  if (!poisoned) {
+    stage_load(kt0, s0);
+    stage_load(min(kt0 + 1, kt1), s1);
+    stage_load(min(kt0 + 2, kt1), s2);
+    stage_store(0, s0);
+    __syncthreads();
+  }
   auto step = [&](int rel, Stage& cur, const Stage& next) __attribute__((always_inline)) {
     stage_store((rel + 1) & 1, next);
     stage_load(min(kt0 + rel + 3, kt1), cur);
@@ -386,7 +525,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_tile_kernel(PrefillArgs a)
     step(3 * i + 2, s2, s0);
   }
 
-  // ---- normalise and store: lane l holds dims 16 mb + 4 (l / 16) + i of row l % 16
+  // ---- normalise and store (or hand the state to the merge):
+  // lane l holds dims 16 mb + 4 (l / 16) + i of row l % 16
   if (!wave_live) return;
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) {
@@ -395,11 +535,23 @@ __global__ __launch_bounds__(kPfThreads) void prefill_tile_kernel(PrefillArgs a)
     lt += __shfl_xor(lt, 32);
     // every lane takes part in both exchanges (no short-circuit: a lane that
     // skipped the exchange would not hand its flag to the others)
-    int bi = bad[nb] ? 1 : 0;
+    int bi = (bad[nb] || poisoned) ? 1 : 0;
     bi |= __shfl_xor(bi, 16);
     bi |= __shfl_xor(bi, 32);
     const bool b = bi != 0;
     if (!row_ok[nb]) continue;
+    if (slot >= 0) {
+      // rows of a slot: wave, then row block, then row of the block
+      const int rho = wave * (NBW * 16) + nb * 16 + ln16;
+      float* pa = a.part + ((int64_t)slot * (TWG * G) + rho) * D + 4 * grp;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) *reinterpret_cast<pf_f32x4*>(pa + 16 * mb) = acc[nb][mb];
+      if (grp == 0) {
+        float* ml = a.part + (int64_t)2 * a.workers * (TWG * G) * D + ((int64_t)slot * (TWG * G) + rho) * 2;
+        *reinterpret_cast<float2*>(ml) = make_float2(m[nb], b ? __builtin_nanf("") : lt);
+      }
+      continue;
+    }
     const float inv = a.v_scale / lt;
     uint16_t* dst = out + ((int64_t)(q0 + row_t[nb]) * hq + row_h[nb]) * D + 4 * grp;
 #pragma unroll
@@ -413,6 +565,113 @@ __global__ __launch_bounds__(kPfThreads) void prefill_tile_kernel(PrefillArgs a)
       }
       *reinterpret_cast<uint2*>(dst + 16 * mb) = w;
     }
+  }
+}
+
+template <int D, int G, int KV>
+__global__ __launch_bounds__(kPfThreads) void prefill_tile_kernel(PrefillArgs a) {
+  constexpr int TWG = PfShape<D, G>::TWG;
+  extern __shared__ __align__(16) char lds[];
+  const int W = (int)gridDim.x;
+  const int w = pf_share_of_block((int)blockIdx.x, W);
+  int r;
+  long long rfirst;
+  const long long U = pf_scan<TWG>(a, -1, r, rfirst);
+  const long long b = pf_bound(U, w, W), e = pf_bound(U, w + 1, W);
+  if (b >= e) return;
+  pf_scan<TWG>(a, b, r, rfirst);
+  if (r < 0) return;   // (cannot happen: both scans count the same units)
+  PfReq q = pf_req<TWG>(a, r);
+  long long span = pf_head_units<TWG>(a, q) * a.num_kv_heads;
+  for (long long u = b; u < e;) {
+    while (u >= rfirst + span) {   // next request with units (single-query ones have none)
+      if (r + 1 >= a.num_reqs) return;
+      rfirst += span;
+      ++r;
+      q = pf_req<TWG>(a, r);
+      span = pf_head_units<TWG>(a, q) * a.num_kv_heads;
+    }
+    const PfItem it = pf_item<TWG>(a, q, rfirst, u);
+    const long long end = it.first + it.units;
+    const long long pend = end < e ? end : e;
+    const bool whole = u == it.first && end <= e;
+    const int slot = whole ? -1 : (it.first < b ? 2 * w : 2 * w + 1);
+    pf_piece<D, G, KV>(a, lds, q, it.kvh, it.qt, (int)(u - it.first), (int)(pend - it.first), slot);
+    u = pend;
+  }
+}
+
+// Combines the slots of every item cut by share boundaries.  Workgroup j
+// takes the item holding the first unit of share j when that item began in
+// share j - 1; its pieces are slot 2 (j - 1) + 1, then slot 2 w of every
+// later non-empty share w that the item reaches.  Each thread merges one
+// row's half of the dimensions.
+template <int D, int G>
+__global__ __launch_bounds__(kPfThreads) void prefill_merge_kernel(PrefillArgs a) {
+  using S = PfShape<D, G>;
+  constexpr int TWG = S::TWG, TW = S::TW, TPN = S::TPN, NBW = S::NBW;
+  constexpr int ROWS = TWG * G;                 // rows of a slot (256)
+  constexpr int TPR = kPfThreads / ROWS;        // threads per row
+  constexpr int DPT = D / TPR;                  // dims per thread
+  static_assert(kPfThreads % ROWS == 0 && D % (4 * TPR) == 0, "merge thread layout");
+  const int W = a.workers;
+  const int j = (int)blockIdx.x;
+  if (j == 0 || j >= W) return;
+  int r;
+  long long rfirst;
+  const long long U = pf_scan<TWG>(a, -1, r, rfirst);
+  const long long bj = pf_bound(U, j, W), bp = pf_bound(U, j - 1, W);
+  if (bj >= U || bp >= bj) return;
+  pf_scan<TWG>(a, bj, r, rfirst);
+  if (r < 0) return;
+  PfReq q = pf_req<TWG>(a, r);
+  const PfItem it = pf_item<TWG>(a, q, rfirst, bj);
+  if (!(it.first < bj && it.first >= bp)) return;
+  const long long end = it.first + it.units;
+
+  const int rho = (int)threadIdx.x / TPR;
+  const int d0 = ((int)threadIdx.x % TPR) * DPT;
+  const int wv = rho / (NBW * 16), nb = (rho / 16) % NBW, l16 = rho % 16;
+  const int tok = it.qt * TWG + wv * TW + nb * TPN + l16 / G;
+  const int head = it.kvh * G + l16 % G;
+  if (tok >= min(q.ql, it.qt * TWG + TWG)) return;
+  const float* ml = a.part + (int64_t)2 * W * ROWS * D;
+  auto for_slots = [&](auto&& f) __attribute__((always_inline)) {
+    f(2 * (j - 1) + 1);
+    for (int w = j; w < W; ++w) {
+      const long long bw = pf_bound(U, w, W);
+      if (bw >= end) break;
+      if (bw < pf_bound(U, w + 1, W)) f(2 * w);
+    }
+  };
+  float mx = -INFINITY;
+  for_slots([&](int sl) { mx = fmaxf(mx, ml[((int64_t)sl * ROWS + rho) * 2]); });
+  float den = 0.f;
+  float num[DPT];
+#pragma unroll
+  for (int i = 0; i < DPT; ++i) num[i] = 0.f;
+  for_slots([&](int sl) {
+    const float2 rec = *reinterpret_cast<const float2*>(ml + ((int64_t)sl * ROWS + rho) * 2);
+    const float wgt = rec.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rec.x - mx);
+    den += wgt * rec.y;
+    const float* src = a.part + ((int64_t)sl * ROWS + rho) * D + d0;
+#pragma unroll
+    for (int i = 0; i < DPT; i += 4) {
+      const pf_f32x4 v = *reinterpret_cast<const pf_f32x4*>(src + i);
+      num[i] += wgt * v[0];
+      num[i + 1] += wgt * v[1];
+      num[i + 2] += wgt * v[2];
+      num[i + 3] += wgt * v[3];
+    }
+  });
+  const float inv = a.v_scale / den;
+  uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(q.q0 + tok) * a.num_q_heads + head) * D + d0;
+#pragma unroll
+  for (int i = 0; i < DPT; i += 4) {
+    uint2 o;
+    o.x = f32_to_bf16_rne(num[i] * inv) | (f32_to_bf16_rne(num[i + 1] * inv) << 16);
+    o.y = f32_to_bf16_rne(num[i + 2] * inv) | (f32_to_bf16_rne(num[i + 3] * inv) << 16);
+    *reinterpret_cast<uint2*>(dst + i) = o;
   }
 }
 
@@ -442,8 +701,8 @@ int pf_tokens(int d, int g) {
 
 template <int D, int G, int KV>
 void pf_launch(const PrefillArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((long long)a.num_reqs * a.tiles_per_req), (unsigned)a.num_kv_heads);
-  prefill_tile_kernel<D, G, KV><<<grid, kPfThreads, pf_lds_bytes<D, G>(a.max_blocks), s>>>(a);
+  prefill_tile_kernel<D, G, KV><<<a.workers, kPfThreads, pf_lds_bytes<D, G>(a.max_blocks), s>>>(a);
+  prefill_merge_kernel<D, G><<<a.workers, kPfThreads, 0, s>>>(a);
 }
 
 template <int D, int KV>
@@ -484,8 +743,21 @@ bool prefill_supported(int kv_dtype, int head_dim, int group, int max_seq_len, i
   return bytes <= 64 * 1024;
 }
 
+// One workgroup per compute unit (eight waves fill a CU at this kernel's
+// register count); two slots of 256 rows x (D + 2) floats each.
+static int pf_workers() {
+  const int cus = device_cu_count();
+  return cus > 0 ? cus : 1;
+}
+
+size_t prefill_workspace_bytes(int head_dim) {
+  return (size_t)2 * pf_workers() * 256 * (size_t)(head_dim + 2) * sizeof(float);
+}
+
 int launch_prefill(const PrefillArgs& a0, int kv_dtype, int head_dim, hipStream_t s) {
   PrefillArgs a = a0;
+  a.workers = pf_workers();
+  if (!a.part) return PKV_ERR_WORKSPACE;
   const int g = a.num_q_heads / a.num_kv_heads;
   const int tok = pf_tokens(head_dim, g);
   if (tok == 0) return PKV_ERR_UNSUPPORTED;
@@ -493,7 +765,6 @@ int launch_prefill(const PrefillArgs& a0, int kv_dtype, int head_dim, hipStream_
   a.max_blocks = pf_max_blocks(a.max_seq_len, 1 << a.bs_log2, a.window,
                                tok > a.max_query_len ? tok : a.max_query_len);
   if (a.num_reqs == 0 || a.tiles_per_req == 0) return PKV_OK;
-  if ((long long)a.num_reqs * a.tiles_per_req > 0x7FFFFFFFLL) return PKV_ERR_SHAPE;
   const bool bf = kv_dtype == PKV_BF16;
   switch (head_dim) {
     case 64: return bf ? pf_launch_g<64, PKV_BF16>(a, g, s) : pf_launch_g<64, PKV_FP8_E4M3>(a, g, s);
