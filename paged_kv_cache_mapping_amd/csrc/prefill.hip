@@ -216,11 +216,28 @@ __device__ __forceinline__ PfItem pf_item(const PrefillArgs& a, const PfReq& q, 
   return it;
 }
 
+// What share w tells the merge: the total unit count, and the item its first
+// piece continues (head = 1) when that item began in an earlier share.
+struct PfShareRec {
+  long long units;   // U
+  long long first;   // the item's first and one-past-last unit
+  long long end;
+  int q0, ql, kvh, qt;
+  int head;
+  int pad;
+};
+static_assert(sizeof(PfShareRec) == 48, "share record layout");
+
 // Share boundaries and the XCD-aware order of shares: workgroups are dealt
 // to the eight XCDs in turn, so share w goes to the workgroup that puts
 // consecutive shares (which read the same KV head) on one XCD's L2.
 __device__ __forceinline__ long long pf_bound(long long U, int w, int W) {
   return U * w / W;
+}
+// Floats of the slot region (accumulators, then (m, l) pairs); the share
+// records follow it.
+__host__ __device__ constexpr long long pf_slot_floats(int W, int D) {
+  return (long long)2 * W * 256 * (D + 2);
 }
 __device__ __forceinline__ int pf_share_of_block(int b, int W) {
   return (W % 8 == 0) ? (b % 8) * (W / 8) + b / 8 : b;
@@ -578,7 +595,15 @@ __global__ __launch_bounds__(kPfThreads) void prefill_tile_kernel(PrefillArgs a)
   long long rfirst;
   const long long U = pf_scan<TWG>(a, -1, r, rfirst);
   const long long b = pf_bound(U, w, W), e = pf_bound(U, w + 1, W);
-  if (b >= e) return;
+  PfShareRec* rec = reinterpret_cast<PfShareRec*>(a.part + pf_slot_floats(W, D)) + w;
+  if (b >= e) {
+    if (threadIdx.x == 0) {
+      PfShareRec x = {};
+      x.units = U;
+      *rec = x;
+    }
+    return;
+  }
   pf_scan<TWG>(a, b, r, rfirst);
   if (r < 0) return;   // (cannot happen: both scans count the same units)
   PfReq q = pf_req<TWG>(a, r);
@@ -596,16 +621,28 @@ __global__ __launch_bounds__(kPfThreads) void prefill_tile_kernel(PrefillArgs a)
     const long long pend = end < e ? end : e;
     const bool whole = u == it.first && end <= e;
     const int slot = whole ? -1 : (it.first < b ? 2 * w : 2 * w + 1);
+    if (u == b && threadIdx.x == 0) {
+      PfShareRec x = {};
+      x.units = U;
+      x.first = it.first;
+      x.end = end;
+      x.q0 = q.q0;
+      x.ql = q.ql;
+      x.kvh = it.kvh;
+      x.qt = it.qt;
+      x.head = it.first < b ? 1 : 0;
+      *rec = x;
+    }
     pf_piece<D, G, KV>(a, lds, q, it.kvh, it.qt, (int)(u - it.first), (int)(pend - it.first), slot);
     u = pend;
   }
 }
 
 // Combines the slots of every item cut by share boundaries.  Workgroup j
-// takes the item holding the first unit of share j when that item began in
-// share j - 1; its pieces are slot 2 (j - 1) + 1, then slot 2 w of every
-// later non-empty share w that the item reaches.  Each thread merges one
-// row's half of the dimensions.
+// takes the item that share j's first piece continues when that item began
+// in the closest earlier share j' holding units; its pieces are slot
+// 2 j' + 1, then slot 2 w of every non-empty share w >= j that the item
+// reaches.  Each thread merges one row's share of the dimensions.
 template <int D, int G>
 __global__ __launch_bounds__(kPfThreads) void prefill_merge_kernel(PrefillArgs a) {
   using S = PfShape<D, G>;
@@ -617,27 +654,25 @@ __global__ __launch_bounds__(kPfThreads) void prefill_merge_kernel(PrefillArgs a
   const int W = a.workers;
   const int j = (int)blockIdx.x;
   if (j == 0 || j >= W) return;
-  int r;
-  long long rfirst;
-  const long long U = pf_scan<TWG>(a, -1, r, rfirst);
-  const long long bj = pf_bound(U, j, W), bp = pf_bound(U, j - 1, W);
-  if (bj >= U || bp >= bj) return;
-  pf_scan<TWG>(a, bj, r, rfirst);
-  if (r < 0) return;
-  PfReq q = pf_req<TWG>(a, r);
-  const PfItem it = pf_item<TWG>(a, q, rfirst, bj);
-  if (!(it.first < bj && it.first >= bp)) return;
-  const long long end = it.first + it.units;
+  const PfShareRec it = reinterpret_cast<const PfShareRec*>(a.part + pf_slot_floats(W, D))[j];
+  const long long U = it.units;
+  if (!it.head || pf_bound(U, j, W) >= pf_bound(U, j + 1, W)) return;
+  // the share before j that holds units (shares in between are empty); the
+  // item must have begun there, or an earlier share merges it
+  int jp = j - 1;
+  while (jp >= 0 && pf_bound(U, jp, W) >= pf_bound(U, jp + 1, W)) --jp;
+  if (jp < 0 || it.first < pf_bound(U, jp, W)) return;
+  const long long end = it.end;
 
   const int rho = (int)threadIdx.x / TPR;
   const int d0 = ((int)threadIdx.x % TPR) * DPT;
   const int wv = rho / (NBW * 16), nb = (rho / 16) % NBW, l16 = rho % 16;
   const int tok = it.qt * TWG + wv * TW + nb * TPN + l16 / G;
   const int head = it.kvh * G + l16 % G;
-  if (tok >= min(q.ql, it.qt * TWG + TWG)) return;
+  if (tok >= min(it.ql, it.qt * TWG + TWG)) return;
   const float* ml = a.part + (int64_t)2 * W * ROWS * D;
   auto for_slots = [&](auto&& f) __attribute__((always_inline)) {
-    f(2 * (j - 1) + 1);
+    f(2 * jp + 1);
     for (int w = j; w < W; ++w) {
       const long long bw = pf_bound(U, w, W);
       if (bw >= end) break;
@@ -665,7 +700,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_merge_kernel(PrefillArgs a
     }
   });
   const float inv = a.v_scale / den;
-  uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(q.q0 + tok) * a.num_q_heads + head) * D + d0;
+  uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)(it.q0 + tok) * a.num_q_heads + head) * D + d0;
 #pragma unroll
   for (int i = 0; i < DPT; i += 4) {
     uint2 o;
@@ -744,14 +779,16 @@ bool prefill_supported(int kv_dtype, int head_dim, int group, int max_seq_len, i
 }
 
 // One workgroup per compute unit (eight waves fill a CU at this kernel's
-// register count); two slots of 256 rows x (D + 2) floats each.
+// register count); two slots of 256 rows x (D + 2) floats each, and one
+// share record per workgroup.
 static int pf_workers() {
   const int cus = device_cu_count();
   return cus > 0 ? cus : 1;
 }
 
 size_t prefill_workspace_bytes(int head_dim) {
-  return (size_t)2 * pf_workers() * 256 * (size_t)(head_dim + 2) * sizeof(float);
+  const int w = pf_workers();
+  return (size_t)pf_slot_floats(w, head_dim) * sizeof(float) + (size_t)w * sizeof(PfShareRec);
 }
 
 int launch_prefill(const PrefillArgs& a0, int kv_dtype, int head_dim, hipStream_t s) {
