@@ -140,6 +140,33 @@ __device__ __forceinline__ RowInfo row_info(const DecodeArgs& a, int row) {
 template <typename T>
 __device__ __forceinline__ T shfl_xor_t(T v, int m) { return __shfl_xor(v, m); }
 
+// Lane H of each 16-lane row, handed to every lane of that row (DPP
+// row_newbcast).
+template <int H>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + H,
+                                                               0xF, 0xF, false));
+}
+
+// f(std::integral_constant<int, I>{}) for I = B .. E - 1.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Maximum over the four 16-lane rows (lanes l, l^16, l^32, l^48) on the
+// lane-swap instructions: swapping a value with itself across the halves,
+// then across odd and even rows, hands each lane its partners' copies.
+__device__ __forceinline__ float rows4_max(float x) {
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Store n consecutive floats of one output row as the output dtype.
 template <int OT, int N>
 __device__ __forceinline__ void store_out(void* base, int64_t elem, const float (&v)[N]) {
@@ -878,6 +905,14 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
   constexpr int NC = S::NC, VLPR = S::VLPR, VRPW = S::VRPW, VU = S::VU, VEPL = S::VEPL;
   constexpr int KB = S::KB, RG = S::RG, kElt = S::kElt, QE = S::QE, QL = S::QL;
   static_assert(DEPTH >= 1 && DEPTH <= 4, "prefetch depth");
+  // Row-broadcast scheme, when one V token row fits in a 16-lane row: the
+  // scores come out transposed (S^T = K Q^T, same registers with the MFMA
+  // operands swapped), so lane l holds tokens 4 (l / 16) .. + 3 of head
+  // l % 16; V loads put tokens 4 R .. 4 R + 3 in row R; each probability a
+  // lane needs then sits in its own row and arrives by DPP broadcast.
+  // Otherwise (a token spans two rows) probabilities move by LDS permute.
+  constexpr bool RB = VLPR <= 16;
+  constexpr int TPRV = RB ? 16 / VLPR : 1;          // V tokens per 16-lane row and load
   extern __shared__ __align__(16) char lds[];
   const FlatLds L = flat_lds_layout(a.num_rows, GT, D, a.lds_budget);
   int* cum = reinterpret_cast<int*>(lds + L.cum_off);     // cum[r]: visible blocks of rows < r
@@ -920,7 +955,8 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
   const int row_bytes = a.num_kv_heads * D * kElt;          // one token, all KV heads
   const int vg = lane / VLPR, vsub = lane % VLPR;
   const uint32_t k_lane = (uint32_t)((lane % 16) * row_bytes + (lane / 16) * KB);
-  const uint32_t v_lane = (uint32_t)(vg * row_bytes + vsub * 16);
+  const uint32_t v_lane = RB ? (uint32_t)((4 * (lane / 16) + (lane % 16) / VLPR) * row_bytes + vsub * 16)
+                             : (uint32_t)(vg * row_bytes + vsub * 16);
 
   // one lane's unit record
   int rec_phys = -1, rec_hoff = 0, rec_gid = -1, rec_pos0 = 0, rec_lo = 0, rec_hi = -1, rec_tok = 0;
@@ -933,6 +969,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
   float acc[GT][VEPL];
   float m[GT];
   f32x4_t lsum = {0.f, 0.f, 0.f, 0.f};
+  float m1 = -INFINITY, ls1 = 0.f;   // row-broadcast scheme: head lane % 16's max and sum
 
   // first query element of the piece (gid = row * kvgroups + head group)
   auto q_elem = [&](int gid, int tok) __attribute__((always_inline)) -> int64_t {
@@ -983,6 +1020,8 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
       for (int e = 0; e < VEPL; ++e) acc[h][e] = 0.f;
     }
     lsum[0] = lsum[1] = lsum[2] = lsum[3] = 0.f;
+    m1 = -INFINITY;
+    ls1 = 0.f;
   };
   auto flush = [&]() __attribute__((always_inline)) {
     const int b = cur / kvgroups;
@@ -1001,6 +1040,8 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
         for (int e = 0; e < VEPL; ++e) acc[h][e] = __builtin_nanf("");
       }
       lsum[0] = lsum[1] = lsum[2] = lsum[3] = __builtin_nanf("");
+      m1 = 0.f;
+      ls1 = __builtin_nanf("");
     }
     // the V layout's token groups hold partial sums under the same maxima
 #pragma unroll
@@ -1009,13 +1050,26 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
       for (int h = 0; h < GT; ++h)
 #pragma unroll
         for (int e = 0; e < VEPL; ++e) acc[h][e] += shfl_xor_t(acc[h][e], step);
-    float lt[4];
+    float lh[GT], mh[GT];   // each head's sum and max
+    if constexpr (RB) {
+      float lt = ls1;
+      lt += shfl_xor_t(lt, 16);
+      lt += shfl_xor_t(lt, 32);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lt[i] = group_sum<16>(lsum[i]);
-    float lh[GT];
+      for (int h = 0; h < GT; ++h) {
+        lh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lt), h));
+        mh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m1), h));
+      }
+    } else {
+      float lt[4];
 #pragma unroll
-    for (int h = 0; h < GT; ++h)
-      lh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lt[h % 4]), 16 * (h / 4)));
+      for (int i = 0; i < 4; ++i) lt[i] = group_sum<16>(lsum[i]);
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        lh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lt[h % 4]), 16 * (h / 4)));
+        mh[h] = m[h];
+      }
+    }
     const int64_t out_row = ((int64_t)s_tok * a.num_q_heads + h0) * D;
     if (vg == 0) {
       if (npieces == 1) {
@@ -1052,7 +1106,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
         float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < 2 * GT; ++e)
-          if (e / 4 == lane) v[e % 4] = e < GT ? m[e] : lh[e - GT];
+          if (e / 4 == lane) v[e % 4] = e < GT ? mh[e] : lh[e - GT];
         if constexpr (2 * GT >= 4) {
           const f32x4_t v4 = {v[0], v[1], v[2], v[3]};
           __builtin_nontemporal_store(v4, reinterpret_cast<f32x4_t*>(ml + 4 * lane));
@@ -1180,11 +1234,106 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
       }
 #pragma unroll
       for (int u = 0; u < VU; ++u)
-        bf.v[u] = *reinterpret_cast<const uint4*>(vp + v_lane + (int64_t)u * VRPW * row_bytes);
+        bf.v[u] = *reinterpret_cast<const uint4*>(vp + v_lane + (int64_t)u * (RB ? TPRV : VRPW) * row_bytes);
+    };
+
+    // V as floats, zero for keys outside the piece's span
+    auto v_floats = [&](auto full_tag, int p0, int tok, const uint4& raw, float (&vf)[VEPL])
+        __attribute__((always_inline)) {
+      constexpr bool full = decltype(full_tag)::value;
+      const uint32_t vwa[4] = {raw.x, raw.y, raw.z, raw.w};
+      if constexpr (KV == PKV_BF16) {
+#pragma unroll
+        for (int i = 0; i < VEPL / 2; ++i) { vf[2 * i] = bf16_lo(vwa[i]); vf[2 * i + 1] = bf16_hi(vwa[i]); }
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEPL / 4; ++i) {
+          const f32x2 v01 = e4m3x2_to_f32<false>(vwa[i]);
+          const f32x2 v23 = e4m3x2_to_f32<true>(vwa[i]);
+          vf[4 * i] = v01.x; vf[4 * i + 1] = v01.y; vf[4 * i + 2] = v23.x; vf[4 * i + 3] = v23.y;
+        }
+      }
+      if constexpr (!full) {
+        const int pos = p0 + tok;
+        const bool live = pos >= s_lo && pos <= s_hi;
+#pragma unroll
+        for (int e = 0; e < VEPL; ++e) vf[e] = live ? vf[e] : 0.f;
+      }
+    };
+
+    // row-broadcast fold of one 16-token step
+    auto body_rb = [&](auto full_tag, int p0, const Buf& bf) __attribute__((always_inline)) {
+      constexpr bool full = decltype(full_tag)::value;
+      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        uint4 kw;
+        if constexpr (KB == 16) {
+          kw = make_uint4(bf.k[c][0], bf.k[c][1], bf.k[c][2], bf.k[c][3]);
+        } else {
+          kw = make_uint4(e4m3x2_to_bf16x2<false>(bf.k[c][0]), e4m3x2_to_bf16x2<true>(bf.k[c][0]),
+                          e4m3x2_to_bf16x2<false>(bf.k[c][1]), e4m3x2_to_bf16x2<true>(bf.k[c][1]));
+        }
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kw), qa[c], sc, 0, 0, 0);
+      }
+      // lane l: tokens 4 (l / 16) + i of head l % 16
+      float z[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[i] = sc[i] * a.scale_log2;
+      if constexpr (!full) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pos = p0 + 4 * (lane / 16) + i;
+          if (pos < s_lo || pos > s_hi) z[i] = -INFINITY;
+        }
+      }
+      const float mx = rows4_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+      const bool grow = mx > m1 + kLazyRescale;
+      if (__ballot(grow) != 0) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m1 - mx) : 1.0f;   // 0 when m = -inf
+        if (grow) m1 = mx;
+        ls1 *= alpha;
+        static_for<0, GT>([&](auto hc) __attribute__((always_inline)) {
+          constexpr int h = decltype(hc)::value;
+          const float ah = row_bcast<h>(alpha);
+#pragma unroll
+          for (int e = 0; e < VEPL; ++e) acc[h][e] *= ah;
+        });
+      }
+      float pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float p = __builtin_amdgcn_exp2f(z[i] - m1);
+        if constexpr (!full) p = z[i] == -INFINITY ? 0.f : p;
+        pv[i] = p;
+        ls1 += p;
+      }
+#pragma unroll
+      for (int u = 0; u < VU; ++u) {
+        // this lane's V token: 4 R + u TPRV + (l % 16) / VLPR, probability slot u TPRV + ...
+        const int sub = (lane % 16) / VLPR;
+        float vf[VEPL];
+        v_floats(full_tag, p0, 4 * (lane / 16) + u * TPRV + sub, bf.v[u], vf);
+        static_for<0, GT>([&](auto hc) __attribute__((always_inline)) {
+          constexpr int h = decltype(hc)::value;
+          float ph = row_bcast<h>(pv[u * TPRV]);
+#pragma unroll
+          for (int k = 1; k < TPRV; ++k) {
+            const float t = row_bcast<h>(pv[u * TPRV + k]);
+            ph = sub == k ? t : ph;
+          }
+#pragma unroll
+          for (int e = 0; e < VEPL; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
+        });
+      }
     };
 
     auto body = [&](auto full_tag, int p0, const Buf& bf) __attribute__((always_inline)) {
       constexpr bool full = decltype(full_tag)::value;
+      if constexpr (RB) {
+        body_rb(full_tag, p0, bf);
+        return;
+      }
       f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
