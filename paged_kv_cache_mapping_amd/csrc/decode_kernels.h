@@ -1491,34 +1491,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 // more than one piece.  The split phase leaves, per (row, group), the piece
 // count and the output row, so the wave needs no row lookup.  Lane l takes
 // head l / LPH of the group and DPL consecutive dims, so it reads one (m, l)
-// pair and one run of acc per piece and merges online, four pieces' loads in
-// flight at a time.
+// pair and one run of acc per piece and merges online, eight pieces' loads
+// in flight at a time (the first eight issued with the piece count).
 template <int D, int GT, int OT>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   constexpr int LPH = kWave / GT;                   // lanes per head
   constexpr int DPL = D >= LPH ? D / LPH : 1;       // dims per lane
-  constexpr int U = 4;                              // pieces per round of loads
+  constexpr int U = 8;                              // pieces per round of loads
   const int lane = threadIdx.x;
   const int groups = a.num_q_heads / GT;
   const int b = blockIdx.x / groups;
   const int g = blockIdx.x % groups;
   const int64_t rg = (int64_t)b * groups + g;
-  const int np = min(a.ws_np[2 * rg], a.max_splits);
-  if (np <= 1) return;                              // written by the split phase (or rejected)
-  const int tok = a.ws_np[2 * rg + 1];
-  if (tok < 0 || tok >= a.num_tokens) return;       // not a row this call wrote
   const int h = lane / LPH;
   const int d0 = (lane % LPH) * DPL;
   const bool active = d0 < D;
   const float* ml = a.ws_m + rg * a.max_splits * (2 * GT);
   const float* accp = a.ws_acc + (((int64_t)b * a.num_q_heads + g * GT + h) * a.max_splits) * D +
                       (active ? d0 : 0);
-  float M = -INFINITY, den = 0.f;
-  float num[DPL];
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) num[i] = 0.f;
-  for (int s0 = 0; s0 < np; s0 += U) {
-    float mv[U], lv[U], av[U][DPL];
+  float mv[U], lv[U], av[U][DPL];
+  // the first round of pieces is read together with the piece count (the
+  // slots exist whatever the count; words past it are ignored)
+  auto load_round = [&](int s0, int np) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = min(s0 + u, np - 1);            // past the end: repeat the last (skipped below)
@@ -1527,6 +1521,19 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < DPL; ++i) av[u][i] = accp[(int64_t)s * D + i];
     }
+  };
+  const int np_word = a.ws_np[2 * rg];
+  const int tok = a.ws_np[2 * rg + 1];
+  load_round(0, a.max_splits);
+  const int np = min(np_word, a.max_splits);
+  if (np <= 1) return;                              // written by the split phase (or rejected)
+  if (tok < 0 || tok >= a.num_tokens) return;       // not a row this call wrote
+  float M = -INFINITY, den = 0.f;
+  float num[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) num[i] = 0.f;
+  for (int s0 = 0; s0 < np; s0 += U) {
+    if (s0 > 0) load_round(s0, np);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (s0 + u >= np) break;

@@ -26,10 +26,25 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ nc,
     int32_t bs_log2, int32_t num_blocks, int32_t num_tokens,
     int64_t* __restrict__ out, int32_t* __restrict__ err) {
+  // query_start_loc and num_computed go to LDS in one load round when they
+  // fit, so a token's chain of dependent global loads is just the table entry
+  constexpr int kStage = 1024;
+  __shared__ int sq[kStage + 1];
+  __shared__ int snc[kStage];
+  const bool staged = num_reqs <= kStage;
+  if (staged) {
+    for (int i = threadIdx.x; i <= num_reqs; i += 256) {
+      sq[i] = qsl[i];
+      if (i < num_reqs) snc[i] = nc[i];
+    }
+    __syncthreads();
+  }
+  const int* q = staged ? sq : qsl;
+  const int* ncs = staged ? snc : nc;
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= num_tokens) return;
-  const int first = qsl[0];
-  const int end = qsl[num_reqs];
+  const int first = q[0];
+  const int end = q[num_reqs];
   if (t < first || t >= end) {  // padding: no request owns this token
     out[t] = -1;
     return;
@@ -37,10 +52,10 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(
   int lo = 0, hi = num_reqs;  // largest r < num_reqs with qsl[r] <= t
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (qsl[mid] <= t) lo = mid; else hi = mid;
+    if (q[mid] <= t) lo = mid; else hi = mid;
   }
   const int r = lo;
-  const int64_t pos = (int64_t)nc[r] + (t - qsl[r]);
+  const int64_t pos = (int64_t)ncs[r] + (t - q[r]);
   const int64_t logical = pos >> bs_log2;
   int64_t slot = -1;
   if (pos >= 0 && logical < bt_stride) {
