@@ -216,6 +216,65 @@ def test_chunked_unmapped_block_poisons_only_rows_that_reach_it():
     assert max_err(got[:1], ref[:1]) <= 2e-3
 
 
+def test_chunked_requests_with_inconsistent_lengths_get_nan_rows():
+    """Requests whose lengths contradict the arguments (q_len > seq_len, or
+    seq_len > max_seq_len), among valid single- and multi-query requests:
+    their rows are NaN, every other row is exact.  The reference uses the
+    valid lengths, so only the rows of the two broken requests differ."""
+    say("chunked inconsistent lengths")
+    c = _chunk_case(1900, R=7, Lmax=300, qmax=50, Hq=8, Hkv=2, D=128, bs=16)
+    ql = np.diff(c["qsl"])
+    multi = [r for r in range(1, 7) if ql[r] >= 2]
+    assert len(multi) >= 2
+    short, long_ = multi[0], multi[1]
+    Lmax = int(c["L"].max())
+    ref = attention.paged_attention(c["q"], "bf16", c["kp"], c["vp"], "bf16", c["bt"], c["L"], c["qsl"], 0.125)
+    L = c["L"].copy()
+    L[short] = ql[short] - 1              # fewer keys than queries
+    L[long_] = Lmax + 5                   # past max_seq_len
+
+    def dev16(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    cache = pkv.CacheView.from_planes(dev16(c["kp"]), dev16(c["vp"]))
+    out = pkv.paged_attention_chunked(dev16(c["q"]), torch.from_numpy(c["qsl"]).cuda(), torch.from_numpy(L).cuda(),
+                                      int(ql.max()), cache, torch.from_numpy(c["bt"]).cuda(), Lmax, 0.125)
+    torch.cuda.synchronize()
+    got = out_f64(out)
+    broken = np.zeros(int(c["qsl"][-1]), bool)
+    for r in (short, long_):
+        broken[c["qsl"][r]:c["qsl"][r + 1]] = True
+    assert np.isnan(got[broken]).all()
+    assert max_err(got[~broken], ref[~broken]) <= 2e-3
+
+
+def test_chunked_one_long_item_cut_by_every_share():
+    """One prefill item (64 queries, one KV head) over 20,000 keys: the
+    balanced partition cuts it at every share boundary, so the merge combines
+    one piece from every share."""
+    say("chunked one item over every share")
+    bs, D, Hq, Hkv = 16, 128, 8, 1
+    rng = np.random.default_rng(2024)
+    L = np.array([20000], np.int32)
+    ql = np.array([64], np.int32)
+    qsl = np.array([0, 64], np.int32)
+    nblk = -(-int(L[0]) // bs)
+    nb = nblk + 7
+    bt = rng.permutation(nb)[:nblk].astype(np.int32).reshape(1, nblk)
+    shape = (nb, bs, Hkv, D)
+    kp = bf16_bits(rng.standard_normal(shape).astype(np.float32) * 0.4)
+    vp = bf16_bits(rng.standard_normal(shape).astype(np.float32) * 0.4)
+    q = bf16_bits(rng.standard_normal((64, Hq, D)).astype(np.float32) * 0.4)
+    ref = attention.paged_attention(q, "bf16", kp, vp, "bf16", bt, L, qsl, 0.125)
+
+    def dev16(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    cache = pkv.CacheView.from_planes(dev16(kp), dev16(vp))
+    out = pkv.paged_attention_chunked(dev16(q), torch.from_numpy(qsl).cuda(), torch.from_numpy(L).cuda(), 64,
+                                      cache, torch.from_numpy(bt).cuda(), int(L[0]), 0.125)
+    torch.cuda.synchronize()
+    assert max_err(out_f64(out), ref) <= 2e-3
+
+
 # --------------------------------------------------------------------------- hybrid
 
 def test_hybrid_groups_full_size_sampled_rows():
