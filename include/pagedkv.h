@@ -160,6 +160,26 @@ PKV_API int pkv_cache_write(const void* key, const void* value, int32_t src_dtyp
                     const pkv_cache* cache, hipStream_t stream);
 
 /*
+ * Block copy for prefix sharing [W-zh § PagedAttention与Block管理: requests
+ * that share a prompt prefix point their tables' leading entries at the same
+ * physical blocks, each block counting its references and returning to the
+ * pool at zero].  A request about to write into a block it shares first
+ * moves to a private copy (copy-on-write, this build's reading of the
+ * sharing scheme); this call makes the copies.
+ *
+ * src_ids, dst_ids [num_pairs] device int32: block src_ids[i] is copied to
+ *                  block dst_ids[i], every element of the K and the V plane
+ *                  (block_size * num_kv_heads * head_dim elements each).
+ * err_count        optional device int32; a pair with an id outside
+ *                  [0, num_blocks) is skipped and adds 1.  The caller zeroes it.
+ * A block that is a destination and also a source, or two pairs with one
+ * destination, in one call: undefined (the copies race).
+ */
+PKV_API int pkv_copy_blocks(const pkv_cache* cache, const int32_t* src_ids,
+                    const int32_t* dst_ids, int32_t num_pairs,
+                    int32_t* err_count, hipStream_t stream);
+
+/*
  * Plan of the decode attention: how each row's visible blocks are cut into
  * pieces that are folded independently and merged afterwards, and the
  * workspace the partial results need.  Depends only on the arguments and on
@@ -180,7 +200,8 @@ typedef struct {
   int32_t kernel_variant; /* 0: the library's choice.  Tuning only: 1 = vector
                              ALUs for the scores (scheme 0 only); 2..5 =
                              scheme 1 with K/V loads issued 1..4 steps
-                             ahead.  Every variant computes the same result
+                             ahead; 6, 7 = scheme 1, 1 or 2 steps ahead,
+                             compiled for two waves per SIMD.  Every variant computes the same result
                              up to rounding order.                           */
   size_t workspace_bytes; /* partial (acc, m, l) storage (+ piece counts)         */
   int32_t scheme;         /* 0 or 1, see above                                    */

@@ -189,3 +189,43 @@ def unused_slot_mask(num_blocks, block_size, block_table, seq_lens):
                 if b * block_size + o < L:
                     live[phys, o] = True
     return ~live
+
+
+# --------------------------------------------------------------------------
+# Prefix sharing (Chinese worker-side page, § PagedAttention与Block管理:
+# requests that start with the same prompt point the leading entries of
+# their block tables at the same physical blocks; each block counts the
+# logical entries that reference it and returns to the pool only when that
+# count reaches zero).  Reading where the page is silent: a request that must
+# write into a block it shares first moves to a private copy of it.
+
+
+def refcounts(tables, num_blocks):
+    """References to each physical block: the number of table entries, over
+    every row of every table given, that hold its id (entries < 0 hold none)."""
+    counts = np.zeros(num_blocks, dtype=np.int64)
+    for t in tables:
+        for row in np.atleast_2d(np.asarray(t)):
+            for e in row:
+                e = int(e)
+                if e >= 0:
+                    counts[e] += 1
+    return counts
+
+
+def copy_blocks(k_plane, v_plane, src, dst):
+    """Block dst[i] of each plane becomes a copy of block src[i] of the
+    plane as it was before the call (the pairs are independent); a pair
+    with an id outside [0, num_blocks) changes nothing and is counted.
+
+    Returns (k_plane', v_plane', error count)."""
+    nb = k_plane.shape[0]
+    k_out, v_out = k_plane.copy(), v_plane.copy()
+    errors = 0
+    for s_, d_ in zip(np.asarray(src).tolist(), np.asarray(dst).tolist()):
+        if not (0 <= s_ < nb and 0 <= d_ < nb):
+            errors += 1
+            continue
+        k_out[d_] = k_plane[s_]
+        v_out[d_] = v_plane[s_]
+    return k_out, v_out, errors

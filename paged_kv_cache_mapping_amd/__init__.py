@@ -8,7 +8,7 @@ pool and layout helpers.  Importing it does not load the library; the first
 call does, and fails loudly if it has not been built.
 """
 
-from .api import (CacheView, cache_write, chunked_workspace_size, decode_plan,  # noqa: F401
+from .api import (CacheView, cache_write, chunked_workspace_size, copy_blocks, decode_plan,  # noqa: F401
                   fp8_dequantize, fp8_quantize, kv_bytes_per_token, paged_attention_chunked,
                   paged_attention_decode, paged_attention_decode_combine,
                   paged_attention_decode_partials, slot_mapping, status_string, tune_plan)

@@ -132,6 +132,20 @@ def cache_write(key, value, slot_mapping_, cache):
         ctypes.byref(c), _stream(key.device)))
 
 
+def copy_blocks(src_ids, dst_ids, cache, err_count=None):
+    """Copy blocks src_ids[i] -> dst_ids[i] (int32 device tensors) in both planes."""
+    lib = load()
+    _i32(src_ids, "src_ids")
+    _i32(dst_ids, "dst_ids")
+    _need(src_ids.numel() == dst_ids.numel(), "src_ids and dst_ids differ in length")
+    if err_count is not None:
+        _need(err_count.dtype == torch.int32, "err_count must be int32")
+    c = cache.c_struct()
+    check("pkv_copy_blocks", lib.pkv_copy_blocks(
+        ctypes.byref(c), _ptr(src_ids), _ptr(dst_ids), src_ids.numel(), _ptr(err_count),
+        _stream(src_ids.device)))
+
+
 def decode_plan(num_rows, num_q_heads, cache, max_seq_len, sliding_window=0):
     lib = load()
     plan = PkvDecodePlan()

@@ -1663,6 +1663,7 @@ void launch_stream(const DecodeArgs& a, int workers, hipStream_t s) {
     case 4: decode_flat_kernel<D, GT, KV, 3><<<workers, 64, lds, s>>>(a); break;
     case 5: decode_flat_kernel<D, GT, KV, 4><<<workers, 64, lds, s>>>(a); break;
     case 6: decode_flat_kernel_2w<D, GT, KV, 1><<<workers, 64, lds, s>>>(a); break;
+    case 7: decode_flat_kernel_2w<D, GT, KV, 2><<<workers, 64, lds, s>>>(a); break;
     default:
       // up to four heads per item the plan counts on two waves per SIMD, so
       // the kernel must fit in 256 registers (the fp8 build does not unless

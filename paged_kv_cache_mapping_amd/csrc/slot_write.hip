@@ -334,3 +334,43 @@ extern "C" int pkv_fp8_e4m3_dequantize(const uint8_t* codes, int64_t n, float sc
     fp8_dequantize_bf16_kernel<<<grid, 256, 0, stream>>>(codes, n, reinterpret_cast<uint16_t*>(out));
   return launch_status();
 }
+
+// ------------------------------------------------------------------ block copy
+// Copy-on-write support for blocks shared between requests: every element of
+// block src is copied to block dst in both planes.  One workgroup per (pair,
+// plane), 16-byte moves (block bases and block data sizes are multiples of
+// 16 bytes).
+__global__ __launch_bounds__(256) void copy_blocks_kernel(char* k, char* v, int64_t stride_bytes,
+                                                          int64_t data_bytes, const int32_t* __restrict__ src,
+                                                          const int32_t* __restrict__ dst, int32_t num_blocks,
+                                                          int32_t* err) {
+  const int pair = blockIdx.x;
+  const int s = src[pair];
+  const int d = dst[pair];
+  if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks) {
+    if (blockIdx.y == 0 && threadIdx.x == 0 && err) atomicAdd(err, 1);
+    return;
+  }
+  char* base = blockIdx.y == 0 ? k : v;
+  const uint4* from = reinterpret_cast<const uint4*>(base + (int64_t)s * stride_bytes);
+  uint4* to = reinterpret_cast<uint4*>(base + (int64_t)d * stride_bytes);
+  const int64_t n = data_bytes / 16;
+  for (int64_t i = threadIdx.x; i < n; i += 256) to[i] = from[i];
+}
+
+extern "C" int pkv_copy_blocks(const pkv_cache* cache, const int32_t* src_ids, const int32_t* dst_ids,
+                               int32_t num_pairs, int32_t* err_count, hipStream_t stream) {
+  int st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (num_pairs < 0) return PKV_ERR_SHAPE;
+  if (num_pairs == 0) return PKV_OK;
+  if (!src_ids || !dst_ids) return PKV_ERR_NULL;
+  const int es = dtype_size(cache->dtype);
+  const int64_t data = (int64_t)cache->block_size * cache->num_kv_heads * cache->head_dim * es;
+  if (data % 16) return PKV_ERR_UNSUPPORTED;
+  const dim3 grid((unsigned)num_pairs, 2);
+  copy_blocks_kernel<<<grid, 256, 0, stream>>>(reinterpret_cast<char*>(cache->k), reinterpret_cast<char*>(cache->v),
+                                               cache->block_stride * es, data, src_ids, dst_ids,
+                                               cache->num_blocks, err_count);
+  return launch_status();
+}

@@ -215,6 +215,40 @@ class GroupBlockTables:
                     self.pool.release([row[b]])
                     row[b] = -1
 
+    def fork(self, src_req, dst_req, num_tokens):
+        """Start dst_req with src_req's first num_tokens positions, sharing
+        their physical blocks (Chinese worker-side page, § PagedAttention与
+        Block管理: requests with a common prompt point their leading table
+        entries at the same blocks, each block counting its references)."""
+        need = -(-int(num_tokens) // self.block_size)
+        for g in range(len(self.windows)):
+            row = self.rows[g][src_req]
+            if need > len(row):
+                raise ValueError("request %r holds fewer than %d positions" % (src_req, num_tokens))
+            shared = list(row[:need])
+            self.pool.share([i for i in shared if i >= 0])
+            self.rows[g][dst_req] = shared
+
+    def prepare_write(self, req, pos_lo, pos_hi):
+        """Make the blocks that positions pos_lo .. pos_hi - 1 fall in private
+        to req before its tokens are written there: the row grows as needed,
+        and a block other tables still reference is replaced by a fresh one.
+        Returns the (old id, new id) pairs whose contents must be copied
+        (pkv_copy_blocks) before the write; the old ids stay live."""
+        self.grow(req, pos_hi)
+        pairs = []
+        lo, hi = int(pos_lo) // self.block_size, -(-int(pos_hi) // self.block_size)
+        for g in range(len(self.windows)):
+            row = self.rows[g][req]
+            for b in range(lo, min(hi, len(row))):
+                old = row[b]
+                if old >= 0 and self.pool.refcount[old] > 1:
+                    new = self.pool.allocate(1)[0]
+                    self.pool.release([old])
+                    row[b] = new
+                    pairs.append((old, new))
+        return pairs
+
     def finish(self, req):
         for g in range(len(self.windows)):
             self.pool.release([i for i in self.rows[g].pop(req) if i >= 0])

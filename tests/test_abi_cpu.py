@@ -35,7 +35,7 @@ def test_header_declares_the_expected_calls():
                  "pkv_paged_attention_chunked", "pkv_decode_plan_make",
                  "pkv_paged_attention_decode_partials", "pkv_paged_attention_decode_combine",
                  "pkv_chunked_workspace_size", "pkv_kv_bytes_per_token", "pkv_status_string",
-                 "pkv_fp8_e4m3_quantize", "pkv_fp8_e4m3_dequantize"):
+                 "pkv_fp8_e4m3_quantize", "pkv_fp8_e4m3_dequantize", "pkv_copy_blocks"):
         assert want in names
     assert set(names) == set(_lib.SIGNATURES)   # the binding covers every declaration
 
@@ -121,3 +121,8 @@ def test_argument_checks_return_before_launching(lib):
     assert lib.pkv_fp8_e4m3_dequantize(0x100, 16, 2.0, _lib.PKV_BF16, 0x100, None) == \
         _lib.PKV_ERR_UNSUPPORTED
     assert lib.pkv_fp8_e4m3_dequantize(0x100, 0, 1.0, _lib.PKV_F32, 0x100, None) == _lib.PKV_OK
+    # block copy: bad cache, negative or empty pair lists, missing id arrays
+    assert lib.pkv_copy_blocks(ctypes.byref(_cache(k=0)), 0x100, 0x100, 4, None, None) == _lib.PKV_ERR_NULL
+    assert lib.pkv_copy_blocks(ctypes.byref(c), 0x100, 0x100, -1, None, None) == _lib.PKV_ERR_SHAPE
+    assert lib.pkv_copy_blocks(ctypes.byref(c), None, 0x100, 4, None, None) == _lib.PKV_ERR_NULL
+    assert lib.pkv_copy_blocks(ctypes.byref(c), None, None, 0, None, None) == _lib.PKV_OK

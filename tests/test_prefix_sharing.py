@@ -1,0 +1,150 @@
+"""Prefix sharing: oracle pins for reference counts and block copies, and the
+host tables' fork / copy-on-write logic against the oracle's counts (CPU).
+
+The pages' case (Chinese worker-side page, § PagedAttention与Block管理):
+requests with a common prompt point their leading table entries at the same
+physical blocks; a block counts the entries that reference it and is freed
+at zero.  Copy-on-write before a private write is this build's reading.
+"""
+
+import numpy as np
+import pytest
+
+from paged_kv_cache_mapping_amd import kv_cache
+from oracle import attention, bf16, paging
+
+
+# ---------------------------------------------------------------- oracle pins
+
+def test_refcounts_hand_example():
+    tables = [np.array([[3, 5, -1], [3, 7, 5]]), np.array([[7, -1, -1]])]
+    c = paging.refcounts(tables, 9)
+    assert c.tolist() == [0, 0, 0, 2, 0, 2, 0, 2, 0]
+    assert c.sum() == sum(int((np.asarray(t) >= 0).sum()) for t in tables)
+
+
+def test_copy_blocks_reads_back_through_the_table():
+    """After copying src -> dst, gathering a request's positions through a
+    table row that points at dst gives the rows it gave through src; blocks
+    outside the pairs keep their bits; bad pairs are counted and skipped."""
+    rng = np.random.default_rng(3)
+    nb, bs, H, D = 10, 4, 2, 8
+    kp = rng.integers(0, 1 << 16, size=(nb, bs, H, D), dtype=np.uint16)
+    vp = rng.integers(0, 1 << 16, size=(nb, bs, H, D), dtype=np.uint16)
+    src, dst = [2, 7, 4, -1, 3], [5, 0, 9, 1, 12]
+    k2, v2, err = paging.copy_blocks(kp, vp, src, dst)
+    assert err == 2
+    pos = np.arange(bs)
+    for s, d in zip(src[:3], dst[:3]):
+        for plane, out in ((kp, k2), (vp, v2)):
+            np.testing.assert_array_equal(paging.gather_positions(out, [d], pos, bs),
+                                          paging.gather_positions(plane, [s], pos, bs))
+    untouched = [b for b in range(nb) if b not in dst[:3]]
+    np.testing.assert_array_equal(k2[untouched], kp[untouched])
+    np.testing.assert_array_equal(v2[untouched], vp[untouched])
+
+
+def test_shared_prefix_attention_equals_private_copies():
+    """Attention over tables whose leading entries are shared equals
+    attention over tables where every request holds a private copy of the
+    prompt (exact, in the oracle)."""
+    rng = np.random.default_rng(11)
+    bs, H, D, Hq = 4, 1, 8, 2
+    prompt_blocks, R = 3, 3
+    nb = prompt_blocks * (R + 1) + R
+    kp = bf16.from_f32(rng.standard_normal((nb, bs, H, D)).astype(np.float32))
+    vp = bf16.from_f32(rng.standard_normal((nb, bs, H, D)).astype(np.float32))
+    shared = list(range(prompt_blocks))
+    tail = [nb - 1 - r for r in range(R)]
+    t_shared = np.array([shared + [tail[r]] for r in range(R)], np.int32)
+    src = [b for r in range(R) for b in shared]
+    dst = [prompt_blocks * (r + 1) + i for r in range(R) for i in range(prompt_blocks)]
+    k2, v2, err = paging.copy_blocks(kp, vp, src, dst)
+    assert err == 0
+    t_private = np.array([dst[r * prompt_blocks:(r + 1) * prompt_blocks] + [tail[r]] for r in range(R)],
+                         np.int32)
+    L = np.array([prompt_blocks * bs + 1 + r for r in range(R)], np.int32)
+    qsl = np.arange(R + 1, dtype=np.int32)
+    q = bf16.from_f32(rng.standard_normal((R, Hq, D)).astype(np.float32))
+    a = attention.paged_attention(q, "bf16", kp, vp, "bf16", t_shared, L, qsl, 0.3)
+    b = attention.paged_attention(q, "bf16", k2, v2, "bf16", t_private, L, qsl, 0.3)
+    np.testing.assert_array_equal(a, b)
+
+
+# ---------------------------------------------------------------- host logic
+
+def _all_tables(tabs, reqs):
+    return [tabs.table(g, reqs) for g in range(len(tabs.windows))] if reqs else []
+
+
+def test_fork_shares_the_prompt_and_cow_copies_the_partial_block():
+    bs = 16
+    pool = kv_cache.BlockPool(64, order=np.random.default_rng(1).permutation(64))
+    tabs = kv_cache.GroupBlockTables(pool, [0], bs)
+    tabs.add_request(0)
+    assert tabs.prepare_write(0, 0, 40) == []          # private from the start
+    for r in (1, 2, 3):
+        tabs.fork(0, r, 40)                              # 40 tokens: 2 full blocks + 8 of a third
+    assert all(tabs.rows[0][r] == tabs.rows[0][0] for r in (1, 2, 3))
+    np.testing.assert_array_equal(pool.refcount, paging.refcounts(_all_tables(tabs, [0, 1, 2, 3]), 64))
+    old = tabs.rows[0][0][2]
+    pairs = tabs.prepare_write(1, 40, 45)                # request 1 appends into the shared third block
+    assert len(pairs) == 1 and pairs[0][0] == old
+    new = pairs[0][1]
+    assert tabs.rows[0][1][2] == new and tabs.rows[0][1][:2] == tabs.rows[0][0][:2]
+    assert pool.refcount[new] == 1 and pool.refcount[old] == 3
+    np.testing.assert_array_equal(pool.refcount, paging.refcounts(_all_tables(tabs, [0, 1, 2, 3]), 64))
+    # writing past the shared blocks (a fresh fourth block) needs no copy
+    assert tabs.prepare_write(2, 48, 60) == []
+    assert tabs.rows[0][2][:3] == tabs.rows[0][0][:3] and pool.refcount[tabs.rows[0][2][3]] == 1
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_random_fork_write_finish_keeps_counts_exact(seed):
+    """Random forks, appends and finishes: the pool's counts always equal the
+    oracle's count of table entries; a block a request just prepared for
+    writing is referenced by that request alone; no id is both free and live;
+    every copy pair's source is still live."""
+    rng = np.random.default_rng(seed)
+    bs, nb = 8, 400
+    pool = kv_cache.BlockPool(nb, order=rng.permutation(nb))
+    tabs = kv_cache.GroupBlockTables(pool, [0, 0], bs)
+    lens = {}
+    nxt = 0
+    for _ in range(300):
+        op = rng.integers(0, 4)
+        live = sorted(lens)
+        if op == 0 or not live:
+            tabs.add_request(nxt)
+            lens[nxt] = 0
+            nxt += 1
+        elif op == 1:
+            src = int(rng.choice(live))
+            if lens[src] > 0:
+                n = int(rng.integers(1, lens[src] + 1))
+                tabs.add_request(nxt)
+                tabs.fork(src, nxt, n)
+                lens[nxt] = n
+                nxt += 1
+        elif op == 2:
+            r = int(rng.choice(live))
+            grow = int(rng.integers(1, 3 * bs))
+            if pool.num_free < 2 * (grow // bs + 2):
+                continue
+            pairs = tabs.prepare_write(r, lens[r], lens[r] + grow)
+            for s, d in pairs:
+                assert pool.refcount[s] >= 1 and pool.refcount[d] == 1
+            for g in range(2):
+                row = tabs.rows[g][r]
+                for b in range(lens[r] // bs, -(-(lens[r] + grow) // bs)):
+                    assert pool.refcount[row[b]] == 1
+            lens[r] += grow
+        else:
+            r = int(rng.choice(live))
+            tabs.finish(r)
+            del lens[r]
+        reqs = sorted(lens)
+        counts = paging.refcounts(_all_tables(tabs, reqs), nb) if reqs else np.zeros(nb, np.int64)
+        np.testing.assert_array_equal(pool.refcount, counts)
+        assert not (set(pool._free) & set(np.nonzero(counts)[0].tolist()))
+        assert pool.num_free + int((counts > 0).sum()) == nb
