@@ -35,6 +35,8 @@ DATA_NOTE = {
            "lognormal lengths, median 1024, clipped to 16..32768)",
     "hybrid": "synthetic (seeded N(0,1)/sqrt(128) bf16; 96 decode requests 1k..16k + 4 prefill "
               "chunks of 512, full and sliding-window groups over shared tensors)",
+    "prefix": "synthetic (seeded N(0,1)/sqrt(128) bf16; 100 requests sharing the blocks of one "
+              "2000-token prompt, 1..64 private tokens each)",
 }
 POOLS = 3
 SPLIT_KERNEL = "decode_flat_kernel_2w"
@@ -45,8 +47,10 @@ KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_mapping_amd", "csrc", "decode
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--workload", default="llama8b", choices=["llama8b", "llama70b", "fp8", "hybrid"],
-                   help="llama8b (default line), llama70b (80 allocated layers), fp8, hybrid")
+    p.add_argument("--workload", default="llama8b",
+                   choices=["llama8b", "llama70b", "fp8", "hybrid", "prefix"],
+                   help="llama8b (default line), llama70b (80 allocated layers), fp8, hybrid, "
+                        "prefix (shared prompt blocks)")
     p.add_argument("--layers", type=int, default=80, help="llama70b: layers allocated and rotated")
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
@@ -86,7 +90,8 @@ def algorithmic_bytes(w):
     """HBM bytes a decode step must move, by kernel (see the roofline notes)."""
     B, Hq, D, Hkv = w.num_reqs, w.num_q_heads, w.head_dim, w.num_kv_heads
     nblk = int(sum(-(-int(L) // w.block_size) for L in w.seq_lens))
-    kv = w.kv_read_bytes()
+    # with shared prompt blocks, HBM need deliver each distinct row only once
+    kv = w.info.get("unique_kv_bytes", w.kv_read_bytes())
     q = B * Hq * D * 2
     out = B * Hq * D * 2
     split = kv + q + nblk * 4 + B * 4
@@ -380,7 +385,7 @@ def main():
     if args.workload == "hybrid":
         return bench_hybrid(args, dev)
     w = {"llama8b": workloads.llama8b_decode, "llama70b": workloads.llama70b_decode,
-         "fp8": workloads.fp8_decode}[args.workload]()
+         "fp8": workloads.fp8_decode, "prefix": workloads.shared_prefix_decode}[args.workload]()
     base = w.device(dev)
     nb = w.num_blocks
     extra = {}
@@ -479,6 +484,33 @@ def main():
     torch.cuda.synchronize()
     writes["bf16_T64_step"] = dict(us=round(a.elapsed_time(b) / 50 * 1e3, 2))
 
+    sharing = {}
+    if args.workload == "prefix":
+        # logical reads (every request's whole context) and the block saving
+        logical = w.kv_read_bytes()
+        sharing = dict(logical_kv_bytes=logical, unique_kv_bytes=w.info["unique_kv_bytes"],
+                       logical_split_GBps=round(logical / (split_ms * 1e-3) / 1e9, 1),
+                       blocks_with_sharing=w.info["blocks_used"],
+                       blocks_without_sharing=w.info["blocks_without_sharing"],
+                       cow_pairs=w.info["cow_pairs"])
+        # copy-on-write throughput: 4096 disjoint block pairs, both planes
+        gen = torch.Generator(device=dev).manual_seed(7)
+        perm = torch.randperm(nb, generator=gen, device=dev).to(torch.int32)
+        src, dst = perm[:4096].contiguous(), perm[4096:8192].contiguous()
+        cache = pools[0][0]
+        for _ in range(3):
+            pkv.copy_blocks(src, dst, cache)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(20):
+            pkv.copy_blocks(src, dst, cache)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / 20
+        blk = w.block_size * w.num_kv_heads * w.head_dim * 2
+        sharing["copy_blocks_4096_pairs"] = dict(us=round(ms * 1e3, 2),
+                                                 GBps=round(4096 * blk * 2 * 2 / (ms * 1e-3) / 1e9, 1))
+
     if args.calibration_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -514,6 +546,7 @@ def main():
                              "split_GBps": round(split_gbps, 1),
                              "kv_bytes": ab["kv"], "step_bytes": ab["step"]},
         "kv_write": writes,
+        **({"prefix_sharing": sharing} if sharing else {}),
         "roofline": {"bound": "hbm", "achieved": round(split_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(split_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": SPLIT_KERNEL,

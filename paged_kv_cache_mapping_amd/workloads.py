@@ -236,6 +236,55 @@ def fp8_decode(seed=4, batch=128, sigma_len=1.0):
         q_dtype="bf16", sigma=1.0, fp8_amax_scale=True)
 
 
+def shared_prefix_decode(seed=6, num_reqs=100, prompt=2000, suffix_hi=64, pool=16384, block_size=16):
+    """Prefix sharing (Chinese worker-side page, § PagedAttention与Block管理:
+    100 requests opening with one 2000-token system prompt): every request's
+    table starts with the prompt's blocks, held once in the pool by
+    reference; each request then has 1..suffix_hi private tokens, the last
+    being this step's decode token.  bf16, 32/8 heads, D 128, block 16.
+
+    The tables come from the host pool: request 0 writes the prompt, the
+    others fork it, and every request makes its suffix blocks private
+    (copy-on-write pairs only arise when the prompt ends inside a block)."""
+    D, Hq, Hkv = 128, 32, 8
+    rng = np.random.default_rng(seed)
+    suffix = rng.integers(1, suffix_hi + 1, size=num_reqs)                      # lengths
+    lengths = (prompt + suffix).astype(np.int32)
+    perm = rng.permutation(pool)                                                # permutation
+    bp = kv_cache.BlockPool(pool, order=perm)
+    tabs = kv_cache.GroupBlockTables(bp, [0], block_size)
+    tabs.add_request(0)
+    tabs.prepare_write(0, 0, prompt)
+    for r in range(1, num_reqs):
+        tabs.add_request(r)
+        tabs.fork(0, r, prompt)
+    cow = []
+    for r in range(num_reqs):
+        cow += tabs.prepare_write(r, prompt, int(lengths[r]))
+    bt = tabs.table(0, list(range(num_reqs)))
+    ids = np.nonzero(bp.refcount)[0].astype(np.int32)
+    shape = (pool, block_size, Hkv, D)
+    sigma = 1.0 / np.sqrt(D)
+    kp, vp = nan_plane(shape, "bf16"), nan_plane(shape, "bf16")
+    _fill_history(rng, kp, ids, shape[1:], "bf16", sigma)                       # K history
+    _fill_history(rng, vp, ids, shape[1:], "bf16", sigma)                       # V history
+    for src, dst in cow:                                                        # copied blocks
+        kp[dst], vp[dst] = kp[src], vp[src]
+    nk = bf16_bits(rng.standard_normal((num_reqs, Hkv, D), dtype=np.float32) * np.float32(sigma))
+    nv = bf16_bits(rng.standard_normal((num_reqs, Hkv, D), dtype=np.float32) * np.float32(sigma))
+    q = bf16_bits(rng.standard_normal((num_reqs, Hq, D), dtype=np.float32) * np.float32(sigma))  # Q
+    without = int(sum(-(-int(L) // block_size) for L in lengths))
+    unique_rows = prompt + int(suffix.sum())
+    return Workload(
+        name="shared_prefix_decode_b%d_prompt%d" % (num_reqs, prompt), block_size=block_size,
+        num_blocks=pool, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, cache_dtype="bf16",
+        q_dtype="bf16", k_plane=kp, v_plane=vp, new_k=nk, new_v=nv, q=q, block_table=bt,
+        seq_lens=lengths, query_start_loc=np.arange(num_reqs + 1, dtype=np.int32),
+        num_computed=(lengths - 1).astype(np.int32), scale=float(1.0 / np.sqrt(D)), decode=True,
+        info=dict(seed=seed, blocks_used=int(len(ids)), blocks_without_sharing=without,
+                  cow_pairs=len(cow), unique_kv_bytes=unique_rows * Hkv * D * 2 * 2))
+
+
 # ---------------------------------------------------------------------------
 # Hybrid groups with chunked prefill.
 

@@ -148,3 +148,24 @@ def test_random_fork_write_finish_keeps_counts_exact(seed):
         np.testing.assert_array_equal(pool.refcount, counts)
         assert not (set(pool._free) & set(np.nonzero(counts)[0].tolist()))
         assert pool.num_free + int((counts > 0).sum()) == nb
+
+
+def test_shared_prefix_workload_tables():
+    """The bench's prefix workload: the prompt's 125 blocks are referenced
+    by all 100 rows and by nothing else; every other live block by exactly
+    one row; live blocks hold finite data, the rest of the pool is NaN."""
+    from paged_kv_cache_mapping_amd import workloads
+    from oracle import bf16 as obf16
+    w = workloads.shared_prefix_decode()
+    bt = w.block_table
+    counts = paging.refcounts([bt], w.num_blocks)
+    prompt_ids = bt[0, :125]
+    assert (bt[:, :125] == prompt_ids).all()
+    assert (counts[prompt_ids] == 100).all()
+    others = np.setdiff1d(np.nonzero(counts)[0], prompt_ids)
+    assert (counts[others] == 1).all()
+    assert len(prompt_ids) + len(others) == w.info["blocks_used"]
+    live = np.nonzero(counts)[0]
+    assert np.isfinite(obf16.to_f64(w.k_plane[live])).all()
+    dead = np.setdiff1d(np.arange(w.num_blocks), live)[:64]
+    assert np.isnan(obf16.to_f64(w.k_plane[dead])).all()
