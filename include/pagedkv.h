@@ -114,6 +114,24 @@ PKV_API int64_t pkv_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads,
                                int32_t head_dim, int32_t dtype);
 
 /*
+ * Blocks a memory budget holds [P § Memory Pre-allocation Logic: the budget
+ * is total GPU memory times the utilisation ratio; KV bytes are the budget
+ * less the non-KV memory; the block count divides them by one block's size
+ * and the number of layers].  With hybrid groups the layers that share one
+ * block pool are the KV tensors (one per position within a group, W §
+ * Hybrid Attention Mechanisms), so num_tensors takes their count.
+ * One block = block_size * num_kv_heads * head_dim * 2 (K and V) * element
+ * bytes.  budget = floor(total_bytes * utilization) (double arithmetic).
+ * Host-only.  Returns the count (0 when the budget leaves no KV bytes), or
+ * PKV_ERR_DTYPE / PKV_ERR_SHAPE (utilization outside (0, 1], sizes <= 0,
+ * negative byte counts).
+ */
+PKV_API int64_t pkv_num_blocks_for_budget(int64_t total_bytes, double utilization,
+                               int64_t non_kv_bytes, int32_t num_tensors,
+                               int32_t block_size, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t dtype);
+
+/*
  * Step 1 -- slot mapping [W § Pinpointing the Token Slot; E § Slot mapping은
  * 왜 필요한가; E § EngineCore가 하는 일 (num_new_tokens)].
  *

@@ -63,6 +63,7 @@ _int = ctypes.c_int
 SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [_int]),
     "pkv_kv_bytes_per_token": (_i64, [_i32, _i32, _i32, _i32]),
+    "pkv_num_blocks_for_budget": (_i64, [_i64, ctypes.c_double, _i64, _i32, _i32, _i32, _i32, _i32]),
     "pkv_slot_mapping": (_int, [_vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "pkv_cache_write": (_int, [_vp, _vp, _i32, _i64, _i64, _vp, _i32, ctypes.POINTER(PkvCache), _vp]),
     "pkv_decode_plan_make": (_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,

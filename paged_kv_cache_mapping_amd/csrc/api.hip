@@ -47,3 +47,21 @@ extern "C" int64_t pkv_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_hea
   if (elt == 0 || num_layers < 0 || num_kv_heads < 0 || head_dim < 0) return -1;
   return (int64_t)num_layers * num_kv_heads * head_dim * 2 * elt;
 }
+
+// Blocks a memory budget holds: floor(total * utilisation) - non-KV bytes,
+// divided by one block's K+V bytes times the KV tensors sharing the pool.
+extern "C" int64_t pkv_num_blocks_for_budget(int64_t total_bytes, double utilization,
+                                             int64_t non_kv_bytes, int32_t num_tensors,
+                                             int32_t block_size, int32_t num_kv_heads,
+                                             int32_t head_dim, int32_t dtype) {
+  const int elt = pkv::dtype_size(dtype);
+  if (elt == 0) return PKV_ERR_DTYPE;
+  if (total_bytes < 0 || non_kv_bytes < 0 || num_tensors <= 0 || block_size <= 0 ||
+      num_kv_heads <= 0 || head_dim <= 0 || !(utilization > 0.0 && utilization <= 1.0))
+    return PKV_ERR_SHAPE;
+  const int64_t budget = (int64_t)((double)total_bytes * utilization);
+  const int64_t available = budget - non_kv_bytes;
+  if (available <= 0) return 0;
+  const int64_t per_block = (int64_t)block_size * num_kv_heads * head_dim * 2 * elt * num_tensors;
+  return available / per_block;
+}

@@ -98,6 +98,29 @@ def hybrid_config(groups, num_blocks):
     return KVCacheConfig(num_blocks=num_blocks, groups=list(groups), tensors=tensors)
 
 
+def num_blocks_for_budget(total_bytes, utilization, non_kv_bytes, spec, num_tensors):
+    """Blocks a memory budget holds (PageAttention blog, § Memory
+    Pre-allocation Logic), computed by the library: floor(total *
+    utilisation) less the non-KV bytes, over one block's K+V bytes times the
+    KV tensors that share the pool."""
+    from . import _lib
+    code = {"f32": _lib.PKV_F32, "bf16": _lib.PKV_BF16, "fp8": _lib.PKV_FP8_E4M3}[spec.dtype]
+    n = _lib.load().pkv_num_blocks_for_budget(int(total_bytes), float(utilization), int(non_kv_bytes),
+                                              int(num_tensors), spec.block_size, spec.num_kv_heads,
+                                              spec.head_dim, code)
+    if n < 0:
+        raise ValueError("bad budget arguments (%s)" % _lib.load().pkv_status_string(int(n)).decode())
+    return int(n)
+
+
+def budget_config(groups, total_bytes, utilization, non_kv_bytes):
+    """hybrid_config with as many blocks as the budget holds: every slot's
+    tensor gets num_blocks pages."""
+    nslots = max(len(grp.layer_names) for grp in groups)
+    n = num_blocks_for_budget(total_bytes, utilization, non_kv_bytes, groups[0].spec, nslots)
+    return hybrid_config(groups, n)
+
+
 def allocate(config, device, zero=False, k_scale=1.0, v_scale=1.0):
     """Allocate every tensor as a byte buffer and return {layer: CacheView}.
 

@@ -126,3 +126,34 @@ def test_argument_checks_return_before_launching(lib):
     assert lib.pkv_copy_blocks(ctypes.byref(c), 0x100, 0x100, -1, None, None) == _lib.PKV_ERR_SHAPE
     assert lib.pkv_copy_blocks(ctypes.byref(c), None, 0x100, 4, None, None) == _lib.PKV_ERR_NULL
     assert lib.pkv_copy_blocks(ctypes.byref(c), None, None, 0, None, None) == _lib.PKV_OK
+
+
+def test_num_blocks_for_budget_matches_the_oracle(lib):
+    """The library's budget arithmetic equals the oracle's closed form
+    (PageAttention blog, § Memory Pre-allocation Logic) over a grid."""
+    from oracle import sizing
+    codes = {"f32": _lib.PKV_F32, "bf16": _lib.PKV_BF16, "fp8": _lib.PKV_FP8_E4M3}
+    for total in (0, 10 ** 9, 64 * 2 ** 30, 288 * 10 ** 9):
+        for util in (0.5, 0.9, 0.95, 1.0):
+            for non_kv in (0, 10 ** 9, 20 * 10 ** 9):
+                for layers in (1, 12, 80):
+                    for dt in ("f32", "bf16", "fp8"):
+                        got = lib.pkv_num_blocks_for_budget(total, util, non_kv, layers, 16, 8, 128, codes[dt])
+                        assert got == sizing.num_blocks_for_budget(total, util, non_kv, layers, 16, 8, 128, dt)
+    assert lib.pkv_num_blocks_for_budget(10 ** 9, 0.0, 0, 1, 16, 8, 128, _lib.PKV_BF16) == _lib.PKV_ERR_SHAPE
+    assert lib.pkv_num_blocks_for_budget(10 ** 9, 1.5, 0, 1, 16, 8, 128, _lib.PKV_BF16) == _lib.PKV_ERR_SHAPE
+    assert lib.pkv_num_blocks_for_budget(10 ** 9, 0.9, 0, 0, 16, 8, 128, _lib.PKV_BF16) == _lib.PKV_ERR_SHAPE
+    assert lib.pkv_num_blocks_for_budget(10 ** 9, 0.9, 0, 1, 16, 8, 128, 9) == _lib.PKV_ERR_DTYPE
+
+
+def test_budget_config_fills_the_budget(lib):
+    """Hybrid groups sized from a budget: the tensors fit in what the budget
+    leaves for KV, and one more block per tensor would not."""
+    from paged_kv_cache_mapping_amd import kv_cache
+    spec = kv_cache.KVCacheSpec(16, 8, 128, "bf16")
+    groups = [kv_cache.KVCacheGroupSpec(["L0", "L2"], spec), kv_cache.KVCacheGroupSpec(["L1", "L3"], spec)]
+    total, util, non_kv = 288 * 10 ** 9, 0.9, 17 * 10 ** 9
+    cfg = kv_cache.budget_config(groups, total, util, non_kv)
+    kv = int(total * util) - non_kv
+    used = sum(t.size for t in cfg.tensors)
+    assert len(cfg.tensors) == 2 and used <= kv < used + len(cfg.tensors) * spec.page_bytes
