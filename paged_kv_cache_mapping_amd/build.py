@@ -32,7 +32,12 @@ COMMON_FLAGS = [
 
 
 def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    """Every .hip source; the heavy instantiation units first, so that the
+    parallel build does not end on a long one started late."""
+    def weight(f):
+        return (0 if f.startswith("decode_multi_d") else 1 if f.startswith("decode_d") else 2, f)
+    return [os.path.join(CSRC, f) for f in sorted((f for f in os.listdir(CSRC) if f.endswith(".hip")),
+                                                  key=weight)]
 
 
 def _compile(src):

@@ -150,6 +150,9 @@ PKV_DECODE_ALL_D(extern, 32)
 PKV_DECODE_ALL_D(extern, 64)
 PKV_DECODE_ALL_D(extern, 128)
 PKV_DECODE_ALL_D(extern, 256)
+PKV_DECODE_MULTI_INST(extern, 128, PKV_BF16)
+PKV_DECODE_MULTI_INST(extern, 128, PKV_FP8_E4M3)
+PKV_DECODE_MERGE_MULTI_INST(extern, 128)
 
 template <int D>
 static int split_d(const DecodeArgs& a, int gt, int kv, hipStream_t s) {
@@ -177,6 +180,14 @@ static int stream_d(const DecodeArgs& a, int kv, int workers, hipStream_t s) {
   return PKV_ERR_UNSUPPORTED;
 }
 
+// Multi-token items (row mode 3), head size 128.
+static int dispatch_multi(const DecodeArgs& a, int kv, int workers, hipStream_t s) {
+  if (a.head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (kv == PKV_BF16) return run_multi_dk<128, PKV_BF16>(a, workers, s);
+  if (kv == PKV_FP8_E4M3) return run_multi_dk<128, PKV_FP8_E4M3>(a, workers, s);
+  return PKV_ERR_UNSUPPORTED;
+}
+
 static int dispatch_stream(const DecodeArgs& a, int kv, int workers, hipStream_t s) {
   switch (a.head_dim) {
     case 32: return stream_d<32>(a, kv, workers, s);
@@ -188,6 +199,7 @@ static int dispatch_stream(const DecodeArgs& a, int kv, int workers, hipStream_t
 }
 
 static int dispatch_combine(const DecodeArgs& a, int ot, hipStream_t s) {
+  if (a.qt > 1) return a.head_dim == 128 ? run_merge_multi_d<128>(a, ot, s) : PKV_ERR_UNSUPPORTED;
   switch (a.head_dim) {
     case 8: return run_combine_d<8>(a, ot, s);
     case 16: return run_combine_d<16>(a, ot, s);
@@ -224,7 +236,7 @@ static int prepare(DecodeArgs& a, void* out, const void* q, int q_dtype, int row
   if (hq % cache->num_kv_heads) return PKV_ERR_SHAPE;
   const int want_q = cache->dtype == PKV_F32 ? PKV_F32 : PKV_BF16;
   if (q_dtype != want_q) return PKV_ERR_DTYPE;
-  const int extra = (row_mode == 1 && !causal && max_query_len > 0) ? max_query_len - 1 : 0;
+  const int extra = ((row_mode == 1 && !causal) || row_mode == 3) && max_query_len > 0 ? max_query_len - 1 : 0;
   st = check_plan(plan, rows, hq, cache->num_kv_heads, cache->head_dim, cache->block_size,
                   cache->dtype, max_seq_len, window, extra);
   if (st != PKV_OK) return st;
@@ -276,6 +288,7 @@ static int prepare(DecodeArgs& a, void* out, const void* q, int q_dtype, int row
   a.heads_per_item = plan->heads_per_item;
   a.lead_workers = plan->lead_workers;
   a.trail_pct = plan->trail_share_pct;
+  a.qt = 1;
   {
     // LDS one worker may take so that all workers stay resident
     const long long cus = device_cu_count();
@@ -293,7 +306,8 @@ static int prepare(DecodeArgs& a, void* out, const void* q, int q_dtype, int row
 static int run_split(const DecodeArgs& a, const pkv_decode_plan& plan, int kv_dtype, hipStream_t s) {
   if (a.num_rows == 0) return PKV_OK;
   int st;
-  if (plan.scheme == 1) st = dispatch_stream(a, kv_dtype, plan.num_workers, s);
+  if (plan.scheme == 1 && a.qt > 1) st = dispatch_multi(a, kv_dtype, plan.num_workers, s);
+  else if (plan.scheme == 1) st = dispatch_stream(a, kv_dtype, plan.num_workers, s);
   else st = dispatch_split(a, a.group / a.sub_groups, kv_dtype, s);
   if (st != PKV_OK) return st;
   return launch_status();
@@ -400,10 +414,25 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dt
 // query take the decode kernels (rows = requests), every other request's
 // tokens take the per-token rows.  Each pass has its own workspace region.
 struct ChunkPlans {
-  pkv_decode_plan single, multi;
-  size_t single_bytes, multi_bytes;   // multi_bytes: the per-token rows, or the prefill slots
+  pkv_decode_plan single, multi, spec;
+  size_t single_bytes, multi_bytes;   // multi_bytes: the multi-query requests' region
   bool prefill;           // multi-query requests on the matrix-core prefill kernel
+  int spec_qt;            // > 0: multi-query requests as multi-token decode items
 };
+
+// Query tokens per item when the step's multi-query requests are short
+// enough to run as decode items (2 .. 8 tokens; a power of two at least
+// max_query_len, times the group at most 16 MFMA rows), else 0.
+static int multi_token_qt(const pkv_cache* c, int hq, int max_query_len, int num_reqs) {
+  if (max_query_len < 2 || max_query_len > 8 || num_reqs > kMaxStreamRows) return 0;
+  if (!mfma_eligible(c->dtype, c->head_dim, c->block_size)) return 0;
+  if (c->head_dim != 128) return 0;
+  const int g = hq / c->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return 0;
+  int qt = 2;
+  while (qt < max_query_len) qt <<= 1;
+  return g * qt <= 16 ? qt : 0;
+}
 
 static int chunk_plans(int num_tokens, int num_reqs, int hq, const pkv_cache* c, int max_query_len,
                        int max_seq_len, int window, ChunkPlans& p) {
@@ -416,9 +445,18 @@ static int chunk_plans(int num_tokens, int num_reqs, int hq, const pkv_cache* c,
                  max_seq_len, window, extra, false, &p.multi);
   if (st != PKV_OK) return st;
   p.single_bytes = (p.single.workspace_bytes + 255) & ~(size_t)255;
-  p.prefill = prefill_supported(c->dtype, c->head_dim, hq / c->num_kv_heads, max_seq_len,
-                                c->block_size, window, max_query_len);
+  p.spec_qt = multi_token_qt(c, hq, max_query_len, num_reqs);
+  if (p.spec_qt > 0) {
+    // one item per (request, KV head): the group's heads times the tokens
+    const int g = hq / c->num_kv_heads;
+    st = make_plan(num_reqs, hq * p.spec_qt, c->num_kv_heads, c->head_dim, c->block_size, c->dtype,
+                   max_seq_len, window, max_query_len - 1, true, &p.spec);
+    if (st != PKV_OK || p.spec.scheme != 1 || p.spec.heads_per_item != g * p.spec_qt) p.spec_qt = 0;
+  }
+  p.prefill = p.spec_qt == 0 && prefill_supported(c->dtype, c->head_dim, hq / c->num_kv_heads,
+                                                  max_seq_len, c->block_size, window, max_query_len);
   p.multi_bytes = max_query_len <= 1 ? 0
+                  : p.spec_qt > 0   ? p.spec.workspace_bytes
                   : p.prefill       ? prefill_workspace_bytes(c->head_dim)
                                     : p.multi.workspace_bytes;
   return PKV_OK;
@@ -475,7 +513,26 @@ extern "C" int pkv_paged_attention_chunked(void* out, const void* q, int32_t q_d
                max_query_len, 1, &p.single, ws, p.single_bytes);
   if (st != PKV_OK) return st;
   a1.num_tokens = num_tokens;
-  if (max_query_len > 1 && p.prefill) {
+  if (max_query_len > 1 && p.spec_qt > 0) {
+    // multi-query requests as decode items of heads x query tokens; the
+    // plan and workspace count one "head" per (token, head) pair
+    if (!out || !q || !block_table || !seq_lens) return PKV_ERR_NULL;
+    DecodeArgs a3;
+    st = prepare(a3, out, q, q_dtype, num_reqs, num_q_heads * p.spec_qt, cache, block_table, bt_stride,
+                 seq_lens, max_seq_len, softmax_scale, sliding_window, 3, query_start_loc, num_reqs,
+                 max_query_len, causal, &p.spec, ws + p.single_bytes, p.multi_bytes);
+    if (st != PKV_OK) return st;
+    a3.num_q_heads = num_q_heads;
+    a3.group = num_q_heads / cache->num_kv_heads;
+    a3.sub_groups = 1;
+    a3.heads_per_item = a3.group;
+    a3.qt = p.spec_qt;
+    a3.num_tokens = num_tokens;
+    st = run_split(a3, p.spec, cache->dtype, stream);
+    if (st != PKV_OK) return st;
+    st = run_combine(a3, q_dtype, stream);
+    if (st != PKV_OK) return st;
+  } else if (max_query_len > 1 && p.prefill) {
     if (!out || !q || !block_table || !seq_lens) return PKV_ERR_NULL;
     if (bt_stride <= 0 || max_seq_len < 0 || sliding_window < 0) return PKV_ERR_SHAPE;
     if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return PKV_ERR_SHAPE;

@@ -42,6 +42,8 @@ struct DecodeArgs {
   //   Tokens of single-query requests are skipped when skip_single is set.
   // 2 (chunked requests): row r is request r; only requests with exactly one
   //   query are processed (their query token is qsl[r]).
+  // 3 (chunked multi-token requests): row r is request r with 2 .. qt query
+  //   tokens qsl[r] ..; one work item holds all of them for its heads.
   int32_t row_mode;
   int32_t causal;
   int32_t skip_single;
@@ -79,6 +81,7 @@ struct DecodeArgs {
   int32_t lead_workers;     // balanced partition: workers with a full share (0: all)
   int32_t trail_pct;        // share of the other workers, percent of a full share
   int32_t lds_budget;       // bytes of LDS one worker may take
+  int32_t qt;               // row mode 3: query tokens one item holds (else 1)
 };
 
 // What one row attends to.
@@ -90,6 +93,7 @@ struct RowInfo {
   int lo, hi;     // inclusive visible key positions
   int first_blk;  // lo / block_size
   int nvis;       // visible logical blocks
+  int ntok;       // query tokens of the row (row mode 3; else 1)
 };
 
 __device__ __forceinline__ RowInfo row_info(const DecodeArgs& a, int row) {
@@ -99,7 +103,27 @@ __device__ __forceinline__ RowInfo row_info(const DecodeArgs& a, int row) {
   r.req = row;
   r.tok = row;
   r.nvis = 0;
+  r.ntok = 1;
   int L, p;
+  if (a.row_mode == 3) {
+    // keys of the request's query tokens together: from the first token's
+    // window start to the last token (non-causal: to seq_len - 1, the same)
+    const int t0 = a.qsl[row];
+    const int ql = a.qsl[row + 1] - t0;
+    if (ql < 2 || t0 < 0 || t0 + ql > a.num_tokens) { r.skip = true; return r; }
+    r.tok = t0;
+    r.ntok = ql;
+    L = a.seq_lens[row];
+    if (L <= 0 || L > a.max_seq_len || ql > L || ql > a.max_query_len || ql > a.qt) return r;
+    r.hi = L - 1;
+    r.lo = a.window > 0 ? max(0, L - ql - a.window + 1) : 0;
+    r.first_blk = r.lo >> a.bs_log2;
+    const int last3 = r.hi >> a.bs_log2;
+    if (last3 >= a.bt_stride) return r;
+    r.nvis = last3 - r.first_blk + 1;
+    r.valid = true;
+    return r;
+  }
   if (a.row_mode == 0) {
     L = a.seq_lens[row];
     p = L - 1;
@@ -899,11 +923,16 @@ __device__ inline Shares make_shares(long long U, int W, int lead, int pct, int 
   return s;
 }
 
-template <int D, int GT, int KV, int DEPTH>
+template <int D, int GT, int KV, int DEPTH, int QT = 1>
 __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
   using S = MfmaShape<D, GT, KV>;
   constexpr int NC = S::NC, VLPR = S::VLPR, VRPW = S::VRPW, VU = S::VU, VEPL = S::VEPL;
-  constexpr int KB = S::KB, RG = S::RG, kElt = S::kElt, QE = S::QE, QL = S::QL;
+  constexpr int KB = S::KB, RG = S::RG, kElt = S::kElt;
+  // MFMA rows of an item: (query token t, head h) as row t * GT + h
+  constexpr int RI = GT * QT;
+  constexpr int QE = RI * D;                                   // query elements of one piece
+  constexpr int QL = (QE + 8 * kWave - 1) / (8 * kWave);       // 16-byte loads per lane
+  static_assert(RI <= 16, "at most 16 MFMA rows per item");
   static_assert(DEPTH >= 1 && DEPTH <= 4, "prefetch depth");
   // Row-broadcast scheme, when one V token row fits in a 16-lane row: the
   // scores come out transposed (S^T = K Q^T, same registers with the MFMA
@@ -913,8 +942,9 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
   // Otherwise (a token spans two rows) probabilities move by LDS permute.
   constexpr bool RB = VLPR <= 16;
   constexpr int TPRV = RB ? 16 / VLPR : 1;          // V tokens per 16-lane row and load
+  static_assert(QT == 1 || RB, "multi-token items need the row-broadcast scheme");
   extern __shared__ __align__(16) char lds[];
-  const FlatLds L = flat_lds_layout(a.num_rows, GT, D, a.lds_budget);
+  const FlatLds L = flat_lds_layout(a.num_rows, RI, D, a.lds_budget);
   int* cum = reinterpret_cast<int*>(lds + L.cum_off);     // cum[r]: visible blocks of rows < r
   int4* rrec = reinterpret_cast<int4*>(lds + L.rec_off);  // {req, tok, lo, hi}
   uint16_t* qst = reinterpret_cast<uint16_t*>(lds + L.q_off);
@@ -963,10 +993,11 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
 
   // running piece
   int cur = -1, s_lo = 0, s_hi = -1, s_tok = 0, s_ord = 0;
+  int s_ql = 1, s_flo = 0, s_fhi = -1;   // query tokens; keys every row of the piece sees
   long long s_first = 0;
   bool s_bad = false;
   bf16x8_t qa[NC];
-  float acc[GT][VEPL];
+  float acc[RI][VEPL];
   float m[GT];
   f32x4_t lsum = {0.f, 0.f, 0.f, 0.f};
   float m1 = -INFINITY, ls1 = 0.f;   // row-broadcast scheme: head lane % 16's max and sum
@@ -985,17 +1016,18 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       uint4 t = make_uint4(0, 0, 0, 0);
-      if (row < GT) t = *reinterpret_cast<const uint4*>(src + 32 * c);
+      if (row < RI) t = *reinterpret_cast<const uint4*>(src + 32 * c);
       qa[c] = __builtin_bit_cast(bf16x8_t, t);
     }
   };
   auto q_from_global = [&](int64_t qe) __attribute__((always_inline)) {
     const int row = lane % 16;
-    const uint16_t* src = reinterpret_cast<const uint16_t*>(a.q) + qe + row * D + 8 * (lane / 16);
+    const int64_t roff = (int64_t)(row / GT) * a.num_q_heads * D + (row % GT) * D;
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(a.q) + qe + roff + 8 * (lane / 16);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       uint4 t = make_uint4(0, 0, 0, 0);
-      if (row < GT) t = *reinterpret_cast<const uint4*>(src + 32 * c);
+      if (row < RI && row / GT < s_ql) t = *reinterpret_cast<const uint4*>(src + 32 * c);
       qa[c] = __builtin_bit_cast(bf16x8_t, t);
     }
     // settle here, so that no wait for these loads lands inside the loop
@@ -1013,12 +1045,22 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
     s_hi = __builtin_amdgcn_readlane(rec_hi, unit);
     s_tok = __builtin_amdgcn_readlane(rec_tok, unit);
     s_bad = false;
+    s_flo = s_lo;
+    s_fhi = s_hi;
+    if constexpr (QT > 1) {
+      // token t sits at s_hi - (ql - 1 - t); the first token sees the fewest
+      // keys (causal), the last the latest window start
+      const int b = gid / kvgroups;
+      s_ql = a.qsl[b + 1] - a.qsl[b];
+      if (a.causal) s_fhi = s_hi - (s_ql - 1);
+      if (a.window > 0) s_flo = max(s_lo, s_hi - a.window + 1);
+    }
 #pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      m[h] = -INFINITY;
+    for (int h = 0; h < GT; ++h) m[h] = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < RI; ++h)
 #pragma unroll
       for (int e = 0; e < VEPL; ++e) acc[h][e] = 0.f;
-    }
     lsum[0] = lsum[1] = lsum[2] = lsum[3] = 0.f;
     m1 = -INFINITY;
     ls1 = 0.f;
@@ -1034,11 +1076,11 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
     const int npieces = (int)(sh.range_of(seg_base + nv - 1) - r0 + 1);
     if (s_bad) {
 #pragma unroll
-      for (int h = 0; h < GT; ++h) {
-        m[h] = 0.f;
+      for (int h = 0; h < GT; ++h) m[h] = 0.f;
+#pragma unroll
+      for (int h = 0; h < RI; ++h)
 #pragma unroll
         for (int e = 0; e < VEPL; ++e) acc[h][e] = __builtin_nanf("");
-      }
       lsum[0] = lsum[1] = lsum[2] = lsum[3] = __builtin_nanf("");
       m1 = 0.f;
       ls1 = __builtin_nanf("");
@@ -1047,16 +1089,16 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
 #pragma unroll
     for (int step = VLPR; step < kWave; step <<= 1)
 #pragma unroll
-      for (int h = 0; h < GT; ++h)
+      for (int h = 0; h < RI; ++h)
 #pragma unroll
         for (int e = 0; e < VEPL; ++e) acc[h][e] += shfl_xor_t(acc[h][e], step);
-    float lh[GT], mh[GT];   // each head's sum and max
+    float lh[RI], mh[RI];   // each row's sum and max
     if constexpr (RB) {
       float lt = ls1;
       lt += shfl_xor_t(lt, 16);
       lt += shfl_xor_t(lt, 32);
 #pragma unroll
-      for (int h = 0; h < GT; ++h) {
+      for (int h = 0; h < RI; ++h) {
         lh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lt), h));
         mh[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m1), h));
       }
@@ -1070,23 +1112,25 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
         mh[h] = m[h];
       }
     }
-    const int64_t out_row = ((int64_t)s_tok * a.num_q_heads + h0) * D;
     if (vg == 0) {
       if (npieces == 1) {
+        // row r = t * GT + h: query token t of the piece, head h0 + h
 #pragma unroll
-        for (int h = 0; h < GT; ++h) {
+        for (int h = 0; h < RI; ++h) {
+          if (h / GT >= s_ql) continue;
+          const int64_t out_row = ((int64_t)(s_tok + h / GT) * a.num_q_heads + h0 + h % GT) * D;
           const float inv = a.v_scale / lh[h];
           float o[VEPL];
 #pragma unroll
           for (int e = 0; e < VEPL; ++e) o[e] = acc[h][e] * inv;
-          store_out<PKV_BF16, VEPL>(a.out, out_row + h * D + vsub * VEPL, o);
+          store_out<PKV_BF16, VEPL>(a.out, out_row + vsub * VEPL, o);
         }
       } else {
         // acc rows: full 128-byte lines, streamed past the caches (the
         // combine kernel reads them once)
 #pragma unroll
-        for (int h = 0; h < GT; ++h) {
-          const int64_t pr = ((int64_t)b * a.num_q_heads + h0 + h) * a.max_splits + piece;
+        for (int h = 0; h < RI; ++h) {
+          const int64_t pr = (((int64_t)b * kvgroups + kvg) * RI + h) * a.max_splits + piece;
           float* dst = a.ws_acc + pr * D + vsub * VEPL;
 #pragma unroll
           for (int e = 0; e < VEPL; e += 4) {
@@ -1099,15 +1143,15 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
       }
     }
     if (npieces > 1) {
-      // m and l of the piece's heads side by side: one record of 2 GT floats
-      float* ml = a.ws_m + (((int64_t)b * kvgroups + kvg) * a.max_splits + piece) * (2 * GT);
-      constexpr int NV = (2 * GT + 3) / 4;
+      // m and l of the piece's rows side by side: one record of 2 RI floats
+      float* ml = a.ws_m + (((int64_t)b * kvgroups + kvg) * a.max_splits + piece) * (2 * RI);
+      constexpr int NV = (2 * RI + 3) / 4;
       if (lane < NV) {
         float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 2 * GT; ++e)
-          if (e / 4 == lane) v[e % 4] = e < GT ? mh[e] : lh[e - GT];
-        if constexpr (2 * GT >= 4) {
+        for (int e = 0; e < 2 * RI; ++e)
+          if (e / 4 == lane) v[e % 4] = e < RI ? mh[e] : lh[e - RI];
+        if constexpr (2 * RI >= 4) {
           const f32x4_t v4 = {v[0], v[1], v[2], v[3]};
           __builtin_nontemporal_store(v4, reinterpret_cast<f32x4_t*>(ml + 4 * lane));
         } else {
@@ -1175,13 +1219,19 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
           if (s0 + k < nstage) {
             const int ln = __builtin_ctzll(sm);
             sm &= sm - 1;
-            const int64_t qe = q_elem(__builtin_amdgcn_readlane(rec_gid, ln),
-                                      __builtin_amdgcn_readlane(rec_tok, ln));
+            const int gk = __builtin_amdgcn_readlane(rec_gid, ln);
+            const int64_t qe = q_elem(gk, __builtin_amdgcn_readlane(rec_tok, ln));
             const uint16_t* src = reinterpret_cast<const uint16_t*>(a.q) + qe;
+            int qlk = 1;                            // query tokens of the piece
+            if constexpr (QT > 1) qlk = a.qsl[gk / kvgroups + 1] - a.qsl[gk / kvgroups];
 #pragma unroll
             for (int i = 0; i < QL; ++i) {
+              // element e: token e / (GT D) of the piece, then its GT heads
               const int e = (i * kWave + lane) * 8;
-              qv[k][i] = e < QE ? *reinterpret_cast<const uint4*>(src + e) : make_uint4(0, 0, 0, 0);
+              const int t = e / (GT * D);
+              const int64_t off = (int64_t)t * a.num_q_heads * D + (e - t * GT * D);
+              qv[k][i] = (e < QE && t < qlk) ? *reinterpret_cast<const uint4*>(src + off)
+                                              : make_uint4(0, 0, 0, 0);
             }
           }
         }
@@ -1281,10 +1331,19 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) z[i] = sc[i] * a.scale_log2;
       if constexpr (!full) {
+        // this lane's row: token t of the piece (t >= ql: a padding row)
+        int rlo = s_lo, rhi = s_hi;
+        if constexpr (QT > 1) {
+          const int t = (lane % 16) / GT;
+          const int pt = s_hi - (s_ql - 1 - t);
+          if (a.causal) rhi = pt;
+          if (a.window > 0) rlo = max(s_lo, pt - a.window + 1);
+          if (t >= s_ql) rhi = rlo - 1;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int pos = p0 + 4 * (lane / 16) + i;
-          if (pos < s_lo || pos > s_hi) z[i] = -INFINITY;
+          if (pos < rlo || pos > rhi) z[i] = -INFINITY;
         }
       }
       const float mx = rows4_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
@@ -1293,7 +1352,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
         const float alpha = grow ? __builtin_amdgcn_exp2f(m1 - mx) : 1.0f;   // 0 when m = -inf
         if (grow) m1 = mx;
         ls1 *= alpha;
-        static_for<0, GT>([&](auto hc) __attribute__((always_inline)) {
+        static_for<0, RI>([&](auto hc) __attribute__((always_inline)) {
           constexpr int h = decltype(hc)::value;
           const float ah = row_bcast<h>(alpha);
 #pragma unroll
@@ -1314,7 +1373,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
         const int sub = (lane % 16) / VLPR;
         float vf[VEPL];
         v_floats(full_tag, p0, 4 * (lane / 16) + u * TPRV + sub, bf.v[u], vf);
-        static_for<0, GT>([&](auto hc) __attribute__((always_inline)) {
+        static_for<0, RI>([&](auto hc) __attribute__((always_inline)) {
           constexpr int h = decltype(hc)::value;
           float ph = row_bcast<h>(pv[u * TPRV]);
 #pragma unroll
@@ -1436,7 +1495,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
       }
       s_bad |= __builtin_amdgcn_readlane(rec_phys, unit) < 0;
       const int p0 = __builtin_amdgcn_readlane(rec_pos0, unit) + (st & smask) * 16;
-      if (p0 >= s_lo && p0 + 15 <= s_hi) body(std::true_type{}, p0, bf);
+      if (p0 >= s_flo && p0 + 15 <= s_fhi) body(std::true_type{}, p0, bf);
       else body(std::false_type{}, p0, bf);
     };
 
@@ -1464,7 +1523,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
     if (ri.valid && !ri.skip) continue;
     if (!ri.skip) {
       const int64_t base = (int64_t)ri.tok * a.num_q_heads * D;
-      for (int e = lane; e < a.num_q_heads * D; e += kWave)
+      for (int e = lane; e < ri.ntok * a.num_q_heads * D; e += kWave)
         reinterpret_cast<uint16_t*>(a.out)[base + e] = 0x7FC0;
     }
     for (int g = lane; g < kvgroups; g += kWave) a.ws_np[2 * ((int64_t)r * kvgroups + g)] = 0;
@@ -1476,15 +1535,15 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
 // The balanced kernel; decode_flat_kernel_2w asks the compiler to fit two
 // waves per SIMD (used for eight query heads per item, where the default
 // register allocation leaves room for only one).
-template <int D, int GT, int KV, int DEPTH>
+template <int D, int GT, int KV, int DEPTH, int QT = 1>
 __global__ __launch_bounds__(64) void decode_flat_kernel(DecodeArgs a) {
-  decode_flat_body<D, GT, KV, DEPTH>(a);
+  decode_flat_body<D, GT, KV, DEPTH, QT>(a);
 }
 
-template <int D, int GT, int KV, int DEPTH>
+template <int D, int GT, int KV, int DEPTH, int QT = 1>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_flat_kernel_2w(
     DecodeArgs a) {
-  decode_flat_body<D, GT, KV, DEPTH>(a);
+  decode_flat_body<D, GT, KV, DEPTH, QT>(a);
 }
 
 // Merge phase of the balanced scheme: one wave per (row, head group) with
@@ -1493,9 +1552,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 // head l / LPH of the group and DPL consecutive dims, so it reads one (m, l)
 // pair and one run of acc per piece and merges online, eight pieces' loads
 // in flight at a time (the first eight issued with the piece count).
-template <int D, int GT, int OT>
+template <int D, int GT, int OT, int QT = 1>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
-  constexpr int LPH = kWave / GT;                   // lanes per head
+  constexpr int RI = GT * QT;                       // rows of an item: (token, head)
+  constexpr int LPH = kWave / RI;                   // lanes per row
   constexpr int DPL = D >= LPH ? D / LPH : 1;       // dims per lane
   constexpr int U = 8;                              // pieces per round of loads
   const int lane = threadIdx.x;
@@ -1506,9 +1566,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int h = lane / LPH;
   const int d0 = (lane % LPH) * DPL;
   const bool active = d0 < D;
-  const float* ml = a.ws_m + rg * a.max_splits * (2 * GT);
-  const float* accp = a.ws_acc + (((int64_t)b * a.num_q_heads + g * GT + h) * a.max_splits) * D +
-                      (active ? d0 : 0);
+  const float* ml = a.ws_m + rg * a.max_splits * (2 * RI);
+  const float* accp = a.ws_acc + ((rg * RI + h) * a.max_splits) * D + (active ? d0 : 0);
   float mv[U], lv[U], av[U][DPL];
   // the first round of pieces is read together with the piece count (the
   // slots exist whatever the count; words past it are ignored)
@@ -1516,8 +1575,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = min(s0 + u, np - 1);            // past the end: repeat the last (skipped below)
-      mv[u] = ml[s * (2 * GT) + h];
-      lv[u] = ml[s * (2 * GT) + GT + h];
+      mv[u] = ml[s * (2 * RI) + h];
+      lv[u] = ml[s * (2 * RI) + RI + h];
 #pragma unroll
       for (int i = 0; i < DPL; ++i) av[u][i] = accp[(int64_t)s * D + i];
     }
@@ -1547,11 +1606,16 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
     }
   }
   if (!active) return;
+  // row h = t * GT + head: query token t of the row's request
+  const int t = h / GT;
+  if constexpr (QT > 1) {
+    if (t >= a.qsl[b + 1] - a.qsl[b] || tok + t >= a.num_tokens) return;
+  }
   const float inv = 1.0f / den;
   float o[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) o[i] = num[i] * inv;
-  store_out<OT, DPL>(a.out, ((int64_t)tok * a.num_q_heads + g * GT + h) * D + d0, o);
+  store_out<OT, DPL>(a.out, ((int64_t)(tok + t) * a.num_q_heads + g * GT + h % GT) * D + d0, o);
 }
 
 template <int D, int OT>
@@ -1650,26 +1714,26 @@ int run_split_dk(const DecodeArgs& a, int gt, hipStream_t s) {
   return PKV_ERR_UNSUPPORTED;
 }
 
-template <int D, int GT, int KV>
+template <int D, int GT, int KV, int QT = 1>
 void launch_stream(const DecodeArgs& a, int workers, hipStream_t s) {
-  const size_t lds = flat_lds_layout(a.num_rows, GT, D, a.lds_budget).bytes;
+  const size_t lds = flat_lds_layout(a.num_rows, GT * QT, D, a.lds_budget).bytes;
   // loads one step ahead: deeper rings measured slower here (more requests in
   // flight raise the latency of all of them, and past 256 registers only one
   // wave fits on a SIMD)
   constexpr int kDepth = 1;
   switch (a.kernel_variant) {
-    case 2: decode_flat_kernel<D, GT, KV, 1><<<workers, 64, lds, s>>>(a); break;
-    case 3: decode_flat_kernel<D, GT, KV, 2><<<workers, 64, lds, s>>>(a); break;
-    case 4: decode_flat_kernel<D, GT, KV, 3><<<workers, 64, lds, s>>>(a); break;
-    case 5: decode_flat_kernel<D, GT, KV, 4><<<workers, 64, lds, s>>>(a); break;
-    case 6: decode_flat_kernel_2w<D, GT, KV, 1><<<workers, 64, lds, s>>>(a); break;
-    case 7: decode_flat_kernel_2w<D, GT, KV, 2><<<workers, 64, lds, s>>>(a); break;
+    case 2: decode_flat_kernel<D, GT, KV, 1, QT><<<workers, 64, lds, s>>>(a); break;
+    case 3: decode_flat_kernel<D, GT, KV, 2, QT><<<workers, 64, lds, s>>>(a); break;
+    case 4: decode_flat_kernel<D, GT, KV, 3, QT><<<workers, 64, lds, s>>>(a); break;
+    case 5: decode_flat_kernel<D, GT, KV, 4, QT><<<workers, 64, lds, s>>>(a); break;
+    case 6: decode_flat_kernel_2w<D, GT, KV, 1, QT><<<workers, 64, lds, s>>>(a); break;
+    case 7: decode_flat_kernel_2w<D, GT, KV, 2, QT><<<workers, 64, lds, s>>>(a); break;
     default:
-      // up to four heads per item the plan counts on two waves per SIMD, so
+      // up to four rows per item the plan counts on two waves per SIMD, so
       // the kernel must fit in 256 registers (the fp8 build does not unless
-      // asked); eight or more heads run one wave per SIMD
-      if constexpr (GT <= 4) decode_flat_kernel_2w<D, GT, KV, kDepth><<<workers, 64, lds, s>>>(a);
-      else decode_flat_kernel<D, GT, KV, kDepth><<<workers, 64, lds, s>>>(a);
+      // asked); eight or more rows run one wave per SIMD
+      if constexpr (GT * QT <= 4) decode_flat_kernel_2w<D, GT, KV, kDepth, QT><<<workers, 64, lds, s>>>(a);
+      else decode_flat_kernel<D, GT, KV, kDepth, QT><<<workers, 64, lds, s>>>(a);
   }
 }
 
@@ -1688,11 +1752,48 @@ int run_stream_dk(const DecodeArgs& a, int workers, hipStream_t s) {
   return PKV_ERR_UNSUPPORTED;
 }
 
-template <int D, int GT>
+template <int D, int GT, int QT = 1>
 void launch_merge(const DecodeArgs& a, int ot, hipStream_t s) {
   const dim3 grid((unsigned)((long long)a.num_rows * (a.num_q_heads / GT)));
-  if (ot == PKV_F32) decode_merge_kernel<D, GT, PKV_F32><<<grid, 64, 0, s>>>(a);
-  else decode_merge_kernel<D, GT, PKV_BF16><<<grid, 64, 0, s>>>(a);
+  if (ot == PKV_F32) decode_merge_kernel<D, GT, PKV_F32, QT><<<grid, 64, 0, s>>>(a);
+  else decode_merge_kernel<D, GT, PKV_BF16, QT><<<grid, 64, 0, s>>>(a);
+}
+
+// Multi-token items (row mode 3): a.heads_per_item query heads times a.qt
+// query tokens as one item's MFMA rows.  Shapes where a V token row fits
+// in 16 lanes (bf16 up to D 128, fp8 up to D 256).
+template <int D, int KV>
+int run_multi_dk(const DecodeArgs& a, int workers, hipStream_t s) {
+  if constexpr (KV != PKV_F32 && D * (KV == PKV_BF16 ? 2 : 1) >= 64 && D * (KV == PKV_BF16 ? 2 : 1) <= 256) {
+    switch (a.heads_per_item * 100 + a.qt) {
+      case 102: launch_stream<D, 1, KV, 2>(a, workers, s); return PKV_OK;
+      case 104: launch_stream<D, 1, KV, 4>(a, workers, s); return PKV_OK;
+      case 108: launch_stream<D, 1, KV, 8>(a, workers, s); return PKV_OK;
+      case 202: launch_stream<D, 2, KV, 2>(a, workers, s); return PKV_OK;
+      case 204: launch_stream<D, 2, KV, 4>(a, workers, s); return PKV_OK;
+      case 208: launch_stream<D, 2, KV, 8>(a, workers, s); return PKV_OK;
+      case 402: launch_stream<D, 4, KV, 2>(a, workers, s); return PKV_OK;
+      case 404: launch_stream<D, 4, KV, 4>(a, workers, s); return PKV_OK;
+      case 802: launch_stream<D, 8, KV, 2>(a, workers, s); return PKV_OK;
+    }
+  }
+  return PKV_ERR_UNSUPPORTED;
+}
+
+template <int D>
+int run_merge_multi_d(const DecodeArgs& a, int ot, hipStream_t s) {
+  switch (a.heads_per_item * 100 + a.qt) {
+    case 102: launch_merge<D, 1, 2>(a, ot, s); return PKV_OK;
+    case 104: launch_merge<D, 1, 4>(a, ot, s); return PKV_OK;
+    case 108: launch_merge<D, 1, 8>(a, ot, s); return PKV_OK;
+    case 202: launch_merge<D, 2, 2>(a, ot, s); return PKV_OK;
+    case 204: launch_merge<D, 2, 4>(a, ot, s); return PKV_OK;
+    case 208: launch_merge<D, 2, 8>(a, ot, s); return PKV_OK;
+    case 402: launch_merge<D, 4, 2>(a, ot, s); return PKV_OK;
+    case 404: launch_merge<D, 4, 4>(a, ot, s); return PKV_OK;
+    case 802: launch_merge<D, 8, 2>(a, ot, s); return PKV_OK;
+  }
+  return PKV_ERR_UNSUPPORTED;
 }
 
 template <int D>
@@ -1721,6 +1822,10 @@ int run_combine_d(const DecodeArgs& a, int ot, hipStream_t s) {
   EXT template int run_stream_dk<D, KV>(const DecodeArgs&, int, hipStream_t);
 #define PKV_DECODE_COMBINE_INST(EXT, D) \
   EXT template int run_combine_d<D>(const DecodeArgs&, int, hipStream_t);
+#define PKV_DECODE_MULTI_INST(EXT, D, KV) \
+  EXT template int run_multi_dk<D, KV>(const DecodeArgs&, int, hipStream_t);
+#define PKV_DECODE_MERGE_MULTI_INST(EXT, D) \
+  EXT template int run_merge_multi_d<D>(const DecodeArgs&, int, hipStream_t);
 #define PKV_DECODE_ALL_D(EXT, D)                  \
   PKV_DECODE_SPLIT_INST(EXT, D, PKV_F32)          \
   PKV_DECODE_SPLIT_INST(EXT, D, PKV_BF16)         \
