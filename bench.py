@@ -37,6 +37,8 @@ DATA_NOTE = {
               "chunks of 512, full and sliding-window groups over shared tensors)",
     "prefix": "synthetic (seeded N(0,1)/sqrt(128) bf16; 100 requests sharing the blocks of one "
               "2000-token prompt, 1..64 private tokens each)",
+    "spec": "synthetic (seeded N(0,1)/sqrt(128) bf16; 64 requests, lengths uniform 128..2048, "
+            "4 query (draft) tokens each)",
 }
 POOLS = 3
 SPLIT_KERNEL = "decode_flat_kernel_2w"
@@ -48,9 +50,9 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--workload", default="llama8b",
-                   choices=["llama8b", "llama70b", "fp8", "hybrid", "prefix"],
+                   choices=["llama8b", "llama70b", "fp8", "hybrid", "prefix", "spec"],
                    help="llama8b (default line), llama70b (80 allocated layers), fp8, hybrid, "
-                        "prefix (shared prompt blocks)")
+                        "prefix (shared prompt blocks), spec (4 query tokens per request)")
     p.add_argument("--layers", type=int, default=80, help="llama70b: layers allocated and rotated")
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
@@ -275,6 +277,70 @@ def hybrid_layer_bytes(w, W):
     return kv + qo, write, flops
 
 
+def bench_spec(args, dev):
+    """Speculative decode: every request checks 4 draft tokens at once; one
+    step = slot mapping + cache write of the 4 tokens + chunked attention
+    (multi-token decode items).  Rotates over 3 pools like the decode line."""
+    import torch
+    import paged_kv_cache_mapping_amd as pkv
+    from paged_kv_cache_mapping_amd import workloads
+    w = workloads.spec_decode()
+    base = w.device(dev)
+    pools = rotating_pools(w, base, dev, POOLS)
+    T, R = w.num_tokens, w.num_reqs
+    nbytes = pkv.chunked_workspace_size(T, R, w.num_q_heads, base.cache, w.max_query_len, w.max_seq_len)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(base.q)
+    slots = torch.empty(T, dtype=torch.int64, device=dev)
+
+    def attend(i):
+        cache, bt = pools[i % len(pools)]
+        pkv.paged_attention_chunked(base.q, base.query_start_loc, base.seq_lens, w.max_query_len, cache, bt,
+                                    w.max_seq_len, w.scale, causal=True, out=out, workspace=ws)
+
+    def step(i):
+        cache, bt = pools[i % len(pools)]
+        pkv.slot_mapping(bt, base.query_start_loc, base.num_computed, w.block_size, w.num_blocks, out=slots)
+        pkv.cache_write(base.new_k, base.new_v, slots, cache)
+        attend(i)
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(args.steps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    ms_step = timed(step)
+    ms_attn = timed(attend)
+    kv = w.kv_read_bytes()                      # each request's keys once (all 4 queries share them)
+    qo = T * w.num_q_heads * w.head_dim * 2 * 2
+    attn_bytes = kv + qo
+    step_bytes = attn_bytes + T * w.num_kv_heads * w.head_dim * 2 * 2 * 2 + T * 8
+    gbps = attn_bytes / (ms_attn * 1e-3) / 1e9
+    res = {
+        "metric": "paged decode attention HBM GB/s (% of peak) + KV cache writes tokens/s, 1 GPU",
+        "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": DATA_NOTE["spec"],
+        "config": {"workload": w.name, "batch": R, "query_tokens": T, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": w.block_size,
+                   "pool_blocks": w.num_blocks, "rotating_pools": len(pools),
+                   "context_tokens": int(w.seq_lens.sum()), "parallelism": "none (1 GPU)"},
+        "attention": {"us": round(ms_attn * 1e3, 2), "GBps": round(gbps, 1), "kv_bytes": kv},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "chunked attention (multi-token decode items + merge)"},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def bench_hybrid(args, dev):
     """Hybrid KV groups with chunked prefill: four layers (full, SWA, full,
     SWA) over two shared tensors and two group tables; one step = per group
@@ -384,6 +450,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload == "hybrid":
         return bench_hybrid(args, dev)
+    if args.workload == "spec":
+        return bench_spec(args, dev)
     w = {"llama8b": workloads.llama8b_decode, "llama70b": workloads.llama70b_decode,
          "fp8": workloads.fp8_decode, "prefix": workloads.shared_prefix_decode}[args.workload]()
     base = w.device(dev)

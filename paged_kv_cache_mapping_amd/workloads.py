@@ -236,6 +236,35 @@ def fp8_decode(seed=4, batch=128, sigma_len=1.0):
         q_dtype="bf16", sigma=1.0, fp8_amax_scale=True)
 
 
+def spec_decode(seed=7, batch=64, q_len=4, lo=128, hi=2048, pool=16384):
+    """Speculative decode step on the Llama-3-8B shape: 64 requests with
+    contexts uniform in [lo, hi] (including this step's tokens), each
+    checking q_len draft tokens at once (q_len query tokens at positions
+    L - q_len .. L - 1, causal).  bf16, 32/8 heads, D 128, block 16."""
+    D, Hq, Hkv, bs = 128, 32, 8, 16
+    rng = np.random.default_rng(seed)
+    lengths = rng.integers(lo, hi + 1, size=batch).astype(np.int32)            # lengths
+    perm = rng.permutation(pool).astype(np.int32)                               # permutation
+    bt, used = _tables_from_pool(lengths, bs, perm)
+    ids = perm[:used]
+    shape = (pool, bs, Hkv, D)
+    sigma = 1.0 / np.sqrt(D)
+    kp, vp = nan_plane(shape, "bf16"), nan_plane(shape, "bf16")
+    _fill_history(rng, kp, ids, shape[1:], "bf16", sigma)                       # K history
+    _fill_history(rng, vp, ids, shape[1:], "bf16", sigma)                       # V history
+    T = batch * q_len
+    nk = bf16_bits(rng.standard_normal((T, Hkv, D), dtype=np.float32) * np.float32(sigma))
+    nv = bf16_bits(rng.standard_normal((T, Hkv, D), dtype=np.float32) * np.float32(sigma))
+    q = bf16_bits(rng.standard_normal((T, Hq, D), dtype=np.float32) * np.float32(sigma))   # Q
+    return Workload(
+        name="spec_decode_b%d_q%d_L%d-%d" % (batch, q_len, lo, hi), block_size=bs, num_blocks=pool,
+        num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, cache_dtype="bf16", q_dtype="bf16",
+        k_plane=kp, v_plane=vp, new_k=nk, new_v=nv, q=q, block_table=bt, seq_lens=lengths,
+        query_start_loc=(np.arange(batch + 1) * q_len).astype(np.int32),
+        num_computed=(lengths - q_len).astype(np.int32), scale=float(1.0 / np.sqrt(D)), decode=False,
+        info=dict(seed=seed, blocks_used=used, q_len=q_len))
+
+
 def shared_prefix_decode(seed=6, num_reqs=100, prompt=2000, suffix_hi=64, pool=16384, block_size=16):
     """Prefix sharing (Chinese worker-side page, § PagedAttention与Block管理:
     100 requests opening with one 2000-token system prompt): every request's
