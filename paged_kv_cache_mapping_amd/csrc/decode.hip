@@ -64,7 +64,7 @@ static size_t plan_bytes(const pkv_decode_plan& p, int rows, int hq, int d) {
 }
 
 static int make_plan(int rows, int hq, int hkv, int d, int bs, int kv_dtype, int max_seq_len,
-                     int window, int extra, bool allow_stream, pkv_decode_plan* plan) {
+                     int window, int extra, bool allow_stream, pkv_decode_plan* plan, int force_hpi = 0) {
   if (!plan) return PKV_ERR_NULL;
   if (rows < 0 || hq <= 0 || hkv <= 0 || max_seq_len < 0 || window < 0) return PKV_ERR_SHAPE;
   if (hq % hkv) return PKV_ERR_SHAPE;
@@ -73,7 +73,7 @@ static int make_plan(int rows, int hq, int hkv, int d, int bs, int kv_dtype, int
   const int group = hq / hkv;
   const int nvis = max_visible_blocks(max_seq_len, bs, window, extra);
   const long long cus = device_cu_count();
-  const int gm = heads_per_item_mfma(group);
+  const int gm = force_hpi > 0 ? force_hpi : heads_per_item_mfma(group);
   plan->kernel_variant = 0;
   if (allow_stream && mfma_eligible(kv_dtype, d, bs) && gm > 0 && rows <= kMaxStreamRows) {
     // balanced partition over resident wave slots
@@ -418,20 +418,22 @@ struct ChunkPlans {
   size_t single_bytes, multi_bytes;   // multi_bytes: the multi-query requests' region
   bool prefill;           // multi-query requests on the matrix-core prefill kernel
   int spec_qt;            // > 0: multi-query requests as multi-token decode items
+  int spec_heads;         // query heads per multi-token item
 };
 
 // Query tokens per item when the step's multi-query requests are short
-// enough to run as decode items (2 .. 8 tokens; a power of two at least
-// max_query_len, times the group at most 16 MFMA rows), else 0.
+// enough to run as decode items (2 .. 8 tokens: a power of two at least
+// max_query_len), else 0.  Items hold as many of the group's heads as fit
+// in 16 MFMA rows.
 static int multi_token_qt(const pkv_cache* c, int hq, int max_query_len, int num_reqs) {
   if (max_query_len < 2 || max_query_len > 8 || num_reqs > kMaxStreamRows) return 0;
   if (!mfma_eligible(c->dtype, c->head_dim, c->block_size)) return 0;
   if (c->head_dim != 128) return 0;
   const int g = hq / c->num_kv_heads;
-  if (g != 1 && g != 2 && g != 4 && g != 8) return 0;
+  if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16) return 0;
   int qt = 2;
   while (qt < max_query_len) qt <<= 1;
-  return g * qt <= 16 ? qt : 0;
+  return qt;
 }
 
 static int chunk_plans(int num_tokens, int num_reqs, int hq, const pkv_cache* c, int max_query_len,
@@ -447,11 +449,15 @@ static int chunk_plans(int num_tokens, int num_reqs, int hq, const pkv_cache* c,
   p.single_bytes = (p.single.workspace_bytes + 255) & ~(size_t)255;
   p.spec_qt = multi_token_qt(c, hq, max_query_len, num_reqs);
   if (p.spec_qt > 0) {
-    // one item per (request, KV head): the group's heads times the tokens
+    // one item per (request, head sub-group): its heads times the tokens
     const int g = hq / c->num_kv_heads;
+    // the whole group where it fits in 16 rows (measured fastest: items of
+    // 16 rows beat 8 and 4 on 64 x 4-token requests, 144 vs 149 vs 201 us)
+    p.spec_heads = g;
+    while (p.spec_heads * p.spec_qt > 16) p.spec_heads >>= 1;
     st = make_plan(num_reqs, hq * p.spec_qt, c->num_kv_heads, c->head_dim, c->block_size, c->dtype,
-                   max_seq_len, window, max_query_len - 1, true, &p.spec);
-    if (st != PKV_OK || p.spec.scheme != 1 || p.spec.heads_per_item != g * p.spec_qt) p.spec_qt = 0;
+                   max_seq_len, window, max_query_len - 1, true, &p.spec, p.spec_heads * p.spec_qt);
+    if (st != PKV_OK || p.spec.scheme != 1) p.spec_qt = 0;
   }
   p.prefill = p.spec_qt == 0 && prefill_supported(c->dtype, c->head_dim, hq / c->num_kv_heads,
                                                   max_seq_len, c->block_size, window, max_query_len);
@@ -524,8 +530,8 @@ extern "C" int pkv_paged_attention_chunked(void* out, const void* q, int32_t q_d
     if (st != PKV_OK) return st;
     a3.num_q_heads = num_q_heads;
     a3.group = num_q_heads / cache->num_kv_heads;
-    a3.sub_groups = 1;
-    a3.heads_per_item = a3.group;
+    a3.sub_groups = a3.group / p.spec_heads;
+    a3.heads_per_item = p.spec_heads;
     a3.qt = p.spec_qt;
     a3.num_tokens = num_tokens;
     st = run_split(a3, p.spec, cache->dtype, stream);

@@ -21,8 +21,9 @@ def _gpu():
     gpu_or_skip()
 
 
-# (Hq, Hkv, max query tokens): items of 8 or 16 MFMA rows, groups 1 .. 8
-SHAPES = [(32, 8, 2), (32, 8, 4), (64, 8, 2), (8, 4, 8), (16, 8, 8), (8, 8, 8), (32, 8, 3)]
+# (Hq, Hkv, max query tokens): items of 8 or 16 MFMA rows, groups 1 .. 16
+SHAPES = [(32, 8, 2), (32, 8, 4), (64, 8, 2), (8, 4, 8), (16, 8, 8), (8, 8, 8), (32, 8, 3),
+          (64, 4, 4), (64, 8, 8)]   # last two: groups split into items of 4 and 2 heads
 
 
 @pytest.mark.parametrize("Hq,Hkv,qmax", SHAPES)
