@@ -22,6 +22,7 @@ Modules:
 
 * :mod:`oracle.paging`    -- slot mapping, cache write, gather by block table.
 * :mod:`oracle.e4m3`      -- the OCP FP8 E4M3 ("FN") codec.
+* :mod:`oracle.int4`      -- the 4-bit integer codec (zero point 8, packed).
 * :mod:`oracle.bf16`      -- bf16 <-> float conversions from the bit layout.
 * :mod:`oracle.attention` -- softmax attention over a paged cache (fp64).
 * :mod:`oracle.sizing`    -- KV bytes-per-token and pool-size closed forms.
@@ -32,4 +33,4 @@ values the pages print, closed forms, library special cases or brute force.
 No function is "parity unpinned".
 """
 
-from . import bf16, e4m3, paging, attention, sizing, layout  # noqa: F401
+from . import bf16, e4m3, int4, paging, attention, sizing, layout  # noqa: F401

@@ -11,7 +11,7 @@ and, for query head h, uses KV head h // G where G = Hq / Hkv (grouped-query
 attention: consecutive query heads share one KV head).
     z_j = scale * <q_h, k_j>,   out = sum_j softmax(z)_j v_j.
 K and V are gathered in logical order by following the request's block table
-row; fp8 caches are dequantised exactly (code value times the per-tensor
+row; fp8 and int4 caches are dequantised exactly (code value times the per-tensor
 scale), bf16 widened exactly.
 
 Sources: attention reads past K/V through the block table, never assuming one

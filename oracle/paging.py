@@ -32,6 +32,7 @@ import numpy as np
 
 from . import bf16 as _bf16
 from . import e4m3 as _e4m3
+from . import int4 as _int4
 
 
 def num_logical_blocks(num_tokens, block_size):
@@ -88,9 +89,10 @@ def convert_for_cache(x, src_dtype, cache_dtype, scale=1.0):
     """Source elements -> the cache's storage bits.
 
     src_dtype: 'f32' (float32 values) or 'bf16' (uint16 bit patterns).
-    cache_dtype: 'f32', 'bf16' or 'fp8' (uint8 E4M3 codes).
+    cache_dtype: 'f32', 'bf16', 'fp8' (uint8 E4M3 codes) or 'int4' (rows of
+    D / 2 bytes, two 4-bit codes each).
     Same type: a bit copy.  f32 -> bf16: round to nearest even.
-    -> fp8: quantise the float32 value with the per-tensor scale.
+    -> fp8 / int4: quantise the float32 value with the per-tensor scale.
     """
     x = np.asarray(x)
     if src_dtype == "bf16":
@@ -105,6 +107,8 @@ def convert_for_cache(x, src_dtype, cache_dtype, scale=1.0):
         return _bf16.from_f32(as_f32)
     if cache_dtype == "fp8":
         return _e4m3.quantize(as_f32, scale)
+    if cache_dtype == "int4":
+        return _int4.quantize_packed(as_f32, scale)
     raise ValueError((src_dtype, cache_dtype))
 
 
@@ -133,7 +137,8 @@ def cache_write(k_plane, v_plane, key, value, slots, src_dtype, cache_dtype,
 
 
 def plane_to_f64(plane, cache_dtype, scale=1.0):
-    """Storage bits -> float64 values (fp8 codes are dequantised)."""
+    """Storage bits -> float64 values (fp8 and int4 codes are dequantised;
+    an int4 row of D / 2 bytes becomes D values)."""
     if cache_dtype == "bf16":
         return _bf16.to_f64(plane)
     if cache_dtype == "f32":
@@ -142,6 +147,8 @@ def plane_to_f64(plane, cache_dtype, scale=1.0):
         return np.asarray(plane, dtype=np.float64)
     if cache_dtype == "fp8":
         return _e4m3.dequantize(plane, scale)
+    if cache_dtype == "int4":
+        return _int4.dequantize(plane, scale)
     raise ValueError(cache_dtype)
 
 

@@ -3,7 +3,8 @@
 Per-token KV bytes = layers * KV heads * head_dim * 2 (K and V) * element
 bytes (Worker-Side KV Init (zh), § KV Cache技术背景, the LLaMA-70B worked
 example: 80 layers, 8 KV heads, head_dim 128, FP16).  An FP8 cache stores one
-byte per element and halves it (same section, next paragraph).
+byte per element and halves it; an INT4 cache stores half a byte and quarters
+it (same section, next paragraph).
 
 The page prints about 640 KB for that product; its factors give
 80*8*128*2*2 = 327,680 bytes.  The factors are taken as authoritative; the
@@ -18,16 +19,19 @@ Pre-allocation Logic): budget = total * utilisation; available = budget -
 non-KV bytes; blocks = floor(available / (bytes per block per layer * layers)).
 """
 
-ELEMENT_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1}
+ELEMENT_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1, "int4": 0.5}
+ELEMENT_BITS = {"f32": 32, "bf16": 16, "f16": 16, "fp8": 8, "int4": 4}
 
 
 def kv_bytes_per_token(num_layers, num_kv_heads, head_dim, dtype):
-    return int(num_layers) * int(num_kv_heads) * int(head_dim) * 2 * ELEMENT_BYTES[dtype]
+    bits = int(num_layers) * int(num_kv_heads) * int(head_dim) * 2 * ELEMENT_BITS[dtype]
+    return bits // 8
 
 
 def block_bytes(block_size, num_kv_heads, head_dim, dtype):
     """K+V bytes of one block of one layer."""
-    return int(block_size) * int(num_kv_heads) * int(head_dim) * 2 * ELEMENT_BYTES[dtype]
+    bits = int(block_size) * int(num_kv_heads) * int(head_dim) * 2 * ELEMENT_BITS[dtype]
+    return bits // 8
 
 
 def pool_bytes(num_blocks, num_layers, block_size, num_kv_heads, head_dim, dtype):
