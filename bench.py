@@ -39,6 +39,8 @@ DATA_NOTE = {
               "2000-token prompt, 1..64 private tokens each)",
     "spec": "synthetic (seeded N(0,1)/sqrt(128) bf16; 64 requests, lengths uniform 128..2048, "
             "4 query (draft) tokens each)",
+    "int4": "synthetic (seeded INT4 K/V codes round(2 N(0,1)) in [-8, 7] with scales 0.5/sqrt(128), "
+            "N(0,1)/sqrt(128) bf16 Q and new K/V; lengths uniform 128..2048)",
 }
 POOLS = 3
 SPLIT_KERNEL = "decode_flat_kernel_2w"
@@ -50,7 +52,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--workload", default="llama8b",
-                   choices=["llama8b", "llama70b", "fp8", "hybrid", "prefix", "spec"],
+                   choices=["llama8b", "llama70b", "fp8", "hybrid", "prefix", "spec", "int4"],
                    help="llama8b (default line), llama70b (80 allocated layers), fp8, hybrid, "
                         "prefix (shared prompt blocks), spec (4 query tokens per request)")
     p.add_argument("--layers", type=int, default=80, help="llama70b: layers allocated and rotated")
@@ -99,7 +101,9 @@ def algorithmic_bytes(w):
     split = kv + q + nblk * 4 + B * 4
     combine = out
     slot = B * (4 * 3 + 4 + 8)            # qsl, computed, table entry, slot out
-    write = B * Hkv * D * 2 * 2 * 2 + B * 8  # read + write K and V rows, slots
+    elt = {"f32": 4, "bf16": 2, "fp8": 1, "int4": 0.5}[w.cache_dtype]
+    src = 4 if w.q_dtype == "f32" else 2
+    write = int(B * Hkv * D * 2 * (src + elt)) + B * 8  # read + write K and V rows, slots
     return dict(kv=kv, split=split, combine=combine, slot=slot, write=write,
                 step=split + combine + slot + write)
 
@@ -217,7 +221,8 @@ def rotating_pools(w, base, dev, count):
         k2.index_copy_(0, pt, base.cache.k)
         v2.index_copy_(0, pt, base.cache.v)
         bt = np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)], -1).astype(np.int32)
-        pools.append((pkv.CacheView.from_planes(k2, v2, base.cache.k_scale, base.cache.v_scale),
+        pools.append((pkv.CacheView.from_planes(k2, v2, base.cache.k_scale, base.cache.v_scale,
+                                                int4=base.cache.int4),
                       torch.from_numpy(bt).to(dev)))
     return pools
 
@@ -453,7 +458,8 @@ def main():
     if args.workload == "spec":
         return bench_spec(args, dev)
     w = {"llama8b": workloads.llama8b_decode, "llama70b": workloads.llama70b_decode,
-         "fp8": workloads.fp8_decode, "prefix": workloads.shared_prefix_decode}[args.workload]()
+         "fp8": workloads.fp8_decode, "prefix": workloads.shared_prefix_decode,
+         "int4": workloads.int4_decode}[args.workload]()
     base = w.device(dev)
     nb = w.num_blocks
     extra = {}
@@ -599,7 +605,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.cache_dtype == "bf16" else "e4m3 KV, bf16 q/out",
+        "dtype": {"bf16": "bf16", "fp8": "e4m3 KV, bf16 q/out", "int4": "int4 KV, bf16 q/out"}[w.cache_dtype],
         "data": DATA_NOTE[args.workload],
         "config": {"workload": w.name, "batch": w.num_reqs, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,

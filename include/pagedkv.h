@@ -63,7 +63,8 @@ typedef enum {
 typedef enum {
   PKV_F32 = 0,       /* IEEE binary32                                        */
   PKV_BF16 = 1,      /* bfloat16                                             */
-  PKV_FP8_E4M3 = 2   /* OCP FP8 E4M3 ("FN"): bias 7, max 448, NaN = 0x7F/0xFF */
+  PKV_FP8_E4M3 = 2,  /* OCP FP8 E4M3 ("FN"): bias 7, max 448, NaN = 0x7F/0xFF */
+  PKV_INT4 = 3       /* 4-bit integer, zero point 8, two per byte (see pkv_cache) */
 } pkv_dtype;
 
 /*
@@ -86,7 +87,16 @@ typedef enum {
  * dtype PKV_FP8_E4M3: stored code c means value decode(c) * k_scale (or
  * v_scale); a write quantises x as encode(float(x) * (1.0f / scale)) with
  * round-to-nearest-even and saturation to +-448 [W-zh § KV Cache技术背景:
- * one byte per element halves the cache].  Scales are ignored otherwise.
+ * one byte per element halves the cache].
+ *
+ * dtype PKV_INT4 [W-zh § KV Cache技术背景: half a byte per element, scales
+ * fixed offline from calibration data; § 第一步：物理分配: the byte buffer
+ * is viewed per precision]: element 2j of a row is the low nibble of byte j,
+ * element 2j + 1 the high nibble; nibble u means value (u - 8) * k_scale (or
+ * v_scale).  A write stores u = clamp(rint(float(x) * (1.0f / scale)), -8, 7)
+ * + 8, rint rounding half to even; NaN stores u = 8.  block_stride counts
+ * elements (two per byte) and must be even; head_dim must be a multiple of
+ * 32.  Scales are ignored for the other dtypes.
  */
 typedef struct {
   void* k;
@@ -95,7 +105,7 @@ typedef struct {
   int32_t num_blocks;
   int32_t block_size;    /* 4, 8, 16 or 32 tokens [W § PagedAttention and Block Management] */
   int32_t num_kv_heads;
-  int32_t head_dim;      /* 8, 16, 32, 64, 128 or 256 */
+  int32_t head_dim;      /* 8, 16, 32, 64, 128 or 256 (PKV_INT4: 32 .. 256) */
   int32_t dtype;         /* pkv_dtype */
   float k_scale;
   float v_scale;
@@ -168,8 +178,8 @@ PKV_API int pkv_slot_mapping(const int32_t* block_table, int32_t bt_stride,
  *                  block s / block_size; s < 0 is skipped; s >= num_blocks *
  *                  block_size is skipped too (never written out of range).
  * cache            destination planes.  Same dtype as the source: bit copy.
- *                  F32 -> BF16: round to nearest even.  -> FP8_E4M3: quantise
- *                  with the cache's k_scale / v_scale.
+ *                  F32 -> BF16: round to nearest even.  -> FP8_E4M3 or INT4:
+ *                  quantise with the cache's k_scale / v_scale.
  * Two tokens with one slot in a call race (the pages leave it undefined).
  */
 PKV_API int pkv_cache_write(const void* key, const void* value, int32_t src_dtype,
@@ -250,8 +260,11 @@ PKV_API int pkv_decode_plan_make(int32_t num_rows, int32_t num_q_heads,
  * Attention Mechanisms (GQA, sliding window)].
  *
  * out, q           [num_seqs, num_q_heads, head_dim], dtype q_dtype.  q_dtype
- *                  is PKV_F32 for an F32 cache and PKV_BF16 for BF16 / FP8
- *                  caches; out has q's dtype.
+ *                  is PKV_F32 for an F32 cache and PKV_BF16 for BF16 / FP8 /
+ *                  INT4 caches; out has q's dtype.
+ * INT4 caches take head_dim 128, block sizes 16 and 32, groups 1, 2, 4, 8
+ * or multiples of 16, and at most 4096 rows; other shapes return
+ * PKV_ERR_UNSUPPORTED.
  * block_table      [num_seqs, bt_stride] int32 physical ids.
  * seq_lens         [num_seqs] int32 in [1, max_seq_len]: tokens of the
  *                  sequence including this step's (already written) token.
@@ -343,6 +356,8 @@ PKV_API int pkv_chunked_workspace_size(int32_t num_tokens, int32_t num_reqs,
  * sliding_window   0, or W: keys >= p - W + 1 only.
  * workspace        at least pkv_chunked_workspace_size(...) bytes.
  * Invalid rows (q_len > seq_len, lengths out of range, missing blocks) get NaN.
+ * INT4 caches: the decode form's shapes, and steps whose requests have at
+ * most 8 query tokens; a longer request returns PKV_ERR_UNSUPPORTED.
  */
 PKV_API int pkv_paged_attention_chunked(void* out, const void* q, int32_t q_dtype,
                                 int32_t num_tokens, int32_t num_q_heads,
@@ -371,6 +386,21 @@ PKV_API int pkv_fp8_e4m3_quantize(const void* x, int32_t src_dtype, int64_t n,
                           float scale, uint8_t* codes, hipStream_t stream);
 PKV_API int pkv_fp8_e4m3_dequantize(const uint8_t* codes, int64_t n, float scale,
                             int32_t out_dtype, void* out, hipStream_t stream);
+
+/*
+ * INT4 bulk codec with the conversions the cache write uses [W-zh § KV
+ * Cache技术背景, the INT4 format of pkv_cache].
+ *   quantize:   packed[j] = u(2j) | u(2j + 1) << 4 with
+ *               u(i) = clamp(rint(float(x[i]) * (1.0f / scale)), -8, 7) + 8,
+ *               NaN -> 8; x of src_dtype (PKV_F32 or PKV_BF16); n elements,
+ *               n even, packed holds n / 2 bytes.
+ *   dequantize: out[i] = (u(i) - 8) * scale as float32 (out_dtype PKV_F32).
+ * Returns PKV_ERR_SHAPE for odd n or a scale that is not positive and finite.
+ */
+PKV_API int pkv_int4_quantize(const void* x, int32_t src_dtype, int64_t n, float scale,
+                      uint8_t* packed, hipStream_t stream);
+PKV_API int pkv_int4_dequantize(const uint8_t* packed, int64_t n, float scale,
+                        int32_t out_dtype, void* out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

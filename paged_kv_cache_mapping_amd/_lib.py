@@ -21,6 +21,7 @@ PKV_ERR_HIP = -6
 PKV_F32 = 0
 PKV_BF16 = 1
 PKV_FP8_E4M3 = 2
+PKV_INT4 = 3
 
 
 class PkvCache(ctypes.Structure):
@@ -83,6 +84,8 @@ SIGNATURES = {
     "pkv_copy_blocks": (_int, [ctypes.POINTER(PkvCache), _vp, _vp, _i32, _vp, _vp]),
     "pkv_fp8_e4m3_quantize": (_int, [_vp, _i32, _i64, _f32, _vp, _vp]),
     "pkv_fp8_e4m3_dequantize": (_int, [_vp, _i64, _f32, _i32, _vp, _vp]),
+    "pkv_int4_quantize": (_int, [_vp, _i32, _i64, _f32, _vp, _vp]),
+    "pkv_int4_dequantize": (_int, [_vp, _i64, _f32, _i32, _vp, _vp]),
 }
 
 _lib = None

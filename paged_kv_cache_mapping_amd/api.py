@@ -12,7 +12,7 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import PKV_BF16, PKV_F32, PKV_FP8_E4M3, PkvCache, PkvDecodePlan, check, load
+from ._lib import PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_INT4, PkvCache, PkvDecodePlan, check, load
 
 _DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16, torch.uint8: PKV_FP8_E4M3}
 if hasattr(torch, "float8_e4m3fn"):
@@ -53,6 +53,8 @@ class CacheView:
     ``block_stride`` elements after block b-1.  Typically views
     ``[num_blocks, block_size, num_kv_heads, head_dim]`` of one byte buffer.
     fp8 caches use dtype uint8 (or float8_e4m3fn) with per-tensor scales.
+    int4 caches are uint8 planes of head_dim / 2 bytes per row (two elements
+    a byte) with per-tensor scales; head_dim and block_stride count elements.
     """
     k: torch.Tensor
     v: torch.Tensor
@@ -63,20 +65,25 @@ class CacheView:
     block_stride: int
     k_scale: float = 1.0
     v_scale: float = 1.0
+    int4: bool = False
 
     @classmethod
-    def from_planes(cls, k, v, k_scale=1.0, v_scale=1.0):
-        """Planes shaped [num_blocks, block_size, num_kv_heads, head_dim]."""
+    def from_planes(cls, k, v, k_scale=1.0, v_scale=1.0, int4=False):
+        """Planes shaped [num_blocks, block_size, num_kv_heads, head_dim]
+        (int4: uint8 planes [..., head_dim / 2])."""
         _need(k.dim() == 4 and k.shape == v.shape and k.dtype == v.dtype, "k/v planes mismatch")
         _need(k.stride(3) == 1 and k.stride(2) == k.shape[3] and k.stride(1) == k.shape[2] * k.shape[3],
               "each block must be contiguous [block_size, heads, dim]")
         _need(k.stride() == v.stride(), "k and v strides differ")
         nb, bs, h, d = k.shape
+        if int4:
+            _need(k.dtype == torch.uint8, "int4 planes are uint8 bytes")
+            return cls(k, v, nb, bs, h, 2 * d, 2 * k.stride(0), float(k_scale), float(v_scale), True)
         return cls(k, v, nb, bs, h, d, k.stride(0), float(k_scale), float(v_scale))
 
     @property
     def dtype(self):
-        return _dt(self.k)
+        return PKV_INT4 if self.int4 else _dt(self.k)
 
     def c_struct(self):
         return PkvCache(k=self.k.data_ptr(), v=self.v.data_ptr(), block_stride=self.block_stride,
@@ -91,7 +98,7 @@ def status_string(status):
 
 def kv_bytes_per_token(num_layers, num_kv_heads, head_dim, dtype):
     """Closed form of the per-token KV footprint (host arithmetic in the library)."""
-    dt = {"f32": PKV_F32, "bf16": PKV_BF16, "fp8": PKV_FP8_E4M3}[dtype]
+    dt = {"f32": PKV_F32, "bf16": PKV_BF16, "fp8": PKV_FP8_E4M3, "int4": PKV_INT4}[dtype]
     return int(load().pkv_kv_bytes_per_token(num_layers, num_kv_heads, head_dim, dt))
 
 
@@ -288,6 +295,29 @@ def fp8_quantize(x, scale, out=None):
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     check("pkv_fp8_e4m3_quantize", lib.pkv_fp8_e4m3_quantize(
         _ptr(x), _dt(x), x.numel(), float(scale), _ptr(out), _stream(x.device)))
+    return out
+
+
+def int4_quantize(x, scale, out=None):
+    """x [..., n] (n even) -> packed uint8 [..., n / 2]."""
+    lib = load()
+    _need(x.is_contiguous() and x.shape[-1] % 2 == 0, "x must be contiguous with an even last dimension")
+    if out is None:
+        out = torch.empty(x.shape[:-1] + (x.shape[-1] // 2,), dtype=torch.uint8, device=x.device)
+    check("pkv_int4_quantize", lib.pkv_int4_quantize(
+        _ptr(x), _dt(x), x.numel(), float(scale), _ptr(out), _stream(x.device)))
+    return out
+
+
+def int4_dequantize(packed, scale, out=None):
+    """packed uint8 [..., m] -> float32 [..., 2 m]."""
+    lib = load()
+    _need(packed.dtype == torch.uint8 and packed.is_contiguous(), "packed must be contiguous uint8")
+    if out is None:
+        out = torch.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=torch.float32,
+                          device=packed.device)
+    check("pkv_int4_dequantize", lib.pkv_int4_dequantize(
+        _ptr(packed), 2 * packed.numel(), float(scale), PKV_F32, _ptr(out), _stream(packed.device)))
     return out
 
 

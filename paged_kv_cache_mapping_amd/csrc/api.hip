@@ -40,12 +40,13 @@ extern "C" const char* pkv_status_string(int status) {
   }
 }
 
-// Per-token KV bytes over all layers: layers * kv_heads * head_dim * 2 * elt.
+// Per-token KV bytes over all layers: layers * kv_heads * head_dim * 2 * elt
+// (elt half a byte for INT4).
 extern "C" int64_t pkv_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads,
                                           int32_t head_dim, int32_t dtype) {
-  const int elt = pkv::dtype_size(dtype);
-  if (elt == 0 || num_layers < 0 || num_kv_heads < 0 || head_dim < 0) return -1;
-  return (int64_t)num_layers * num_kv_heads * head_dim * 2 * elt;
+  const int bits = pkv::dtype_bits(dtype);
+  if (bits == 0 || num_layers < 0 || num_kv_heads < 0 || head_dim < 0) return -1;
+  return (int64_t)num_layers * num_kv_heads * head_dim * 2 * bits / 8;
 }
 
 // Blocks a memory budget holds: floor(total * utilisation) - non-KV bytes,
@@ -54,14 +55,14 @@ extern "C" int64_t pkv_num_blocks_for_budget(int64_t total_bytes, double utiliza
                                              int64_t non_kv_bytes, int32_t num_tensors,
                                              int32_t block_size, int32_t num_kv_heads,
                                              int32_t head_dim, int32_t dtype) {
-  const int elt = pkv::dtype_size(dtype);
-  if (elt == 0) return PKV_ERR_DTYPE;
+  const int bits = pkv::dtype_bits(dtype);
+  if (bits == 0) return PKV_ERR_DTYPE;
   if (total_bytes < 0 || non_kv_bytes < 0 || num_tensors <= 0 || block_size <= 0 ||
       num_kv_heads <= 0 || head_dim <= 0 || !(utilization > 0.0 && utilization <= 1.0))
     return PKV_ERR_SHAPE;
   const int64_t budget = (int64_t)((double)total_bytes * utilization);
   const int64_t available = budget - non_kv_bytes;
   if (available <= 0) return 0;
-  const int64_t per_block = (int64_t)block_size * num_kv_heads * head_dim * 2 * elt * num_tensors;
+  const int64_t per_block = (int64_t)block_size * num_kv_heads * head_dim * 2 * bits / 8 * num_tensors;
   return available / per_block;
 }

@@ -70,6 +70,23 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t packed) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// ---------------------------------------------------------------- INT4
+// 4-bit integer code with zero point 8: the integer nearest to y (ties to
+// even) limited to [-8, 7], plus 8; NaN gives 8 (value 0).
+__device__ __forceinline__ uint32_t int4_encode(float y) {
+  const float k = fminf(fmaxf(__builtin_rintf(y), -8.0f), 7.0f);
+  return y == y ? (uint32_t)((int)k + 8) : 8u;
+}
+
+// Eight codes (element n in bits 4n .. 4n + 3) packed from eight values
+// already multiplied by the inverse scale.
+__device__ __forceinline__ uint32_t int4_pack8(const float* y) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) w |= int4_encode(y[n]) << (4 * n);
+  return w;
+}
+
 // ---------------------------------------------------------------- dot products
 // a.x*b.x + a.y*b.y + c on packed bfloat16 pairs, fp32 accumulate.
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
@@ -107,6 +124,11 @@ __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b -
 
 __host__ __device__ __forceinline__ int dtype_bytes(int dt) {
   return dt == PKV_F32 ? 4 : (dt == PKV_BF16 ? 2 : 1);
+}
+
+// Bits per element of a cache type (compile-time use in the kernels).
+__host__ __device__ constexpr int kv_bits(int dt) {
+  return dt == PKV_F32 ? 32 : (dt == PKV_BF16 ? 16 : (dt == PKV_FP8_E4M3 ? 8 : 4));
 }
 
 }  // namespace pkv

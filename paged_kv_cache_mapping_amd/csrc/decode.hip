@@ -31,16 +31,23 @@ static int heads_per_item_valu(int group) {
   return (group == 1 || group == 2 || group == 4) ? group : 0;
 }
 
+// MFMA rows one matrix-core work item may hold: 16 for bf16; 8 for fp8 and
+// int4, whose lanes accumulate 16 elements per row (16 rows would need 256
+// accumulator registers and spill).
+static int max_item_rows(int kv_dtype) { return kv_dtype == PKV_BF16 ? 16 : 8; }
+
 // Query heads one matrix-core work item handles (MFMA rows).
-static int heads_per_item_mfma(int group) {
-  if (group >= 16) return (group % 16 == 0) ? 16 : 0;
+static int heads_per_item_mfma(int group, int kv_dtype) {
+  const int cap = max_item_rows(kv_dtype);
+  if (group >= cap) return (group % cap == 0) ? cap : 0;
   return (group == 1 || group == 2 || group == 4 || group == 8) ? group : 0;
 }
 
 static bool mfma_eligible(int kv_dtype, int d, int bs) {
+  if (bs % 16 != 0) return false;
+  if (kv_dtype == PKV_INT4) return d == 128;   // the one INT4 head size built
   const int elt = dtype_size(kv_dtype);
-  return (kv_dtype == PKV_BF16 || kv_dtype == PKV_FP8_E4M3) && d % 32 == 0 && d * elt >= 64 &&
-         bs % 16 == 0;
+  return (kv_dtype == PKV_BF16 || kv_dtype == PKV_FP8_E4M3) && d % 32 == 0 && d * elt >= 64;
 }
 
 constexpr int kMaxStreamRows = 4096;   // prefix sums of the balanced scheme live in LDS
@@ -68,12 +75,12 @@ static int make_plan(int rows, int hq, int hkv, int d, int bs, int kv_dtype, int
   if (!plan) return PKV_ERR_NULL;
   if (rows < 0 || hq <= 0 || hkv <= 0 || max_seq_len < 0 || window < 0) return PKV_ERR_SHAPE;
   if (hq % hkv) return PKV_ERR_SHAPE;
-  if (dtype_size(kv_dtype) == 0) return PKV_ERR_DTYPE;
+  if (dtype_bits(kv_dtype) == 0) return PKV_ERR_DTYPE;
   if (!head_dim_supported(d) || !block_size_supported(bs)) return PKV_ERR_UNSUPPORTED;
   const int group = hq / hkv;
   const int nvis = max_visible_blocks(max_seq_len, bs, window, extra);
   const long long cus = device_cu_count();
-  const int gm = force_hpi > 0 ? force_hpi : heads_per_item_mfma(group);
+  const int gm = force_hpi > 0 ? force_hpi : heads_per_item_mfma(group, kv_dtype);
   plan->kernel_variant = 0;
   if (allow_stream && mfma_eligible(kv_dtype, d, bs) && gm > 0 && rows <= kMaxStreamRows) {
     // balanced partition over resident wave slots
@@ -98,6 +105,7 @@ static int make_plan(int rows, int hq, int hkv, int d, int bs, int kv_dtype, int
   } else {
     const int gt = heads_per_item_valu(group);
     if (gt == 0) return PKV_ERR_UNSUPPORTED;
+    if (kv_dtype == PKV_INT4) return PKV_ERR_UNSUPPORTED;   // matrix-core path only
     // fixed splits: about 16 single-wave work items per compute unit if
     // every row were as long as the longest; powers of two in [1, 64]
     const long long items1 = (long long)(rows > 0 ? rows : 1) * (hq / gt) * nvis;
@@ -127,7 +135,7 @@ static int check_plan(const pkv_decode_plan* plan, int rows, int hq, int hkv, in
     // any of 1, 2, 4, 8, 16 that divides the group (items of a KV head then
     // share its blocks); the planner picks the largest
     const int hpi = plan->heads_per_item;
-    if (hpi <= 0 || hpi > 16 || (hpi & (hpi - 1)) || group % hpi) return PKV_ERR_SHAPE;
+    if (hpi <= 0 || hpi > max_item_rows(kv_dtype) || (hpi & (hpi - 1)) || group % hpi) return PKV_ERR_SHAPE;
     if (plan->split_blocks < 1 || plan->num_workers < 1) return PKV_ERR_SHAPE;
     if (plan->lead_workers < 0 || plan->lead_workers > plan->num_workers) return PKV_ERR_SHAPE;
     if (plan->trail_share_pct < 1 || plan->trail_share_pct > 100) return PKV_ERR_SHAPE;
@@ -135,6 +143,7 @@ static int check_plan(const pkv_decode_plan* plan, int rows, int hq, int hkv, in
     return PKV_OK;
   }
   if (plan->scheme != 0) return PKV_ERR_SHAPE;
+  if (kv_dtype == PKV_INT4) return PKV_ERR_UNSUPPORTED;
   if (plan->split_blocks < 1 || plan->split_blocks > 64) return PKV_ERR_SHAPE;
   const int gt = heads_per_item_valu(group);
   if (gt == 0) return PKV_ERR_UNSUPPORTED;
@@ -150,15 +159,18 @@ PKV_DECODE_ALL_D(extern, 32)
 PKV_DECODE_ALL_D(extern, 64)
 PKV_DECODE_ALL_D(extern, 128)
 PKV_DECODE_ALL_D(extern, 256)
+PKV_DECODE_STREAM_INST(extern, 128, PKV_INT4)
 PKV_DECODE_MULTI_INST(extern, 128, PKV_BF16)
 PKV_DECODE_MULTI_INST(extern, 128, PKV_FP8_E4M3)
+PKV_DECODE_MULTI_INST(extern, 128, PKV_INT4)
 PKV_DECODE_MERGE_MULTI_INST(extern, 128)
 
 template <int D>
 static int split_d(const DecodeArgs& a, int gt, int kv, hipStream_t s) {
   if (kv == PKV_F32) return run_split_dk<D, PKV_F32>(a, gt, s);
   if (kv == PKV_BF16) return run_split_dk<D, PKV_BF16>(a, gt, s);
-  return run_split_dk<D, PKV_FP8_E4M3>(a, gt, s);
+  if (kv == PKV_FP8_E4M3) return run_split_dk<D, PKV_FP8_E4M3>(a, gt, s);
+  return PKV_ERR_UNSUPPORTED;
 }
 
 static int dispatch_split(const DecodeArgs& a, int gt, int kv, hipStream_t s) {
@@ -177,6 +189,9 @@ template <int D>
 static int stream_d(const DecodeArgs& a, int kv, int workers, hipStream_t s) {
   if (kv == PKV_BF16) return run_stream_dk<D, PKV_BF16>(a, workers, s);
   if (kv == PKV_FP8_E4M3) return run_stream_dk<D, PKV_FP8_E4M3>(a, workers, s);
+  if constexpr (D == 128) {
+    if (kv == PKV_INT4) return run_stream_dk<128, PKV_INT4>(a, workers, s);
+  }
   return PKV_ERR_UNSUPPORTED;
 }
 
@@ -185,6 +200,7 @@ static int dispatch_multi(const DecodeArgs& a, int kv, int workers, hipStream_t 
   if (a.head_dim != 128) return PKV_ERR_UNSUPPORTED;
   if (kv == PKV_BF16) return run_multi_dk<128, PKV_BF16>(a, workers, s);
   if (kv == PKV_FP8_E4M3) return run_multi_dk<128, PKV_FP8_E4M3>(a, workers, s);
+  if (kv == PKV_INT4) return run_multi_dk<128, PKV_INT4>(a, workers, s);
   return PKV_ERR_UNSUPPORTED;
 }
 
@@ -297,8 +313,9 @@ static int prepare(DecodeArgs& a, void* out, const void* q, int q_dtype, int row
     if (budget > 64 * 1024) budget = 64 * 1024;
     a.lds_budget = (int32_t)(budget & ~15LL);
   }
-  a.scale_log2 = scale * log2e * (cache->dtype == PKV_FP8_E4M3 ? cache->k_scale : 1.0f);
-  a.v_scale = cache->dtype == PKV_FP8_E4M3 ? cache->v_scale : 1.0f;
+  const bool scaled = cache->dtype == PKV_FP8_E4M3 || cache->dtype == PKV_INT4;
+  a.scale_log2 = scale * log2e * (scaled ? cache->k_scale : 1.0f);
+  a.v_scale = scaled ? cache->v_scale : 1.0f;
   bind_workspace(a, ws, rows, hq, cache->head_dim, plan->max_splits, plan->heads_per_item);
   return PKV_OK;
 }
@@ -445,22 +462,27 @@ static int chunk_plans(int num_tokens, int num_reqs, int hq, const pkv_cache* c,
   const int extra = max_query_len > 0 ? max_query_len - 1 : 0;
   st = make_plan(num_tokens, hq, c->num_kv_heads, c->head_dim, c->block_size, c->dtype,
                  max_seq_len, window, extra, false, &p.multi);
-  if (st != PKV_OK) return st;
+  // INT4 has no vector-ALU fallback: its multi-query requests need the
+  // multi-token items (checked below)
+  const bool multi_ok = st == PKV_OK;
+  if (!multi_ok && !(st == PKV_ERR_UNSUPPORTED && c->dtype == PKV_INT4)) return st;
   p.single_bytes = (p.single.workspace_bytes + 255) & ~(size_t)255;
   p.spec_qt = multi_token_qt(c, hq, max_query_len, num_reqs);
   if (p.spec_qt > 0) {
     // one item per (request, head sub-group): its heads times the tokens
     const int g = hq / c->num_kv_heads;
-    // the whole group where it fits in 16 rows (measured fastest: items of
-    // 16 rows beat 8 and 4 on 64 x 4-token requests, 144 vs 149 vs 201 us)
+    // the whole group where it fits in the item rows (bf16 measured fastest
+    // with 16: items of 16 rows beat 8 and 4 on 64 x 4-token requests, 144
+    // vs 149 vs 201 us)
     p.spec_heads = g;
-    while (p.spec_heads * p.spec_qt > 16) p.spec_heads >>= 1;
+    while (p.spec_heads > 1 && p.spec_heads * p.spec_qt > max_item_rows(c->dtype)) p.spec_heads >>= 1;
     st = make_plan(num_reqs, hq * p.spec_qt, c->num_kv_heads, c->head_dim, c->block_size, c->dtype,
                    max_seq_len, window, max_query_len - 1, true, &p.spec, p.spec_heads * p.spec_qt);
     if (st != PKV_OK || p.spec.scheme != 1) p.spec_qt = 0;
   }
   p.prefill = p.spec_qt == 0 && prefill_supported(c->dtype, c->head_dim, hq / c->num_kv_heads,
                                                   max_seq_len, c->block_size, window, max_query_len);
+  if (max_query_len > 1 && p.spec_qt == 0 && !p.prefill && !multi_ok) return PKV_ERR_UNSUPPORTED;
   p.multi_bytes = max_query_len <= 1 ? 0
                   : p.spec_qt > 0   ? p.spec.workspace_bytes
                   : p.prefill       ? prefill_workspace_bytes(c->head_dim)

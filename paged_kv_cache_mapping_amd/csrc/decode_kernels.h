@@ -845,19 +845,48 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <int D, int GT, int KV>
 struct MfmaShape {
-  static constexpr int kElt = KV == PKV_BF16 ? 2 : 1;
+  static constexpr int kBits = kv_bits(KV);          // 16 bf16, 8 fp8, 4 int4
+  static constexpr int kRowBytes = D * kBits / 8;    // one token of one KV head
   static constexpr int NC = D / 32;                  // MFMA k-chunks
-  static constexpr int VLPR = D * kElt / 16;         // V: lanes per row
+  // V: bytes per lane and load; INT4 takes 8 (16 elements), so that a lane
+  // accumulates as many elements per row as with fp8
+  static constexpr int kVBytes = KV == PKV_INT4 ? 8 : 16;
+  static constexpr int VLPR = kRowBytes / kVBytes;   // V: lanes per row
   static constexpr int VRPW = kWave / VLPR;          // V: rows per load
   static constexpr int VU = 16 / VRPW;               // V: loads per 16-token step
-  static constexpr int VEPL = 16 / kElt;             // V: elements per lane
-  static constexpr int KB = 8 * kElt;                // K: bytes per lane per chunk
+  static constexpr int VEPL = kVBytes * 8 / kBits;   // V: elements per lane
+  static constexpr int KB = kBits;                   // K: bytes per lane per chunk (8 elements)
   static constexpr int RG = (GT + 3) / 4;            // MFMA row groups in use
   static constexpr int QE = GT * D;                  // query elements of one piece
   static constexpr int QL = (QE + 8 * kWave - 1) / (8 * kWave);  // 16-byte loads per lane
   static_assert(VRPW <= 16 && VU * VRPW == 16, "V layout");
   static_assert(GT <= 16, "at most 16 query heads per item");
+  static_assert(KV != PKV_INT4 || D % 128 == 0, "INT4 rows span whole 64-byte K loads");
 };
+
+// INT4 K words for the matrix cores.  A word holds elements n = 0..7 of a
+// lane's k-chunk as nibbles u (element n in bits 4n .. 4n + 3).  Each nibble
+// becomes the bfloat16 value 192 + u (exponent of 128, mantissa bits
+// 0x40 | u, exact), so the products need a per-row correction of
+// -200 * sum(q) to give (u - 8) . q.  The four dwords hold elements in the
+// order 0, 2, 4, 6, 1, 3, 5, 7; the query operand is permuted to match
+// (int4_q_perm).
+__device__ __forceinline__ uint4 int4_k_bf16(uint32_t w) {
+  const uint32_t x = (w & 0x0F0F0F0Fu) | 0x40404040u;          // bytes 0x40|u0, u2, u4, u6
+  const uint32_t y = ((w >> 4) & 0x0F0F0F0Fu) | 0x40404040u;   // bytes 0x40|u1, u3, u5, u7
+  constexpr uint32_t kHi = 0x43004300u;                        // high bytes of both halves
+  return make_uint4((x & 0xFFu) | ((x << 8) & 0xFF0000u) | kHi,
+                    ((x >> 16) & 0xFFu) | ((x >> 8) & 0xFF0000u) | kHi,
+                    (y & 0xFFu) | ((y << 8) & 0xFF0000u) | kHi,
+                    ((y >> 16) & 0xFFu) | ((y >> 8) & 0xFF0000u) | kHi);
+}
+
+// Eight query elements (pairs q0q1, q2q3, q4q5, q6q7) into the order of
+// int4_k_bf16: q0q2, q4q6, q1q3, q5q7.
+__device__ __forceinline__ uint4 int4_q_perm(uint4 t) {
+  return make_uint4((t.x & 0xFFFFu) | (t.y << 16), (t.z & 0xFFFFu) | (t.w << 16),
+                    (t.x >> 16) | (t.y & 0xFFFF0000u), (t.z >> 16) | (t.w & 0xFFFF0000u));
+}
 
 // LDS layout of the balanced kernel (dynamic shared memory, 16-byte aligned
 // sections) within a budget of bytes per worker: prefix sums cum[rows + 1];
@@ -927,7 +956,8 @@ template <int D, int GT, int KV, int DEPTH, int QT = 1>
 __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
   using S = MfmaShape<D, GT, KV>;
   constexpr int NC = S::NC, VLPR = S::VLPR, VRPW = S::VRPW, VU = S::VU, VEPL = S::VEPL;
-  constexpr int KB = S::KB, RG = S::RG, kElt = S::kElt;
+  constexpr int KB = S::KB, RG = S::RG;
+  constexpr bool kI4 = KV == PKV_INT4;
   // MFMA rows of an item: (query token t, head h) as row t * GT + h
   constexpr int RI = GT * QT;
   constexpr int QE = RI * D;                                   // query elements of one piece
@@ -981,12 +1011,16 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
   const long long u_hi = min(U, sh.begin((long long)blockIdx.x + 1));
 
   const int spb_log2 = a.bs_log2 - 4;                     // 16-token steps per block
-  const int64_t blk_bytes = a.block_stride * kElt;
-  const int row_bytes = a.num_kv_heads * D * kElt;          // one token, all KV heads
+  const int64_t blk_bytes = a.block_stride * S::kBits / 8;
+  const int row_bytes = a.num_kv_heads * S::kRowBytes;      // one token, all KV heads
   const int vg = lane / VLPR, vsub = lane % VLPR;
-  const uint32_t k_lane = (uint32_t)((lane % 16) * row_bytes + (lane / 16) * KB);
-  const uint32_t v_lane = RB ? (uint32_t)((4 * (lane / 16) + (lane % 16) / VLPR) * row_bytes + vsub * 16)
-                             : (uint32_t)(vg * row_bytes + vsub * 16);
+  // K: lane l reads token l % 16; bf16 / fp8 take chunk c's elements
+  // 32 c + 8 (l / 16) .. + 7, INT4 one 16-byte load of elements
+  // 128 j + 32 (l / 16) .. + 31 per 64-byte half j (chunk 4 j + c' is the
+  // load's word c')
+  const uint32_t k_lane = (uint32_t)((lane % 16) * row_bytes + (lane / 16) * (kI4 ? 16 : KB));
+  const uint32_t v_lane = RB ? (uint32_t)((4 * (lane / 16) + (lane % 16) / VLPR) * row_bytes + vsub * S::kVBytes)
+                             : (uint32_t)(vg * row_bytes + vsub * S::kVBytes);
 
   // one lane's unit record
   int rec_phys = -1, rec_hoff = 0, rec_gid = -1, rec_pos0 = 0, rec_lo = 0, rec_hi = -1, rec_tok = 0;
@@ -1001,6 +1035,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
   float m[GT];
   f32x4_t lsum = {0.f, 0.f, 0.f, 0.f};
   float m1 = -INFINITY, ls1 = 0.f;   // row-broadcast scheme: head lane % 16's max and sum
+  float kqz = 0.f;                    // INT4: 200 * sum(q) of row lane % 16, times scale_log2
 
   // first query element of the piece (gid = row * kvgroups + head group)
   auto q_elem = [&](int gid, int tok) __attribute__((always_inline)) -> int64_t {
@@ -1008,30 +1043,54 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
     const int h0 = (kvg / a.sub_groups) * a.group + (kvg % a.sub_groups) * GT;
     return ((int64_t)tok * a.num_q_heads + h0) * D;
   };
+  // query element offset of chunk c for this lane, matching the K layout
+  auto q_chunk = [&](int c) __attribute__((always_inline)) -> int {
+    return kI4 ? 128 * (c / 4) + 32 * (lane / 16) + 8 * (c % 4) : 32 * c + 8 * (lane / 16);
+  };
+  // INT4: reorder each chunk to the K operand's element order and form the
+  // row's correction (the four lanes of a row hold a quarter of it each)
+  auto q_int4 = [&]() __attribute__((always_inline)) {
+    if constexpr (kI4) {
+      float sq = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const uint4 t = __builtin_bit_cast(uint4, qa[c]);
+        const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sq += bf16_lo(w[i]) + bf16_hi(w[i]);
+        qa[c] = __builtin_bit_cast(bf16x8_t, int4_q_perm(t));
+      }
+      sq += shfl_xor_t(sq, 16);
+      sq += shfl_xor_t(sq, 32);
+      kqz = 200.0f * sq * a.scale_log2;
+    }
+  };
   // A operand of the piece's query rows: lane l takes row l % 16, elements
-  // 32 c + 8 (l / 16) .. + 8 (rows past GT are zero)
+  // q_chunk(c) .. + 8 (rows past GT are zero)
   auto q_from_lds = [&](int slot) __attribute__((always_inline)) {
     const int row = lane % 16;
-    const uint16_t* src = qst + (size_t)slot * QE + row * D + 8 * (lane / 16);
+    const uint16_t* src = qst + (size_t)slot * QE + row * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       uint4 t = make_uint4(0, 0, 0, 0);
-      if (row < RI) t = *reinterpret_cast<const uint4*>(src + 32 * c);
+      if (row < RI) t = *reinterpret_cast<const uint4*>(src + q_chunk(c));
       qa[c] = __builtin_bit_cast(bf16x8_t, t);
     }
+    q_int4();
   };
   auto q_from_global = [&](int64_t qe) __attribute__((always_inline)) {
     const int row = lane % 16;
     const int64_t roff = (int64_t)(row / GT) * a.num_q_heads * D + (row % GT) * D;
-    const uint16_t* src = reinterpret_cast<const uint16_t*>(a.q) + qe + roff + 8 * (lane / 16);
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(a.q) + qe + roff;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       uint4 t = make_uint4(0, 0, 0, 0);
-      if (row < RI && row / GT < s_ql) t = *reinterpret_cast<const uint4*>(src + 32 * c);
+      if (row < RI && row / GT < s_ql) t = *reinterpret_cast<const uint4*>(src + q_chunk(c));
       qa[c] = __builtin_bit_cast(bf16x8_t, t);
     }
     // settle here, so that no wait for these loads lands inside the loop
     __builtin_amdgcn_s_waitcnt(0);
+    q_int4();
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       uint4 t = __builtin_bit_cast(uint4, qa[c]);
@@ -1112,6 +1171,14 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
         mh[h] = m[h];
       }
     }
+    if constexpr (kI4) {
+      // V held the nibbles u; the values are u - 8: take 8 times each row's
+      // probability sum off its accumulator
+#pragma unroll
+      for (int h = 0; h < RI; ++h)
+#pragma unroll
+        for (int e = 0; e < VEPL; ++e) acc[h][e] = fmaf(-8.0f, lh[h], acc[h][e]);
+    }
     if (vg == 0) {
       if (npieces == 1) {
         // row r = t * GT + h: query token t of the piece, head h0 + h
@@ -1166,9 +1233,10 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
     }
   };
 
+  using VT = std::conditional_t<S::kVBytes == 16, uint4, uint2>;
   struct Buf {
     uint32_t k[NC][KB / 4];
-    uint4 v[VU];
+    VT v[VU];
   };
 
   for (long long wbase = u_lo; wbase < u_hi; wbase += kWave) {
@@ -1198,7 +1266,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
       const int first_blk = klo >> a.bs_log2;
       const int t = a.bt[(int64_t)req * a.bt_stride + first_blk + j];
       rec_phys = (t >= 0 && t < a.num_blocks) ? t : -1;
-      rec_hoff = (kvg / a.sub_groups) * D * kElt;
+      rec_hoff = (kvg / a.sub_groups) * S::kRowBytes;
       rec_gid = b * kvgroups + kvg;
       rec_pos0 = (first_blk + j) << a.bs_log2;
       rec_lo = klo;
@@ -1272,29 +1340,50 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
       const int64_t off = (int64_t)phys * blk_bytes + hoff + (int64_t)r0 * row_bytes;
       const char* kp = a.kbase + off;
       const char* vp = a.vbase + off;
+      if constexpr (kI4) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        if constexpr (KB == 16) {
-          const uint4 t = *reinterpret_cast<const uint4*>(kp + k_lane + c * 32 * kElt);
-          bf.k[c][0] = t.x; bf.k[c][1] = t.y; bf.k[c][2] = t.z; bf.k[c][3] = t.w;
-        } else {
-          const uint2 t = *reinterpret_cast<const uint2*>(kp + k_lane + c * 32 * kElt);
-          bf.k[c][0] = t.x; bf.k[c][1] = t.y;
+        for (int j = 0; j < NC / 4; ++j) {
+          const uint4 t = *reinterpret_cast<const uint4*>(kp + k_lane + j * 64);
+          bf.k[4 * j][0] = t.x; bf.k[4 * j + 1][0] = t.y; bf.k[4 * j + 2][0] = t.z; bf.k[4 * j + 3][0] = t.w;
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          if constexpr (KB == 16) {
+            const uint4 t = *reinterpret_cast<const uint4*>(kp + k_lane + c * 64);
+            bf.k[c][0] = t.x; bf.k[c][1] = t.y; bf.k[c][2] = t.z; bf.k[c][3] = t.w;
+          } else {
+            const uint2 t = *reinterpret_cast<const uint2*>(kp + k_lane + c * 32);
+            bf.k[c][0] = t.x; bf.k[c][1] = t.y;
+          }
         }
       }
 #pragma unroll
       for (int u = 0; u < VU; ++u)
-        bf.v[u] = *reinterpret_cast<const uint4*>(vp + v_lane + (int64_t)u * (RB ? TPRV : VRPW) * row_bytes);
+        bf.v[u] = *reinterpret_cast<const VT*>(vp + v_lane + (int64_t)u * (RB ? TPRV : VRPW) * row_bytes);
     };
 
     // V as floats, zero for keys outside the piece's span
-    auto v_floats = [&](auto full_tag, int p0, int tok, const uint4& raw, float (&vf)[VEPL])
+    auto v_floats = [&](auto full_tag, int p0, int tok, const VT& raw, float (&vf)[VEPL])
         __attribute__((always_inline)) {
       constexpr bool full = decltype(full_tag)::value;
-      const uint32_t vwa[4] = {raw.x, raw.y, raw.z, raw.w};
+      uint32_t vwa[S::kVBytes / 4];
+      __builtin_memcpy(vwa, &raw, sizeof(raw));
       if constexpr (KV == PKV_BF16) {
 #pragma unroll
         for (int i = 0; i < VEPL / 2; ++i) { vf[2 * i] = bf16_lo(vwa[i]); vf[2 * i + 1] = bf16_hi(vwa[i]); }
+      } else if constexpr (kI4) {
+        // the unsigned nibbles u (0..15); the zero point comes off at the
+        // flush, as 8 times the row's probability sum
+#pragma unroll
+        for (int i = 0; i < S::kVBytes / 4; ++i) {
+          const uint32_t ev = vwa[i] & 0x0F0F0F0Fu, od = (vwa[i] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            vf[8 * i + 2 * b] = (float)((ev >> (8 * b)) & 0xFFu);
+            vf[8 * i + 2 * b + 1] = (float)((od >> (8 * b)) & 0xFFu);
+          }
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < VEPL / 4; ++i) {
@@ -1311,25 +1400,31 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
       }
     };
 
+    // chunk c of the step's K rows as the MFMA operand (bf16 pairs)
+    auto k_operand = [&](const Buf& bf, int c) __attribute__((always_inline)) -> uint4 {
+      if constexpr (KV == PKV_BF16) {
+        return make_uint4(bf.k[c][0], bf.k[c][1], bf.k[c][2], bf.k[c][3]);
+      } else if constexpr (kI4) {
+        return int4_k_bf16(bf.k[c][0]);
+      } else {
+        return make_uint4(e4m3x2_to_bf16x2<false>(bf.k[c][0]), e4m3x2_to_bf16x2<true>(bf.k[c][0]),
+                          e4m3x2_to_bf16x2<false>(bf.k[c][1]), e4m3x2_to_bf16x2<true>(bf.k[c][1]));
+      }
+    };
+
     // row-broadcast fold of one 16-token step
     auto body_rb = [&](auto full_tag, int p0, const Buf& bf) __attribute__((always_inline)) {
       constexpr bool full = decltype(full_tag)::value;
       f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        uint4 kw;
-        if constexpr (KB == 16) {
-          kw = make_uint4(bf.k[c][0], bf.k[c][1], bf.k[c][2], bf.k[c][3]);
-        } else {
-          kw = make_uint4(e4m3x2_to_bf16x2<false>(bf.k[c][0]), e4m3x2_to_bf16x2<true>(bf.k[c][0]),
-                          e4m3x2_to_bf16x2<false>(bf.k[c][1]), e4m3x2_to_bf16x2<true>(bf.k[c][1]));
-        }
+        const uint4 kw = k_operand(bf, c);
         sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kw), qa[c], sc, 0, 0, 0);
       }
       // lane l: tokens 4 (l / 16) + i of head l % 16
       float z[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) z[i] = sc[i] * a.scale_log2;
+      for (int i = 0; i < 4; ++i) z[i] = kI4 ? fmaf(sc[i], a.scale_log2, -kqz) : sc[i] * a.scale_log2;
       if constexpr (!full) {
         // this lane's row: token t of the piece (t >= ql: a padding row)
         int rlo = s_lo, rhi = s_hi;
@@ -1396,13 +1491,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
       f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        uint4 kw;
-        if constexpr (KB == 16) {
-          kw = make_uint4(bf.k[c][0], bf.k[c][1], bf.k[c][2], bf.k[c][3]);
-        } else {
-          kw = make_uint4(e4m3x2_to_bf16x2<false>(bf.k[c][0]), e4m3x2_to_bf16x2<true>(bf.k[c][0]),
-                          e4m3x2_to_bf16x2<false>(bf.k[c][1]), e4m3x2_to_bf16x2<true>(bf.k[c][1]));
-        }
+        const uint4 kw = k_operand(bf, c);
         sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[c], __builtin_bit_cast(bf16x8_t, kw), sc, 0, 0, 0);
       }
       float z[4];
@@ -1452,25 +1541,8 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
 #pragma unroll
       for (int u = 0; u < VU; ++u) {
         const int tok = u * VRPW + vg;                // token inside the step
-        const uint32_t vwa[4] = {bf.v[u].x, bf.v[u].y, bf.v[u].z, bf.v[u].w};
         float vf[VEPL];
-        if constexpr (KV == PKV_BF16) {
-#pragma unroll
-          for (int i = 0; i < VEPL / 2; ++i) { vf[2 * i] = bf16_lo(vwa[i]); vf[2 * i + 1] = bf16_hi(vwa[i]); }
-        } else {
-#pragma unroll
-          for (int i = 0; i < VEPL / 4; ++i) {
-            const f32x2 v01 = e4m3x2_to_f32<false>(vwa[i]);
-            const f32x2 v23 = e4m3x2_to_f32<true>(vwa[i]);
-            vf[4 * i] = v01.x; vf[4 * i + 1] = v01.y; vf[4 * i + 2] = v23.x; vf[4 * i + 3] = v23.y;
-          }
-        }
-        if constexpr (!full) {
-          const int pos = p0 + tok;
-          const bool live = pos >= s_lo && pos <= s_hi;
-#pragma unroll
-          for (int e = 0; e < VEPL; ++e) vf[e] = live ? vf[e] : 0.f;
-        }
+        v_floats(full_tag, p0, tok, bf.v[u], vf);
 #pragma unroll
         for (int h = 0; h < GT; ++h) {
           const int src = (tok + 16 * (h / 4)) * 4;
@@ -1740,13 +1812,20 @@ void launch_stream(const DecodeArgs& a, int workers, hipStream_t s) {
 // Balanced partition (matrix cores), a.heads_per_item query heads per item.
 template <int D, int KV>
 int run_stream_dk(const DecodeArgs& a, int workers, hipStream_t s) {
-  if constexpr (KV != PKV_F32 && D * (KV == PKV_BF16 ? 2 : 1) >= 64) {
+  if constexpr (KV != PKV_F32 && D * kv_bits(KV) / 8 >= 64 && (KV != PKV_INT4 || D % 128 == 0)) {
     switch (a.heads_per_item) {
       case 1: launch_stream<D, 1, KV>(a, workers, s); return PKV_OK;
       case 2: launch_stream<D, 2, KV>(a, workers, s); return PKV_OK;
       case 4: launch_stream<D, 4, KV>(a, workers, s); return PKV_OK;
       case 8: launch_stream<D, 8, KV>(a, workers, s); return PKV_OK;
-      case 16: launch_stream<D, 16, KV>(a, workers, s); return PKV_OK;
+      case 16:
+        // 16 rows of 16-element accumulators (fp8, int4) do not fit in the
+        // registers; those caches take items of 8 rows
+        if constexpr (MfmaShape<D, 16, KV>::VEPL <= 8) {
+          launch_stream<D, 16, KV>(a, workers, s);
+          return PKV_OK;
+        }
+        break;
     }
   }
   return PKV_ERR_UNSUPPORTED;
@@ -1761,20 +1840,26 @@ void launch_merge(const DecodeArgs& a, int ot, hipStream_t s) {
 
 // Multi-token items (row mode 3): a.heads_per_item query heads times a.qt
 // query tokens as one item's MFMA rows.  Shapes where a V token row fits
-// in 16 lanes (bf16 up to D 128, fp8 up to D 256).
+// in 16 lanes (bf16 up to D 128, fp8 up to D 256, int4 D 128 and 256).
 template <int D, int KV>
 int run_multi_dk(const DecodeArgs& a, int workers, hipStream_t s) {
-  if constexpr (KV != PKV_F32 && D * (KV == PKV_BF16 ? 2 : 1) >= 64 && D * (KV == PKV_BF16 ? 2 : 1) <= 256) {
+  if constexpr (KV != PKV_F32 && D * kv_bits(KV) / 8 >= 64 && D * kv_bits(KV) / 8 <= 256 &&
+                (KV != PKV_INT4 || D % 128 == 0)) {
     switch (a.heads_per_item * 100 + a.qt) {
       case 102: launch_stream<D, 1, KV, 2>(a, workers, s); return PKV_OK;
       case 104: launch_stream<D, 1, KV, 4>(a, workers, s); return PKV_OK;
       case 108: launch_stream<D, 1, KV, 8>(a, workers, s); return PKV_OK;
       case 202: launch_stream<D, 2, KV, 2>(a, workers, s); return PKV_OK;
       case 204: launch_stream<D, 2, KV, 4>(a, workers, s); return PKV_OK;
-      case 208: launch_stream<D, 2, KV, 8>(a, workers, s); return PKV_OK;
       case 402: launch_stream<D, 4, KV, 2>(a, workers, s); return PKV_OK;
-      case 404: launch_stream<D, 4, KV, 4>(a, workers, s); return PKV_OK;
-      case 802: launch_stream<D, 8, KV, 2>(a, workers, s); return PKV_OK;
+    }
+    // items of 16 rows: bf16 only (see run_stream_dk)
+    if constexpr (MfmaShape<D, 16, KV>::VEPL <= 8) {
+      switch (a.heads_per_item * 100 + a.qt) {
+        case 208: launch_stream<D, 2, KV, 8>(a, workers, s); return PKV_OK;
+        case 404: launch_stream<D, 4, KV, 4>(a, workers, s); return PKV_OK;
+        case 802: launch_stream<D, 8, KV, 2>(a, workers, s); return PKV_OK;
+      }
     }
   }
   return PKV_ERR_UNSUPPORTED;

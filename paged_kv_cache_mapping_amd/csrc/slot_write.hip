@@ -1,4 +1,4 @@
-// Slot mapping (step 1), KV cache write (step 2) and the bulk FP8 codec.
+// Slot mapping (step 1), KV cache write (step 2), block copies and the bulk FP8 and INT4 codecs.
 //
 // Slot mapping follows the page "Deep Dive into vLLM Worker-Side GPU KV Cache
 // Initialization", section "Pinpointing the Token Slot": position p of a
@@ -122,7 +122,7 @@ __device__ __forceinline__ void load_as_f32(const void* p, float (&x)[N]) {
 // destination, or the whole row when a row is shorter).
 template <int SRC, int DST, int CE>
 __global__ __launch_bounds__(256) void cache_write_kernel(WriteArgs a) {
-  constexpr int kDstElt = DST == PKV_F32 ? 4 : (DST == PKV_BF16 ? 2 : 1);
+  constexpr int kDstBits = kv_bits(DST);
   constexpr int kSrcElt = SRC == PKV_F32 ? 4 : 2;
   const int chunks_per_head = a.head_dim / CE;
   const int chunks_per_plane = a.num_kv_heads * chunks_per_head;
@@ -143,11 +143,12 @@ __global__ __launch_bounds__(256) void cache_write_kernel(WriteArgs a) {
 
   const char* src = reinterpret_cast<const char*>(kv ? a.value : a.key) +
                     ((int64_t)t * a.tok_stride + (int64_t)h * a.head_stride + (int64_t)c * CE) * kSrcElt;
+  // element index times bits over 8 (INT4 chunks start at even elements)
   char* dst = reinterpret_cast<char*>(kv ? a.vdst : a.kdst) +
-              (blk * a.block_stride + (off * a.num_kv_heads + h) * a.head_dim + (int64_t)c * CE) * kDstElt;
+              (blk * a.block_stride + (off * a.num_kv_heads + h) * a.head_dim + (int64_t)c * CE) * kDstBits / 8;
 
   if constexpr (SRC == DST) {
-    constexpr int kBytes = CE * kDstElt;
+    constexpr int kBytes = CE * kDstBits / 8;
     constexpr int kStep = kBytes >= 16 ? 16 : kBytes;
     using T = typename RawChunk<kStep>::T;
 #pragma unroll
@@ -167,6 +168,15 @@ __global__ __launch_bounds__(256) void cache_write_kernel(WriteArgs a) {
       for (int i = 0; i < CE / 8; ++i)
         reinterpret_cast<uint4*>(dst)[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
     }
+  } else if constexpr (DST == PKV_INT4) {  // 32 elements -> 16 bytes of nibbles
+    static_assert(CE == 32, "INT4 chunks are 32 elements");
+    const float inv = kv ? a.inv_v_scale : a.inv_k_scale;
+    float x[CE];
+    load_as_f32<SRC, CE>(src, x);
+#pragma unroll
+    for (int i = 0; i < CE; ++i) x[i] *= inv;
+    *reinterpret_cast<uint4*>(dst) = make_uint4(int4_pack8(x), int4_pack8(x + 8), int4_pack8(x + 16),
+                                                int4_pack8(x + 24));
   } else {  // -> fp8 e4m3 with the per-tensor inverse scale
     const float inv = kv ? a.inv_v_scale : a.inv_k_scale;
     float x[CE];
@@ -214,6 +224,32 @@ __global__ __launch_bounds__(256) void fp8_dequantize_bf16_kernel(const uint8_t*
   out[i] = (uint16_t)(e4m3x2_to_bf16x2<false>((uint32_t)codes[i]) & 0xFFFFu);
 }
 
+// INT4: one thread per output byte (two elements).
+template <int SRC>
+__global__ __launch_bounds__(256) void int4_quantize_kernel(const void* __restrict__ x, int64_t nbytes,
+                                                            float inv, uint8_t* __restrict__ packed) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= nbytes) return;
+  float v0, v1;
+  if constexpr (SRC == PKV_F32) {
+    v0 = reinterpret_cast<const float*>(x)[2 * j];
+    v1 = reinterpret_cast<const float*>(x)[2 * j + 1];
+  } else {
+    v0 = as_float((uint32_t)reinterpret_cast<const uint16_t*>(x)[2 * j] << 16);
+    v1 = as_float((uint32_t)reinterpret_cast<const uint16_t*>(x)[2 * j + 1] << 16);
+  }
+  packed[j] = (uint8_t)(int4_encode(v0 * inv) | (int4_encode(v1 * inv) << 4));
+}
+
+__global__ __launch_bounds__(256) void int4_dequantize_kernel(const uint8_t* __restrict__ packed,
+                                                              int64_t n, float scale,
+                                                              float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t u = ((uint32_t)packed[i >> 1] >> (4 * (i & 1))) & 0xFu;
+  out[i] = (float)((int)u - 8) * scale;
+}
+
 static int log2_int(int x) {
   int l = 0;
   while ((1 << l) < x) ++l;
@@ -226,8 +262,9 @@ static void launch_write(const WriteArgs& a, int ce, hipStream_t s) {
   const dim3 grid((unsigned)((threads + 255) / 256));
   switch (ce) {
     case 4: if constexpr (DST == PKV_F32) { cache_write_kernel<SRC, DST, 4><<<grid, 256, 0, s>>>(a); } break;
-    case 8: if constexpr (DST != PKV_F32) { cache_write_kernel<SRC, DST, 8><<<grid, 256, 0, s>>>(a); } break;
+    case 8: if constexpr (DST == PKV_BF16 || DST == PKV_FP8_E4M3) { cache_write_kernel<SRC, DST, 8><<<grid, 256, 0, s>>>(a); } break;
     case 16: if constexpr (DST == PKV_FP8_E4M3) { cache_write_kernel<SRC, DST, 16><<<grid, 256, 0, s>>>(a); } break;
+    case 32: if constexpr (DST == PKV_INT4) { cache_write_kernel<SRC, DST, 32><<<grid, 256, 0, s>>>(a); } break;
   }
 }
 
@@ -272,7 +309,7 @@ extern "C" int pkv_cache_write(const void* key, const void* value, int32_t src_d
       (src_head_stride * se) % 16)
     return PKV_ERR_SHAPE;
   // destination elements per thread: 16 bytes of destination, capped by the row
-  int ce = 16 / dtype_size(dst);
+  int ce = 128 / dtype_bits(dst);
   if (ce > D) ce = D;
   // sources narrower than 16 bytes per chunk are not vectorised: bf16 -> fp8
   // with D = 8 reads 16 bytes (fine); everything else keeps >= 16 source bytes.
@@ -298,10 +335,12 @@ extern "C" int pkv_cache_write(const void* key, const void* value, int32_t src_d
   if (src_dtype == PKV_F32) {
     if (dst == PKV_F32) launch_write<PKV_F32, PKV_F32>(a, ce, stream);
     else if (dst == PKV_BF16) launch_write<PKV_F32, PKV_BF16>(a, ce, stream);
-    else launch_write<PKV_F32, PKV_FP8_E4M3>(a, ce, stream);
+    else if (dst == PKV_FP8_E4M3) launch_write<PKV_F32, PKV_FP8_E4M3>(a, ce, stream);
+    else launch_write<PKV_F32, PKV_INT4>(a, ce, stream);
   } else {
     if (dst == PKV_BF16) launch_write<PKV_BF16, PKV_BF16>(a, ce, stream);
-    else launch_write<PKV_BF16, PKV_FP8_E4M3>(a, ce, stream);
+    else if (dst == PKV_FP8_E4M3) launch_write<PKV_BF16, PKV_FP8_E4M3>(a, ce, stream);
+    else launch_write<PKV_BF16, PKV_INT4>(a, ce, stream);
   }
   return launch_status();
 }
@@ -335,6 +374,33 @@ extern "C" int pkv_fp8_e4m3_dequantize(const uint8_t* codes, int64_t n, float sc
   return launch_status();
 }
 
+extern "C" int pkv_int4_quantize(const void* x, int32_t src_dtype, int64_t n, float scale,
+                                 uint8_t* packed, hipStream_t stream) {
+  if (n < 0 || (n & 1)) return PKV_ERR_SHAPE;
+  if (src_dtype != PKV_F32 && src_dtype != PKV_BF16) return PKV_ERR_DTYPE;
+  if (!(scale > 0.0f && scale < 3.0e38f)) return PKV_ERR_SHAPE;
+  if (n == 0) return PKV_OK;
+  if (!x || !packed) return PKV_ERR_NULL;
+  const float inv = 1.0f / scale;
+  const int64_t nb = n / 2;
+  const dim3 grid((unsigned)((nb + 255) / 256));
+  if (src_dtype == PKV_F32) int4_quantize_kernel<PKV_F32><<<grid, 256, 0, stream>>>(x, nb, inv, packed);
+  else int4_quantize_kernel<PKV_BF16><<<grid, 256, 0, stream>>>(x, nb, inv, packed);
+  return launch_status();
+}
+
+extern "C" int pkv_int4_dequantize(const uint8_t* packed, int64_t n, float scale, int32_t out_dtype,
+                                   void* out, hipStream_t stream) {
+  if (n < 0 || (n & 1)) return PKV_ERR_SHAPE;
+  if (out_dtype != PKV_F32) return PKV_ERR_DTYPE;
+  if (!(scale > 0.0f && scale < 3.0e38f)) return PKV_ERR_SHAPE;
+  if (n == 0) return PKV_OK;
+  if (!packed || !out) return PKV_ERR_NULL;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  int4_dequantize_kernel<<<grid, 256, 0, stream>>>(packed, n, scale, reinterpret_cast<float*>(out));
+  return launch_status();
+}
+
 // ------------------------------------------------------------------ block copy
 // Copy-on-write support for blocks shared between requests: every element of
 // block src is copied to block dst in both planes.  One workgroup per (pair,
@@ -365,12 +431,12 @@ extern "C" int pkv_copy_blocks(const pkv_cache* cache, const int32_t* src_ids, c
   if (num_pairs < 0) return PKV_ERR_SHAPE;
   if (num_pairs == 0) return PKV_OK;
   if (!src_ids || !dst_ids) return PKV_ERR_NULL;
-  const int es = dtype_size(cache->dtype);
-  const int64_t data = (int64_t)cache->block_size * cache->num_kv_heads * cache->head_dim * es;
+  const int64_t data = elem_bytes((int64_t)cache->block_size * cache->num_kv_heads * cache->head_dim,
+                                  cache->dtype);
   if (data % 16) return PKV_ERR_UNSUPPORTED;
   const dim3 grid((unsigned)num_pairs, 2);
   copy_blocks_kernel<<<grid, 256, 0, stream>>>(reinterpret_cast<char*>(cache->k), reinterpret_cast<char*>(cache->v),
-                                               cache->block_stride * es, data, src_ids, dst_ids,
+                                               elem_bytes(cache->block_stride, cache->dtype), data, src_ids, dst_ids,
                                                cache->num_blocks, err_count);
   return launch_status();
 }

@@ -30,8 +30,8 @@ import torch
 
 from .api import CacheView
 
-ELEMENT_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
-TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+ELEMENT_BITS = {"f32": 32, "bf16": 16, "fp8": 8, "int4": 4}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8, "int4": torch.uint8}
 ALIGN = 256
 
 
@@ -47,7 +47,7 @@ class KVCacheSpec:
     @property
     def block_bytes(self):
         """Bytes of one block of one plane (K or V)."""
-        return self.block_size * self.num_kv_heads * self.head_dim * ELEMENT_BYTES[self.dtype]
+        return self.block_size * self.num_kv_heads * self.head_dim * ELEMENT_BITS[self.dtype] // 8
 
     @property
     def page_bytes(self):
@@ -104,7 +104,8 @@ def num_blocks_for_budget(total_bytes, utilization, non_kv_bytes, spec, num_tens
     utilisation) less the non-KV bytes, over one block's K+V bytes times the
     KV tensors that share the pool."""
     from . import _lib
-    code = {"f32": _lib.PKV_F32, "bf16": _lib.PKV_BF16, "fp8": _lib.PKV_FP8_E4M3}[spec.dtype]
+    code = {"f32": _lib.PKV_F32, "bf16": _lib.PKV_BF16, "fp8": _lib.PKV_FP8_E4M3,
+            "int4": _lib.PKV_INT4}[spec.dtype]
     n = _lib.load().pkv_num_blocks_for_budget(int(total_bytes), float(utilization), int(non_kv_bytes),
                                               int(num_tensors), spec.block_size, spec.num_kv_heads,
                                               spec.head_dim, code)
@@ -125,7 +126,8 @@ def allocate(config, device, zero=False, k_scale=1.0, v_scale=1.0):
     """Allocate every tensor as a byte buffer and return {layer: CacheView}.
 
     Each buffer is laid out as [2 (K, V), num_blocks, block_size, kv_heads,
-    head_dim] of the layer's dtype; all layers sharing it get the same view.
+    head_dim] of the layer's dtype (int4: bytes [..., head_dim / 2]); all
+    layers sharing it get the same view.
     """
     views = {}
     buffers = []
@@ -144,9 +146,11 @@ def allocate(config, device, zero=False, k_scale=1.0, v_scale=1.0):
             n = 2 * config.num_blocks * spec.block_bytes
             if n > t.size:
                 raise ValueError("tensor too small for layer %s" % name)
+            i4 = spec.dtype == "int4"
             typed = buf[:n].view(TORCH_DTYPE[spec.dtype]).view(
-                2, config.num_blocks, spec.block_size, spec.num_kv_heads, spec.head_dim)
-            views[name] = CacheView.from_planes(typed[0], typed[1], k_scale, v_scale)
+                2, config.num_blocks, spec.block_size, spec.num_kv_heads,
+                spec.head_dim // 2 if i4 else spec.head_dim)
+            views[name] = CacheView.from_planes(typed[0], typed[1], k_scale, v_scale, int4=i4)
     return views, buffers
 
 

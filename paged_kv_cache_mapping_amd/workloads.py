@@ -5,8 +5,11 @@ drawn from ``numpy.random.default_rng(seed)`` (PCG64) in a fixed order:
 lengths -> block-pool permutation -> K history -> V history -> new K/V -> Q.
 float32 draws become bfloat16 by round-to-nearest-even (torch's conversion)
 and FP8 history by torch's E4M3 conversion after clamping to +-448 with the
-per-tensor scale amax/448.  Blocks no request owns are filled with NaN so
-that any stray read shows up.
+per-tensor scale amax/448.  INT4 history is drawn as integer codes directly:
+round(2 z) for standard normal z, limited to [-8, 7], with scales sigma / 2,
+stored as nibbles (element 2j low, 2j + 1 high).  Blocks no request owns are
+filled with NaN (INT4, which has no NaN: 0xFF, the largest value) so that
+any stray read shows up.
 
 Block tables come from a shuffled free pool, as a scheduler would hand them
 out; the hybrid workload drives :class:`kv_cache.GroupBlockTables` so that
@@ -20,8 +23,8 @@ import torch
 
 from . import kv_cache
 
-NAN_BITS = {"bf16": np.uint16(0x7FC0), "fp8": np.uint8(0x7F)}
-STORAGE = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}
+NAN_BITS = {"bf16": np.uint16(0x7FC0), "fp8": np.uint8(0x7F), "int4": np.uint8(0xFF)}
+STORAGE = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "int4": np.uint8}
 
 
 def bf16_bits(x):
@@ -34,6 +37,13 @@ def fp8_codes(x, scale):
     """float32 array -> E4M3 codes of clamp(x / scale) (torch conversion)."""
     y = np.clip(np.asarray(x, np.float32) * (np.float32(1) / np.float32(scale)), -448.0, 448.0)
     return torch.from_numpy(y.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def int4_history(rng, shape):
+    """Packed INT4 rows [..., D / 2] of codes round(2 z) in [-8, 7]."""
+    k = np.clip(np.rint(rng.standard_normal(shape, dtype=np.float32) * np.float32(2.0)), -8, 7)
+    u = (k + 8).astype(np.uint8)
+    return (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
 
 
 def nan_plane(shape, dtype):
@@ -87,13 +97,13 @@ class Workload:
 
     def kv_read_bytes(self):
         """Cache bytes an attention pass must read: visible keys x Hkv x D x 2."""
-        elt = {"f32": 4, "bf16": 2, "fp8": 1}[self.cache_dtype]
+        elt = {"f32": 4, "bf16": 2, "fp8": 1, "int4": 0.5}[self.cache_dtype]
         total = 0
         for L, q0, q1 in zip(self.seq_lens, self.query_start_loc[:-1], self.query_start_loc[1:]):
             p0 = int(L) - int(q1 - q0)
             lo = max(0, p0 - self.window + 1) if self.window > 0 else 0
             total += int(L) - lo
-        return total * self.num_kv_heads * self.head_dim * 2 * elt
+        return int(total * self.num_kv_heads * self.head_dim * 2 * elt)
 
     def device(self, device="cuda"):
         """Device copies: a one-layer KV tensor (byte buffer + typed views)."""
@@ -161,9 +171,17 @@ def decode_workload(name, seed, lengths_fn, num_blocks_fn, *, block_size, num_q_
     ids = perm[:used]
     shape = (nb, block_size, num_kv_heads, head_dim)
     tail = shape[1:]
-    kp, vp = nan_plane(shape, cache_dtype), nan_plane(shape, cache_dtype)
+    pshape = shape[:3] + (head_dim // 2,) if cache_dtype == "int4" else shape
+    kp, vp = nan_plane(pshape, cache_dtype), nan_plane(pshape, cache_dtype)
     B = len(lengths)
-    if cache_dtype == "fp8":
+    if cache_dtype == "int4":
+        kp[ids] = int4_history(rng, (used,) + tail)                             # K history
+        vp[ids] = int4_history(rng, (used,) + tail)                             # V history
+        nk = rng.standard_normal((B, num_kv_heads, head_dim), dtype=np.float32) * np.float32(sigma)
+        nv = rng.standard_normal((B, num_kv_heads, head_dim), dtype=np.float32) * np.float32(sigma)
+        new_k, new_v = bf16_bits(nk), bf16_bits(nv)
+        k_scale = v_scale = float(np.float32(sigma / 2.0))
+    elif cache_dtype == "fp8":
         kx = rng.standard_normal((used,) + tail, dtype=np.float32) * np.float32(sigma)   # K history
         vx = rng.standard_normal((used,) + tail, dtype=np.float32) * np.float32(sigma)   # V history
         nk = rng.standard_normal((B, num_kv_heads, head_dim), dtype=np.float32) * np.float32(sigma)
@@ -234,6 +252,16 @@ def fp8_decode(seed=4, batch=128, sigma_len=1.0):
         "fp8_e4m3_decode_b128_lognormal1024", seed, lengths, lambda n: int(np.ceil(n * 1.25)),
         block_size=16, num_q_heads=32, num_kv_heads=8, head_dim=128, cache_dtype="fp8",
         q_dtype="bf16", sigma=1.0, fp8_amax_scale=True)
+
+
+def int4_decode(seed=8, batch=64, lo=128, hi=2048, pool=16384):
+    """The Llama-3-8B decode layer with an INT4 cache (half a byte per
+    element): 32/8 heads, D 128, block 16, 64 sequences with lengths uniform
+    in [128, 2048], 16384-block pool, per-tensor scales sigma / 2."""
+    return decode_workload(
+        "int4_decode_b64_L128-2048", seed, lambda rng: rng.integers(lo, hi + 1, size=batch),
+        None, pool_blocks=pool, block_size=16, num_q_heads=32, num_kv_heads=8, head_dim=128,
+        cache_dtype="int4", q_dtype="bf16", sigma=1.0 / np.sqrt(128.0))
 
 
 def spec_decode(seed=7, batch=64, q_len=4, lo=128, hi=2048, pool=16384):
@@ -441,4 +469,4 @@ def hybrid_chunked(seed=5, num_decode=96, num_prefill=4, chunk=512, window=4096,
 
 
 ALL = {"tiny": tiny, "llama8b": llama8b_decode, "llama70b": llama70b_decode,
-       "fp8": fp8_decode, "hybrid": hybrid_chunked}
+       "fp8": fp8_decode, "hybrid": hybrid_chunked, "int4": int4_decode}

@@ -35,7 +35,8 @@ def test_header_declares_the_expected_calls():
                  "pkv_paged_attention_chunked", "pkv_decode_plan_make",
                  "pkv_paged_attention_decode_partials", "pkv_paged_attention_decode_combine",
                  "pkv_chunked_workspace_size", "pkv_kv_bytes_per_token", "pkv_status_string",
-                 "pkv_fp8_e4m3_quantize", "pkv_fp8_e4m3_dequantize", "pkv_copy_blocks"):
+                 "pkv_fp8_e4m3_quantize", "pkv_fp8_e4m3_dequantize", "pkv_copy_blocks",
+                 "pkv_int4_quantize", "pkv_int4_dequantize", "pkv_num_blocks_for_budget"):
         assert want in names
     assert set(names) == set(_lib.SIGNATURES)   # the binding covers every declaration
 
@@ -54,8 +55,10 @@ def test_library_exports_every_declared_symbol_and_nothing_else(lib):
 def test_kv_bytes_per_token_matches_the_oracle_closed_form(lib):
     assert lib.pkv_kv_bytes_per_token(80, 8, 128, _lib.PKV_BF16) == 327680
     assert lib.pkv_kv_bytes_per_token(80, 8, 128, _lib.PKV_FP8_E4M3) == 163840
+    assert lib.pkv_kv_bytes_per_token(80, 8, 128, _lib.PKV_INT4) == 81920
     for layers, heads, d in ((1, 1, 8), (32, 8, 128), (12, 12, 64)):
-        for dt, name in ((_lib.PKV_F32, "f32"), (_lib.PKV_BF16, "bf16"), (_lib.PKV_FP8_E4M3, "fp8")):
+        for dt, name in ((_lib.PKV_F32, "f32"), (_lib.PKV_BF16, "bf16"), (_lib.PKV_FP8_E4M3, "fp8"),
+                         (_lib.PKV_INT4, "int4")):
             assert lib.pkv_kv_bytes_per_token(layers, heads, d, dt) == \
                 sizing.kv_bytes_per_token(layers, heads, d, name)
     assert lib.pkv_kv_bytes_per_token(1, 1, 8, 7) == -1
@@ -82,6 +85,9 @@ def _cache(**kw):
     (dict(block_stride=100), _lib.PKV_ERR_SHAPE),
     (dict(k=0x1008), _lib.PKV_ERR_SHAPE),                     # misaligned plane
     (dict(dtype=_lib.PKV_FP8_E4M3, k_scale=0.0), _lib.PKV_ERR_SHAPE),
+    (dict(dtype=_lib.PKV_INT4, v_scale=-1.0), _lib.PKV_ERR_SHAPE),
+    (dict(dtype=_lib.PKV_INT4, head_dim=16, block_stride=16 * 8 * 16), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(dtype=_lib.PKV_INT4, block_stride=16 * 8 * 128 + 16), _lib.PKV_ERR_SHAPE),   # 8-byte blocks
 ])
 def test_cache_descriptor_checks(lib, kw, status):
     c = _cache(**kw)
@@ -121,6 +127,21 @@ def test_argument_checks_return_before_launching(lib):
     assert lib.pkv_fp8_e4m3_dequantize(0x100, 16, 2.0, _lib.PKV_BF16, 0x100, None) == \
         _lib.PKV_ERR_UNSUPPORTED
     assert lib.pkv_fp8_e4m3_dequantize(0x100, 0, 1.0, _lib.PKV_F32, 0x100, None) == _lib.PKV_OK
+    assert lib.pkv_int4_quantize(0x100, _lib.PKV_BF16, 15, 1.0, 0x100, None) == _lib.PKV_ERR_SHAPE   # odd
+    assert lib.pkv_int4_quantize(0x100, _lib.PKV_INT4, 16, 1.0, 0x100, None) == _lib.PKV_ERR_DTYPE
+    assert lib.pkv_int4_quantize(0x100, _lib.PKV_F32, 16, float("inf"), 0x100, None) == _lib.PKV_ERR_SHAPE
+    assert lib.pkv_int4_quantize(None, _lib.PKV_F32, 16, 1.0, 0x100, None) == _lib.PKV_ERR_NULL
+    assert lib.pkv_int4_dequantize(0x100, 16, 1.0, _lib.PKV_BF16, 0x100, None) == _lib.PKV_ERR_DTYPE
+    assert lib.pkv_int4_dequantize(0x100, 0, 1.0, _lib.PKV_F32, 0x100, None) == _lib.PKV_OK
+    # int4 attention: shapes without an int4 kernel are refused on the host
+    ci4 = _cache(dtype=_lib.PKV_INT4, head_dim=64, block_stride=16 * 8 * 64)
+    assert lib.pkv_paged_attention_decode(0x100, 0x100, _lib.PKV_BF16, 4, 32, ctypes.byref(ci4), 0x100, 8,
+                                          0x100, 64, 0.1, 0, None, 0, None) == _lib.PKV_ERR_UNSUPPORTED
+    ws = ctypes.c_size_t(0)
+    assert lib.pkv_chunked_workspace_size(64, 4, 32, 8, 128, 16, _lib.PKV_INT4, 40, 512, 0,
+                                          ctypes.byref(ws)) == _lib.PKV_ERR_UNSUPPORTED
+    assert lib.pkv_chunked_workspace_size(64, 16, 32, 8, 128, 16, _lib.PKV_INT4, 8, 512, 0,
+                                          ctypes.byref(ws)) == _lib.PKV_OK and ws.value > 0
     # block copy: bad cache, negative or empty pair lists, missing id arrays
     assert lib.pkv_copy_blocks(ctypes.byref(_cache(k=0)), 0x100, 0x100, 4, None, None) == _lib.PKV_ERR_NULL
     assert lib.pkv_copy_blocks(ctypes.byref(c), 0x100, 0x100, -1, None, None) == _lib.PKV_ERR_SHAPE
@@ -132,12 +153,12 @@ def test_num_blocks_for_budget_matches_the_oracle(lib):
     """The library's budget arithmetic equals the oracle's closed form
     (PageAttention blog, § Memory Pre-allocation Logic) over a grid."""
     from oracle import sizing
-    codes = {"f32": _lib.PKV_F32, "bf16": _lib.PKV_BF16, "fp8": _lib.PKV_FP8_E4M3}
+    codes = {"f32": _lib.PKV_F32, "bf16": _lib.PKV_BF16, "fp8": _lib.PKV_FP8_E4M3, "int4": _lib.PKV_INT4}
     for total in (0, 10 ** 9, 64 * 2 ** 30, 288 * 10 ** 9):
         for util in (0.5, 0.9, 0.95, 1.0):
             for non_kv in (0, 10 ** 9, 20 * 10 ** 9):
                 for layers in (1, 12, 80):
-                    for dt in ("f32", "bf16", "fp8"):
+                    for dt in ("f32", "bf16", "fp8", "int4"):
                         got = lib.pkv_num_blocks_for_budget(total, util, non_kv, layers, 16, 8, 128, codes[dt])
                         assert got == sizing.num_blocks_for_budget(total, util, non_kv, layers, 16, 8, 128, dt)
     assert lib.pkv_num_blocks_for_budget(10 ** 9, 0.0, 0, 1, 16, 8, 128, _lib.PKV_BF16) == _lib.PKV_ERR_SHAPE
