@@ -43,6 +43,12 @@ static int heads_per_item_mfma(int group, int kv_dtype) {
   return (group == 1 || group == 2 || group == 4 || group == 8) ? group : 0;
 }
 
+// INT4 decode items may span two KV heads: head size 128, an even number of
+// KV heads and at most 8 rows per pair.
+static bool int4_pairs(int kv_dtype, int d, int hkv, int group) {
+  return kv_dtype == PKV_INT4 && d == 128 && hkv % 2 == 0 && group >= 1 && 2 * group <= 8;
+}
+
 static bool mfma_eligible(int kv_dtype, int d, int bs) {
   if (bs % 16 != 0) return false;
   if (kv_dtype == PKV_INT4) return d == 128;   // the one INT4 head size built
@@ -56,8 +62,11 @@ constexpr int kTrailPct = 80;            // second wave on a SIMD: share in perc
 constexpr int kLdsPerCU = 160 * 1024;
 
 // Resident waves per CU for the balanced kernels: two per SIMD while the
-// registers allow it (up to four query heads per item), else one.
-static int stream_waves_per_cu(int heads_per_item) { return heads_per_item <= 4 ? 8 : 4; }
+// registers allow it (up to four query heads per item; eight with INT4,
+// whose lanes keep 8 accumulators per row), else one.
+static int stream_waves_per_cu(int heads_per_item, int kv_dtype) {
+  return heads_per_item <= (kv_dtype == PKV_INT4 ? 8 : 4) ? 8 : 4;
+}
 
 static size_t partial_bytes(int rows, int hq, int splits, int d) {
   return (size_t)rows * hq * splits * ((size_t)d + 2) * sizeof(float);
@@ -80,12 +89,15 @@ static int make_plan(int rows, int hq, int hkv, int d, int bs, int kv_dtype, int
   const int group = hq / hkv;
   const int nvis = max_visible_blocks(max_seq_len, bs, window, extra);
   const long long cus = device_cu_count();
-  const int gm = force_hpi > 0 ? force_hpi : heads_per_item_mfma(group, kv_dtype);
+  int gm = force_hpi > 0 ? force_hpi : heads_per_item_mfma(group, kv_dtype);
+  // INT4 items over two adjacent KV heads (whole 128-byte lines) when the
+  // pair's rows fit: heads_per_item = 2 * group marks them
+  if (force_hpi == 0 && int4_pairs(kv_dtype, d, hkv, group)) gm = 2 * group;
   plan->kernel_variant = 0;
   if (allow_stream && mfma_eligible(kv_dtype, d, bs) && gm > 0 && rows <= kMaxStreamRows) {
     // balanced partition over resident wave slots
     const long long units = (long long)(rows > 0 ? rows : 1) * (hq / gm) * nvis;
-    const int per_cu = stream_waves_per_cu(gm);
+    const int per_cu = stream_waves_per_cu(gm, kv_dtype);
     long long workers = cus * per_cu;
     const long long need = (units + kStreamMinUnits - 1) / kStreamMinUnits;
     plan->lead_workers = 0;
@@ -135,7 +147,9 @@ static int check_plan(const pkv_decode_plan* plan, int rows, int hq, int hkv, in
     // any of 1, 2, 4, 8, 16 that divides the group (items of a KV head then
     // share its blocks); the planner picks the largest
     const int hpi = plan->heads_per_item;
-    if (hpi <= 0 || hpi > max_item_rows(kv_dtype) || (hpi & (hpi - 1)) || group % hpi) return PKV_ERR_SHAPE;
+    const bool pair = hpi == 2 * group && int4_pairs(kv_dtype, d, hkv, group);
+    if (!pair && (hpi <= 0 || hpi > max_item_rows(kv_dtype) || (hpi & (hpi - 1)) || group % hpi))
+      return PKV_ERR_SHAPE;
     if (plan->split_blocks < 1 || plan->num_workers < 1) return PKV_ERR_SHAPE;
     if (plan->lead_workers < 0 || plan->lead_workers > plan->num_workers) return PKV_ERR_SHAPE;
     if (plan->trail_share_pct < 1 || plan->trail_share_pct > 100) return PKV_ERR_SHAPE;
@@ -160,6 +174,7 @@ PKV_DECODE_ALL_D(extern, 64)
 PKV_DECODE_ALL_D(extern, 128)
 PKV_DECODE_ALL_D(extern, 256)
 PKV_DECODE_STREAM_INST(extern, 128, PKV_INT4)
+PKV_DECODE_PAIR_INST(extern, 128)
 PKV_DECODE_MULTI_INST(extern, 128, PKV_BF16)
 PKV_DECODE_MULTI_INST(extern, 128, PKV_FP8_E4M3)
 PKV_DECODE_MULTI_INST(extern, 128, PKV_INT4)
@@ -205,6 +220,7 @@ static int dispatch_multi(const DecodeArgs& a, int kv, int workers, hipStream_t 
 }
 
 static int dispatch_stream(const DecodeArgs& a, int kv, int workers, hipStream_t s) {
+  if (a.pair) return a.head_dim == 128 ? run_stream_pair_d<128>(a, workers, s) : PKV_ERR_UNSUPPORTED;
   switch (a.head_dim) {
     case 32: return stream_d<32>(a, kv, workers, s);
     case 64: return stream_d<64>(a, kv, workers, s);
@@ -285,6 +301,14 @@ static int prepare(DecodeArgs& a, void* out, const void* q, int q_dtype, int row
   a.num_q_heads = hq;
   a.num_kv_heads = cache->num_kv_heads;
   a.group = hq / cache->num_kv_heads;
+  a.pair = 0;
+  if (plan->scheme == 1 && plan->heads_per_item == 2 * a.group && row_mode != 3) {
+    // INT4 pair items (checked by check_plan): the kernels see Hkv / 2 heads
+    // of two heads' rows each, every item holding both heads' query heads
+    a.pair = 1;
+    a.num_kv_heads /= 2;
+    a.group *= 2;
+  }
   a.sub_groups = a.group / plan->heads_per_item;
   a.head_dim = cache->head_dim;
   a.kbase = reinterpret_cast<const char*>(cache->k);

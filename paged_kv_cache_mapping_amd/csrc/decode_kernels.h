@@ -82,6 +82,7 @@ struct DecodeArgs {
   int32_t trail_pct;        // share of the other workers, percent of a full share
   int32_t lds_budget;       // bytes of LDS one worker may take
   int32_t qt;               // row mode 3: query tokens one item holds (else 1)
+  int32_t pair;             // INT4: items span two adjacent KV heads (see kInt4Pair)
 };
 
 // What one row attends to.
@@ -843,15 +844,25 @@ __global__ __launch_bounds__(64) void decode_split_uni_kernel(DecodeArgs a) {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+// INT4 work items over two adjacent KV heads.  A 64-byte INT4 head row is
+// half a 128-byte line, and the two halves belong to different items that
+// different waves read at different times: the line was fetched twice (136.8
+// MB per launch against 67.1 MB of K/V).  A pair item reads whole lines: its
+// first GT / 2 rows are the query heads of the first KV head, the rest those
+// of the second; the kernel sees the cache as Hkv / 2 heads of 128-byte rows.
+constexpr int kInt4Pair = 0x100 | PKV_INT4;
+
 template <int D, int GT, int KV>
 struct MfmaShape {
+  static constexpr bool kPair = KV == kInt4Pair;
   static constexpr int kBits = kv_bits(KV);          // 16 bf16, 8 fp8, 4 int4
-  static constexpr int kRowBytes = D * kBits / 8;    // one token of one KV head
+  static constexpr int kHeadBytes = D * kBits / 8;   // one token of one KV head
+  static constexpr int kRowBytes = kHeadBytes * (kPair ? 2 : 1);   // one token of an item
   static constexpr int NC = D / 32;                  // MFMA k-chunks
-  // V: bytes per lane and load; INT4 takes 8 (16 elements), so that a lane
-  // accumulates as many elements per row as with fp8
-  static constexpr int kVBytes = KV == PKV_INT4 ? 8 : 16;
-  static constexpr int VLPR = kRowBytes / kVBytes;   // V: lanes per row
+  // V: bytes per lane and load; INT4 takes 4 (8 elements, a 16-lane row per
+  // token), so that a lane accumulates as many elements per row as with bf16
+  static constexpr int kVBytes = kBits == 4 ? 4 : 16;
+  static constexpr int VLPR = kHeadBytes / kVBytes;  // V: lanes per row
   static constexpr int VRPW = kWave / VLPR;          // V: rows per load
   static constexpr int VU = 16 / VRPW;               // V: loads per 16-token step
   static constexpr int VEPL = kVBytes * 8 / kBits;   // V: elements per lane
@@ -861,7 +872,8 @@ struct MfmaShape {
   static constexpr int QL = (QE + 8 * kWave - 1) / (8 * kWave);  // 16-byte loads per lane
   static_assert(VRPW <= 16 && VU * VRPW == 16, "V layout");
   static_assert(GT <= 16, "at most 16 query heads per item");
-  static_assert(KV != PKV_INT4 || D % 128 == 0, "INT4 rows span whole 64-byte K loads");
+  static_assert(kBits != 4 || D % 128 == 0, "INT4 rows span whole 64-byte K loads");
+  static_assert(!kPair || GT % 2 == 0, "pair items hold both heads' rows");
 };
 
 // INT4 K words for the matrix cores.  A word holds elements n = 0..7 of a
@@ -871,14 +883,28 @@ struct MfmaShape {
 // -200 * sum(q) to give (u - 8) . q.  The four dwords hold elements in the
 // order 0, 2, 4, 6, 1, 3, 5, 7; the query operand is permuted to match
 // (int4_q_perm).
+// v_perm_b32 selects bytes of {S0 (high), S1 (low)}: selector 0..3 picks a
+// byte of S1, 4..7 a byte of S0, 0x0C gives zero.
 __device__ __forceinline__ uint4 int4_k_bf16(uint32_t w) {
   const uint32_t x = (w & 0x0F0F0F0Fu) | 0x40404040u;          // bytes 0x40|u0, u2, u4, u6
   const uint32_t y = ((w >> 4) & 0x0F0F0F0Fu) | 0x40404040u;   // bytes 0x40|u1, u3, u5, u7
-  constexpr uint32_t kHi = 0x43004300u;                        // high bytes of both halves
-  return make_uint4((x & 0xFFu) | ((x << 8) & 0xFF0000u) | kHi,
-                    ((x >> 16) & 0xFFu) | ((x >> 8) & 0xFF0000u) | kHi,
-                    (y & 0xFFu) | ((y << 8) & 0xFF0000u) | kHi,
-                    ((y >> 16) & 0xFFu) | ((y >> 8) & 0xFF0000u) | kHi);
+  constexpr uint32_t kHi = 0x43434343u;                        // the high byte of each bf16
+  return make_uint4(__builtin_amdgcn_perm(x, kHi, 0x00050004u), __builtin_amdgcn_perm(x, kHi, 0x00070006u),
+                    __builtin_amdgcn_perm(y, kHi, 0x00050004u), __builtin_amdgcn_perm(y, kHi, 0x00070006u));
+}
+
+// INT4 V for the packed fp16 dot products: element n of two tokens' words
+// a and b (same dimensions) as the fp16 pair (1024 + u_a, 1024 + u_b)
+// (exponent of 1024, mantissa u, exact); out[n] for n = 0..7.
+__device__ __forceinline__ void int4_v_f16_pairs(uint32_t a, uint32_t b, uint32_t (&out)[8]) {
+  const uint32_t xa = a & 0x0F0F0F0Fu, xb = b & 0x0F0F0F0Fu;                  // even elements
+  const uint32_t ya = (a >> 4) & 0x0F0F0F0Fu, yb = (b >> 4) & 0x0F0F0F0Fu;    // odd elements
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t sel = 0x0C000C00u | ((4u + j) << 16) | (uint32_t)j;        // a.b_j, 0, b.b_j, 0
+    out[2 * j] = __builtin_amdgcn_perm(xb, xa, sel) | 0x64006400u;
+    out[2 * j + 1] = __builtin_amdgcn_perm(yb, ya, sel) | 0x64006400u;
+  }
 }
 
 // Eight query elements (pairs q0q1, q2q3, q4q5, q6q7) into the order of
@@ -957,7 +983,10 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
   using S = MfmaShape<D, GT, KV>;
   constexpr int NC = S::NC, VLPR = S::VLPR, VRPW = S::VRPW, VU = S::VU, VEPL = S::VEPL;
   constexpr int KB = S::KB, RG = S::RG;
-  constexpr bool kI4 = KV == PKV_INT4;
+  constexpr bool kI4 = S::kBits == 4;
+  constexpr bool kPair = S::kPair;
+  constexpr int NH = kPair ? 2 : 1;                  // KV heads of an item
+  static_assert(!kPair || QT == 1, "pair items are single-query");
   // MFMA rows of an item: (query token t, head h) as row t * GT + h
   constexpr int RI = GT * QT;
   constexpr int QE = RI * D;                                   // query elements of one piece
@@ -1172,12 +1201,12 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
       }
     }
     if constexpr (kI4) {
-      // V held the nibbles u; the values are u - 8: take 8 times each row's
-      // probability sum off its accumulator
+      // V entered as 1024 + u; the values are u - 8: take 1032 times each
+      // row's weight sum off its accumulator
 #pragma unroll
       for (int h = 0; h < RI; ++h)
 #pragma unroll
-        for (int e = 0; e < VEPL; ++e) acc[h][e] = fmaf(-8.0f, lh[h], acc[h][e]);
+        for (int e = 0; e < VEPL; ++e) acc[h][e] = fmaf(-1032.0f, lh[h], acc[h][e]);
     }
     if (vg == 0) {
       if (npieces == 1) {
@@ -1233,10 +1262,10 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
     }
   };
 
-  using VT = std::conditional_t<S::kVBytes == 16, uint4, uint2>;
+  using VT = std::conditional_t<S::kVBytes == 16, uint4, std::conditional_t<S::kVBytes == 8, uint2, uint32_t>>;
   struct Buf {
-    uint32_t k[NC][KB / 4];
-    VT v[VU];
+    uint32_t k[NC * NH][KB / 4];   // chunks of the item's first KV head, then the second's
+    VT v[VU][NH];
   };
 
   for (long long wbase = u_lo; wbase < u_hi; wbase += kWave) {
@@ -1342,10 +1371,13 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
       const char* vp = a.vbase + off;
       if constexpr (kI4) {
 #pragma unroll
-        for (int j = 0; j < NC / 4; ++j) {
-          const uint4 t = *reinterpret_cast<const uint4*>(kp + k_lane + j * 64);
-          bf.k[4 * j][0] = t.x; bf.k[4 * j + 1][0] = t.y; bf.k[4 * j + 2][0] = t.z; bf.k[4 * j + 3][0] = t.w;
-        }
+        for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+          for (int j = 0; j < NC / 4; ++j) {
+            const uint4 t = *reinterpret_cast<const uint4*>(kp + k_lane + hh * S::kHeadBytes + j * 64);
+            const int c0 = hh * NC + 4 * j;
+            bf.k[c0][0] = t.x; bf.k[c0 + 1][0] = t.y; bf.k[c0 + 2][0] = t.z; bf.k[c0 + 3][0] = t.w;
+          }
       } else {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
@@ -1360,7 +1392,10 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
       }
 #pragma unroll
       for (int u = 0; u < VU; ++u)
-        bf.v[u] = *reinterpret_cast<const VT*>(vp + v_lane + (int64_t)u * (RB ? TPRV : VRPW) * row_bytes);
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh)
+          bf.v[u][hh] = *reinterpret_cast<const VT*>(vp + v_lane + hh * S::kHeadBytes +
+                                                    (int64_t)u * (RB ? TPRV : VRPW) * row_bytes);
     };
 
     // V as floats, zero for keys outside the piece's span
@@ -1421,6 +1456,19 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
         const uint4 kw = k_operand(bf, c);
         sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kw), qa[c], sc, 0, 0, 0);
       }
+      if constexpr (kPair) {
+        // the second KV head's keys against the same query rows; its rows
+        // are the upper half
+        f32x4_t sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const uint4 kw = k_operand(bf, NC + c);
+          sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kw), qa[c], sb, 0, 0, 0);
+        }
+        const bool upper = (lane % 16) >= GT / 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[i] = upper ? sb[i] : sc[i];
+      }
       // lane l: tokens 4 (l / 16) + i of head l % 16
       float z[4];
 #pragma unroll
@@ -1459,15 +1507,42 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
       for (int i = 0; i < 4; ++i) {
         float p = __builtin_amdgcn_exp2f(z[i] - m1);
         if constexpr (!full) p = z[i] == -INFINITY ? 0.f : p;
+        // INT4: the weights enter fp16 dot products; the sum takes the same
+        // rounded weights, so the softmax stays normalised
+        if constexpr (kI4) p = (float)(_Float16)p;
         pv[i] = p;
         ls1 += p;
       }
+      if constexpr (kI4) {
+        // load u of a 16-token step gives this lane token 4 R + u at 8
+        // dimensions; tokens (4 R, 4 R + 1) and (4 R + 2, 4 R + 3) form the
+        // fp16 pairs, weighted by the row's probabilities (broadcast from its
+        // lane).  Keys outside the piece have weight 0 and finite values.
+        static_assert(VU == 4 && TPRV == 1 && VEPL == 8, "INT4 step layout");
+        uint32_t vpair[NH][2][8];
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) {
+          int4_v_f16_pairs(bf.v[0][hh], bf.v[1][hh], vpair[hh][0]);
+          int4_v_f16_pairs(bf.v[2][hh], bf.v[3][hh], vpair[hh][1]);
+        }
+        static_for<0, RI>([&](auto hc) __attribute__((always_inline)) {
+          constexpr int h = decltype(hc)::value;
+          constexpr int hh = (kPair && h >= GT / 2) ? 1 : 0;   // the row's KV head
+          const auto p01 = __builtin_amdgcn_cvt_pkrtz(row_bcast<h>(pv[0]), row_bcast<h>(pv[1]));   // exact
+          const auto p23 = __builtin_amdgcn_cvt_pkrtz(row_bcast<h>(pv[2]), row_bcast<h>(pv[3]));
+#pragma unroll
+          for (int e = 0; e < VEPL; ++e) {
+            acc[h][e] = __builtin_amdgcn_fdot2(p01, __builtin_bit_cast(decltype(p01), vpair[hh][0][e]), acc[h][e], false);
+            acc[h][e] = __builtin_amdgcn_fdot2(p23, __builtin_bit_cast(decltype(p23), vpair[hh][1][e]), acc[h][e], false);
+          }
+        });
+      } else {
 #pragma unroll
       for (int u = 0; u < VU; ++u) {
         // this lane's V token: 4 R + u TPRV + (l % 16) / VLPR, probability slot u TPRV + ...
         const int sub = (lane % 16) / VLPR;
         float vf[VEPL];
-        v_floats(full_tag, p0, 4 * (lane / 16) + u * TPRV + sub, bf.v[u], vf);
+        v_floats(full_tag, p0, 4 * (lane / 16) + u * TPRV + sub, bf.v[u][0], vf);
         static_for<0, RI>([&](auto hc) __attribute__((always_inline)) {
           constexpr int h = decltype(hc)::value;
           float ph = row_bcast<h>(pv[u * TPRV]);
@@ -1480,14 +1555,14 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
           for (int e = 0; e < VEPL; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
         });
       }
+      }
     };
 
     auto body = [&](auto full_tag, int p0, const Buf& bf) __attribute__((always_inline)) {
       constexpr bool full = decltype(full_tag)::value;
       if constexpr (RB) {
         body_rb(full_tag, p0, bf);
-        return;
-      }
+      } else {
       f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -1542,7 +1617,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
       for (int u = 0; u < VU; ++u) {
         const int tok = u * VRPW + vg;                // token inside the step
         float vf[VEPL];
-        v_floats(full_tag, p0, tok, bf.v[u], vf);
+        v_floats(full_tag, p0, tok, bf.v[u][0], vf);
 #pragma unroll
         for (int h = 0; h < GT; ++h) {
           const int src = (tok + 16 * (h / 4)) * 4;
@@ -1551,6 +1626,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
 #pragma unroll
           for (int e = 0; e < VEPL; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
         }
+      }
       }
     };
 
@@ -1793,6 +1869,10 @@ void launch_stream(const DecodeArgs& a, int workers, hipStream_t s) {
   // flight raise the latency of all of them, and past 256 registers only one
   // wave fits on a SIMD)
   constexpr int kDepth = 1;
+  if constexpr (KV == kInt4Pair) {   // one variant: items of 2 .. 8 rows, two waves per SIMD
+    decode_flat_kernel_2w<D, GT, KV, kDepth, QT><<<workers, 64, lds, s>>>(a);
+    return;
+  }
   switch (a.kernel_variant) {
     case 2: decode_flat_kernel<D, GT, KV, 1, QT><<<workers, 64, lds, s>>>(a); break;
     case 3: decode_flat_kernel<D, GT, KV, 2, QT><<<workers, 64, lds, s>>>(a); break;
@@ -1804,7 +1884,9 @@ void launch_stream(const DecodeArgs& a, int workers, hipStream_t s) {
       // up to four rows per item the plan counts on two waves per SIMD, so
       // the kernel must fit in 256 registers (the fp8 build does not unless
       // asked); eight or more rows run one wave per SIMD
-      if constexpr (GT * QT <= 4) decode_flat_kernel_2w<D, GT, KV, kDepth, QT><<<workers, 64, lds, s>>>(a);
+      // (INT4 keeps 8 accumulators per row and lane: two waves up to 8 rows)
+      if constexpr (GT * QT <= (kv_bits(KV) == 4 ? 8 : 4))
+        decode_flat_kernel_2w<D, GT, KV, kDepth, QT><<<workers, 64, lds, s>>>(a);
       else decode_flat_kernel<D, GT, KV, kDepth, QT><<<workers, 64, lds, s>>>(a);
   }
 }
@@ -1827,6 +1909,17 @@ int run_stream_dk(const DecodeArgs& a, int workers, hipStream_t s) {
         }
         break;
     }
+  }
+  return PKV_ERR_UNSUPPORTED;
+}
+
+// INT4 pair items (a.pair): a.heads_per_item rows over two KV heads.
+template <int D>
+int run_stream_pair_d(const DecodeArgs& a, int workers, hipStream_t s) {
+  switch (a.heads_per_item) {
+    case 2: launch_stream<D, 2, kInt4Pair>(a, workers, s); return PKV_OK;
+    case 4: launch_stream<D, 4, kInt4Pair>(a, workers, s); return PKV_OK;
+    case 8: launch_stream<D, 8, kInt4Pair>(a, workers, s); return PKV_OK;
   }
   return PKV_ERR_UNSUPPORTED;
 }
@@ -1909,6 +2002,8 @@ int run_combine_d(const DecodeArgs& a, int ot, hipStream_t s) {
   EXT template int run_combine_d<D>(const DecodeArgs&, int, hipStream_t);
 #define PKV_DECODE_MULTI_INST(EXT, D, KV) \
   EXT template int run_multi_dk<D, KV>(const DecodeArgs&, int, hipStream_t);
+#define PKV_DECODE_PAIR_INST(EXT, D) \
+  EXT template int run_stream_pair_d<D>(const DecodeArgs&, int, hipStream_t);
 #define PKV_DECODE_MERGE_MULTI_INST(EXT, D) \
   EXT template int run_merge_multi_d<D>(const DecodeArgs&, int, hipStream_t);
 #define PKV_DECODE_ALL_D(EXT, D)                  \

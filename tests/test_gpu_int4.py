@@ -134,10 +134,11 @@ def _attend(w, window=0, split=None):
     return out, ref
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (8, 8), (16, 8), (64, 8), (32, 2), (64, 4)])
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (8, 8), (16, 8), (64, 8), (32, 2), (64, 4), (12, 3)])
 @pytest.mark.parametrize("bs", [16, 32])
 def test_decode_groups_and_block_sizes(Hq, Hkv, bs):
-    """Groups 1, 2, 4, 8, 16 (two items of 8 heads) over ragged lengths 1..700
+    """Groups 1, 2, 4 (items over two KV heads), 8, 16 (two items of 8 heads)
+    and an odd KV head count (single-head items) over ragged lengths 1..700
     (single tokens, partial blocks, several pieces per row)."""
     say("int4 decode", Hq, Hkv, bs)
     w = _small(700 + Hq + Hkv + bs, 9, 1, 700, Hq, Hkv, bs)
@@ -159,6 +160,27 @@ def test_decode_split_plans(split):
     say("int4 decode split", split)
     w = _small(900 + split, 13, 200, 1500, 32, 8, 16)
     out, ref = _attend(w, split=split)
+    assert max_err(out_f64(out), ref) <= TOL
+
+
+@pytest.mark.parametrize("hpi", [4, 8])
+def test_single_head_and_pair_items_agree_with_the_oracle(hpi):
+    """Group 4: the planner's items over two KV heads (8 rows) and forced
+    single-head items (4 rows) both match the oracle."""
+    say("int4 items", hpi)
+    w = _small(990, 10, 100, 1200, 32, 8, 16)
+    d = w.device()
+    plan = pkv.decode_plan(w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len)
+    assert plan.heads_per_item == 8
+    pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len, heads_per_item=hpi)
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d.q)
+    pkv.paged_attention_decode_partials(d.q, d.cache, d.block_table, d.seq_lens, w.max_seq_len, w.scale,
+                                        plan, ws, out)
+    pkv.paged_attention_decode_combine(out, d.seq_lens, w.block_size, plan, ws)
+    torch.cuda.synchronize()
+    ref = attention.paged_decode(w.q, "bf16", w.k_plane, w.v_plane, "int4", w.block_table, w.seq_lens,
+                                 w.scale, k_scale=w.k_scale, v_scale=w.v_scale)
     assert max_err(out_f64(out), ref) <= TOL
 
 
