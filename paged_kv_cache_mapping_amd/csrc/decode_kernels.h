@@ -1700,18 +1700,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 // head l / LPH of the group and DPL consecutive dims, so it reads one (m, l)
 // pair and one run of acc per piece and merges online, eight pieces' loads
 // in flight at a time (the first eight issued with the piece count).
+// Rows of an item one merge wave takes: items of more than 4 rows are merged
+// by several waves (more waves in flight, fewer loads per lane).
+__host__ __device__ constexpr int merge_rows_per_wave(int rows) { return rows > 4 ? 4 : rows; }
+
 template <int D, int GT, int OT, int QT = 1>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   constexpr int RI = GT * QT;                       // rows of an item: (token, head)
-  constexpr int LPH = kWave / RI;                   // lanes per row
+  constexpr int RW = merge_rows_per_wave(RI);       // rows one wave merges
+  constexpr int LPH = kWave / RW;                   // lanes per row
   constexpr int DPL = D >= LPH ? D / LPH : 1;       // dims per lane
   constexpr int U = 8;                              // pieces per round of loads
   const int lane = threadIdx.x;
   const int groups = a.num_q_heads / GT;
-  const int b = blockIdx.x / groups;
-  const int g = blockIdx.x % groups;
+  const int item = blockIdx.x / (RI / RW);
+  const int b = item / groups;
+  const int g = item % groups;
   const int64_t rg = (int64_t)b * groups + g;
-  const int h = lane / LPH;
+  const int h = (blockIdx.x % (RI / RW)) * RW + lane / LPH;
   const int d0 = (lane % LPH) * DPL;
   const bool active = d0 < D;
   const float* ml = a.ws_m + rg * a.max_splits * (2 * RI);
@@ -1926,7 +1932,8 @@ int run_stream_pair_d(const DecodeArgs& a, int workers, hipStream_t s) {
 
 template <int D, int GT, int QT = 1>
 void launch_merge(const DecodeArgs& a, int ot, hipStream_t s) {
-  const dim3 grid((unsigned)((long long)a.num_rows * (a.num_q_heads / GT)));
+  constexpr int kWaves = GT * QT / merge_rows_per_wave(GT * QT);   // waves per item
+  const dim3 grid((unsigned)((long long)a.num_rows * (a.num_q_heads / GT) * kWaves));
   if (ot == PKV_F32) decode_merge_kernel<D, GT, PKV_F32, QT><<<grid, 64, 0, s>>>(a);
   else decode_merge_kernel<D, GT, PKV_BF16, QT><<<grid, 64, 0, s>>>(a);
 }
