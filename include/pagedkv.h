@@ -356,8 +356,8 @@ PKV_API int pkv_chunked_workspace_size(int32_t num_tokens, int32_t num_reqs,
  * sliding_window   0, or W: keys >= p - W + 1 only.
  * workspace        at least pkv_chunked_workspace_size(...) bytes.
  * Invalid rows (q_len > seq_len, lengths out of range, missing blocks) get NaN.
- * INT4 caches: the decode form's shapes, and steps whose requests have at
- * most 8 query tokens; a longer request returns PKV_ERR_UNSUPPORTED.
+ * INT4 caches: the decode form's shapes (head_dim 128); others return
+ * PKV_ERR_UNSUPPORTED.
  */
 PKV_API int pkv_paged_attention_chunked(void* out, const void* q, int32_t q_dtype,
                                 int32_t num_tokens, int32_t num_q_heads,

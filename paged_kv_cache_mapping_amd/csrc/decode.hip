@@ -610,8 +610,9 @@ extern "C" int pkv_paged_attention_chunked(void* out, const void* q, int32_t q_d
     pa.causal = causal != 0;
     pa.window = sliding_window;
     const float log2e = 1.4426950408889634f;
-    pa.scale_log2 = softmax_scale * log2e * (cache->dtype == PKV_FP8_E4M3 ? cache->k_scale : 1.0f);
-    pa.v_scale = cache->dtype == PKV_FP8_E4M3 ? cache->v_scale : 1.0f;
+    const bool scaled = cache->dtype == PKV_FP8_E4M3 || cache->dtype == PKV_INT4;
+    pa.scale_log2 = softmax_scale * log2e * (scaled ? cache->k_scale : 1.0f);
+    pa.v_scale = scaled ? cache->v_scale : 1.0f;
     pa.part = reinterpret_cast<float*>(ws + p.single_bytes);
     st = launch_prefill(pa, cache->dtype, cache->head_dim, stream);
     if (st != PKV_OK) return st;

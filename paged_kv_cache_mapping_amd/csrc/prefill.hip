@@ -254,7 +254,7 @@ __device__ __forceinline__ void pf_piece(const PrefillArgs& a, char* lds, const 
   constexpr int NBW = S::NBW, TPN = S::TPN, TW = S::TW, TWG = S::TWG;
   constexpr int NC = S::NC, MB = S::MB, RSK = S::RSK, RSV = S::RSV, TILE = S::TILE;
   constexpr int CPR = S::CPR, CPT = S::CPT, CPTH = S::CPTH;
-  constexpr int kElt = KV == PKV_BF16 ? 2 : 1;
+  constexpr int kBits = kv_bits(KV);                    // 16 bf16, 8 fp8, 4 int4
   int* tab = reinterpret_cast<int*>(lds + 2 * TILE);   // phys block or -1, from block b0
 
   const int tid = threadIdx.x;
@@ -353,10 +353,12 @@ __device__ __forceinline__ void pf_piece(const PrefillArgs& a, char* lds, const 
   // ---- staging: chunk c = tid + 512 j of a tile is key c / CPR, 16 bytes
   // (8 bf16) at column chunk c % CPR; keys outside [klo, khi] or on an
   // unmapped block stage as zeros
-  const int64_t blk_bytes = a.block_stride * kElt;
-  const int row_bytes = a.num_kv_heads * D * kElt;
+  const int64_t blk_bytes = a.block_stride * kBits / 8;
+  const int row_bytes = a.num_kv_heads * D * kBits / 8;
   const int bmask = (1 << a.bs_log2) - 1;
-  typedef typename std::conditional<KV == PKV_BF16, uint4, uint2>::type Raw;
+  // 8 elements of the cache: 16 bytes bf16, 8 fp8, 4 int4
+  typedef typename std::conditional<kBits == 16, uint4,
+                                    typename std::conditional<kBits == 8, uint2, uint32_t>::type>::type Raw;
   // Loads are issued unconditionally (keys outside [klo, khi] or on unmapped
   // blocks read block 0's first row, which always exists) and their data is
   // dropped afterwards: a load skipped under a branch would leave the wait
@@ -375,8 +377,8 @@ __device__ __forceinline__ void pf_piece(const PrefillArgs& a, char* lds, const 
       const int phys = in ? tab[(kp >> a.bs_log2) - b0] : -1;
       const bool ok = phys >= 0;
       const int64_t off = ok ? (int64_t)phys * blk_bytes + (int64_t)(kp & bmask) * row_bytes +
-                                   kvh * D * kElt + cc * 8 * kElt
-                             : (int64_t)(cc * 8 * kElt);
+                                   kvh * D * kBits / 8 + cc * kBits
+                             : (int64_t)(cc * kBits);
       st.k[j] = *reinterpret_cast<const Raw*>(a.kbase + off);
       st.v[j] = *reinterpret_cast<const Raw*>(a.vbase + off);
       st.ok[j] = ok;
@@ -385,6 +387,17 @@ __device__ __forceinline__ void pf_piece(const PrefillArgs& a, char* lds, const 
   auto widen = [&](const Raw& x) __attribute__((always_inline)) -> uint4 {
     if constexpr (KV == PKV_BF16) {
       return x;
+    } else if constexpr (KV == PKV_INT4) {
+      // nibble n (element n) holds u; the staged value is the integer u - 8,
+      // exact in bf16 (the scales are applied to the scores and the output)
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = (float)((int)((x >> (8 * i)) & 0xFu) - 8);
+        const float hi = (float)((int)((x >> (8 * i + 4)) & 0xFu) - 8);
+        w[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+      }
+      return make_uint4(w[0], w[1], w[2], w[3]);
     } else {
       return make_uint4(e4m3x2_to_bf16x2<false>(x.x), e4m3x2_to_bf16x2<true>(x.x),
                         e4m3x2_to_bf16x2<false>(x.y), e4m3x2_to_bf16x2<true>(x.y));
@@ -767,8 +780,9 @@ int pf_max_blocks(int max_seq_len, int bs, int window, int tokens) {
 
 bool prefill_supported(int kv_dtype, int head_dim, int group, int max_seq_len, int block_size,
                        int window, int max_query_len) {
-  if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3) return false;
+  if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3 && kv_dtype != PKV_INT4) return false;
   if (head_dim != 64 && head_dim != 128) return false;   // 256: tiles exceed 64 KiB of LDS
+  if (kv_dtype == PKV_INT4 && head_dim != 128) return false;   // the INT4 head size built
   if (group < 1 || group > 16 || 16 % group) return false;
   if (max_query_len < 2) return false;
   const int tok = pf_tokens(head_dim, group);
@@ -805,7 +819,9 @@ int launch_prefill(const PrefillArgs& a0, int kv_dtype, int head_dim, hipStream_
   const bool bf = kv_dtype == PKV_BF16;
   switch (head_dim) {
     case 64: return bf ? pf_launch_g<64, PKV_BF16>(a, g, s) : pf_launch_g<64, PKV_FP8_E4M3>(a, g, s);
-    case 128: return bf ? pf_launch_g<128, PKV_BF16>(a, g, s) : pf_launch_g<128, PKV_FP8_E4M3>(a, g, s);
+    case 128:
+      if (kv_dtype == PKV_INT4) return pf_launch_g<128, PKV_INT4>(a, g, s);
+      return bf ? pf_launch_g<128, PKV_BF16>(a, g, s) : pf_launch_g<128, PKV_FP8_E4M3>(a, g, s);
   }
   return PKV_ERR_UNSUPPORTED;
 }

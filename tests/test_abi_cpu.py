@@ -138,8 +138,10 @@ def test_argument_checks_return_before_launching(lib):
     assert lib.pkv_paged_attention_decode(0x100, 0x100, _lib.PKV_BF16, 4, 32, ctypes.byref(ci4), 0x100, 8,
                                           0x100, 64, 0.1, 0, None, 0, None) == _lib.PKV_ERR_UNSUPPORTED
     ws = ctypes.c_size_t(0)
-    assert lib.pkv_chunked_workspace_size(64, 4, 32, 8, 128, 16, _lib.PKV_INT4, 40, 512, 0,
+    assert lib.pkv_chunked_workspace_size(64, 4, 32, 8, 64, 16, _lib.PKV_INT4, 40, 512, 0,
                                           ctypes.byref(ws)) == _lib.PKV_ERR_UNSUPPORTED
+    assert lib.pkv_chunked_workspace_size(64, 4, 32, 8, 128, 16, _lib.PKV_INT4, 40, 512, 0,
+                                          ctypes.byref(ws)) == _lib.PKV_OK
     assert lib.pkv_chunked_workspace_size(64, 16, 32, 8, 128, 16, _lib.PKV_INT4, 8, 512, 0,
                                           ctypes.byref(ws)) == _lib.PKV_OK and ws.value > 0
     # block copy: bad cache, negative or empty pair lists, missing id arrays

@@ -1,7 +1,7 @@
 """GPU parity for the INT4 KV cache (half a byte per element; Worker-Side KV
 Init (zh), § KV Cache技术背景): the codec, the cache write and block copies
-bit-exact against the oracle; decode and short multi-query attention against
-the oracle's attention over the same codes.
+bit-exact against the oracle; decode, short multi-query and prefill-chunk
+attention against the oracle's attention over the same codes.
 
 Tolerance: the oracle attends over the dequantised codes in float64, so the
 kernels differ from it only by their own arithmetic -- bf16 query, exact
@@ -259,10 +259,12 @@ def test_chunked_short_multi_query_requests(Hq, Hkv, qmax, causal, W):
     assert max_err(out_f64(out), ref) <= TOL
 
 
-def test_chunked_long_queries_are_refused():
-    """Requests of more than 8 query tokens have no INT4 kernel: the call
-    reports it and launches nothing."""
-    say("int4 chunked long")
-    c = _int4_chunk_case(1300, 4, 300, 40, 32, 8)
-    with pytest.raises(pkv.PkvError):
-        _run_int4_chunked(c, True, 0)
+@pytest.mark.parametrize("causal,W", [(True, 0), (True, 64), (False, 0)])
+def test_chunked_prefill_chunks(causal, W):
+    """Requests with up to 90 query tokens: the matrix-core prefill kernel
+    stages INT4 tiles widened to the integers u - 8 (scales on the scores and
+    the output); single-query rows on the decode kernels."""
+    say("int4 chunked prefill", causal, W)
+    c = _int4_chunk_case(1300 + W + causal, 6, 600, 90, 32, 8)
+    out, ref = _run_int4_chunked(c, causal, W)
+    assert max_err(out_f64(out), ref) <= TOL
