@@ -62,10 +62,12 @@ constexpr int kTrailPct = 80;            // second wave on a SIMD: share in perc
 constexpr int kLdsPerCU = 160 * 1024;
 
 // Resident waves per CU for the balanced kernels: two per SIMD while the
-// registers allow it (up to four query heads per item; eight with INT4,
-// whose lanes keep 8 accumulators per row), else one.
-static int stream_waves_per_cu(int heads_per_item, int kv_dtype) {
-  return heads_per_item <= (kv_dtype == PKV_INT4 ? 8 : 4) ? 8 : 4;
+// registers allow it (two_waves: 4 rows per item; 8 with INT4, whose lanes
+// keep 8 accumulators per row; 16 where P.V accumulates in the matrix
+// cores), else one.  Multi-token plans count rows as heads (qt unknown
+// here: any qt > 1 behaves alike).
+static int stream_waves_per_cu(int heads_per_item, int kv_dtype, int d, bool multi) {
+  return two_waves(d, kv_dtype, multi ? 1 : heads_per_item, multi ? heads_per_item : 1) ? 8 : 4;
 }
 
 static size_t partial_bytes(int rows, int hq, int splits, int d) {
@@ -97,7 +99,7 @@ static int make_plan(int rows, int hq, int hkv, int d, int bs, int kv_dtype, int
   if (allow_stream && mfma_eligible(kv_dtype, d, bs) && gm > 0 && rows <= kMaxStreamRows) {
     // balanced partition over resident wave slots
     const long long units = (long long)(rows > 0 ? rows : 1) * (hq / gm) * nvis;
-    const int per_cu = stream_waves_per_cu(gm, kv_dtype);
+    const int per_cu = stream_waves_per_cu(gm, kv_dtype, d, force_hpi > 0);
     long long workers = cus * per_cu;
     const long long need = (units + kStreamMinUnits - 1) / kStreamMinUnits;
     plan->lead_workers = 0;

@@ -843,6 +843,13 @@ __global__ __launch_bounds__(64) void decode_split_uni_kernel(DecodeArgs a) {
 // query heads per item.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));   // 4 bf16, 16x16x16 MFMA operand
+
+// P.V on the matrix cores: bf16 caches of head size 128, except single-query
+// items of 8 rows (see decode_flat_body).
+__host__ __device__ constexpr bool mfma_pv(int d, int kv, int gt, int qt) {
+  return kv == PKV_BF16 && d == 128 && !(gt == 8 && qt == 1);
+}
 
 // INT4 work items over two adjacent KV heads.  A 64-byte INT4 head row is
 // half a 128-byte line, and the two halves belong to different items that
@@ -1002,6 +1009,16 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
   constexpr bool RB = VLPR <= 16;
   constexpr int TPRV = RB ? 16 / VLPR : 1;          // V tokens per 16-lane row and load
   static_assert(QT == 1 || RB, "multi-token items need the row-broadcast scheme");
+  // P.V on the matrix cores (bf16, head size 128): the score MFMA leaves this
+  // lane's weights where the A operand of v_mfma_f32_16x16x16_bf16 wants them
+  // (row l % 16, tokens 4 (l / 16) + i), and with output column n of tile t
+  // standing for dimension 8 n + t the lane's own V loads (tokens 4 R + u,
+  // dimensions 8 (l % 16) .. + 7) are the B operand: no data moves.  The
+  // lane then holds rows 4 R + i at dimensions 8 (l % 16) .. + 7.  P enters
+  // as a bf16 high part plus a bf16 remainder.  Single-query items of 8 rows
+  // keep the vector ALUs (measured faster there: 102-106 against 108-117 us
+  // on 32 x 4096 tokens with 64 query heads).
+  constexpr bool kMPV = mfma_pv(D, KV, GT, QT) && RB && VLPR == 16 && VU == 4 && VEPL == 8;
   extern __shared__ __align__(16) char lds[];
   const FlatLds L = flat_lds_layout(a.num_rows, RI, D, a.lds_budget);
   int* cum = reinterpret_cast<int*>(lds + L.cum_off);     // cum[r]: visible blocks of rows < r
@@ -1060,7 +1077,8 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
   long long s_first = 0;
   bool s_bad = false;
   bf16x8_t qa[NC];
-  float acc[RI][VEPL];
+  float acc[kMPV ? 1 : RI][VEPL];     // vector-ALU P.V: row h, this lane's elements
+  f32x4_t accm[kMPV ? VEPL : 1];      // matrix-core P.V: tile t, rows 4 R + i
   float m[GT];
   f32x4_t lsum = {0.f, 0.f, 0.f, 0.f};
   float m1 = -INFINITY, ls1 = 0.f;   // row-broadcast scheme: head lane % 16's max and sum
@@ -1145,10 +1163,15 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
     }
 #pragma unroll
     for (int h = 0; h < GT; ++h) m[h] = -INFINITY;
+    if constexpr (kMPV) {
 #pragma unroll
-    for (int h = 0; h < RI; ++h)
+      for (int t = 0; t < VEPL; ++t) accm[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    } else {
 #pragma unroll
-      for (int e = 0; e < VEPL; ++e) acc[h][e] = 0.f;
+      for (int h = 0; h < RI; ++h)
+#pragma unroll
+        for (int e = 0; e < VEPL; ++e) acc[h][e] = 0.f;
+    }
     lsum[0] = lsum[1] = lsum[2] = lsum[3] = 0.f;
     m1 = -INFINITY;
     ls1 = 0.f;
@@ -1165,21 +1188,30 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
     if (s_bad) {
 #pragma unroll
       for (int h = 0; h < GT; ++h) m[h] = 0.f;
+      if constexpr (kMPV) {
+        const float qn = __builtin_nanf("");
 #pragma unroll
-      for (int h = 0; h < RI; ++h)
+        for (int t = 0; t < VEPL; ++t) accm[t] = f32x4_t{qn, qn, qn, qn};
+      } else {
 #pragma unroll
-        for (int e = 0; e < VEPL; ++e) acc[h][e] = __builtin_nanf("");
+        for (int h = 0; h < RI; ++h)
+#pragma unroll
+          for (int e = 0; e < VEPL; ++e) acc[h][e] = __builtin_nanf("");
+      }
       lsum[0] = lsum[1] = lsum[2] = lsum[3] = __builtin_nanf("");
       m1 = 0.f;
       ls1 = __builtin_nanf("");
     }
     // the V layout's token groups hold partial sums under the same maxima
+    // (the matrix-core form sums all tokens inside the products)
+    if constexpr (!kMPV) {
 #pragma unroll
-    for (int step = VLPR; step < kWave; step <<= 1)
+      for (int step = VLPR; step < kWave; step <<= 1)
 #pragma unroll
-      for (int h = 0; h < RI; ++h)
+        for (int h = 0; h < RI; ++h)
 #pragma unroll
-        for (int e = 0; e < VEPL; ++e) acc[h][e] += shfl_xor_t(acc[h][e], step);
+          for (int e = 0; e < VEPL; ++e) acc[h][e] += shfl_xor_t(acc[h][e], step);
+    }
     float lh[RI], mh[RI];   // each row's sum and max
     if constexpr (RB) {
       float lt = ls1;
@@ -1208,7 +1240,37 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
 #pragma unroll
         for (int e = 0; e < VEPL; ++e) acc[h][e] = fmaf(-1032.0f, lh[h], acc[h][e]);
     }
-    if (vg == 0) {
+    if constexpr (kMPV) {
+      // lane (R, c): rows 4 R + i, dimensions 8 c .. 8 c + 7
+      const int R = lane / 16, c = lane % 16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * R + i;
+        if (r >= RI) continue;
+        float lr = lh[i < RI ? i : 0];
+#pragma unroll
+        for (int rr = 1; rr < 4; ++rr)
+          if (4 * rr + i < RI && R == rr) lr = lh[(4 * rr + i) % RI];
+        if (npieces == 1) {
+          if (r / GT >= s_ql) continue;
+          const int64_t out_row = ((int64_t)(s_tok + r / GT) * a.num_q_heads + h0 + r % GT) * D;
+          const float inv = a.v_scale / lr;
+          float o[VEPL];
+#pragma unroll
+          for (int t = 0; t < VEPL; ++t) o[t] = accm[t][i] * inv;
+          store_out<PKV_BF16, VEPL>(a.out, out_row + c * VEPL, o);
+        } else {
+          const int64_t pr = (((int64_t)b * kvgroups + kvg) * RI + r) * a.max_splits + piece;
+          float* dst = a.ws_acc + pr * D + c * VEPL;
+#pragma unroll
+          for (int t = 0; t < VEPL; t += 4) {
+            const f32x4_t v4 = {accm[t][i] * a.v_scale, accm[t + 1][i] * a.v_scale,
+                                accm[t + 2][i] * a.v_scale, accm[t + 3][i] * a.v_scale};
+            __builtin_nontemporal_store(v4, reinterpret_cast<f32x4_t*>(dst + t));
+          }
+        }
+      }
+    } else if (vg == 0) {
       if (npieces == 1) {
         // row r = t * GT + h: query token t of the piece, head h0 + h
 #pragma unroll
@@ -1495,12 +1557,22 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
         const float alpha = grow ? __builtin_amdgcn_exp2f(m1 - mx) : 1.0f;   // 0 when m = -inf
         if (grow) m1 = mx;
         ls1 *= alpha;
-        static_for<0, RI>([&](auto hc) __attribute__((always_inline)) {
-          constexpr int h = decltype(hc)::value;
-          const float ah = row_bcast<h>(alpha);
+        if constexpr (kMPV) {
+          // this lane's rows 4 R + i take the factors of lanes 4 R + i
 #pragma unroll
-          for (int e = 0; e < VEPL; ++e) acc[h][e] *= ah;
-        });
+          for (int i = 0; i < 4; ++i) {
+            const float ai = __shfl(alpha, 4 * (lane / 16) + i);
+#pragma unroll
+            for (int t = 0; t < VEPL; ++t) accm[t][i] *= ai;
+          }
+        } else {
+          static_for<0, RI>([&](auto hc) __attribute__((always_inline)) {
+            constexpr int h = decltype(hc)::value;
+            const float ah = row_bcast<h>(alpha);
+#pragma unroll
+            for (int e = 0; e < VEPL; ++e) acc[h][e] *= ah;
+          });
+        }
       }
       float pv[4];
 #pragma unroll
@@ -1513,7 +1585,41 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
         pv[i] = p;
         ls1 += p;
       }
-      if constexpr (kI4) {
+      if constexpr (kMPV) {
+        uint32_t hi2[2], lo2[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint32_t h0b = f32_to_bf16_rne(pv[2 * j]), h1b = f32_to_bf16_rne(pv[2 * j + 1]);
+          const float r0 = pv[2 * j] - as_float(h0b << 16), r1 = pv[2 * j + 1] - as_float(h1b << 16);
+          hi2[j] = h0b | (h1b << 16);
+          lo2[j] = f32_to_bf16_rne(r0) | (f32_to_bf16_rne(r1) << 16);
+        }
+        const s16x4_t pa_hi = __builtin_bit_cast(s16x4_t, make_uint2(hi2[0], hi2[1]));
+        const s16x4_t pa_lo = __builtin_bit_cast(s16x4_t, make_uint2(lo2[0], lo2[1]));
+        // V rows of tokens 4 R + u; keys outside the piece's span are zeroed
+        // (their weights are 0, but the slots may hold anything)
+        uint32_t vw[4][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint4 raw = bf.v[u][0];
+          vw[u][0] = raw.x; vw[u][1] = raw.y; vw[u][2] = raw.z; vw[u][3] = raw.w;
+          if constexpr (!full) {
+            const int pos = p0 + 4 * (lane / 16) + u;
+            const bool live = pos >= s_lo && pos <= s_hi;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) vw[u][k] = live ? vw[u][k] : 0u;
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < VEPL; ++t) {
+          const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
+          const uint32_t b01 = __builtin_amdgcn_perm(vw[1][t / 2], vw[0][t / 2], sel);
+          const uint32_t b23 = __builtin_amdgcn_perm(vw[3][t / 2], vw[2][t / 2], sel);
+          const s16x4_t vb = __builtin_bit_cast(s16x4_t, make_uint2(b01, b23));
+          accm[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_hi, vb, accm[t], 0, 0, 0);
+          accm[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_lo, vb, accm[t], 0, 0, 0);
+        }
+      } else if constexpr (kI4) {
         // load u of a 16-token step gives this lane token 4 R + u at 8
         // dimensions; tokens (4 R, 4 R + 1) and (4 R + 2, 4 R + 3) form the
         // fp16 pairs, weighted by the row's probabilities (broadcast from its
@@ -1868,6 +1974,12 @@ int run_split_dk(const DecodeArgs& a, int gt, hipStream_t s) {
   return PKV_ERR_UNSUPPORTED;
 }
 
+// Whether the balanced kernel fits two waves per SIMD (256 registers) for
+// items of gt heads times qt query tokens.
+__host__ __device__ constexpr bool two_waves(int d, int kv, int gt, int qt) {
+  return mfma_pv(d, kv, gt, qt) ? gt * qt <= 16 : gt * qt <= (kv_bits(kv) == 4 ? 8 : 4);
+}
+
 template <int D, int GT, int KV, int QT = 1>
 void launch_stream(const DecodeArgs& a, int workers, hipStream_t s) {
   const size_t lds = flat_lds_layout(a.num_rows, GT * QT, D, a.lds_budget).bytes;
@@ -1890,8 +2002,9 @@ void launch_stream(const DecodeArgs& a, int workers, hipStream_t s) {
       // up to four rows per item the plan counts on two waves per SIMD, so
       // the kernel must fit in 256 registers (the fp8 build does not unless
       // asked); eight or more rows run one wave per SIMD
-      // (INT4 keeps 8 accumulators per row and lane: two waves up to 8 rows)
-      if constexpr (GT * QT <= (kv_bits(KV) == 4 ? 8 : 4))
+      // (INT4 keeps 8 accumulators per row and lane: two waves up to 8 rows;
+      // bf16 head size 128 accumulating in the matrix cores: up to 16)
+      if constexpr (two_waves(D, KV, GT, QT))
         decode_flat_kernel_2w<D, GT, KV, kDepth, QT><<<workers, 64, lds, s>>>(a);
       else decode_flat_kernel<D, GT, KV, kDepth, QT><<<workers, 64, lds, s>>>(a);
   }
