@@ -845,10 +845,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));   // 4 bf16, 16x16x16 MFMA operand
 
-// P.V on the matrix cores: bf16 caches of head size 128, except single-query
-// items of 8 rows (see decode_flat_body).
+// P.V on the matrix cores: bf16 and fp8 caches of head size 128 (fp8 widened
+// to bf16, exact), except single-query items of 8 rows (see decode_flat_body).
 __host__ __device__ constexpr bool mfma_pv(int d, int kv, int gt, int qt) {
-  return kv == PKV_BF16 && d == 128 && !(gt == 8 && qt == 1);
+  return (kv == PKV_BF16 || kv == PKV_FP8_E4M3) && d == 128 && !(gt == 8 && qt == 1);
 }
 
 // INT4 work items over two adjacent KV heads.  A 64-byte INT4 head row is
@@ -868,7 +868,8 @@ struct MfmaShape {
   static constexpr int NC = D / 32;                  // MFMA k-chunks
   // V: bytes per lane and load; INT4 takes 4 (8 elements, a 16-lane row per
   // token), so that a lane accumulates as many elements per row as with bf16
-  static constexpr int kVBytes = kBits == 4 ? 4 : 16;
+  // (fp8 at head size 128: 8, the bf16 lane layout for the matrix-core P.V)
+  static constexpr int kVBytes = kBits == 4 ? 4 : (kBits == 8 && D == 128 ? 8 : 16);
   static constexpr int VLPR = kHeadBytes / kVBytes;  // V: lanes per row
   static constexpr int VRPW = kWave / VLPR;          // V: rows per load
   static constexpr int VU = 16 / VRPW;               // V: loads per 16-token step
@@ -1601,8 +1602,14 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
         uint32_t vw[4][4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const uint4 raw = bf.v[u][0];
-          vw[u][0] = raw.x; vw[u][1] = raw.y; vw[u][2] = raw.z; vw[u][3] = raw.w;
+          if constexpr (KV == PKV_BF16) {
+            const uint4 raw = bf.v[u][0];
+            vw[u][0] = raw.x; vw[u][1] = raw.y; vw[u][2] = raw.z; vw[u][3] = raw.w;
+          } else {   // fp8 codes widened to bf16 pairs (exact; the V scale comes at the flush)
+            const uint2 raw = bf.v[u][0];
+            vw[u][0] = e4m3x2_to_bf16x2<false>(raw.x); vw[u][1] = e4m3x2_to_bf16x2<true>(raw.x);
+            vw[u][2] = e4m3x2_to_bf16x2<false>(raw.y); vw[u][3] = e4m3x2_to_bf16x2<true>(raw.y);
+          }
           if constexpr (!full) {
             const int pos = p0 + 4 * (lane / 16) + u;
             const bool live = pos >= s_lo && pos <= s_hi;
