@@ -845,10 +845,11 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));   // 4 bf16, 16x16x16 MFMA operand
 
-// P.V on the matrix cores: bf16 and fp8 caches of head size 128 (fp8 widened
-// to bf16, exact), except single-query items of 8 rows (see decode_flat_body).
+// P.V on the matrix cores at head size 128: bf16, fp8 and INT4 caches (fp8
+// and INT4 widened to bf16 in registers, exact), except bf16 / fp8
+// single-query items of 8 rows (see decode_flat_body).
 __host__ __device__ constexpr bool mfma_pv(int d, int kv, int gt, int qt) {
-  return (kv == PKV_BF16 || kv == PKV_FP8_E4M3) && d == 128 && !(gt == 8 && qt == 1);
+  return d == 128 && (kv_bits(kv) == 4 || ((kv == PKV_BF16 || kv == PKV_FP8_E4M3) && !(gt == 8 && qt == 1)));
 }
 
 // INT4 work items over two adjacent KV heads.  A 64-byte INT4 head row is
@@ -899,20 +900,6 @@ __device__ __forceinline__ uint4 int4_k_bf16(uint32_t w) {
   constexpr uint32_t kHi = 0x43434343u;                        // the high byte of each bf16
   return make_uint4(__builtin_amdgcn_perm(x, kHi, 0x00050004u), __builtin_amdgcn_perm(x, kHi, 0x00070006u),
                     __builtin_amdgcn_perm(y, kHi, 0x00050004u), __builtin_amdgcn_perm(y, kHi, 0x00070006u));
-}
-
-// INT4 V for the packed fp16 dot products: element n of two tokens' words
-// a and b (same dimensions) as the fp16 pair (1024 + u_a, 1024 + u_b)
-// (exponent of 1024, mantissa u, exact); out[n] for n = 0..7.
-__device__ __forceinline__ void int4_v_f16_pairs(uint32_t a, uint32_t b, uint32_t (&out)[8]) {
-  const uint32_t xa = a & 0x0F0F0F0Fu, xb = b & 0x0F0F0F0Fu;                  // even elements
-  const uint32_t ya = (a >> 4) & 0x0F0F0F0Fu, yb = (b >> 4) & 0x0F0F0F0Fu;    // odd elements
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t sel = 0x0C000C00u | ((4u + j) << 16) | (uint32_t)j;        // a.b_j, 0, b.b_j, 0
-    out[2 * j] = __builtin_amdgcn_perm(xb, xa, sel) | 0x64006400u;
-    out[2 * j + 1] = __builtin_amdgcn_perm(yb, ya, sel) | 0x64006400u;
-  }
 }
 
 // Eight query elements (pairs q0q1, q2q3, q4q5, q6q7) into the order of
@@ -1020,6 +1007,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
   // keep the vector ALUs (measured faster there: 102-106 against 108-117 us
   // on 32 x 4096 tokens with 64 query heads).
   constexpr bool kMPV = mfma_pv(D, KV, GT, QT) && RB && VLPR == 16 && VU == 4 && VEPL == 8;
+  static_assert(!kI4 || kMPV, "INT4 runs on the matrix-core P.V");
   extern __shared__ __align__(16) char lds[];
   const FlatLds L = flat_lds_layout(a.num_rows, RI, D, a.lds_budget);
   int* cum = reinterpret_cast<int*>(lds + L.cum_off);     // cum[r]: visible blocks of rows < r
@@ -1233,14 +1221,6 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
         mh[h] = m[h];
       }
     }
-    if constexpr (kI4) {
-      // V entered as 1024 + u; the values are u - 8: take 1032 times each
-      // row's weight sum off its accumulator
-#pragma unroll
-      for (int h = 0; h < RI; ++h)
-#pragma unroll
-        for (int e = 0; e < VEPL; ++e) acc[h][e] = fmaf(-1032.0f, lh[h], acc[h][e]);
-    }
     if constexpr (kMPV) {
       // lane (R, c): rows 4 R + i, dimensions 8 c .. 8 c + 7
       const int R = lane / 16, c = lane % 16;
@@ -1252,21 +1232,23 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
 #pragma unroll
         for (int rr = 1; rr < 4; ++rr)
           if (4 * rr + i < RI && R == rr) lr = lh[(4 * rr + i) % RI];
+        // INT4 values entered as 128 + u: the row's values are u - 8
+        const float off = kI4 ? -136.0f * lr : 0.0f;
         if (npieces == 1) {
           if (r / GT >= s_ql) continue;
           const int64_t out_row = ((int64_t)(s_tok + r / GT) * a.num_q_heads + h0 + r % GT) * D;
           const float inv = a.v_scale / lr;
           float o[VEPL];
 #pragma unroll
-          for (int t = 0; t < VEPL; ++t) o[t] = accm[t][i] * inv;
+          for (int t = 0; t < VEPL; ++t) o[t] = (accm[t][i] + off) * inv;
           store_out<PKV_BF16, VEPL>(a.out, out_row + c * VEPL, o);
         } else {
           const int64_t pr = (((int64_t)b * kvgroups + kvg) * RI + r) * a.max_splits + piece;
           float* dst = a.ws_acc + pr * D + c * VEPL;
 #pragma unroll
           for (int t = 0; t < VEPL; t += 4) {
-            const f32x4_t v4 = {accm[t][i] * a.v_scale, accm[t + 1][i] * a.v_scale,
-                                accm[t + 2][i] * a.v_scale, accm[t + 3][i] * a.v_scale};
+            const f32x4_t v4 = {(accm[t][i] + off) * a.v_scale, (accm[t + 1][i] + off) * a.v_scale,
+                                (accm[t + 2][i] + off) * a.v_scale, (accm[t + 3][i] + off) * a.v_scale};
             __builtin_nontemporal_store(v4, reinterpret_cast<f32x4_t*>(dst + t));
           }
         }
@@ -1470,18 +1452,6 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
       if constexpr (KV == PKV_BF16) {
 #pragma unroll
         for (int i = 0; i < VEPL / 2; ++i) { vf[2 * i] = bf16_lo(vwa[i]); vf[2 * i + 1] = bf16_hi(vwa[i]); }
-      } else if constexpr (kI4) {
-        // the unsigned nibbles u (0..15); the zero point comes off at the
-        // flush, as 8 times the row's probability sum
-#pragma unroll
-        for (int i = 0; i < S::kVBytes / 4; ++i) {
-          const uint32_t ev = vwa[i] & 0x0F0F0F0Fu, od = (vwa[i] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            vf[8 * i + 2 * b] = (float)((ev >> (8 * b)) & 0xFFu);
-            vf[8 * i + 2 * b + 1] = (float)((od >> (8 * b)) & 0xFFu);
-          }
-        }
       } else {
 #pragma unroll
         for (int i = 0; i < VEPL / 4; ++i) {
@@ -1576,79 +1546,74 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
         }
       }
       float pv[4];
+      uint32_t phi[4], plo[4];   // matrix-core P.V: bf16 high part and remainder
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float p = __builtin_amdgcn_exp2f(z[i] - m1);
         if constexpr (!full) p = z[i] == -INFINITY ? 0.f : p;
-        // INT4: the weights enter fp16 dot products; the sum takes the same
-        // rounded weights, so the softmax stays normalised
-        if constexpr (kI4) p = (float)(_Float16)p;
+        if constexpr (kMPV) {
+          phi[i] = f32_to_bf16_rne(p);
+          plo[i] = f32_to_bf16_rne(p - as_float(phi[i] << 16));
+          // INT4 values enter with an offset that the flush takes off as a
+          // multiple of the weight sum: the sum takes the weights the
+          // products use
+          if constexpr (kI4) p = as_float(phi[i] << 16) + as_float(plo[i] << 16);
+        }
         pv[i] = p;
         ls1 += p;
       }
       if constexpr (kMPV) {
-        uint32_t hi2[2], lo2[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint32_t h0b = f32_to_bf16_rne(pv[2 * j]), h1b = f32_to_bf16_rne(pv[2 * j + 1]);
-          const float r0 = pv[2 * j] - as_float(h0b << 16), r1 = pv[2 * j + 1] - as_float(h1b << 16);
-          hi2[j] = h0b | (h1b << 16);
-          lo2[j] = f32_to_bf16_rne(r0) | (f32_to_bf16_rne(r1) << 16);
-        }
-        const s16x4_t pa_hi = __builtin_bit_cast(s16x4_t, make_uint2(hi2[0], hi2[1]));
-        const s16x4_t pa_lo = __builtin_bit_cast(s16x4_t, make_uint2(lo2[0], lo2[1]));
-        // V rows of tokens 4 R + u; keys outside the piece's span are zeroed
-        // (their weights are 0, but the slots may hold anything)
-        uint32_t vw[4][4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if constexpr (KV == PKV_BF16) {
-            const uint4 raw = bf.v[u][0];
-            vw[u][0] = raw.x; vw[u][1] = raw.y; vw[u][2] = raw.z; vw[u][3] = raw.w;
-          } else {   // fp8 codes widened to bf16 pairs (exact; the V scale comes at the flush)
-            const uint2 raw = bf.v[u][0];
-            vw[u][0] = e4m3x2_to_bf16x2<false>(raw.x); vw[u][1] = e4m3x2_to_bf16x2<true>(raw.x);
-            vw[u][2] = e4m3x2_to_bf16x2<false>(raw.y); vw[u][3] = e4m3x2_to_bf16x2<true>(raw.y);
-          }
-          if constexpr (!full) {
-            const int pos = p0 + 4 * (lane / 16) + u;
-            const bool live = pos >= s_lo && pos <= s_hi;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) vw[u][k] = live ? vw[u][k] : 0u;
-          }
-        }
-#pragma unroll
-        for (int t = 0; t < VEPL; ++t) {
-          const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
-          const uint32_t b01 = __builtin_amdgcn_perm(vw[1][t / 2], vw[0][t / 2], sel);
-          const uint32_t b23 = __builtin_amdgcn_perm(vw[3][t / 2], vw[2][t / 2], sel);
-          const s16x4_t vb = __builtin_bit_cast(s16x4_t, make_uint2(b01, b23));
-          accm[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_hi, vb, accm[t], 0, 0, 0);
-          accm[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_lo, vb, accm[t], 0, 0, 0);
-        }
-      } else if constexpr (kI4) {
-        // load u of a 16-token step gives this lane token 4 R + u at 8
-        // dimensions; tokens (4 R, 4 R + 1) and (4 R + 2, 4 R + 3) form the
-        // fp16 pairs, weighted by the row's probabilities (broadcast from its
-        // lane).  Keys outside the piece have weight 0 and finite values.
-        static_assert(VU == 4 && TPRV == 1 && VEPL == 8, "INT4 step layout");
-        uint32_t vpair[NH][2][8];
+        const s16x4_t pa_hi = __builtin_bit_cast(s16x4_t, make_uint2(phi[0] | (phi[1] << 16), phi[2] | (phi[3] << 16)));
+        const s16x4_t pa_lo = __builtin_bit_cast(s16x4_t, make_uint2(plo[0] | (plo[1] << 16), plo[2] | (plo[3] << 16)));
+        const s16x4_t zero4 = {0, 0, 0, 0};
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh) {
-          int4_v_f16_pairs(bf.v[0][hh], bf.v[1][hh], vpair[hh][0]);
-          int4_v_f16_pairs(bf.v[2][hh], bf.v[3][hh], vpair[hh][1]);
-        }
-        static_for<0, RI>([&](auto hc) __attribute__((always_inline)) {
-          constexpr int h = decltype(hc)::value;
-          constexpr int hh = (kPair && h >= GT / 2) ? 1 : 0;   // the row's KV head
-          const auto p01 = __builtin_amdgcn_cvt_pkrtz(row_bcast<h>(pv[0]), row_bcast<h>(pv[1]));   // exact
-          const auto p23 = __builtin_amdgcn_cvt_pkrtz(row_bcast<h>(pv[2]), row_bcast<h>(pv[3]));
+          // V rows of tokens 4 R + u as bf16 pairs (elements 2k, 2k + 1 in
+          // dword k); keys outside the piece's span are zeroed (their weights
+          // are 0, but the slots may hold anything)
+          uint32_t vw[4][4];
 #pragma unroll
-          for (int e = 0; e < VEPL; ++e) {
-            acc[h][e] = __builtin_amdgcn_fdot2(p01, __builtin_bit_cast(decltype(p01), vpair[hh][0][e]), acc[h][e], false);
-            acc[h][e] = __builtin_amdgcn_fdot2(p23, __builtin_bit_cast(decltype(p23), vpair[hh][1][e]), acc[h][e], false);
+          for (int u = 0; u < 4; ++u) {
+            if constexpr (KV == PKV_BF16) {
+              const uint4 raw = bf.v[u][hh];
+              vw[u][0] = raw.x; vw[u][1] = raw.y; vw[u][2] = raw.z; vw[u][3] = raw.w;
+            } else if constexpr (kI4) {
+              // nibble u as the bf16 value 128 + u (exponent of 128, mantissa
+              // u, exact); the flush takes 136 times the weight sum off
+              const uint32_t raw = bf.v[u][hh];
+              const uint32_t xa = raw & 0x0F0F0F0Fu, ya = (raw >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+              for (int k = 0; k < 4; ++k)
+                vw[u][k] = __builtin_amdgcn_perm(ya, xa, 0x0C000C00u | ((4u + k) << 16) | (uint32_t)k) | 0x43004300u;
+            } else {   // fp8 codes widened to bf16 pairs (exact; the V scale comes at the flush)
+              const uint2 raw = bf.v[u][hh];
+              vw[u][0] = e4m3x2_to_bf16x2<false>(raw.x); vw[u][1] = e4m3x2_to_bf16x2<true>(raw.x);
+              vw[u][2] = e4m3x2_to_bf16x2<false>(raw.y); vw[u][3] = e4m3x2_to_bf16x2<true>(raw.y);
+            }
+            if constexpr (!full) {
+              const int pos = p0 + 4 * (lane / 16) + u;
+              const bool live = pos >= s_lo && pos <= s_hi;
+#pragma unroll
+              for (int k = 0; k < 4; ++k) vw[u][k] = live ? vw[u][k] : 0u;
+            }
           }
-        });
+          // pair items: each KV head's V meets only its own rows' weights
+          s16x4_t ah = pa_hi, al = pa_lo;
+          if constexpr (kPair) {
+            const bool mine = ((lane % 16) >= GT / 2) == (hh == 1);
+            ah = mine ? pa_hi : zero4;
+            al = mine ? pa_lo : zero4;
+          }
+#pragma unroll
+          for (int t = 0; t < VEPL; ++t) {
+            const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
+            const uint32_t b01 = __builtin_amdgcn_perm(vw[1][t / 2], vw[0][t / 2], sel);
+            const uint32_t b23 = __builtin_amdgcn_perm(vw[3][t / 2], vw[2][t / 2], sel);
+            const s16x4_t vb = __builtin_bit_cast(s16x4_t, make_uint2(b01, b23));
+            accm[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, vb, accm[t], 0, 0, 0);
+            accm[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, vb, accm[t], 0, 0, 0);
+          }
+        }
       } else {
 #pragma unroll
       for (int u = 0; u < VU; ++u) {
