@@ -305,8 +305,8 @@ def bench_spec(args, dev):
 
     def step(i):
         cache, bt = pools[i % len(pools)]
-        pkv.slot_mapping(bt, base.query_start_loc, base.num_computed, w.block_size, w.num_blocks, out=slots)
-        pkv.cache_write(base.new_k, base.new_v, slots, cache)
+        pkv.slot_mapping_cache_write(bt, base.query_start_loc, base.num_computed, base.new_k, base.new_v,
+                                     cache, out=slots)
         attend(i)
 
     def timed(fn):
@@ -482,8 +482,9 @@ def main():
 
     def step(i):
         cache, bt = pools[i % npools]
-        pkv.slot_mapping(bt, base.query_start_loc, base.num_computed, w.block_size, nb, out=slots)
-        pkv.cache_write(base.new_k, base.new_v, slots, cache)
+        # slot mapping and the write of the step's K/V rows in one launch
+        pkv.slot_mapping_cache_write(bt, base.query_start_loc, base.num_computed, base.new_k, base.new_v,
+                                     cache, out=slots)
         pkv.paged_attention_decode_partials(base.q, cache, bt, base.seq_lens, w.max_seq_len, w.scale,
                                             plan, ws, out)
         pkv.paged_attention_decode_combine(out, base.seq_lens, w.block_size, plan, ws)
@@ -557,6 +558,15 @@ def main():
     b.record()
     torch.cuda.synchronize()
     writes["bf16_T64_step"] = dict(us=round(a.elapsed_time(b) / 50 * 1e3, 2))
+    # the same with its slot mapping in the one launch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(50):
+        pkv.slot_mapping_cache_write(pools[0][1], base.query_start_loc, base.num_computed, base.new_k,
+                                     base.new_v, pools[0][0], out=slots)
+    b.record()
+    torch.cuda.synchronize()
+    writes["slot_mapping_and_write_T64_step"] = dict(us=round(a.elapsed_time(b) / 50 * 1e3, 2))
 
     sharing = {}
     if args.workload == "prefix":

@@ -188,6 +188,24 @@ PKV_API int pkv_cache_write(const void* key, const void* value, int32_t src_dtyp
                     const pkv_cache* cache, hipStream_t stream);
 
 /*
+ * Steps 1 and 2 in one launch [W § Pinpointing the Token Slot and § Summary;
+ * E § Slot mapping은 왜 필요한가]: exactly pkv_slot_mapping (block size and
+ * pool size from `cache`) followed by pkv_cache_write with the slots it
+ * produced.  Every argument means what it means in those two calls;
+ * slot_mapping [num_tokens] is written (the caller may read it afterwards)
+ * and err_count, when given, counts bad lookups as pkv_slot_mapping does.
+ * Rows of key/value for padding tokens or bad lookups are not written.
+ * Errors: those of either call, checked before anything is launched.
+ */
+PKV_API int pkv_slot_mapping_cache_write(const int32_t* block_table, int32_t bt_stride,
+                                 int32_t num_reqs, const int32_t* query_start_loc,
+                                 const int32_t* num_computed, int32_t num_tokens,
+                                 int64_t* slot_mapping, int32_t* err_count,
+                                 const void* key, const void* value, int32_t src_dtype,
+                                 int64_t src_token_stride, int64_t src_head_stride,
+                                 const pkv_cache* cache, hipStream_t stream);
+
+/*
  * Block copy for prefix sharing [W-zh § PagedAttention与Block管理: requests
  * that share a prompt prefix point their tables' leading entries at the same
  * physical blocks, each block counting its references and returning to the

@@ -67,6 +67,8 @@ SIGNATURES = {
     "pkv_num_blocks_for_budget": (_i64, [_i64, ctypes.c_double, _i64, _i32, _i32, _i32, _i32, _i32]),
     "pkv_slot_mapping": (_int, [_vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "pkv_cache_write": (_int, [_vp, _vp, _i32, _i64, _i64, _vp, _i32, ctypes.POINTER(PkvCache), _vp]),
+    "pkv_slot_mapping_cache_write": (_int, [_vp, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i64,
+                                            _i64, ctypes.POINTER(PkvCache), _vp]),
     "pkv_decode_plan_make": (_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                     ctypes.POINTER(PkvDecodePlan)]),
     "pkv_paged_attention_decode": (_int, [_vp, _vp, _i32, _i32, _i32, ctypes.POINTER(PkvCache), _vp, _i32,

@@ -139,6 +139,33 @@ def cache_write(key, value, slot_mapping_, cache):
         ctypes.byref(c), _stream(key.device)))
 
 
+def slot_mapping_cache_write(block_table, query_start_loc, num_computed, key, value, cache,
+                             out=None, err_count=None):
+    """slot_mapping followed by cache_write in one launch; returns the slots
+    (int64 [T], T = key rows)."""
+    lib = load()
+    _i32(block_table, "block_table")
+    _i32(query_start_loc, "query_start_loc")
+    _i32(num_computed, "num_computed")
+    num_reqs = num_computed.numel()
+    _need(query_start_loc.numel() == num_reqs + 1, "query_start_loc needs num_reqs + 1 entries")
+    _need(block_table.dim() == 2 and block_table.shape[0] >= num_reqs, "block_table must be [R, max_blocks]")
+    _need(key.shape == value.shape and key.dim() == 3 and key.dtype == value.dtype, "key/value mismatch")
+    _need(key.stride() == value.stride() and key.stride(2) == 1, "key/value need unit dim stride")
+    T = key.shape[0]
+    if out is None:
+        out = torch.empty(T, dtype=torch.int64, device=key.device)
+    _need(out.dtype == torch.int64 and out.is_contiguous() and out.numel() >= T, "bad out")
+    if err_count is not None:
+        _need(err_count.dtype == torch.int32, "err_count must be int32")
+    c = cache.c_struct()
+    check("pkv_slot_mapping_cache_write", lib.pkv_slot_mapping_cache_write(
+        _ptr(block_table), block_table.shape[1], num_reqs, _ptr(query_start_loc), _ptr(num_computed), T,
+        _ptr(out), _ptr(err_count), _ptr(key), _ptr(value), _dt(key), key.stride(0), key.stride(1),
+        ctypes.byref(c), _stream(key.device)))
+    return out
+
+
 def copy_blocks(src_ids, dst_ids, cache, err_count=None):
     """Copy blocks src_ids[i] -> dst_ids[i] (int32 device tensors) in both planes."""
     lib = load()

@@ -830,17 +830,17 @@ __global__ __launch_bounds__(64) void decode_split_uni_kernel(DecodeArgs a) {
 // reads the physical block of each step with one lane read, and crossing
 // into the next piece costs an LDS read instead of a wait on memory.
 //
-// Scores of a 16-token step are one chain of 16x16x32 bf16 MFMAs,
-// S[q head][token] = Q . K^T: Q is the A operand (rows = query heads of the
-// item, unused rows zero) and K rows load straight into the B operand (lane l:
-// token l % 16, 8 consecutive elements from 32c + 8 (l / 16)).  The running
-// max of every head is wave-uniform (a 16-lane max of S read into a scalar
-// register), so one scalar test per head and step decides the lazy rescale.
-// P.V stays on the vector ALUs in fp32: lane L = VLPR g + sub holds
-// V[token u VRPW + g][sub VEPL ..] and fetches that token's probability with
-// a lane permute.  Requirements: bf16 or fp8 cache, bf16 query, head_dim % 32
-// == 0, row of at least 64 bytes, block size a multiple of 16, at most 16
-// query heads per item.
+// Scores of a 16-token step are one chain of 16x16x32 bf16 MFMAs, computed
+// transposed (S^T = K Q^T, the same registers with the operands swapped):
+// K rows load straight into one operand (lane l: token l % 16, 8 elements of
+// a 32-element chunk) and the item's query rows, staged in LDS, are the other
+// (unused rows zero).  Lane l then holds the scores of row l % 16 for tokens
+// 4 (l / 16) .. + 3, so each row's running max and sum live in one lane.
+// P.V runs on the matrix cores where mfma_pv says so (decode_flat_body
+// describes the layout), else on the vector ALUs in fp32 with each weight
+// arriving by a DPP row broadcast.  Requirements: bf16, fp8 or INT4 cache,
+// bf16 query, head_dim % 32 == 0, row of at least 64 bytes, block size a
+// multiple of 16, at most 16 MFMA rows per item.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));   // 4 bf16, 16x16x16 MFMA operand
@@ -1003,9 +1003,9 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
   // standing for dimension 8 n + t the lane's own V loads (tokens 4 R + u,
   // dimensions 8 (l % 16) .. + 7) are the B operand: no data moves.  The
   // lane then holds rows 4 R + i at dimensions 8 (l % 16) .. + 7.  P enters
-  // as a bf16 high part plus a bf16 remainder.  Single-query items of 8 rows
-  // keep the vector ALUs (measured faster there: 102-106 against 108-117 us
-  // on 32 x 4096 tokens with 64 query heads).
+  // as a bf16 high part plus a bf16 remainder.  bf16 and fp8 single-query
+  // items of 8 rows keep the vector ALUs (measured faster there: 102-106
+  // against 108-117 us on 32 x 4096 tokens with 64 query heads).
   constexpr bool kMPV = mfma_pv(D, KV, GT, QT) && RB && VLPR == 16 && VU == 4 && VEPL == 8;
   static_assert(!kI4 || kMPV, "INT4 runs on the matrix-core P.V");
   extern __shared__ __align__(16) char lds[];

@@ -18,37 +18,18 @@
 namespace pkv {
 
 // ------------------------------------------------------------------ K1
-// One thread per token of the step.  The owning request is found by binary
-// search over query_start_loc; all reads stay inside the arrays the caller
-// described (block-table row index < bt_stride, request index < num_reqs).
-__global__ __launch_bounds__(256) void slot_mapping_kernel(
-    const int32_t* __restrict__ bt, int32_t bt_stride, int32_t num_reqs,
-    const int32_t* __restrict__ qsl, const int32_t* __restrict__ nc,
-    int32_t bs_log2, int32_t num_blocks, int32_t num_tokens,
-    int64_t* __restrict__ out, int32_t* __restrict__ err) {
-  // query_start_loc and num_computed go to LDS in one load round when they
-  // fit, so a token's chain of dependent global loads is just the table entry
-  constexpr int kStage = 1024;
-  __shared__ int sq[kStage + 1];
-  __shared__ int snc[kStage];
-  const bool staged = num_reqs <= kStage;
-  if (staged) {
-    for (int i = threadIdx.x; i <= num_reqs; i += 256) {
-      sq[i] = qsl[i];
-      if (i < num_reqs) snc[i] = nc[i];
-    }
-    __syncthreads();
-  }
-  const int* q = staged ? sq : qsl;
-  const int* ncs = staged ? snc : nc;
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= num_tokens) return;
-  const int first = q[0];
-  const int end = q[num_reqs];
-  if (t < first || t >= end) {  // padding: no request owns this token
-    out[t] = -1;
-    return;
-  }
+// Slot of token t of the step, -1 for padding or a bad lookup; `owned` tells
+// whether a request owns t.  q and ncs are query_start_loc and num_computed
+// (in LDS or global memory).  Position p of request r lives in logical block
+// p / block_size at offset p % block_size.
+constexpr int kSlotStage = 1024;   // requests whose metadata a workgroup stages in LDS
+
+__device__ __forceinline__ int64_t token_slot(int t, const int* q, const int* ncs,
+                                              const int32_t* __restrict__ bt, int32_t bt_stride,
+                                              int32_t num_reqs, int32_t bs_log2, int32_t num_blocks,
+                                              bool& owned) {
+  owned = t >= q[0] && t < q[num_reqs];
+  if (!owned) return -1;
   int lo = 0, hi = num_reqs;  // largest r < num_reqs with qsl[r] <= t
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -63,8 +44,37 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(
     if (id >= 0 && id < num_blocks)
       slot = ((int64_t)id << bs_log2) + (pos & ((1 << bs_log2) - 1));
   }
+  return slot;
+}
+
+// One thread per token of the step.  The owning request is found by binary
+// search over query_start_loc; all reads stay inside the arrays the caller
+// described (block-table row index < bt_stride, request index < num_reqs).
+__global__ __launch_bounds__(256) void slot_mapping_kernel(
+    const int32_t* __restrict__ bt, int32_t bt_stride, int32_t num_reqs,
+    const int32_t* __restrict__ qsl, const int32_t* __restrict__ nc,
+    int32_t bs_log2, int32_t num_blocks, int32_t num_tokens,
+    int64_t* __restrict__ out, int32_t* __restrict__ err) {
+  // query_start_loc and num_computed go to LDS in one load round when they
+  // fit, so a token's chain of dependent global loads is just the table entry
+  __shared__ int sq[kSlotStage + 1];
+  __shared__ int snc[kSlotStage];
+  const bool staged = num_reqs <= kSlotStage;
+  if (staged) {
+    for (int i = threadIdx.x; i <= num_reqs; i += 256) {
+      sq[i] = qsl[i];
+      if (i < num_reqs) snc[i] = nc[i];
+    }
+    __syncthreads();
+  }
+  const int* q = staged ? sq : qsl;
+  const int* ncs = staged ? snc : nc;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= num_tokens) return;
+  bool owned;
+  const int64_t slot = token_slot(t, q, ncs, bt, bt_stride, num_reqs, bs_log2, num_blocks, owned);
   out[t] = slot;
-  if (slot < 0 && err) atomicAdd(err, 1);
+  if (owned && slot < 0 && err) atomicAdd(err, 1);   // padding is not an error
 }
 
 // ------------------------------------------------------------------ K2
@@ -84,6 +94,16 @@ struct WriteArgs {
   void* vdst;
   float inv_k_scale;
   float inv_v_scale;
+  // fused slot mapping (cache_write_kernel<..., true>): the slots are
+  // computed here and stored to slots_out
+  const int32_t* bt;
+  int32_t bt_stride;
+  int32_t num_reqs;
+  const int32_t* qsl;
+  const int32_t* nc;
+  int32_t num_blocks;
+  int64_t* slots_out;
+  int32_t* err;
 };
 
 template <int kBytes>
@@ -120,7 +140,9 @@ __device__ __forceinline__ void load_as_f32(const void* p, float (&x)[N]) {
 
 // SRC, DST: pkv_dtype; CE: destination elements per thread (16 bytes of
 // destination, or the whole row when a row is shorter).
-template <int SRC, int DST, int CE>
+// FUSED: the token's slot is computed as in slot_mapping_kernel (and stored
+// once per token) instead of read.
+template <int SRC, int DST, int CE, bool FUSED = false>
 __global__ __launch_bounds__(256) void cache_write_kernel(WriteArgs a) {
   constexpr int kDstBits = kv_bits(DST);
   constexpr int kSrcElt = SRC == PKV_F32 ? 4 : 2;
@@ -128,15 +150,39 @@ __global__ __launch_bounds__(256) void cache_write_kernel(WriteArgs a) {
   const int chunks_per_plane = a.num_kv_heads * chunks_per_head;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = (int64_t)a.num_tokens * 2 * chunks_per_plane;
-  if (idx >= total) return;
-  const int t = (int)(idx / (2 * chunks_per_plane));
-  const int rem = (int)(idx - (int64_t)t * 2 * chunks_per_plane);
+  int64_t slot;
+  int t, rem;
+  if constexpr (FUSED) {
+    __shared__ int sq[kSlotStage + 1];
+    __shared__ int snc[kSlotStage];
+    const bool staged = a.num_reqs <= kSlotStage;   // uniform across the workgroup
+    if (staged) {
+      for (int i = threadIdx.x; i <= a.num_reqs; i += 256) {
+        sq[i] = a.qsl[i];
+        if (i < a.num_reqs) snc[i] = a.nc[i];
+      }
+      __syncthreads();
+    }
+    if (idx >= total) return;
+    t = (int)(idx / (2 * chunks_per_plane));
+    rem = (int)(idx - (int64_t)t * 2 * chunks_per_plane);
+    bool owned;
+    slot = token_slot(t, staged ? sq : a.qsl, staged ? snc : a.nc, a.bt, a.bt_stride, a.num_reqs,
+                      a.bs_log2, a.num_blocks, owned);
+    if (rem == 0) {
+      a.slots_out[t] = slot;
+      if (owned && slot < 0 && a.err) atomicAdd(a.err, 1);
+    }
+  } else {
+    if (idx >= total) return;
+    t = (int)(idx / (2 * chunks_per_plane));
+    rem = (int)(idx - (int64_t)t * 2 * chunks_per_plane);
+    slot = a.slots[t];
+  }
   const int kv = rem >= chunks_per_plane;
   const int j = rem - kv * chunks_per_plane;
   const int h = j / chunks_per_head;
   const int c = j - h * chunks_per_head;
-
-  const int64_t slot = a.slots[t];
   if (slot < 0 || slot >= a.num_slots) return;
   const int64_t blk = slot >> a.bs_log2;
   const int64_t off = slot & ((1 << a.bs_log2) - 1);
@@ -256,15 +302,15 @@ static int log2_int(int x) {
   return l;
 }
 
-template <int SRC, int DST>
+template <int SRC, int DST, bool FUSED = false>
 static void launch_write(const WriteArgs& a, int ce, hipStream_t s) {
   const int64_t threads = (int64_t)a.num_tokens * 2 * a.num_kv_heads * (a.head_dim / ce);
   const dim3 grid((unsigned)((threads + 255) / 256));
   switch (ce) {
-    case 4: if constexpr (DST == PKV_F32) { cache_write_kernel<SRC, DST, 4><<<grid, 256, 0, s>>>(a); } break;
-    case 8: if constexpr (DST == PKV_BF16 || DST == PKV_FP8_E4M3) { cache_write_kernel<SRC, DST, 8><<<grid, 256, 0, s>>>(a); } break;
-    case 16: if constexpr (DST == PKV_FP8_E4M3) { cache_write_kernel<SRC, DST, 16><<<grid, 256, 0, s>>>(a); } break;
-    case 32: if constexpr (DST == PKV_INT4) { cache_write_kernel<SRC, DST, 32><<<grid, 256, 0, s>>>(a); } break;
+    case 4: if constexpr (DST == PKV_F32) { cache_write_kernel<SRC, DST, 4, FUSED><<<grid, 256, 0, s>>>(a); } break;
+    case 8: if constexpr (DST == PKV_BF16 || DST == PKV_FP8_E4M3) { cache_write_kernel<SRC, DST, 8, FUSED><<<grid, 256, 0, s>>>(a); } break;
+    case 16: if constexpr (DST == PKV_FP8_E4M3) { cache_write_kernel<SRC, DST, 16, FUSED><<<grid, 256, 0, s>>>(a); } break;
+    case 32: if constexpr (DST == PKV_INT4) { cache_write_kernel<SRC, DST, 32, FUSED><<<grid, 256, 0, s>>>(a); } break;
   }
 }
 
@@ -289,18 +335,22 @@ extern "C" int pkv_slot_mapping(const int32_t* block_table, int32_t bt_stride, i
   return launch_status();
 }
 
-extern "C" int pkv_cache_write(const void* key, const void* value, int32_t src_dtype,
-                               int64_t src_token_stride, int64_t src_head_stride,
-                               const int64_t* slot_mapping, int32_t num_tokens,
-                               const pkv_cache* cache, hipStream_t stream) {
+// Checks of a cache write and its arguments (no slots yet); fills `a` and
+// the destination elements per thread.  PKV_OK with a.num_tokens == 0 means
+// nothing to launch.
+static int prepare_write(WriteArgs& a, int& ce, const void* key, const void* value, int32_t src_dtype,
+                         int64_t src_token_stride, int64_t src_head_stride, int32_t num_tokens,
+                         const pkv_cache* cache) {
   int st = check_cache(cache);
   if (st != PKV_OK) return st;
   if (num_tokens < 0) return PKV_ERR_SHAPE;
   if (src_dtype != PKV_F32 && src_dtype != PKV_BF16) return PKV_ERR_DTYPE;
   const int dst = cache->dtype;
   if (dst == PKV_F32 && src_dtype != PKV_F32) return PKV_ERR_DTYPE;
+  a = WriteArgs{};
+  a.num_tokens = num_tokens;
   if (num_tokens == 0) return PKV_OK;
-  if (!key || !value || !slot_mapping) return PKV_ERR_NULL;
+  if (!key || !value) return PKV_ERR_NULL;
   const int se = dtype_size(src_dtype);
   const int D = cache->head_dim;
   if (src_head_stride < D || src_token_stride < src_head_stride * (cache->num_kv_heads - 1) + D)
@@ -309,19 +359,16 @@ extern "C" int pkv_cache_write(const void* key, const void* value, int32_t src_d
       (src_head_stride * se) % 16)
     return PKV_ERR_SHAPE;
   // destination elements per thread: 16 bytes of destination, capped by the row
-  int ce = 128 / dtype_bits(dst);
+  ce = 128 / dtype_bits(dst);
   if (ce > D) ce = D;
   // sources narrower than 16 bytes per chunk are not vectorised: bf16 -> fp8
   // with D = 8 reads 16 bytes (fine); everything else keeps >= 16 source bytes.
   if (ce * se < 16) return PKV_ERR_UNSUPPORTED;
 
-  WriteArgs a;
   a.key = key;
   a.value = value;
   a.tok_stride = src_token_stride;
   a.head_stride = src_head_stride;
-  a.slots = slot_mapping;
-  a.num_tokens = num_tokens;
   a.num_kv_heads = cache->num_kv_heads;
   a.head_dim = D;
   a.bs_log2 = log2_int(cache->block_size);
@@ -331,18 +378,63 @@ extern "C" int pkv_cache_write(const void* key, const void* value, int32_t src_d
   a.vdst = cache->v;
   a.inv_k_scale = 1.0f / cache->k_scale;
   a.inv_v_scale = 1.0f / cache->v_scale;
+  return PKV_OK;
+}
 
+template <bool FUSED>
+static int dispatch_write(const WriteArgs& a, int ce, int src_dtype, int dst, hipStream_t stream) {
   if (src_dtype == PKV_F32) {
-    if (dst == PKV_F32) launch_write<PKV_F32, PKV_F32>(a, ce, stream);
-    else if (dst == PKV_BF16) launch_write<PKV_F32, PKV_BF16>(a, ce, stream);
-    else if (dst == PKV_FP8_E4M3) launch_write<PKV_F32, PKV_FP8_E4M3>(a, ce, stream);
-    else launch_write<PKV_F32, PKV_INT4>(a, ce, stream);
+    if (dst == PKV_F32) launch_write<PKV_F32, PKV_F32, FUSED>(a, ce, stream);
+    else if (dst == PKV_BF16) launch_write<PKV_F32, PKV_BF16, FUSED>(a, ce, stream);
+    else if (dst == PKV_FP8_E4M3) launch_write<PKV_F32, PKV_FP8_E4M3, FUSED>(a, ce, stream);
+    else launch_write<PKV_F32, PKV_INT4, FUSED>(a, ce, stream);
   } else {
-    if (dst == PKV_BF16) launch_write<PKV_BF16, PKV_BF16>(a, ce, stream);
-    else if (dst == PKV_FP8_E4M3) launch_write<PKV_BF16, PKV_FP8_E4M3>(a, ce, stream);
-    else launch_write<PKV_BF16, PKV_INT4>(a, ce, stream);
+    if (dst == PKV_BF16) launch_write<PKV_BF16, PKV_BF16, FUSED>(a, ce, stream);
+    else if (dst == PKV_FP8_E4M3) launch_write<PKV_BF16, PKV_FP8_E4M3, FUSED>(a, ce, stream);
+    else launch_write<PKV_BF16, PKV_INT4, FUSED>(a, ce, stream);
   }
   return launch_status();
+}
+
+extern "C" int pkv_cache_write(const void* key, const void* value, int32_t src_dtype,
+                               int64_t src_token_stride, int64_t src_head_stride,
+                               const int64_t* slot_mapping, int32_t num_tokens,
+                               const pkv_cache* cache, hipStream_t stream) {
+  WriteArgs a;
+  int ce = 0;
+  const int st = prepare_write(a, ce, key, value, src_dtype, src_token_stride, src_head_stride,
+                               num_tokens, cache);
+  if (st != PKV_OK || num_tokens == 0) return st;
+  if (!slot_mapping) return PKV_ERR_NULL;
+  a.slots = slot_mapping;
+  return dispatch_write<false>(a, ce, src_dtype, cache->dtype, stream);
+}
+
+extern "C" int pkv_slot_mapping_cache_write(const int32_t* block_table, int32_t bt_stride,
+                                            int32_t num_reqs, const int32_t* query_start_loc,
+                                            const int32_t* num_computed, int32_t num_tokens,
+                                            int64_t* slot_mapping, int32_t* err_count,
+                                            const void* key, const void* value, int32_t src_dtype,
+                                            int64_t src_token_stride, int64_t src_head_stride,
+                                            const pkv_cache* cache, hipStream_t stream) {
+  if (num_reqs < 0 || bt_stride < 0 || num_tokens < 0) return PKV_ERR_SHAPE;
+  WriteArgs a;
+  int ce = 0;
+  const int st = prepare_write(a, ce, key, value, src_dtype, src_token_stride, src_head_stride,
+                               num_tokens, cache);
+  if (st != PKV_OK || num_tokens == 0) return st;
+  if (!slot_mapping || !query_start_loc) return PKV_ERR_NULL;
+  if (num_reqs > 0 && (!block_table || !num_computed)) return PKV_ERR_NULL;
+  if (num_reqs > 0 && bt_stride == 0) return PKV_ERR_SHAPE;
+  a.bt = block_table;
+  a.bt_stride = bt_stride;
+  a.num_reqs = num_reqs;
+  a.qsl = query_start_loc;
+  a.nc = num_computed;
+  a.num_blocks = cache->num_blocks;
+  a.slots_out = slot_mapping;
+  a.err = err_count;
+  return dispatch_write<true>(a, ce, src_dtype, cache->dtype, stream);
 }
 
 extern "C" int pkv_fp8_e4m3_quantize(const void* x, int32_t src_dtype, int64_t n, float scale,

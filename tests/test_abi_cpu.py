@@ -36,7 +36,8 @@ def test_header_declares_the_expected_calls():
                  "pkv_paged_attention_decode_partials", "pkv_paged_attention_decode_combine",
                  "pkv_chunked_workspace_size", "pkv_kv_bytes_per_token", "pkv_status_string",
                  "pkv_fp8_e4m3_quantize", "pkv_fp8_e4m3_dequantize", "pkv_copy_blocks",
-                 "pkv_int4_quantize", "pkv_int4_dequantize", "pkv_num_blocks_for_budget"):
+                 "pkv_int4_quantize", "pkv_int4_dequantize", "pkv_num_blocks_for_budget",
+                 "pkv_slot_mapping_cache_write"):
         assert want in names
     assert set(names) == set(_lib.SIGNATURES)   # the binding covers every declaration
 
@@ -144,6 +145,17 @@ def test_argument_checks_return_before_launching(lib):
                                           ctypes.byref(ws)) == _lib.PKV_OK
     assert lib.pkv_chunked_workspace_size(64, 16, 32, 8, 128, 16, _lib.PKV_INT4, 8, 512, 0,
                                           ctypes.byref(ws)) == _lib.PKV_OK and ws.value > 0
+    # fused slot mapping + write: either call's checks, nothing launched
+    assert lib.pkv_slot_mapping_cache_write(0x100, 4, -1, 0x100, 0x100, 4, 0x100, None, 0x100, 0x100,
+                                            _lib.PKV_BF16, 1024, 128, ctypes.byref(c), None) == _lib.PKV_ERR_SHAPE
+    assert lib.pkv_slot_mapping_cache_write(0x100, 4, 1, None, 0x100, 4, 0x100, None, 0x100, 0x100,
+                                            _lib.PKV_BF16, 1024, 128, ctypes.byref(c), None) == _lib.PKV_ERR_NULL
+    assert lib.pkv_slot_mapping_cache_write(0x100, 4, 1, 0x100, 0x100, 4, 0x100, None, 0x100, 0x100,
+                                            _lib.PKV_BF16, 1024, 128, ctypes.byref(c32), None) == _lib.PKV_ERR_DTYPE
+    assert lib.pkv_slot_mapping_cache_write(0x100, 4, 1, 0x100, 0x100, 4, 0x100, None, 0x108, 0x100,
+                                            _lib.PKV_BF16, 1024, 128, ctypes.byref(c), None) == _lib.PKV_ERR_SHAPE
+    assert lib.pkv_slot_mapping_cache_write(0x100, 4, 1, 0x100, 0x100, 0, 0x100, None, 0x100, 0x100,
+                                            _lib.PKV_BF16, 1024, 128, ctypes.byref(c), None) == _lib.PKV_OK
     # block copy: bad cache, negative or empty pair lists, missing id arrays
     assert lib.pkv_copy_blocks(ctypes.byref(_cache(k=0)), 0x100, 0x100, 4, None, None) == _lib.PKV_ERR_NULL
     assert lib.pkv_copy_blocks(ctypes.byref(c), 0x100, 0x100, -1, None, None) == _lib.PKV_ERR_SHAPE
