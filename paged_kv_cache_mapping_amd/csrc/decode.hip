@@ -568,8 +568,8 @@ extern "C" int pkv_paged_attention_chunked(void* out, const void* q, int32_t q_d
   if (st != PKV_OK) return st;
   a1.num_tokens = num_tokens;
   if (max_query_len > 1 && p.spec_qt > 0) {
-    // multi-query requests as decode items of heads x query tokens; the
-    // plan and workspace count one "head" per (token, head) pair
+    // every request (1 .. 8 query tokens) as decode items of heads x query
+    // tokens; the plan and workspace count one "head" per (token, head) pair
     if (!out || !q || !block_table || !seq_lens) return PKV_ERR_NULL;
     DecodeArgs a3;
     st = prepare(a3, out, q, q_dtype, num_reqs, num_q_heads * p.spec_qt, cache, block_table, bt_stride,
@@ -584,8 +584,8 @@ extern "C" int pkv_paged_attention_chunked(void* out, const void* q, int32_t q_d
     a3.num_tokens = num_tokens;
     st = run_split(a3, p.spec, cache->dtype, stream);
     if (st != PKV_OK) return st;
-    st = run_combine(a3, q_dtype, stream);
-    if (st != PKV_OK) return st;
+    // the items hold the single-query requests too: no separate pass
+    return run_combine(a3, q_dtype, stream);
   } else if (max_query_len > 1 && p.prefill) {
     if (!out || !q || !block_table || !seq_lens) return PKV_ERR_NULL;
     if (bt_stride <= 0 || max_seq_len < 0 || sliding_window < 0) return PKV_ERR_SHAPE;

@@ -42,7 +42,7 @@ struct DecodeArgs {
   //   Tokens of single-query requests are skipped when skip_single is set.
   // 2 (chunked requests): row r is request r; only requests with exactly one
   //   query are processed (their query token is qsl[r]).
-  // 3 (chunked multi-token requests): row r is request r with 2 .. qt query
+  // 3 (chunked multi-token requests): row r is request r with 1 .. qt query
   //   tokens qsl[r] ..; one work item holds all of them for its heads.
   int32_t row_mode;
   int32_t causal;
@@ -111,7 +111,7 @@ __device__ __forceinline__ RowInfo row_info(const DecodeArgs& a, int row) {
     // window start to the last token (non-causal: to seq_len - 1, the same)
     const int t0 = a.qsl[row];
     const int ql = a.qsl[row + 1] - t0;
-    if (ql < 2 || t0 < 0 || t0 + ql > a.num_tokens) { r.skip = true; return r; }
+    if (ql < 1 || t0 < 0 || t0 + ql > a.num_tokens) { r.skip = true; return r; }
     r.tok = t0;
     r.ntok = ql;
     L = a.seq_lens[row];
