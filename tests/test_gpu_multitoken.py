@@ -106,3 +106,47 @@ def test_spec_workload_sampled_requests():
     ref = attention.paged_attention(w.q[rows], "bf16", kp, vp, "bf16", w.block_table[reqs], w.seq_lens[reqs],
                                     qsl, w.scale)
     assert max_err(out_f64(out)[rows], ref) <= 2e-3
+
+
+def test_single_query_requests_ride_in_the_items():
+    """A step declared with up to 4 query tokens whose requests all have one:
+    every request runs as a multi-token item, and the output equals the
+    oracle and the decode form's output for the same queries."""
+    say("multi-token single-query requests")
+    c = _chunk_case(3300, R=12, Lmax=900, qmax=1, Hq=32, Hkv=8, D=128, bs=16, v_sigma=0.2)
+    assert (np.diff(c["qsl"]) == 1).all()
+
+    def dev16(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    cache = pkv.CacheView.from_planes(dev16(c["kp"]), dev16(c["vp"]))
+    args = (torch.from_numpy(c["qsl"]).cuda(), torch.from_numpy(c["L"]).cuda())
+    out = pkv.paged_attention_chunked(dev16(c["q"]), *args, 4, cache, torch.from_numpy(c["bt"]).cuda(),
+                                      int(c["L"].max()), 0.125)
+    dec = pkv.paged_attention_decode(dev16(c["q"]), cache, torch.from_numpy(c["bt"]).cuda(), args[1],
+                                     int(c["L"].max()), 0.125)
+    torch.cuda.synchronize()
+    ref = attention.paged_attention(c["q"], "bf16", c["kp"], c["vp"], "bf16", c["bt"], c["L"], c["qsl"], 0.125)
+    assert max_err(out_f64(out), ref) <= 2e-3
+    assert max_err(out_f64(dec), ref) <= 2e-3
+
+
+def test_empty_requests_among_multi_token_requests():
+    """Requests with no query tokens in a multi-token step: nothing is written
+    for them and every other row matches the oracle."""
+    say("multi-token empty requests")
+    c = _chunk_case(3400, R=10, Lmax=700, qmax=4, Hq=32, Hkv=8, D=128, bs=16, v_sigma=0.2)
+    ql = np.diff(c["qsl"])
+    ql[[2, 5]] = 0
+    c["qsl"] = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    T = int(c["qsl"][-1])
+    c["q"] = c["q"][:T]
+
+    def dev16(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    cache = pkv.CacheView.from_planes(dev16(c["kp"]), dev16(c["vp"]))
+    out = pkv.paged_attention_chunked(dev16(c["q"]), torch.from_numpy(c["qsl"]).cuda(),
+                                      torch.from_numpy(c["L"]).cuda(), int(ql.max()), cache,
+                                      torch.from_numpy(c["bt"]).cuda(), int(c["L"].max()), 0.125)
+    torch.cuda.synchronize()
+    ref = attention.paged_attention(c["q"], "bf16", c["kp"], c["vp"], "bf16", c["bt"], c["L"], c["qsl"], 0.125)
+    assert max_err(out_f64(out), ref) <= 2e-3
