@@ -192,3 +192,26 @@ def test_budget_config_fills_the_budget(lib):
     kv = int(total * util) - non_kv
     used = sum(t.size for t in cfg.tensors)
     assert len(cfg.tensors) == 2 and used <= kv < used + len(cfg.tensors) * spec.page_bytes
+
+
+@pytest.mark.parametrize("hq,hkv,dtype,hpi,per_cu", [
+    (32, 8, _lib.PKV_BF16, 4, 8),       # 4 rows, matrix-core P.V: two waves per SIMD
+    (64, 8, _lib.PKV_BF16, 8, 4),       # single-query 8-row bf16 items keep the vector ALUs: one wave
+    (128, 8, _lib.PKV_BF16, 16, 8),     # 16 rows, matrix-core P.V: two waves
+    (32, 8, _lib.PKV_FP8_E4M3, 4, 8),
+    (64, 8, _lib.PKV_FP8_E4M3, 8, 4),
+    (128, 8, _lib.PKV_FP8_E4M3, 8, 4),  # fp8 items hold at most 8 rows
+    (32, 8, _lib.PKV_INT4, 8, 8),       # INT4 items over two KV heads (8 rows), two waves
+    (16, 8, _lib.PKV_INT4, 4, 8),
+    (12, 3, _lib.PKV_INT4, 4, 8),       # odd KV head count: single-head items
+    (64, 8, _lib.PKV_INT4, 8, 8),
+])
+def test_plan_rows_and_waves_follow_the_kernels(lib, hq, hkv, dtype, hpi, per_cu):
+    """The decode plan's item height and worker count match what the kernels
+    launch for the shape (host arithmetic; 256 compute units without a GPU):
+    two waves per SIMD where the kernel fits 256 registers, one elsewhere."""
+    plan = _lib.PkvDecodePlan()
+    st = lib.pkv_decode_plan_make(64, hq, hkv, 128, 16, dtype, 2048, 0, ctypes.byref(plan))
+    assert st == _lib.PKV_OK and plan.scheme == 1
+    assert plan.heads_per_item == hpi
+    assert plan.num_workers == 256 * per_cu
