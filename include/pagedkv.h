@@ -242,13 +242,19 @@ typedef struct {
   int32_t split_blocks;   /* scheme 0: blocks per split; 1: least blocks per worker */
   int32_t max_splits;     /* partial slots per (row, query head)                  */
   int32_t heads_per_item; /* query heads one work item processes (scheme 1: a
-                             power of two up to 16 dividing the group)     */
+                             power of two dividing the group, up to 16 for
+                             bf16 and 8 for fp8 / INT4; INT4 also takes
+                             twice the group, up to 8, for items over two
+                             adjacent KV heads, which read whole 128-byte
+                             lines; the planner picks that when it can)      */
   int32_t kernel_variant; /* 0: the library's choice.  Tuning only: 1 = vector
                              ALUs for the scores (scheme 0 only); 2..5 =
                              scheme 1 with K/V loads issued 1..4 steps
                              ahead; 6, 7 = scheme 1, 1 or 2 steps ahead,
-                             compiled for two waves per SIMD.  Every variant computes the same result
-                             up to rounding order.                           */
+                             compiled for two waves per SIMD (INT4 items
+                             over two KV heads take the library's choice).
+                             Every variant computes the same result up to
+                             rounding order.                                 */
   size_t workspace_bytes; /* partial (acc, m, l) storage (+ piece counts)         */
   int32_t scheme;         /* 0 or 1, see above                                    */
   int32_t num_workers;    /* scheme 1: workers launched                           */

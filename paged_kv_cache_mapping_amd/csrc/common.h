@@ -122,10 +122,6 @@ __device__ __forceinline__ float group_sum(float v) {
 // ---------------------------------------------------------------- misc
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-__host__ __device__ __forceinline__ int dtype_bytes(int dt) {
-  return dt == PKV_F32 ? 4 : (dt == PKV_BF16 ? 2 : 1);
-}
-
 // Bits per element of a cache type (compile-time use in the kernels).
 __host__ __device__ constexpr int kv_bits(int dt) {
   return dt == PKV_F32 ? 32 : (dt == PKV_BF16 ? 16 : (dt == PKV_FP8_E4M3 ? 8 : 4));
