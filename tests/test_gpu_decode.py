@@ -115,7 +115,7 @@ def test_sliding_window(W):
 
 
 @pytest.mark.parametrize("split", [1, 2, 3, 8, 64])
-@pytest.mark.parametrize("variant", [0, 2, 3, 4, 5])
+@pytest.mark.parametrize("variant", [0, 2, 3, 4, 5, 7])
 def test_any_split_plan_gives_the_same_answer(split, variant):
     say("decode split", split, "variant", variant)
     w = _small(150, B=6, Lmax=1500, Hq=32, Hkv=8, D=128, bs=16, Lmin=200)
@@ -123,6 +123,17 @@ def test_any_split_plan_gives_the_same_answer(split, variant):
     assert err <= TOL["bf16"]
     _, err = _check_attention_only(w, window=333, plan_split=split, variant=variant)
     assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("variant", [0, 2, 5, 6, 7])
+@pytest.mark.parametrize("Hq,Hkv,dtype", [(64, 4, "bf16"), (64, 8, "bf16"), (32, 8, "fp8"), (64, 8, "fp8")])
+def test_variants_over_item_heights_and_dtypes(variant, Hq, Hkv, dtype):
+    """Items of 16 and 8 rows (matrix-core and vector-ALU P.V) and fp8 items
+    under every kernel variant (prefetch depth, one or two waves per SIMD)."""
+    say("decode variants", variant, Hq, Hkv, dtype)
+    w = _small(160 + Hq + Hkv, B=7, Lmax=1300, Hq=Hq, Hkv=Hkv, D=128, bs=16, dtype=dtype, Lmin=100)
+    _, err = _check_attention_only(w, plan_split=2, variant=variant)
+    assert err <= TOL[dtype]
 
 
 @pytest.mark.parametrize("split", [1, 8, 64])
