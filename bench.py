@@ -404,17 +404,58 @@ def bench_hybrid(args, dev):
         b.record()
         torch.cuda.synchronize()
         per_layer[name] = a.elapsed_time(b) / args.steps
+    # the prefill requests alone, in a chunked call of their own (the prefill
+    # tile and its merge): the matrix-core share of the prefill part
+    ql_h = np.diff(w.query_start_loc).astype(np.int64)
+    pre = np.nonzero(ql_h > 1)[0]
+    pre_tok = np.concatenate([np.arange(w.query_start_loc[r], w.query_start_loc[r + 1]) for r in pre])
+    pre_qsl = torch.from_numpy(np.concatenate([[0], np.cumsum(ql_h[pre])]).astype(np.int32)).to(dev)
+    pre_sl = torch.from_numpy(w.seq_lens[pre].astype(np.int32)).to(dev)
+    pre_tok_t = torch.from_numpy(pre_tok.astype(np.int64)).to(dev)
+    pre_t = torch.from_numpy(pre.astype(np.int64)).to(dev)
+    pre_mql = int(ql_h[pre].max())
+    prefill_ms = {}
+    for name in layers:
+        g = group_of[name]
+        pq = inputs[name][0].index_select(0, pre_tok_t).contiguous()
+        ptab = tables[g].index_select(0, pre_t).contiguous()
+        pout = torch.empty_like(pq)
+        nbytes = pkv.chunked_workspace_size(len(pre_tok), len(pre), w.num_q_heads, views[name], pre_mql,
+                                            w.max_seq_len, w.windows[g])
+        pws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+
+        def prefill_call():
+            pkv.paged_attention_chunked(pq, pre_qsl, pre_sl, pre_mql, views[name], ptab, w.max_seq_len,
+                                        w.scale, causal=True, sliding_window=w.windows[g], out=pout,
+                                        workspace=pws)
+        for _ in range(args.warmup):
+            prefill_call()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(args.steps):
+            prefill_call()
+        b.record()
+        torch.cuda.synchronize()
+        prefill_ms[name] = a.elapsed_time(b) / args.steps
     step_bytes = 0
     layer_rec = {}
     total_flops = 0
+    prefill_total_ms = 0.0
     for name in layers:
         W = w.windows[group_of[name]]
         rd, wr, fl = hybrid_layer_bytes(w, W)
         step_bytes += rd + wr
         total_flops += fl
+        prefill_total_ms += prefill_ms[name]
+        pt = fl / (prefill_ms[name] * 1e-3) / 1e12
         layer_rec[name] = {"window": W, "us": round(per_layer[name] * 1e3, 1),
                            "GBps": round((rd + wr) / (per_layer[name] * 1e-3) / 1e9, 1),
-                           "prefill_gflop": round(fl / 1e9, 2)}
+                           "prefill_gflop": round(fl / 1e9, 2),
+                           "prefill_alone_us": round(prefill_ms[name] * 1e3, 1),
+                           "prefill_TFLOPs": round(pt, 1),
+                           "prefill_mfma_frac": round(pt / MFMA_BF16_PEAK_TFLOPS, 4)}
+    prefill_tflops = total_flops / (prefill_total_ms * 1e-3) / 1e12
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dom = max(layers, key=lambda n: per_layer[n])
     rd, wr, _ = hybrid_layer_bytes(w, w.windows[group_of[dom]])
@@ -431,6 +472,11 @@ def bench_hybrid(args, dev):
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "layers": layer_rec,
         "prefill_gflop_per_step": round(total_flops / 1e9, 1),
+        "prefill_part": {"requests": int(len(pre)), "query_tokens": int(len(pre_tok)),
+                         "us_per_step": round(prefill_total_ms * 1e3, 1),
+                         "TFLOPs": round(prefill_tflops, 1), "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                         "mfma_frac": round(prefill_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "flops": "4 D per visible (query token, key, query head): scores and P.V"},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "chunked attention of layer %s (all its kernels)" % dom},
