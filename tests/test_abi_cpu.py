@@ -215,3 +215,19 @@ def test_plan_rows_and_waves_follow_the_kernels(lib, hq, hkv, dtype, hpi, per_cu
     assert st == _lib.PKV_OK and plan.scheme == 1
     assert plan.heads_per_item == hpi
     assert plan.num_workers == 256 * per_cu
+
+
+@pytest.mark.parametrize("rows,dtype,scheme", [
+    (4096, _lib.PKV_BF16, 1),      # the balanced scheme's prefix sums fit in LDS up to 4096 rows
+    (4097, _lib.PKV_BF16, 0),      # beyond: fixed splits on the vector ALUs
+    (4097, _lib.PKV_FP8_E4M3, 0),
+    (4096, _lib.PKV_INT4, 1),
+    (4097, _lib.PKV_INT4, None),   # INT4 runs on the balanced kernels only
+])
+def test_plan_scheme_at_the_row_limit(lib, rows, dtype, scheme):
+    plan = _lib.PkvDecodePlan()
+    st = lib.pkv_decode_plan_make(rows, 32, 8, 128, 16, dtype, 2048, 0, ctypes.byref(plan))
+    if scheme is None:
+        assert st == _lib.PKV_ERR_UNSUPPORTED
+    else:
+        assert st == _lib.PKV_OK and plan.scheme == scheme

@@ -84,6 +84,22 @@ def test_head_dims_and_block_sizes(D, bs):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("B,scheme", [(1500, 1), (4096, 1), (4097, 0)])
+def test_many_rows(B, scheme):
+    """Batches past the rows whose records the balanced kernel keeps in LDS
+    (1024), at its limit (4096 rows of prefix sums in LDS), and one row past
+    it, where the plan falls back to fixed splits.  Rows of at least 32 keys
+    keep the outputs under 0.3, where bf16 rounding of the output stays
+    inside the tolerance (a row of one or two keys returns V rows near 1,
+    whose bf16 half-ulp alone is 3.9e-3)."""
+    say("decode rows", B)
+    w = _small(200 + B, B=B, Lmax=96, Hq=8, Hkv=2, D=128, bs=16, Lmin=32)
+    plan = pkv.decode_plan(w.num_reqs, w.num_q_heads, w.device().cache, w.max_seq_len)
+    assert plan.scheme == scheme
+    _, err = _check_attention_only(w)
+    assert err <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(1, 1), (2, 1), (8, 2), (16, 2), (32, 8), (64, 8), (16, 1)])
 def test_group_sizes(Hq, Hkv):
     say("decode group", Hq, Hkv)
