@@ -231,3 +231,15 @@ def test_plan_scheme_at_the_row_limit(lib, rows, dtype, scheme):
         assert st == _lib.PKV_ERR_UNSUPPORTED
     else:
         assert st == _lib.PKV_OK and plan.scheme == scheme
+
+
+@pytest.mark.parametrize("reqs,dtype,ok", [
+    (4096, _lib.PKV_INT4, True),
+    (4097, _lib.PKV_INT4, False),   # no balanced plan past 4096 rows, and INT4 has no other
+    (4097, _lib.PKV_BF16, True),    # bf16 falls back to the prefill tile and fixed splits
+    (4097, _lib.PKV_FP8_E4M3, True),
+])
+def test_chunked_plans_past_the_row_limit(lib, reqs, dtype, ok):
+    ws = ctypes.c_size_t(0)
+    st = lib.pkv_chunked_workspace_size(2 * reqs, reqs, 32, 8, 128, 16, dtype, 2, 512, 0, ctypes.byref(ws))
+    assert st == (_lib.PKV_OK if ok else _lib.PKV_ERR_UNSUPPORTED)

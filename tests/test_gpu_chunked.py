@@ -56,6 +56,20 @@ def _run_chunked(c, causal, W, scale=0.125):
     return out, ref
 
 
+@pytest.mark.parametrize("R", [4096, 4100])
+def test_chunked_many_requests(R):
+    """Requests of one or two query tokens: 4096 of them run as multi-token
+    decode items (the balanced scheme's row limit); 4100 fall back to the
+    prefill tile for the two-token requests and to fixed splits for the
+    others.  V is scaled so that outputs stay under 0.5 (a request of one
+    or two keys returns V rows), where bf16 output rounding fits the
+    tolerance."""
+    say("chunked many requests", R)
+    c = _chunk_case(900 + R, R=R, Lmax=64, qmax=2, Hq=8, Hkv=2, D=128, bs=16, v_sigma=0.1)
+    out, ref = _run_chunked(c, True, 0)
+    assert max_err(out_f64(out), ref) <= 2e-3
+
+
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("W", [0, 1, 7, 64, 1000])
 def test_chunked_small_cases(causal, W):
