@@ -84,6 +84,20 @@ def test_head_dims_and_block_sizes(D, bs):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_very_long_rows(dtype):
+    """Rows of 131072 and 70001 keys beside a short one: about a thousand
+    pieces per long row, merged in many rounds."""
+    say("decode long rows", dtype)
+    lens = np.array([131072, 70001, 17])
+    nb = int(sum(-(-int(L) // 16) for L in lens)) + 9
+    w = workloads.decode_workload("long", 31, lambda rng: lens.copy(), None, pool_blocks=nb, block_size=16,
+                                  num_q_heads=8, num_kv_heads=2, head_dim=128, cache_dtype=dtype,
+                                  q_dtype="bf16", sigma=0.35)
+    _, err = _check_attention_only(w)
+    assert err <= TOL[dtype]
+
+
 @pytest.mark.parametrize("B,scheme", [(1500, 1), (4096, 1), (4097, 0)])
 def test_many_rows(B, scheme):
     """Batches past the rows whose records the balanced kernel keeps in LDS
