@@ -146,26 +146,44 @@ template <int SRC, int DST, int CE, bool FUSED = false>
 __global__ __launch_bounds__(256) void cache_write_kernel(WriteArgs a) {
   constexpr int kDstBits = kv_bits(DST);
   constexpr int kSrcElt = SRC == PKV_F32 ? 4 : 2;
+  constexpr int kSrcBytes = CE * kSrcElt;
+  static_assert(kSrcBytes % 16 == 0, "source chunks are whole 16-byte vectors");
   const int chunks_per_head = a.head_dim / CE;
   const int chunks_per_plane = a.num_kv_heads * chunks_per_head;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = (int64_t)a.num_tokens * 2 * chunks_per_plane;
+  const bool live = idx < total;
+  const int t = live ? (int)(idx / (2 * chunks_per_plane)) : 0;
+  const int rem = live ? (int)(idx - (int64_t)t * 2 * chunks_per_plane) : 0;
+  const int kv = rem >= chunks_per_plane;
+  const int j = rem - kv * chunks_per_plane;
+  const int h = j / chunks_per_head;
+  const int c = j - h * chunks_per_head;
+  // The new row's bytes do not depend on its slot (padding tokens have rows
+  // too): they are loaded first, so the load overlaps the slot lookup.
+  uint4 raw[kSrcBytes / 16];
+  if (live) {
+    const uint4* s = reinterpret_cast<const uint4*>(
+        reinterpret_cast<const char*>(kv ? a.value : a.key) +
+        ((int64_t)t * a.tok_stride + (int64_t)h * a.head_stride + (int64_t)c * CE) * kSrcElt);
+#pragma unroll
+    for (int i = 0; i < kSrcBytes / 16; ++i) raw[i] = s[i];
+  }
   int64_t slot;
-  int t, rem;
   if constexpr (FUSED) {
     __shared__ int sq[kSlotStage + 1];
     __shared__ int snc[kSlotStage];
     const bool staged = a.num_reqs <= kSlotStage;   // uniform across the workgroup
     if (staged) {
       for (int i = threadIdx.x; i <= a.num_reqs; i += 256) {
-        sq[i] = a.qsl[i];
-        if (i < a.num_reqs) snc[i] = a.nc[i];
+        const int q = a.qsl[i];                       // both loads in flight together
+        const int n = i < a.num_reqs ? a.nc[i] : 0;
+        sq[i] = q;
+        if (i < a.num_reqs) snc[i] = n;
       }
       __syncthreads();
     }
-    if (idx >= total) return;
-    t = (int)(idx / (2 * chunks_per_plane));
-    rem = (int)(idx - (int64_t)t * 2 * chunks_per_plane);
+    if (!live) return;
     bool owned;
     slot = token_slot(t, staged ? sq : a.qsl, staged ? snc : a.nc, a.bt, a.bt_stride, a.num_reqs,
                       a.bs_log2, a.num_blocks, owned);
@@ -174,21 +192,14 @@ __global__ __launch_bounds__(256) void cache_write_kernel(WriteArgs a) {
       if (owned && slot < 0 && a.err) atomicAdd(a.err, 1);
     }
   } else {
-    if (idx >= total) return;
-    t = (int)(idx / (2 * chunks_per_plane));
-    rem = (int)(idx - (int64_t)t * 2 * chunks_per_plane);
+    if (!live) return;
     slot = a.slots[t];
   }
-  const int kv = rem >= chunks_per_plane;
-  const int j = rem - kv * chunks_per_plane;
-  const int h = j / chunks_per_head;
-  const int c = j - h * chunks_per_head;
   if (slot < 0 || slot >= a.num_slots) return;
   const int64_t blk = slot >> a.bs_log2;
   const int64_t off = slot & ((1 << a.bs_log2) - 1);
 
-  const char* src = reinterpret_cast<const char*>(kv ? a.value : a.key) +
-                    ((int64_t)t * a.tok_stride + (int64_t)h * a.head_stride + (int64_t)c * CE) * kSrcElt;
+  const char* src = reinterpret_cast<const char*>(raw);   // the row's bytes, in registers
   // element index times bits over 8 (INT4 chunks start at even elements)
   char* dst = reinterpret_cast<char*>(kv ? a.vdst : a.kdst) +
               (blk * a.block_stride + (off * a.num_kv_heads + h) * a.head_dim + (int64_t)c * CE) * kDstBits / 8;
