@@ -50,6 +50,19 @@ __device__ __forceinline__ int64_t token_slot(int t, const int* q, const int* nc
 // One thread per token of the step.  The owning request is found by binary
 // search over query_start_loc; all reads stay inside the arrays the caller
 // described (block-table row index < bt_stride, request index < num_reqs).
+// query_start_loc[0..R] and num_computed[0..R) into LDS by a workgroup of
+// 256 threads, both loads of an entry issued before either store, so the
+// staging costs one memory round trip (R <= kSlotStage).
+__device__ __forceinline__ void stage_requests(const int32_t* qsl, const int32_t* nc, int num_reqs,
+                                               int* sq, int* snc) {
+  for (int i = threadIdx.x; i <= num_reqs; i += 256) {
+    const int q = qsl[i];
+    const int n = i < num_reqs ? nc[i] : 0;
+    sq[i] = q;
+    if (i < num_reqs) snc[i] = n;
+  }
+}
+
 __global__ __launch_bounds__(256) void slot_mapping_kernel(
     const int32_t* __restrict__ bt, int32_t bt_stride, int32_t num_reqs,
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ nc,
@@ -61,10 +74,7 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(
   __shared__ int snc[kSlotStage];
   const bool staged = num_reqs <= kSlotStage;
   if (staged) {
-    for (int i = threadIdx.x; i <= num_reqs; i += 256) {
-      sq[i] = qsl[i];
-      if (i < num_reqs) snc[i] = nc[i];
-    }
+    stage_requests(qsl, nc, num_reqs, sq, snc);
     __syncthreads();
   }
   const int* q = staged ? sq : qsl;
@@ -175,12 +185,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(WriteArgs a) {
     __shared__ int snc[kSlotStage];
     const bool staged = a.num_reqs <= kSlotStage;   // uniform across the workgroup
     if (staged) {
-      for (int i = threadIdx.x; i <= a.num_reqs; i += 256) {
-        const int q = a.qsl[i];                       // both loads in flight together
-        const int n = i < a.num_reqs ? a.nc[i] : 0;
-        sq[i] = q;
-        if (i < a.num_reqs) snc[i] = n;
-      }
+      stage_requests(a.qsl, a.nc, a.num_reqs, sq, snc);
       __syncthreads();
     }
     if (!live) return;
