@@ -235,8 +235,12 @@ PKV_API int pkv_copy_blocks(const pkv_cache* cache, const int32_t* src_ids,
  *   split_blocks blocks; one work item per (row, head group, split).
  * scheme 1 (balanced): num_workers workers each take an equal contiguous
  *   share (at least split_blocks blocks) of all (row, KV head group, block)
- *   units; a row is cut wherever a share ends.  Used with bf16 / fp8 caches,
- *   head_dim a multiple of 32 and block sizes that are multiples of 16.
+ *   units; a row is cut wherever a share ends.  Used with block sizes that
+ *   are multiples of 16 and bf16 / fp8 caches whose head_dim is a multiple
+ *   of 32 with rows of at least 64 bytes, or INT4 caches with head_dim 128,
+ *   for at most 4096 rows (the rows' prefix sums are kept in LDS).  Other
+ *   bf16 / fp8 / f32 shapes and more rows take scheme 0; INT4 has no
+ *   scheme 0 and returns PKV_ERR_UNSUPPORTED there.
  */
 typedef struct {
   int32_t split_blocks;   /* scheme 0: blocks per split; 1: least blocks per worker */
@@ -380,8 +384,8 @@ PKV_API int pkv_chunked_workspace_size(int32_t num_tokens, int32_t num_reqs,
  * sliding_window   0, or W: keys >= p - W + 1 only.
  * workspace        at least pkv_chunked_workspace_size(...) bytes.
  * Invalid rows (q_len > seq_len, lengths out of range, missing blocks) get NaN.
- * INT4 caches: the decode form's shapes (head_dim 128); others return
- * PKV_ERR_UNSUPPORTED.
+ * INT4 caches: the decode form's shapes (head_dim 128, at most 4096
+ * requests); others return PKV_ERR_UNSUPPORTED.
  */
 PKV_API int pkv_paged_attention_chunked(void* out, const void* q, int32_t q_dtype,
                                 int32_t num_tokens, int32_t num_q_heads,
