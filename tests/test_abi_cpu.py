@@ -243,3 +243,20 @@ def test_chunked_plans_past_the_row_limit(lib, reqs, dtype, ok):
     ws = ctypes.c_size_t(0)
     st = lib.pkv_chunked_workspace_size(2 * reqs, reqs, 32, 8, 128, 16, dtype, 2, 512, 0, ctypes.byref(ws))
     assert st == (_lib.PKV_OK if ok else _lib.PKV_ERR_UNSUPPORTED)
+
+
+@pytest.mark.parametrize("d,bs,dtype,scheme", [
+    (32, 16, _lib.PKV_BF16, 1),        # 64-byte rows
+    (32, 16, _lib.PKV_FP8_E4M3, 0),    # 32-byte rows: fixed splits
+    (64, 16, _lib.PKV_FP8_E4M3, 1),
+    (128, 8, _lib.PKV_BF16, 0),        # blocks of 8 tokens: fixed splits
+    (128, 32, _lib.PKV_INT4, 1),
+    (64, 16, _lib.PKV_INT4, None),     # the one INT4 head size is 128
+])
+def test_plan_scheme_by_head_size_and_block(lib, d, bs, dtype, scheme):
+    plan = _lib.PkvDecodePlan()
+    st = lib.pkv_decode_plan_make(64, 32, 8, d, bs, dtype, 2048, 0, ctypes.byref(plan))
+    if scheme is None:
+        assert st == _lib.PKV_ERR_UNSUPPORTED
+    else:
+        assert st == _lib.PKV_OK and plan.scheme == scheme
