@@ -1249,7 +1249,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
           for (int t = 0; t < VEPL; t += 4) {
             const f32x4_t v4 = {(accm[t][i] + off) * a.v_scale, (accm[t + 1][i] + off) * a.v_scale,
                                 (accm[t + 2][i] + off) * a.v_scale, (accm[t + 3][i] + off) * a.v_scale};
-            __builtin_nontemporal_store(v4, reinterpret_cast<f32x4_t*>(dst + t));
+            *reinterpret_cast<f32x4_t*>(dst + t) = v4;
           }
         }
       }
@@ -1267,8 +1267,9 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
           store_out<PKV_BF16, VEPL>(a.out, out_row + vsub * VEPL, o);
         }
       } else {
-        // acc rows: full 128-byte lines, streamed past the caches (the
-        // combine kernel reads them once)
+        // acc rows: full 128-byte lines, written through the caches: the
+        // merge reads them right after, mostly from L2 (streaming them past
+        // the caches made the merge reread them from HBM)
 #pragma unroll
         for (int h = 0; h < RI; ++h) {
           const int64_t pr = (((int64_t)b * kvgroups + kvg) * RI + h) * a.max_splits + piece;
@@ -1278,7 +1279,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
             // partials hold dequantised V sums (the fp8 V scale applied)
             const f32x4_t v4 = {acc[h][e] * a.v_scale, acc[h][e + 1] * a.v_scale,
                                 acc[h][e + 2] * a.v_scale, acc[h][e + 3] * a.v_scale};
-            __builtin_nontemporal_store(v4, reinterpret_cast<f32x4_t*>(dst + e));
+            *reinterpret_cast<f32x4_t*>(dst + e) = v4;
           }
         }
       }
@@ -1294,7 +1295,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
           if (e / 4 == lane) v[e % 4] = e < RI ? mh[e] : lh[e - RI];
         if constexpr (2 * RI >= 4) {
           const f32x4_t v4 = {v[0], v[1], v[2], v[3]};
-          __builtin_nontemporal_store(v4, reinterpret_cast<f32x4_t*>(ml + 4 * lane));
+          *reinterpret_cast<f32x4_t*>(ml + 4 * lane) = v4;
         } else {
           ml[0] = v[0];
           ml[1] = v[1];
