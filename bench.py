@@ -60,7 +60,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--split-blocks", type=int, default=0, help="override the decode split (tuning)")
-    p.add_argument("--variant", type=int, default=0, help="decode kernel variant (tuning)")
+    p.add_argument("--variant", type=int, default=-1,
+                   help="decode kernel variant (default: 8, streaming K/V loads, for bf16 caches without shared blocks)")
     p.add_argument("--workers", type=int, default=0, help="balanced-scheme workers (tuning)")
     p.add_argument("--lead", type=int, default=-1, help="balanced scheme: full-share workers (tuning)")
     p.add_argument("--trail-pct", type=int, default=0, help="balanced scheme: other share %% (tuning)")
@@ -516,9 +517,13 @@ def main():
     npools = len(pools)
 
     plan = pkv.decode_plan(w.num_reqs, w.num_q_heads, base.cache, w.max_seq_len)
+    # no block is read by two rows unless prefixes are shared: then the K/V
+    # loads may stream past the caches (plan variant 8, bf16 caches)
+    variant = args.variant if args.variant >= 0 else (
+        8 if w.cache_dtype == "bf16" and args.workload != "prefix" else 0)
     pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, base.cache, w.max_seq_len,
                   split_blocks=args.split_blocks or None, num_workers=args.workers or None,
-                  kernel_variant=args.variant,
+                  kernel_variant=variant,
                   lead_workers=args.lead if args.lead >= 0 else None,
                   trail_share_pct=args.trail_pct or None,
                   heads_per_item=args.heads_per_item or None)
@@ -670,6 +675,7 @@ def main():
                    "scheme": int(plan.scheme), "workers": int(plan.num_workers),
                    "split_blocks": int(plan.split_blocks), "max_splits": int(plan.max_splits),
                    "lead_workers": int(plan.lead_workers), "trail_share_pct": int(plan.trail_share_pct),
+                   "kernel_variant": int(plan.kernel_variant),
                    **extra},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_attention": {"split_kernel_us": round(split_ms * 1e3, 2),

@@ -256,8 +256,13 @@ typedef struct {
                              scheme 1 with K/V loads issued 1..4 steps
                              ahead; 6, 7 = scheme 1, 1 or 2 steps ahead,
                              compiled for two waves per SIMD (INT4 items
-                             over two KV heads take the library's choice).
-                             Every variant computes the same result up to
+                             over two KV heads take the library's choice);
+                             8 = the library's choice with non-temporal
+                             K/V loads for bf16 caches: faster when no
+                             block is read by more than one row, much
+                             slower when rows share blocks (prefix
+                             sharing), so the caller decides.  Every
+                             variant computes the same result up to
                              rounding order.                                 */
   size_t workspace_bytes; /* partial (acc, m, l) storage (+ piece counts)         */
   int32_t scheme;         /* 0 or 1, see above                                    */

@@ -141,7 +141,7 @@ static int make_plan(int rows, int hq, int hkv, int d, int bs, int kv_dtype, int
 static int check_plan(const pkv_decode_plan* plan, int rows, int hq, int hkv, int d, int bs,
                       int kv_dtype, int max_seq_len, int window, int extra) {
   if (!plan) return PKV_ERR_NULL;
-  if (plan->kernel_variant < 0 || plan->kernel_variant > 7) return PKV_ERR_SHAPE;
+  if (plan->kernel_variant < 0 || plan->kernel_variant > 8) return PKV_ERR_SHAPE;
   const int group = hq / hkv;
   const int nvis = max_visible_blocks(max_seq_len, bs, window, extra);
   if (plan->scheme == 1) {

@@ -848,6 +848,33 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));   // 4 bf16, 16x16x16
 // P.V on the matrix cores at head size 128: bf16, fp8 and INT4 caches (fp8
 // and INT4 widened to bf16 in registers, exact), except bf16 / fp8
 // single-query items of 8 rows (see decode_flat_body).
+// K/V loads of the balanced kernel.  With NTL (kernel variant 8, bf16) they
+// carry a non-temporal hint: a stream read once then does not displace what
+// is reused from the caches (table entries, staged queries, the partials the
+// merge reads next); on the Llama-3-8B batch the split kernel went from 64.2
+// to 59.4 us.  Where blocks are shared by many rows (prefix sharing) the hint
+// sends every row back to HBM (75 -> 146 us there), and 8-byte fp8 loads
+// were slower with it too, so it is the caller's choice, not the default.
+template <typename T>
+__device__ __forceinline__ T load_stream(const char* p) {
+  if constexpr (sizeof(T) == 16) {
+    typedef unsigned v4_t __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const v4_t*>(p)));
+  } else if constexpr (sizeof(T) == 8) {
+    typedef unsigned v2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const v2_t*>(p)));
+  } else {
+    static_assert(sizeof(T) == 4, "4, 8 or 16 bytes per lane");
+    return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(p)));
+  }
+}
+
+template <typename T, bool NTL>
+__device__ __forceinline__ T kv_load(const char* p) {
+  if constexpr (NTL) return load_stream<T>(p);
+  else return *reinterpret_cast<const T*>(p);
+}
+
 __host__ __device__ constexpr bool mfma_pv(int d, int kv, int gt, int qt) {
   return d == 128 && (kv_bits(kv) == 4 || ((kv == PKV_BF16 || kv == PKV_FP8_E4M3) && !(gt == 8 && qt == 1)));
 }
@@ -973,7 +1000,7 @@ __device__ inline Shares make_shares(long long U, int W, int lead, int pct, int 
   return s;
 }
 
-template <int D, int GT, int KV, int DEPTH, int QT = 1>
+template <int D, int GT, int KV, int DEPTH, int QT = 1, bool NTL = false>
 __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
   using S = MfmaShape<D, GT, KV>;
   constexpr int NC = S::NC, VLPR = S::VLPR, VRPW = S::VRPW, VU = S::VU, VEPL = S::VEPL;
@@ -1420,7 +1447,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
         for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
           for (int j = 0; j < NC / 4; ++j) {
-            const uint4 t = *reinterpret_cast<const uint4*>(kp + k_lane + hh * S::kHeadBytes + j * 64);
+            const uint4 t = kv_load<uint4, NTL>(kp + k_lane + hh * S::kHeadBytes + j * 64);
             const int c0 = hh * NC + 4 * j;
             bf.k[c0][0] = t.x; bf.k[c0 + 1][0] = t.y; bf.k[c0 + 2][0] = t.z; bf.k[c0 + 3][0] = t.w;
           }
@@ -1428,10 +1455,10 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           if constexpr (KB == 16) {
-            const uint4 t = *reinterpret_cast<const uint4*>(kp + k_lane + c * 64);
+            const uint4 t = kv_load<uint4, NTL>(kp + k_lane + c * 64);
             bf.k[c][0] = t.x; bf.k[c][1] = t.y; bf.k[c][2] = t.z; bf.k[c][3] = t.w;
           } else {
-            const uint2 t = *reinterpret_cast<const uint2*>(kp + k_lane + c * 32);
+            const uint2 t = kv_load<uint2, NTL>(kp + k_lane + c * 32);
             bf.k[c][0] = t.x; bf.k[c][1] = t.y;
           }
         }
@@ -1440,8 +1467,8 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
       for (int u = 0; u < VU; ++u)
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh)
-          bf.v[u][hh] = *reinterpret_cast<const VT*>(vp + v_lane + hh * S::kHeadBytes +
-                                                    (int64_t)u * (RB ? TPRV : VRPW) * row_bytes);
+          bf.v[u][hh] = kv_load<VT, NTL>(vp + v_lane + hh * S::kHeadBytes +
+                                         (int64_t)u * (RB ? TPRV : VRPW) * row_bytes);
     };
 
     // V as floats, zero for keys outside the piece's span
@@ -1767,10 +1794,10 @@ __global__ __launch_bounds__(64) void decode_flat_kernel(DecodeArgs a) {
   decode_flat_body<D, GT, KV, DEPTH, QT>(a);
 }
 
-template <int D, int GT, int KV, int DEPTH, int QT = 1>
+template <int D, int GT, int KV, int DEPTH, int QT = 1, bool NTL = false>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_flat_kernel_2w(
     DecodeArgs a) {
-  decode_flat_body<D, GT, KV, DEPTH, QT>(a);
+  decode_flat_body<D, GT, KV, DEPTH, QT, NTL>(a);
 }
 
 // Merge phase of the balanced scheme: one wave per (row, head group) with
@@ -1971,6 +1998,12 @@ void launch_stream(const DecodeArgs& a, int workers, hipStream_t s) {
     case 5: decode_flat_kernel<D, GT, KV, 4, QT><<<workers, 64, lds, s>>>(a); break;
     case 6: decode_flat_kernel_2w<D, GT, KV, 1, QT><<<workers, 64, lds, s>>>(a); break;
     case 7: decode_flat_kernel_2w<D, GT, KV, 2, QT><<<workers, 64, lds, s>>>(a); break;
+    case 8:   // the default form with non-temporal K/V loads (bf16 items on two waves)
+      if constexpr (KV == PKV_BF16 && two_waves(D, KV, GT, QT)) {
+        decode_flat_kernel_2w<D, GT, KV, kDepth, QT, true><<<workers, 64, lds, s>>>(a);
+        break;
+      }
+      [[fallthrough]];
     default:
       // up to four rows per item the plan counts on two waves per SIMD, so
       // the kernel must fit in 256 registers (the fp8 build does not unless

@@ -145,7 +145,7 @@ def test_sliding_window(W):
 
 
 @pytest.mark.parametrize("split", [1, 2, 3, 8, 64])
-@pytest.mark.parametrize("variant", [0, 2, 3, 4, 5, 7])
+@pytest.mark.parametrize("variant", [0, 2, 3, 4, 5, 7, 8])
 def test_any_split_plan_gives_the_same_answer(split, variant):
     say("decode split", split, "variant", variant)
     w = _small(150, B=6, Lmax=1500, Hq=32, Hkv=8, D=128, bs=16, Lmin=200)
@@ -155,7 +155,7 @@ def test_any_split_plan_gives_the_same_answer(split, variant):
     assert err <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("variant", [0, 2, 5, 6, 7])
+@pytest.mark.parametrize("variant", [0, 2, 5, 6, 7, 8])
 @pytest.mark.parametrize("Hq,Hkv,dtype", [(64, 4, "bf16"), (64, 8, "bf16"), (32, 8, "fp8"), (64, 8, "fp8")])
 def test_variants_over_item_heights_and_dtypes(variant, Hq, Hkv, dtype):
     """Items of 16 and 8 rows (matrix-core and vector-ALU P.V) and fp8 items
