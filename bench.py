@@ -60,8 +60,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--split-blocks", type=int, default=0, help="override the decode split (tuning)")
-    p.add_argument("--variant", type=int, default=-1,
-                   help="decode kernel variant (default: 8, streaming K/V loads, for bf16 caches without shared blocks)")
+    p.add_argument("--shared-blocks", action="store_true",
+                   help="plan as if blocks could be shared (no PKV_PLAN_BLOCKS_NOT_SHARED); "
+                        "the prefix workload always is")
     p.add_argument("--workers", type=int, default=0, help="balanced-scheme workers (tuning)")
     p.add_argument("--lead", type=int, default=-1, help="balanced scheme: full-share workers (tuning)")
     p.add_argument("--trail-pct", type=int, default=0, help="balanced scheme: other share %% (tuning)")
@@ -107,6 +108,32 @@ def algorithmic_bytes(w):
     write = int(B * Hkv * D * 2 * (src + elt)) + B * 8  # read + write K and V rows, slots
     return dict(kv=kv, split=split, combine=combine, slot=slot, write=write,
                 step=split + combine + slot + write)
+
+
+def decode_plan_for(pkv, w, cache, shared_blocks=False, **tune):
+    """The plan the decode line times: the library's plan for the workload,
+    declaring PKV_PLAN_BLOCKS_NOT_SHARED unless blocks are shared (the
+    prefix workload) or the caller says they may be; `tune` overrides
+    fields through pkv.tune_plan (None keeps the library's value)."""
+    not_shared = not shared_blocks and not w.info.get("shares_blocks", False)
+    plan = pkv.decode_plan(w.num_reqs, w.num_q_heads, cache, w.max_seq_len,
+                           blocks_not_shared=not_shared)
+    if any(v is not None for v in tune.values()):
+        pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, cache, w.max_seq_len, **tune)
+    return plan
+
+
+def decode_step_fn(pkv, w, base, plan, ws, out, slots):
+    """One timed decode step over a (cache view, block table) pair: slot
+    mapping and the write of the step's K/V rows in one launch, then the
+    decode attention's two phases."""
+    def step(cache, bt):
+        pkv.slot_mapping_cache_write(bt, base.query_start_loc, base.num_computed, base.new_k,
+                                     base.new_v, cache, out=slots)
+        pkv.paged_attention_decode_partials(base.q, cache, bt, base.seq_lens, w.max_seq_len, w.scale,
+                                            plan, ws, out)
+        pkv.paged_attention_decode_combine(out, base.seq_lens, w.block_size, plan, ws)
+    return step
 
 
 def cpu_baseline(w, sample_seqs, min_seconds=10.0):
@@ -516,29 +543,18 @@ def main():
         pools = rotating_pools(w, base, dev, POOLS)
     npools = len(pools)
 
-    plan = pkv.decode_plan(w.num_reqs, w.num_q_heads, base.cache, w.max_seq_len)
-    # no block is read by two rows unless prefixes are shared: then the K/V
-    # loads may stream past the caches (plan variant 8, bf16 caches)
-    variant = args.variant if args.variant >= 0 else (
-        8 if w.cache_dtype == "bf16" and args.workload != "prefix" else 0)
-    pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, base.cache, w.max_seq_len,
-                  split_blocks=args.split_blocks or None, num_workers=args.workers or None,
-                  kernel_variant=variant,
-                  lead_workers=args.lead if args.lead >= 0 else None,
-                  trail_share_pct=args.trail_pct or None,
-                  heads_per_item=args.heads_per_item or None)
+    plan = decode_plan_for(pkv, w, base.cache, shared_blocks=args.shared_blocks,
+                           split_blocks=args.split_blocks or None, num_workers=args.workers or None,
+                           lead_workers=args.lead if args.lead >= 0 else None,
+                           trail_share_pct=args.trail_pct or None,
+                           heads_per_item=args.heads_per_item or None)
     ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
     out = torch.empty_like(base.q)
     slots = torch.empty(w.num_reqs, dtype=torch.int64, device=dev)
+    run_step = decode_step_fn(pkv, w, base, plan, ws, out, slots)
 
     def step(i):
-        cache, bt = pools[i % npools]
-        # slot mapping and the write of the step's K/V rows in one launch
-        pkv.slot_mapping_cache_write(bt, base.query_start_loc, base.num_computed, base.new_k, base.new_v,
-                                     cache, out=slots)
-        pkv.paged_attention_decode_partials(base.q, cache, bt, base.seq_lens, w.max_seq_len, w.scale,
-                                            plan, ws, out)
-        pkv.paged_attention_decode_combine(out, base.seq_lens, w.block_size, plan, ws)
+        run_step(*pools[i % npools])
 
     for i in range(args.warmup):
         step(i)
@@ -675,7 +691,7 @@ def main():
                    "scheme": int(plan.scheme), "workers": int(plan.num_workers),
                    "split_blocks": int(plan.split_blocks), "max_splits": int(plan.max_splits),
                    "lead_workers": int(plan.lead_workers), "trail_share_pct": int(plan.trail_share_pct),
-                   "kernel_variant": int(plan.kernel_variant),
+                   "plan_flags": int(plan.flags),
                    **extra},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_attention": {"split_kernel_us": round(split_ms * 1e3, 2),

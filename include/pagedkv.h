@@ -228,20 +228,41 @@ PKV_API int pkv_copy_blocks(const pkv_cache* cache, const int32_t* src_ids,
 /*
  * Plan of the decode attention: how each row's visible blocks are cut into
  * pieces that are folded independently and merged afterwards, and the
- * workspace the partial results need.  Depends only on the arguments and on
- * the current device's compute-unit count.
+ * workspace the partial results need [P § Handling Softmax Across Blocks:
+ * one softmax normaliser spans every block of a row; W-zh §
+ * Worker与ModelRunner的协作: kernels tile the keys with an online softmax].
+ * Depends only on the arguments and on the current device's compute-unit
+ * count.
  *
  * scheme 0 (fixed splits): row r's visible blocks are cut into splits of
  *   split_blocks blocks; one work item per (row, head group, split).
- * scheme 1 (balanced): num_workers workers each take an equal contiguous
- *   share (at least split_blocks blocks) of all (row, KV head group, block)
- *   units; a row is cut wherever a share ends.  Used with block sizes that
- *   are multiples of 16 and bf16 / fp8 caches whose head_dim is a multiple
- *   of 32 with rows of at least 64 bytes, or INT4 caches with head_dim 128,
- *   for at most 4096 rows (the rows' prefix sums are kept in LDS).  Other
- *   bf16 / fp8 / f32 shapes and more rows take scheme 0; INT4 has no
- *   scheme 0 and returns PKV_ERR_UNSUPPORTED there.
+ * scheme 1 (balanced): num_workers workers each take a contiguous share (at
+ *   least split_blocks blocks) of all (row, KV head group, block) units; a
+ *   row is cut wherever a share ends.  Used with block sizes that are
+ *   multiples of 16 and bf16 / fp8 caches whose head_dim is a multiple of 32
+ *   with rows of at least 64 bytes, or INT4 caches with head_dim 128, for at
+ *   most 4096 rows (the rows' prefix sums are kept in LDS).  Other bf16 /
+ *   fp8 / f32 shapes and more rows take scheme 0; INT4 has no scheme 0 and
+ *   returns PKV_ERR_UNSUPPORTED there.
+ *
+ * The planner fills every field.  A caller may change split_blocks,
+ * num_workers, lead_workers, trail_share_pct or heads_per_item (for tuning)
+ * and must then call pkv_decode_plan_resize, which recomputes max_splits and
+ * workspace_bytes from them.
  */
+
+/* Flags of pkv_decode_plan_make. */
+#define PKV_PLAN_BLOCKS_NOT_SHARED 1  /* the caller guarantees that no physical
+                                         block is read by two rows of one call
+                                         (no shared prefix blocks [W-zh §
+                                         PagedAttention与Block管理]); bf16
+                                         caches then read K/V with
+                                         non-temporal loads, which stream past
+                                         the caches.  Results are identical
+                                         either way; a wrong promise costs
+                                         time only (shared blocks are then
+                                         re-read from HBM by every row).      */
+
 typedef struct {
   int32_t split_blocks;   /* scheme 0: blocks per split; 1: least blocks per worker */
   int32_t max_splits;     /* partial slots per (row, query head)                  */
@@ -251,19 +272,7 @@ typedef struct {
                              twice the group, up to 8, for items over two
                              adjacent KV heads, which read whole 128-byte
                              lines; the planner picks that when it can)      */
-  int32_t kernel_variant; /* 0: the library's choice.  Tuning only: 1 = vector
-                             ALUs for the scores (scheme 0 only); 2..5 =
-                             scheme 1 with K/V loads issued 1..4 steps
-                             ahead; 6, 7 = scheme 1, 1 or 2 steps ahead,
-                             compiled for two waves per SIMD (INT4 items
-                             over two KV heads take the library's choice);
-                             8 = the library's choice with non-temporal
-                             K/V loads for bf16 caches: faster when no
-                             block is read by more than one row, much
-                             slower when rows share blocks (prefix
-                             sharing), so the caller decides.  Every
-                             variant computes the same result up to
-                             rounding order.                                 */
+  int32_t flags;          /* PKV_PLAN_* bits given to pkv_decode_plan_make     */
   size_t workspace_bytes; /* partial (acc, m, l) storage (+ piece counts)         */
   int32_t scheme;         /* 0 or 1, see above                                    */
   int32_t num_workers;    /* scheme 1: workers launched                           */
@@ -277,13 +286,30 @@ typedef struct {
 /*
  * Fill `plan` for a decode (one query token per row) over `num_rows` rows of
  * a cache of `kv_dtype`.  max_seq_len bounds every seq_lens entry;
- * sliding_window 0 = full attention.
+ * sliding_window 0 = full attention; flags: PKV_PLAN_* bits (0 = none).
+ * Returns PKV_ERR_SHAPE for unknown flags.
  */
 PKV_API int pkv_decode_plan_make(int32_t num_rows, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim,
                                  int32_t block_size, int32_t kv_dtype,
                                  int32_t max_seq_len, int32_t sliding_window,
-                                 pkv_decode_plan* plan);
+                                 int32_t flags, pkv_decode_plan* plan);
+
+/*
+ * After a caller changed a plan's tuning fields (split_blocks, num_workers,
+ * lead_workers, trail_share_pct, heads_per_item), recompute max_splits and
+ * workspace_bytes for the same num_rows, num_q_heads, head_dim, block_size,
+ * max_seq_len and sliding_window that made it.  Host arithmetic only.
+ * Returns PKV_ERR_SHAPE for fields no kernel takes (split_blocks outside
+ * 1..64 for scheme 0 or below 1 for scheme 1, heads_per_item not dividing
+ * num_q_heads, workers below 1, lead_workers outside 0..num_workers,
+ * trail_share_pct outside 1..100); whether the heads_per_item suits the
+ * cache is checked by the attention calls.
+ */
+PKV_API int pkv_decode_plan_resize(int32_t num_rows, int32_t num_q_heads,
+                                   int32_t head_dim, int32_t block_size,
+                                   int32_t max_seq_len, int32_t sliding_window,
+                                   pkv_decode_plan* plan);
 
 /*
  * Step 3 (decode form) -- paged attention, one query token per sequence

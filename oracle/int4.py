@@ -11,7 +11,9 @@ The pages fix nothing else.  Readings taken here:
 * Element value = (u - 8) * s: u is the unsigned 4-bit code 0..15 (zero
   point 8, so values -8 s .. 7 s) and s a per-tensor scale that is chosen
   offline -- the calibration the page speaks of; the synthetic workloads
-  take s = amax / 7.  Nothing about s is computed at write time.
+  draw codes directly and take s = sigma / 2 (sigma the data's standard
+  deviation, 1 / sqrt(128) for the Llama-shaped workloads).  Nothing about
+  s is computed at write time.
 * Quantisation: y = float32(x) * inv_s with inv_s = float32(1 / float32(s))
   (the float32 product, as for the FP8 cache); k = the integer nearest to y,
   ties to the even integer, limited to [-8, 7]; u = k + 8.  A NaN element

@@ -72,19 +72,6 @@ def slot_mapping(block_table, query_start_loc, num_computed, block_size,
     return slots, errors
 
 
-def positions(query_start_loc, num_computed, num_tokens=None):
-    """Sequence position of every token of the step (-1 for padding)."""
-    qsl = np.asarray(query_start_loc)
-    nc = np.asarray(num_computed)
-    R = len(nc)
-    T = int(qsl[R]) if num_tokens is None else int(num_tokens)
-    pos = np.full(T, -1, dtype=np.int64)
-    for r in range(R):
-        for t in range(int(qsl[r]), int(qsl[r + 1])):
-            pos[t] = int(nc[r]) + (t - int(qsl[r]))
-    return pos
-
-
 def convert_for_cache(x, src_dtype, cache_dtype, scale=1.0):
     """Source elements -> the cache's storage bits.
 

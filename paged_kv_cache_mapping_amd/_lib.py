@@ -17,6 +17,9 @@ PKV_ERR_UNSUPPORTED = -4
 PKV_ERR_WORKSPACE = -5
 PKV_ERR_HIP = -6
 
+# pkv_decode_plan_make flags
+PKV_PLAN_BLOCKS_NOT_SHARED = 1
+
 # pkv_dtype
 PKV_F32 = 0
 PKV_BF16 = 1
@@ -44,7 +47,7 @@ class PkvDecodePlan(ctypes.Structure):
         ("split_blocks", ctypes.c_int32),
         ("max_splits", ctypes.c_int32),
         ("heads_per_item", ctypes.c_int32),
-        ("kernel_variant", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
         ("scheme", ctypes.c_int32),
         ("num_workers", ctypes.c_int32),
@@ -69,8 +72,9 @@ SIGNATURES = {
     "pkv_cache_write": (_int, [_vp, _vp, _i32, _i64, _i64, _vp, _i32, ctypes.POINTER(PkvCache), _vp]),
     "pkv_slot_mapping_cache_write": (_int, [_vp, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i64,
                                             _i64, ctypes.POINTER(PkvCache), _vp]),
-    "pkv_decode_plan_make": (_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+    "pkv_decode_plan_make": (_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                     ctypes.POINTER(PkvDecodePlan)]),
+    "pkv_decode_plan_resize": (_int, [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(PkvDecodePlan)]),
     "pkv_paged_attention_decode": (_int, [_vp, _vp, _i32, _i32, _i32, ctypes.POINTER(PkvCache), _vp, _i32,
                                           _vp, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pkv_paged_attention_decode_partials": (_int, [_vp, _vp, _i32, _i32, _i32, ctypes.POINTER(PkvCache), _vp,

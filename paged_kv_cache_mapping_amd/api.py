@@ -12,7 +12,8 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_INT4, PkvCache, PkvDecodePlan, check, load
+from ._lib import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_INT4, PKV_PLAN_BLOCKS_NOT_SHARED, PkvCache,
+                   PkvDecodePlan, check, load)
 
 _DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16, torch.uint8: PKV_FP8_E4M3}
 if hasattr(torch, "float8_e4m3fn"):
@@ -180,29 +181,29 @@ def copy_blocks(src_ids, dst_ids, cache, err_count=None):
         _stream(src_ids.device)))
 
 
-def decode_plan(num_rows, num_q_heads, cache, max_seq_len, sliding_window=0):
+def decode_plan(num_rows, num_q_heads, cache, max_seq_len, sliding_window=0, blocks_not_shared=False):
+    """The library's plan (pkv_decode_plan_make); blocks_not_shared sets
+    PKV_PLAN_BLOCKS_NOT_SHARED (no block is read by two rows of a call)."""
     lib = load()
     plan = PkvDecodePlan()
+    flags = PKV_PLAN_BLOCKS_NOT_SHARED if blocks_not_shared else 0
     check("pkv_decode_plan_make", lib.pkv_decode_plan_make(
         num_rows, num_q_heads, cache.num_kv_heads, cache.head_dim, cache.block_size,
-        cache.dtype, max_seq_len, sliding_window, ctypes.byref(plan)))
+        cache.dtype, max_seq_len, sliding_window, flags, ctypes.byref(plan)))
     return plan
 
 
 def tune_plan(plan, num_rows, num_q_heads, cache, max_seq_len, sliding_window=0,
-              split_blocks=None, num_workers=None, kernel_variant=None, lead_workers=None,
-              trail_share_pct=None, heads_per_item=None):
-    """Override a plan's tuning fields and recompute the sizes they imply.
+              split_blocks=None, num_workers=None, lead_workers=None, trail_share_pct=None,
+              heads_per_item=None):
+    """Override a plan's tuning fields; the library recomputes the sizes they
+    imply (pkv_decode_plan_resize).
 
     Scheme 0: split_blocks = blocks per split.  Scheme 1: split_blocks =
     least blocks per worker, num_workers = workers launched, lead_workers /
-    trail_share_pct = unequal shares (see pagedkv.h).  The sizes follow
-    the rules documented with ``pkv_decode_plan`` in pagedkv.h.
+    trail_share_pct = unequal shares (see pagedkv.h).  Changing num_workers
+    alone keeps the half-and-half lead split when the plan had one.
     """
-    bs = cache.block_size
-    nvis = -(-max(max_seq_len, 1) // bs)
-    if sliding_window > 0:
-        nvis = min(nvis, -(-(sliding_window + bs - 1) // bs))
     if split_blocks is not None:
         plan.split_blocks = int(split_blocks)
     if num_workers is not None:
@@ -215,16 +216,9 @@ def tune_plan(plan, num_rows, num_q_heads, cache, max_seq_len, sliding_window=0,
         plan.trail_share_pct = int(trail_share_pct)
     if heads_per_item is not None:
         plan.heads_per_item = int(heads_per_item)
-    if kernel_variant is not None:
-        plan.kernel_variant = int(kernel_variant)
-    per_slot = num_rows * num_q_heads * (cache.head_dim + 2) * 4
-    if plan.scheme == 1:
-        plan.max_splits = -(-nvis // plan.split_blocks) + 1
-        plan.workspace_bytes = (per_slot * plan.max_splits
-                                + num_rows * (num_q_heads // plan.heads_per_item) * 8)
-    else:
-        plan.max_splits = -(-nvis // plan.split_blocks)
-        plan.workspace_bytes = per_slot * plan.max_splits if plan.max_splits > 1 else 0
+    check("pkv_decode_plan_resize", load().pkv_decode_plan_resize(
+        num_rows, num_q_heads, cache.head_dim, cache.block_size, max_seq_len, sliding_window,
+        ctypes.byref(plan)))
     return plan
 
 

@@ -81,10 +81,14 @@ static size_t plan_bytes(const pkv_decode_plan& p, int rows, int hq, int d) {
   return p.max_splits > 1 ? partial_bytes(rows, hq, p.max_splits, d) : 0;
 }
 
+constexpr int kKnownPlanFlags = PKV_PLAN_BLOCKS_NOT_SHARED;
+
 static int make_plan(int rows, int hq, int hkv, int d, int bs, int kv_dtype, int max_seq_len,
-                     int window, int extra, bool allow_stream, pkv_decode_plan* plan, int force_hpi = 0) {
+                     int window, int extra, bool allow_stream, pkv_decode_plan* plan, int force_hpi = 0,
+                     int flags = 0) {
   if (!plan) return PKV_ERR_NULL;
   if (rows < 0 || hq <= 0 || hkv <= 0 || max_seq_len < 0 || window < 0) return PKV_ERR_SHAPE;
+  if (flags & ~kKnownPlanFlags) return PKV_ERR_SHAPE;
   if (hq % hkv) return PKV_ERR_SHAPE;
   if (dtype_bits(kv_dtype) == 0) return PKV_ERR_DTYPE;
   if (!head_dim_supported(d) || !block_size_supported(bs)) return PKV_ERR_UNSUPPORTED;
@@ -95,7 +99,7 @@ static int make_plan(int rows, int hq, int hkv, int d, int bs, int kv_dtype, int
   // INT4 items over two adjacent KV heads (whole 128-byte lines) when the
   // pair's rows fit: heads_per_item = 2 * group marks them
   if (force_hpi == 0 && int4_pairs(kv_dtype, d, hkv, group)) gm = 2 * group;
-  plan->kernel_variant = 0;
+  plan->flags = flags;
   if (allow_stream && mfma_eligible(kv_dtype, d, bs) && gm > 0 && rows <= kMaxStreamRows) {
     // balanced partition over resident wave slots
     const long long units = (long long)(rows > 0 ? rows : 1) * (hq / gm) * nvis;
@@ -141,7 +145,7 @@ static int make_plan(int rows, int hq, int hkv, int d, int bs, int kv_dtype, int
 static int check_plan(const pkv_decode_plan* plan, int rows, int hq, int hkv, int d, int bs,
                       int kv_dtype, int max_seq_len, int window, int extra) {
   if (!plan) return PKV_ERR_NULL;
-  if (plan->kernel_variant < 0 || plan->kernel_variant > 8) return PKV_ERR_SHAPE;
+  if (plan->flags & ~kKnownPlanFlags) return PKV_ERR_SHAPE;
   const int group = hq / hkv;
   const int nvis = max_visible_blocks(max_seq_len, bs, window, extra);
   if (plan->scheme == 1) {
@@ -325,7 +329,7 @@ static int prepare(DecodeArgs& a, void* out, const void* q, int q_dtype, int row
   a.window = window;
   a.split_blocks = plan->split_blocks;
   a.max_splits = plan->max_splits;
-  a.kernel_variant = plan->kernel_variant;
+  a.stream_loads = plan->scheme == 1 && (plan->flags & PKV_PLAN_BLOCKS_NOT_SHARED) != 0;
   a.stream = plan->scheme == 1;
   a.heads_per_item = plan->heads_per_item;
   a.lead_workers = plan->lead_workers;
@@ -369,10 +373,34 @@ using namespace pkv;
 
 extern "C" int pkv_decode_plan_make(int32_t num_rows, int32_t num_q_heads, int32_t num_kv_heads,
                                     int32_t head_dim, int32_t block_size, int32_t kv_dtype,
-                                    int32_t max_seq_len, int32_t sliding_window,
+                                    int32_t max_seq_len, int32_t sliding_window, int32_t flags,
                                     pkv_decode_plan* plan) {
   return make_plan(num_rows, num_q_heads, num_kv_heads, head_dim, block_size, kv_dtype,
-                   max_seq_len, sliding_window, 0, true, plan);
+                   max_seq_len, sliding_window, 0, true, plan, 0, flags);
+}
+
+extern "C" int pkv_decode_plan_resize(int32_t num_rows, int32_t num_q_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_seq_len,
+                                      int32_t sliding_window, pkv_decode_plan* plan) {
+  if (!plan) return PKV_ERR_NULL;
+  if (num_rows < 0 || num_q_heads <= 0 || max_seq_len < 0 || sliding_window < 0) return PKV_ERR_SHAPE;
+  if (!head_dim_supported(head_dim) || !block_size_supported(block_size)) return PKV_ERR_UNSUPPORTED;
+  if (plan->flags & ~kKnownPlanFlags) return PKV_ERR_SHAPE;
+  if (plan->heads_per_item < 1 || num_q_heads % plan->heads_per_item) return PKV_ERR_SHAPE;
+  const int nvis = max_visible_blocks(max_seq_len, block_size, sliding_window, 0);
+  if (plan->scheme == 1) {
+    if (plan->split_blocks < 1 || plan->num_workers < 1) return PKV_ERR_SHAPE;
+    if (plan->lead_workers < 0 || plan->lead_workers > plan->num_workers) return PKV_ERR_SHAPE;
+    if (plan->trail_share_pct < 1 || plan->trail_share_pct > 100) return PKV_ERR_SHAPE;
+    plan->max_splits = ceil_div(nvis, plan->split_blocks) + 1;
+  } else if (plan->scheme == 0) {
+    if (plan->split_blocks < 1 || plan->split_blocks > 64) return PKV_ERR_SHAPE;
+    plan->max_splits = ceil_div(nvis, plan->split_blocks);
+  } else {
+    return PKV_ERR_SHAPE;
+  }
+  plan->workspace_bytes = plan_bytes(*plan, num_rows, num_q_heads, head_dim);
+  return PKV_OK;
 }
 
 extern "C" int pkv_paged_attention_decode_partials(

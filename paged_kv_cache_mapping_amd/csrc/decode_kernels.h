@@ -74,7 +74,7 @@ struct DecodeArgs {
   float* ws_acc;
   float* ws_m;
   float* ws_l;
-  int32_t kernel_variant;   // 0 default; tuning: 1 vector-only, 2..5 loads 1..4 steps ahead, 6 two waves per SIMD
+  int32_t stream_loads;     // balanced scheme, bf16: non-temporal K/V loads (no block read twice)
   int32_t stream;           // balanced partition (piece counts in ws_np)
   int32_t heads_per_item;
   int32_t* ws_np;           // balanced partition: pieces per (row, head group)
@@ -848,13 +848,14 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));   // 4 bf16, 16x16x16
 // P.V on the matrix cores at head size 128: bf16, fp8 and INT4 caches (fp8
 // and INT4 widened to bf16 in registers, exact), except bf16 / fp8
 // single-query items of 8 rows (see decode_flat_body).
-// K/V loads of the balanced kernel.  With NTL (kernel variant 8, bf16) they
-// carry a non-temporal hint: a stream read once then does not displace what
-// is reused from the caches (table entries, staged queries, the partials the
-// merge reads next); on the Llama-3-8B batch the split kernel went from 64.2
-// to 59.4 us.  Where blocks are shared by many rows (prefix sharing) the hint
+// K/V loads of the balanced kernel.  With NTL (bf16 caches whose blocks the
+// caller declares unshared, PKV_PLAN_BLOCKS_NOT_SHARED) they carry a
+// non-temporal hint: a stream read once then does not displace what is reused
+// from the caches (table entries, staged queries, the partials the merge
+// reads next); on the Llama-3-8B batch the split kernel went from 64.2 to
+// 59.4 us.  Where blocks are shared by many rows (prefix sharing) the hint
 // sends every row back to HBM (75 -> 146 us there), and 8-byte fp8 loads
-// were slower with it too, so it is the caller's choice, not the default.
+// were slower with it too, so only the caller can ask for it.
 template <typename T>
 __device__ __forceinline__ T load_stream(const char* p) {
   if constexpr (sizeof(T) == 16) {
@@ -1433,12 +1434,17 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
     const int last = nsteps - 1;
     const int smask = (1 << spb_log2) - 1;
 
+    // loads of step st; a step past the window's last one (issued only to
+    // keep the pipeline's wait counts static, its data never used) reads
+    // the first rows of block 0, which every such load shares, so it is
+    // served by the caches instead of fetching the last step again
     auto issue = [&](int st, Buf& bf) __attribute__((always_inline)) {
-      const int unit = st >> spb_log2;
-      const int r0 = (st & smask) * 16;
+      const bool past = st > last;
+      const int unit = (past ? last : st) >> spb_log2;
+      const int r0 = past ? 0 : (st & smask) * 16;
       int phys = __builtin_amdgcn_readlane(rec_phys, unit);
-      const int hoff = __builtin_amdgcn_readlane(rec_hoff, unit);
-      phys = phys < 0 ? 0 : phys;             // flagged at the fold; block 0 is always mapped
+      const int hoff = past ? 0 : __builtin_amdgcn_readlane(rec_hoff, unit);
+      phys = (phys < 0 || past) ? 0 : phys;   // bad ids are flagged at the fold; block 0 always exists
       const int64_t off = (int64_t)phys * blk_bytes + hoff + (int64_t)r0 * row_bytes;
       const char* kp = a.kbase + off;
       const char* vp = a.vbase + off;
@@ -1753,16 +1759,16 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
       else body(std::false_type{}, p0, bf);
     };
 
-    // loads run DEPTH steps ahead, unconditionally (past the end the last
-    // step is fetched again, an L2 hit), so the wait counts stay static; the
-    // ring of DEPTH + 1 buffers is unrolled so every index is a constant
+    // loads run DEPTH steps ahead, unconditionally (past the end see issue),
+    // so the wait counts stay static; the ring of DEPTH + 1 buffers is
+    // unrolled so every index is a constant
     Buf ring[DEPTH + 1];
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) issue(min(d, last), ring[d]);
+    for (int d = 0; d < DEPTH; ++d) issue(d, ring[d]);
     for (int st = 0; st < nsteps; st += DEPTH + 1) {
 #pragma unroll
       for (int k = 0; k <= DEPTH; ++k) {
-        issue(min(st + k + DEPTH, last), ring[(k + DEPTH) % (DEPTH + 1)]);
+        issue(st + k + DEPTH, ring[(k + DEPTH) % (DEPTH + 1)]);
         if (st + k < nsteps) run(st + k, ring[k]);
       }
     }
@@ -1991,29 +1997,22 @@ void launch_stream(const DecodeArgs& a, int workers, hipStream_t s) {
     decode_flat_kernel_2w<D, GT, KV, kDepth, QT><<<workers, 64, lds, s>>>(a);
     return;
   }
-  switch (a.kernel_variant) {
-    case 2: decode_flat_kernel<D, GT, KV, 1, QT><<<workers, 64, lds, s>>>(a); break;
-    case 3: decode_flat_kernel<D, GT, KV, 2, QT><<<workers, 64, lds, s>>>(a); break;
-    case 4: decode_flat_kernel<D, GT, KV, 3, QT><<<workers, 64, lds, s>>>(a); break;
-    case 5: decode_flat_kernel<D, GT, KV, 4, QT><<<workers, 64, lds, s>>>(a); break;
-    case 6: decode_flat_kernel_2w<D, GT, KV, 1, QT><<<workers, 64, lds, s>>>(a); break;
-    case 7: decode_flat_kernel_2w<D, GT, KV, 2, QT><<<workers, 64, lds, s>>>(a); break;
-    case 8:   // the default form with non-temporal K/V loads (bf16 items on two waves)
-      if constexpr (KV == PKV_BF16 && two_waves(D, KV, GT, QT)) {
-        decode_flat_kernel_2w<D, GT, KV, kDepth, QT, true><<<workers, 64, lds, s>>>(a);
-        break;
-      }
-      [[fallthrough]];
-    default:
-      // up to four rows per item the plan counts on two waves per SIMD, so
-      // the kernel must fit in 256 registers (the fp8 build does not unless
-      // asked); eight or more rows run one wave per SIMD
-      // (INT4 keeps 8 accumulators per row and lane: two waves up to 8 rows;
-      // bf16 head size 128 accumulating in the matrix cores: up to 16)
-      if constexpr (two_waves(D, KV, GT, QT))
-        decode_flat_kernel_2w<D, GT, KV, kDepth, QT><<<workers, 64, lds, s>>>(a);
-      else decode_flat_kernel<D, GT, KV, kDepth, QT><<<workers, 64, lds, s>>>(a);
+  // non-temporal K/V loads when the caller promised that no block is read
+  // by two rows (bf16 items on two waves; see kv_load)
+  if constexpr (KV == PKV_BF16 && two_waves(D, KV, GT, QT)) {
+    if (a.stream_loads) {
+      decode_flat_kernel_2w<D, GT, KV, kDepth, QT, true><<<workers, 64, lds, s>>>(a);
+      return;
+    }
   }
+  // up to four rows per item the plan counts on two waves per SIMD, so the
+  // kernel must fit in 256 registers (the fp8 build does not unless asked);
+  // eight or more rows run one wave per SIMD (INT4 keeps 8 accumulators per
+  // row and lane: two waves up to 8 rows; head size 128 accumulating in the
+  // matrix cores: up to 16)
+  if constexpr (two_waves(D, KV, GT, QT))
+    decode_flat_kernel_2w<D, GT, KV, kDepth, QT><<<workers, 64, lds, s>>>(a);
+  else decode_flat_kernel<D, GT, KV, kDepth, QT><<<workers, 64, lds, s>>>(a);
 }
 
 // Balanced partition (matrix cores), a.heads_per_item query heads per item.

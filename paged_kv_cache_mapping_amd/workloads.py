@@ -338,7 +338,7 @@ def shared_prefix_decode(seed=6, num_reqs=100, prompt=2000, suffix_hi=64, pool=1
         q_dtype="bf16", k_plane=kp, v_plane=vp, new_k=nk, new_v=nv, q=q, block_table=bt,
         seq_lens=lengths, query_start_loc=np.arange(num_reqs + 1, dtype=np.int32),
         num_computed=(lengths - 1).astype(np.int32), scale=float(1.0 / np.sqrt(D)), decode=True,
-        info=dict(seed=seed, blocks_used=int(len(ids)), blocks_without_sharing=without,
+        info=dict(seed=seed, shares_blocks=True, blocks_used=int(len(ids)), blocks_without_sharing=without,
                   cow_pairs=len(cow), unique_kv_bytes=unique_rows * Hkv * D * 2 * 2))
 
 

@@ -1,5 +1,7 @@
 """Shared helpers for the GPU parity tests (test-side plumbing only)."""
 
+import json
+import os
 import sys
 
 import numpy as np
@@ -82,3 +84,44 @@ def compact_planes(k_plane_dev, v_plane_dev, tables, rows):
         sub = t[rows].astype(np.int64)
         out.append(np.where(sub >= 0, remap[np.maximum(sub, 0)], -1).astype(np.int32))
     return k, v, out
+
+
+# ---- element-wise bounds at the output's precision, logged
+
+PARITY_LOG = os.environ.get("PKV_PARITY_LOG")
+BF16_REL = 2.0 ** -8     # half an ulp of bfloat16, relative to the value
+
+
+def check_close(name, got, ref, max_abs, floor):
+    """Compare a bf16 (or f32) output with the fp64 oracle element by element.
+
+    Two bounds, both asserted: the spec max-abs bound (2e-3 bf16 KV,
+    3e-2 fp8 KV) and a per-element bound at the output's own precision,
+    |got - ref| <= 2^-8 |ref| + floor: rounding to bf16 moves a value by at
+    most half an ulp (2^-8 of it), and `floor` covers the float32 arithmetic
+    before that rounding (stated per test from the data's scale).  Logs the
+    max-abs and max-relative errors (to stdout, and to $PKV_PARITY_LOG as a
+    JSON line when set).
+    """
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), "non-finite output"
+    assert np.isfinite(ref).all(), "non-finite oracle output"
+    diff = np.abs(got - ref)
+    bound = BF16_REL * np.abs(ref) + floor
+    mask = np.abs(ref) > 100 * floor
+    rec = dict(case=name, n=int(got.size), max_abs=float(diff.max()),
+               max_rel=float((diff[mask] / np.abs(ref[mask])).max()) if mask.any() else 0.0,
+               worst_vs_bound=float((diff / bound).max()), floor=floor, max_abs_bound=max_abs,
+               ref_max=float(np.abs(ref).max()), ref_std=float(ref.std()))
+    say("parity", json.dumps(rec))
+    if PARITY_LOG:
+        try:
+            with open(PARITY_LOG, "a") as f:
+                f.write(json.dumps(rec) + "\n")
+        except OSError:
+            pass
+    assert rec["max_abs"] <= max_abs, rec
+    bad = np.argwhere(diff > bound)
+    assert len(bad) == 0, "%d elements beyond |d| <= 2^-8 |ref| + %g, first %s: got %r ref %r" % (
+        len(bad), floor, bad[0].tolist(), got[tuple(bad[0])], ref[tuple(bad[0])])
+    return rec

@@ -37,7 +37,7 @@ def test_header_declares_the_expected_calls():
                  "pkv_chunked_workspace_size", "pkv_kv_bytes_per_token", "pkv_status_string",
                  "pkv_fp8_e4m3_quantize", "pkv_fp8_e4m3_dequantize", "pkv_copy_blocks",
                  "pkv_int4_quantize", "pkv_int4_dequantize", "pkv_num_blocks_for_budget",
-                 "pkv_slot_mapping_cache_write"):
+                 "pkv_slot_mapping_cache_write", "pkv_decode_plan_resize"):
         assert want in names
     assert set(names) == set(_lib.SIGNATURES)   # the binding covers every declaration
 
@@ -211,7 +211,7 @@ def test_plan_rows_and_waves_follow_the_kernels(lib, hq, hkv, dtype, hpi, per_cu
     launch for the shape (host arithmetic; 256 compute units without a GPU):
     two waves per SIMD where the kernel fits 256 registers, one elsewhere."""
     plan = _lib.PkvDecodePlan()
-    st = lib.pkv_decode_plan_make(64, hq, hkv, 128, 16, dtype, 2048, 0, ctypes.byref(plan))
+    st = lib.pkv_decode_plan_make(64, hq, hkv, 128, 16, dtype, 2048, 0, 0, ctypes.byref(plan))
     assert st == _lib.PKV_OK and plan.scheme == 1
     assert plan.heads_per_item == hpi
     assert plan.num_workers == 256 * per_cu
@@ -226,7 +226,7 @@ def test_plan_rows_and_waves_follow_the_kernels(lib, hq, hkv, dtype, hpi, per_cu
 ])
 def test_plan_scheme_at_the_row_limit(lib, rows, dtype, scheme):
     plan = _lib.PkvDecodePlan()
-    st = lib.pkv_decode_plan_make(rows, 32, 8, 128, 16, dtype, 2048, 0, ctypes.byref(plan))
+    st = lib.pkv_decode_plan_make(rows, 32, 8, 128, 16, dtype, 2048, 0, 0, ctypes.byref(plan))
     if scheme is None:
         assert st == _lib.PKV_ERR_UNSUPPORTED
     else:
@@ -255,8 +255,68 @@ def test_chunked_plans_past_the_row_limit(lib, reqs, dtype, ok):
 ])
 def test_plan_scheme_by_head_size_and_block(lib, d, bs, dtype, scheme):
     plan = _lib.PkvDecodePlan()
-    st = lib.pkv_decode_plan_make(64, 32, 8, d, bs, dtype, 2048, 0, ctypes.byref(plan))
+    st = lib.pkv_decode_plan_make(64, 32, 8, d, bs, dtype, 2048, 0, 0, ctypes.byref(plan))
     if scheme is None:
         assert st == _lib.PKV_ERR_UNSUPPORTED
     else:
         assert st == _lib.PKV_OK and plan.scheme == scheme
+
+
+def test_plan_flags_are_checked(lib):
+    plan = _lib.PkvDecodePlan()
+    st = lib.pkv_decode_plan_make(64, 32, 8, 128, 16, _lib.PKV_BF16, 2048, 0,
+                                  _lib.PKV_PLAN_BLOCKS_NOT_SHARED, ctypes.byref(plan))
+    assert st == _lib.PKV_OK and plan.flags == _lib.PKV_PLAN_BLOCKS_NOT_SHARED
+    assert lib.pkv_decode_plan_make(64, 32, 8, 128, 16, _lib.PKV_BF16, 2048, 0, 6,
+                                    ctypes.byref(plan)) == _lib.PKV_ERR_SHAPE
+
+
+@pytest.mark.parametrize("rows,hq,window,split,workers,hpi", [
+    (64, 32, 0, 8, 2048, 4),
+    (64, 32, 0, 3, 100, 2),
+    (7, 8, 333, 1, 5, 1),
+    (32, 64, 0, 16, 1024, 8),
+])
+def test_plan_resize_recomputes_the_sizes(lib, rows, hq, window, split, workers, hpi):
+    """After the tuning fields change, the sizes follow the workspace layout
+    of pagedkv.h: acc [rows, Hq, max_splits, D] and m, l per slot as floats,
+    plus an int32 pair per (row, head group); max_splits = pieces a row's
+    visible blocks can be cut into by shares of at least split blocks."""
+    D, bs, L = 128, 16, 2048
+    plan = _lib.PkvDecodePlan()
+    assert lib.pkv_decode_plan_make(rows, hq, 8 if hq >= 8 else 2, D, bs, _lib.PKV_BF16, L, window, 0,
+                                    ctypes.byref(plan)) == _lib.PKV_OK
+    assert plan.scheme == 1
+    plan.split_blocks, plan.num_workers, plan.heads_per_item = split, workers, hpi
+    plan.lead_workers = workers // 2
+    assert lib.pkv_decode_plan_resize(rows, hq, D, bs, L, window, ctypes.byref(plan)) == _lib.PKV_OK
+    nvis = -(-L // bs) if window == 0 else min(-(-L // bs), -(-(window + bs - 1) // bs))
+    assert plan.max_splits == -(-nvis // split) + 1
+    assert plan.workspace_bytes == rows * hq * plan.max_splits * (D + 2) * 4 + rows * (hq // hpi) * 8
+
+
+def test_plan_resize_rejects_fields_no_kernel_takes(lib):
+    plan = _lib.PkvDecodePlan()
+    assert lib.pkv_decode_plan_make(64, 32, 8, 128, 16, _lib.PKV_BF16, 2048, 0, 0,
+                                    ctypes.byref(plan)) == _lib.PKV_OK
+    good = (plan.split_blocks, plan.num_workers, plan.lead_workers, plan.trail_share_pct, plan.heads_per_item)
+
+    def resize_with(**kw):
+        (plan.split_blocks, plan.num_workers, plan.lead_workers, plan.trail_share_pct,
+         plan.heads_per_item) = good
+        for k, v in kw.items():
+            setattr(plan, k, v)
+        return lib.pkv_decode_plan_resize(64, 32, 128, 16, 2048, 0, ctypes.byref(plan))
+
+    assert resize_with() == _lib.PKV_OK
+    for bad in (dict(split_blocks=0), dict(num_workers=0), dict(lead_workers=-1),
+                dict(lead_workers=good[1] + 1), dict(trail_share_pct=0), dict(trail_share_pct=101),
+                dict(heads_per_item=3), dict(heads_per_item=0), dict(flags=8)):
+        assert resize_with(**bad) == _lib.PKV_ERR_SHAPE, bad
+    plan.flags = 0
+    plan.scheme, plan.heads_per_item = 0, 4
+    plan.split_blocks = 65
+    assert lib.pkv_decode_plan_resize(64, 32, 128, 16, 2048, 0, ctypes.byref(plan)) == _lib.PKV_ERR_SHAPE
+    plan.split_blocks = 64
+    assert lib.pkv_decode_plan_resize(64, 32, 128, 16, 2048, 0, ctypes.byref(plan)) == _lib.PKV_OK
+    assert plan.max_splits == 2

@@ -8,9 +8,9 @@ import torch
 import paged_kv_cache_mapping_amd as pkv
 from paged_kv_cache_mapping_amd import workloads
 from paged_kv_cache_mapping_amd.workloads import bf16_bits
-from oracle import attention, layout, paging
+from oracle import attention
 
-from helpers import compact_planes, gpu_or_skip, host_bits, max_err, out_f64, say
+from helpers import gpu_or_skip, max_err, out_f64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -287,62 +287,3 @@ def test_chunked_one_long_item_cut_by_every_share():
                                       cache, torch.from_numpy(bt).cuda(), int(L[0]), 0.125)
     torch.cuda.synchronize()
     assert max_err(out_f64(out), ref) <= 2e-3
-
-
-# --------------------------------------------------------------------------- hybrid
-
-def test_hybrid_groups_full_size_sampled_rows():
-    """Four layers over two shared tensors and two group tables; every layer:
-    slot mapping (bit-exact), cache write (bit-exact on the written rows),
-    chunked attention on sampled requests (both kinds) against the oracle."""
-    w = workloads.hybrid_chunked()
-    layout.check_group_tables(w.tables, w.seq_lens, w.num_computed, w.windows, w.block_size,
-                              w.num_blocks)
-    cfg, views, bufs = w.device_tensors()
-    qsl_d = torch.from_numpy(w.query_start_loc).cuda()
-    L_d = torch.from_numpy(w.seq_lens).cuda()
-    nc_d = torch.from_numpy(w.num_computed).cuda()
-    ql = np.diff(w.query_start_loc)
-    rng = np.random.default_rng(55)
-    # sampled queries: 6 decode requests and 16 positions in each of 2 prefill
-    # chunks; a causal query at position p of request r sees exactly what a
-    # single-query request of length p + 1 over the same table row sees.
-    picks = []   # (request, token index, position)
-    for r in rng.choice(np.where(ql == 1)[0], 6, replace=False):
-        picks.append((r, int(w.query_start_loc[r]), int(w.seq_lens[r]) - 1))
-    for r in np.where(ql > 1)[0][:2]:
-        for i in sorted(rng.choice(int(ql[r]), 16, replace=False)):
-            picks.append((r, int(w.query_start_loc[r]) + int(i),
-                          int(w.seq_lens[r]) - int(ql[r]) + int(i)))
-    sample = np.array([p[0] for p in picks])
-    tok = np.array([p[1] for p in picks])
-    pos = np.array([p[2] for p in picks])
-    for li, layer in enumerate(["L0", "L1", "L2", "L3"]):
-        g = cfg.layer_group(layer)
-        W = w.windows[g]
-        cache = views[layer]
-        say("hybrid layer", layer, "group", g, "window", W)
-        bt_d = torch.from_numpy(w.tables[g]).cuda()
-        slots = pkv.slot_mapping(bt_d, qsl_d, nc_d, w.block_size, w.num_blocks)
-        ref_slots, errs = paging.slot_mapping(w.tables[g], w.query_start_loc, w.num_computed,
-                                              w.block_size, num_blocks=w.num_blocks)
-        assert errs == 0 and np.array_equal(slots.cpu().numpy(), ref_slots)
-        q, nk, nv = w.step_inputs(li)
-        pkv.cache_write(nk, nv, slots, cache)
-        out = pkv.paged_attention_chunked(q, qsl_d, L_d, w.max_query_len, cache, bt_d,
-                                          w.max_seq_len, w.scale, causal=True, sliding_window=W)
-        torch.cuda.synchronize()
-        # written rows hold the new K/V bits
-        sl = torch.from_numpy(ref_slots).cuda()
-        blk, off = sl // w.block_size, sl % w.block_size
-        assert torch.equal(cache.k[blk, off].view(torch.int16), nk.view(torch.int16))
-        assert torch.equal(cache.v[blk, off].view(torch.int16), nv.view(torch.int16))
-        # oracle on the sampled requests, over just the blocks they reference
-        k_h, v_h, (bt_h,) = compact_planes(cache.k, cache.v, [w.tables[g]], sample)
-        q_h = host_bits(q)[tok]
-        ref = attention.paged_attention(q_h, "bf16", k_h, v_h, "bf16", bt_h, pos + 1,
-                                        np.arange(len(picks) + 1), w.scale, causal=True,
-                                        sliding_window=W)
-        err = max_err(out_f64(out)[tok], ref)
-        say("hybrid layer", layer, "max err", err)
-        assert err <= 2e-3

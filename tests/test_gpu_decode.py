@@ -13,7 +13,7 @@ import paged_kv_cache_mapping_amd as pkv
 from paged_kv_cache_mapping_amd import workloads
 from oracle import attention, paging
 
-from helpers import (gpu_or_skip, host_bits, max_err, oracle_decode_step, out_f64,
+from helpers import (check_close, gpu_or_skip, host_bits, max_err, oracle_decode_step, out_f64,
                      run_decode_step, say)
 
 pytestmark = pytest.mark.gpu
@@ -36,9 +36,13 @@ def test_full_decode_step_matches_oracle(name):
     assert np.array_equal(slots.cpu().numpy(), ref_slots)
     assert host_bits(d.cache.k).tobytes() == kp.tobytes()
     assert host_bits(d.cache.v).tobytes() == vp.tobytes()
-    err = max_err(out_f64(out), ref)
-    say(name, "max abs err", err)
-    assert err <= TOL[w.cache_dtype]
+    if w.q_dtype == "f32":
+        err = max_err(out_f64(out), ref)
+        say(name, "max abs err", err)
+        assert err <= TOL[w.cache_dtype]
+    else:
+        check_close("decode_step_" + name, out_f64(out), ref, TOL[w.cache_dtype],
+                    1e-4 if w.cache_dtype == "fp8" else 1e-5)
 
 
 def _small(seed, B, Lmax, Hq, Hkv, D, bs, dtype="bf16", Lmin=1, pool=None):
@@ -51,17 +55,19 @@ def _small(seed, B, Lmax, Hq, Hkv, D, bs, dtype="bf16", Lmin=1, pool=None):
         sigma=1.0 if dtype == "f32" else 0.35)
 
 
-def _check_attention_only(w, window=0, plan_split=None, variant=None):
+def _check_attention_only(w, window=0, plan_split=None, not_shared=False):
     """Decode attention over the planes as given (no write) vs the oracle."""
     d = w.device()
-    if plan_split is None:
+    if plan_split is None and not not_shared:
         out = pkv.paged_attention_decode(d.q, d.cache, d.block_table, d.seq_lens, w.max_seq_len,
                                          w.scale, sliding_window=window)
     else:
-        plan = pkv.decode_plan(w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len, window)
-        workers = None if plan.scheme == 0 else max(1, plan.num_workers // plan_split)
-        pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len, window,
-                      split_blocks=plan_split, num_workers=workers, kernel_variant=variant)
+        plan = pkv.decode_plan(w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len, window,
+                               blocks_not_shared=not_shared)
+        if plan_split is not None:
+            workers = None if plan.scheme == 0 else max(1, plan.num_workers // plan_split)
+            pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len, window,
+                          split_blocks=plan_split, num_workers=workers)
         ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
         out = torch.empty_like(d.q)
         pkv.paged_attention_decode_partials(d.q, d.cache, d.block_table, d.seq_lens, w.max_seq_len,
@@ -82,20 +88,6 @@ def test_head_dims_and_block_sizes(D, bs):
     w = _small(40 + D + bs, B=5, Lmax=300, Hq=4, Hkv=2, D=D, bs=bs)
     _, err = _check_attention_only(w)
     assert err <= TOL["bf16"]
-
-
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_very_long_rows(dtype):
-    """Rows of 131072 and 70001 keys beside a short one: about a thousand
-    pieces per long row, merged in many rounds."""
-    say("decode long rows", dtype)
-    lens = np.array([131072, 70001, 17])
-    nb = int(sum(-(-int(L) // 16) for L in lens)) + 9
-    w = workloads.decode_workload("long", 31, lambda rng: lens.copy(), None, pool_blocks=nb, block_size=16,
-                                  num_q_heads=8, num_kv_heads=2, head_dim=128, cache_dtype=dtype,
-                                  q_dtype="bf16", sigma=0.35)
-    _, err = _check_attention_only(w)
-    assert err <= TOL[dtype]
 
 
 @pytest.mark.parametrize("B,scheme", [(1500, 1), (4096, 1), (4097, 0)])
@@ -145,24 +137,25 @@ def test_sliding_window(W):
 
 
 @pytest.mark.parametrize("split", [1, 2, 3, 8, 64])
-@pytest.mark.parametrize("variant", [0, 2, 3, 4, 5, 7, 8])
-def test_any_split_plan_gives_the_same_answer(split, variant):
-    say("decode split", split, "variant", variant)
+@pytest.mark.parametrize("not_shared", [False, True])
+def test_any_split_plan_gives_the_same_answer(split, not_shared):
+    say("decode split", split, "blocks not shared", not_shared)
     w = _small(150, B=6, Lmax=1500, Hq=32, Hkv=8, D=128, bs=16, Lmin=200)
-    _, err = _check_attention_only(w, plan_split=split, variant=variant)
+    _, err = _check_attention_only(w, plan_split=split, not_shared=not_shared)
     assert err <= TOL["bf16"]
-    _, err = _check_attention_only(w, window=333, plan_split=split, variant=variant)
+    _, err = _check_attention_only(w, window=333, plan_split=split, not_shared=not_shared)
     assert err <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("variant", [0, 2, 5, 6, 7, 8])
+@pytest.mark.parametrize("not_shared", [False, True])
 @pytest.mark.parametrize("Hq,Hkv,dtype", [(64, 4, "bf16"), (64, 8, "bf16"), (32, 8, "fp8"), (64, 8, "fp8")])
-def test_variants_over_item_heights_and_dtypes(variant, Hq, Hkv, dtype):
-    """Items of 16 and 8 rows (matrix-core and vector-ALU P.V) and fp8 items
-    under every kernel variant (prefetch depth, one or two waves per SIMD)."""
-    say("decode variants", variant, Hq, Hkv, dtype)
+def test_item_heights_and_dtypes(not_shared, Hq, Hkv, dtype):
+    """Items of 16 and 8 rows (matrix-core and vector-ALU P.V) and fp8 items,
+    with and without the non-temporal loads of unshared blocks (which fp8
+    does not take)."""
+    say("decode item heights", not_shared, Hq, Hkv, dtype)
     w = _small(160 + Hq + Hkv, B=7, Lmax=1300, Hq=Hq, Hkv=Hkv, D=128, bs=16, dtype=dtype, Lmin=100)
-    _, err = _check_attention_only(w, plan_split=2, variant=variant)
+    _, err = _check_attention_only(w, plan_split=2, not_shared=not_shared)
     assert err <= TOL[dtype]
 
 
@@ -176,8 +169,7 @@ def test_vector_alu_fixed_split_path(split):
     if plan.scheme != 0:
         # build the equivalent scheme-0 plan by hand: vector kernels, fixed splits
         plan.scheme, plan.num_workers, plan.heads_per_item = 0, 0, 4
-    pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len, split_blocks=split,
-                  kernel_variant=1)
+    pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len, split_blocks=split)
     ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(d.q)
     pkv.paged_attention_decode_partials(d.q, d.cache, d.block_table, d.seq_lens, w.max_seq_len,
@@ -219,8 +211,7 @@ def test_fp8_phases_called_separately(split):
     plan = pkv.decode_plan(w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len)
     if split == 32:
         plan.scheme, plan.num_workers, plan.heads_per_item = 0, 0, 4
-        pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len, split_blocks=8,
-                      kernel_variant=1)
+        pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len, split_blocks=8)
     elif split is not None:
         pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len,
                       num_workers=max(1, plan.num_workers // split))

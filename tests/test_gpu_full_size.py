@@ -1,0 +1,264 @@
+"""GPU parity at the workloads' full sizes, every output row against the fp64
+oracle.
+
+Each output element is held to two bounds (helpers.check_close): the
+spec max-abs bound (2e-3 with bf16 K/V, 3e-2 with fp8 K/V) and a bound
+at the output's own precision, |got - ref| <= 2^-8 |ref| + floor.  The
+workloads' data are N(0, 1/128), so outputs are small (about 1e-3 .. 2e-2);
+the second bound is what makes a dropped or doubled block visible there.
+floor = 1e-5 for data of that scale and 1e-4 for the fp8 workload's N(0, 1)
+data: the kernels' float32 arithmetic before the final rounding (score sums,
+the weights' bf16 high part and remainder, about 2^-17 relative, the
+accumulation over a few thousand keys) stays below a tenth of it.
+
+Inputs come from the seeded generators or from torch's generator on the
+device (history of the hybrid workload); every expected value comes from
+`oracle/` applied to host copies of those inputs (the cache write, too, is
+the oracle's own).  Sources of the behaviour checked: "Deep Dive into vLLM
+Worker-Side GPU KV Cache Initialization" (Pinpointing the Token Slot; Hybrid
+Attention Mechanisms), its Chinese original (KV Cache技术背景: the 80-layer
+LLaMA-70B example), "Understanding PageAttention Memory Optimization"
+(Handling Softmax Across Blocks).
+"""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle_pool
+import paged_kv_cache_mapping_amd as pkv
+from helpers import (check_close, gpu_or_skip, host_bits, oracle_decode_step, out_f64, say)
+from oracle import attention, layout, paging
+from paged_kv_cache_mapping_amd import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+import bench  # noqa: E402  (the bench's plan and step, run as it times them)
+
+pytestmark = pytest.mark.gpu
+
+FLOOR_SMALL = 1e-5     # data N(0, 1/128)
+FLOOR_UNIT = 1e-4      # data N(0, 1)
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    gpu_or_skip()
+
+
+def _bench_decode_step(w, base, cache=None, bt=None):
+    plan = bench.decode_plan_for(pkv, w, base.cache)
+    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(base.q)
+    slots = torch.empty(w.num_reqs, dtype=torch.int64, device="cuda")
+    step = bench.decode_step_fn(pkv, w, base, plan, ws, out, slots)
+    step(base.cache if cache is None else cache, base.block_table if bt is None else bt)
+    torch.cuda.synchronize()
+    return plan, slots, out
+
+
+@pytest.mark.parametrize("name,floor,tol", [("llama8b", FLOOR_SMALL, 2e-3),
+                                            ("fp8", FLOOR_UNIT, 3e-2),
+                                            ("int4", FLOOR_SMALL, 2e-3)])
+def test_bench_decode_step_every_row(name, floor, tol):
+    """The decode step exactly as bench.py times it (its plan, its calls), on
+    the full workload: slots and cache bit-exact, every output row bounded."""
+    say("bench decode step", name)
+    w = workloads.ALL[name]()
+    base = w.device()
+    plan, slots, out = _bench_decode_step(w, base)
+    say(name, "plan scheme", plan.scheme, "workers", plan.num_workers, "flags", plan.flags)
+    ref_slots, kp, vp, ref = oracle_decode_step(w, "bf16")
+    assert np.array_equal(slots.cpu().numpy(), ref_slots)
+    assert host_bits(base.cache.k).tobytes() == kp.tobytes()
+    assert host_bits(base.cache.v).tobytes() == vp.tobytes()
+    check_close("bench_step_" + name, out_f64(out), ref, tol, floor)
+
+
+def test_llama70b_layers_0_39_79_of_the_80_layer_cache():
+    """The LLaMA-70B-shaped decode on three layers of the whole 80-layer cache
+    (80 GiB, one byte buffer per layer, as the bench allocates it): each
+    layer holds the same logical history under its own block permutation, so
+    every layer must match the oracle and give the same bits."""
+    say("llama70b 80-layer cache")
+    w = workloads.llama70b_decode()
+    base = w.device()
+    pools, info = bench.layer_pools(w, base, torch.device("cuda:0"), 80)
+    assert info["layers_allocated"] == 80 and info["allocated_bytes"] >= 80 * (1 << 30)
+    ref_slots, kp, vp, ref = oracle_decode_step(w, "bf16")
+    outs = []
+    for layer in (0, 39, 79):
+        cache, bt = pools[layer]
+        say("llama70b layer", layer)
+        _, slots, out = _bench_decode_step(w, base, cache, bt)
+        # the slots follow this layer's table; its cache holds the new rows
+        bt_h = bt.cpu().numpy()
+        s_ref, e = paging.slot_mapping(bt_h, w.query_start_loc, w.num_computed, w.block_size,
+                                       num_blocks=w.num_blocks)
+        assert e == 0 and np.array_equal(slots.cpu().numpy(), s_ref)
+        blk = torch.from_numpy(s_ref // w.block_size).cuda()
+        off = torch.from_numpy(s_ref % w.block_size).cuda()
+        assert torch.equal(cache.k[blk, off].view(torch.int16), base.new_k.view(torch.int16))
+        assert torch.equal(cache.v[blk, off].view(torch.int16), base.new_v.view(torch.int16))
+        check_close("llama70b_layer%d" % layer, out_f64(out), ref, 2e-3, FLOOR_SMALL)
+        outs.append(out.clone())
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    del pools
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.oracle_pool
+@pytest.mark.parametrize("layer", ["L0", "L1", "L2", "L3"])
+def test_hybrid_every_row(layer):
+    """One layer of the hybrid step (full-attention layers L0, L2; sliding
+    window 4096 layers L1, L3; two groups over shared tensors): slot mapping
+    bit-exact, the written rows bit-exact, and every one of the 2144 query
+    rows (96 decode requests, 4 prefill chunks of 512) against the oracle."""
+    w = workloads.hybrid_chunked()
+    layout.check_group_tables(w.tables, w.seq_lens, w.num_computed, w.windows, w.block_size,
+                              w.num_blocks)
+    cfg, views, bufs = w.device_tensors()
+    g = cfg.layer_group(layer)
+    W = w.windows[g]
+    li = int(layer[1:])
+    cache = views[layer]
+    table = w.tables[g]
+    say("hybrid layer", layer, "group", g, "window", W)
+    # history of this layer's blocks, copied before the write
+    ids = np.unique(table[table >= 0]).astype(np.int64)
+    idx = torch.from_numpy(ids).cuda()
+    k_hist = host_bits(cache.k.index_select(0, idx))
+    v_hist = host_bits(cache.v.index_select(0, idx))
+    remap = np.full(int(table.max()) + 1, -1, np.int64)
+    remap[ids] = np.arange(len(ids))
+    ctab = np.where(table >= 0, remap[np.maximum(table, 0)], -1).astype(np.int32)
+
+    qsl_d = torch.from_numpy(w.query_start_loc).cuda()
+    L_d = torch.from_numpy(w.seq_lens).cuda()
+    nc_d = torch.from_numpy(w.num_computed).cuda()
+    bt_d = torch.from_numpy(table).cuda()
+    slots = pkv.slot_mapping(bt_d, qsl_d, nc_d, w.block_size, w.num_blocks)
+    q, nk, nv = w.step_inputs(li)
+    pkv.cache_write(nk, nv, slots, cache)
+    out = pkv.paged_attention_chunked(q, qsl_d, L_d, w.max_query_len, cache, bt_d, w.max_seq_len,
+                                      w.scale, causal=True, sliding_window=W)
+    torch.cuda.synchronize()
+
+    ref_slots, errs = paging.slot_mapping(table, w.query_start_loc, w.num_computed, w.block_size,
+                                          num_blocks=w.num_blocks)
+    assert errs == 0 and np.array_equal(slots.cpu().numpy(), ref_slots)
+    sl = torch.from_numpy(ref_slots).cuda()
+    blk, off = sl // w.block_size, sl % w.block_size
+    assert torch.equal(cache.k[blk, off].view(torch.int16), nk.view(torch.int16))
+    assert torch.equal(cache.v[blk, off].view(torch.int16), nv.view(torch.int16))
+
+    # the oracle's own write into the host copy, then every row
+    cslots, e2 = paging.slot_mapping(ctab, w.query_start_loc, w.num_computed, w.block_size)
+    assert e2 == 0
+    kp, vp = paging.cache_write(k_hist, v_hist, host_bits(nk), host_bits(nv), cslots, "bf16", "bf16")
+    ref = oracle_pool.paged_attention_all_rows(
+        host_bits(q), "bf16", oracle_pool.host_block_fetcher(kp, vp, ctab, w.block_size), "bf16", ctab,
+        w.seq_lens, w.query_start_loc, w.scale, causal=True, window=W)
+    check_close("hybrid_" + layer, out_f64(out), ref, 2e-3, FLOOR_SMALL)
+    del views, bufs
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.oracle_pool
+def test_spec_workload_every_row():
+    """The bench's speculative-decode step (64 requests, 4 draft tokens each):
+    slot mapping and cache write bit-exact, every query row bounded."""
+    say("spec workload every row")
+    w = workloads.spec_decode()
+    d = w.device()
+    slots = pkv.slot_mapping(d.block_table, d.query_start_loc, d.num_computed, w.block_size, w.num_blocks)
+    pkv.cache_write(d.new_k, d.new_v, slots, d.cache)
+    out = pkv.paged_attention_chunked(d.q, d.query_start_loc, d.seq_lens, w.max_query_len, d.cache,
+                                      d.block_table, w.max_seq_len, w.scale)
+    torch.cuda.synchronize()
+    s_ref, e = paging.slot_mapping(w.block_table, w.query_start_loc, w.num_computed, w.block_size)
+    assert e == 0 and np.array_equal(slots.cpu().numpy(), s_ref)
+    kp, vp = paging.cache_write(w.k_plane, w.v_plane, w.new_k, w.new_v, s_ref, "bf16", "bf16")
+    assert host_bits(d.cache.k).tobytes() == kp.tobytes()
+    ref = oracle_pool.paged_attention_all_rows(
+        w.q, "bf16", oracle_pool.host_block_fetcher(kp, vp, w.block_table, w.block_size), "bf16",
+        w.block_table, w.seq_lens, w.query_start_loc, w.scale, causal=True)
+    check_close("spec_all_rows", out_f64(out), ref, 2e-3, FLOOR_SMALL)
+
+
+def test_shared_prefix_workload_every_row():
+    """The full prefix workload (100 requests over one 2000-token prompt's
+    blocks) in the bench's launch configuration (no non-temporal loads,
+    since blocks are shared): every row bounded."""
+    say("shared prefix every row")
+    w = workloads.shared_prefix_decode()
+    base = w.device()
+    plan, slots, out = _bench_decode_step(w, base)
+    assert plan.flags == 0
+    s_ref, kp, vp, ref = oracle_decode_step(w, "bf16")
+    assert np.array_equal(slots.cpu().numpy(), s_ref)
+    check_close("prefix_all_rows", out_f64(out), ref, 2e-3, FLOOR_SMALL)
+
+
+def _signed_v(w, dtype, amp, group, seed):
+    """Give V a random +-amp offset per (row, group of `group` positions,
+    KV head, dim), so that every group of keys moves the output by about
+    amp * group / L in every dimension: a dropped or doubled piece of a long
+    row then shows at many times the bound."""
+    rng = np.random.default_rng(seed)
+    bs = w.block_size
+    Hkv, D = w.num_kv_heads, w.head_dim
+    vals = {}
+    for r, L in enumerate(w.seq_lens):
+        L = int(L)
+        # short rows keep plain noise (an average of few offsets would be
+        # near 1, where bf16 rounding alone exceeds the max-abs bound)
+        a = amp if L >= 1024 else 0.0
+        sig = rng.choice([-a, a], size=(-(-L // group), Hkv, D)).astype(np.float32)
+        noise = rng.standard_normal((L, Hkv, D), dtype=np.float32) * np.float32(0.35)
+        v = noise + np.repeat(sig, group, axis=0)[:L]
+        for j in range(-(-L // bs)):
+            phys = int(w.block_table[r, j])
+            rows = v[j * bs:(j + 1) * bs]
+            vals[phys] = (rows, len(rows))
+    if dtype == "bf16":
+        for phys, (rows, n) in vals.items():
+            w.v_plane[phys, :n] = workloads.bf16_bits(rows)
+    else:
+        amax = max(float(np.abs(rows).max()) for rows, _ in vals.values())
+        w.v_scale = float(np.float32(amax / 448.0))
+        for phys, (rows, n) in vals.items():
+            w.v_plane[phys, :n] = workloads.fp8_codes(rows, w.v_scale)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_very_long_rows_every_piece_counts(dtype):
+    """Rows of 131072 and 70001 keys beside a short one (about a thousand
+    pieces per long row, merged in many rounds).  V carries a +-1 offset per
+    group of 64 positions, so dropping or repeating any 64 keys shifts every
+    output element by about 5e-4 .. 9e-4, several times the per-element
+    bound."""
+    say("decode long rows", dtype)
+    lens = np.array([131072, 70001, 17])
+    nb = int(sum(-(-int(L) // 16) for L in lens)) + 9
+    w = workloads.decode_workload("long", 31, lambda rng: lens.copy(), None, pool_blocks=nb, block_size=16,
+                                  num_q_heads=8, num_kv_heads=2, head_dim=128, cache_dtype=dtype,
+                                  q_dtype="bf16", sigma=0.35)
+    _signed_v(w, dtype, 1.0, 64, 311)
+    d = w.device()
+    out = pkv.paged_attention_decode(d.q, d.cache, d.block_table, d.seq_lens, w.max_seq_len, w.scale)
+    torch.cuda.synchronize()
+    ref = attention.paged_decode(w.q, "bf16", w.k_plane, w.v_plane, dtype, w.block_table, w.seq_lens,
+                                 w.scale, k_scale=w.k_scale, v_scale=w.v_scale)
+    got = out_f64(out)
+    # the long rows' outputs are averages of +-1 offsets over about 1000-2000
+    # groups: |out| around 0.02 .. 0.05, so the bound is about 1e-4 there
+    check_close("long_rows_" + dtype, got[:2], ref[:2], 2e-3 if dtype == "bf16" else 3e-2,
+                FLOOR_SMALL if dtype == "bf16" else FLOOR_UNIT)
+    check_close("long_rows_short_" + dtype, got[2:], ref[2:], 2e-3 if dtype == "bf16" else 3e-2,
+                FLOOR_SMALL if dtype == "bf16" else FLOOR_UNIT)

@@ -19,7 +19,7 @@ import paged_kv_cache_mapping_amd as pkv
 from paged_kv_cache_mapping_amd import workloads
 from oracle import attention, int4, paging
 
-from helpers import (gpu_or_skip, host_bits, max_err, oracle_decode_step, out_f64, run_decode_step,
+from helpers import (check_close, gpu_or_skip, host_bits, max_err, oracle_decode_step, out_f64, run_decode_step,
                      say)
 
 pytestmark = pytest.mark.gpu
@@ -211,9 +211,7 @@ def test_full_int4_decode_step():
     assert np.array_equal(slots.cpu().numpy(), ref_slots)
     assert host_bits(d.cache.k).tobytes() == kp.tobytes()
     assert host_bits(d.cache.v).tobytes() == vp.tobytes()
-    err = max_err(out_f64(out), ref)
-    say("int4 full step max abs err", err)
-    assert err <= TOL
+    check_close("int4_decode_step", out_f64(out), ref, TOL, 1e-5)
 
 
 def _int4_chunk_case(seed, R, Lmax, qmax, Hq, Hkv, bs=16):

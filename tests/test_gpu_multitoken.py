@@ -82,32 +82,6 @@ def test_multitoken_inconsistent_lengths_get_nan_rows():
     assert max_err(got[~broken], ref[~broken]) <= 2e-3
 
 
-def test_spec_workload_sampled_requests():
-    """The bench's speculative-decode step at full size (64 requests, 4 draft
-    tokens each): slot mapping, cache write and chunked attention, sampled
-    requests against the oracle."""
-    from paged_kv_cache_mapping_amd import workloads
-    from oracle import paging
-    say("spec workload")
-    w = workloads.spec_decode()
-    d = w.device()
-    slots = pkv.slot_mapping(d.block_table, d.query_start_loc, d.num_computed, w.block_size, w.num_blocks)
-    pkv.cache_write(d.new_k, d.new_v, slots, d.cache)
-    out = pkv.paged_attention_chunked(d.q, d.query_start_loc, d.seq_lens, w.max_query_len, d.cache,
-                                      d.block_table, w.max_seq_len, w.scale)
-    torch.cuda.synchronize()
-    s_ref, e = paging.slot_mapping(w.block_table, w.query_start_loc, w.num_computed, w.block_size)
-    assert e == 0
-    kp, vp = paging.cache_write(w.k_plane, w.v_plane, w.new_k, w.new_v, s_ref, "bf16", "bf16")
-    reqs = [0, 17, 40, 63]
-    ql = w.info["q_len"]
-    rows = np.concatenate([np.arange(r * ql, (r + 1) * ql) for r in reqs])
-    qsl = (np.arange(len(reqs) + 1) * ql).astype(np.int32)
-    ref = attention.paged_attention(w.q[rows], "bf16", kp, vp, "bf16", w.block_table[reqs], w.seq_lens[reqs],
-                                    qsl, w.scale)
-    assert max_err(out_f64(out)[rows], ref) <= 2e-3
-
-
 def test_single_query_requests_ride_in_the_items():
     """A step declared with up to 4 query tokens whose requests all have one:
     every request runs as a multi-token item, and the output equals the

@@ -140,24 +140,3 @@ def test_shared_prefix_decode_matches_oracle_and_private_copies():
     assert not (bt2[:, :12] == bt2[0, :12]).all()
     np.testing.assert_array_equal(ref, ref2)
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
-
-
-def test_shared_prefix_workload_sampled_rows():
-    """The full-size prefix workload (100 requests over one 2000-token
-    prompt's blocks): a decode step's output against the oracle on sampled
-    requests, in the launch configuration the bench times."""
-    from paged_kv_cache_mapping_amd import workloads
-    say("shared prefix workload")
-    w = workloads.shared_prefix_decode()
-    d = w.device()
-    slots = pkv.slot_mapping(d.block_table, d.query_start_loc, d.num_computed, w.block_size, w.num_blocks)
-    pkv.cache_write(d.new_k, d.new_v, slots, d.cache)
-    out = pkv.paged_attention_decode(d.q, d.cache, d.block_table, d.seq_lens, w.max_seq_len, w.scale)
-    torch.cuda.synchronize()
-    s_ref, e = paging.slot_mapping(w.block_table, w.query_start_loc, w.num_computed, w.block_size)
-    assert e == 0
-    kp, vp = paging.cache_write(w.k_plane, w.v_plane, w.new_k, w.new_v, s_ref, "bf16", "bf16")
-    rows = [0, 1, 37, 64, 99]
-    ref = attention.paged_decode(w.q[rows], "bf16", kp, vp, "bf16", w.block_table[rows], w.seq_lens[rows],
-                                 w.scale)
-    assert max_err(out_f64(out)[rows], ref) <= 2e-3
