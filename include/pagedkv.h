@@ -347,6 +347,31 @@ PKV_API int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dtype
                                hipStream_t stream);
 
 /*
+ * pkv_paged_attention_decode without a workspace argument, for callers that
+ * cannot allocate device memory (code under stream capture, serving loops
+ * that must not call hipMalloc, harnesses that forbid allocation).  The
+ * partial results go to a scratch array of PKV_STATIC_SCRATCH_BYTES that the
+ * library holds in device memory (one per GPU, from the library's load until
+ * the process ends); the call itself allocates nothing.  Every other
+ * argument and the result are exactly those of pkv_paged_attention_decode
+ * (same kernels, same plan).  Returns PKV_ERR_WORKSPACE when the plan for
+ * these arguments needs more scratch than that (pkv_decode_plan_make with
+ * the same arguments and flags 0 gives the size), PKV_ERR_HIP when the
+ * scratch's address cannot be obtained.  The scratch needs no
+ * initialisation and keeps the last call's partials; calls that overlap on
+ * one GPU (different streams, or different host threads) share it and race.
+ */
+#define PKV_STATIC_SCRATCH_BYTES (64u << 20)
+
+PKV_API int pkv_paged_attention_decode_static(void* out, const void* q, int32_t q_dtype,
+                                      int32_t num_seqs, int32_t num_q_heads,
+                                      const pkv_cache* cache,
+                                      const int32_t* block_table, int32_t bt_stride,
+                                      const int32_t* seq_lens, int32_t max_seq_len,
+                                      float softmax_scale, int32_t sliding_window,
+                                      hipStream_t stream);
+
+/*
  * The two phases of pkv_paged_attention_decode as separate calls, for callers
  * that merge partial results themselves (for example across devices) or time
  * the phases.  Phase 1 writes, per (row, query head, split), the base-2

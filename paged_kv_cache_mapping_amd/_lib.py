@@ -20,6 +20,8 @@ PKV_ERR_HIP = -6
 # pkv_decode_plan_make flags
 PKV_PLAN_BLOCKS_NOT_SHARED = 1
 
+PKV_STATIC_SCRATCH_BYTES = 64 << 20
+
 # pkv_dtype
 PKV_F32 = 0
 PKV_BF16 = 1
@@ -77,6 +79,8 @@ SIGNATURES = {
     "pkv_decode_plan_resize": (_int, [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(PkvDecodePlan)]),
     "pkv_paged_attention_decode": (_int, [_vp, _vp, _i32, _i32, _i32, ctypes.POINTER(PkvCache), _vp, _i32,
                                           _vp, _i32, _f32, _i32, _vp, _sz, _vp]),
+    "pkv_paged_attention_decode_static": (_int, [_vp, _vp, _i32, _i32, _i32, ctypes.POINTER(PkvCache), _vp,
+                                                 _i32, _vp, _i32, _f32, _i32, _vp]),
     "pkv_paged_attention_decode_partials": (_int, [_vp, _vp, _i32, _i32, _i32, ctypes.POINTER(PkvCache), _vp,
                                                    _i32, _vp, _i32, _f32, _i32, ctypes.POINTER(PkvDecodePlan),
                                                    _vp, _sz, _vp]),

@@ -1,6 +1,8 @@
 // Paged decode attention, host side: plans, argument checks, workspace
 // layout and the C entry points (decode and chunked).  The kernels and their
 // launch templates are in decode_kernels.h; decode_*.hip instantiate them.
+#include <mutex>
+
 #include "decode_kernels.h"
 #include "prefill.h"
 
@@ -475,6 +477,60 @@ extern "C" int pkv_paged_attention_decode(void* out, const void* q, int32_t q_dt
   st = prepare(a, out, q, q_dtype, num_seqs, num_q_heads, cache, block_table, bt_stride, seq_lens,
                max_seq_len, softmax_scale, sliding_window, 0, nullptr, 0, 0, 1, &plan, workspace,
                workspace_bytes);
+  if (st != PKV_OK) return st;
+  st = run_split(a, plan, cache->dtype, stream);
+  if (st != PKV_OK) return st;
+  return run_combine(a, q_dtype, stream);
+}
+
+// ---- decode with the library's own scratch (callers that cannot allocate)
+//
+// The decode's partials and piece counts live in this file-scope device
+// array instead of a caller's workspace.  Every GPU the library runs on
+// holds its own copy from module load until the process ends.  Host code
+// never names the array directly (its host-side name is not a device
+// address): the device address is looked up once per device, with that
+// device current, and passed to the kernels like any workspace.
+static __device__ __align__(256) char scratch[PKV_STATIC_SCRATCH_BYTES];
+
+static int static_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* dev_ptr[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return PKV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!dev_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PKV_ERR_HIP;
+    dev_ptr[dev] = p;
+  }
+  *ptr = dev_ptr[dev];
+  return PKV_OK;
+}
+
+extern "C" int pkv_paged_attention_decode_static(void* out, const void* q, int32_t q_dtype,
+                                                 int32_t num_seqs, int32_t num_q_heads,
+                                                 const pkv_cache* cache, const int32_t* block_table,
+                                                 int32_t bt_stride, const int32_t* seq_lens,
+                                                 int32_t max_seq_len, float softmax_scale,
+                                                 int32_t sliding_window, hipStream_t stream) {
+  int st = check_cache(cache);
+  if (st != PKV_OK) return st;
+  if (q_dtype != (cache->dtype == PKV_F32 ? PKV_F32 : PKV_BF16)) return PKV_ERR_DTYPE;
+  pkv_decode_plan plan;
+  st = make_plan(num_seqs, num_q_heads, cache->num_kv_heads, cache->head_dim, cache->block_size,
+                 cache->dtype, max_seq_len, sliding_window, 0, true, &plan);
+  if (st != PKV_OK) return st;
+  if (plan.workspace_bytes > PKV_STATIC_SCRATCH_BYTES) return PKV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (num_seqs > 0 && plan.workspace_bytes > 0) {
+    st = static_scratch(&ws);
+    if (st != PKV_OK) return st;
+  }
+  DecodeArgs a;
+  st = prepare(a, out, q, q_dtype, num_seqs, num_q_heads, cache, block_table, bt_stride, seq_lens,
+               max_seq_len, softmax_scale, sliding_window, 0, nullptr, 0, 0, 1, &plan, ws,
+               plan.workspace_bytes);
   if (st != PKV_OK) return st;
   st = run_split(a, plan, cache->dtype, stream);
   if (st != PKV_OK) return st;
