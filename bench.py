@@ -233,6 +233,75 @@ def summarize_profiles(out_dir):
     return rec
 
 
+def stream_probe(w, pools, dev, steps):
+    """The streaming-read probe (libpkvprobe.so): the K/V bytes of the decode
+    step's (row, KV head, block) units, read in the decode's order by
+    single-wave workers with nothing else to do, rotating over the same
+    pools; and the same number of units read block-contiguously.  Returns
+    GB/s of the bytes read (whole 16-token blocks) per setting and the best,
+    the practical ceiling the split kernel is held against."""
+    import ctypes
+    import torch
+    from paged_kv_cache_mapping_amd import build as pkv_build
+    lib = ctypes.CDLL(pkv_build.PROBE_LIB)
+    fn = lib.pkvprobe_stream_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                   ctypes.c_void_p]
+    elt = {"bf16": 2, "fp8": 1}.get(w.cache_dtype)
+    if elt is None or w.head_dim * elt != 256 or w.block_size != 16:
+        return None
+    row_bytes = w.num_kv_heads * w.head_dim * elt
+    nb = pools[0][0].num_blocks
+    blk_bytes = pools[0][0].block_stride * elt
+    lists = {"decode_order": [], "contiguous": []}
+    for p, (cache, bt) in enumerate(pools):
+        bt_h = bt.cpu().numpy()
+        offs = []
+        for r, L in enumerate(w.seq_lens):
+            n = -(-int(L) // w.block_size)
+            phys = bt_h[r, :n].astype(np.int64)
+            for h in range(w.num_kv_heads):
+                offs.append(phys * blk_bytes + h * w.head_dim * elt)
+        offs = np.concatenate(offs)
+        lists["decode_order"].append(torch.from_numpy(offs).to(dev))
+        u = np.arange(len(offs), dtype=np.int64)
+        first = (p * (nb // len(pools))) % max(1, nb - len(offs) // w.num_kv_heads - 1)
+        lists["contiguous"].append(torch.from_numpy((first + u // w.num_kv_heads) * blk_bytes
+                                                    + (u % w.num_kv_heads) * w.head_dim * elt).to(dev))
+    units = int(lists["decode_order"][0].numel())
+    nbytes = units * w.block_size * w.head_dim * elt * 2
+    sink = torch.empty(4096, dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    res = {"bytes_per_launch": nbytes, "units": units, "settings": {}}
+    for name, offs in lists.items():
+        for workers, depth in ((2048, 1), (1024, 1), (1024, 2), (2048, 2)):
+            def launch(i):
+                cache = pools[i % len(pools)][0]
+                st = fn(ctypes.c_void_p(cache.k.data_ptr()), ctypes.c_void_p(cache.v.data_ptr()),
+                        ctypes.c_void_p(offs[i % len(pools)].data_ptr()), units, row_bytes, 256, 16,
+                        workers, depth, ctypes.c_void_p(sink.data_ptr()), stream)
+                assert st == 0, st
+            for i in range(5):
+                launch(i)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for i in range(steps):
+                launch(i)
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) / steps * 1e3
+            res["settings"]["%s_w%d_d%d" % (name, workers, depth)] = dict(
+                us=round(us, 2), GBps=round(nbytes / (us * 1e-6) / 1e9, 1))
+    best = max(res["settings"].items(), key=lambda kv: kv[1]["GBps"] if kv[0].startswith("decode") else 0)
+    res["best_decode_order"] = dict(setting=best[0], **best[1])
+    bestc = max((v["GBps"] for k, v in res["settings"].items() if k.startswith("contiguous")))
+    res["best_contiguous_GBps"] = bestc
+    return res
+
+
 def rotating_pools(w, base, dev, count):
     """`count` KV pools holding the same logical data under different physical
     block permutations (so the last-level cache cannot serve the reads)."""
@@ -322,7 +391,7 @@ def bench_spec(args, dev):
     pools = rotating_pools(w, base, dev, POOLS)
     T, R = w.num_tokens, w.num_reqs
     nbytes = pkv.chunked_workspace_size(T, R, w.num_q_heads, base.cache, w.max_query_len, w.max_seq_len)
-    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    ws = pkv.new_workspace(nbytes, dev)
     out = torch.empty_like(base.q)
     slots = torch.empty(T, dtype=torch.int64, device=dev)
 
@@ -397,7 +466,7 @@ def bench_hybrid(args, dev):
     for g, W in enumerate(w.windows):
         nbytes = pkv.chunked_workspace_size(w.num_tokens, len(w.seq_lens), w.num_q_heads, views[layers[0]],
                                             w.max_query_len, w.max_seq_len, W)
-        ws[g] = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        ws[g] = pkv.new_workspace(nbytes, dev)
 
     def attend(name):
         g = group_of[name]
@@ -450,7 +519,7 @@ def bench_hybrid(args, dev):
         pout = torch.empty_like(pq)
         nbytes = pkv.chunked_workspace_size(len(pre_tok), len(pre), w.num_q_heads, views[name], pre_mql,
                                             w.max_seq_len, w.windows[g])
-        pws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        pws = pkv.new_workspace(nbytes, dev)
 
         def prefill_call():
             pkv.paged_attention_chunked(pq, pre_qsl, pre_sl, pre_mql, views[name], ptab, w.max_seq_len,
@@ -548,7 +617,7 @@ def main():
                            lead_workers=args.lead if args.lead >= 0 else None,
                            trail_share_pct=args.trail_pct or None,
                            heads_per_item=args.heads_per_item or None)
-    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device=dev)
+    ws = pkv.new_workspace(plan.workspace_bytes, dev)
     out = torch.empty_like(base.q)
     slots = torch.empty(w.num_reqs, dtype=torch.int64, device=dev)
     run_step = decode_step_fn(pkv, w, base, plan, ws, out, slots)
@@ -670,6 +739,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    probe = stream_probe(w, pools, dev, min(args.steps, 100)) if args.workload == "llama8b" else None
     traffic = traffic_from_profile() if args.workload == "llama8b" else None
     res = {
         "metric": "paged decode attention HBM GB/s (% of peak) + KV cache writes tokens/s, 1 GPU",
@@ -698,6 +768,11 @@ def main():
                              "split_GBps": round(split_gbps, 1),
                              "kv_bytes": ab["kv"], "step_bytes": ab["step"]},
         "kv_write": writes,
+        # the split kernel's GB/s (algorithmic bytes) against the probe's
+        # (every byte of the blocks it reads): a conservative fraction
+        **({"stream_probe": probe,
+            "split_pct_of_probe": round(100 * split_gbps / probe["best_decode_order"]["GBps"], 2)}
+           if probe else {}),
         **({"prefix_sharing": sharing} if sharing else {}),
         "roofline": {"bound": "hbm", "achieved": round(split_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(split_gbps / HBM_PEAK_GBPS, 4),

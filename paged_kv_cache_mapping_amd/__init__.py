@@ -13,6 +13,6 @@ from .api import (CacheView, cache_write, chunked_workspace_size, copy_blocks, d
                   paged_attention_chunked,
                   paged_attention_decode, paged_attention_decode_combine,
                   paged_attention_decode_partials, slot_mapping, slot_mapping_cache_write, status_string,
-                  tune_plan)
+                  new_workspace, tune_plan)
 from ._lib import PkvError, load  # noqa: F401
 from . import kv_cache, workloads  # noqa: F401

@@ -222,11 +222,17 @@ def tune_plan(plan, num_rows, num_q_heads, cache, max_seq_len, sliding_window=0,
     return plan
 
 
+def new_workspace(nbytes, device):
+    """A workspace for the attention calls (at least 16 bytes; its contents
+    need no initialisation)."""
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
 def _workspace(nbytes, device, workspace):
     if nbytes == 0:
         return workspace, 0
     if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        workspace = new_workspace(nbytes, device)
     _need(workspace.numel() * workspace.element_size() >= nbytes, "workspace too small")
     return workspace, workspace.numel() * workspace.element_size()
 

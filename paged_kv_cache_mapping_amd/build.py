@@ -1,7 +1,9 @@
 """Build libpagedkv.so (gfx950) in-tree with hipcc.
 
 Every HIP source under ``csrc/`` is compiled to an object in parallel and
-linked into ``paged_kv_cache_mapping_amd/libpagedkv.so``.  hipcc
+linked into ``paged_kv_cache_mapping_amd/libpagedkv.so``; ``csrc/probe``
+(the streaming-read probe that bench.py measures the ceiling with) becomes
+``libpkvprobe.so``.  hipcc
 cross-compiles, so this runs on a machine without a GPU.
 """
 
@@ -17,6 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
+PROBE_LIB = os.path.join(PKG, "libpkvprobe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "probe", "stream_read.hip")]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -49,21 +53,29 @@ def _compile(src):
     return obj
 
 
-def build(verbose=True, jobs=None):
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    jobs = jobs or min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=True, jobs=None):
+    """Compile every source, link the shared library and the streaming-read
+    probe's library (csrc/probe, used by bench.py only); returns the
+    library's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources() + PROBE_SOURCES
+    jobs = jobs or min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, srcs))
+    n = len(srcs) - len(PROBE_SOURCES)
+    _link(objs[:n], LIB)
+    _link(objs[n:], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

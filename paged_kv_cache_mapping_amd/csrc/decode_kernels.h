@@ -975,15 +975,15 @@ __host__ __device__ inline FlatLds flat_lds_layout(int rows, int gt, int d, int 
 struct Shares {
   long long p_lead, p_trail, lead_end;
   int lead;
-  __device__ long long begin(long long w) const {
+  __device__ __forceinline__ long long begin(long long w) const {
     return w <= lead ? w * p_lead : lead_end + (w - lead) * p_trail;
   }
-  __device__ long long range_of(long long u) const {
+  __device__ __forceinline__ long long range_of(long long u) const {
     return u < lead_end ? u / p_lead : lead + (u - lead_end) / p_trail;
   }
 };
 
-__device__ inline Shares make_shares(long long U, int W, int lead, int pct, int min_units) {
+__device__ __forceinline__ Shares make_shares(long long U, int W, int lead, int pct, int min_units) {
   Shares s;
   if (lead <= 0 || lead >= W || pct >= 100 || pct <= 0) {
     s.lead = W;
@@ -1779,6 +1779,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
   // pass owns them) get a piece count of 0 so that the merge phase leaves
   // them alone; rows that cannot be computed also get NaN output
   for (int r = blockIdx.x; r < a.num_rows; r += W) {
+    if (cum[r + 1] != cum[r]) continue;       // a row with units: written by its pieces
     const RowInfo ri = row_info(a, r);
     if (ri.valid && !ri.skip) continue;
     if (!ri.skip) {
@@ -1791,7 +1792,6 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
 }
 
 // --------------------------------------------------------------------------
-// Combine phase: one wave per (row, query head) with more than one split.
 // The balanced kernel; decode_flat_kernel_2w asks the compiler to fit two
 // waves per SIMD (used for eight query heads per item, where the default
 // register allocation leaves room for only one).
@@ -1884,6 +1884,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   store_out<OT, DPL>(a.out, ((int64_t)(tok + t) * a.num_q_heads + g * GT + h % GT) * D + d0, o);
 }
 
+// Combine phase of the fixed splits: one wave per (row, query head) with
+// more than one split.
 template <int D, int OT>
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   constexpr int PER = D >= kWave ? D / kWave : 1;  // elements per lane
@@ -1895,35 +1897,14 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   const RowInfo span = row_info(a, b);
   if (span.skip || !span.valid) return;
   const int tok = span.tok;
-  int nsplit;
-  if (a.stream) {   // rows the split phase rejected have a piece count of 0
-    const int groups = a.num_q_heads / a.heads_per_item;
-    nsplit = a.ws_np[2 * ((int64_t)b * groups + h / a.heads_per_item)];
-  } else {
-    nsplit = ceil_div(span.nvis, a.split_blocks);
-  }
-  nsplit = min(nsplit, a.max_splits);
+  const int nsplit = min(ceil_div(span.nvis, a.split_blocks), a.max_splits);
   if (nsplit <= 1) return;
 
   const int64_t pr0 = ((int64_t)b * a.num_q_heads + h) * a.max_splits;
-  // where piece s keeps m and l: fixed splits use two plain arrays; the
-  // balanced kernel packs the heads of a piece into one record (m..., l...)
-  const float* mp;
-  const float* lp;
-  int mstride;
-  if (a.stream) {
-    const int gt = a.heads_per_item;
-    const int64_t rec0 = ((int64_t)b * (a.num_q_heads / gt) + h / gt) * a.max_splits;
-    mp = a.ws_m + rec0 * 2 * gt + h % gt;
-    lp = mp + gt;
-    mstride = 2 * gt;
-  } else {
-    mp = a.ws_m + pr0;
-    lp = a.ws_l + pr0;
-    mstride = 1;
-  }
+  const float* mp = a.ws_m + pr0;
+  const float* lp = a.ws_l + pr0;
   float M = -INFINITY;
-  for (int s = lane; s < nsplit; s += kWave) M = fmaxf(M, mp[(int64_t)s * mstride]);
+  for (int s = lane; s < nsplit; s += kWave) M = fmaxf(M, mp[s]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
 
@@ -1933,9 +1914,9 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   for (int i = 0; i < PER; ++i) num[i] = 0.f;
   const bool active = D >= kWave || lane < D;
   for (int s = 0; s < nsplit; ++s) {
-    const float ms = mp[(int64_t)s * mstride];
+    const float ms = mp[s];
     const float wgt = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-    den = fmaf(wgt, lp[(int64_t)s * mstride], den);
+    den = fmaf(wgt, lp[s], den);
     if (active) {
       const float* src = a.ws_acc + (pr0 + s) * D;
 #pragma unroll

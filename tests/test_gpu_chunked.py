@@ -169,12 +169,14 @@ def test_chunked_long_queries_span_several_tiles(Hq, Hkv, causal, W):
     assert max_err(out_f64(out), ref) <= 2e-3
 
 
-def test_chunked_workspace_contents_do_not_matter():
-    """The chunked call on a workspace filled with large garbage words: rows
-    of multi-query requests are skipped by the single-query pass, which must
-    still leave a piece count of 0 for them so that the merge phase never
-    reads stale counts or output rows."""
-    say("chunked garbage workspace")
+def test_chunked_stale_workspace_contents_do_not_matter():
+    """The chunked call on a workspace that a different step used before
+    (all requests single-query, so every row left a piece count and output
+    row behind): rows of multi-query requests are skipped by the
+    single-query pass, which must still leave a piece count of 0 for them so
+    that the merge phase never reads the stale counts.  The workspace starts
+    zeroed, as the contract asks, and is never cleared again."""
+    say("chunked stale workspace")
     c = _chunk_case(1700, R=9, Lmax=400, qmax=60, Hq=8, Hkv=2, D=128, bs=16)
 
     def dev16(a):
@@ -183,14 +185,20 @@ def test_chunked_workspace_contents_do_not_matter():
     T, R = int(c["qsl"][-1]), len(c["L"])
     qmax, Lmax = int(np.diff(c["qsl"]).max()), int(c["L"].max())
     n = pkv.chunked_workspace_size(T, R, 8, cache, qmax, Lmax)
-    ws = torch.full((max(n, 16),), 0x7F, dtype=torch.uint8, device="cuda")
-    out = pkv.paged_attention_chunked(dev16(c["q"]), torch.from_numpy(c["qsl"]).cuda(),
-                                      torch.from_numpy(c["L"]).cuda(), qmax, cache,
-                                      torch.from_numpy(c["bt"]).cuda(), Lmax, 0.125, workspace=ws)
-    torch.cuda.synchronize()
-    ref = attention.paged_attention(c["q"], "bf16", c["kp"], c["vp"], "bf16", c["bt"], c["L"],
-                                    c["qsl"], 0.125)
-    assert max_err(out_f64(out), ref) <= 2e-3
+    ws = pkv.new_workspace(n, "cuda")
+    # the earlier step: one query per request, at each request's last position
+    qsl1 = np.arange(R + 1, dtype=np.int32)
+    q1 = c["q"][c["qsl"][1:] - 1].copy()
+    pkv.paged_attention_chunked(dev16(q1), torch.from_numpy(qsl1).cuda(), torch.from_numpy(c["L"]).cuda(),
+                                qmax, cache, torch.from_numpy(c["bt"]).cuda(), Lmax, 0.125, workspace=ws)
+    for _ in range(2):
+        out = pkv.paged_attention_chunked(dev16(c["q"]), torch.from_numpy(c["qsl"]).cuda(),
+                                          torch.from_numpy(c["L"]).cuda(), qmax, cache,
+                                          torch.from_numpy(c["bt"]).cuda(), Lmax, 0.125, workspace=ws)
+        torch.cuda.synchronize()
+        ref = attention.paged_attention(c["q"], "bf16", c["kp"], c["vp"], "bf16", c["bt"], c["L"],
+                                        c["qsl"], 0.125)
+        assert max_err(out_f64(out), ref) <= 2e-3
 
 
 def test_chunked_unmapped_block_poisons_only_rows_that_reach_it():

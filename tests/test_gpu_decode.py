@@ -68,7 +68,7 @@ def _check_attention_only(w, window=0, plan_split=None, not_shared=False):
             workers = None if plan.scheme == 0 else max(1, plan.num_workers // plan_split)
             pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len, window,
                           split_blocks=plan_split, num_workers=workers)
-        ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+        ws = pkv.new_workspace(plan.workspace_bytes, "cuda")
         out = torch.empty_like(d.q)
         pkv.paged_attention_decode_partials(d.q, d.cache, d.block_table, d.seq_lens, w.max_seq_len,
                                             w.scale, plan, ws, out, sliding_window=window)
@@ -170,7 +170,7 @@ def test_vector_alu_fixed_split_path(split):
         # build the equivalent scheme-0 plan by hand: vector kernels, fixed splits
         plan.scheme, plan.num_workers, plan.heads_per_item = 0, 0, 4
     pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len, split_blocks=split)
-    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    ws = pkv.new_workspace(plan.workspace_bytes, "cuda")
     out = torch.empty_like(d.q)
     pkv.paged_attention_decode_partials(d.q, d.cache, d.block_table, d.seq_lens, w.max_seq_len,
                                         w.scale, plan, ws, out)
@@ -187,7 +187,7 @@ def test_phases_equal_the_one_call_form_bit_for_bit():
     d = w.device()
     one = pkv.paged_attention_decode(d.q, d.cache, d.block_table, d.seq_lens, w.max_seq_len, w.scale)
     plan = pkv.decode_plan(w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len)
-    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    ws = pkv.new_workspace(plan.workspace_bytes, "cuda")
     two = torch.empty_like(d.q)
     pkv.paged_attention_decode_partials(d.q, d.cache, d.block_table, d.seq_lens, w.max_seq_len,
                                         w.scale, plan, ws, two)
@@ -215,7 +215,7 @@ def test_fp8_phases_called_separately(split):
     elif split is not None:
         pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len,
                       num_workers=max(1, plan.num_workers // split))
-    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    ws = pkv.new_workspace(plan.workspace_bytes, "cuda")
     out = torch.empty_like(d.q)
     pkv.paged_attention_decode_partials(d.q, d.cache, d.block_table, d.seq_lens, w.max_seq_len,
                                         w.scale, plan, ws, out)
@@ -304,3 +304,28 @@ def test_edge_cases_empty_batch_length_one_and_invalid_rows():
     ref = attention.paged_decode(w.q[4:], "bf16", w.k_plane, w.v_plane, "bf16", w.block_table[4:],
                                  w.seq_lens[4:], w.scale)
     assert max_err(o[4:], ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("rows", [23, 64])
+def test_stale_workspace_gives_the_same_bits(rows):
+    """A workspace that a larger call used before (its partial records and
+    row-group entries left behind) gives exactly the bits of a fresh one:
+    every record a merge reads was written by the same call.  Batches with
+    fewer units than the workers could take leave static shares empty."""
+    say("decode stale workspace", rows)
+    w = workloads.llama8b_decode()
+    d = w.device()
+    big = pkv.decode_plan(w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len)
+    ws = pkv.new_workspace(big.workspace_bytes, "cuda")
+    junk = torch.empty_like(d.q)
+    pkv.paged_attention_decode(d.q, d.cache, d.block_table, d.seq_lens, w.max_seq_len, w.scale,
+                               workspace=ws, out=junk)
+    stale = pkv.paged_attention_decode(d.q[:rows], d.cache, d.block_table[:rows], d.seq_lens[:rows],
+                                       w.max_seq_len, w.scale, workspace=ws)
+    fresh = pkv.paged_attention_decode(d.q[:rows], d.cache, d.block_table[:rows], d.seq_lens[:rows],
+                                       w.max_seq_len, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(stale.view(torch.int16), fresh.view(torch.int16))
+    ref = attention.paged_decode(w.q[:rows], "bf16", w.k_plane, w.v_plane, "bf16", w.block_table[:rows],
+                                 w.seq_lens[:rows], w.scale)
+    check_close("stale_ws_%d" % rows, out_f64(stale), ref, 2e-3, 1e-5)

@@ -52,7 +52,7 @@ def _gpu():
 
 def _bench_decode_step(w, base, cache=None, bt=None):
     plan = bench.decode_plan_for(pkv, w, base.cache)
-    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    ws = pkv.new_workspace(plan.workspace_bytes, "cuda")
     out = torch.empty_like(base.q)
     slots = torch.empty(w.num_reqs, dtype=torch.int64, device="cuda")
     step = bench.decode_step_fn(pkv, w, base, plan, ws, out, slots)

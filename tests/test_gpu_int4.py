@@ -123,7 +123,7 @@ def _attend(w, window=0, split=None):
         plan = pkv.decode_plan(w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len, window)
         pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len, window, split_blocks=split,
                       num_workers=max(1, plan.num_workers // split))
-        ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+        ws = pkv.new_workspace(plan.workspace_bytes, "cuda")
         out = torch.empty_like(d.q)
         pkv.paged_attention_decode_partials(d.q, d.cache, d.block_table, d.seq_lens, w.max_seq_len, w.scale,
                                             plan, ws, out, sliding_window=window)
@@ -173,7 +173,7 @@ def test_single_head_and_pair_items_agree_with_the_oracle(hpi):
     plan = pkv.decode_plan(w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len)
     assert plan.heads_per_item == 8
     pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len, heads_per_item=hpi)
-    ws = torch.empty(max(plan.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    ws = pkv.new_workspace(plan.workspace_bytes, "cuda")
     out = torch.empty_like(d.q)
     pkv.paged_attention_decode_partials(d.q, d.cache, d.block_table, d.seq_lens, w.max_seq_len, w.scale,
                                         plan, ws, out)

@@ -74,18 +74,34 @@ def test_static_scratch_decode_small_shapes_and_window():
 
 
 def test_static_scratch_refuses_plans_past_its_size():
-    """A batch whose plan needs more than the scratch holds returns
-    PKV_ERR_WORKSPACE (checked on the host; nothing launched)."""
+    """A batch whose plan needs more than the scratch holds (4096 rows of the
+    Llama-3-8B shape: one partial record per share, run-time chunk and row
+    group) returns PKV_ERR_WORKSPACE, checked on the host before anything is
+    launched; the workspace form of the same call runs."""
     lib = _lib.load()
     w = workloads.llama8b_decode()
     d = w.device()
-    # 64 rows of up to 2**20 keys: max_splits ~ 8193 slots per (row, head)
-    big = 1 << 20
+    rows = 4096
     plan = _lib.PkvDecodePlan()
-    assert lib.pkv_decode_plan_make(64, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
-                                    _lib.PKV_BF16, big, 0, 0, ctypes.byref(plan)) == _lib.PKV_OK
+    assert lib.pkv_decode_plan_make(rows, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                                    _lib.PKV_BF16, w.max_seq_len, 0, 0, ctypes.byref(plan)) == _lib.PKV_OK
     assert plan.workspace_bytes > _lib.PKV_STATIC_SCRATCH_BYTES
-    out = torch.empty_like(d.q)
-    st = _static_call(lib, out, d, w, 64, big)
+    # a batch of that many rows: every row one copy of row 0 of the workload
+    q = d.q[:1].expand(rows, -1, -1).contiguous()
+    bt = d.block_table[:1].expand(rows, -1).contiguous()
+    sl = d.seq_lens[:1].expand(rows).contiguous()
+
+    class Big:
+        pass
+    big = Big()
+    big.q, big.block_table, big.seq_lens, big.cache = q, bt, sl, d.cache
+    out = torch.full_like(q, float("nan"))
+    st = _static_call(lib, out, big, w, rows, w.max_seq_len)
     assert st == _lib.PKV_ERR_WORKSPACE
-    assert np.isfinite(out_f64(_workspace_call(d, w, 64, w.max_seq_len))).all()
+    torch.cuda.synchronize()
+    assert torch.isnan(out.float()).all()          # nothing was launched
+    got = pkv.paged_attention_decode(q, d.cache, bt, sl, w.max_seq_len, w.scale)
+    torch.cuda.synchronize()
+    ref0 = attention.paged_decode(w.q[:1], "bf16", w.k_plane, w.v_plane, "bf16", w.block_table[:1],
+                                  w.seq_lens[:1], w.scale)
+    assert max_err(out_f64(got), np.broadcast_to(ref0, got.shape)) <= 2e-3
