@@ -32,9 +32,12 @@
  *   returns PKV_ERR_HIP.  Zero-sized work (no tokens, no sequences) returns
  *   PKV_OK and launches nothing.
  * - Data-dependent errors never fault: see each call.
- * - The only library state is a per-device cache of the compute-unit count;
- *   calls are reentrant.  Calls on one stream run in order; calls that share
- *   an output or workspace on different streams race.
+ * - Library state: a per-device cache of the compute-unit count and, once a
+ *   chunked call has run a prefill part on a device, one more stream and two
+ *   events on that device (created on first use, default priority, kept
+ *   until the process ends; see pkv_paged_attention_chunked).  Calls are
+ *   reentrant.  Calls on one stream run in order; calls that share an output
+ *   or workspace on different streams race.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
@@ -442,6 +445,12 @@ PKV_API int pkv_chunked_workspace_size(int32_t num_tokens, int32_t num_reqs,
  * Invalid rows (q_len > seq_len, lengths out of range, missing blocks) get NaN.
  * INT4 caches: the decode form's shapes (head_dim 128, at most 4096
  * requests); others return PKV_ERR_UNSUPPORTED.
+ * When max_query_len is above 8 (the matrix-core prefill path), the requests
+ * with more than one query token run
+ * on the library's second stream of the device, forked from `stream` by an
+ * event and joined back into it by another, beside the single-query
+ * requests' part on `stream`: later work on `stream` sees the whole result,
+ * as if the call had run on `stream` alone (stream capture included).
  */
 PKV_API int pkv_paged_attention_chunked(void* out, const void* q, int32_t q_dtype,
                                 int32_t num_tokens, int32_t num_q_heads,

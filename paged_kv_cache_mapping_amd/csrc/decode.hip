@@ -537,6 +537,37 @@ extern "C" int pkv_paged_attention_decode_static(void* out, const void* q, int32
   return run_combine(a, q_dtype, stream);
 }
 
+// ---- a second stream per device, on which a chunked call runs its prefill
+// part beside its decode part.  Events order the side stream after the
+// caller's stream's earlier work and the caller's stream after the side
+// stream's, so the call behaves as if it ran on the caller's stream alone.
+// One mutex covers each fork / join sequence, so calls from several host
+// threads never interleave their event records.  Default priority (the
+// stream is created like any other).
+struct SideStream {
+  hipStream_t stream;
+  hipEvent_t fork, join;
+};
+static std::mutex g_side_mu;
+
+// Under g_side_mu.
+static int side_stream(SideStream** out) {
+  static SideStream side[64];
+  static bool made[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return PKV_ERR_HIP;
+  if (!made[dev]) {
+    SideStream x;
+    if (hipStreamCreateWithFlags(&x.stream, hipStreamNonBlocking) != hipSuccess) return PKV_ERR_HIP;
+    if (hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) != hipSuccess) return PKV_ERR_HIP;
+    if (hipEventCreateWithFlags(&x.join, hipEventDisableTiming) != hipSuccess) return PKV_ERR_HIP;
+    side[dev] = x;
+    made[dev] = true;
+  }
+  *out = &side[dev];
+  return PKV_OK;
+}
+
 // The chunked form runs two passes over disjoint rows: requests with one
 // query take the decode kernels (rows = requests), every other request's
 // tokens take the per-token rows.  Each pass has its own workspace region.
@@ -700,10 +731,25 @@ extern "C" int pkv_paged_attention_chunked(void* out, const void* q, int32_t q_d
     pa.scale_log2 = softmax_scale * log2e * (scaled ? cache->k_scale : 1.0f);
     pa.v_scale = scaled ? cache->v_scale : 1.0f;
     pa.part = reinterpret_cast<float*>(ws + p.single_bytes);
-    st = launch_prefill(pa, cache->dtype, cache->head_dim, stream);
+    // The prefill tile runs on the side stream, the single-query requests'
+    // decode pass on the caller's stream: the two kernels are launched
+    // together and the GPU runs whatever fits of the second beside the
+    // first (their ramps and tails overlap; their full-occupancy bodies
+    // cannot share a compute unit at these register counts).
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream* side = nullptr;
+    st = side_stream(&side);
     if (st != PKV_OK) return st;
-    st = launch_status();
-    if (st != PKV_OK) return st;
+    if (hipEventRecord(side->fork, stream) != hipSuccess) return PKV_ERR_HIP;
+    if (hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess) return PKV_ERR_HIP;
+    st = launch_prefill(pa, cache->dtype, cache->head_dim, side->stream);
+    if (st == PKV_OK) st = launch_status();
+    if (hipEventRecord(side->join, side->stream) != hipSuccess) return PKV_ERR_HIP;
+    int st2 = run_split(a1, p.single, cache->dtype, stream);
+    if (st2 == PKV_OK) st2 = run_combine(a1, q_dtype, stream);
+    // the caller's stream waits for the prefill part whatever happened
+    if (hipStreamWaitEvent(stream, side->join, 0) != hipSuccess) return PKV_ERR_HIP;
+    return st != PKV_OK ? st : st2;
   } else if (max_query_len > 1) {
     DecodeArgs a2;
     st = prepare(a2, out, q, q_dtype, num_tokens, num_q_heads, cache, block_table, bt_stride,

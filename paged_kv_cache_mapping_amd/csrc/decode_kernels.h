@@ -1346,6 +1346,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
     const int nunits = (int)min((long long)kWave, u_hi - wbase);
     // ---- unit records of this window
     rec_phys = -1; rec_gid = -1;
+    int bt_raw = -1;    // the unit's table entry, checked once the query loads are in flight too
     if (lane < nunits) {
       const long long u = wbase + lane;
       int lo = 0, hi = a.num_rows;            // largest b with cum[b] * kvgroups <= u
@@ -1367,8 +1368,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
         req = ri.req; tok = ri.tok; klo = ri.lo; khi = ri.hi;
       }
       const int first_blk = klo >> a.bs_log2;
-      const int t = a.bt[(int64_t)req * a.bt_stride + first_blk + j];
-      rec_phys = (t >= 0 && t < a.num_blocks) ? t : -1;
+      bt_raw = a.bt[(int64_t)req * a.bt_stride + first_blk + j];
       rec_hoff = (kvg / a.sub_groups) * S::kRowBytes;
       rec_gid = b * kvgroups + kvg;
       rec_pos0 = (first_blk + j) << a.bs_log2;
@@ -1419,6 +1419,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
+    rec_phys = (lane < nunits && bt_raw >= 0 && bt_raw < a.num_blocks) ? bt_raw : -1;
     asm volatile("" : "+v"(rec_phys), "+v"(rec_gid), "+v"(rec_hoff), "+v"(rec_pos0),
                  "+v"(rec_lo), "+v"(rec_hi), "+v"(rec_tok));
     const int g0 = __builtin_amdgcn_readfirstlane(rec_gid);

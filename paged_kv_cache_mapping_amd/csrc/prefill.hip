@@ -46,17 +46,22 @@ typedef float pf_f32x4 __attribute__((ext_vector_type(4)));
 typedef short pf_i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) pf_i16x4 lds_i16x4;
 
-constexpr int kPfWaves = 8;          // two per SIMD: one computes while the other waits
-constexpr int kPfThreads = kPfWaves * 64;
+// Waves per workgroup: two per SIMD, one computes while the other waits.  (A
+// four-wave form, one per SIMD so that a decode wave fits beside it, folded
+// at about 60 % of this one's rate and was slower overall.)  The merge kernel
+// runs 512 threads.
+constexpr int kPfWavesAlone = 8;
+constexpr int kPfMergeThreads = 512;
 constexpr int kPfKeys = 32;          // keys per tile
 constexpr float kPfLazy = 8.0f;      // keep a stale max until a score beats it by 2^8
 
-template <int D, int G>
+template <int D, int G, int NW>
 struct PfShape {
+  static constexpr int NT = NW * 64;             // threads per workgroup
   static constexpr int NBW = 2;                  // 16-row blocks per wave
   static constexpr int TPN = 16 / G;             // query tokens per row block
   static constexpr int TW = NBW * TPN;           // query tokens per wave
-  static constexpr int TWG = kPfWaves * TW;      // query tokens per workgroup
+  static constexpr int TWG = NW * TW;            // query tokens per workgroup
   static constexpr int NC = D / 32;              // k-chunks of the score product
   static constexpr int MB = D / 16;              // 16-dim blocks of the output
   // LDS bytes per staged key row.  K rows are read 16 rows x 16 bytes per
@@ -69,7 +74,7 @@ struct PfShape {
   static constexpr int TILE = TILEK + TILEV;     // LDS bytes of one staged K + V tile
   static constexpr int CPR = D / 8;              // 16-byte bf16 chunks per key row
   static constexpr int CPT = kPfKeys * CPR;      // chunks per tile
-  static constexpr int CPTH = (CPT + kPfThreads - 1) / kPfThreads;  // chunks per thread and plane
+  static constexpr int CPTH = (CPT + NT - 1) / NT;  // chunks per thread and plane
   static_assert(16 % G == 0, "group must divide 16");
 };
 
@@ -88,7 +93,7 @@ __device__ __forceinline__ float pf_group4_max(float x) {
 
 template <int D, int G>
 size_t pf_lds_bytes(int max_blocks) {
-  return 2 * (size_t)PfShape<D, G>::TILE + pf_align16((size_t)max_blocks * sizeof(int));
+  return 2 * (size_t)PfShape<D, G, kPfWavesAlone>::TILE + pf_align16((size_t)max_blocks * sizeof(int));
 }
 
 // ---- the balanced partition
@@ -147,9 +152,10 @@ __device__ __forceinline__ long long pf_head_units(const PrefillArgs& a, const P
 
 // Whole workgroup: the total unit count; for target >= 0 also the request
 // holding unit `target` and that request's first unit.
-template <int TWG>
+template <int TWG, int NW>
 __device__ long long pf_scan(const PrefillArgs& a, long long target, int& req, long long& req_first) {
-  __shared__ long long wsum[kPfWaves];
+  constexpr int NT = NW * 64;
+  __shared__ long long wsum[NW];
   __shared__ long long found[2];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();   // an earlier call may still be reading `found`
@@ -159,7 +165,7 @@ __device__ long long pf_scan(const PrefillArgs& a, long long target, int& req, l
   }
   __syncthreads();
   long long carry = 0;
-  for (int base = 0; base < a.num_reqs; base += kPfThreads) {
+  for (int base = 0; base < a.num_reqs; base += NT) {
     const int r = base + (int)threadIdx.x;
     long long u = 0;
     if (r < a.num_reqs) u = pf_head_units<TWG>(a, pf_req<TWG>(a, r)) * a.num_kv_heads;
@@ -172,7 +178,7 @@ __device__ long long pf_scan(const PrefillArgs& a, long long target, int& req, l
     if (lane == 63) wsum[wave] = x;
     __syncthreads();
     long long before = carry, chunk = 0;
-    for (int i = 0; i < kPfWaves; ++i) {
+    for (int i = 0; i < NW; ++i) {
       if (i < wave) before += wsum[i];
       chunk += wsum[i];
     }
@@ -247,10 +253,11 @@ __device__ __forceinline__ int pf_share_of_block(int b, int W) {
 // qt), counted from the item's first key tile.  slot < 0: the piece is the
 // whole item and writes the output; otherwise it writes its unnormalised
 // state to that slot.
-template <int D, int G, int KV>
+template <int D, int G, int KV, int NW>
 __device__ __forceinline__ void pf_piece(const PrefillArgs& a, char* lds, const PfReq& rq, int kvh,
                                          int qt, int ta, int tb, int slot) {
-  using S = PfShape<D, G>;
+  using S = PfShape<D, G, NW>;
+  constexpr int kPfThreads = S::NT;
   constexpr int NBW = S::NBW, TPN = S::TPN, TW = S::TW, TWG = S::TWG;
   constexpr int NC = S::NC, MB = S::MB, RSK = S::RSK, RSV = S::RSV, TILE = S::TILE;
   constexpr int CPR = S::CPR, CPT = S::CPT, CPTH = S::CPTH;
@@ -598,15 +605,16 @@ __device__ __forceinline__ void pf_piece(const PrefillArgs& a, char* lds, const 
   }
 }
 
-template <int D, int G, int KV>
-__global__ __launch_bounds__(kPfThreads) void prefill_tile_kernel(PrefillArgs a) {
-  constexpr int TWG = PfShape<D, G>::TWG;
+template <int D, int G, int KV, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_tile_kernel(
+    PrefillArgs a) {
+  constexpr int TWG = PfShape<D, G, NW>::TWG;
   extern __shared__ __align__(16) char lds[];
   const int W = (int)gridDim.x;
   const int w = pf_share_of_block((int)blockIdx.x, W);
   int r;
   long long rfirst;
-  const long long U = pf_scan<TWG>(a, -1, r, rfirst);
+  const long long U = pf_scan<TWG, NW>(a, -1, r, rfirst);
   const long long b = pf_bound(U, w, W), e = pf_bound(U, w + 1, W);
   PfShareRec* rec = reinterpret_cast<PfShareRec*>(a.part + pf_slot_floats(W, D)) + w;
   if (b >= e) {
@@ -617,7 +625,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_tile_kernel(PrefillArgs a)
     }
     return;
   }
-  pf_scan<TWG>(a, b, r, rfirst);
+  pf_scan<TWG, NW>(a, b, r, rfirst);
   if (r < 0) return;   // (cannot happen: both scans count the same units)
   PfReq q = pf_req<TWG>(a, r);
   long long span = pf_head_units<TWG>(a, q) * a.num_kv_heads;
@@ -646,7 +654,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_tile_kernel(PrefillArgs a)
       x.head = it.first < b ? 1 : 0;
       *rec = x;
     }
-    pf_piece<D, G, KV>(a, lds, q, it.kvh, it.qt, (int)(u - it.first), (int)(pend - it.first), slot);
+    pf_piece<D, G, KV, NW>(a, lds, q, it.kvh, it.qt, (int)(u - it.first), (int)(pend - it.first), slot);
     u = pend;
   }
 }
@@ -656,9 +664,10 @@ __global__ __launch_bounds__(kPfThreads) void prefill_tile_kernel(PrefillArgs a)
 // in the closest earlier share j' holding units; its pieces are slot
 // 2 j' + 1, then slot 2 w of every non-empty share w >= j that the item
 // reaches.  Each thread merges one row's share of the dimensions.
-template <int D, int G>
-__global__ __launch_bounds__(kPfThreads) void prefill_merge_kernel(PrefillArgs a) {
-  using S = PfShape<D, G>;
+template <int D, int G, int NW>
+__global__ __launch_bounds__(kPfMergeThreads) void prefill_merge_kernel(PrefillArgs a) {
+  using S = PfShape<D, G, NW>;
+  constexpr int kPfThreads = kPfMergeThreads;
   constexpr int TWG = S::TWG, TW = S::TW, TPN = S::TPN, NBW = S::NBW;
   constexpr int ROWS = TWG * G;                 // rows of a slot (256)
   constexpr int TPR = kPfThreads / ROWS;        // threads per row
@@ -724,7 +733,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_merge_kernel(PrefillArgs a
 }
 
 template <int D, int G>
-constexpr int pf_tokens_per_wg() { return PfShape<D, G>::TWG; }
+constexpr int pf_tokens_per_wg() { return PfShape<D, G, kPfWavesAlone>::TWG; }
 
 int pf_tokens(int d, int g) {
   switch (d * 100 + g) {
@@ -749,8 +758,9 @@ int pf_tokens(int d, int g) {
 
 template <int D, int G, int KV>
 void pf_launch(const PrefillArgs& a, hipStream_t s) {
-  prefill_tile_kernel<D, G, KV><<<a.workers, kPfThreads, pf_lds_bytes<D, G>(a.max_blocks), s>>>(a);
-  prefill_merge_kernel<D, G><<<a.workers, kPfThreads, 0, s>>>(a);
+  const size_t lds = pf_lds_bytes<D, G>(a.max_blocks);
+  prefill_tile_kernel<D, G, KV, kPfWavesAlone><<<a.workers, kPfWavesAlone * 64, lds, s>>>(a);
+  prefill_merge_kernel<D, G, kPfWavesAlone><<<a.workers, kPfMergeThreads, 0, s>>>(a);
 }
 
 template <int D, int KV>
