@@ -53,6 +53,21 @@ __device__ __forceinline__ uint32_t e4m3_encode(float x) {
   return sign | code;
 }
 
+// Four binary32 values, none of them NaN, to four codes (byte i holds value
+// i), equal to e4m3_encode of each: the clamp to [-448, 448] gives the
+// saturation (infinities included), and the hardware conversion rounds to
+// nearest even, subnormals included.  Callers send chunks that hold a NaN to
+// e4m3_encode instead (a clamp would turn NaN into a finite value).
+__device__ __forceinline__ uint32_t e4m3x4_encode_no_nan(float a, float b, float c, float d) {
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+  d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
 // Two codes (kHighWord false: bytes 0,1 of the dword; true: bytes 2,3) to
 // two binary32 values, exact (hardware OCP conversion on gfx950).
 typedef float f32x2 __attribute__((ext_vector_type(2)));

@@ -243,11 +243,22 @@ __global__ __launch_bounds__(256) void cache_write_kernel(WriteArgs a) {
     const float inv = kv ? a.inv_v_scale : a.inv_k_scale;
     float x[CE];
     load_as_f32<SRC, CE>(src, x);
-    uint32_t w[CE / 4];
+    bool nan = false;
 #pragma unroll
-    for (int i = 0; i < CE / 4; ++i) {
-      w[i] = e4m3_encode(x[4 * i] * inv) | (e4m3_encode(x[4 * i + 1] * inv) << 8) |
-             (e4m3_encode(x[4 * i + 2] * inv) << 16) | (e4m3_encode(x[4 * i + 3] * inv) << 24);
+    for (int i = 0; i < CE; ++i) {
+      x[i] *= inv;
+      nan |= x[i] != x[i];
+    }
+    uint32_t w[CE / 4];
+    if (!nan) {  // the hardware conversion (a few operations per element)
+#pragma unroll
+      for (int i = 0; i < CE / 4; ++i)
+        w[i] = e4m3x4_encode_no_nan(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+    } else {     // a NaN in the chunk: the integer encoder keeps it
+#pragma unroll
+      for (int i = 0; i < CE / 4; ++i)
+        w[i] = e4m3_encode(x[4 * i]) | (e4m3_encode(x[4 * i + 1]) << 8) |
+               (e4m3_encode(x[4 * i + 2]) << 16) | (e4m3_encode(x[4 * i + 3]) << 24);
     }
     if constexpr (CE == 16) {
       *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
