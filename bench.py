@@ -15,7 +15,6 @@ bulk KV-write rates, and the CPU oracle on a bounded sample of the same step.
 """
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -25,6 +24,8 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+import bench_profiles  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E, AMD's published peak
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
@@ -43,9 +44,8 @@ DATA_NOTE = {
             "N(0,1)/sqrt(128) bf16 Q and new K/V; lengths uniform 128..2048)",
 }
 POOLS = 3
-SPLIT_KERNEL = "decode_flat_kernel_2w"
-PMC_FILE = os.path.join(ROOT, "profiles", "decode_split_llama8b_b64_pmc.json")
-KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_mapping_amd", "csrc", "decode_kernels.h")
+SPLIT_KERNEL = "decode_flat_kernel"     # the split phase's kernels (1- and 2-wave forms)
+MERGE_KERNEL = "decode_merge_kernel"
 
 
 def parse():
@@ -67,29 +67,11 @@ def parse():
     p.add_argument("--lead", type=int, default=-1, help="balanced scheme: full-share workers (tuning)")
     p.add_argument("--trail-pct", type=int, default=0, help="balanced scheme: other share %% (tuning)")
     p.add_argument("--heads-per-item", type=int, default=0, help="balanced scheme: query heads per item")
-    p.add_argument("--summarize-profiles", default="",
-                   help="write profiles/ summaries from rocprofv3 output under this folder")
+    p.add_argument("--no-prefill-part", action="store_true",
+                   help="hybrid: skip the leg that times the prefill requests in calls of their own")
     p.add_argument("--calibration-copy", action="store_true",
                    help="also run a plain 1 GiB device copy (scale reference for HBM counters)")
     return p.parse_args()
-
-
-def source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
-
-
-def traffic_from_profile():
-    """HBM bytes per split-kernel launch from committed rocprofv3 counters,
-    or None when absent or taken on a different kernel source."""
-    try:
-        with open(PMC_FILE) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if rec.get("kernel_source_sha256_16") != source_hash():
-        return None
-    return rec.get("hbm_bytes_per_launch")
 
 
 def algorithmic_bytes(w):
@@ -171,66 +153,6 @@ def cpu_baseline(w, sample_seqs, min_seconds=10.0):
                 sample="%d of %d sequences of one step (%d tokens of context), %d repeats, %.1f s"
                        % (sample_seqs, w.num_reqs, int(sub.seq_lens.sum()), reps, dt),
                 seconds=round(dt, 2), bytes=ab)
-
-
-PROFILE_CMDS = {
-    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_decode -o run "
-             "-- python bench.py --no-cpu-baseline --steps 200",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o p "
-             "-- python bench.py --no-cpu-baseline --steps 20 --warmup 2 --calibration-copy",
-    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o p "
-             "-- python bench.py --no-cpu-baseline --steps 20 --warmup 2 --calibration-copy",
-}
-CALIBRATION_BYTES = 3 * (1 << 30)   # three 1 GiB copies under --calibration-copy
-
-
-def _find(d, suffix):
-    for root, _, files in os.walk(d):
-        for f in files:
-            if f.endswith(suffix):
-                return os.path.join(root, f)
-    raise FileNotFoundError("%s under %s" % (suffix, d))
-
-
-def summarize_profiles(out_dir):
-    """Turn the rocprofv3 outputs of PROFILE_CMDS (under out_dir) into the
-    short summaries kept in profiles/ (run on the host after the GPU run)."""
-    import csv
-    prof = os.path.join(ROOT, "profiles")
-    os.makedirs(prof, exist_ok=True)
-    stats = list(csv.DictReader(open(_find(os.path.join(out_dir, "prof_decode"), "kernel_stats.csv"))))
-    lines = ["rocprofv3 kernel trace of the Llama-3-8B-shaped decode step (bench.py)",
-             "command: " + PROFILE_CMDS["trace"], "",
-             "%-70s %7s %12s %10s" % ("kernel", "calls", "avg us", "share %")]
-    for r in stats:
-        name = r["Name"].split("(")[0][:70]
-        lines.append("%-70s %7s %12.2f %10.2f" % (name, r["Calls"], float(r["AverageNs"]) / 1e3,
-                                                   float(r["Percentage"])))
-    with open(os.path.join(prof, "decode_llama8b_b64_kernel_trace.txt"), "w") as f:
-        f.write("\n".join(lines) + "\n")
-
-    def counters(sub, name):
-        rows = list(csv.DictReader(open(_find(os.path.join(out_dir, sub), "counter_collection.csv"))))
-        split = [float(r["Counter_Value"]) for r in rows
-                 if SPLIT_KERNEL in r["Kernel_Name"] and r["Counter_Name"] == name]
-        copy = [float(r["Counter_Value"]) for r in rows
-                if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == name]
-        return float(np.mean(split)), len(split), float(np.mean(copy)), len(copy)
-
-    fetch, nf, fcopy, ncf = counters("pmc_fetch", "FETCH_SIZE")
-    write, nw, wcopy, ncw = counters("pmc_write", "WRITE_SIZE")
-    f_fetch = (CALIBRATION_BYTES / ncf) / (fcopy * 1024.0)   # known bytes per copy dispatch
-    f_write = (CALIBRATION_BYTES / ncw) / (wcopy * 1024.0)
-    hbm = fetch * 1024.0 * f_fetch + write * 1024.0 * f_write
-    rec = dict(kernel=SPLIT_KERNEL, kernel_source_sha256_16=source_hash(),
-               fetch_kib_per_launch=fetch, write_kib_per_launch=write, launches=[nf, nw],
-               calibration=dict(copy_dispatch_bytes=[CALIBRATION_BYTES / ncf, CALIBRATION_BYTES / ncw],
-                                fetch_kib=fcopy, write_kib=wcopy, fetch_factor=f_fetch,
-                                write_factor=f_write),
-               hbm_bytes_per_launch=int(hbm), commands=[PROFILE_CMDS["fetch"], PROFILE_CMDS["write"]])
-    with open(PMC_FILE, "w") as f:
-        json.dump(rec, f, indent=1)
-    return rec
 
 
 def stream_probe(w, pools, dev, steps):
@@ -359,6 +281,18 @@ def layer_pools(w, base, dev, layers):
                    "allocation_s": round(alloc_s, 3)}
 
 
+def calibration_copy(dev):
+    """Three plain 1 GiB device-to-device copies: the known-size reference
+    that turns HBM counter values of the same run into bytes."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def hybrid_layer_bytes(w, W):
     """Algorithmic bytes of one hybrid layer's attention: every request reads
     the keys its queries can see once (K and V), plus q and out."""
@@ -425,6 +359,8 @@ def bench_spec(args, dev):
     attn_bytes = kv + qo
     step_bytes = attn_bytes + T * w.num_kv_heads * w.head_dim * 2 * 2 * 2 + T * 8
     gbps = attn_bytes / (ms_attn * 1e-3) / 1e9
+    if args.calibration_copy:
+        calibration_copy(dev)
     res = {
         "metric": "paged decode attention HBM GB/s (% of peak) + KV cache writes tokens/s, 1 GPU",
         "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
@@ -437,7 +373,9 @@ def bench_spec(args, dev):
                    "context_tokens": int(w.seq_lens.sum()), "parallelism": "none (1 GPU)"},
         "attention": {"us": round(ms_attn * 1e3, 2), "GBps": round(gbps, 1), "kv_bytes": kv},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": bench_profiles.traffic(bench_profiles.WORKLOAD_SET["spec"],
+                                                       [SPLIT_KERNEL, MERGE_KERNEL]),
                      "kernel": "chunked attention (multi-token decode items + merge)"},
     }
     print(json.dumps(res), flush=True)
@@ -512,7 +450,9 @@ def bench_hybrid(args, dev):
     pre_t = torch.from_numpy(pre.astype(np.int64)).to(dev)
     pre_mql = int(ql_h[pre].max())
     prefill_ms = {}
-    for name in layers:
+    # (--no-prefill-part skips this leg: a kernel trace then holds only the
+    # whole-layer calls)
+    for name in ([] if args.no_prefill_part else layers):
         g = group_of[name]
         pq = inputs[name][0].index_select(0, pre_tok_t).contiguous()
         ptab = tables[g].index_select(0, pre_t).contiguous()
@@ -544,16 +484,19 @@ def bench_hybrid(args, dev):
         rd, wr, fl = hybrid_layer_bytes(w, W)
         step_bytes += rd + wr
         total_flops += fl
-        prefill_total_ms += prefill_ms[name]
-        pt = fl / (prefill_ms[name] * 1e-3) / 1e12
         layer_rec[name] = {"window": W, "us": round(per_layer[name] * 1e3, 1),
                            "GBps": round((rd + wr) / (per_layer[name] * 1e-3) / 1e9, 1),
-                           "prefill_gflop": round(fl / 1e9, 2),
-                           "prefill_alone_us": round(prefill_ms[name] * 1e3, 1),
-                           "prefill_TFLOPs": round(pt, 1),
-                           "prefill_mfma_frac": round(pt / MFMA_BF16_PEAK_TFLOPS, 4)}
-    prefill_tflops = total_flops / (prefill_total_ms * 1e-3) / 1e12
+                           "prefill_gflop": round(fl / 1e9, 2)}
+        if name in prefill_ms:
+            prefill_total_ms += prefill_ms[name]
+            pt = fl / (prefill_ms[name] * 1e-3) / 1e12
+            layer_rec[name].update({"prefill_alone_us": round(prefill_ms[name] * 1e3, 1),
+                                    "prefill_TFLOPs": round(pt, 1),
+                                    "prefill_mfma_frac": round(pt / MFMA_BF16_PEAK_TFLOPS, 4)})
+    prefill_tflops = total_flops / (prefill_total_ms * 1e-3) / 1e12 if prefill_ms else None
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    if args.calibration_copy:
+        calibration_copy(dev)
     dom = max(layers, key=lambda n: per_layer[n])
     rd, wr, _ = hybrid_layer_bytes(w, w.windows[group_of[dom]])
     gbps = (rd + wr) / (per_layer[dom] * 1e-3) / 1e9
@@ -569,11 +512,12 @@ def bench_hybrid(args, dev):
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "layers": layer_rec,
         "prefill_gflop_per_step": round(total_flops / 1e9, 1),
-        "prefill_part": {"requests": int(len(pre)), "query_tokens": int(len(pre_tok)),
-                         "us_per_step": round(prefill_total_ms * 1e3, 1),
-                         "TFLOPs": round(prefill_tflops, 1), "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
-                         "mfma_frac": round(prefill_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "flops": "4 D per visible (query token, key, query head): scores and P.V"},
+        **({"prefill_part": {"requests": int(len(pre)), "query_tokens": int(len(pre_tok)),
+                             "us_per_step": round(prefill_total_ms * 1e3, 1),
+                             "TFLOPs": round(prefill_tflops, 1), "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                             "mfma_frac": round(prefill_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "flops": "4 D per visible (query token, key, query head): scores and P.V"}}
+           if prefill_ms else {}),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "chunked attention of layer %s (all its kernels)" % dom},
@@ -583,9 +527,6 @@ def bench_hybrid(args, dev):
 
 def main():
     args = parse()
-    if args.summarize_profiles:
-        print(json.dumps(summarize_profiles(args.summarize_profiles)))
-        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -732,15 +673,10 @@ def main():
                                                  GBps=round(4096 * blk * 2 * 2 / (ms * 1e-3) / 1e9, 1))
 
     if args.calibration_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(dev)
 
     probe = stream_probe(w, pools, dev, min(args.steps, 100)) if args.workload == "llama8b" else None
-    traffic = traffic_from_profile() if args.workload == "llama8b" else None
+    traffic = bench_profiles.traffic(bench_profiles.WORKLOAD_SET[args.workload], [SPLIT_KERNEL])
     res = {
         "metric": "paged decode attention HBM GB/s (% of peak) + KV cache writes tokens/s, 1 GPU",
         "value": round(value, 1),
