@@ -121,7 +121,8 @@ PKV_API const char* pkv_status_string(int status);
  * KV bytes one token occupies across `num_layers` layers:
  * num_layers * num_kv_heads * head_dim * 2 (K and V) * element bytes
  * [W-zh § KV Cache技术背景, the 80-layer / 8-head / 128-dim example].
- * Host-only arithmetic.  Returns -1 for a bad dtype or negative sizes.
+ * Host-only arithmetic.  Returns -1 for a bad dtype, negative sizes, or a
+ * result past int64.
  */
 PKV_API int64_t pkv_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads,
                                int32_t head_dim, int32_t dtype);
@@ -135,7 +136,8 @@ PKV_API int64_t pkv_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_heads,
  * Hybrid Attention Mechanisms), so num_tensors takes their count.
  * One block = block_size * num_kv_heads * head_dim * 2 (K and V) * element
  * bytes.  budget = floor(total_bytes * utilization) (double arithmetic).
- * Host-only.  Returns the count (0 when the budget leaves no KV bytes), or
+ * Host-only.  Returns the count (0 when the budget leaves no KV bytes, or
+ * when one block's bytes are past int64), or
  * PKV_ERR_DTYPE / PKV_ERR_SHAPE (utilization outside (0, 1], sizes <= 0,
  * negative byte counts).
  */

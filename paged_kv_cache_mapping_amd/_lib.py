@@ -6,7 +6,10 @@ Loading fails loudly: there is no fallback path when the library is missing.
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+# PKV_LIBRARY names another build of the library to load instead of the
+# in-tree one (the host-sanitizer build of the CPU tests).
+LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                          "libpagedkv.so")
 
 # pkv_status
 PKV_OK = 0

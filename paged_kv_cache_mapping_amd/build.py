@@ -79,6 +79,57 @@ def build(verbose=True, jobs=None):
     return LIB
 
 
+# Host-side sanitizer build (AddressSanitizer + UndefinedBehaviorSanitizer)
+# for the CPU tests of argument checks, plans and sizing: the flags reach
+# the host compilation only; the device code is built as usual.
+SANITIZE_DIR = os.path.join(BUILD, "host_sanitize")
+SANITIZE_LIB = os.path.join(SANITIZE_DIR, "libpagedkv.so")
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined"]
+CLANG = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "llvm", "bin", "clang++")
+
+
+def _compile_host_sanitized(src):
+    obj = os.path.join(SANITIZE_DIR, os.path.basename(src)[:-4] + ".o")
+    cmd = ([HIPCC] + COMMON_FLAGS + ["-Xarch_host", "-O1", "-Xarch_host", "-g", "-Xarch_host",
+                                     "-fno-omit-frame-pointer"]
+           + SANITIZE_FLAGS + ["-c", src, "-o", obj])
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed on %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
+    return obj
+
+
+def sanitizer_runtime():
+    """The shared AddressSanitizer runtime the sanitized library needs
+    preloaded into the Python process."""
+    r = subprocess.run([CLANG, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                       text=True, check=True)
+    return r.stdout.strip()
+
+
+def build_host_sanitized(jobs=None):
+    """Build SANITIZE_LIB unless it is newer than every source; returns its
+    path."""
+    os.makedirs(SANITIZE_DIR, exist_ok=True)
+    srcs = sources()
+    deps = srcs + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
+    deps += [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE)] + [os.path.abspath(__file__)]
+    if os.path.exists(SANITIZE_LIB) and os.path.getmtime(SANITIZE_LIB) > max(map(os.path.getmtime, deps)):
+        return SANITIZE_LIB
+    jobs = jobs or max(1, min(8, os.cpu_count() or 1))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile_host_sanitized, srcs))
+    tmp = SANITIZE_LIB + ".tmp"
+    cmd = ([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-shared-libsan"] + SANITIZE_FLAGS
+           + ["-o", tmp] + objs)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
+    os.replace(tmp, SANITIZE_LIB)
+    return SANITIZE_LIB
+
+
 if __name__ == "__main__":
     build()
     sys.exit(0)

@@ -46,7 +46,10 @@ extern "C" int64_t pkv_kv_bytes_per_token(int32_t num_layers, int32_t num_kv_hea
                                           int32_t head_dim, int32_t dtype) {
   const int bits = pkv::dtype_bits(dtype);
   if (bits == 0 || num_layers < 0 || num_kv_heads < 0 || head_dim < 0) return -1;
-  return (int64_t)num_layers * num_kv_heads * head_dim * 2 * bits / 8;
+  int64_t bits_total;   // layers * heads * dim * 2 * bits, -1 past int64
+  if (__builtin_mul_overflow((int64_t)num_layers * num_kv_heads, (int64_t)head_dim * 2 * bits, &bits_total))
+    return -1;
+  return bits_total / 8;
 }
 
 // Blocks a memory budget holds: floor(total * utilisation) - non-KV bytes,
@@ -60,9 +63,15 @@ extern "C" int64_t pkv_num_blocks_for_budget(int64_t total_bytes, double utiliza
   if (total_bytes < 0 || non_kv_bytes < 0 || num_tensors <= 0 || block_size <= 0 ||
       num_kv_heads <= 0 || head_dim <= 0 || !(utilization > 0.0 && utilization <= 1.0))
     return PKV_ERR_SHAPE;
-  const int64_t budget = (int64_t)((double)total_bytes * utilization);
+  // floor(total * utilization) <= total <= INT64_MAX, but the product is
+  // rounded to a double first and 2^63 itself does not convert
+  const double b = (double)total_bytes * utilization;
+  const int64_t budget = b >= 0x1p63 ? INT64_MAX : (int64_t)b;
   const int64_t available = budget - non_kv_bytes;
   if (available <= 0) return 0;
-  const int64_t per_block = (int64_t)block_size * num_kv_heads * head_dim * 2 * bits / 8 * num_tensors;
+  int64_t block_bits, per_block;
+  if (__builtin_mul_overflow((int64_t)block_size * num_kv_heads, (int64_t)head_dim * 2 * bits, &block_bits) ||
+      __builtin_mul_overflow(block_bits / 8, (int64_t)num_tensors, &per_block))
+    return 0;   // one block is larger than any budget
   return available / per_block;
 }

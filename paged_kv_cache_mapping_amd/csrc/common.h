@@ -135,7 +135,10 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 // ---------------------------------------------------------------- misc
-__host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+// b > 0; a + b - 1 is never formed for a > 0, so no int overflow near INT_MAX
+__host__ __device__ __forceinline__ int ceil_div(int a, int b) {
+  return a > 0 ? (a - 1) / b + 1 : (a + b - 1) / b;
+}
 
 // Bits per element of a cache type (compile-time use in the kernels).
 __host__ __device__ constexpr int kv_bits(int dt) {

@@ -23,8 +23,8 @@ static int log2_int(int x) {
 static int max_visible_blocks(int max_seq_len, int bs, int window, int extra) {
   const int full = ceil_div(max_seq_len > 0 ? max_seq_len : 1, bs);
   if (window <= 0) return full;
-  const int win = ceil_div(window + extra + bs - 1, bs);
-  return full < win ? full : win;
+  const long long win = ((long long)window + extra + bs - 1 + bs - 1) / bs;   // no int overflow
+  return full < win ? full : (int)win;
 }
 
 // Query heads one vector-ALU work item handles.
