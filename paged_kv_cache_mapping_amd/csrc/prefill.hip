@@ -42,6 +42,7 @@ namespace pkv {
 namespace {
 
 typedef __bf16 pf_bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 pf_bf16x2 __attribute__((ext_vector_type(2)));
 typedef float pf_f32x4 __attribute__((ext_vector_type(4)));
 typedef short pf_i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) pf_i16x4 lds_i16x4;
@@ -485,29 +486,36 @@ __device__ __forceinline__ void pf_piece(const PrefillArgs& a, char* lds, const 
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[nb][mb] *= alpha;
       }
+      // a row with no visible key so far keeps m = -inf: subtract 0 instead,
+      // so that masked scores (-inf) give exp2(-inf) = 0 without a select
+      const float msub = m[nb] == -INFINITY ? 0.f : m[nb];
       float p[2][4];
       float ps = 0.f;
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(z[kh][i] - m[nb]);
-          p[kh][i] = z[kh][i] == -INFINITY ? 0.f : e;
+          p[kh][i] = __builtin_amdgcn_exp2f(z[kh][i] - msub);
           ps += p[kh][i];
         }
       lsum[nb] += ps;
       // k slots 8 (l / 16) + i: keys 4 (l / 16) + i, then 16 + 4 (l / 16) + i.
-      // P goes in as two bf16 terms (high part and the rest), so that the
-      // product keeps about 16 bits of each probability.
-      __bf16 hi[8], lo[8];
+      // P goes in as two bf16 terms, so that the product keeps about 16 bits
+      // of each probability: the high half of the binary32 bits (exact), and
+      // the remainder x - high (exact in binary32) rounded to bf16.
+      uint32_t hw[4], lw[4];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float x = p[k / 4][k % 4];
-        hi[k] = (__bf16)x;
-        lo[k] = (__bf16)(x - (float)hi[k]);
+      for (int k = 0; k < 4; ++k) {
+        const float x0 = p[(2 * k) / 4][(2 * k) % 4], x1 = p[(2 * k + 1) / 4][(2 * k + 1) % 4];
+        const uint32_t u0 = __float_as_uint(x0), u1 = __float_as_uint(x1);
+        hw[k] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);   // high halves of x0 (low), x1 (high)
+        const float r0 = x0 - __uint_as_float(u0 & 0xFFFF0000u);
+        const float r1 = x1 - __uint_as_float(u1 & 0xFFFF0000u);
+        const pf_bf16x2 rb = {(__bf16)r0, (__bf16)r1};                 // nearest even
+        lw[k] = __builtin_bit_cast(uint32_t, rb);
       }
-      pb[nb] = pf_bf16x8{hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7]};
-      pl[nb] = pf_bf16x8{lo[0], lo[1], lo[2], lo[3], lo[4], lo[5], lo[6], lo[7]};
+      pb[nb] = __builtin_bit_cast(pf_bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      pl[nb] = __builtin_bit_cast(pf_bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
     }
 
     // O^T += V^T P^T: A = V^T from the tile by transpose reads.  Lane s of a
@@ -515,19 +523,25 @@ __device__ __forceinline__ void pf_piece(const PrefillArgs& a, char* lds, const 
     // then holds V[k0 + i][d0 + j], i = 0..3.
     const int vrow = 4 * grp + (ln16 >> 2);
     const int vcol = 4 * (ln16 & 3);
+    // every V^T operand is read before the products, so the LDS latency is
+    // paid once per tile rather than once per 16 dims
+    pf_bf16x8 av[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const char* v1 = vt_l + vrow * RSV + (16 * mb + vcol) * 2;
       const char* v2 = v1 + 16 * RSV;
       const pf_i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v1));
       const pf_i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v2));
-      const pf_bf16x8 av = __builtin_bit_cast(
+      av[mb] = __builtin_bit_cast(
           pf_bf16x8, (short __attribute__((ext_vector_type(8)))){lo4[0], lo4[1], lo4[2], lo4[3],
                                                                   hi4[0], hi4[1], hi4[2], hi4[3]});
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) {
-        acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[nb], acc[nb][mb], 0, 0, 0);
-        acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pl[nb], acc[nb][mb], 0, 0, 0);
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mb], pb[nb], acc[nb][mb], 0, 0, 0);
+        acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mb], pl[nb], acc[nb][mb], 0, 0, 0);
       }
     }
   };
