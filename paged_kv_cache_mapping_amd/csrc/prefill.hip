@@ -10,11 +10,14 @@
 // window keeps the most recent W positions ("Deep Dive into vLLM Worker-Side
 // GPU KV Cache Initialization", "Hybrid Attention Mechanisms").
 //
-// Decomposition (MI355X): one workgroup of eight waves per (request, KV head,
-// tile of query tokens).  A wave owns NBW blocks of 16 rows; a row is one
-// (query token, query head of the group).  Keys stream through LDS in tiles
-// of 32 (K and V double-buffered, staged by the whole workgroup from the
-// block table slice in LDS).  Per tile and 16-row block:
+// Decomposition (MI355X): one persistent workgroup of eight waves per
+// compute unit.  The work is cut into units of 32 keys of an item (request,
+// KV head, tile of query tokens), and workgroup w takes a contiguous,
+// balanced share of the units; a share that ends inside an item leaves its
+// state in a slot for the merge kernel.  A wave owns NBW blocks of 16 rows;
+// a row is one (query token, query head of the group).  Keys stream through
+// LDS in tiles of 32 (K and V double-buffered, staged by the whole
+// workgroup from the block table slice in LDS).  Per tile and 16-row block:
 //   S^T = K Q^T   on v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = Q
 //                 rows kept in registers): lane l holds keys 4(l/16)+i of
 //                 row l%16, so each row's softmax state lives in one lane
@@ -805,7 +808,9 @@ int pf_max_blocks(int max_seq_len, int bs, int window, int tokens) {
 bool prefill_supported(int kv_dtype, int head_dim, int group, int max_seq_len, int block_size,
                        int window, int max_query_len) {
   if (kv_dtype != PKV_BF16 && kv_dtype != PKV_FP8_E4M3 && kv_dtype != PKV_INT4) return false;
-  if (head_dim != 64 && head_dim != 128) return false;   // 256: tiles exceed 64 KiB of LDS
+  // 256: the accumulators and query rows of two row blocks alone would take
+  // 192 of a wave's 256 registers
+  if (head_dim != 64 && head_dim != 128) return false;
   if (kv_dtype == PKV_INT4 && head_dim != 128) return false;   // the INT4 head size built
   if (group < 1 || group > 16 || 16 % group) return false;
   if (max_query_len < 2) return false;
