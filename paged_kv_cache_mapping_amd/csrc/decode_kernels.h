@@ -1581,25 +1581,38 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
         }
       }
       float pv[4];
-      uint32_t phi[4], plo[4];   // matrix-core P.V: bf16 high part and remainder
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float p = __builtin_amdgcn_exp2f(z[i] - m1);
         if constexpr (!full) p = z[i] == -INFINITY ? 0.f : p;
-        if constexpr (kMPV) {
-          phi[i] = f32_to_bf16_rne(p);
-          plo[i] = f32_to_bf16_rne(p - as_float(phi[i] << 16));
+        pv[i] = p;
+      }
+      // matrix-core P.V: each weight as a bf16 high part and the bf16
+      // remainder, both rounded to nearest even by the hardware conversion
+      // (pairs of weights per instruction, no branches)
+      uint32_t phw[2], plw[2];
+      if constexpr (kMPV) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const bf16x2_t h = {(__bf16)pv[2 * j], (__bf16)pv[2 * j + 1]};
+          phw[j] = __builtin_bit_cast(uint32_t, h);
+          const bf16x2_t l = {(__bf16)(pv[2 * j] - as_float(phw[j] << 16)),
+                              (__bf16)(pv[2 * j + 1] - as_float(phw[j] & 0xFFFF0000u))};
+          plw[j] = __builtin_bit_cast(uint32_t, l);
           // INT4 values enter with an offset that the flush takes off as a
           // multiple of the weight sum: the sum takes the weights the
           // products use
-          if constexpr (kI4) p = as_float(phi[i] << 16) + as_float(plo[i] << 16);
+          if constexpr (kI4) {
+            pv[2 * j] = as_float(phw[j] << 16) + as_float(plw[j] << 16);
+            pv[2 * j + 1] = as_float(phw[j] & 0xFFFF0000u) + as_float(plw[j] & 0xFFFF0000u);
+          }
         }
-        pv[i] = p;
-        ls1 += p;
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ls1 += pv[i];
       if constexpr (kMPV) {
-        const s16x4_t pa_hi = __builtin_bit_cast(s16x4_t, make_uint2(phi[0] | (phi[1] << 16), phi[2] | (phi[3] << 16)));
-        const s16x4_t pa_lo = __builtin_bit_cast(s16x4_t, make_uint2(plo[0] | (plo[1] << 16), plo[2] | (plo[3] << 16)));
+        const s16x4_t pa_hi = __builtin_bit_cast(s16x4_t, make_uint2(phw[0], phw[1]));
+        const s16x4_t pa_lo = __builtin_bit_cast(s16x4_t, make_uint2(plw[0], plw[1]));
         const s16x4_t zero4 = {0, 0, 0, 0};
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh) {
