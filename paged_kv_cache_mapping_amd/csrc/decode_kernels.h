@@ -971,14 +971,21 @@ __host__ __device__ inline FlatLds flat_lds_layout(int rows, int gt, int d, int 
 
 // Contiguous shares of the unit range [0, U): workers w < lead take p_lead
 // units each, the others p_trail (both at least min_units).  With lead equal
-// to the worker count every share is equal.  range_of(u) numbers the shares.
+// to the worker count every share is equal.  range_of(u) numbers the shares;
+// below 2^31 units (narrow) it divides in 32 bits, a few instructions
+// instead of the long software sequence of a 64-bit division.
 struct Shares {
   long long p_lead, p_trail, lead_end;
   int lead;
+  bool narrow;
   __device__ __forceinline__ long long begin(long long w) const {
     return w <= lead ? w * p_lead : lead_end + (w - lead) * p_trail;
   }
   __device__ __forceinline__ long long range_of(long long u) const {
+    if (narrow) {
+      const uint32_t v = (uint32_t)u, le = (uint32_t)lead_end;
+      return v < le ? v / (uint32_t)p_lead : lead + (v - le) / (uint32_t)p_trail;
+    }
     return u < lead_end ? u / p_lead : lead + (u - lead_end) / p_trail;
   }
 };
@@ -998,6 +1005,7 @@ __device__ __forceinline__ Shares make_shares(long long U, int W, int lead, int 
   const long long rest = U - s.lead_end;
   s.p_trail = (s.lead < W && rest > 0) ? (rest + (W - s.lead) - 1) / (W - s.lead) : 1;
   if (s.p_trail < min_units) s.p_trail = min_units;
+  s.narrow = U < (1LL << 31);
   return s;
 }
 
@@ -1357,7 +1365,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
       const int b = lo;
       const int nv = cum[b + 1] - cum[b];
       const long long rel = u - (long long)cum[b] * kvgroups;
-      const int kvg = (int)(rel / nv);
+      const int kvg = sh.narrow ? (int)((uint32_t)rel / (uint32_t)nv) : (int)(rel / nv);
       const int j = (int)(rel - (long long)kvg * nv);
       int req, tok, klo, khi;
       if (have_rec) {
