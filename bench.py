@@ -60,6 +60,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--split-blocks", type=int, default=0, help="override the decode split (tuning)")
+    p.add_argument("--decode-step", action="store_true",
+                   help="time the step as one pkv_paged_attention_decode_step call (write in its merge)")
     p.add_argument("--shared-blocks", action="store_true",
                    help="plan as if blocks could be shared (no PKV_PLAN_BLOCKS_NOT_SHARED); "
                         "the prefix workload always is")
@@ -105,17 +107,23 @@ def decode_plan_for(pkv, w, cache, shared_blocks=False, **tune):
     return plan
 
 
-def decode_step_fn(pkv, w, base, plan, ws, out, slots):
+def decode_step_fn(pkv, w, base, plan, ws, out, slots, one_call=False):
     """One timed decode step over a (cache view, block table) pair: slot
     mapping and the write of the step's K/V rows in one launch, then the
-    decode attention's two phases."""
+    decode attention's two phases; or with one_call (balanced plans) the
+    decode step call, whose split attends to the cached keys and whose merge
+    adds the step's own token and writes its K/V and slot."""
     def step(cache, bt):
+        pkv.paged_attention_decode_step(base.q, base.new_k, base.new_v, cache, bt, base.seq_lens,
+                                        w.max_seq_len, w.scale, plan, ws, out, slots=slots)
+
+    def step3(cache, bt):
         pkv.slot_mapping_cache_write(bt, base.query_start_loc, base.num_computed, base.new_k,
                                      base.new_v, cache, out=slots)
         pkv.paged_attention_decode_partials(base.q, cache, bt, base.seq_lens, w.max_seq_len, w.scale,
                                             plan, ws, out)
         pkv.paged_attention_decode_combine(out, base.seq_lens, w.block_size, plan, ws)
-    return step
+    return step if one_call and plan.scheme == 1 else step3
 
 
 def cpu_baseline(w, sample_seqs, min_seconds=10.0):
@@ -561,7 +569,7 @@ def main():
     ws = pkv.new_workspace(plan.workspace_bytes, dev)
     out = torch.empty_like(base.q)
     slots = torch.empty(w.num_reqs, dtype=torch.int64, device=dev)
-    run_step = decode_step_fn(pkv, w, base, plan, ws, out, slots)
+    run_step = decode_step_fn(pkv, w, base, plan, ws, out, slots, one_call=args.decode_step)
 
     def step(i):
         run_step(*pools[i % npools])
@@ -698,6 +706,8 @@ def main():
                    "split_blocks": int(plan.split_blocks), "max_splits": int(plan.max_splits),
                    "lead_workers": int(plan.lead_workers), "trail_share_pct": int(plan.trail_share_pct),
                    "plan_flags": int(plan.flags),
+                   "step_calls": ("decode_step" if args.decode_step and plan.scheme == 1
+                                  else "slot_mapping_cache_write + decode_partials + decode_combine"),
                    **extra},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_attention": {"split_kernel_us": round(split_ms * 1e3, 2),

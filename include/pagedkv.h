@@ -419,6 +419,43 @@ PKV_API int pkv_paged_attention_decode_combine(void* out, int32_t out_dtype,
                                        hipStream_t stream);
 
 /*
+ * One decode step in two launches: the step's new K/V rows written to their
+ * slots and every sequence's attention over its cache and that token
+ * [W § Pinpointing the Token Slot and § Summary (write through the slot
+ * mapping); P § Handling Softmax Across Blocks].  Sequence r's new token
+ * sits at position seq_lens[r] - 1; its slot is
+ * block_table[r][(seq_lens[r] - 1) / block_size] * block_size +
+ * (seq_lens[r] - 1) % block_size.  The split pass attends to the cached
+ * keys before that position; the merge adds the new token's term (its key
+ * and value taken through the cache's format as the write stores them: fp8
+ * and INT4 encoded with the inverse scales), writes its K/V codes to the
+ * slot and the slot to slot_mapping.
+ * Equivalent to pkv_slot_mapping_cache_write (query_start_loc 0..num_seqs,
+ * num_computed = seq_lens - 1) followed by pkv_paged_attention_decode_partials
+ * and _combine with the same plan: the same cache bytes and slots, and
+ * outputs within the attention bounds of each other (the new token joins the
+ * softmax in another order, so bits may differ).
+ *   new_k, new_v  [num_seqs, Hkv, D] bf16, 16-byte aligned.
+ *   slot_mapping  [num_seqs] int64 out, or NULL: -1 for a sequence whose new
+ *                 token has no mapped block (its K/V are not written and its
+ *                 output is NaN) or whose seq_len is out of range (NaN
+ *                 output, nothing written).
+ *   plan          a balanced plan (scheme 1) from pkv_decode_plan_make for
+ *                 these sizes; others return PKV_ERR_UNSUPPORTED.
+ * bf16, fp8 and INT4 caches (f32: PKV_ERR_DTYPE); q and out bf16.
+ */
+PKV_API int pkv_paged_attention_decode_step(void* out, const void* q, int32_t q_dtype,
+                                    const void* new_k, const void* new_v,
+                                    int32_t num_seqs, int32_t num_q_heads,
+                                    const pkv_cache* cache,
+                                    const int32_t* block_table, int32_t bt_stride,
+                                    const int32_t* seq_lens, int32_t max_seq_len,
+                                    float softmax_scale, int32_t sliding_window,
+                                    const pkv_decode_plan* plan,
+                                    void* workspace, size_t workspace_bytes,
+                                    int64_t* slot_mapping, hipStream_t stream);
+
+/*
  * Workspace bytes pkv_paged_attention_chunked needs for these arguments.
  */
 PKV_API int pkv_chunked_workspace_size(int32_t num_tokens, int32_t num_reqs,

@@ -11,7 +11,7 @@ call does, and fails loudly if it has not been built.
 from .api import (CacheView, cache_write, chunked_workspace_size, copy_blocks, decode_plan,  # noqa: F401
                   fp8_dequantize, fp8_quantize, int4_dequantize, int4_quantize, kv_bytes_per_token,
                   paged_attention_chunked,
-                  paged_attention_decode, paged_attention_decode_combine,
+                  paged_attention_decode, paged_attention_decode_combine, paged_attention_decode_step,
                   paged_attention_decode_partials, slot_mapping, slot_mapping_cache_write, status_string,
                   new_workspace, tune_plan)
 from ._lib import PkvError, load  # noqa: F401

@@ -87,6 +87,9 @@ SIGNATURES = {
     "pkv_paged_attention_decode_partials": (_int, [_vp, _vp, _i32, _i32, _i32, ctypes.POINTER(PkvCache), _vp,
                                                    _i32, _vp, _i32, _f32, _i32, ctypes.POINTER(PkvDecodePlan),
                                                    _vp, _sz, _vp]),
+    "pkv_paged_attention_decode_step": (_int, [_vp, _vp, _i32, _vp, _vp, _i32, _i32, ctypes.POINTER(PkvCache), _vp,
+                                               _i32, _vp, _i32, _f32, _i32, ctypes.POINTER(PkvDecodePlan), _vp,
+                                               _sz, _vp, _vp]),
     "pkv_paged_attention_decode_combine": (_int, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _i32,
                                                   ctypes.POINTER(PkvDecodePlan), _vp, _sz, _vp]),
     "pkv_chunked_workspace_size": (_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,

@@ -281,6 +281,24 @@ def paged_attention_decode_combine(out, seq_lens, block_size, plan, workspace, s
         ctypes.byref(plan), _ptr(workspace), wsb, _stream(out.device)))
 
 
+def paged_attention_decode_step(q, new_k, new_v, cache, block_table, seq_lens, max_seq_len,
+                                softmax_scale, plan, workspace, out, slots=None, sliding_window=0):
+    """One decode step (see pagedkv.h): the new K/V rows [B, Hkv, D] bf16 are
+    written at position seq_lens - 1 and attended to with the cache; `slots`
+    (int64 [B], optional) receives their slots."""
+    lib = load()
+    B, Hq, _ = q.shape
+    _need(new_k.is_contiguous() and new_v.is_contiguous() and new_k.dtype == torch.bfloat16
+          and new_v.dtype == torch.bfloat16, "new_k / new_v must be contiguous bf16 [B, Hkv, D]")
+    c = cache.c_struct()
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check("pkv_paged_attention_decode_step", lib.pkv_paged_attention_decode_step(
+        _ptr(out), _ptr(q), _dt(q), _ptr(new_k), _ptr(new_v), B, Hq, ctypes.byref(c), _ptr(block_table),
+        block_table.shape[1], _ptr(seq_lens), max_seq_len, softmax_scale, sliding_window,
+        ctypes.byref(plan), _ptr(workspace), wsb, _ptr(slots) if slots is not None else None,
+        _stream(q.device)))
+
+
 def chunked_workspace_size(num_tokens, num_reqs, num_q_heads, cache, max_query_len, max_seq_len,
                            sliding_window=0):
     lib = load()

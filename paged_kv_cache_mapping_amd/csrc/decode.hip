@@ -418,6 +418,37 @@ extern "C" int pkv_paged_attention_decode_partials(
   return run_split(a, *plan, cache->dtype, stream);
 }
 
+extern "C" int pkv_paged_attention_decode_step(
+    void* out, const void* q, int32_t q_dtype, const void* new_k, const void* new_v, int32_t num_seqs,
+    int32_t num_q_heads, const pkv_cache* cache, const int32_t* block_table, int32_t bt_stride,
+    const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale, int32_t sliding_window,
+    const pkv_decode_plan* plan, void* workspace, size_t workspace_bytes, int64_t* slot_mapping,
+    hipStream_t stream) {
+  DecodeArgs a;
+  int st = prepare(a, out, q, q_dtype, num_seqs, num_q_heads, cache, block_table, bt_stride,
+                   seq_lens, max_seq_len, softmax_scale, sliding_window, 0, nullptr, 0, 0, 1, plan,
+                   workspace, workspace_bytes);
+  if (st != PKV_OK) return st;
+  if (plan->scheme != 1) return PKV_ERR_UNSUPPORTED;
+  if (cache->dtype == PKV_F32) return PKV_ERR_DTYPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!new_k || !new_v) return PKV_ERR_NULL;
+  if (!workspace) return PKV_ERR_WORKSPACE;
+  a.new_token = 1;
+  a.new_k = new_k;
+  a.new_v = new_v;
+  a.slots_out = slot_mapping;
+  a.kv_dtype = cache->dtype;
+  a.kv_heads = cache->num_kv_heads;
+  a.inv_k_scale = 1.0f / cache->k_scale;
+  a.inv_v_scale = 1.0f / cache->v_scale;
+  st = run_split(a, *plan, cache->dtype, stream);
+  if (st != PKV_OK) return st;
+  st = dispatch_combine(a, PKV_BF16, stream);
+  if (st != PKV_OK) return st;
+  return launch_status();
+}
+
 extern "C" int pkv_paged_attention_decode_combine(void* out, int32_t out_dtype, int32_t num_seqs,
                                                   int32_t num_q_heads, int32_t head_dim,
                                                   int32_t block_size, const int32_t* seq_lens,

@@ -83,6 +83,20 @@ struct DecodeArgs {
   int32_t lds_budget;       // bytes of LDS one worker may take
   int32_t qt;               // row mode 3: query tokens one item holds (else 1)
   int32_t pair;             // INT4: items span two adjacent KV heads (see kInt4Pair)
+  // Decode step with its own token (pkv_paged_attention_decode_step, row
+  // mode 0, balanced partition): the split leaves position seq_len - 1 out
+  // and keeps every piece as a partial; the merge adds that token's term,
+  // its key and value read from new_k / new_v ([rows, Hkv, D] bf16) and
+  // rounded through the cache's format, writes them to the token's slot
+  // and the slot to slots_out.
+  int32_t new_token;
+  const void* new_k;
+  const void* new_v;
+  int64_t* slots_out;
+  int32_t kv_dtype;
+  int32_t kv_heads;         // the cache's KV heads (pair items halve num_kv_heads)
+  float inv_k_scale;
+  float inv_v_scale;
 };
 
 // What one row attends to.
@@ -129,6 +143,19 @@ __device__ __forceinline__ RowInfo row_info(const DecodeArgs& a, int row) {
     L = a.seq_lens[row];
     p = L - 1;
     if (L <= 0 || L > a.max_seq_len) return r;
+    if (a.new_token) {
+      // the cached keys end before the step's own token (the merge adds it);
+      // a row with none of them is valid with no blocks
+      r.hi = p - 1;
+      r.lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
+      r.valid = true;
+      if (r.lo > r.hi) return r;
+      r.first_blk = r.lo >> a.bs_log2;
+      const int last0 = r.hi >> a.bs_log2;
+      if (last0 >= a.bt_stride) { r.valid = false; return r; }
+      r.nvis = last0 - r.first_blk + 1;
+      return r;
+    }
   } else if (a.row_mode == 2) {
     const int t0 = a.qsl[row];
     if (a.qsl[row + 1] - t0 != 1 || t0 < 0 || t0 >= a.num_tokens) { r.skip = true; return r; }
@@ -1210,6 +1237,9 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
     const long long r0 = sh.range_of(seg_base);
     const int piece = (int)(sh.range_of(s_first) - r0);
     const int npieces = (int)(sh.range_of(seg_base + nv - 1) - r0 + 1);
+    // a piece that is its whole row writes the output, unless the merge still
+    // adds the step's own token
+    const bool whole = npieces == 1 && !a.new_token;
     if (s_bad) {
 #pragma unroll
       for (int h = 0; h < GT; ++h) m[h] = 0.f;
@@ -1270,7 +1300,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
           if (4 * rr + i < RI && R == rr) lr = lh[(4 * rr + i) % RI];
         // INT4 values entered as 128 + u: the row's values are u - 8
         const float off = kI4 ? -136.0f * lr : 0.0f;
-        if (npieces == 1) {
+        if (whole) {
           if (r / GT >= s_ql) continue;
           const int64_t out_row = ((int64_t)(s_tok + r / GT) * a.num_q_heads + h0 + r % GT) * D;
           const float inv = a.v_scale / lr;
@@ -1290,7 +1320,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
         }
       }
     } else if (vg == 0) {
-      if (npieces == 1) {
+      if (whole) {
         // row r = t * GT + h: query token t of the piece, head h0 + h
 #pragma unroll
         for (int h = 0; h < RI; ++h) {
@@ -1320,7 +1350,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
         }
       }
     }
-    if (npieces > 1) {
+    if (!whole) {
       // m and l of the piece's rows side by side: one record of 2 RI floats
       float* ml = a.ws_m + (((int64_t)b * kvgroups + kvg) * a.max_splits + piece) * (2 * RI);
       constexpr int NV = (2 * RI + 3) / 4;
@@ -1803,13 +1833,25 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
   for (int r = blockIdx.x; r < a.num_rows; r += W) {
     if (cum[r + 1] != cum[r]) continue;       // a row with units: written by its pieces
     const RowInfo ri = row_info(a, r);
+    if (a.new_token && ri.valid) {
+      // no cached key: the merge makes the output from the step's own token
+      for (int g = lane; g < kvgroups; g += kWave) {
+        a.ws_np[2 * ((int64_t)r * kvgroups + g)] = 0;
+        a.ws_np[2 * ((int64_t)r * kvgroups + g) + 1] = ri.tok;
+      }
+      continue;
+    }
     if (ri.valid && !ri.skip) continue;
     if (!ri.skip) {
       const int64_t base = (int64_t)ri.tok * a.num_q_heads * D;
       for (int e = lane; e < ri.ntok * a.num_q_heads * D; e += kWave)
         reinterpret_cast<uint16_t*>(a.out)[base + e] = 0x7FC0;
     }
-    for (int g = lane; g < kvgroups; g += kWave) a.ws_np[2 * ((int64_t)r * kvgroups + g)] = 0;
+    for (int g = lane; g < kvgroups; g += kWave) {
+      a.ws_np[2 * ((int64_t)r * kvgroups + g)] = 0;
+      if (a.new_token) a.ws_np[2 * ((int64_t)r * kvgroups + g) + 1] = -1;   // the merge leaves it
+    }
+    if (a.new_token && a.slots_out && lane == 0) a.slots_out[r] = -1;    // nothing written
   }
 }
 
@@ -1838,7 +1880,97 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 // by several waves (more waves in flight, fewer loads per lane).
 __host__ __device__ constexpr int merge_rows_per_wave(int rows) { return rows > 4 ? 4 : rows; }
 
-template <int D, int GT, int OT, int QT = 1>
+// The step's own token (position seq_len - 1 of row b, pkv_paged_attention_
+// decode_step) joining a merge wave's online softmax for its row h (query
+// head `head`): its key and value are the row's new_k / new_v entries taken
+// through the cache's format exactly as the write stores them (bf16 as is;
+// fp8 and INT4 encoded with the inverse scale, their code values then
+// scaled as the cached keys' are).  The lanes of the first query head of
+// each KV head also write the codes to the token's slot, and one lane the
+// slot.  A token whose block the table does not map makes the row NaN and
+// is not written (slot -1): a write through an unmapped slot is skipped and
+// attention over an unmapped block gives NaN.  Every lane of the wave calls
+// this (the dot product is reduced across a row's LPH lanes).
+template <int D, int LPH, int DPL>
+__device__ __forceinline__ void merge_own_token(const DecodeArgs& a, int b, int head, int tok, int d0,
+                                                bool active, int pos, int phys, float& M, float& den,
+                                                float (&num)[DPL]) {
+  const int qpk = a.num_q_heads / a.kv_heads;
+  const int kvh = head / qpk;
+  const bool ok = phys >= 0 && phys < a.num_blocks;
+  const int64_t src = ((int64_t)b * a.kv_heads + kvh) * D + (active ? d0 : 0);
+  const uint16_t* kn = reinterpret_cast<const uint16_t*>(a.new_k) + src;
+  const uint16_t* vn = reinterpret_cast<const uint16_t*>(a.new_v) + src;
+  const uint16_t* qn = reinterpret_cast<const uint16_t*>(a.q) +
+                       ((int64_t)tok * a.num_q_heads + head) * D + (active ? d0 : 0);
+  uint32_t kc[DPL], vc[DPL];      // the cache's codes (bf16 bits for a bf16 cache)
+  float dot = 0.f, vv[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) {
+    const uint32_t kb = active ? kn[i] : 0u, vb = active ? vn[i] : 0u;
+    const float qx = active ? as_float((uint32_t)qn[i] << 16) : 0.f;
+    float kx = as_float(kb << 16), vx = as_float(vb << 16);
+    if (a.kv_dtype == PKV_FP8_E4M3) {
+      kc[i] = e4m3_encode(kx * a.inv_k_scale);
+      vc[i] = e4m3_encode(vx * a.inv_v_scale);
+      kx = e4m3x2_to_f32<false>(kc[i]).x;
+      vx = e4m3x2_to_f32<false>(vc[i]).x;
+    } else if (a.kv_dtype == PKV_INT4) {
+      kc[i] = int4_encode(kx * a.inv_k_scale);
+      vc[i] = int4_encode(vx * a.inv_v_scale);
+      kx = (float)((int)kc[i] - 8);
+      vx = (float)((int)vc[i] - 8);
+    } else {
+      kc[i] = kb;
+      vc[i] = vb;
+    }
+    dot = fmaf(qx, kx, dot);
+    vv[i] = vx * a.v_scale;
+  }
+#pragma unroll
+  for (int o = LPH / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
+  const float s = dot * a.scale_log2;   // an unmapped token's row is set to NaN after its store
+  const float mn = fmaxf(M, s);
+  const float c_old = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mn);
+  const float c_new = __builtin_amdgcn_exp2f(s - mn);
+  den = den * c_old + c_new;
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) num[i] = num[i] * c_old + vv[i] * c_new;
+  M = mn;
+  const int bits = kv_bits(a.kv_dtype);
+  const int in_blk = pos & ((1 << a.bs_log2) - 1);
+  if (ok && active && head % qpk == 0) {
+    const int64_t row_bytes = (int64_t)a.kv_heads * D * bits / 8;
+    const int64_t off = (int64_t)phys * (a.block_stride * bits / 8) + (int64_t)in_blk * row_bytes +
+                        ((int64_t)kvh * D + d0) * bits / 8;
+    uint8_t* kd = reinterpret_cast<uint8_t*>(const_cast<char*>(a.kbase) + off);
+    uint8_t* vd = reinterpret_cast<uint8_t*>(const_cast<char*>(a.vbase) + off);
+    if (bits == 16) {
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) {
+        reinterpret_cast<uint16_t*>(kd)[i] = (uint16_t)kc[i];
+        reinterpret_cast<uint16_t*>(vd)[i] = (uint16_t)vc[i];
+      }
+    } else if (bits == 8) {
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) {
+        kd[i] = (uint8_t)kc[i];
+        vd[i] = (uint8_t)vc[i];
+      }
+    } else {   // two codes per byte, element 2j in the low nibble of byte j
+#pragma unroll
+      for (int i = 0; i < DPL; i += 2) {
+        const uint32_t k1 = i + 1 < DPL ? kc[i + 1] : 0u, v1 = i + 1 < DPL ? vc[i + 1] : 0u;
+        kd[i / 2] = (uint8_t)(kc[i] | (k1 << 4));
+        vd[i / 2] = (uint8_t)(vc[i] | (v1 << 4));
+      }
+    }
+  }
+  if (a.slots_out && head == 0 && d0 == 0)
+    a.slots_out[b] = ok ? ((int64_t)phys << a.bs_log2) + in_blk : -1;
+}
+
+template <int D, int GT, int OT, int QT = 1, bool NT = false>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   constexpr int RI = GT * QT;                       // rows of an item: (token, head)
   constexpr int RW = merge_rows_per_wave(RI);       // rows one wave merges
@@ -1871,9 +2003,17 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   };
   const int np_word = a.ws_np[2 * rg];
   const int tok = a.ws_np[2 * rg + 1];
+  // the step's own token: its position and block, read with the first
+  // round so that the table lookup overlaps it
+  int own_pos = 0, own_phys = -1;
+  if constexpr (NT) {
+    own_pos = a.seq_lens[b] - 1;
+    const int blk = own_pos >> a.bs_log2;
+    if (own_pos >= 0 && blk < a.bt_stride) own_phys = a.bt[(int64_t)b * a.bt_stride + blk];
+  }
   load_round(0, a.max_splits);
   const int np = min(np_word, a.max_splits);
-  if (np <= 1) return;                              // written by the split phase (or rejected)
+  if (!NT && np <= 1) return;                       // written by the split phase (or rejected)
   if (tok < 0 || tok >= a.num_tokens) return;       // not a row this call wrote
   float M = -INFINITY, den = 0.f;
   float num[DPL];
@@ -1893,6 +2033,10 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
       M = mn;
     }
   }
+  if constexpr (NT) {
+    static_assert(QT == 1, "one query token per row");
+    merge_own_token<D, LPH, DPL>(a, b, g * GT + h % GT, tok, d0, active, own_pos, own_phys, M, den, num);
+  }
   if (!active) return;
   // row h = t * GT + head: query token t of the row's request
   const int t = h / GT;
@@ -1903,7 +2047,15 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   float o[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) o[i] = num[i] * inv;
-  store_out<OT, DPL>(a.out, ((int64_t)(tok + t) * a.num_q_heads + g * GT + h % GT) * D + d0, o);
+  const int64_t out_elem = ((int64_t)(tok + t) * a.num_q_heads + g * GT + h % GT) * D + d0;
+  store_out<OT, DPL>(a.out, out_elem, o);
+  if constexpr (NT) {
+    if (!(own_phys >= 0 && own_phys < a.num_blocks)) {   // the token has no slot: NaN row
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) o[i] = __builtin_nanf("");
+      store_out<OT, DPL>(a.out, out_elem, o);
+    }
+  }
 }
 
 // Combine phase of the fixed splits: one wave per (row, query head) with
@@ -2055,6 +2207,12 @@ template <int D, int GT, int QT = 1>
 void launch_merge(const DecodeArgs& a, int ot, hipStream_t s) {
   constexpr int kWaves = GT * QT / merge_rows_per_wave(GT * QT);   // waves per item
   const dim3 grid((unsigned)((long long)a.num_rows * (a.num_q_heads / GT) * kWaves));
+  if constexpr (QT == 1) {
+    if (a.new_token) {   // bf16 output (the step's queries are bf16)
+      decode_merge_kernel<D, GT, PKV_BF16, 1, true><<<grid, 64, 0, s>>>(a);
+      return;
+    }
+  }
   if (ot == PKV_F32) decode_merge_kernel<D, GT, PKV_F32, QT><<<grid, 64, 0, s>>>(a);
   else decode_merge_kernel<D, GT, PKV_BF16, QT><<<grid, 64, 0, s>>>(a);
 }
