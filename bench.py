@@ -340,7 +340,8 @@ def bench_spec(args, dev):
     def attend(i):
         cache, bt = pools[i % len(pools)]
         pkv.paged_attention_chunked(base.q, base.query_start_loc, base.seq_lens, w.max_query_len, cache, bt,
-                                    w.max_seq_len, w.scale, causal=True, out=out, workspace=ws)
+                                    w.max_seq_len, w.scale, causal=True, out=out, workspace=ws,
+                                    blocks_not_shared=True)
 
     def step(i):
         cache, bt = pools[i % len(pools)]
@@ -420,7 +421,7 @@ def bench_hybrid(args, dev):
         pkv.cache_write(nk, nv, slots[g], views[name])
         pkv.paged_attention_chunked(q, qsl, sl, w.max_query_len, views[name], tables[g], w.max_seq_len,
                                     w.scale, causal=True, sliding_window=w.windows[g], out=outs[name],
-                                    workspace=ws[g])
+                                    workspace=ws[g], blocks_not_shared=True)
 
     def step():
         for g in range(len(w.groups)):
@@ -472,7 +473,7 @@ def bench_hybrid(args, dev):
         def prefill_call():
             pkv.paged_attention_chunked(pq, pre_qsl, pre_sl, pre_mql, views[name], ptab, w.max_seq_len,
                                         w.scale, causal=True, sliding_window=w.windows[g], out=pout,
-                                        workspace=pws)
+                                        workspace=pws, blocks_not_shared=True)
         for _ in range(args.warmup):
             prefill_call()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

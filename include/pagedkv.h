@@ -480,6 +480,10 @@ PKV_API int pkv_chunked_workspace_size(int32_t num_tokens, int32_t num_reqs,
  * max_query_len    bounds every q_len_r; max_seq_len bounds every seq_lens[r].
  * causal           1: query at p sees keys <= p.  0: all keys < seq_len.
  * sliding_window   0, or W: keys >= p - W + 1 only.
+ * flags            0 or PKV_PLAN_BLOCKS_NOT_SHARED: the same promise as for
+ *                  decode plans (no physical block read by two requests of
+ *                  the call); the decode rows' bf16 loads then bypass the
+ *                  caches.  Other bits return PKV_ERR_SHAPE.
  * workspace        at least pkv_chunked_workspace_size(...) bytes.
  * Invalid rows (q_len > seq_len, lengths out of range, missing blocks) get NaN.
  * INT4 caches: the decode form's shapes (head_dim 128, at most 4096
@@ -499,8 +503,8 @@ PKV_API int pkv_paged_attention_chunked(void* out, const void* q, int32_t q_dtyp
                                 const int32_t* block_table, int32_t bt_stride,
                                 int32_t max_seq_len, float softmax_scale,
                                 int32_t causal, int32_t sliding_window,
-                                void* workspace, size_t workspace_bytes,
-                                hipStream_t stream);
+                                int32_t flags, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
 
 /*
  * FP8 E4M3 bulk codec with the exact conversions the cache write and the

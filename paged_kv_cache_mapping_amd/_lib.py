@@ -96,7 +96,7 @@ SIGNATURES = {
                                           ctypes.POINTER(_sz)]),
     "pkv_paged_attention_chunked": (_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _i32, _i32,
                                            ctypes.POINTER(PkvCache), _vp, _i32, _i32, _f32, _i32, _i32,
-                                           _vp, _sz, _vp]),
+                                           _i32, _vp, _sz, _vp]),
     "pkv_copy_blocks": (_int, [ctypes.POINTER(PkvCache), _vp, _vp, _i32, _vp, _vp]),
     "pkv_fp8_e4m3_quantize": (_int, [_vp, _i32, _i64, _f32, _vp, _vp]),
     "pkv_fp8_e4m3_dequantize": (_int, [_vp, _i64, _f32, _i32, _vp, _vp]),

@@ -311,8 +311,10 @@ def chunked_workspace_size(num_tokens, num_reqs, num_q_heads, cache, max_query_l
 
 def paged_attention_chunked(q, query_start_loc, seq_lens, max_query_len, cache, block_table,
                             max_seq_len, softmax_scale, causal=True, sliding_window=0,
-                            workspace=None, out=None):
-    """Mixed prefill/decode step: q [T, Hq, D] -> out [T, Hq, D]."""
+                            workspace=None, out=None, blocks_not_shared=False):
+    """Mixed prefill/decode step: q [T, Hq, D] -> out [T, Hq, D];
+    blocks_not_shared passes PKV_PLAN_BLOCKS_NOT_SHARED (no block read by
+    two requests of the call)."""
     lib = load()
     _need(q.dim() == 3 and q.is_contiguous(), "q must be contiguous [T, Hq, D]")
     _i32(query_start_loc, "query_start_loc")
@@ -329,7 +331,8 @@ def paged_attention_chunked(q, query_start_loc, seq_lens, max_query_len, cache, 
     check("pkv_paged_attention_chunked", lib.pkv_paged_attention_chunked(
         _ptr(out), _ptr(q), _dt(q), T, Hq, _ptr(query_start_loc), _ptr(seq_lens), R, max_query_len,
         ctypes.byref(c), _ptr(block_table), block_table.shape[1], max_seq_len, softmax_scale,
-        1 if causal else 0, sliding_window, _ptr(ws), wsb, _stream(q.device)))
+        1 if causal else 0, sliding_window, PKV_PLAN_BLOCKS_NOT_SHARED if blocks_not_shared else 0,
+        _ptr(ws), wsb, _stream(q.device)))
     return out
 
 

@@ -625,10 +625,11 @@ static int multi_token_qt(const pkv_cache* c, int hq, int max_query_len, int num
   return qt;
 }
 
+// flags: PKV_PLAN_* bits for the balanced plans (they change loads, not sizes)
 static int chunk_plans(int num_tokens, int num_reqs, int hq, const pkv_cache* c, int max_query_len,
-                       int max_seq_len, int window, ChunkPlans& p) {
+                       int max_seq_len, int window, ChunkPlans& p, int flags = 0) {
   int st = make_plan(num_reqs, hq, c->num_kv_heads, c->head_dim, c->block_size, c->dtype,
-                     max_seq_len, window, 0, true, &p.single);
+                     max_seq_len, window, 0, true, &p.single, 0, flags);
   if (st != PKV_OK) return st;
   // Non-causal windowed rows see up to W + q_len - 1 keys; size for that case.
   const int extra = max_query_len > 0 ? max_query_len - 1 : 0;
@@ -649,7 +650,7 @@ static int chunk_plans(int num_tokens, int num_reqs, int hq, const pkv_cache* c,
     p.spec_heads = g;
     while (p.spec_heads > 1 && p.spec_heads * p.spec_qt > max_item_rows(c->dtype)) p.spec_heads >>= 1;
     st = make_plan(num_reqs, hq * p.spec_qt, c->num_kv_heads, c->head_dim, c->block_size, c->dtype,
-                   max_seq_len, window, max_query_len - 1, true, &p.spec, p.spec_heads * p.spec_qt);
+                   max_seq_len, window, max_query_len - 1, true, &p.spec, p.spec_heads * p.spec_qt, flags);
     if (st != PKV_OK || p.spec.scheme != 1) p.spec_qt = 0;
   }
   p.prefill = p.spec_qt == 0 && prefill_supported(c->dtype, c->head_dim, hq / c->num_kv_heads,
@@ -690,7 +691,7 @@ extern "C" int pkv_paged_attention_chunked(void* out, const void* q, int32_t q_d
                                            int32_t max_query_len, const pkv_cache* cache,
                                            const int32_t* block_table, int32_t bt_stride,
                                            int32_t max_seq_len, float softmax_scale,
-                                           int32_t causal, int32_t sliding_window,
+                                           int32_t causal, int32_t sliding_window, int32_t flags,
                                            void* workspace, size_t workspace_bytes,
                                            hipStream_t stream) {
   int st = check_cache(cache);
@@ -699,9 +700,10 @@ extern "C" int pkv_paged_attention_chunked(void* out, const void* q, int32_t q_d
   if (q_dtype != (cache->dtype == PKV_F32 ? PKV_F32 : PKV_BF16)) return PKV_ERR_DTYPE;
   if (num_tokens == 0 || num_reqs == 0) return PKV_OK;
   if (!query_start_loc) return PKV_ERR_NULL;
+  if (flags & ~PKV_PLAN_BLOCKS_NOT_SHARED) return PKV_ERR_SHAPE;
   ChunkPlans p;
   st = chunk_plans(num_tokens, num_reqs, num_q_heads, cache, max_query_len, max_seq_len,
-                   sliding_window, p);
+                   sliding_window, p, flags);
   if (st != PKV_OK) return st;
   if (p.single_bytes + p.multi_bytes > 0 && (!workspace || workspace_bytes < p.single_bytes + p.multi_bytes))
     return PKV_ERR_WORKSPACE;

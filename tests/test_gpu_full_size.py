@@ -145,9 +145,14 @@ def test_hybrid_every_row(layer):
     slots = pkv.slot_mapping(bt_d, qsl_d, nc_d, w.block_size, w.num_blocks)
     q, nk, nv = w.step_inputs(li)
     pkv.cache_write(nk, nv, slots, cache)
+    # as the bench calls it (no block is read by two requests: the decode
+    # rows' loads bypass the caches), and without the promise: the same bits
     out = pkv.paged_attention_chunked(q, qsl_d, L_d, w.max_query_len, cache, bt_d, w.max_seq_len,
-                                      w.scale, causal=True, sliding_window=W)
+                                      w.scale, causal=True, sliding_window=W, blocks_not_shared=True)
+    out_plain = pkv.paged_attention_chunked(q, qsl_d, L_d, w.max_query_len, cache, bt_d, w.max_seq_len,
+                                            w.scale, causal=True, sliding_window=W)
     torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_plain.view(torch.int16))
 
     ref_slots, errs = paging.slot_mapping(table, w.query_start_loc, w.num_computed, w.block_size,
                                           num_blocks=w.num_blocks)
@@ -179,8 +184,11 @@ def test_spec_workload_every_row():
     slots = pkv.slot_mapping(d.block_table, d.query_start_loc, d.num_computed, w.block_size, w.num_blocks)
     pkv.cache_write(d.new_k, d.new_v, slots, d.cache)
     out = pkv.paged_attention_chunked(d.q, d.query_start_loc, d.seq_lens, w.max_query_len, d.cache,
-                                      d.block_table, w.max_seq_len, w.scale)
+                                      d.block_table, w.max_seq_len, w.scale, blocks_not_shared=True)
+    out_plain = pkv.paged_attention_chunked(d.q, d.query_start_loc, d.seq_lens, w.max_query_len, d.cache,
+                                            d.block_table, w.max_seq_len, w.scale)
     torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_plain.view(torch.int16))
     s_ref, e = paging.slot_mapping(w.block_table, w.query_start_loc, w.num_computed, w.block_size)
     assert e == 0 and np.array_equal(slots.cpu().numpy(), s_ref)
     kp, vp = paging.cache_write(w.k_plane, w.v_plane, w.new_k, w.new_v, s_ref, "bf16", "bf16")

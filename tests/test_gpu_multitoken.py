@@ -124,3 +124,25 @@ def test_empty_requests_among_multi_token_requests():
     torch.cuda.synchronize()
     ref = attention.paged_attention(c["q"], "bf16", c["kp"], c["vp"], "bf16", c["bt"], c["L"], c["qsl"], 0.125)
     assert max_err(out_f64(out), ref) <= 2e-3
+
+
+@pytest.mark.parametrize("qmax,W", [(1, 0), (4, 0), (4, 100), (64, 0)])
+def test_blocks_not_shared_gives_the_same_bits(qmax, W):
+    """The promise that no block is read by two requests only changes how
+    the decode items load the cache (past the caches); single-query rows,
+    multi-token items and prefill tiles return the same bits either way."""
+    say("blocks not shared", qmax, W)
+    c = _chunk_case(3300 + qmax + W, R=12, Lmax=1500, qmax=qmax, Hq=32, Hkv=8, D=128, bs=16, v_sigma=0.2)
+
+    def dev16(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    cache = pkv.CacheView.from_planes(dev16(c["kp"]), dev16(c["vp"]))
+    args = (dev16(c["q"]), torch.from_numpy(c["qsl"]).cuda(), torch.from_numpy(c["L"]).cuda(),
+            int(np.diff(c["qsl"]).max()), cache, torch.from_numpy(c["bt"]).cuda(), int(c["L"].max()), 0.125)
+    plain = pkv.paged_attention_chunked(*args, causal=True, sliding_window=W)
+    ntl = pkv.paged_attention_chunked(*args, causal=True, sliding_window=W, blocks_not_shared=True)
+    torch.cuda.synchronize()
+    assert torch.equal(plain.view(torch.int16), ntl.view(torch.int16))
+    ref = attention.paged_attention(c["q"], "bf16", c["kp"], c["vp"], "bf16", c["bt"], c["L"], c["qsl"], 0.125,
+                                    causal=True, sliding_window=W)
+    assert max_err(out_f64(ntl), ref) <= 2e-3
