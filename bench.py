@@ -509,6 +509,15 @@ def bench_hybrid(args, dev):
     dom = max(layers, key=lambda n: per_layer[n])
     rd, wr, _ = hybrid_layer_bytes(w, w.windows[group_of[dom]])
     gbps = (rd + wr) / (per_layer[dom] * 1e-3) / 1e9
+    # HBM bytes of one whole step from the counter passes: each kernel's bytes
+    # per launch (averaged over the four layers' launches) times its launches
+    # per step (slot mapping once per group, the others once per layer)
+    per_step = [(len(w.groups), "slot_mapping_kernel"), (len(layers), "cache_write_kernel"),
+                (len(layers), "prefill_tile_kernel"), (len(layers), "prefill_merge_kernel"),
+                (len(layers), SPLIT_KERNEL), (len(layers), MERGE_KERNEL)]
+    parts = [bench_profiles.traffic(bench_profiles.WORKLOAD_SET["hybrid"], [frag]) for _, frag in per_step]
+    step_traffic = (sum(n * t for (n, _), t in zip(per_step, parts))
+                    if all(t is not None for t in parts) else None)
     res = {
         "metric": "paged decode attention HBM GB/s (% of peak) + KV cache writes tokens/s, 1 GPU",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -527,9 +536,14 @@ def bench_hybrid(args, dev):
                              "mfma_frac": round(prefill_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                              "flops": "4 D per visible (query token, key, query head): scores and P.V"}}
            if prefill_ms else {}),
-        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "chunked attention of layer %s (all its kernels)" % dom},
+        # the unit is the whole step (its kernels are timed together; the
+        # counters give bytes per kernel averaged over the layers)
+        "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBPS, 4), "traffic": step_traffic,
+                     "algorithmic_bytes": int(step_bytes),
+                     "kernel": "whole step: 4 layers of cache write + chunked attention, and the slot "
+                               "mappings"},
+        "dominant_layer": {"layer": dom, "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)},
     }
     print(json.dumps(res), flush=True)
 
