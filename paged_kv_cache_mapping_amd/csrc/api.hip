@@ -25,6 +25,27 @@ int device_cu_count() {
   return cus;
 }
 
+int device_max_lds() {
+  constexpr int kDefault = 160 * 1024;   // gfx950: a workgroup may take the whole CU's LDS
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return kDefault;
+  if (dev < 64) {
+    std::lock_guard<std::mutex> lock(mu);
+    if (cached[dev] > 0) return cached[dev];
+  }
+  int bytes = 0;
+  if (hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+      bytes <= 0)
+    bytes = kDefault;
+  if (dev < 64) {
+    std::lock_guard<std::mutex> lock(mu);
+    cached[dev] = bytes;
+  }
+  return bytes;
+}
+
 }  // namespace pkv
 
 extern "C" const char* pkv_status_string(int status) {

@@ -12,6 +12,10 @@ namespace pkv {
 // Compute units of the current device (cached per device id).
 int device_cu_count();
 
+// LDS bytes one workgroup may take on the current device (its attribute;
+// 160 KiB, gfx950's per-CU LDS, when there is no device to ask).
+int device_max_lds();
+
 inline bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -776,6 +776,11 @@ int pf_tokens(int d, int g) {
 template <int D, int G, int KV>
 void pf_launch(const PrefillArgs& a, hipStream_t s) {
   const size_t lds = pf_lds_bytes<D, G>(a.max_blocks);
+  // past 64 KiB the kernel asks for the larger dynamic LDS explicitly (a
+  // refusal surfaces as the launch's error)
+  if (lds > 64 * 1024)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_tile_kernel<D, G, KV, kPfWavesAlone>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   prefill_tile_kernel<D, G, KV, kPfWavesAlone><<<a.workers, kPfWavesAlone * 64, lds, s>>>(a);
   prefill_merge_kernel<D, G, kPfWavesAlone><<<a.workers, kPfMergeThreads, 0, s>>>(a);
 }
@@ -816,9 +821,12 @@ bool prefill_supported(int kv_dtype, int head_dim, int group, int max_seq_len, i
   if (max_query_len < 2) return false;
   const int tok = pf_tokens(head_dim, group);
   const int mb = pf_max_blocks(max_seq_len, block_size, window, tok > max_query_len ? tok : max_query_len);
-  // the staged tiles plus the table slice within 64 KiB of LDS per workgroup
+  // the staged tiles plus the table slice within the LDS one workgroup may
+  // take (one workgroup runs per CU: on gfx950 the CU's whole 160 KiB, which
+  // holds the table slice of contexts up to about 500K tokens at head size
+  // 128 and block size 16)
   const size_t bytes = 2 * (size_t)(32 * (head_dim * 4 + 48)) + pf_align16((size_t)mb * 4);
-  return bytes <= 64 * 1024;
+  return bytes <= (size_t)device_max_lds();
 }
 
 // One workgroup per compute unit (eight waves fill a CU at this kernel's

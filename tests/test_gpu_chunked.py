@@ -295,3 +295,68 @@ def test_chunked_one_long_item_cut_by_every_share():
                                       cache, torch.from_numpy(bt).cuda(), int(L[0]), 0.125)
     torch.cuda.synchronize()
     assert max_err(out_f64(out), ref) <= 2e-3
+
+
+def _long_prefill_case(seed, lens, qlens, Hq, Hkv, D, bs):
+    """Prefill chunks at the end of very long contexts; V carries a +-1 offset
+    per group of 64 positions (and K, Q plain noise), so that a dropped or
+    repeated key tile shows at several times the per-element bound."""
+    rng = np.random.default_rng(seed)
+    R = len(lens)
+    L = np.asarray(lens, np.int32)
+    ql = np.asarray(qlens, np.int32)
+    nb = int(sum(-(-int(x) // bs) for x in L)) + 3
+    perm = rng.permutation(nb)
+    width = int(max(-(-int(x) // bs) for x in L))
+    bt = np.full((R, width), -1, np.int32)
+    kp = np.zeros((nb, bs, Hkv, D), np.uint16)
+    vp = np.zeros((nb, bs, Hkv, D), np.uint16)
+    k = 0
+    for r in range(R):
+        n = -(-int(L[r]) // bs)
+        bt[r, :n] = perm[k:k + n]
+        k += n
+        pos = int(L[r])
+        kr = rng.standard_normal((pos, Hkv, D), dtype=np.float32) * np.float32(0.35)
+        sig = rng.choice([-1.0, 1.0], size=(-(-pos // 64), Hkv, D)).astype(np.float32)
+        vr = rng.standard_normal((pos, Hkv, D), dtype=np.float32) * np.float32(0.35) + \
+            np.repeat(sig, 64, axis=0)[:pos]
+        pad = n * bs - pos
+        kr = np.concatenate([kr, np.zeros((pad, Hkv, D), np.float32)]).reshape(n, bs, Hkv, D)
+        vr = np.concatenate([vr, np.zeros((pad, Hkv, D), np.float32)]).reshape(n, bs, Hkv, D)
+        kp[bt[r, :n]] = bf16_bits(kr)
+        vp[bt[r, :n]] = bf16_bits(vr)
+    qsl = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    q = bf16_bits(rng.standard_normal((int(qsl[-1]), Hq, D)).astype(np.float32) * 0.35)
+    return dict(L=L, qsl=qsl, bt=bt, kp=kp, vp=vp, q=q, nb=nb, bs=bs, Hkv=Hkv, D=D)
+
+
+def test_prefill_tile_takes_long_contexts():
+    """Contexts whose table slice takes the prefill tile past 64 KiB of LDS
+    (about 120K tokens at head size 128, block size 16) stay on the tile:
+    the chunked call's workspace for the multi-query part is the tile's, the
+    same as for a short context, and the output is within the per-element
+    bound of every element."""
+    from helpers import check_close
+    props = torch.cuda.get_device_properties(0)
+    say("long-context prefill, LDS per block", getattr(props, "shared_memory_per_block", None))
+    lens, qlens = [125000, 119001], [40, 17]
+    Hq, Hkv, D, bs = 4, 2, 128, 16
+    c = _long_prefill_case(4100, lens, qlens, Hq, Hkv, D, bs)
+    cache = pkv.CacheView.from_planes(
+        torch.from_numpy(c["kp"].view(np.int16)).view(torch.bfloat16).cuda(),
+        torch.from_numpy(c["vp"].view(np.int16)).view(torch.bfloat16).cuda())
+
+    def multi_part(max_seq_len):
+        T, R = int(c["qsl"][-1]), len(lens)
+        return (pkv.chunked_workspace_size(T, R, Hq, cache, max(qlens), max_seq_len, 0)
+                - pkv.chunked_workspace_size(T, R, Hq, cache, 1, max_seq_len, 0))
+    assert multi_part(max(lens)) == multi_part(4096)
+    out = pkv.paged_attention_chunked(
+        torch.from_numpy(c["q"].view(np.int16)).view(torch.bfloat16).cuda(), torch.from_numpy(c["qsl"]).cuda(),
+        torch.from_numpy(c["L"]).cuda(), max(qlens), cache, torch.from_numpy(c["bt"]).cuda(), max(lens), 0.125)
+    torch.cuda.synchronize()
+    ref = attention.paged_attention(c["q"], "bf16", c["kp"], c["vp"], "bf16", c["bt"], c["L"], c["qsl"], 0.125)
+    # floor: the fp32 sums over 120K keys of unit-scale V (outputs ~0.02);
+    # a dropped or repeated 32-key tile moves an output by about 3e-4
+    check_close("long_context_prefill", out_f64(out), ref, 2e-3, 5e-5)
