@@ -60,8 +60,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--split-blocks", type=int, default=0, help="override the decode split (tuning)")
-    p.add_argument("--decode-step", action="store_true",
-                   help="time the step as one pkv_paged_attention_decode_step call (write in its merge)")
+    p.add_argument("--three-call", action="store_true",
+                   help="time the step as slot mapping + write, split, merge (three calls) instead of "
+                        "one pkv_paged_attention_decode_step call")
     p.add_argument("--shared-blocks", action="store_true",
                    help="plan as if blocks could be shared (no PKV_PLAN_BLOCKS_NOT_SHARED); "
                         "the prefix workload always is")
@@ -107,12 +108,13 @@ def decode_plan_for(pkv, w, cache, shared_blocks=False, **tune):
     return plan
 
 
-def decode_step_fn(pkv, w, base, plan, ws, out, slots, one_call=False):
-    """One timed decode step over a (cache view, block table) pair: slot
-    mapping and the write of the step's K/V rows in one launch, then the
-    decode attention's two phases; or with one_call (balanced plans) the
-    decode step call, whose split attends to the cached keys and whose merge
-    adds the step's own token and writes its K/V and slot."""
+def decode_step_fn(pkv, w, base, plan, ws, out, slots, one_call=True):
+    """One timed decode step over a (cache view, block table) pair: with
+    one_call (balanced plans; the default) the decode step call, whose split
+    attends to the cached keys and writes the step's K/V rows and slots and
+    whose merge adds each row's own token; otherwise slot mapping and the
+    write of the step's K/V rows in one launch, then the decode attention's
+    two phases."""
     def step(cache, bt):
         pkv.paged_attention_decode_step(base.q, base.new_k, base.new_v, cache, bt, base.seq_lens,
                                         w.max_seq_len, w.scale, plan, ws, out, slots=slots)
@@ -584,7 +586,7 @@ def main():
     ws = pkv.new_workspace(plan.workspace_bytes, dev)
     out = torch.empty_like(base.q)
     slots = torch.empty(w.num_reqs, dtype=torch.int64, device=dev)
-    run_step = decode_step_fn(pkv, w, base, plan, ws, out, slots, one_call=args.decode_step)
+    run_step = decode_step_fn(pkv, w, base, plan, ws, out, slots, one_call=not args.three_call)
 
     def step(i):
         run_step(*pools[i % npools])
@@ -721,7 +723,7 @@ def main():
                    "split_blocks": int(plan.split_blocks), "max_splits": int(plan.max_splits),
                    "lead_workers": int(plan.lead_workers), "trail_share_pct": int(plan.trail_share_pct),
                    "plan_flags": int(plan.flags),
-                   "step_calls": ("decode_step" if args.decode_step and plan.scheme == 1
+                   "step_calls": ("decode_step" if not args.three_call and plan.scheme == 1
                                   else "slot_mapping_cache_write + decode_partials + decode_combine"),
                    **extra},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),

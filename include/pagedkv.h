@@ -391,7 +391,9 @@ PKV_API int pkv_paged_attention_decode_static(void* out, const void* q, int32_t 
  * scheme 0 m [rows, Hq, max_splits] and l [rows, Hq, max_splits]; for
  * scheme 1 (G = heads_per_item) records [rows, Hq / G, max_splits, 2, G]
  * holding the G heads' m then their l, followed by int32 pairs (piece
- * count, output row) [rows, Hq / G, 2].  acc holds dequantised V sums (for an
+ * count, output row) [rows, Hq / G, 2] and an int32 per row (used by
+ * pkv_paged_attention_decode_step: 1 when the row's new token has a slot).
+ * acc holds dequantised V sums (for an
  * fp8 cache the V scale is already applied), so phase 2 needs no cache.
  */
 PKV_API int pkv_paged_attention_decode_partials(void* out, const void* q,
@@ -426,10 +428,12 @@ PKV_API int pkv_paged_attention_decode_combine(void* out, int32_t out_dtype,
  * sits at position seq_lens[r] - 1; its slot is
  * block_table[r][(seq_lens[r] - 1) / block_size] * block_size +
  * (seq_lens[r] - 1) % block_size.  The split pass attends to the cached
- * keys before that position; the merge adds the new token's term (its key
- * and value taken through the cache's format as the write stores them: fp8
- * and INT4 encoded with the inverse scales), writes its K/V codes to the
- * slot and the slot to slot_mapping.
+ * keys before that position and also writes each new token's K/V codes to
+ * its slot and the slot to slot_mapping (one worker per sequence, after its
+ * share of the attention; no sequence's visible keys include a slot being
+ * written); the merge adds the new token's term (its key and value taken
+ * through the cache's format as the write stores them: fp8 and INT4
+ * encoded with the inverse scales).
  * Equivalent to pkv_slot_mapping_cache_write (query_start_loc 0..num_seqs,
  * num_computed = seq_lens - 1) followed by pkv_paged_attention_decode_partials
  * and _combine with the same plan: the same cache bytes and slots, and

@@ -77,9 +77,11 @@ static size_t partial_bytes(int rows, int hq, int splits, int d) {
 }
 
 static size_t plan_bytes(const pkv_decode_plan& p, int rows, int hq, int d) {
+  // balanced: the partials, a piece count and output row per (row, head
+  // group), and per row the decode step's own-token flag
   if (p.scheme == 1)
     return partial_bytes(rows, hq, p.max_splits, d) +
-           (size_t)rows * (hq / p.heads_per_item) * 2 * sizeof(int32_t);
+           (size_t)rows * (hq / p.heads_per_item) * 2 * sizeof(int32_t) + (size_t)rows * sizeof(int32_t);
   return p.max_splits > 1 ? partial_bytes(rows, hq, p.max_splits, d) : 0;
 }
 
@@ -259,7 +261,7 @@ static void bind_workspace(DecodeArgs& a, void* ws, int rows, int hq, int d, int
   a.ws_m = wsf ? wsf + nacc * d : nullptr;
   a.ws_l = wsf ? a.ws_m + nacc : nullptr;
   a.ws_np = wsf ? reinterpret_cast<int32_t*>(a.ws_l + nacc) : nullptr;
-  (void)gt;
+  a.ws_own = wsf && gt > 0 ? a.ws_np + (size_t)rows * (hq / gt) * 2 : nullptr;
 }
 
 // Validates everything host-visible and fills DecodeArgs (no launch).
@@ -433,6 +435,7 @@ extern "C" int pkv_paged_attention_decode_step(
   if (cache->dtype == PKV_F32) return PKV_ERR_DTYPE;
   if (num_seqs == 0) return PKV_OK;
   if (!new_k || !new_v) return PKV_ERR_NULL;
+  if (!aligned16(new_k) || !aligned16(new_v)) return PKV_ERR_SHAPE;
   if (!workspace) return PKV_ERR_WORKSPACE;
   a.new_token = 1;
   a.new_k = new_k;

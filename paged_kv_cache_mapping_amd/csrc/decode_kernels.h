@@ -78,6 +78,7 @@ struct DecodeArgs {
   int32_t stream;           // balanced partition (piece counts in ws_np)
   int32_t heads_per_item;
   int32_t* ws_np;           // balanced partition: pieces per (row, head group)
+  int32_t* ws_own;          // decode step: per row, 1 when its own token has a slot
   int32_t lead_workers;     // balanced partition: workers with a full share (0: all)
   int32_t trail_pct;        // share of the other workers, percent of a full share
   int32_t lds_budget;       // bytes of LDS one worker may take
@@ -85,10 +86,11 @@ struct DecodeArgs {
   int32_t pair;             // INT4: items span two adjacent KV heads (see kInt4Pair)
   // Decode step with its own token (pkv_paged_attention_decode_step, row
   // mode 0, balanced partition): the split leaves position seq_len - 1 out
-  // and keeps every piece as a partial; the merge adds that token's term,
-  // its key and value read from new_k / new_v ([rows, Hkv, D] bf16) and
-  // rounded through the cache's format, writes them to the token's slot
-  // and the slot to slots_out.
+  // and keeps every piece as a partial, and one worker per row writes that
+  // token's key and value (new_k / new_v, [rows, Hkv, D] bf16, encoded as
+  // the cache write does) to its slot, the slot to slots_out and whether it
+  // had one to ws_own; the merge adds the token's term from new_k / new_v
+  // rounded through the cache's format.
   int32_t new_token;
   const void* new_k;
   const void* new_v;
@@ -1036,6 +1038,84 @@ __device__ __forceinline__ Shares make_shares(long long U, int W, int lead, int 
   return s;
 }
 
+// The decode step's own token of row r (position seq_len - 1), written by
+// one wave: its key and value rows from new_k / new_v, encoded exactly as
+// the cache write does (bf16 as is; fp8 e4m3 and INT4 with the inverse
+// scales), to the slot its block-table entry gives; the slot to slots_out
+// (-1 for a block the table does not map, whose row the merge makes NaN)
+// and the verdict to ws_own.  Rows whose lengths the split rejects are left
+// to the rows-without-units pass.
+template <int D>
+__device__ __forceinline__ void write_own_token(const DecodeArgs& a, int r, int lane) {
+  const int L = a.seq_lens[r];
+  if (L <= 0 || L > a.max_seq_len) return;
+  const int pos = L - 1;
+  const int blk = pos >> a.bs_log2;
+  const int phys = blk < a.bt_stride ? a.bt[(int64_t)r * a.bt_stride + blk] : -1;
+  const bool ok = phys >= 0 && phys < a.num_blocks;
+  const int in_blk = pos & ((1 << a.bs_log2) - 1);
+  if (lane == 0) {
+    a.ws_own[r] = ok ? 1 : 0;
+    if (a.slots_out) a.slots_out[r] = ok ? ((int64_t)phys << a.bs_log2) + in_blk : -1;
+  }
+  if (!ok) return;
+  const int bits = kv_bits(a.kv_dtype);
+  const int n = a.kv_heads * D;                   // elements of one token row
+  const int64_t row = (int64_t)phys * (a.block_stride * bits / 8) + (int64_t)in_blk * n * bits / 8;
+  const uint16_t* kn = reinterpret_cast<const uint16_t*>(a.new_k) + (int64_t)r * n;
+  const uint16_t* vn = reinterpret_cast<const uint16_t*>(a.new_v) + (int64_t)r * n;
+  uint8_t* kd = reinterpret_cast<uint8_t*>(const_cast<char*>(a.kbase) + row);
+  uint8_t* vd = reinterpret_cast<uint8_t*>(const_cast<char*>(a.vbase) + row);
+  // eight elements per lane and pass (16 bytes of new_k / new_v)
+  for (int e = lane * 8; e < n; e += kWave * 8) {
+    const uint4 kw = *reinterpret_cast<const uint4*>(kn + e);
+    const uint4 vw = *reinterpret_cast<const uint4*>(vn + e);
+    const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w}, vk[4] = {vw.x, vw.y, vw.z, vw.w};
+    if (bits == 16) {
+      *reinterpret_cast<uint4*>(kd + (int64_t)e * 2) = kw;
+      *reinterpret_cast<uint4*>(vd + (int64_t)e * 2) = vw;
+    } else if (bits == 8) {
+      // the hardware conversion unless a NaN is among the eight (the
+      // integer encoder keeps it), as the cache write does
+      float kx[8], vx[8];
+      bool nan = false;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        kx[i] = as_float(((kk[i / 2] >> (16 * (i % 2))) & 0xFFFFu) << 16) * a.inv_k_scale;
+        vx[i] = as_float(((vk[i / 2] >> (16 * (i % 2))) & 0xFFFFu) << 16) * a.inv_v_scale;
+        nan |= kx[i] != kx[i] || vx[i] != vx[i];
+      }
+      uint32_t kc[2], vc[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (!nan) {
+          kc[j] = e4m3x4_encode_no_nan(kx[4 * j], kx[4 * j + 1], kx[4 * j + 2], kx[4 * j + 3]);
+          vc[j] = e4m3x4_encode_no_nan(vx[4 * j], vx[4 * j + 1], vx[4 * j + 2], vx[4 * j + 3]);
+        } else {
+          kc[j] = vc[j] = 0u;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            kc[j] |= e4m3_encode(kx[4 * j + i]) << (8 * i);
+            vc[j] |= e4m3_encode(vx[4 * j + i]) << (8 * i);
+          }
+        }
+      }
+      *reinterpret_cast<uint2*>(kd + e) = make_uint2(kc[0], kc[1]);
+      *reinterpret_cast<uint2*>(vd + e) = make_uint2(vc[0], vc[1]);
+    } else {   // two codes per byte, element 2j in the low nibble of byte j
+      uint32_t kc = 0u, vc = 0u;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t kb = (kk[i / 2] >> (16 * (i % 2))) & 0xFFFFu, vb = (vk[i / 2] >> (16 * (i % 2))) & 0xFFFFu;
+        kc |= int4_encode(as_float(kb << 16) * a.inv_k_scale) << (4 * i);
+        vc |= int4_encode(as_float(vb << 16) * a.inv_v_scale) << (4 * i);
+      }
+      *reinterpret_cast<uint32_t*>(kd + e / 2) = kc;
+      *reinterpret_cast<uint32_t*>(vd + e / 2) = vc;
+    }
+  }
+}
+
 template <int D, int GT, int KV, int DEPTH, int QT = 1, bool NTL = false>
 __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
   using S = MfmaShape<D, GT, KV>;
@@ -1827,6 +1907,13 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
   }
   if (cur >= 0) flush();
 
+  // ---- the decode step's own tokens: row r by worker W - 1 - r % W (the
+  // last workers, whose shares are the smaller ones with lead shares), after
+  // its own units (the split reads no token's slot it could race with: the
+  // rows' visible keys end before their own token)
+  if (a.new_token)
+    for (int r = W - 1 - blockIdx.x; r < a.num_rows; r += W) write_own_token<D>(a, r, lane);
+
   // ---- rows without units, one worker each: rows this pass skips (another
   // pass owns them) get a piece count of 0 so that the merge phase leaves
   // them alone; rows that cannot be computed also get NaN output
@@ -1878,8 +1965,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 // dims, so it reads one (m, l) pair and one run of acc per piece and merges
 // online, eight pieces' loads in flight per half (sixteen per wave, the
 // first sixteen issued with the piece count); the halves' states then
-// combine across the wave.  (The step's own token, where the merge adds
-// it, keeps one half: every lane takes every piece.)
+// combine across the wave, and for the decode step the first half adds the
+// step's own token.
 // Rows of an item one merge wave takes: items of more than 2 rows are merged
 // by several waves (more waves in flight, fewer loads per lane: measured
 // faster than 4 rows per wave on the decode steps, 0.2 to 1.3 us).
@@ -1888,98 +1975,64 @@ __host__ __device__ constexpr int merge_rows_per_wave(int rows) { return rows > 
 // The step's own token (position seq_len - 1 of row b, pkv_paged_attention_
 // decode_step) joining a merge wave's online softmax for its row h (query
 // head `head`): its key and value are the row's new_k / new_v entries taken
-// through the cache's format exactly as the write stores them (bf16 as is;
-// fp8 and INT4 encoded with the inverse scale, their code values then
-// scaled as the cached keys' are).  The lanes of the first query head of
-// each KV head also write the codes to the token's slot, and one lane the
-// slot.  A token whose block the table does not map makes the row NaN and
-// is not written (slot -1): a write through an unmapped slot is skipped and
-// attention over an unmapped block gives NaN.  Every lane of the wave calls
-// this (the dot product is reduced across a row's LPH lanes).
+// through the cache's format exactly as the split's write stores them (bf16
+// as is; fp8 and INT4 encoded with the inverse scale, their code values then
+// scaled as the cached keys' are).  The lane's query, key and value
+// elements are loaded with the merge's first round of partials
+// (OwnToken::load) and joined after the pieces (OwnToken::merge; every lane
+// of the half calls it: the dot product is reduced across a row's LPH
+// lanes).
 template <int D, int LPH, int DPL>
-__device__ __forceinline__ void merge_own_token(const DecodeArgs& a, int b, int head, int tok, int d0,
-                                                bool active, int pos, int phys, float& M, float& den,
-                                                float (&num)[DPL]) {
-  const int qpk = a.num_q_heads / a.kv_heads;
-  const int kvh = head / qpk;
-  const bool ok = phys >= 0 && phys < a.num_blocks;
-  const int64_t src = ((int64_t)b * a.kv_heads + kvh) * D + (active ? d0 : 0);
-  const uint16_t* kn = reinterpret_cast<const uint16_t*>(a.new_k) + src;
-  const uint16_t* vn = reinterpret_cast<const uint16_t*>(a.new_v) + src;
-  const uint16_t* qn = reinterpret_cast<const uint16_t*>(a.q) +
-                       ((int64_t)tok * a.num_q_heads + head) * D + (active ? d0 : 0);
-  uint32_t kc[DPL], vc[DPL];      // the cache's codes (bf16 bits for a bf16 cache)
-  float dot = 0.f, vv[DPL];
+struct OwnToken {
+  uint16_t qb[DPL], kb[DPL], vb[DPL];
+  __device__ __forceinline__ void load(const DecodeArgs& a, int b, int head, int tok, int d0, bool active) {
+    const int kvh = head / (a.num_q_heads / a.kv_heads);
+    const int64_t src = ((int64_t)b * a.kv_heads + kvh) * D + (active ? d0 : 0);
+    const uint16_t* kn = reinterpret_cast<const uint16_t*>(a.new_k) + src;
+    const uint16_t* vn = reinterpret_cast<const uint16_t*>(a.new_v) + src;
+    const uint16_t* qn = reinterpret_cast<const uint16_t*>(a.q) +
+                         ((int64_t)tok * a.num_q_heads + head) * D + (active ? d0 : 0);
 #pragma unroll
-  for (int i = 0; i < DPL; ++i) {
-    const uint32_t kb = active ? kn[i] : 0u, vb = active ? vn[i] : 0u;
-    const float qx = active ? as_float((uint32_t)qn[i] << 16) : 0.f;
-    float kx = as_float(kb << 16), vx = as_float(vb << 16);
-    if (a.kv_dtype == PKV_FP8_E4M3) {
-      kc[i] = e4m3_encode(kx * a.inv_k_scale);
-      vc[i] = e4m3_encode(vx * a.inv_v_scale);
-      kx = e4m3x2_to_f32<false>(kc[i]).x;
-      vx = e4m3x2_to_f32<false>(vc[i]).x;
-    } else if (a.kv_dtype == PKV_INT4) {
-      kc[i] = int4_encode(kx * a.inv_k_scale);
-      vc[i] = int4_encode(vx * a.inv_v_scale);
-      kx = (float)((int)kc[i] - 8);
-      vx = (float)((int)vc[i] - 8);
-    } else {
-      kc[i] = kb;
-      vc[i] = vb;
-    }
-    dot = fmaf(qx, kx, dot);
-    vv[i] = vx * a.v_scale;
-  }
-#pragma unroll
-  for (int o = LPH / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
-  const float s = dot * a.scale_log2;   // an unmapped token's row is set to NaN after its store
-  const float mn = fmaxf(M, s);
-  const float c_old = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mn);
-  const float c_new = __builtin_amdgcn_exp2f(s - mn);
-  den = den * c_old + c_new;
-#pragma unroll
-  for (int i = 0; i < DPL; ++i) num[i] = num[i] * c_old + vv[i] * c_new;
-  M = mn;
-  const int bits = kv_bits(a.kv_dtype);
-  const int in_blk = pos & ((1 << a.bs_log2) - 1);
-  if (ok && active && head % qpk == 0) {
-    const int64_t row_bytes = (int64_t)a.kv_heads * D * bits / 8;
-    const int64_t off = (int64_t)phys * (a.block_stride * bits / 8) + (int64_t)in_blk * row_bytes +
-                        ((int64_t)kvh * D + d0) * bits / 8;
-    uint8_t* kd = reinterpret_cast<uint8_t*>(const_cast<char*>(a.kbase) + off);
-    uint8_t* vd = reinterpret_cast<uint8_t*>(const_cast<char*>(a.vbase) + off);
-    if (bits == 16) {
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) {
-        reinterpret_cast<uint16_t*>(kd)[i] = (uint16_t)kc[i];
-        reinterpret_cast<uint16_t*>(vd)[i] = (uint16_t)vc[i];
-      }
-    } else if (bits == 8) {
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) {
-        kd[i] = (uint8_t)kc[i];
-        vd[i] = (uint8_t)vc[i];
-      }
-    } else {   // two codes per byte, element 2j in the low nibble of byte j
-#pragma unroll
-      for (int i = 0; i < DPL; i += 2) {
-        const uint32_t k1 = i + 1 < DPL ? kc[i + 1] : 0u, v1 = i + 1 < DPL ? vc[i + 1] : 0u;
-        kd[i / 2] = (uint8_t)(kc[i] | (k1 << 4));
-        vd[i / 2] = (uint8_t)(vc[i] | (v1 << 4));
-      }
+    for (int i = 0; i < DPL; ++i) {
+      qb[i] = active ? qn[i] : (uint16_t)0;
+      kb[i] = active ? kn[i] : (uint16_t)0;
+      vb[i] = active ? vn[i] : (uint16_t)0;
     }
   }
-  if (a.slots_out && head == 0 && d0 == 0)
-    a.slots_out[b] = ok ? ((int64_t)phys << a.bs_log2) + in_blk : -1;
-}
+  __device__ __forceinline__ void merge(const DecodeArgs& a, float& M, float& den, float (&num)[DPL]) const {
+    float dot = 0.f, vv[DPL];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      const float qx = as_float((uint32_t)qb[i] << 16);
+      float kx = as_float((uint32_t)kb[i] << 16), vx = as_float((uint32_t)vb[i] << 16);
+      if (a.kv_dtype == PKV_FP8_E4M3) {
+        kx = e4m3x2_to_f32<false>(e4m3_encode(kx * a.inv_k_scale)).x;
+        vx = e4m3x2_to_f32<false>(e4m3_encode(vx * a.inv_v_scale)).x;
+      } else if (a.kv_dtype == PKV_INT4) {
+        kx = (float)((int)int4_encode(kx * a.inv_k_scale) - 8);
+        vx = (float)((int)int4_encode(vx * a.inv_v_scale) - 8);
+      }
+      dot = fmaf(qx, kx, dot);
+      vv[i] = vx * a.v_scale;
+    }
+#pragma unroll
+    for (int o = LPH / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
+    const float s = dot * a.scale_log2;
+    const float mn = fmaxf(M, s);
+    const float c_old = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mn);
+    const float c_new = __builtin_amdgcn_exp2f(s - mn);
+    den = den * c_old + c_new;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) num[i] = num[i] * c_old + vv[i] * c_new;
+    M = mn;
+  }
+};
 
 template <int D, int GT, int OT, int QT = 1, bool NT = false>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   constexpr int RI = GT * QT;                       // rows of an item: (token, head)
   constexpr int RW = merge_rows_per_wave(RI);       // rows one wave merges
-  constexpr int NH = NT ? 1 : 2;                    // wave halves taking alternate pieces
+  constexpr int NH = 2;                             // wave halves taking alternate pieces
   constexpr int LPH = kWave / NH / RW;              // lanes per row within a half
   constexpr int DPL = D >= LPH ? D / LPH : 1;       // dims per lane
   constexpr int U = 8;                              // pieces per half and round of loads
@@ -2012,13 +2065,13 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   };
   const int np_word = a.ws_np[2 * rg];
   const int tok = a.ws_np[2 * rg + 1];
-  // the step's own token: its position and block, read with the first
-  // round so that the table lookup overlaps it
-  int own_pos = 0, own_phys = -1;
+  // the step's own token: whether the split found it a slot, and this
+  // lane's query, key and value elements, read with the first round
+  int own_ok = 1;
+  OwnToken<D, LPH, DPL> own;
   if constexpr (NT) {
-    own_pos = a.seq_lens[b] - 1;
-    const int blk = own_pos >> a.bs_log2;
-    if (own_pos >= 0 && blk < a.bt_stride) own_phys = a.bt[(int64_t)b * a.bt_stride + blk];
+    own_ok = a.ws_own[b];
+    own.load(a, b, g * GT + h % GT, b, d0, active);   // decode rows: query row b
   }
   load_round(0, a.max_splits);
   const int np = min(np_word, a.max_splits);
@@ -2057,7 +2110,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   }
   if constexpr (NT) {
     static_assert(QT == 1, "one query token per row");
-    merge_own_token<D, LPH, DPL>(a, b, g * GT + h % GT, tok, d0, active, own_pos, own_phys, M, den, num);
+    own.merge(a, M, den, num);
   }
   if (!active) return;
   // row h = t * GT + head: query token t of the row's request
@@ -2072,7 +2125,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int64_t out_elem = ((int64_t)(tok + t) * a.num_q_heads + g * GT + h % GT) * D + d0;
   store_out<OT, DPL>(a.out, out_elem, o);
   if constexpr (NT) {
-    if (!(own_phys >= 0 && own_phys < a.num_blocks)) {   // the token has no slot: NaN row
+    if (!own_ok) {   // the token has no slot: NaN row
 #pragma unroll
       for (int i = 0; i < DPL; ++i) o[i] = __builtin_nanf("");
       store_out<OT, DPL>(a.out, out_elem, o);

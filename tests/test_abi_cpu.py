@@ -280,8 +280,9 @@ def test_plan_flags_are_checked(lib):
 def test_plan_resize_recomputes_the_sizes(lib, rows, hq, window, split, workers, hpi):
     """After the tuning fields change, the sizes follow the workspace layout
     of pagedkv.h: acc [rows, Hq, max_splits, D] and m, l per slot as floats,
-    plus an int32 pair per (row, head group); max_splits = pieces a row's
-    visible blocks can be cut into by shares of at least split blocks."""
+    plus an int32 pair per (row, head group) and an int32 per row;
+    max_splits = pieces a row's visible blocks can be cut into by shares of
+    at least split blocks."""
     D, bs, L = 128, 16, 2048
     plan = _lib.PkvDecodePlan()
     assert lib.pkv_decode_plan_make(rows, hq, 8 if hq >= 8 else 2, D, bs, _lib.PKV_BF16, L, window, 0,
@@ -292,7 +293,7 @@ def test_plan_resize_recomputes_the_sizes(lib, rows, hq, window, split, workers,
     assert lib.pkv_decode_plan_resize(rows, hq, D, bs, L, window, ctypes.byref(plan)) == _lib.PKV_OK
     nvis = -(-L // bs) if window == 0 else min(-(-L // bs), -(-(window + bs - 1) // bs))
     assert plan.max_splits == -(-nvis // split) + 1
-    assert plan.workspace_bytes == rows * hq * plan.max_splits * (D + 2) * 4 + rows * (hq // hpi) * 8
+    assert plan.workspace_bytes == rows * hq * plan.max_splits * (D + 2) * 4 + rows * (hq // hpi) * 8 + rows * 4
 
 
 def test_plan_resize_rejects_fields_no_kernel_takes(lib):

@@ -50,12 +50,12 @@ def _gpu():
     gpu_or_skip()
 
 
-def _bench_decode_step(w, base, cache=None, bt=None):
+def _bench_decode_step(w, base, cache=None, bt=None, one_call=True):
     plan = bench.decode_plan_for(pkv, w, base.cache)
     ws = pkv.new_workspace(plan.workspace_bytes, "cuda")
     out = torch.empty_like(base.q)
     slots = torch.empty(w.num_reqs, dtype=torch.int64, device="cuda")
-    step = bench.decode_step_fn(pkv, w, base, plan, ws, out, slots)
+    step = bench.decode_step_fn(pkv, w, base, plan, ws, out, slots, one_call=one_call)
     step(base.cache if cache is None else cache, base.block_table if bt is None else bt)
     torch.cuda.synchronize()
     return plan, slots, out
@@ -65,18 +65,24 @@ def _bench_decode_step(w, base, cache=None, bt=None):
                                             ("fp8", FLOOR_UNIT, 3e-2),
                                             ("int4", FLOOR_SMALL, 2e-3)])
 def test_bench_decode_step_every_row(name, floor, tol):
-    """The decode step exactly as bench.py times it (its plan, its calls), on
-    the full workload: slots and cache bit-exact, every output row bounded."""
+    """The decode step exactly as bench.py times it (its plan, one
+    pkv_paged_attention_decode_step call), on the full workload: slots and
+    cache bit-exact, every output row bounded; then the three-call form
+    (bench.py --three-call) on the same inputs, which writes the same bytes
+    again."""
     say("bench decode step", name)
     w = workloads.ALL[name]()
     base = w.device()
-    plan, slots, out = _bench_decode_step(w, base)
-    say(name, "plan scheme", plan.scheme, "workers", plan.num_workers, "flags", plan.flags)
     ref_slots, kp, vp, ref = oracle_decode_step(w, "bf16")
-    assert np.array_equal(slots.cpu().numpy(), ref_slots)
-    assert host_bits(base.cache.k).tobytes() == kp.tobytes()
-    assert host_bits(base.cache.v).tobytes() == vp.tobytes()
-    check_close("bench_step_" + name, out_f64(out), ref, tol, floor)
+    for one_call in (True, False):
+        plan, slots, out = _bench_decode_step(w, base, one_call=one_call)
+        say(name, "one call", one_call, "plan scheme", plan.scheme, "workers", plan.num_workers,
+            "flags", plan.flags)
+        assert np.array_equal(slots.cpu().numpy(), ref_slots)
+        assert host_bits(base.cache.k).tobytes() == kp.tobytes()
+        assert host_bits(base.cache.v).tobytes() == vp.tobytes()
+        check_close("bench_step_%s_%s" % (name, "one_call" if one_call else "three_calls"), out_f64(out), ref,
+                    tol, floor)
 
 
 def test_llama70b_layers_0_39_79_of_the_80_layer_cache():
