@@ -1,6 +1,6 @@
 """GPU parity: pkv_paged_attention_decode_step, the decode step whose split
-pass attends to the cached keys and whose merge adds the step's own token
-and writes it to its slot.
+pass attends to the cached keys and writes the step's own token to its
+slot, and whose merge adds that token's term.
 
 Against the three-call form (slot mapping + write, then the decode phases)
 the cache bytes and slots must be identical and the outputs within the
@@ -42,8 +42,8 @@ def _three_calls(w, d, plan, window=0):
     return slots, out
 
 
-def _step(w, d, plan, window=0, max_seq_len=None):
-    slots = torch.full((w.num_reqs,), 12345, dtype=torch.int64, device="cuda")
+def _step(w, d, plan, window=0, max_seq_len=None, with_slots=True):
+    slots = torch.full((w.num_reqs,), 12345, dtype=torch.int64, device="cuda") if with_slots else None
     ws = pkv.new_workspace(plan.workspace_bytes, "cuda")
     out = torch.empty_like(d.q)
     pkv.paged_attention_decode_step(d.q, d.new_k, d.new_v, d.cache, d.block_table, d.seq_lens,
@@ -69,13 +69,17 @@ def test_decode_step_equals_the_three_calls(name):
     check_close("decode_step_" + name, out_f64(ob), ref, TOL[w.cache_dtype], FLOOR[w.cache_dtype])
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8", "int4"])
-def test_decode_step_edges(dtype):
+@pytest.mark.parametrize("dtype,workers", [("bf16", None), ("fp8", None), ("int4", None), ("bf16", 4),
+                                           ("int4", 3)])
+def test_decode_step_edges(dtype, workers):
     """Length-1 rows (the new token alone), a window of one key, rows whose
     new token has no mapped block (slot -1, nothing written, NaN output),
     seq_len 0 and past max_seq_len (NaN, slot -1), and ordinary rows around
-    them; the written planes must equal the oracle's write."""
-    say("decode step edges", dtype)
+    them; the written planes must equal the oracle's write.  With fewer
+    workers than rows some workers write several rows' new tokens; there the
+    slots are not asked for (NULL), and the planes and outputs must not
+    change."""
+    say("decode step edges", dtype, "workers", workers)
     rng = np.random.default_rng(17)
     B, bs, Hq, Hkv, D = 9, 16, 32, 8, 128
     lens = np.array([1, 17, 16, 33, 200, 0, 500, 64, 2], np.int32)
@@ -92,14 +96,18 @@ def test_decode_step_edges(dtype):
     for window in (0, 1, 40):
         d = w.device()
         plan = pkv.decode_plan(B, Hq, d.cache, max_len, window, blocks_not_shared=True)
-        slots, out = _step(w, d, plan, window, max_len)
+        if workers:
+            pkv.tune_plan(plan, B, Hq, d.cache, max_len, window, num_workers=workers, lead_workers=0)
+            assert plan.num_workers == workers < B
+        slots, out = _step(w, d, plan, window, max_len, with_slots=workers is None)
         torch.cuda.synchronize()
-        s = slots.cpu().numpy()
         ok = np.array([0, 1, 2, 3, 4, 8])
-        assert (s[[5, 6, 7]] == -1).all()
         ref_slots, _ = paging.slot_mapping(bt, np.arange(B + 1, dtype=np.int32), np.maximum(lens - 1, 0),
                                            bs, num_blocks=w.num_blocks)
-        assert np.array_equal(s[ok], ref_slots[ok])
+        if slots is not None:
+            s = slots.cpu().numpy()
+            assert (s[[5, 6, 7]] == -1).all()
+            assert np.array_equal(s[ok], ref_slots[ok])
         # the planes: the oracle's write of the valid rows only
         kp, vp = paging.cache_write(w.k_plane, w.v_plane, w.new_k[ok], w.new_v[ok], ref_slots[ok], "bf16",
                                     w.cache_dtype, w.k_scale, w.v_scale)
@@ -111,4 +119,4 @@ def test_decode_step_edges(dtype):
                                      sliding_window=window, k_scale=w.k_scale, v_scale=w.v_scale)
         # single-key rows return v itself (up to about 1.2 here), so the
         # bf16 output's half ulp reaches 3.9e-3: bound per element instead
-        check_close("decode_step_edges_%s_w%d" % (dtype, window), o[ok], ref, 8e-3, 1e-4)
+        check_close("decode_step_edges_%s_w%d_%s" % (dtype, window, workers), o[ok], ref, 8e-3, 1e-4)
