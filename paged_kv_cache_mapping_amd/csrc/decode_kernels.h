@@ -1908,8 +1908,8 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
   if (cur >= 0) flush();
 
   // ---- the decode step's own tokens: row r by worker W - 1 - r % W (the
-  // last workers, whose shares are the smaller ones with lead shares), after
-  // its own units (the split reads no token's slot it could race with: the
+  // last workers: when the plan has lead shares theirs are the smaller
+  // ones), after its own units (no worker reads a slot being written: the
   // rows' visible keys end before their own token)
   if (a.new_token)
     for (int r = W - 1 - blockIdx.x; r < a.num_rows; r += W) write_own_token<D>(a, r, lane);
@@ -2037,7 +2037,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   constexpr int DPL = D >= LPH ? D / LPH : 1;       // dims per lane
   constexpr int U = 8;                              // pieces per half and round of loads
   const int lane = threadIdx.x;
-  const int half = NH == 1 ? 0 : lane / (kWave / NH);
+  const int half = lane / (kWave / NH);
   const int hl = lane % (kWave / NH);               // lane within its half
   const int groups = a.num_q_heads / GT;
   const int item = blockIdx.x / (RI / RW);
