@@ -2001,13 +2001,50 @@ struct OwnToken {
   }
   __device__ __forceinline__ void merge(const DecodeArgs& a, float& M, float& den, float (&num)[DPL]) const {
     float dot = 0.f, vv[DPL];
+    // fp8: the codes through the hardware conversion, four at a time, as
+    // the write makes them (a group holding a NaN takes the integer encoder)
+    float k8[DPL], v8[DPL];
+    if (a.kv_dtype == PKV_FP8_E4M3) {
+#pragma unroll
+      for (int i0 = 0; i0 < DPL; i0 += 4) {
+        constexpr int G4 = DPL < 4 ? DPL : 4;
+        float kx[4], vx[4];
+        bool nan = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          kx[i] = i < G4 ? as_float((uint32_t)kb[i0 + i] << 16) * a.inv_k_scale : 0.f;
+          vx[i] = i < G4 ? as_float((uint32_t)vb[i0 + i] << 16) * a.inv_v_scale : 0.f;
+          nan |= kx[i] != kx[i] || vx[i] != vx[i];
+        }
+        uint32_t kc, vc;
+        if (!nan) {
+          kc = e4m3x4_encode_no_nan(kx[0], kx[1], kx[2], kx[3]);
+          vc = e4m3x4_encode_no_nan(vx[0], vx[1], vx[2], vx[3]);
+        } else {
+          kc = vc = 0u;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            kc |= e4m3_encode(kx[i]) << (8 * i);
+            vc |= e4m3_encode(vx[i]) << (8 * i);
+          }
+        }
+        const f32x2 ka = e4m3x2_to_f32<false>(kc), kh = e4m3x2_to_f32<true>(kc);
+        const f32x2 va = e4m3x2_to_f32<false>(vc), vh = e4m3x2_to_f32<true>(vc);
+        const float kd[4] = {ka.x, ka.y, kh.x, kh.y}, vd[4] = {va.x, va.y, vh.x, vh.y};
+#pragma unroll
+        for (int i = 0; i < G4; ++i) {
+          k8[i0 + i] = kd[i];
+          v8[i0 + i] = vd[i];
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < DPL; ++i) {
       const float qx = as_float((uint32_t)qb[i] << 16);
       float kx = as_float((uint32_t)kb[i] << 16), vx = as_float((uint32_t)vb[i] << 16);
       if (a.kv_dtype == PKV_FP8_E4M3) {
-        kx = e4m3x2_to_f32<false>(e4m3_encode(kx * a.inv_k_scale)).x;
-        vx = e4m3x2_to_f32<false>(e4m3_encode(vx * a.inv_v_scale)).x;
+        kx = k8[i];
+        vx = v8[i];
       } else if (a.kv_dtype == PKV_INT4) {
         kx = (float)((int)int4_encode(kx * a.inv_k_scale) - 8);
         vx = (float)((int)int4_encode(vx * a.inv_v_scale) - 8);
