@@ -1946,9 +1946,9 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
 // The balanced kernel; decode_flat_kernel_2w asks the compiler to fit two
 // waves per SIMD (used for eight query heads per item, where the default
 // register allocation leaves room for only one).
-template <int D, int GT, int KV, int DEPTH, int QT = 1>
+template <int D, int GT, int KV, int DEPTH, int QT = 1, bool NTL = false>
 __global__ __launch_bounds__(64) void decode_flat_kernel(DecodeArgs a) {
-  decode_flat_body<D, GT, KV, DEPTH, QT>(a);
+  decode_flat_body<D, GT, KV, DEPTH, QT, NTL>(a);
 }
 
 template <int D, int GT, int KV, int DEPTH, int QT = 1, bool NTL = false>
@@ -2265,10 +2265,12 @@ void launch_stream(const DecodeArgs& a, int workers, hipStream_t s) {
     return;
   }
   // non-temporal K/V loads when the caller promised that no block is read
-  // by two rows (bf16 items on two waves; see kv_load)
-  if constexpr (KV == PKV_BF16 && two_waves(D, KV, GT, QT)) {
+  // by two rows (bf16 items; see kv_load)
+  if constexpr (KV == PKV_BF16) {
     if (a.stream_loads) {
-      decode_flat_kernel_2w<D, GT, KV, kDepth, QT, true><<<workers, 64, lds, s>>>(a);
+      if constexpr (two_waves(D, KV, GT, QT))
+        decode_flat_kernel_2w<D, GT, KV, kDepth, QT, true><<<workers, 64, lds, s>>>(a);
+      else decode_flat_kernel<D, GT, KV, kDepth, QT, true><<<workers, 64, lds, s>>>(a);
       return;
     }
   }
