@@ -1959,18 +1959,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 
 // Merge phase of the balanced scheme: one wave per (row, head group) with
 // more than one piece.  The split phase leaves, per (row, group), the piece
-// count and the output row, so the wave needs no row lookup.  The two
-// halves of the wave take alternate pieces (half j pieces j, j + 2, ...);
-// within a half, lane l takes head l / LPH of the rows and DPL consecutive
-// dims, so it reads one (m, l) pair and one run of acc per piece and merges
-// online, eight pieces' loads in flight per half (sixteen per wave, the
-// first sixteen issued with the piece count); the halves' states then
-// combine across the wave, and for the decode step the first half adds the
-// step's own token.
-// Rows of an item one merge wave takes: items of more than 2 rows are merged
-// by several waves (more waves in flight, fewer loads per lane: measured
-// faster than 4 rows per wave on the decode steps, 0.2 to 1.3 us).
-__host__ __device__ constexpr int merge_rows_per_wave(int rows) { return rows > 2 ? 2 : rows; }
+// count and the output row, so the wave needs no row lookup.  The wave's
+// four 16-lane parts take alternate pieces (part j pieces j, j + 4, ...);
+// within a part, lane l takes DPL consecutive dims of the row, so it reads
+// one (m, l) pair and one run of acc per piece and merges online, eight
+// pieces' loads in flight per part (32 per wave, the first 32 issued with
+// the piece count); the parts' states then combine across the wave, and for
+// the decode step the first part adds the step's own token.
+// Rows of an item one merge wave takes: one (an item of R rows is merged by
+// R waves: more waves in flight, fewer loads per lane; measured faster than
+// waves of 2 and 4 rows with halves or whole waves on every piece).
+__host__ __device__ constexpr int merge_rows_per_wave(int rows) { return rows > 1 ? 1 : rows; }
 
 // The step's own token (position seq_len - 1 of row b, pkv_paged_attention_
 // decode_step) joining a merge wave's online softmax for its row h (query
@@ -1980,7 +1979,7 @@ __host__ __device__ constexpr int merge_rows_per_wave(int rows) { return rows > 
 // scaled as the cached keys' are).  The lane's query, key and value
 // elements are loaded with the merge's first round of partials
 // (OwnToken::load) and joined after the pieces (OwnToken::merge; every lane
-// of the half calls it: the dot product is reduced across a row's LPH
+// of the first part calls it: the dot product is reduced across a row's LPH
 // lanes).
 template <int D, int LPH, int DPL>
 struct OwnToken {
@@ -2069,13 +2068,13 @@ template <int D, int GT, int OT, int QT = 1, bool NT = false>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   constexpr int RI = GT * QT;                       // rows of an item: (token, head)
   constexpr int RW = merge_rows_per_wave(RI);       // rows one wave merges
-  constexpr int NH = 2;                             // wave halves taking alternate pieces
-  constexpr int LPH = kWave / NH / RW;              // lanes per row within a half
+  constexpr int NH = 4;                             // wave parts taking alternate pieces
+  constexpr int LPH = kWave / NH / RW;              // lanes per row within a part
   constexpr int DPL = D >= LPH ? D / LPH : 1;       // dims per lane
-  constexpr int U = 8;                              // pieces per half and round of loads
+  constexpr int U = 8;                              // pieces per part and round of loads
   const int lane = threadIdx.x;
-  const int half = lane / (kWave / NH);
-  const int hl = lane % (kWave / NH);               // lane within its half
+  const int half = lane / (kWave / NH);             // the wave part
+  const int hl = lane % (kWave / NH);               // lane within its part
   const int groups = a.num_q_heads / GT;
   const int item = blockIdx.x / (RI / RW);
   const int b = item / groups;
@@ -2087,7 +2086,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const float* ml = a.ws_m + rg * a.max_splits * (2 * RI);
   const float* accp = a.ws_acc + ((rg * RI + h) * a.max_splits) * D + (active ? d0 : 0);
   float mv[U], lv[U], av[U][DPL];
-  // round r: this half's pieces r NH U + NH u + half; the first round is
+  // round r: this part's pieces r NH U + NH u + half; the first round is
   // read together with the piece count (the slots exist whatever the count;
   // words past it are ignored)
   auto load_round = [&](int s0, int np) __attribute__((always_inline)) {
@@ -2132,18 +2131,21 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
       M = mn;
     }
   }
-  if constexpr (NH == 2) {
-    // the other half's state for the same row and dims (lane l ^ 32)
-    const float Mo = __shfl_xor(M, kWave / 2);
-    const float deno = __shfl_xor(den, kWave / 2);
-    const float mn = fmaxf(M, Mo);
-    const float c_me = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mn);
-    const float c_ot = Mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mo - mn);
-    den = den * c_me + deno * c_ot;
+  if constexpr (NH > 1) {
+    // the other parts' states for the same row and dims (lanes l ^ 16, l ^ 32)
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) num[i] = num[i] * c_me + __shfl_xor(num[i], kWave / 2) * c_ot;
-    M = mn;
-    if (half != 0) return;                           // one half writes
+    for (int o = kWave / NH; o < kWave; o <<= 1) {
+      const float Mo = __shfl_xor(M, o);
+      const float deno = __shfl_xor(den, o);
+      const float mn = fmaxf(M, Mo);
+      const float c_me = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mn);
+      const float c_ot = Mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mo - mn);
+      den = den * c_me + deno * c_ot;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) num[i] = num[i] * c_me + __shfl_xor(num[i], o) * c_ot;
+      M = mn;
+    }
+    if (half != 0) return;                           // one part writes
   }
   if constexpr (NT) {
     static_assert(QT == 1, "one query token per row");
