@@ -774,25 +774,26 @@ int pf_tokens(int d, int g) {
 }
 
 template <int D, int G, int KV>
-void pf_launch(const PrefillArgs& a, hipStream_t s) {
+int pf_launch(const PrefillArgs& a, hipStream_t s) {
   const size_t lds = pf_lds_bytes<D, G>(a.max_blocks);
-  // past 64 KiB the kernel asks for the larger dynamic LDS explicitly (a
-  // refusal surfaces as the launch's error)
-  if (lds > 64 * 1024)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_tile_kernel<D, G, KV, kPfWavesAlone>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // past 64 KiB the kernel asks for the larger dynamic LDS explicitly
+  if (lds > 64 * 1024 &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_tile_kernel<D, G, KV, kPfWavesAlone>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    return PKV_ERR_HIP;
   prefill_tile_kernel<D, G, KV, kPfWavesAlone><<<a.workers, kPfWavesAlone * 64, lds, s>>>(a);
   prefill_merge_kernel<D, G, kPfWavesAlone><<<a.workers, kPfMergeThreads, 0, s>>>(a);
+  return PKV_OK;
 }
 
 template <int D, int KV>
 int pf_launch_g(const PrefillArgs& a, int g, hipStream_t s) {
   switch (g) {
-    case 1: pf_launch<D, 1, KV>(a, s); return PKV_OK;
-    case 2: pf_launch<D, 2, KV>(a, s); return PKV_OK;
-    case 4: pf_launch<D, 4, KV>(a, s); return PKV_OK;
-    case 8: pf_launch<D, 8, KV>(a, s); return PKV_OK;
-    case 16: pf_launch<D, 16, KV>(a, s); return PKV_OK;
+    case 1: return pf_launch<D, 1, KV>(a, s);
+    case 2: return pf_launch<D, 2, KV>(a, s);
+    case 4: return pf_launch<D, 4, KV>(a, s);
+    case 8: return pf_launch<D, 8, KV>(a, s);
+    case 16: return pf_launch<D, 16, KV>(a, s);
   }
   return PKV_ERR_UNSUPPORTED;
 }
