@@ -107,7 +107,14 @@ static int make_plan(int rows, int hq, int hkv, int d, int bs, int kv_dtype, int
   if (allow_stream && mfma_eligible(kv_dtype, d, bs) && gm > 0 && rows <= kMaxStreamRows) {
     // balanced partition over resident wave slots
     const long long units = (long long)(rows > 0 ? rows : 1) * (hq / gm) * nvis;
-    const int per_cu = stream_waves_per_cu(gm, kv_dtype, d, force_hpi > 0);
+    int per_cu = stream_waves_per_cu(gm, kv_dtype, d, force_hpi > 0);
+    // bf16 single-query items of up to 4 rows: one wave per SIMD in equal
+    // shares measured a little faster than two with lead and trail shares
+    // (C2 step 64.7 -> 64.2 us, alternating runs; the shared-prefix step
+    // the same).  The partition does not depend on the plan's flags, so
+    // that PKV_PLAN_BLOCKS_NOT_SHARED changes how blocks are loaded, not
+    // the bits.
+    if (kv_dtype == PKV_BF16 && force_hpi == 0 && gm <= 4 && per_cu == 8) per_cu = 4;
     long long workers = cus * per_cu;
     const long long need = (units + kStreamMinUnits - 1) / kStreamMinUnits;
     plan->lead_workers = 0;
