@@ -944,16 +944,16 @@ struct MfmaShape {
 
 // INT4 K words for the matrix cores.  A word holds elements n = 0..7 of a
 // lane's k-chunk as nibbles u (element n in bits 4n .. 4n + 3).  Each nibble
-// becomes the bfloat16 value 192 + u (exponent of 128, mantissa bits
-// 0x40 | u, exact), so the products need a per-row correction of
-// -200 * sum(q) to give (u - 8) . q.  The four dwords hold elements in the
+// becomes the bfloat16 value 128 + u (high byte 0x43, low byte u: exponent
+// of 128, mantissa u, exact), so the products need a per-row correction of
+// -136 * sum(q) to give (u - 8) . q.  The four dwords hold elements in the
 // order 0, 2, 4, 6, 1, 3, 5, 7; the query operand is permuted to match
 // (int4_q_perm).
 // v_perm_b32 selects bytes of {S0 (high), S1 (low)}: selector 0..3 picks a
 // byte of S1, 4..7 a byte of S0, 0x0C gives zero.
 __device__ __forceinline__ uint4 int4_k_bf16(uint32_t w) {
-  const uint32_t x = (w & 0x0F0F0F0Fu) | 0x40404040u;          // bytes 0x40|u0, u2, u4, u6
-  const uint32_t y = ((w >> 4) & 0x0F0F0F0Fu) | 0x40404040u;   // bytes 0x40|u1, u3, u5, u7
+  const uint32_t x = w & 0x0F0F0F0Fu;          // bytes u0, u2, u4, u6
+  const uint32_t y = (w >> 4) & 0x0F0F0F0Fu;   // bytes u1, u3, u5, u7
   constexpr uint32_t kHi = 0x43434343u;                        // the high byte of each bf16
   return make_uint4(__builtin_amdgcn_perm(x, kHi, 0x00050004u), __builtin_amdgcn_perm(x, kHi, 0x00070006u),
                     __builtin_amdgcn_perm(y, kHi, 0x00050004u), __builtin_amdgcn_perm(y, kHi, 0x00070006u));
@@ -1214,7 +1214,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
   float m[GT];
   f32x4_t lsum = {0.f, 0.f, 0.f, 0.f};
   float m1 = -INFINITY, ls1 = 0.f;   // row-broadcast scheme: head lane % 16's max and sum
-  float kqz = 0.f;                    // INT4: 200 * sum(q) of row lane % 16, times scale_log2
+  float kqz = 0.f;                    // INT4: 136 * sum(q) of row lane % 16, times scale_log2
 
   // first query element of the piece (gid = row * kvgroups + head group)
   auto q_elem = [&](int gid, int tok) __attribute__((always_inline)) -> int64_t {
@@ -1241,7 +1241,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
       }
       sq += shfl_xor_t(sq, 16);
       sq += shfl_xor_t(sq, 32);
-      kqz = 200.0f * sq * a.scale_log2;
+      kqz = 136.0f * sq * a.scale_log2;
     }
   };
   // A operand of the piece's query rows: lane l takes row l % 16, elements
@@ -1734,6 +1734,35 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
         const s16x4_t zero4 = {0, 0, 0, 0};
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh) {
+          // B operand of tile t: the bf16 values of dimension t of tokens
+          // 4 R .. 4 R + 3, two to a dword (the first token in the low half)
+          uint32_t bw[2][VEPL];
+          if constexpr (kI4) {
+            // nibble u as the bf16 value 128 + u (high byte 0x43, low byte u:
+            // exponent of 128, mantissa u, exact); the flush takes 136 times
+            // the weight sum off.  Every code is a finite value, so keys
+            // outside the piece's span (weight 0) need no zeroing.  Bytes of
+            // x: dimensions 0, 2, 4, 6; of y: 1, 3, 5, 7.  v_perm_b32 picks
+            // bytes of {S0 (high), S1 (low)}: selector 0..3 a byte of S1,
+            // 4..7 a byte of S0.
+            constexpr uint32_t kHi = 0x43434343u;
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+              const uint32_t r0 = bf.v[2 * pp][hh], r1 = bf.v[2 * pp + 1][hh];
+              const uint32_t x0 = r0 & 0x0F0F0F0Fu, x1 = r1 & 0x0F0F0F0Fu;
+              const uint32_t y0 = (r0 >> 4) & 0x0F0F0F0Fu, y1 = (r1 >> 4) & 0x0F0F0F0Fu;
+              // bytes j, j + 1 of both tokens, interleaved (j = 0 and 2)
+              const uint32_t nx[2] = {__builtin_amdgcn_perm(x1, x0, 0x05010400u),
+                                      __builtin_amdgcn_perm(x1, x0, 0x07030602u)};
+              const uint32_t ny[2] = {__builtin_amdgcn_perm(y1, y0, 0x05010400u),
+                                      __builtin_amdgcn_perm(y1, y0, 0x07030602u)};
+#pragma unroll
+              for (int t = 0; t < VEPL; ++t) {
+                const uint32_t n = (t & 1) ? ny[t / 4] : nx[t / 4];
+                bw[pp][t] = __builtin_amdgcn_perm(kHi, n, ((t / 2) & 1) ? 0x04030402u : 0x04010400u);
+              }
+            }
+          } else {
           // V rows of tokens 4 R + u as bf16 pairs (elements 2k, 2k + 1 in
           // dword k); keys outside the piece's span are zeroed (their weights
           // are 0, but the slots may hold anything)
@@ -1743,14 +1772,6 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
             if constexpr (KV == PKV_BF16) {
               const uint4 raw = bf.v[u][hh];
               vw[u][0] = raw.x; vw[u][1] = raw.y; vw[u][2] = raw.z; vw[u][3] = raw.w;
-            } else if constexpr (kI4) {
-              // nibble u as the bf16 value 128 + u (exponent of 128, mantissa
-              // u, exact); the flush takes 136 times the weight sum off
-              const uint32_t raw = bf.v[u][hh];
-              const uint32_t xa = raw & 0x0F0F0F0Fu, ya = (raw >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-              for (int k = 0; k < 4; ++k)
-                vw[u][k] = __builtin_amdgcn_perm(ya, xa, 0x0C000C00u | ((4u + k) << 16) | (uint32_t)k) | 0x43004300u;
             } else {   // fp8 codes widened to bf16 pairs (exact; the V scale comes at the flush)
               const uint2 raw = bf.v[u][hh];
               vw[u][0] = e4m3x2_to_bf16x2<false>(raw.x); vw[u][1] = e4m3x2_to_bf16x2<true>(raw.x);
@@ -1763,6 +1784,13 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
               for (int k = 0; k < 4; ++k) vw[u][k] = live ? vw[u][k] : 0u;
             }
           }
+#pragma unroll
+          for (int t = 0; t < VEPL; ++t) {
+            const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
+            bw[0][t] = __builtin_amdgcn_perm(vw[1][t / 2], vw[0][t / 2], sel);
+            bw[1][t] = __builtin_amdgcn_perm(vw[3][t / 2], vw[2][t / 2], sel);
+          }
+          }
           // pair items: each KV head's V meets only its own rows' weights
           s16x4_t ah = pa_hi, al = pa_lo;
           if constexpr (kPair) {
@@ -1772,10 +1800,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
           }
 #pragma unroll
           for (int t = 0; t < VEPL; ++t) {
-            const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
-            const uint32_t b01 = __builtin_amdgcn_perm(vw[1][t / 2], vw[0][t / 2], sel);
-            const uint32_t b23 = __builtin_amdgcn_perm(vw[3][t / 2], vw[2][t / 2], sel);
-            const s16x4_t vb = __builtin_bit_cast(s16x4_t, make_uint2(b01, b23));
+            const s16x4_t vb = __builtin_bit_cast(s16x4_t, make_uint2(bw[0][t], bw[1][t]));
             accm[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, vb, accm[t], 0, 0, 0);
             accm[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, vb, accm[t], 0, 0, 0);
           }
