@@ -1762,6 +1762,31 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
                 bw[pp][t] = __builtin_amdgcn_perm(kHi, n, ((t / 2) & 1) ? 0x04030402u : 0x04010400u);
               }
             }
+          } else if constexpr (KV == PKV_FP8_E4M3) {
+            // codes of two tokens interleaved byte by byte, so that each
+            // hardware conversion of a code pair (exact; the V scale comes at
+            // the flush) gives one dimension of both; keys outside the
+            // piece's span are zeroed first (code 0 is +0)
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+              uint2 r0 = bf.v[2 * pp][hh], r1 = bf.v[2 * pp + 1][hh];
+              if constexpr (!full) {
+                const int pos = p0 + 4 * (lane / 16) + 2 * pp;
+                const bool live0 = pos >= s_lo && pos <= s_hi, live1 = pos + 1 >= s_lo && pos + 1 <= s_hi;
+                r0 = live0 ? r0 : make_uint2(0, 0);
+                r1 = live1 ? r1 : make_uint2(0, 0);
+              }
+#pragma unroll
+              for (int w = 0; w < 2; ++w) {
+                const uint32_t c0 = w ? r0.y : r0.x, c1 = w ? r1.y : r1.x;   // dimensions 4 w .. 4 w + 3
+                const uint32_t n01 = __builtin_amdgcn_perm(c1, c0, 0x05010400u);
+                const uint32_t n23 = __builtin_amdgcn_perm(c1, c0, 0x07030602u);
+                bw[pp][4 * w] = e4m3x2_to_bf16x2<false>(n01);
+                bw[pp][4 * w + 1] = e4m3x2_to_bf16x2<true>(n01);
+                bw[pp][4 * w + 2] = e4m3x2_to_bf16x2<false>(n23);
+                bw[pp][4 * w + 3] = e4m3x2_to_bf16x2<true>(n23);
+              }
+            }
           } else {
           // V rows of tokens 4 R + u as bf16 pairs (elements 2k, 2k + 1 in
           // dword k); keys outside the piece's span are zeroed (their weights
@@ -1769,14 +1794,8 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
           uint32_t vw[4][4];
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            if constexpr (KV == PKV_BF16) {
-              const uint4 raw = bf.v[u][hh];
-              vw[u][0] = raw.x; vw[u][1] = raw.y; vw[u][2] = raw.z; vw[u][3] = raw.w;
-            } else {   // fp8 codes widened to bf16 pairs (exact; the V scale comes at the flush)
-              const uint2 raw = bf.v[u][hh];
-              vw[u][0] = e4m3x2_to_bf16x2<false>(raw.x); vw[u][1] = e4m3x2_to_bf16x2<true>(raw.x);
-              vw[u][2] = e4m3x2_to_bf16x2<false>(raw.y); vw[u][3] = e4m3x2_to_bf16x2<true>(raw.y);
-            }
+            const uint4 raw = bf.v[u][hh];
+            vw[u][0] = raw.x; vw[u][1] = raw.y; vw[u][2] = raw.z; vw[u][3] = raw.w;
             if constexpr (!full) {
               const int pos = p0 + 4 * (lane / 16) + u;
               const bool live = pos >= s_lo && pos <= s_hi;
