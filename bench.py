@@ -619,8 +619,32 @@ def main():
     torch.cuda.synchronize()
     split_ms = a.elapsed_time(b) / args.steps
 
+    # the same steps recorded once in a HIP graph (one step per pool of the
+    # rotation) and replayed: what a serving loop that replays its step sees
+    graph = None
+    if plan.scheme == 1 and not args.three_call:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(npools):
+                step(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, -(-args.steps // npools))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        gms = a.elapsed_time(b) / (reps * npools)
+        graph = dict(us_per_step=round(gms * 1e3, 2), steps_per_graph=npools, replays=reps)
+        del g
+
     ab = algorithmic_bytes(w)
     value = ab["step"] / (ms_per_step * 1e-3) / 1e9
+    if graph is not None:
+        graph["GBps"] = round(ab["step"] / (graph["us_per_step"] * 1e-6) / 1e9, 1)
     split_gbps = ab["split"] / (split_ms * 1e-3) / 1e9
 
     # bulk KV writes: distinct random slots, bf16 -> bf16 and bf16 -> fp8
@@ -730,6 +754,7 @@ def main():
         "decode_attention": {"split_kernel_us": round(split_ms * 1e3, 2),
                              "split_GBps": round(split_gbps, 1),
                              "kv_bytes": ab["kv"], "step_bytes": ab["step"]},
+        **({"graph_replay": graph} if graph else {}),
         "kv_write": writes,
         # the split kernel's GB/s (algorithmic bytes) against the probe's
         # (every byte of the blocks it reads): a conservative fraction
