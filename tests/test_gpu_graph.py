@@ -10,14 +10,18 @@ device and a synchronisation, with the outputs poisoned in between, and is
 checked on its own ([W] § Pinpointing the Token Slot, [P] § Handling
 Softmax Across Blocks).  The chunked call's prefill part runs on a second
 stream forked from and joined to the caller's, which the recording follows.
+The decode entry point that allocates nothing (its partials in the
+library's static scratch) is recorded too: it exists for such callers.
 """
+
+import ctypes
 
 import numpy as np
 import pytest
 import torch
 
 import paged_kv_cache_mapping_amd as pkv
-from paged_kv_cache_mapping_amd import workloads
+from paged_kv_cache_mapping_amd import _lib, workloads
 
 from helpers import gpu_or_skip, host_bits, say
 from test_gpu_chunked import _chunk_case
@@ -108,6 +112,42 @@ def test_chunked_replays_give_the_eager_bits(qmax, W):
     call()
     torch.cuda.synchronize()
     ref = out.clone()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for i in range(REPLAYS):
+        out.fill_(float("nan"))
+        _eager_work()
+        g.replay()
+        torch.cuda.synchronize()
+        say("replay", i)
+        assert _same_bits(out, ref)
+
+
+def test_static_scratch_decode_replays_give_the_eager_bits():
+    say("graph static-scratch decode")
+    lib = _lib.load()
+    w = workloads.llama8b_decode()
+    d = w.device()
+    out = torch.empty_like(d.q)
+
+    def call():
+        c = d.cache.c_struct()
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        st = lib.pkv_paged_attention_decode_static(
+            ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(d.q.data_ptr()), _lib.PKV_BF16, w.num_reqs,
+            w.num_q_heads, ctypes.byref(c), ctypes.c_void_p(d.block_table.data_ptr()),
+            d.block_table.shape[1], ctypes.c_void_p(d.seq_lens.data_ptr()), w.max_seq_len, w.scale, 0, stream)
+        assert st == _lib.PKV_OK, pkv.status_string(st)
+
+    call()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    ws_form = pkv.paged_attention_decode(d.q, d.cache, d.block_table, d.seq_lens, w.max_seq_len, w.scale)
+    torch.cuda.synchronize()
+    assert _same_bits(ref, ws_form)
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
