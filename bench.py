@@ -9,7 +9,9 @@ last-level cache cannot serve the KV reads.
 
 Prints one JSON line: the whole step's algorithmic HBM bytes per second
 (value), the split kernel's roofline (HIP events around back-to-back launches of it),
-bulk KV-write rates, and the CPU oracle on a bounded sample of the same step.
+bulk KV-write rates, the same steps recorded in a HIP graph and replayed
+(graph_replay; `value` stays the eager step), and the CPU oracle on a bounded
+sample of the same step.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
