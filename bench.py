@@ -100,11 +100,13 @@ def algorithmic_bytes(w):
 def decode_plan_for(pkv, w, cache, shared_blocks=False, **tune):
     """The plan the decode line times: the library's plan for the workload,
     declaring PKV_PLAN_BLOCKS_NOT_SHARED unless blocks are shared (the
-    prefix workload) or the caller says they may be; `tune` overrides
-    fields through pkv.tune_plan (None keeps the library's value)."""
-    not_shared = not shared_blocks and not w.info.get("shares_blocks", False)
+    prefix workload, which declares PKV_PLAN_BLOCKS_SHARED instead) or the
+    caller says they may be; `tune` overrides fields through pkv.tune_plan
+    (None keeps the library's value)."""
+    shares = w.info.get("shares_blocks", False)
+    not_shared = not shared_blocks and not shares
     plan = pkv.decode_plan(w.num_reqs, w.num_q_heads, cache, w.max_seq_len,
-                           blocks_not_shared=not_shared)
+                           blocks_not_shared=not_shared, blocks_shared=shares)
     if any(v is not None for v in tune.values()):
         pkv.tune_plan(plan, w.num_reqs, w.num_q_heads, cache, w.max_seq_len, **tune)
     return plan

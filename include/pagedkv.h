@@ -242,8 +242,8 @@ PKV_API int pkv_copy_blocks(const pkv_cache* cache, const int32_t* src_ids,
  * scheme 0 (fixed splits): row r's visible blocks are cut into splits of
  *   split_blocks blocks; one work item per (row, head group, split).
  * scheme 1 (balanced): num_workers workers each take a contiguous share (at
- *   least split_blocks blocks) of all (row, KV head group, block) units; a
- *   row is cut wherever a share ends.  Used with block sizes that are
+ *   least split_blocks blocks) of all (KV head group, row, block) units,
+ *   ordered head group first; a row is cut wherever a share ends.  Used with block sizes that are
  *   multiples of 16 and bf16 / fp8 caches whose head_dim is a multiple of 32
  *   with rows of at least 64 bytes, or INT4 caches with head_dim 128, for at
  *   most 4096 rows (the rows' prefix sums are kept in LDS).  Other bf16 /
@@ -267,6 +267,22 @@ PKV_API int pkv_copy_blocks(const pkv_cache* cache, const int32_t* src_ids,
                                          either way; a wrong promise costs
                                          time only (shared blocks are then
                                          re-read from HBM by every row).      */
+#define PKV_PLAN_BLOCKS_SHARED 2      /* the caller says that many rows of one
+                                         call read the same physical blocks (a
+                                         common prompt [W-zh §
+                                         PagedAttention与Block管理]).  The
+                                         balanced scheme then runs each
+                                         eighth of its units (about one KV
+                                         head group's) on one XCD, so a block
+                                         that several rows read is re-read
+                                         from that XCD's L2 rather than from
+                                         the memory-side cache.  Rows are cut
+                                         at other places than without the
+                                         flag, so results agree within the
+                                         attention bounds, not bit for bit.
+                                         Not together with
+                                         PKV_PLAN_BLOCKS_NOT_SHARED
+                                         (PKV_ERR_SHAPE).                     */
 
 typedef struct {
   int32_t split_blocks;   /* scheme 0: blocks per split; 1: least blocks per worker */
@@ -484,10 +500,13 @@ PKV_API int pkv_chunked_workspace_size(int32_t num_tokens, int32_t num_reqs,
  * max_query_len    bounds every q_len_r; max_seq_len bounds every seq_lens[r].
  * causal           1: query at p sees keys <= p.  0: all keys < seq_len.
  * sliding_window   0, or W: keys >= p - W + 1 only.
- * flags            0 or PKV_PLAN_BLOCKS_NOT_SHARED: the same promise as for
- *                  decode plans (no physical block read by two requests of
- *                  the call); the decode rows' bf16 loads then bypass the
- *                  caches.  Other bits return PKV_ERR_SHAPE.
+ * flags            0, PKV_PLAN_BLOCKS_NOT_SHARED or PKV_PLAN_BLOCKS_SHARED,
+ *                  as for decode plans, for the decode-shaped parts (single
+ *                  queries and multi-token items): no physical block read by
+ *                  two requests of the call (their bf16 loads then bypass
+ *                  the caches), or many requests reading the same blocks
+ *                  (their units then run an eighth per XCD).  Other bits, or
+ *                  both, return PKV_ERR_SHAPE.
  * workspace        at least pkv_chunked_workspace_size(...) bytes.
  * Invalid rows (q_len > seq_len, lengths out of range, missing blocks) get NaN.
  * INT4 caches: the decode form's shapes (head_dim 128, at most 4096

@@ -22,6 +22,7 @@ PKV_ERR_HIP = -6
 
 # pkv_decode_plan_make flags
 PKV_PLAN_BLOCKS_NOT_SHARED = 1
+PKV_PLAN_BLOCKS_SHARED = 2
 
 PKV_STATIC_SCRATCH_BYTES = 64 << 20
 

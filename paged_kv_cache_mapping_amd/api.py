@@ -12,7 +12,8 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_INT4, PKV_PLAN_BLOCKS_NOT_SHARED, PkvCache,
+from ._lib import (PKV_BF16, PKV_F32, PKV_FP8_E4M3, PKV_INT4, PKV_PLAN_BLOCKS_NOT_SHARED,
+                   PKV_PLAN_BLOCKS_SHARED, PkvCache,
                    PkvDecodePlan, check, load)
 
 _DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16, torch.uint8: PKV_FP8_E4M3}
@@ -181,12 +182,14 @@ def copy_blocks(src_ids, dst_ids, cache, err_count=None):
         _stream(src_ids.device)))
 
 
-def decode_plan(num_rows, num_q_heads, cache, max_seq_len, sliding_window=0, blocks_not_shared=False):
+def decode_plan(num_rows, num_q_heads, cache, max_seq_len, sliding_window=0, blocks_not_shared=False,
+                blocks_shared=False):
     """The library's plan (pkv_decode_plan_make); blocks_not_shared sets
-    PKV_PLAN_BLOCKS_NOT_SHARED (no block is read by two rows of a call)."""
+    PKV_PLAN_BLOCKS_NOT_SHARED (no block is read by two rows of a call),
+    blocks_shared PKV_PLAN_BLOCKS_SHARED (many rows read the same blocks)."""
     lib = load()
     plan = PkvDecodePlan()
-    flags = PKV_PLAN_BLOCKS_NOT_SHARED if blocks_not_shared else 0
+    flags = (PKV_PLAN_BLOCKS_NOT_SHARED if blocks_not_shared else 0) | (PKV_PLAN_BLOCKS_SHARED if blocks_shared else 0)
     check("pkv_decode_plan_make", lib.pkv_decode_plan_make(
         num_rows, num_q_heads, cache.num_kv_heads, cache.head_dim, cache.block_size,
         cache.dtype, max_seq_len, sliding_window, flags, ctypes.byref(plan)))
@@ -311,10 +314,11 @@ def chunked_workspace_size(num_tokens, num_reqs, num_q_heads, cache, max_query_l
 
 def paged_attention_chunked(q, query_start_loc, seq_lens, max_query_len, cache, block_table,
                             max_seq_len, softmax_scale, causal=True, sliding_window=0,
-                            workspace=None, out=None, blocks_not_shared=False):
+                            workspace=None, out=None, blocks_not_shared=False, blocks_shared=False):
     """Mixed prefill/decode step: q [T, Hq, D] -> out [T, Hq, D];
     blocks_not_shared passes PKV_PLAN_BLOCKS_NOT_SHARED (no block read by
-    two requests of the call)."""
+    two requests of the call), blocks_shared PKV_PLAN_BLOCKS_SHARED (many
+    requests read the same blocks)."""
     lib = load()
     _need(q.dim() == 3 and q.is_contiguous(), "q must be contiguous [T, Hq, D]")
     _i32(query_start_loc, "query_start_loc")
@@ -331,7 +335,8 @@ def paged_attention_chunked(q, query_start_loc, seq_lens, max_query_len, cache, 
     check("pkv_paged_attention_chunked", lib.pkv_paged_attention_chunked(
         _ptr(out), _ptr(q), _dt(q), T, Hq, _ptr(query_start_loc), _ptr(seq_lens), R, max_query_len,
         ctypes.byref(c), _ptr(block_table), block_table.shape[1], max_seq_len, softmax_scale,
-        1 if causal else 0, sliding_window, PKV_PLAN_BLOCKS_NOT_SHARED if blocks_not_shared else 0,
+        1 if causal else 0, sliding_window,
+        (PKV_PLAN_BLOCKS_NOT_SHARED if blocks_not_shared else 0) | (PKV_PLAN_BLOCKS_SHARED if blocks_shared else 0),
         _ptr(ws), wsb, _stream(q.device)))
     return out
 

@@ -85,14 +85,20 @@ static size_t plan_bytes(const pkv_decode_plan& p, int rows, int hq, int d) {
   return p.max_splits > 1 ? partial_bytes(rows, hq, p.max_splits, d) : 0;
 }
 
-constexpr int kKnownPlanFlags = PKV_PLAN_BLOCKS_NOT_SHARED;
+constexpr int kKnownPlanFlags = PKV_PLAN_BLOCKS_NOT_SHARED | PKV_PLAN_BLOCKS_SHARED;
+
+// known bits only, and not both promises at once
+static bool plan_flags_ok(int flags) {
+  if (flags & ~kKnownPlanFlags) return false;
+  return (flags & kKnownPlanFlags) != kKnownPlanFlags;
+}
 
 static int make_plan(int rows, int hq, int hkv, int d, int bs, int kv_dtype, int max_seq_len,
                      int window, int extra, bool allow_stream, pkv_decode_plan* plan, int force_hpi = 0,
                      int flags = 0) {
   if (!plan) return PKV_ERR_NULL;
   if (rows < 0 || hq <= 0 || hkv <= 0 || max_seq_len < 0 || window < 0) return PKV_ERR_SHAPE;
-  if (flags & ~kKnownPlanFlags) return PKV_ERR_SHAPE;
+  if (!plan_flags_ok(flags)) return PKV_ERR_SHAPE;
   if (hq % hkv) return PKV_ERR_SHAPE;
   if (dtype_bits(kv_dtype) == 0) return PKV_ERR_DTYPE;
   if (!head_dim_supported(d) || !block_size_supported(bs)) return PKV_ERR_UNSUPPORTED;
@@ -111,9 +117,10 @@ static int make_plan(int rows, int hq, int hkv, int d, int bs, int kv_dtype, int
     // bf16 single-query items of up to 4 rows: one wave per SIMD in equal
     // shares measured a little faster than two with lead and trail shares
     // (C2 step 64.7 -> 64.2 us, alternating runs; the shared-prefix step
-    // the same).  The partition does not depend on the plan's flags, so
-    // that PKV_PLAN_BLOCKS_NOT_SHARED changes how blocks are loaded, not
-    // the bits.
+    // the same).  The shares do not depend on the plan's flags, so that
+    // PKV_PLAN_BLOCKS_NOT_SHARED changes how blocks are loaded, not the
+    // bits (PKV_PLAN_BLOCKS_SHARED changes which workgroup takes which
+    // share, and so where rows are cut).
     if (kv_dtype == PKV_BF16 && force_hpi == 0 && gm <= 4 && per_cu == 8) per_cu = 4;
     long long workers = cus * per_cu;
     const long long need = (units + kStreamMinUnits - 1) / kStreamMinUnits;
@@ -156,7 +163,7 @@ static int make_plan(int rows, int hq, int hkv, int d, int bs, int kv_dtype, int
 static int check_plan(const pkv_decode_plan* plan, int rows, int hq, int hkv, int d, int bs,
                       int kv_dtype, int max_seq_len, int window, int extra) {
   if (!plan) return PKV_ERR_NULL;
-  if (plan->flags & ~kKnownPlanFlags) return PKV_ERR_SHAPE;
+  if (!plan_flags_ok(plan->flags)) return PKV_ERR_SHAPE;
   const int group = hq / hkv;
   const int nvis = max_visible_blocks(max_seq_len, bs, window, extra);
   if (plan->scheme == 1) {
@@ -341,6 +348,7 @@ static int prepare(DecodeArgs& a, void* out, const void* q, int q_dtype, int row
   a.split_blocks = plan->split_blocks;
   a.max_splits = plan->max_splits;
   a.stream_loads = plan->scheme == 1 && (plan->flags & PKV_PLAN_BLOCKS_NOT_SHARED) != 0;
+  a.xcd_local = plan->scheme == 1 && (plan->flags & PKV_PLAN_BLOCKS_SHARED) != 0;
   a.stream = plan->scheme == 1;
   a.heads_per_item = plan->heads_per_item;
   a.lead_workers = plan->lead_workers;
@@ -396,7 +404,7 @@ extern "C" int pkv_decode_plan_resize(int32_t num_rows, int32_t num_q_heads, int
   if (!plan) return PKV_ERR_NULL;
   if (num_rows < 0 || num_q_heads <= 0 || max_seq_len < 0 || sliding_window < 0) return PKV_ERR_SHAPE;
   if (!head_dim_supported(head_dim) || !block_size_supported(block_size)) return PKV_ERR_UNSUPPORTED;
-  if (plan->flags & ~kKnownPlanFlags) return PKV_ERR_SHAPE;
+  if (!plan_flags_ok(plan->flags)) return PKV_ERR_SHAPE;
   if (plan->heads_per_item < 1 || num_q_heads % plan->heads_per_item) return PKV_ERR_SHAPE;
   const int nvis = max_visible_blocks(max_seq_len, block_size, sliding_window, 0);
   if (plan->scheme == 1) {
@@ -710,7 +718,7 @@ extern "C" int pkv_paged_attention_chunked(void* out, const void* q, int32_t q_d
   if (q_dtype != (cache->dtype == PKV_F32 ? PKV_F32 : PKV_BF16)) return PKV_ERR_DTYPE;
   if (num_tokens == 0 || num_reqs == 0) return PKV_OK;
   if (!query_start_loc) return PKV_ERR_NULL;
-  if (flags & ~PKV_PLAN_BLOCKS_NOT_SHARED) return PKV_ERR_SHAPE;
+  if (!plan_flags_ok(flags)) return PKV_ERR_SHAPE;
   ChunkPlans p;
   st = chunk_plans(num_tokens, num_reqs, num_q_heads, cache, max_query_len, max_seq_len,
                    sliding_window, p, flags);

@@ -75,6 +75,7 @@ struct DecodeArgs {
   float* ws_m;
   float* ws_l;
   int32_t stream_loads;     // balanced scheme, bf16: non-temporal K/V loads (no block read twice)
+  int32_t xcd_local;        // balanced scheme: an eighth of the units per XCD (blocks shared by rows)
   int32_t stream;           // balanced partition (piece counts in ws_np)
   int32_t heads_per_item;
   int32_t* ws_np;           // balanced partition: pieces per (row, head group)
@@ -841,11 +842,20 @@ __global__ __launch_bounds__(64) void decode_split_uni_kernel(DecodeArgs a) {
 // --------------------------------------------------------------------------
 // Balanced split phase on the matrix cores, one load pipeline per worker.
 //
-// Work units are (row, KV-head group, visible block), ordered row-major.  The
-// grid is a fixed number of single-wave workers, one per SIMD (a second wave
-// on a SIMD loses instruction issue to the older one and lags it by a fifth,
-// so equal shares would finish unequally); worker w takes the contiguous units
-// [w P, (w + 1) P) with P = max(ceil(U / workers), min_units).  Each stretch
+// Work units are (KV-head group, row, visible block), ordered group-major:
+// unit u is block u - g T - cum[r] of row r in group g, with T the visible
+// blocks of all rows.  The grid is a fixed number of single-wave workers, one
+// per SIMD (a second wave on a SIMD loses instruction issue to the older one
+// and lags it by a fifth, so equal shares would finish unequally); logical
+// worker w takes the contiguous units [w P, (w + 1) P) with
+// P = max(ceil(U / workers), min_units); workgroup b is logical worker b,
+// except under PKV_PLAN_BLOCKS_SHARED with equal shares and a worker count
+// divisible by 8, where it is logical worker (b % 8) (W / 8) + b / 8:
+// workgroups go to the eight XCDs round-robin, so each XCD then gets one
+// contiguous eighth of the units, about one head group's, and blocks that
+// several rows share (a common prompt) are reread from that XCD's L2 rather
+// than from the memory-side cache (on unshared blocks that placement
+// measured slower).  Each stretch
 // of a worker's range that belongs to one (row, head group) is a "piece": it
 // is folded with an online softmax and written either as the final output
 // (when the piece covers the whole row) or as a partial (m, l, acc) in slot
@@ -1185,8 +1195,14 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
   const long long U = (long long)carry * kvgroups;
   const int W = gridDim.x;
   const Shares sh = make_shares(U, W, a.lead_workers, a.trail_pct, a.split_blocks);
-  const long long u_lo = min(U, sh.begin(blockIdx.x));
-  const long long u_hi = min(U, sh.begin((long long)blockIdx.x + 1));
+  // logical worker: an eighth of the units per XCD for shared blocks when
+  // shares are equal (lead and trail shares keep the dispatch order they
+  // are sized for)
+  const int lw = (a.xcd_local && sh.lead >= W && W % 8 == 0)
+                     ? (int)(blockIdx.x % 8) * (W / 8) + (int)(blockIdx.x / 8)
+                     : (int)blockIdx.x;
+  const long long u_lo = min(U, sh.begin(lw));
+  const long long u_hi = min(U, sh.begin((long long)lw + 1));
 
   const int spb_log2 = a.bs_log2 - 4;                     // 16-token steps per block
   const int64_t blk_bytes = a.block_stride * S::kBits / 8;
@@ -1313,7 +1329,7 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
     const int kvg = cur % kvgroups;
     const int h0 = (kvg / a.sub_groups) * a.group + (kvg % a.sub_groups) * GT;
     const int nv = cum[b + 1] - cum[b];
-    const long long seg_base = (long long)cum[b] * kvgroups + (long long)kvg * nv;
+    const long long seg_base = (long long)kvg * carry + cum[b];
     const long long r0 = sh.range_of(seg_base);
     const int piece = (int)(sh.range_of(s_first) - r0);
     const int npieces = (int)(sh.range_of(seg_base + nv - 1) - r0 + 1);
@@ -1467,16 +1483,17 @@ __device__ __forceinline__ void decode_flat_body(const DecodeArgs& a) {
     int bt_raw = -1;    // the unit's table entry, checked once the query loads are in flight too
     if (lane < nunits) {
       const long long u = wbase + lane;
-      int lo = 0, hi = a.num_rows;            // largest b with cum[b] * kvgroups <= u
+      // head group, then the row: the largest b with cum[b] <= the unit's
+      // block index within its group (carry > 0 whenever there are units)
+      const int kvg = sh.narrow ? (int)((uint32_t)u / (uint32_t)carry) : (int)(u / carry);
+      const int rel = (int)(u - (long long)kvg * carry);
+      int lo = 0, hi = a.num_rows;
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if ((long long)cum[mid] * kvgroups <= u) lo = mid; else hi = mid;
+        if (cum[mid] <= rel) lo = mid; else hi = mid;
       }
       const int b = lo;
-      const int nv = cum[b + 1] - cum[b];
-      const long long rel = u - (long long)cum[b] * kvgroups;
-      const int kvg = sh.narrow ? (int)((uint32_t)rel / (uint32_t)nv) : (int)(rel / nv);
-      const int j = (int)(rel - (long long)kvg * nv);
+      const int j = rel - cum[b];
       int req, tok, klo, khi;
       if (have_rec) {
         const int4 rr = rrec[b];

@@ -270,6 +270,13 @@ def test_plan_flags_are_checked(lib):
     assert st == _lib.PKV_OK and plan.flags == _lib.PKV_PLAN_BLOCKS_NOT_SHARED
     assert lib.pkv_decode_plan_make(64, 32, 8, 128, 16, _lib.PKV_BF16, 2048, 0, 6,
                                     ctypes.byref(plan)) == _lib.PKV_ERR_SHAPE
+    st = lib.pkv_decode_plan_make(64, 32, 8, 128, 16, _lib.PKV_BF16, 2048, 0,
+                                  _lib.PKV_PLAN_BLOCKS_SHARED, ctypes.byref(plan))
+    assert st == _lib.PKV_OK and plan.flags == _lib.PKV_PLAN_BLOCKS_SHARED
+    # both promises at once contradict each other
+    both = _lib.PKV_PLAN_BLOCKS_NOT_SHARED | _lib.PKV_PLAN_BLOCKS_SHARED
+    assert lib.pkv_decode_plan_make(64, 32, 8, 128, 16, _lib.PKV_BF16, 2048, 0, both,
+                                    ctypes.byref(plan)) == _lib.PKV_ERR_SHAPE
 
 
 @pytest.mark.parametrize("rows,hq,window,split,workers,hpi", [

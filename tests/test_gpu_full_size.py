@@ -32,7 +32,7 @@ import oracle_pool
 import paged_kv_cache_mapping_amd as pkv
 from helpers import (check_close, gpu_or_skip, host_bits, oracle_decode_step, out_f64, say)
 from oracle import attention, layout, paging
-from paged_kv_cache_mapping_amd import workloads
+from paged_kv_cache_mapping_amd import _lib, workloads
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
@@ -207,16 +207,44 @@ def test_spec_workload_every_row():
 
 def test_shared_prefix_workload_every_row():
     """The full prefix workload (100 requests over one 2000-token prompt's
-    blocks) in the bench's launch configuration (no non-temporal loads,
-    since blocks are shared): every row bounded."""
+    blocks) in the bench's launch configuration (PKV_PLAN_BLOCKS_SHARED:
+    ordinary loads, an eighth of the units per XCD): every row bounded."""
     say("shared prefix every row")
     w = workloads.shared_prefix_decode()
     base = w.device()
     plan, slots, out = _bench_decode_step(w, base)
-    assert plan.flags == 0
+    assert plan.flags == _lib.PKV_PLAN_BLOCKS_SHARED
     s_ref, kp, vp, ref = oracle_decode_step(w, "bf16")
     assert np.array_equal(slots.cpu().numpy(), s_ref)
     check_close("prefix_all_rows", out_f64(out), ref, 2e-3, FLOOR_SMALL)
+
+
+@pytest.mark.parametrize("name,floor,tol", [("llama8b", FLOOR_SMALL, 2e-3),
+                                            ("fp8", FLOOR_UNIT, 3e-2),
+                                            ("int4", FLOOR_SMALL, 2e-3),
+                                            ("prefix", FLOOR_SMALL, 2e-3)])
+def test_blocks_shared_placement_every_row(name, floor, tol):
+    """PKV_PLAN_BLOCKS_SHARED only moves shares between workgroups (each XCD
+    takes an eighth of the units where shares are equal; with lead and trail
+    shares nothing moves): on the full workloads every row of the decode
+    step stays bounded, and the slots and cache bytes equal the oracle's
+    write."""
+    say("blocks-shared placement", name)
+    w = workloads.shared_prefix_decode() if name == "prefix" else workloads.ALL[name]()
+    d = w.device()
+    plan = pkv.decode_plan(w.num_reqs, w.num_q_heads, d.cache, w.max_seq_len, blocks_shared=True)
+    assert plan.flags == _lib.PKV_PLAN_BLOCKS_SHARED
+    ws = pkv.new_workspace(plan.workspace_bytes, "cuda")
+    out = torch.empty_like(d.q)
+    slots = torch.empty(w.num_reqs, dtype=torch.int64, device="cuda")
+    pkv.paged_attention_decode_step(d.q, d.new_k, d.new_v, d.cache, d.block_table, d.seq_lens,
+                                    w.max_seq_len, w.scale, plan, ws, out, slots=slots)
+    torch.cuda.synchronize()
+    s_ref, kp, vp, ref = oracle_decode_step(w, "bf16")
+    assert np.array_equal(slots.cpu().numpy(), s_ref)
+    assert host_bits(d.cache.k).tobytes() == kp.tobytes()
+    assert host_bits(d.cache.v).tobytes() == vp.tobytes()
+    check_close("blocks_shared_" + name, out_f64(out), ref, tol, floor)
 
 
 def _signed_v(w, dtype, amp, group, seed):
