@@ -171,8 +171,9 @@ def cpu_baseline(w, sample_seqs, min_seconds=10.0):
 
 def stream_probe(w, pools, dev, steps):
     """The streaming-read probe (libpkvprobe.so): the K/V bytes of the decode
-    step's (row, KV head, block) units, read in the decode's order by
-    single-wave workers with nothing else to do, rotating over the same
+    step's (KV head, row, block) units, read in the decode's order (head
+    group first; here one KV head per group) by single-wave workers with
+    nothing else to do, rotating over the same
     pools; and the same number of units read block-contiguously.  Returns
     GB/s of the bytes read (whole 16-token blocks) per setting and the best,
     the practical ceiling the split kernel is held against."""
@@ -195,10 +196,10 @@ def stream_probe(w, pools, dev, steps):
     for p, (cache, bt) in enumerate(pools):
         bt_h = bt.cpu().numpy()
         offs = []
-        for r, L in enumerate(w.seq_lens):
-            n = -(-int(L) // w.block_size)
-            phys = bt_h[r, :n].astype(np.int64)
-            for h in range(w.num_kv_heads):
+        for h in range(w.num_kv_heads):
+            for r, L in enumerate(w.seq_lens):
+                n = -(-int(L) // w.block_size)
+                phys = bt_h[r, :n].astype(np.int64)
                 offs.append(phys * blk_bytes + h * w.head_dim * elt)
         offs = np.concatenate(offs)
         lists["decode_order"].append(torch.from_numpy(offs).to(dev))

@@ -114,21 +114,21 @@ static int make_plan(int rows, int hq, int hkv, int d, int bs, int kv_dtype, int
     // balanced partition over resident wave slots
     const long long units = (long long)(rows > 0 ? rows : 1) * (hq / gm) * nvis;
     int per_cu = stream_waves_per_cu(gm, kv_dtype, d, force_hpi > 0);
-    // bf16 single-query items of up to 4 rows: one wave per SIMD in equal
-    // shares measured a little faster than two with lead and trail shares
-    // (C2 step 64.7 -> 64.2 us, alternating runs; the shared-prefix step
-    // the same).  The shares do not depend on the plan's flags, so that
-    // PKV_PLAN_BLOCKS_NOT_SHARED changes how blocks are loaded, not the
-    // bits (PKV_PLAN_BLOCKS_SHARED changes which workgroup takes which
-    // share, and so where rows are cut).
-    if (kv_dtype == PKV_BF16 && force_hpi == 0 && gm <= 4 && per_cu == 8) per_cu = 4;
+    // Under PKV_PLAN_BLOCKS_SHARED every share is equal (the placement of
+    // an eighth of the units per XCD needs equal shares), and bf16
+    // single-query items of up to 4 rows run one wave per SIMD (shared-prefix
+    // split 65.7 us against 68.0 with two waves and lead / trail shares).
+    // PKV_PLAN_BLOCKS_NOT_SHARED leaves the shares alone, so that it changes
+    // how blocks are loaded, not the bits.
+    const bool shared = (flags & PKV_PLAN_BLOCKS_SHARED) != 0;
+    if (shared && kv_dtype == PKV_BF16 && force_hpi == 0 && gm <= 4 && per_cu == 8) per_cu = 4;
     long long workers = cus * per_cu;
     const long long need = (units + kStreamMinUnits - 1) / kStreamMinUnits;
     plan->lead_workers = 0;
     plan->trail_share_pct = 100;
     if (workers > need) {
       workers = need;
-    } else if (per_cu > 4) {
+    } else if (per_cu > 4 && !shared) {
       plan->lead_workers = (int32_t)(workers / 2);
       plan->trail_share_pct = kTrailPct;
     }

@@ -195,7 +195,7 @@ def test_budget_config_fills_the_budget(lib):
 
 
 @pytest.mark.parametrize("hq,hkv,dtype,hpi,per_cu", [
-    (32, 8, _lib.PKV_BF16, 4, 4),       # 4 rows: one wave per SIMD in equal shares (measured)
+    (32, 8, _lib.PKV_BF16, 4, 8),       # 4 rows, matrix-core P.V: two waves
     (64, 8, _lib.PKV_BF16, 8, 4),       # single-query 8-row bf16 items keep the vector ALUs: one wave
     (128, 8, _lib.PKV_BF16, 16, 8),     # 16 rows, matrix-core P.V: two waves
     (32, 8, _lib.PKV_FP8_E4M3, 4, 8),
@@ -209,13 +209,21 @@ def test_budget_config_fills_the_budget(lib):
 def test_plan_rows_and_waves_follow_the_kernels(lib, hq, hkv, dtype, hpi, per_cu):
     """The decode plan's item height and worker count match what the kernels
     launch for the shape (host arithmetic; 256 compute units without a GPU):
-    two waves per SIMD where the kernel fits 256 registers, one elsewhere and
-    for bf16 single-query items of up to 4 rows."""
+    two waves per SIMD where the kernel fits 256 registers, one elsewhere;
+    lead and trail shares with two waves.  Under PKV_PLAN_BLOCKS_SHARED the
+    shares are equal, and bf16 single-query items of up to 4 rows take one
+    wave per SIMD."""
     plan = _lib.PkvDecodePlan()
     st = lib.pkv_decode_plan_make(64, hq, hkv, 128, 16, dtype, 2048, 0, 0, ctypes.byref(plan))
     assert st == _lib.PKV_OK and plan.scheme == 1
     assert plan.heads_per_item == hpi
     assert plan.num_workers == 256 * per_cu
+    assert plan.lead_workers == (plan.num_workers // 2 if per_cu == 8 else 0)
+    st = lib.pkv_decode_plan_make(64, hq, hkv, 128, 16, dtype, 2048, 0, _lib.PKV_PLAN_BLOCKS_SHARED,
+                                  ctypes.byref(plan))
+    assert st == _lib.PKV_OK and plan.lead_workers == 0 and plan.trail_share_pct == 100
+    one_wave = dtype == _lib.PKV_BF16 and hpi <= 4
+    assert plan.num_workers == 256 * (4 if one_wave else per_cu)
 
 
 @pytest.mark.parametrize("rows,dtype,scheme", [
