@@ -844,11 +844,12 @@ __global__ __launch_bounds__(64) void decode_split_uni_kernel(DecodeArgs a) {
 //
 // Work units are (KV-head group, row, visible block), ordered group-major:
 // unit u is block u - g T - cum[r] of row r in group g, with T the visible
-// blocks of all rows.  The grid is a fixed number of single-wave workers, one
-// per SIMD (a second wave on a SIMD loses instruction issue to the older one
-// and lags it by a fifth, so equal shares would finish unequally); logical
-// worker w takes the contiguous units [w P, (w + 1) P) with
-// P = max(ceil(U / workers), min_units); workgroup b is logical worker b,
+// blocks of all rows.  The grid is a fixed number of single-wave workers,
+// one or two per SIMD; logical worker w takes a contiguous run of units,
+// equal shares of P = max(ceil(U / workers), min_units) or, with two waves
+// per SIMD, full shares for the first half of the workers and 80 % shares
+// for the rest (a second wave on a SIMD loses instruction issue to the older
+// one and lags it by a fifth); workgroup b is logical worker b,
 // except under PKV_PLAN_BLOCKS_SHARED with equal shares and a worker count
 // divisible by 8, where it is logical worker (b % 8) (W / 8) + b / 8:
 // workgroups go to the eight XCDs round-robin, so each XCD then gets one
