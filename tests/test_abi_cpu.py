@@ -287,6 +287,23 @@ def test_plan_flags_are_checked(lib):
                                     ctypes.byref(plan)) == _lib.PKV_ERR_SHAPE
 
 
+@pytest.mark.parametrize("flags,status", [
+    (0, _lib.PKV_ERR_WORKSPACE),
+    (_lib.PKV_PLAN_BLOCKS_NOT_SHARED, _lib.PKV_ERR_WORKSPACE),
+    (_lib.PKV_PLAN_BLOCKS_SHARED, _lib.PKV_ERR_WORKSPACE),
+    (_lib.PKV_PLAN_BLOCKS_NOT_SHARED | _lib.PKV_PLAN_BLOCKS_SHARED, _lib.PKV_ERR_SHAPE),
+    (4, _lib.PKV_ERR_SHAPE),
+])
+def test_chunked_flags_are_checked(lib, flags, status):
+    """The chunked call refuses unknown flag bits and both block-sharing
+    statements at once; valid flags get as far as the missing workspace.
+    Either way nothing is launched (the device pointers are stand-ins)."""
+    c = _cache()
+    st = lib.pkv_paged_attention_chunked(0x100, 0x100, _lib.PKV_BF16, 4, 32, 0x100, 0x100, 4, 1,
+                                         ctypes.byref(c), 0x100, 8, 128, 0.1, 1, 0, flags, None, 0, None)
+    assert st == status
+
+
 @pytest.mark.parametrize("rows,hq,window,split,workers,hpi", [
     (64, 32, 0, 8, 2048, 4),
     (64, 32, 0, 3, 100, 2),
