@@ -224,11 +224,10 @@ def test_shared_prefix_workload_every_row():
                                             ("int4", FLOOR_SMALL, 2e-3),
                                             ("prefix", FLOOR_SMALL, 2e-3)])
 def test_blocks_shared_placement_every_row(name, floor, tol):
-    """PKV_PLAN_BLOCKS_SHARED only moves shares between workgroups (each XCD
-    takes an eighth of the units where shares are equal; with lead and trail
-    shares nothing moves): on the full workloads every row of the decode
-    step stays bounded, and the slots and cache bytes equal the oracle's
-    write."""
+    """PKV_PLAN_BLOCKS_SHARED makes the shares equal and moves them between
+    workgroups (each XCD takes an eighth of the units): on the full
+    workloads every row of the decode step stays bounded, and the slots and
+    cache bytes equal the oracle's write."""
     say("blocks-shared placement", name)
     w = workloads.shared_prefix_decode() if name == "prefix" else workloads.ALL[name]()
     d = w.device()
