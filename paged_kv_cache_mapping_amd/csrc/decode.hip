@@ -60,7 +60,7 @@ static bool mfma_eligible(int kv_dtype, int d, int bs) {
 
 constexpr int kMaxStreamRows = 4096;   // prefix sums of the balanced scheme live in LDS
 constexpr int kStreamMinUnits = 8;     // blocks per worker at least (bounds the pieces)
-constexpr int kTrailPct = 80;            // second wave on a SIMD: share in percent
+constexpr int kTrailPct = 90;            // second wave on a SIMD: share in percent
 constexpr int kLdsPerCU = 160 * 1024;
 
 // Resident waves per CU for the balanced kernels: two per SIMD while the

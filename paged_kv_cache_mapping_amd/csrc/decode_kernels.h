@@ -847,7 +847,7 @@ __global__ __launch_bounds__(64) void decode_split_uni_kernel(DecodeArgs a) {
 // blocks of all rows.  The grid is a fixed number of single-wave workers,
 // one or two per SIMD; logical worker w takes a contiguous run of units,
 // equal shares of P = max(ceil(U / workers), min_units) or, with two waves
-// per SIMD, full shares for the first half of the workers and 80 % shares
+// per SIMD, full shares for the first half of the workers and 90 % shares
 // for the rest (a second wave on a SIMD loses instruction issue to the older
 // one and lags it by a fifth); workgroup b is logical worker b,
 // except under PKV_PLAN_BLOCKS_SHARED with equal shares and a worker count
