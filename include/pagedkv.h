@@ -308,7 +308,8 @@ typedef struct {
  * Fill `plan` for a decode (one query token per row) over `num_rows` rows of
  * a cache of `kv_dtype`.  max_seq_len bounds every seq_lens entry;
  * sliding_window 0 = full attention; flags: PKV_PLAN_* bits (0 = none).
- * Returns PKV_ERR_SHAPE for unknown flags.
+ * Returns PKV_ERR_SHAPE for unknown flags and for PKV_PLAN_BLOCKS_NOT_SHARED
+ * together with PKV_PLAN_BLOCKS_SHARED.
  */
 PKV_API int pkv_decode_plan_make(int32_t num_rows, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim,
