@@ -146,3 +146,24 @@ def test_blocks_not_shared_gives_the_same_bits(qmax, W):
     ref = attention.paged_attention(c["q"], "bf16", c["kp"], c["vp"], "bf16", c["bt"], c["L"], c["qsl"], 0.125,
                                     causal=True, sliding_window=W)
     assert max_err(out_f64(ntl), ref) <= 2e-3
+
+
+@pytest.mark.parametrize("qmax,W", [(1, 0), (4, 0), (4, 100), (64, 0)])
+def test_blocks_shared_chunked_calls_match_the_oracle(qmax, W):
+    """PKV_PLAN_BLOCKS_SHARED on a chunked call: its single-query rows and
+    multi-token items run an eighth of their units per XCD (prefill tiles
+    are unaffected); every output stays within the bound of the oracle."""
+    say("blocks shared, chunked", qmax, W)
+    c = _chunk_case(3500 + qmax + W, R=12, Lmax=1500, qmax=qmax, Hq=32, Hkv=8, D=128, bs=16, v_sigma=0.2)
+
+    def dev16(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    cache = pkv.CacheView.from_planes(dev16(c["kp"]), dev16(c["vp"]))
+    out = pkv.paged_attention_chunked(dev16(c["q"]), torch.from_numpy(c["qsl"]).cuda(),
+                                      torch.from_numpy(c["L"]).cuda(), int(np.diff(c["qsl"]).max()), cache,
+                                      torch.from_numpy(c["bt"]).cuda(), int(c["L"].max()), 0.125, causal=True,
+                                      sliding_window=W, blocks_shared=True)
+    torch.cuda.synchronize()
+    ref = attention.paged_attention(c["q"], "bf16", c["kp"], c["vp"], "bf16", c["bt"], c["L"], c["qsl"], 0.125,
+                                    causal=True, sliding_window=W)
+    assert max_err(out_f64(out), ref) <= 2e-3
